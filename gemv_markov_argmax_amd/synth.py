@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the DSpark draft-round hot path.
+
+This module only draws random numbers and arranges them into the shapes the
+hot path consumes. It holds none of the method's arithmetic (no products, no
+argmax), so the fp64 oracle and the HIP path can both be fed from it without
+sharing any computation.
+
+Workload shapes stand in for the lanes described on the pages (none of their
+models, prompts or weights exist here):
+
+* ``tiny`` -- a small case the oracle finishes in well under a second.
+* ``qwen3_8b_head`` -- Qwen3-8B block-7 drafter head: B = k = 7, d = 4096,
+  V = 151936, markov rank 256 (SharpInference #441, section "Observation" and
+  "Proposed work", which sizes markov_w2 at 78 MB).
+* ``lane27b`` -- vllm.cpp #436 "SPEC-DSPARK W7", section "Measured": k = 15
+  drafted rows over a 248320-entry draft vocabulary.
+* ``reduced_vocab_batched`` -- the 35B lane's 32000-entry draft vocabulary
+  (same page, same section), batched over 8 requests with B = k = 9.
+* ``draft_layer`` -- one draft transformer layer's projections at M = 7
+  (SharpInference #441, "Hypothesis") plus a 7424-wide confidence probe
+  (ds4 #772, "Summary").
+
+Every tensor is drawn from its own PCG64 stream, keyed by (seed, stream id,
+block index), so a value never depends on how many threads fill the array.
+Normals are drawn in float32; bf16 tensors are rounded to bf16 by
+round-to-nearest-even on the bit pattern and returned as ``uint16`` bits.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+SEED_BASE = 20261200
+
+# Stream ids: fixed, so adding a tensor never shifts another one's values.
+S_W_LM, S_W1, S_W2, S_H, S_PREV0, S_PROBE_W, S_PROBE_X, S_TIES, S_D2T, S_BASE = range(10)
+S_LAYER = 16  # q, k, v, o, gate, up, down and their inputs follow from here
+
+_BLOCK = 1 << 22  # elements per independently seeded block
+
+CONFIGS = {
+    "tiny": dict(num_reqs=1, B=4, k=4, d=256, V=4096, r=32),
+    "qwen3_8b_head": dict(num_reqs=1, B=7, k=7, d=4096, V=151936, r=256),
+    "lane27b": dict(num_reqs=1, B=15, k=15, d=5120, V=248320, r=256, tie_frac=0.05),
+    "reduced_vocab_batched": dict(num_reqs=8, B=9, k=9, d=5120, V=32000, r=256),
+    "draft_layer": dict(M=7, d=4096, ffn=12288, probe_width=7424),
+}
+CONFIG_SEED_INDEX = {name: i + 1 for i, name in enumerate(CONFIGS)}
+
+W_STD = 0.02  # weights ~ N(0, 0.02)
+TIE_VALUE = np.float32(32.0)  # far above any N(0, 1.3) base draw
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _gen(seed: int, stream: int, block: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, block])))
+
+
+def bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    Inputs must be finite. This is input preparation, not part of the method.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (r >> np.uint32(16)).astype(np.uint16)
+
+
+def _fill_blocks(n: int, fn) -> None:
+    nblk = (n + _BLOCK - 1) // _BLOCK
+    if nblk <= 1:
+        for b in range(nblk):
+            fn(b, b * _BLOCK, min(n, (b + 1) * _BLOCK))
+        return
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        list(ex.map(lambda b: fn(b, b * _BLOCK, min(n, (b + 1) * _BLOCK)), range(nblk)))
+
+
+def normal_f32(seed: int, stream: int, shape, std: float = 1.0) -> np.ndarray:
+    """float32 draws from N(0, std^2), blockwise seeded."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+
+    def fill(b, lo, hi):
+        v = _gen(seed, stream, b).standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        out[lo:hi] = v
+
+    _fill_blocks(n, fill)
+    return out.reshape(shape)
+
+
+def normal_bf16(seed: int, stream: int, shape, std: float = W_STD) -> np.ndarray:
+    """bf16 bits of N(0, std^2) draws (drawn in float32, rounded RNE)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+
+    def fill(b, lo, hi):
+        v = _gen(seed, stream, b).standard_normal(hi - lo, dtype=np.float32)
+        v *= np.float32(std)
+        out[lo:hi] = bf16_bits_rne(v)
+
+    _fill_blocks(n, fill)
+    return out.reshape(shape)
+
+
+def uniform_index(seed: int, stream: int, n: int, high: int) -> np.ndarray:
+    """int64 draws uniform in [0, high)."""
+    return _gen(seed, stream).integers(0, high, size=n, dtype=np.int64)
+
+
+def config_seed(name: str, replica: int = 0) -> int:
+    return SEED_BASE + CONFIG_SEED_INDEX[name] + 1000 * replica
+
+
+# ----------------------------------------------------------------------------
+# Inputs per entry point
+# ----------------------------------------------------------------------------
+
+def gemv_inputs(M: int, N: int, K: int, seed: int, w_std: float = W_STD):
+    """W bf16 bits [N, K] ~ N(0, w_std^2); X float32 [M, K] ~ N(0, 1)."""
+    W = normal_bf16(seed, S_W_LM, (N, K), w_std)
+    X = normal_f32(seed, S_H, (M, K))
+    return W, X
+
+
+def probe_inputs(M: int, D: int, seed: int):
+    """x float32 [M, D] ~ N(0, 1); w bf16 bits [D] ~ N(0, 0.02^2)."""
+    x = normal_f32(seed, S_PROBE_X, (M, D))
+    w = normal_bf16(seed, S_PROBE_W, (D,))
+    return x, w
+
+
+def markov_inputs(num_reqs: int, B: int, V: int, r: int, seed: int,
+                  base_std: float = 1.28, tie_frac: float = 0.0,
+                  tie_exact: bool = True):
+    """Inputs of the Markov loop taken on their own (base drawn directly).
+
+    base float32 [R, B, V] ~ N(0, base_std^2) -- 1.28 is what an lm_head with
+    d = 4096, weights N(0, 0.02^2) and unit hidden states produces;
+    w1, w2 bf16 bits [V, r] ~ N(0, 0.02^2); prev0 int64 [R] uniform in [0, V).
+
+    tie_frac > 0 marks that fraction of the R*B base rows (at least one) as
+    tie rows: two distinct vocabulary entries a < b of the row are both set to
+    TIE_VALUE, well above every other draw. With tie_exact the W2 row b is
+    also made a copy of row a, so the two scores are exactly equal and the
+    lowest-index rule must pick a. Pairs are disjoint across rows.
+    Returns (base, w1, w2, prev0, ties) where ties is a list of
+    (request, row, a, b).
+    """
+    base = normal_f32(seed, S_BASE, (num_reqs, B, V), base_std)
+    w1 = normal_bf16(seed, S_W1, (V, r))
+    w2 = normal_bf16(seed, S_W2, (V, r))
+    prev0 = uniform_index(seed, S_PREV0, num_reqs, V)
+    ties = []
+    if tie_frac > 0:
+        g = _gen(seed, S_TIES)
+        rows = np.flatnonzero(g.random(num_reqs * B) < tie_frac)
+        if rows.size == 0:
+            rows = np.array([int(g.integers(0, num_reqs * B))])
+        idx = g.choice(V, size=2 * rows.size, replace=False)
+        for j, row in enumerate(rows):
+            a, b = sorted((int(idx[2 * j]), int(idx[2 * j + 1])))
+            req, i = divmod(int(row), B)
+            base[req, i, a] = TIE_VALUE
+            base[req, i, b] = TIE_VALUE
+            if tie_exact:
+                w2[b, :] = w2[a, :]
+            ties.append((req, i, a, b))
+    return base, w1, w2, prev0, ties
+
+
+def d2t_map(V: int, seed: int, offset: int = 1000) -> np.ndarray:
+    """An injective draft->target id map (test use only): a seeded
+    permutation of [offset, offset + V)."""
+    return _gen(seed, S_D2T).permutation(V).astype(np.int64) + offset
+
+
+def round_inputs(name: str, seed: int | None = None, with_base: bool = False):
+    """All tensors of one draft round for a head configuration.
+
+    Returns a dict: W_lm [V, d] bf16, H [R*B, d] f32, w1/w2 [V, r] bf16,
+    prev0 [R] int64, probe_w [d] bf16, plus the shape fields.
+    """
+    cfg = dict(CONFIGS[name])
+    if "V" not in cfg:
+        raise ValueError(f"{name} is not a head configuration")
+    seed = config_seed(name) if seed is None else seed
+    R, B, d, V, r = cfg["num_reqs"], cfg["B"], cfg["d"], cfg["V"], cfg["r"]
+    out = dict(cfg, seed=seed, name=name)
+    out["W_lm"] = normal_bf16(seed, S_W_LM, (V, d))
+    out["H"] = normal_f32(seed, S_H, (R * B, d))
+    out["w1"] = normal_bf16(seed, S_W1, (V, r))
+    out["w2"] = normal_bf16(seed, S_W2, (V, r))
+    out["prev0"] = uniform_index(seed, S_PREV0, R, V)
+    out["probe_w"] = normal_bf16(seed, S_PROBE_W, (d,))
+    out["probe_bias"] = np.float32(0.0)
+    out["probe_threshold"] = np.float32(0.0)
+    return out
+
+
+def layer_inputs(seed: int | None = None, copies: int = 1):
+    """One draft layer at M = 7 (q/k/v/o [4096, 4096], gate/up [12288, 4096],
+    down [4096, 12288], bf16 ~ N(0, 0.02^2)), per-projection inputs
+    X [7, K] ~ N(0, 1), and a 7424-wide probe (w ~ N(0, 0.02^2), x ~ N(0, 1)).
+
+    ``copies`` > 1 draws that many independent weight sets.
+    """
+    cfg = CONFIGS["draft_layer"]
+    seed = config_seed("draft_layer") if seed is None else seed
+    M, d, f = cfg["M"], cfg["d"], cfg["ffn"]
+    shapes = dict(q=(d, d), k=(d, d), v=(d, d), o=(d, d), gate=(f, d), up=(f, d), down=(d, f))
+    layers = []
+    for c in range(copies):
+        ws = {}
+        for j, (nm, shp) in enumerate(shapes.items()):
+            ws[nm] = normal_bf16(seed, S_LAYER + 16 * c + j, shp)
+        layers.append(ws)
+    xs = {nm: normal_f32(seed, S_LAYER + 15 * 16 + j, (M, shp[1])) for j, (nm, shp) in enumerate(shapes.items())}
+    px, pw = probe_inputs(M, cfg["probe_width"], seed)
+    return dict(cfg, seed=seed, layers=layers, X=xs, probe_x=px, probe_w=pw,
+                probe_bias=np.float32(0.0), probe_threshold=np.float32(0.0))

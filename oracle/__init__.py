@@ -1,0 +1,9 @@
+"""fp64 CPU oracle of the DSpark draft-round hot path.
+
+Test infrastructure only: used by the tests, the build entry point's smoke
+check and the benchmark's CPU-baseline leg, never by the product path.
+"""
+from .dspark_oracle import (  # noqa: F401
+    NEAR_TIE, StepResult, bf16_to_f64, conf_probe, draft_round, gemv, gemv_rows,
+    greedy_argmax, lm_head, markov_sample, markov_scores, markov_step, proj_smallm,
+)

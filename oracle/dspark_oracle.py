@@ -1,0 +1,211 @@
+"""Plain fp64 CPU oracle for the DSpark draft-round hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check of the build entry point
+and the benchmark's CPU-baseline leg use it. It shares no code with the HIP
+path (the two meet only at the seeded input generator, which does no
+arithmetic of the method).
+
+Sources (the pages; a reader has them, not this copy):
+
+[W7]   vllm.cpp #436, "SPEC-DSPARK W7: the sequential Markov sample loop is
+       HOST-side - 28% of the draft step, 14.9 MB downloaded per step".
+       Sections "Measured", "The fix", "Gate" and the "W7 LANDED" comment.
+[SI441] SharpInference #441, "perf(cuda): DSpark GPU draft round runs ~3x the
+       bandwidth floor - small-M (B=7) projection GEMMs -> weight-stationary
+       matvec". Sections "Observation", "Hypothesis", "Proposed work".
+[DS772] ds4 #772, "dspark: cut per-cycle CUDA overheads (single-draft decode,
+       GPU confidence probe)". Sections "Summary", "Performance".
+
+Every function computes its plain definition in float64 from the exact input
+values (bf16 bits decode exactly; float32 inputs widen exactly). A library
+matmul is used as a step; nothing is blocked, fused or reordered.
+
+Readings taken where the pages leave a step open are listed with each
+function. The argmax decision is taken on float32 scores, the precision the
+pages give the scores ([W7] "W7 LANDED": base logits are f32), from the exact
+fp64 score rounded once to float32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+NEAR_TIE = 1e-3  # top-2 margin below which a drafted id is reported, not required
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the bf16 is the high half of an
+    IEEE binary32, so shifting the 16 bits up by 16 gives the same number."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _finite(*arrays):
+    for a in arrays:
+        if not np.all(np.isfinite(a)):
+            raise ValueError("oracle inputs must be finite")
+
+
+# ---------------------------------------------------------------------------
+# Small-M projections and the lm_head
+# ---------------------------------------------------------------------------
+
+def gemv(W_bits, X) -> np.ndarray:
+    """Y[m, n] = sum_t X[m, t] * W[n, t], in float64.
+
+    [SI441] "Observation": every draft projection and the lm_head multiplies
+    the B drafted positions' activations by one weight matrix, reading the
+    weight once for all B rows. W is [N, K] bf16 (row n is output n), X is
+    [M, K] float32, Y is [M, N].
+    """
+    W = bf16_to_f64(W_bits)
+    X64 = np.asarray(X, dtype=np.float32).astype(np.float64)
+    _finite(W, X64)
+    if W.ndim != 2 or X64.ndim != 2 or W.shape[1] != X64.shape[1]:
+        raise ValueError("gemv: W [N, K] and X [M, K] required")
+    return X64 @ W.T
+
+
+def gemv_rows(W_bits, X, rows) -> np.ndarray:
+    """The same definition evaluated only for the output columns ``rows``
+    (returns [M, len(rows)]); used to check sampled outputs at full size."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return gemv(np.asarray(W_bits)[rows], X)
+
+
+proj_smallm = gemv
+lm_head = gemv
+
+
+# ---------------------------------------------------------------------------
+# Markov-biased greedy sampling loop
+# ---------------------------------------------------------------------------
+
+@dataclass
+class StepResult:
+    tok: int          # drafted id (draft vocabulary), float32 decision
+    margin: float     # s64[tok] - max_{v != tok} s64[v]; 0 for an exact tie
+    runner_up: int    # lowest index attaining that max over v != tok
+    s: np.ndarray     # fp64 scores of the step
+
+
+def markov_scores(base_row, w1_bits, w2, prev: int) -> np.ndarray:
+    """Scores of one step: s[v] = base_row[v] + sum_j W2[v, j] * W1[prev, j].
+
+    [W7] "The fix": gather the markov_w1 row of the previous token, multiply
+    markov_w2 [V, r] by it, add the step's base-logit row. No scale,
+    temperature or nonlinearity appears on the page, so none is applied.
+    ``w2`` may be bf16 bits or an already decoded float64 array.
+    """
+    w1 = np.asarray(w1_bits)
+    V = w1.shape[0]
+    if not (0 <= prev < V):
+        raise ValueError(f"prev {prev} outside [0, {V})")
+    e = bf16_to_f64(w1[prev])
+    W2 = w2 if (isinstance(w2, np.ndarray) and w2.dtype == np.float64) else bf16_to_f64(w2)
+    b = np.asarray(base_row, dtype=np.float32).astype(np.float64)
+    _finite(b)
+    return b + W2 @ e
+
+
+def greedy_argmax(s64: np.ndarray) -> StepResult:
+    """Greedy pick with the lowest index winning ties ([W7] "The fix": the
+    device argmax and the host loop share that tie rule).
+
+    The decision is made on the scores rounded to float32; the reported
+    margin is measured on the exact fp64 scores.
+    """
+    s32 = s64.astype(np.float32)
+    tok = int(np.argmax(s32))  # numpy returns the first (lowest) index of the max
+    rest = s64.copy()
+    rest[tok] = -np.inf
+    runner = int(np.argmax(rest))
+    return StepResult(tok=tok, margin=float(s64[tok] - rest[runner]), runner_up=runner, s=s64)
+
+
+def markov_step(base_row, w1_bits, w2, prev: int) -> StepResult:
+    """One step of the loop from a given previous token."""
+    return greedy_argmax(markov_scores(base_row, w1_bits, w2, prev))
+
+
+def markov_sample(base, w1_bits, w2_bits, prev0, k: int, d2t=None) -> dict:
+    """The k-step loop for every request, in the order the pages give it.
+
+    [W7] "Measured" (the host loop: per step i of k, add the Markov bias to
+    row i and take the argmax) and "The fix" (gather -> GEMV -> add the
+    step's base row -> lowest-index argmax -> d2t -> prev stays the drafted
+    token). Readings:
+      * step i uses base row i of the request (k <= B);
+      * step 0 is biased by prev0, the request's last committed token given
+        in draft-vocabulary space;
+      * prev takes the draft-space token; only the emitted ids go through
+        d2t (identity when d2t is None), since W1 is indexed by draft ids;
+      * requests are independent and share the weights.
+
+    base: float32 [R, B, V]; w1, w2: bf16 bits [V, r]; prev0: int [R].
+    Returns dict(ids [R, k] int64, tok [R, k], margin [R, k] float64,
+    runner_up [R, k]).
+    """
+    base = np.asarray(base, dtype=np.float32)
+    R, B, V = base.shape
+    if not (1 <= k <= B):
+        raise ValueError("need 1 <= k <= B")
+    W2 = bf16_to_f64(w2_bits)
+    _finite(W2)
+    ids = np.empty((R, k), np.int64)
+    tok = np.empty((R, k), np.int64)
+    margin = np.empty((R, k), np.float64)
+    runner = np.empty((R, k), np.int64)
+    for req in range(R):
+        prev = int(prev0[req])
+        for i in range(k):
+            st = markov_step(base[req, i], w1_bits, W2, prev)
+            tok[req, i] = st.tok
+            margin[req, i] = st.margin
+            runner[req, i] = st.runner_up
+            ids[req, i] = st.tok if d2t is None else int(d2t[st.tok])
+            prev = st.tok
+    return dict(ids=ids, tok=tok, margin=margin, runner_up=runner)
+
+
+# ---------------------------------------------------------------------------
+# Confidence probe
+# ---------------------------------------------------------------------------
+
+def conf_probe(x, w_bits, bias: float, threshold: float):
+    """logit[m] = sum_t w[t] * x[m, t] + bias; pass[m] = logit[m] >= threshold.
+
+    [DS772] "Summary": the proposer's confidence probe is one wide dot product
+    on the drafted row's hidden state whose single scalar result gates how
+    many drafted tokens are proposed; "Performance": GPU and CPU evaluations
+    differ only by summation order. Reading: the gate compares the logit
+    itself with a logit-space threshold and keeps drafting when it is at
+    least the threshold (the page names no squashing function).
+    """
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    w = bf16_to_f64(w_bits)
+    _finite(x64, w)
+    logit = x64 @ w + float(np.float32(bias))
+    return logit, logit >= float(np.float32(threshold))
+
+
+# ---------------------------------------------------------------------------
+# One draft round
+# ---------------------------------------------------------------------------
+
+def draft_round(W_lm_bits, H, w1_bits, w2_bits, prev0, num_reqs: int, B: int, k: int,
+                probe_w_bits, probe_bias: float, probe_threshold: float, d2t=None) -> dict:
+    """lm_head -> Markov loop -> probe on every drafted row.
+
+    The base logits handed from the lm_head to the loop are float32 ([W7]
+    "Measured": nqpr x draft_vocab floats), so the fp64 lm_head result is
+    rounded once to float32 before the loop reads it.
+    """
+    base64 = lm_head(W_lm_bits, H)                      # [R*B, V]
+    V = base64.shape[1]
+    base32 = base64.astype(np.float32).reshape(num_reqs, B, V)
+    mk = markov_sample(base32, w1_bits, w2_bits, prev0, k, d2t)
+    logit, passed = conf_probe(H, probe_w_bits, probe_bias, probe_threshold)
+    return dict(base=base64, base32=base32, logit=logit, passed=passed, **mk)
