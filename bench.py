@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Draft-round benchmark of the DSpark hot path on one MI355X.
+
+One step = one draft round of the chosen head workload, every row of the hot
+path: lm_head GEMV over all drafted rows -> k-step on-device Markov loop ->
+confidence probe on every drafted row -> asynchronous copy of the drafted
+ids and probe logits into pinned host memory. Inputs are seeded synthetic
+tensors already resident in HBM when timing starts.
+
+Prints one JSON line (stdout). Progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config qwen3_8b_head]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft rounds/s + achieved HBM GB/s (% of peak), V=151936 r=256 B=7"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def round_bytes(cfg):
+    """Algorithmic HBM bytes of one round (each weight once per use; W2 once per step)."""
+    R, B, k, d, V, r = cfg["num_reqs"], cfg["B"], cfg["k"], cfg["d"], cfg["V"], cfg["r"]
+    rows = R * B
+    lm = V * d * 2 + rows * d * 4 + rows * V * 4
+    mk = k * (V * r * 2 + R * r * 2 + R * V * 4) + R * k * 8 + R * 8
+    pr = rows * d * 4 + d * 2 + rows * 8
+    return lm, mk, pr
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle, as it stands, timed on this host on a bounded sample
+    of one round of the same workload, scaled to rounds/s:
+      * lm_head on the first V/slices vocabulary rows (time x slices),
+      * the full k-step Markov loop over all V (base drawn from the seeded
+        generator: the loop's cost does not depend on the values),
+      * the probe on every drafted row.
+    Repeated until about `seconds` of CPU work has been spent."""
+    import numpy as np
+    import oracle
+    from gemv_markov_argmax_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    R, B, k, V, r = inp["num_reqs"], inp["B"], inp["k"], inp["V"], inp["r"]
+    slices = max(1, V // 16384)
+    rows = np.arange(V // slices)
+    base = synth.normal_f32(inp["seed"], synth.S_BASE, (R, B, V), 1.28)
+    t_lm, t_mk, t_pr, n = 0.0, 0.0, 0.0, 0
+    while True:
+        a = time.perf_counter()
+        oracle.gemv_rows(inp["W_lm"], inp["H"], rows)
+        b = time.perf_counter()
+        oracle.markov_sample(base, inp["w1"], inp["w2"], inp["prev0"], k)
+        c = time.perf_counter()
+        oracle.conf_probe(inp["H"], inp["probe_w"], float(inp["probe_bias"]), float(inp["probe_threshold"]))
+        d = time.perf_counter()
+        t_lm, t_mk, t_pr, n = t_lm + (b - a), t_mk + (c - b), t_pr + (d - c), n + 1
+        log(f"  oracle sample {n}: lm_head slice {b - a:.2f} s, markov {c - b:.2f} s, probe {d - c:.3f} s")
+        if t_lm + t_mk + t_pr >= seconds:
+            break
+    per_round = (t_lm * slices + t_mk + t_pr) / n
+    return dict(value=1.0 / per_round, unit="rounds/s", cores=int(cores), kind="oracle",
+                sample=(f"{n} x [lm_head on {len(rows)} of {V} vocab rows (scaled x{slices}) + full {k}-step "
+                        f"Markov loop over V={V} + probe on {R * B} rows] of the {inp['name']} workload; "
+                        f"fp64 numpy oracle, BLAS threads={cores}"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen3_8b_head",
+                    choices=["tiny", "qwen3_8b_head", "lane27b", "reduced_vocab_batched"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X and no multi-GPU "
+              "path is built (see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gemv_markov_argmax_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+    log(f"[bench] generating {args.config} inputs")
+    inp = synth.round_inputs(args.config)
+    R, B, k, d, V, r = (inp[x] for x in ("num_reqs", "B", "k", "d", "V", "r"))
+    rows = R * B
+
+    W = ops.bf16_from_bits(inp["W_lm"], dev)
+    H = torch.from_numpy(inp["H"]).to(dev)
+    w1 = ops.bf16_from_bits(inp["w1"], dev)
+    w2 = ops.bf16_from_bits(inp["w2"], dev)
+    prev0 = torch.from_numpy(inp["prev0"]).to(dev)
+    pw = ops.bf16_from_bits(inp["probe_w"], dev)
+    logits = torch.empty(rows, V, device=dev)
+    ids = torch.empty(R, k, dtype=torch.int64, device=dev)
+    ws = ops.markov_workspace(R, k, V, dev)
+    plog = torch.empty(rows, device=dev)
+    ppass = torch.empty(rows, dtype=torch.int32, device=dev)
+    ids_h = torch.empty(R, k, dtype=torch.int64, pin_memory=True)
+    plog_h = torch.empty(rows, pin_memory=True)
+    bias, thr = float(inp["probe_bias"]), float(inp["probe_threshold"])
+    torch.cuda.synchronize()
+
+    def one_round(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.lm_head(W, H, out=logits)
+        if ev is not None:
+            ev[1].record()
+        ops.markov_sample(logits.view(R, B, V), w1, w2, prev0, k, out=ids, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        ops.conf_probe(H, pw, bias, thr, logit_out=plog, pass_out=ppass)
+        if ev is not None:
+            ev[3].record()
+        ids_h.copy_(ids, non_blocking=True)
+        plog_h.copy_(plog, non_blocking=True)
+
+    log(f"[bench] warmup {args.warmup} rounds")
+    for _ in range(args.warmup):
+        one_round()
+    torch.cuda.synchronize()
+    first_ids = ids_h.numpy().copy()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} rounds")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_round(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    lm_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    mk_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pr_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    lm_avg = float(np.mean(lm_ms))
+    rounds_per_s = args.steps / elapsed
+    lm_b, mk_b, pr_b = round_bytes(inp)
+    lm_gbs = lm_b / (lm_avg * 1e-3) / 1e9
+    round_gbs = (lm_b + mk_b + pr_b) / elapsed * args.steps / 1e9
+    log(f"[bench] {rounds_per_s:.1f} rounds/s; lm_head {lm_avg * 1e3:.1f} us = {lm_gbs:.0f} GB/s; "
+        f"markov {np.mean(mk_ms) * 1e3:.1f} us; probe {np.mean(pr_ms) * 1e3:.1f} us")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the fp64 oracle on the host")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": rounds_per_s,
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.config, "num_reqs": R, "B": B, "k": k, "d": d, "V": V, "r": r},
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (gemv_kernel)", "achieved": lm_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3},
+        "round_hbm": {"achieved": round_gbs, "unit": "GB/s", "frac": round_gbs / HBM_PEAK_GBS,
+                      "algorithmic_bytes_per_round": lm_b + mk_b + pr_b},
+        "components_us": {"lm_head": lm_avg * 1e3, "markov_sample": float(np.mean(mk_ms)) * 1e3,
+                          "conf_probe": float(np.mean(pr_ms)) * 1e3},
+        "cpu_baseline": cpu,
+        "drafted_ids_round0": first_ids.tolist(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

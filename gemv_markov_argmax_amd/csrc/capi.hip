@@ -1,0 +1,105 @@
+// C ABI of libdspark: argument validation, then the launch.
+//
+// Every host-checkable precondition is tested before the first HIP call, so
+// an invalid call enqueues nothing and leaves the HIP state untouched.
+#include <mutex>
+
+#include "../../include/dspark.h"
+#include "dspark_internal.h"
+
+namespace dspark {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] > 0) return cached[dev];
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    cached[dev] = cus;
+  }
+  return cus;
+}
+
+}  // namespace dspark
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+dspark_status gemv_checks(const uint16_t* W, int N, int K, const float* X, int M, const float* Y) {
+  if (!W || !X || !Y) return DSPARK_ERR_NULL;
+  if (N < 1 || K < 8 || (K % 8) != 0 || M < 1) return DSPARK_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_string(dspark_status status) {
+  switch (status) {
+    case DSPARK_OK: return "DSPARK_OK";
+    case DSPARK_ERR_NULL: return "DSPARK_ERR_NULL: a required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "DSPARK_ERR_SHAPE: a size is out of range or inconsistent";
+    case DSPARK_ERR_ALIGN: return "DSPARK_ERR_ALIGN: a pointer lacks the required alignment";
+    case DSPARK_ERR_WORKSPACE: return "DSPARK_ERR_WORKSPACE: workspace missing or too small";
+    case DSPARK_ERR_HIP: return "DSPARK_ERR_HIP: the HIP runtime refused a call or launch";
+    default: return "DSPARK_ERR_UNKNOWN";
+  }
+}
+
+dspark_status dspark_proj_smallm(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
+                                 void* stream) {
+  const dspark_status st = gemv_checks(W, N, K, X, M, Y);
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv(W, N, K, X, M, Y, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H, int rows, float* logits,
+                             void* stream) {
+  const dspark_status st = gemv_checks(W_lm, V, d, H, rows, logits);
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv(W_lm, V, d, H, rows, logits, static_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V) {
+  return dspark::markov_workspace_bytes(num_reqs, k, V);
+}
+
+dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V, const uint16_t* w1,
+                                   const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0, int k,
+                                   int64_t* ids_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!base || !w1 || !w2 || !prev0 || !ids_out) return DSPARK_ERR_NULL;
+  if (num_reqs < 1 || num_reqs > 16 || B < 1 || V < 1 || k < 1 || k > B || r < 8 || r > 1024 || (r % 8) != 0)
+    return DSPARK_ERR_SHAPE;
+  if (!aligned(base, 4) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(prev0, 8) ||
+      !aligned(ids_out, 8) || (d2t && !aligned(d2t, 8)))
+    return DSPARK_ERR_ALIGN;
+  const size_t need = dspark::markov_workspace_bytes(num_reqs, k, V);
+  if (!workspace || workspace_bytes < need) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_markov(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_conf_probe(const float* x, int M, int D, const uint16_t* w, float bias, float threshold,
+                                float* logit_out, int32_t* pass_out, void* stream) {
+  if (!x || !w || !logit_out) return DSPARK_ERR_NULL;
+  if (M < 1 || D < 8 || (D % 8) != 0) return DSPARK_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(logit_out, 4) || (pass_out && !aligned(pass_out, 4)))
+    return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_probe(x, M, D, w, bias, threshold, logit_out, pass_out,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal helpers shared by the gfx950 kernels of libdspark.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// D = A(16x32) * B(32x16) + C on bf16 operands, fp32 accumulate.
+// Lane l supplies A[l % 16][8*(l/16) + j] and B[8*(l/16) + j][l % 16]
+// (j = 0..7, element j of the 8-wide vector); it receives
+// D[4*(l/16) + v][l % 16] in component v. The k index inside a block is
+// only ever used to pair A with B, so any fixed bijection works as long as
+// both operands use the same one.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Streaming (read-once) 16-byte load: non-temporal hint so a weight stream
+// does not evict data that is reused.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Round a finite float to bf16, nearest-even, returning the 16-bit pattern.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Order-preserving 64-bit key of (score, index): a larger key means a larger
+// score, and for equal scores a smaller index. The maximum key over a set is
+// therefore the greedy pick with the lowest index winning ties, whatever the
+// order in which keys are combined. +0 and -0 map to the same key.
+__device__ __forceinline__ uint64_t score_key(float s, uint32_t idx) {
+  uint32_t u = __float_as_uint(s);
+  if (s == 0.0f) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint64_t>(~idx);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+  return ~static_cast<uint32_t>(key);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (defined next to their kernels).
+// ---------------------------------------------------------------------------
+
+// Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
+hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
+                       hipStream_t stream);
+
+// Markov loop; see dspark_markov_sample.
+size_t markov_workspace_bytes(int num_reqs, int k, int V);
+hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
+                         const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
+                         int k, int64_t* ids, void* workspace, hipStream_t stream);
+
+hipError_t launch_probe(const float* x, int M, int D, const uint16_t* w, float bias,
+                        float threshold, float* logit, int32_t* pass, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace dspark

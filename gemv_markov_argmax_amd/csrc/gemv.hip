@@ -1,0 +1,349 @@
+// Weight-stationary small-M GEMV on gfx950 matrix cores.
+//
+// Y[m, n] = sum_t X[m, t] * W[n, t], W bf16 [N, K], X fp32 [M, K], Y fp32.
+//
+// SharpInference #441 ("Observation", "Proposed work") describes the draft's
+// projections and lm_head as tall-skinny products with M = B ~ 7 drafted
+// rows, whose cost is reading each weight once; its proposal is a
+// weight-stationary matvec that reads every weight row once for all rows.
+//
+// Design on gfx950:
+//  * The weights stream from HBM exactly once, 16 bytes per lane per load,
+//    straight into the B operand of v_mfma_f32_16x16x32_bf16: lane l loads
+//    8 consecutive bf16 of weight row (16*tile + l%16), so one instruction
+//    covers 16 rows x 64 contiguous bytes and no repacking is needed.
+//  * The activations are fp32. Each is split exactly into two bf16 terms,
+//    x = hi + lo + O(2^-17 |x|), and both terms enter the A operand, so the
+//    product keeps ~16 bits of the activation against the bf16 weight and
+//    accumulates in fp32. For M <= 8 the hi and lo rows share one 16-row A
+//    block (rows 0..7 hi, 8..15 lo): one MFMA per 1 KB of weights.
+//    The A fragments of a K-chunk sit in LDS, built once per chunk by the
+//    whole workgroup.
+//  * With M <= 16 the MFMA work per weight byte is tiny (an MFMA per KB),
+//    so the kernel is bound by HBM: the design goal is bytes in flight.
+//    Each wave keeps two stages of 8 outstanding 16-byte loads per lane.
+//  * Work split: 16-row tiles are dealt to workgroups in contiguous ranges.
+//    When there are few tiles (small N), a tile's K range is split over S
+//    waves of one workgroup in 64-element granules (granule q goes to
+//    segment q mod S) and the S partial tiles are added in LDS in a fixed
+//    order. The summation order of an output depends on (K, S) only, never
+//    on M or on the tile's position, so equal weight rows give bit-equal
+//    outputs and a row's result does not depend on the other rows.
+#include "dspark_internal.h"
+
+#include <algorithm>
+
+namespace dspark {
+namespace {
+
+struct GemvParams {
+  const uint16_t* W;
+  const float* X;
+  float* Y;
+  int N, K, M;   // M rows in this launch
+  int ldy;       // row stride of Y
+  int S;         // K segments per tile
+  int KG;        // 64-element granules in K
+  int KGC;       // granules per LDS chunk
+  int tiles;     // ceil(N / 16)
+};
+
+template <int NA, bool PACK, int NW, int TB>
+__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvParams p) {
+  constexpr int F = PACK ? 1 : 2 * NA;           // A fragments per k-block (= accumulators per tile)
+  constexpr int GU = TB >= 4 ? 1 : 4 / TB;       // granules per pipeline stage
+  extern __shared__ __align__(16) unsigned char smem[];
+  u32x4* Alds = reinterpret_cast<u32x4*>(smem);  // [KGC*2][F][64]
+  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(p.KGC) * 2 * F * kWave * 16);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int S = p.S, P = NW / S, pw = w / S, s = w - pw * S;
+  const int N = p.N, K = p.K, M = p.M, KGC = p.KGC, KG = p.KG;
+  const int nchunks = (KG + KGC - 1) / KGC;
+
+  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
+  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
+  const int per_round = P * TB;
+  const int rounds = (t1 - t0 + per_round - 1) / per_round;
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    int tile[TB];
+    bool tvalid[TB];
+    const uint16_t* wrow[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      tile[tb] = t0 + (rd * P + pw) * TB + tb;
+      tvalid[tb] = tile[tb] < t1;
+      const int row = min(tile[tb] * 16 + i, N - 1);  // out-of-range rows read a valid row, never stored
+      wrow[tb] = p.W + static_cast<size_t>(row) * K + 8 * g;
+    }
+    f32x4 acc[TB][F];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[tb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = 0; c < nchunks; ++c) {
+      const int q0 = c * KGC, q1 = min(KG, q0 + KGC);
+      if (nchunks > 1 || rd == 0) {
+        if (!(rd == 0 && c == 0)) __syncthreads();  // previous chunk fully consumed
+        // Build the A fragments of granules [q0, q1): entry e = (kbl*F + f)*64 + lane.
+        const int nent = (q1 - q0) * 2 * F * kWave;
+        for (int e = tid; e < nent; e += NW * kWave) {
+          const int ln = e & 63, fk = e >> 6, f = fk % F, kbl = fk / F;
+          const int ii = ln & 15, gg = ln >> 4;
+          const int k = (q0 * 2 + kbl) * 32 + 8 * gg;
+          int m, half;
+          if (PACK) {
+            m = ii & 7;
+            half = ii >> 3;
+          } else {
+            m = 16 * (f >> 1) + ii;
+            half = f & 1;
+          }
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (m < M && k < K) {
+            const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
+            const float4 x0 = xp[0], x1 = xp[1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t hb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t h = bf16_bits_rne(xs[j]);
+              hb[j] = half ? bf16_bits_rne(xs[j] - bf16_bits_to_f32(h)) : h;
+            }
+            v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                      hb[6] | (hb[7] << 16)};
+          }
+          Alds[e] = v;
+        }
+        __syncthreads();
+      }
+
+      // This wave's granules of the chunk: q = qs + j*S, j < nq.
+      const int qs = q0 + ((s - q0 % S) % S + S) % S;
+      const int nq = qs < q1 ? (q1 - qs + S - 1) / S : 0;
+
+      auto load_stage = [&](u32x4 (&buf)[GU][TB][2], int j0) {
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+          const int j = j0 + u;
+          const int q = qs + j * S;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int kk = (2 * q + h) * 32;
+            const bool ok = (j < nq) && (kk + 8 * g < K);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+              buf[u][tb][h] = ok ? load16_stream(wrow[tb] + kk) : u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      };
+      auto compute_stage = [&](u32x4 (&buf)[GU][TB][2], int j0) {
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+          const int j = j0 + u;
+          if (j < nq) {
+            const int ql = qs + j * S - q0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+              for (int f = 0; f < F; ++f) {
+                const u32x4 av = Alds[((ql * 2 + h) * F + f) * kWave + lane];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) acc[tb][f] = mfma_16x16x32(av, buf[u][tb][h], acc[tb][f]);
+              }
+            }
+          }
+        }
+      };
+
+      u32x4 bufA[GU][TB][2], bufB[GU][TB][2];
+      load_stage(bufA, 0);
+      for (int j0 = 0; j0 < nq; j0 += 2 * GU) {
+        load_stage(bufB, j0 + GU);
+        compute_stage(bufA, j0);
+        load_stage(bufA, j0 + 2 * GU);
+        compute_stage(bufB, j0 + GU);
+      }
+    }
+
+    // ---- epilogue: y = (sum of hi products) + (sum of lo products)
+    if (S == 1) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (!tvalid[tb]) continue;
+        const int n = tile[tb] * 16 + i;
+        if (PACK) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float lo = __shfl_down(acc[tb][0][v], 32);
+            const int m = 4 * g + v;
+            if (g < 2 && m < M && n < N) p.Y[static_cast<size_t>(m) * p.ldy + n] = acc[tb][0][v] + lo;
+          }
+        } else {
+#pragma unroll
+          for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int m = 16 * a + 4 * g + v;
+              if (m < M && n < N)
+                p.Y[static_cast<size_t>(m) * p.ldy + n] = acc[tb][2 * a][v] + acc[tb][2 * a + 1][v];
+            }
+        }
+      }
+    } else {
+      // Partial tiles of the S segments -> LDS, then a fixed-order sum.
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int f = 0; f < F; ++f)
+          reinterpret_cast<f32x4*>(red)[((w * TB + tb) * F + f) * kWave + lane] = acc[tb][f];
+      __syncthreads();
+      constexpr int ROWS = PACK ? 8 : 16 * NA;
+      const int items = P * TB * ROWS * 16;
+      for (int it = tid; it < items; it += NW * kWave) {
+        const int col = it & 15;
+        const int rest = it >> 4;
+        const int m = rest % ROWS;
+        const int tb = (rest / ROWS) % TB;
+        const int pp = rest / (ROWS * TB);
+        const int t = t0 + (rd * P + pp) * TB + tb;
+        const int n = t * 16 + col;
+        if (t >= t1 || m >= M || n >= N) continue;
+        int fh, fl, rh, rl;
+        if (PACK) {
+          fh = fl = 0;
+          rh = m;
+          rl = m + 8;
+        } else {
+          fh = 2 * (m >> 4);
+          fl = fh + 1;
+          rh = rl = m & 15;
+        }
+        float hi = 0.f, lo = 0.f;
+        for (int ss = 0; ss < S; ++ss) {
+          const int wv = pp * S + ss;
+          hi += red[(((wv * TB + tb) * F + fh) * kWave + 16 * (rh >> 2) + col) * 4 + (rh & 3)];
+          lo += red[(((wv * TB + tb) * F + fl) * kWave + 16 * (rl >> 2) + col) * 4 + (rl & 3)];
+        }
+        p.Y[static_cast<size_t>(m) * p.ldy + n] = hi + lo;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+struct Plan {
+  int NA;
+  bool pack;
+  int NW;
+  int TB;
+  int S;
+  int KGC;
+  int grid;
+  size_t lds;
+};
+
+constexpr size_t kLdsBytes = 160 * 1024;
+
+Plan make_plan(int M, int N, int K, int cus) {
+  Plan pl{};
+  if (M <= 8) {
+    pl.NA = 1, pl.pack = true, pl.NW = 16;
+  } else if (M <= 16) {
+    pl.NA = 1, pl.pack = false, pl.NW = 16;
+  } else {
+    pl.NA = (M + 15) / 16, pl.pack = false, pl.NW = 8;
+  }
+  const int F = pl.pack ? 1 : 2 * pl.NA;
+  const int tiles = (N + 15) / 16, KG = (K + 63) / 64;
+  const int cap = cus * pl.NW;
+  int S = 1;
+  if (2 * tiles < cap)
+    while (S < pl.NW && S < KG && tiles * S < cap) S *= 2;
+  pl.S = S;
+  const int P = pl.NW / S;
+  const size_t gran = static_cast<size_t>(2) * F * kWave * 16;
+  const size_t red1 = S > 1 ? static_cast<size_t>(pl.NW) * F * kWave * 16 : 0;
+  if (static_cast<size_t>(KG) * gran + red1 <= kLdsBytes) {
+    pl.TB = 1;
+    pl.KGC = KG;
+    pl.grid = std::min(cus, (tiles + P - 1) / P);
+    pl.lds = KG * gran + red1;
+    return pl;
+  }
+  const int tbmax = F <= 2 ? 4 : 1;
+  int tb = (tiles + P * cus - 1) / (P * cus);
+  tb = tb <= 1 ? 1 : (tb <= 2 ? 2 : 4);
+  pl.TB = std::min(tb, tbmax);
+  const size_t red = S > 1 ? static_cast<size_t>(pl.NW) * pl.TB * F * kWave * 16 : 0;
+  pl.KGC = std::max<int>(1, static_cast<int>((kLdsBytes - red) / gran));
+  pl.grid = (tiles + P * pl.TB - 1) / (P * pl.TB);
+  pl.lds = pl.KGC * gran + red;
+  return pl;
+}
+
+template <int NA, bool PACK, int NW, int TB>
+hipError_t launch_inst(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<NA, PACK, NW, TB>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (attr != hipSuccess) return attr;
+  GemvParams a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(pl.grid), dim3(NW * kWave), args, pl.lds, st);
+}
+
+hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  if (pl.NA == 1) {
+    if (pl.pack) {
+      if (pl.TB == 1) return launch_inst<1, true, 16, 1>(prm, pl, st);
+      if (pl.TB == 2) return launch_inst<1, true, 16, 2>(prm, pl, st);
+      return launch_inst<1, true, 16, 4>(prm, pl, st);
+    }
+    if (pl.TB == 1) return launch_inst<1, false, 16, 1>(prm, pl, st);
+    if (pl.TB == 2) return launch_inst<1, false, 16, 2>(prm, pl, st);
+    return launch_inst<1, false, 16, 4>(prm, pl, st);
+  }
+  switch (pl.NA) {
+    case 2: return launch_inst<2, false, 8, 1>(prm, pl, st);
+    case 3: return launch_inst<3, false, 8, 1>(prm, pl, st);
+    case 4: return launch_inst<4, false, 8, 1>(prm, pl, st);
+    case 5: return launch_inst<5, false, 8, 1>(prm, pl, st);
+    case 6: return launch_inst<6, false, 8, 1>(prm, pl, st);
+    case 7: return launch_inst<7, false, 8, 1>(prm, pl, st);
+    default: return launch_inst<8, false, 8, 1>(prm, pl, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
+                       hipStream_t stream) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorNoDevice;
+  constexpr int kMaxRows = 128;  // 8 row groups of 16 per launch
+  for (int m0 = 0; m0 < M; m0 += kMaxRows) {
+    const int mc = std::min(kMaxRows, M - m0);
+    const Plan pl = make_plan(mc, N, K, cus);
+    GemvParams prm{};
+    prm.W = W;
+    prm.X = X + static_cast<size_t>(m0) * K;
+    prm.Y = Y + static_cast<size_t>(m0) * N;
+    prm.N = N;
+    prm.K = K;
+    prm.M = mc;
+    prm.ldy = N;
+    prm.S = pl.S;
+    prm.KG = (K + 63) / 64;
+    prm.KGC = pl.KGC;
+    prm.tiles = (N + 15) / 16;
+    const hipError_t e = dispatch(prm, pl, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dspark

@@ -1,0 +1,178 @@
+"""Thin ctypes binding of libdspark.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels on the tensors' device;
+PyTorch only supplies device memory and the current stream. There is no CPU
+fallback: CPU tensors, wrong dtypes and a missing library raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "dspark_status_string": (ctypes.c_char_p, [_i]),
+    "dspark_proj_smallm": (_i, [_p, _i, _i, _p, _i, _p, _p]),
+    "dspark_lm_head": (_i, [_p, _i, _i, _p, _i, _p, _p]),
+    "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
+    "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
+    "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
+}
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdspark.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gemv_markov_argmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().dspark_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsparkError(status, status_string(status))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    return t
+
+
+def _gemv(entry, W, X, out):
+    _dev(W, torch.bfloat16, "W", 2)
+    _dev(X, torch.float32, "X", 2)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError(f"X has {X.shape[1]} columns, W has {K}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=W.device)
+    _dev(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check(entry(W.data_ptr(), N, K, X.data_ptr(), M, out.data_ptr(), _stream(W)))
+    return out
+
+
+def proj_smallm(W: torch.Tensor, X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X @ W^T for bf16 W [N, K] and fp32 X [M, K] (dspark_proj_smallm)."""
+    return _gemv(lib().dspark_proj_smallm, W, X, out)
+
+
+def lm_head(W_lm: torch.Tensor, H: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Base logits [rows, V] = H @ W_lm^T (dspark_lm_head)."""
+    return _gemv(lib().dspark_lm_head, W_lm, H, out)
+
+
+def markov_workspace_bytes(num_reqs: int, k: int, V: int) -> int:
+    return int(lib().dspark_markov_workspace_bytes(num_reqs, k, V))
+
+
+def markov_workspace(num_reqs: int, k: int, V: int, device) -> torch.Tensor:
+    n = markov_workspace_bytes(num_reqs, k, V)
+    if n == 0:
+        raise ValueError("sizes out of range for the Markov loop")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor, k: int,
+                  d2t: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Drafted ids [R, k] int64 of the on-device Markov loop (dspark_markov_sample).
+
+    base fp32 [R, B, V]; w1, w2 bf16 [V, r]; prev0 int64 [R]; d2t int64 [V] or None.
+    """
+    _dev(base, torch.float32, "base", 3)
+    _dev(w1, torch.bfloat16, "w1", 2)
+    _dev(w2, torch.bfloat16, "w2", 2)
+    _dev(prev0, torch.int64, "prev0", 1)
+    R, B, V = base.shape
+    r = w1.shape[1]
+    if tuple(w1.shape) != (V, r) or tuple(w2.shape) != (V, r):
+        raise ValueError("w1 and w2 must both be [V, r]")
+    if prev0.shape[0] != R:
+        raise ValueError("prev0 must have num_reqs entries")
+    d2t_ptr = None
+    if d2t is not None:
+        _dev(d2t, torch.int64, "d2t", 1)
+        if d2t.shape[0] != V:
+            raise ValueError("d2t must have V entries")
+        d2t_ptr = d2t.data_ptr()
+    if out is None:
+        out = torch.empty((R, k), dtype=torch.int64, device=base.device)
+    _dev(out, torch.int64, "out", 2)
+    if workspace is None:
+        workspace = markov_workspace(R, k, V, base.device)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    _check(lib().dspark_markov_sample(base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr,
+                                      prev0.data_ptr(), k, out.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), _stream(base)))
+    return out
+
+
+def conf_probe(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, threshold: float = 0.0,
+               logit_out: torch.Tensor | None = None, pass_out: torch.Tensor | None = None,
+               want_pass: bool = True):
+    """(logit fp32 [M], pass int32 [M] or None) of the confidence probe (dspark_conf_probe)."""
+    _dev(x, torch.float32, "x", 2)
+    _dev(w, torch.bfloat16, "w", 1)
+    M, D = x.shape
+    if w.shape[0] != D:
+        raise ValueError("w must have D entries")
+    if logit_out is None:
+        logit_out = torch.empty(M, dtype=torch.float32, device=x.device)
+    _dev(logit_out, torch.float32, "logit_out", 1)
+    if pass_out is None and want_pass:
+        pass_out = torch.empty(M, dtype=torch.int32, device=x.device)
+    if pass_out is not None:
+        _dev(pass_out, torch.int32, "pass_out", 1)
+    _check(lib().dspark_conf_probe(x.data_ptr(), M, D, w.data_ptr(), float(bias), float(threshold),
+                                   logit_out.data_ptr(), None if pass_out is None else pass_out.data_ptr(),
+                                   _stream(x)))
+    return logit_out, pass_out
+
+
+def bf16_from_bits(bits, device) -> torch.Tensor:
+    """Upload numpy uint16 bf16 bit patterns as a torch.bfloat16 device tensor."""
+    import numpy as np
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)

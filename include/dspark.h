@@ -1,0 +1,165 @@
+/*
+ * dspark.h -- C ABI of the DSpark draft-round hot path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library implements, as hand-written HIP kernels, the three steps of a
+ * DSpark drafter round that sit between the draft backbone and the target's
+ * verify pass:
+ *   1. weight-stationary small-M GEMVs (draft projections, lm_head),
+ *   2. the k-step Markov-biased greedy sampling loop, entirely on device,
+ *   3. the confidence probe.
+ *
+ * Sources cited below (a reader has the pages themselves):
+ *   [DS772]  ds4 #772, "dspark: cut per-cycle CUDA overheads (single-draft
+ *            decode, GPU confidence probe)".
+ *   [SI441]  SharpInference #441, "perf(cuda): DSpark GPU draft round runs
+ *            ~3x the bandwidth floor - small-M (B=7) projection GEMMs ->
+ *            weight-stationary matvec (#428 lever 1)".
+ *   [W7]     vllm.cpp #436, "SPEC-DSPARK W7: the sequential Markov sample
+ *            loop is HOST-side - 28% of the draft step, 14.9 MB downloaded
+ *            per step".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The
+ *    library never allocates, frees or copies memory between host and device.
+ *  - Tensors are dense and row-major; there are no stride arguments.
+ *  - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Every call only enqueues work on that stream and returns; no call
+ *    synchronizes or reads device memory from the host, so every call may be
+ *    recorded into a HIP graph.
+ *  - Errors: a violated host-checkable precondition returns a nonzero status
+ *    BEFORE any HIP call is made and nothing is enqueued. A failed launch
+ *    returns DSPARK_ERR_HIP. Faults during execution surface at the caller's
+ *    next synchronization, as usual in HIP.
+ *  - Calls are stateless and reentrant. Calls that share a workspace must
+ *    not run concurrently.
+ *  - Results are deterministic: no floating-point atomics are used, and the
+ *    summation order of every output is fixed by the shapes alone.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int dspark_status;
+
+#define DSPARK_OK 0
+#define DSPARK_ERR_NULL 1      /* a required pointer is NULL                 */
+#define DSPARK_ERR_SHAPE 2     /* a size is out of range or inconsistent     */
+#define DSPARK_ERR_ALIGN 3     /* a pointer lacks the required alignment     */
+#define DSPARK_ERR_WORKSPACE 4 /* workspace missing or smaller than required */
+#define DSPARK_ERR_HIP 5       /* the HIP runtime refused a call or launch   */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* dspark_status_string(dspark_status status);
+
+/*
+ * dspark_proj_smallm -- one draft projection at small M.
+ *
+ * [SI441] "Observation" and "Proposed work": every projection of the draft
+ * block forward multiplies the B drafted positions' activations by one
+ * weight matrix; the weight-stationary form reads each weight row from HBM
+ * once and applies it to all M activation rows.
+ *
+ *   Y[m, n] = sum_{t < K} X[m, t] * W[n, t]      m < M, n < N
+ *
+ *   W  bf16 [N, K]  row n produces output column n    16-byte aligned
+ *   X  fp32 [M, K]  activations                        16-byte aligned
+ *   Y  fp32 [M, N]  output, overwritten                 4-byte aligned
+ * Sizes: N >= 1, K >= 8 and K % 8 == 0, M >= 1. The weight is streamed once
+ * per group of 128 rows of X. Accumulation is fp32; each fp32 activation is
+ * split exactly-to-2^-17 into two bf16 terms, so |error| stays far below
+ * 1e-3 + 1e-3 |Y| at every size in use.
+ */
+dspark_status dspark_proj_smallm(const uint16_t* W, int N, int K, const float* X, int M,
+                                 float* Y, void* stream);
+
+/*
+ * dspark_lm_head -- base logits of every drafted row.
+ *
+ * [W7] "Measured": the drafter's block forward produces nqpr x draft_vocab
+ * float32 logits per round (15 x 248320 on the 27B lane); [SI441]
+ * "Hypothesis": the lm_head is the last of the draft round's small-M GEMMs.
+ *
+ *   logits[m, v] = sum_{t < d} H[m, t] * W_lm[v, t]   m < rows, v < V
+ *
+ *   W_lm   bf16 [V, d]     16-byte aligned
+ *   H      fp32 [rows, d]  16-byte aligned (rows = num_reqs * B)
+ *   logits fp32 [rows, V]   4-byte aligned, overwritten
+ * Same kernel family, sizes, errors and accuracy as dspark_proj_smallm.
+ */
+dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H, int rows,
+                             float* logits, void* stream);
+
+/*
+ * Bytes of device workspace dspark_markov_sample needs for these sizes
+ * (0 when a size is out of range).
+ */
+size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V);
+
+/*
+ * dspark_markov_sample -- the k-step Markov-biased greedy loop on device.
+ *
+ * [W7] "The fix": for each step i the loop gathers markov_w1[prev], forms
+ * the bias as markov_w2 times that row, adds the step's base-logit row,
+ * takes the greedy argmax with the lowest index winning ties, maps the
+ * token through d2t and keeps prev on the device; only the final
+ * [num_reqs, k] ids are read back. "W7 LANDED": markov_w2 is
+ * [draft_vocab, markov_rank] bf16 and is re-read by every step.
+ *
+ * For each request q < num_reqs, with prev = prev0[q]:
+ *   for i < k:
+ *     s[v]      = base[q, i, v] + sum_{j < r} w2[v, j] * w1[prev, j]
+ *     tok       = min { v : s[v] == max_u s[u] }     (fp32 scores)
+ *     ids[q, i] = d2t ? d2t[tok] : tok
+ *     prev      = tok                                (draft vocabulary)
+ *
+ *   base      fp32  [num_reqs, B, V]   4-byte aligned
+ *   w1, w2    bf16  [V, r]            16-byte aligned
+ *   d2t       int64 [V] or NULL (identity); its entries are copied as given
+ *   prev0     int64 [num_reqs], draft-vocabulary ids
+ *   ids_out   int64 [num_reqs, k], overwritten
+ *   workspace >= dspark_markov_workspace_bytes(num_reqs, k, V) bytes,
+ *             8-byte aligned; contents undefined between calls
+ * Sizes: 1 <= num_reqs <= 16, 1 <= k <= B, V >= 1, 8 <= r <= 1024 with
+ * r % 8 == 0. A request whose prev0 lies outside [0, V) gets -1 in every
+ * entry of its ids row (a device-side check; nothing out of range is read).
+ */
+dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V,
+                                   const uint16_t* w1, const uint16_t* w2, int r,
+                                   const int64_t* d2t, const int64_t* prev0, int k,
+                                   int64_t* ids_out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * dspark_conf_probe -- the proposer's confidence probe.
+ *
+ * [DS772] "Summary": one small kernel computes the probe on the drafted
+ * row's hidden state and only a 4-byte scalar goes back to the host, which
+ * decides whether to keep drafting.
+ *
+ *   logit[m] = sum_{t < D} w[t] * x[m, t] + bias
+ *   pass[m]  = logit[m] >= threshold
+ *
+ *   x          fp32  [M, D]  16-byte aligned
+ *   w          bf16  [D]     16-byte aligned
+ *   logit_out  fp32  [M]      4-byte aligned
+ *   pass_out   int32 [M] or NULL
+ * Sizes: M >= 1, D >= 8 and D % 8 == 0. fp32 accumulation in a fixed order.
+ */
+dspark_status dspark_conf_probe(const float* x, int M, int D, const uint16_t* w, float bias,
+                                float threshold, float* logit_out, int32_t* pass_out,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemv_markov_argmax_amd import build as B
+
+HEADER = os.path.join(B.ROOT, "include", "dspark.h")
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(6)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if B.needs_build():
+        B.build()
+    from gemv_markov_argmax_amd import ops
+    return ops.lib()
+
+
+def declared():
+    code = open(HEADER).read()
+    code = re.sub(r"/\*.*?\*/", "", code, flags=re.S)
+    code = re.sub(r"//[^\n]*", "", code)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", code)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
+              "dspark_markov_workspace_bytes", "dspark_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings(L):
+    from gemv_markov_argmax_amd import ops
+    for code in range(6):
+        assert ops.status_string(code).startswith("DSPARK_")
+    assert "UNKNOWN" in ops.status_string(99)
+
+
+A = 0x10000      # 16-byte-aligned fake device addresses: never dereferenced,
+A2 = 0x20000     # every call below fails validation before any HIP call
+MIS = 0x10002
+
+
+def test_gemv_errors(L):
+    for fn in (L.dspark_proj_smallm, L.dspark_lm_head):
+        assert fn(None, 16, 64, A, 7, A2, None) == ERR_NULL
+        assert fn(A, 16, 64, None, 7, A2, None) == ERR_NULL
+        assert fn(A, 16, 64, A, 7, None, None) == ERR_NULL
+        assert fn(A, 0, 64, A, 7, A2, None) == ERR_SHAPE
+        assert fn(A, 16, 0, A, 7, A2, None) == ERR_SHAPE
+        assert fn(A, 16, 12, A, 7, A2, None) == ERR_SHAPE      # K % 8 != 0
+        assert fn(A, 16, 64, A, 0, A2, None) == ERR_SHAPE
+        assert fn(MIS, 16, 64, A, 7, A2, None) == ERR_ALIGN
+        assert fn(A, 16, 64, MIS, 7, A2, None) == ERR_ALIGN
+        assert fn(A, 16, 64, A, 7, A2 + 1, None) == ERR_ALIGN
+
+
+def test_markov_errors(L):
+    f = L.dspark_markov_sample
+    ws = L.dspark_markov_workspace_bytes(1, 7, 151936)
+    assert ws > 0
+    good = dict(base=A, R=1, B=7, V=151936, w1=A, w2=A2, r=256, d2t=None, prev0=A, k=7, ids=A2, ws=A, wsb=ws)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["base"], a["R"], a["B"], a["V"], a["w1"], a["w2"], a["r"], a["d2t"], a["prev0"], a["k"],
+                 a["ids"], a["ws"], a["wsb"], None)
+    assert call(base=None) == ERR_NULL
+    assert call(w1=None) == ERR_NULL
+    assert call(prev0=None) == ERR_NULL
+    assert call(ids=None) == ERR_NULL
+    assert call(R=0) == ERR_SHAPE
+    assert call(R=17) == ERR_SHAPE
+    assert call(k=8) == ERR_SHAPE          # k > B
+    assert call(k=0) == ERR_SHAPE
+    assert call(r=12) == ERR_SHAPE         # r % 8 != 0
+    assert call(r=2048) == ERR_SHAPE
+    assert call(V=0) == ERR_SHAPE
+    assert call(w1=MIS) == ERR_ALIGN
+    assert call(base=A + 2) == ERR_ALIGN
+    assert call(d2t=A + 4) == ERR_ALIGN
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+
+
+def test_markov_workspace_bytes(L):
+    f = L.dspark_markov_workspace_bytes
+    assert f(0, 7, 100) == 0 and f(17, 7, 100) == 0 and f(1, 0, 100) == 0 and f(1, 7, 0) == 0
+    assert f(8, 9, 32000) >= f(1, 9, 32000) > 0
+
+
+def test_probe_errors(L):
+    f = L.dspark_conf_probe
+    assert f(None, 7, 64, A, 0.0, 0.0, A2, None, None) == ERR_NULL
+    assert f(A, 7, 64, None, 0.0, 0.0, A2, None, None) == ERR_NULL
+    assert f(A, 7, 64, A, 0.0, 0.0, None, None, None) == ERR_NULL
+    assert f(A, 0, 64, A, 0.0, 0.0, A2, None, None) == ERR_SHAPE
+    assert f(A, 7, 60, A, 0.0, 0.0, A2, None, None) == ERR_SHAPE
+    assert f(MIS, 7, 64, A, 0.0, 0.0, A2, None, None) == ERR_ALIGN
+    assert f(A, 7, 64, A, 0.0, 0.0, A2, A2 + 2, None) == ERR_ALIGN
+
+
+def test_binding_has_no_cpu_path(L):
+    import torch
+    from gemv_markov_argmax_amd import ops
+    W = torch.zeros(16, 64, dtype=torch.bfloat16)
+    X = torch.zeros(7, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ops.proj_smallm(W, X)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ops.conf_probe(X, torch.zeros(64, dtype=torch.bfloat16))

@@ -1,0 +1,280 @@
+"""Parity of every C-ABI entry point with the fp64 oracle on an MI355X.
+
+Inputs come from the seeded generator; expected values only from the oracle.
+Each case prints its name, seed and shape before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gemv_markov_argmax_amd import synth
+from parity import check_markov, logits_close, probe_close, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gemv_markov_argmax_amd import ops
+    ops.lib()  # fail loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+def _ops():
+    from gemv_markov_argmax_amd import ops
+    return ops
+
+
+def _up(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _bf(bits, dev):
+    return _ops().bf16_from_bits(bits, dev)
+
+
+# ---------------------------------------------------------------------------
+# GEMV: projections and lm_head
+# ---------------------------------------------------------------------------
+
+GEMV_CASES = [
+    # (M, N, K): tiles, ragged N tails, K tails (K % 64 != 0), every row packing
+    (1, 1, 8), (4, 4096, 256), (7, 4096 + 8, 264), (7, 17, 4096), (8, 1000, 520),
+    (9, 333, 264), (15, 4096, 5120), (16, 2049, 1032), (17, 515, 264), (33, 1024, 512),
+    (72, 3203, 640), (130, 300, 136), (7, 4096, 7424), (3, 32000 + 3, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_CASES)
+@pytest.mark.parametrize("entry", ["proj_smallm", "lm_head"])
+def test_gemv_matches_oracle(dev, entry, M, N, K):
+    seed = 7000 + M * 31 + N + K
+    say(f"[gemv {entry}] M={M} N={N} K={K} seed={seed}")
+    W, X = synth.gemv_inputs(M, N, K, seed)
+    y = getattr(_ops(), entry)(_bf(W, dev), _up(X, dev))
+    torch.cuda.synchronize()
+    logits_close(y.cpu().numpy(), oracle.gemv(W, X), f"{entry} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("name", ["draft_layer"])
+def test_draft_layer_projections(dev, name):
+    inp = synth.layer_inputs()
+    for proj, Wb in inp["layers"][0].items():
+        X = inp["X"][proj]
+        say(f"[proj {proj}] W {Wb.shape} X {X.shape} seed={inp['seed']}")
+        y = _ops().proj_smallm(_bf(Wb, dev), _up(X, dev))
+        torch.cuda.synchronize()
+        logits_close(y.cpu().numpy(), oracle.gemv(Wb, X), f"proj {proj}")
+
+
+def test_lm_head_full_size_sampled(dev):
+    """Qwen3-8B-shaped head at full size in the benchmark's launch
+    configuration; oracle on sampled vocabulary rows incl. the ragged tail."""
+    cfg = synth.CONFIGS["qwen3_8b_head"]
+    V, d, rows = cfg["V"], cfg["d"], cfg["B"]
+    seed = synth.config_seed("qwen3_8b_head")
+    say(f"[lm_head full] V={V} d={d} rows={rows} seed={seed}")
+    W = synth.normal_bf16(seed, synth.S_W_LM, (V, d))
+    H = synth.normal_f32(seed, synth.S_H, (rows, d))
+    y = _ops().lm_head(_bf(W, dev), _up(H, dev)).cpu().numpy()
+    pick = np.unique(np.concatenate([np.arange(32), np.arange(V - 48, V),
+                                     np.random.default_rng(1).choice(V, 4000, replace=False)]))
+    logits_close(y[:, pick], oracle.gemv_rows(W, H, pick), "lm_head sampled")
+
+
+def test_gemv_invariants(dev):
+    """Deterministic reruns; a row's output independent of the other rows
+    (M = 1, 7, 15 give bit-identical rows); equal weight rows give equal
+    outputs wherever they sit."""
+    N, K = 9000, 4096
+    say(f"[gemv invariants] N={N} K={K}")
+    W, X = synth.gemv_inputs(15, N, K, 99)
+    W[5000] = W[17]
+    W[8999] = W[17]
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    y15a = _ops().lm_head(Wd, Xd)
+    y15b = _ops().lm_head(Wd, Xd)
+    y7 = _ops().lm_head(Wd, Xd[:7].contiguous())
+    y1 = _ops().lm_head(Wd, Xd[3:4].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y15a, y15b)
+    assert torch.equal(y7, y15a[:7])
+    assert torch.equal(y1[0], y15a[3])
+    assert torch.equal(y15a[:, 5000], y15a[:, 17]) and torch.equal(y15a[:, 8999], y15a[:, 17])
+
+
+# ---------------------------------------------------------------------------
+# Markov loop
+# ---------------------------------------------------------------------------
+
+MARKOV_CASES = [
+    # (R, B, k, V, r)
+    (1, 4, 4, 4096, 32), (1, 7, 7, 1, 8), (1, 3, 2, 5, 8), (2, 5, 5, 17, 16), (1, 7, 7, 20011, 256),
+    (3, 6, 4, 4099, 264), (8, 9, 9, 32000 + 7, 256), (16, 2, 2, 3001, 64), (5, 3, 3, 2000, 1024),
+    (1, 15, 15, 9000, 128),
+]
+
+
+@pytest.mark.parametrize("R,B,k,V,r", MARKOV_CASES)
+def test_markov_matches_oracle(dev, R, B, k, V, r):
+    seed = 500 + R * 7 + V + r
+    say(f"[markov] R={R} B={B} k={k} V={V} r={r} seed={seed}")
+    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, seed)
+    ids = _ops().markov_sample(_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k)
+    torch.cuda.synchronize()
+    check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
+
+
+def test_markov_d2t_and_sentinel(dev):
+    R, B, k, V, r = 4, 5, 5, 3000, 64
+    say(f"[markov d2t+sentinel] R={R} V={V} r={r}")
+    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, 77)
+    prev0[1] = V        # out of range -> -1 row
+    prev0[3] = -5
+    d2t = synth.d2t_map(V, 77)
+    ids = _ops().markov_sample(_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k, d2t=_up(d2t, dev))
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    assert np.all(ids[1] == -1) and np.all(ids[3] == -1)
+    check_markov(ids, base, w1, w2, prev0, k, d2t=d2t)
+
+
+@pytest.mark.parametrize("exact", [True, False])
+def test_markov_constructed_ties(dev, exact):
+    """27B-lane shape with 5% of base rows given a duplicated top value at two
+    indices; with exact=True markov_w2's rows are equal too, so the scores
+    tie exactly and the lower index must win."""
+    cfg = synth.CONFIGS["lane27b"]
+    R, B, V, r = cfg["num_reqs"], cfg["B"], cfg["V"], cfg["r"]
+    seed = synth.config_seed("lane27b")
+    say(f"[markov ties exact={exact}] V={V} r={r} B={B} seed={seed}")
+    base, w1, w2, prev0, ties = synth.markov_inputs(R, B, V, r, seed, tie_frac=0.05, tie_exact=exact)
+    ids = _ops().markov_sample(_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), B)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    if exact:
+        for (q, i, a, b) in ties:
+            assert ids[q, i] == a, f"tie row {i}: ids {ids[q, i]} expected lower index {a} of ({a}, {b})"
+    check_markov(ids, base, w1, w2, prev0, B)
+
+
+def test_markov_full_size_and_invariants(dev):
+    """Qwen3-8B head shape at full size: exact ids, deterministic reruns,
+    and batched requests equal to single-request runs."""
+    cfg = synth.CONFIGS["qwen3_8b_head"]
+    B, V, r = cfg["B"], cfg["V"], cfg["r"]
+    say(f"[markov full] V={V} r={r} B={B}")
+    base, w1, w2, prev0, _ = synth.markov_inputs(3, B, V, r, synth.config_seed("qwen3_8b_head"))
+    bd, w1d, w2d, pd = _up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev)
+    a = _ops().markov_sample(bd, w1d, w2d, pd, B)
+    b = _ops().markov_sample(bd, w1d, w2d, pd, B)
+    singles = [_ops().markov_sample(bd[q:q + 1].contiguous(), w1d, w2d, pd[q:q + 1].contiguous(), B) for q in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for q in range(3):
+        assert torch.equal(a[q], singles[q][0])
+    check_markov(a.cpu().numpy(), base, w1, w2, prev0, B)
+
+
+# ---------------------------------------------------------------------------
+# Probe
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,D", [(1, 8), (4, 256), (7, 4096), (15, 5120), (72, 5120), (7, 7424), (3, 7432)])
+def test_probe_matches_oracle(dev, M, D):
+    seed = 900 + M + D
+    say(f"[probe] M={M} D={D} seed={seed}")
+    x, w = synth.probe_inputs(M, D, seed)
+    logit, passed = _ops().conf_probe(_up(x, dev), _bf(w, dev), 0.25, 0.0)
+    torch.cuda.synchronize()
+    ref_l, ref_p = oracle.conf_probe(x, w, 0.25, 0.0)
+    probe_close(logit.cpu().numpy(), passed.cpu().numpy(), ref_l, ref_p, 0.0)
+
+
+def test_probe_threshold_boundary(dev):
+    """Logit exactly equal to the threshold passes (integer-valued data)."""
+    say("[probe boundary]")
+    x = np.zeros((3, 16), np.float32)
+    x[:, 0], x[:, 1] = 2.0, 2.0
+    w = np.zeros(16, np.float32)
+    w[0], w[1] = 1.0, -0.5
+    wb = synth.bf16_bits_rne(w)
+    logit, passed = _ops().conf_probe(_up(x, dev), _bf(wb, dev), 0.0, 1.0)
+    torch.cuda.synchronize()
+    assert np.all(logit.cpu().numpy() == 1.0) and np.all(passed.cpu().numpy() == 1)
+    logit, passed = _ops().conf_probe(_up(x, dev), _bf(wb, dev), -0.5, 1.0)
+    torch.cuda.synchronize()
+    assert np.all(passed.cpu().numpy() == 0)
+
+
+# ---------------------------------------------------------------------------
+# A whole round, chained, and under graph capture
+# ---------------------------------------------------------------------------
+
+def _round_tensors(name, dev):
+    inp = synth.round_inputs(name)
+    t = dict(W=_bf(inp["W_lm"], dev), H=_up(inp["H"], dev), w1=_bf(inp["w1"], dev), w2=_bf(inp["w2"], dev),
+             prev0=_up(inp["prev0"], dev), pw=_bf(inp["probe_w"], dev))
+    return inp, t
+
+
+def _run_round(inp, t, logits=None, ids=None, ws=None, lg=None, ps=None):
+    ops = _ops()
+    R, B, V = inp["num_reqs"], inp["B"], inp["V"]
+    logits = ops.lm_head(t["W"], t["H"], out=logits)
+    ids = ops.markov_sample(logits.view(R, B, V), t["w1"], t["w2"], t["prev0"], inp["k"], out=ids, workspace=ws)
+    lg, ps = ops.conf_probe(t["H"], t["pw"], float(inp["probe_bias"]), float(inp["probe_threshold"]),
+                            logit_out=lg, pass_out=ps)
+    return logits, ids, lg, ps
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head", "reduced_vocab_batched"])
+def test_round_chained(dev, name):
+    inp, t = _round_tensors(name, dev)
+    say(f"[round {name}] seed={inp['seed']}")
+    logits, ids, lg, ps = _run_round(inp, t)
+    torch.cuda.synchronize()
+    ref = oracle.draft_round(inp["W_lm"], inp["H"], inp["w1"], inp["w2"], inp["prev0"], inp["num_reqs"],
+                             inp["B"], inp["k"], inp["probe_w"], inp["probe_bias"], inp["probe_threshold"])
+    logits_close(logits.cpu().numpy(), ref["base"], f"round {name} logits")
+    # The GPU loop ran on the GPU's own fp32 logits; ids are compared against
+    # the oracle loop on the oracle's fp32 logits, with the near-tie rule.
+    check_markov(ids.cpu().numpy(), ref["base32"], inp["w1"], inp["w2"], inp["prev0"], inp["k"])
+    probe_close(lg.cpu().numpy(), ps.cpu().numpy(), ref["logit"], ref["passed"], float(inp["probe_threshold"]))
+
+
+def test_round_graph_replay(dev):
+    """The whole round recorded once in a HIP graph and replayed, with eager
+    work between replays: every replay equals the eager result."""
+    inp, t = _round_tensors("tiny", dev)
+    say("[round graph replay] tiny")
+    R, B, V, k = inp["num_reqs"], inp["B"], inp["V"], inp["k"]
+    ops = _ops()
+    logits = torch.empty(R * B, V, device=dev)
+    ids = torch.empty(R, k, dtype=torch.int64, device=dev)
+    ws = ops.markov_workspace(R, k, V, dev)
+    lg = torch.empty(R * B, device=dev)
+    ps = torch.empty(R * B, dtype=torch.int32, device=dev)
+    eager = [x.clone() for x in _run_round(inp, t, logits, ids, ws, lg, ps)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _run_round(inp, t, logits, ids, ws, lg, ps)  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _run_round(inp, t, logits, ids, ws, lg, ps)
+    for rep in range(4):
+        logits.fill_(7.0)
+        ids.fill_(-7)
+        lg.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((logits, ids, lg, ps), eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = ops.lm_head(t["W"], t["H"])  # eager work between replays
+        torch.cuda.synchronize()
