@@ -235,7 +235,122 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvParams p) {
   }
 }
 
+// Streaming variant for M <= 16 and K <= 64*16*GPW (F = 1) or 64*16*2 (F = 2):
+// every 16-row tile is split along K over S = min(16, KG) waves (P = 16/S
+// tiles side by side), so all waves of a workgroup do the same amount of work
+// on every tile. Each wave converts its own K slice of X into A fragments
+// once and keeps them in registers; LDS only holds the partial tiles, double
+// buffered, so one barrier per tile suffices. The weight loads of the next
+// two tiles are always in flight while a tile is being reduced.
+template <bool PACK, int GPW>
+__global__ __launch_bounds__(16 * kWave) void gemv_stream_kernel(GemvParams p) {
+  constexpr int NW = 16, F = PACK ? 1 : 2, KBW = 2 * GPW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [2][NW][F][64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int S = p.S, P = NW / S, pw = w / S, s = w - pw * S;
+  const int N = p.N, K = p.K, M = p.M, KG = p.KG;
+
+  // A fragments of this wave's granules q = s + S*j.
+  u32x4 afr[KBW][F];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = s + S * j;
+      const int k = (2 * q + h) * 32 + 8 * g;
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int m = PACK ? (i & 7) : i;
+        const int half = PACK ? (i >> 3) : f;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (q < KG && m < M && k < K) {
+          const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
+          const float4 x0 = xp[0], x1 = xp[1];
+          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          uint32_t hb[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t hv = bf16_bits_rne(xs[e]);
+            hb[e] = half ? bf16_bits_rne(xs[e] - bf16_bits_to_f32(hv)) : hv;
+          }
+          v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+        }
+        afr[2 * j + h][f] = v;
+      }
+    }
+
+  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
+  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
+  const int rounds = (t1 - t0 + P - 1) / P;
+
+  auto load = [&](u32x4 (&b)[KBW], int r) {
+    const int tile = t0 + r * P + pw;
+    const bool ok_t = r < rounds && tile < t1;
+    const int row = min(tile * 16 + i, N - 1);
+    const uint16_t* src = p.W + static_cast<size_t>(row) * K + 8 * g;
+#pragma unroll
+    for (int j = 0; j < GPW; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = s + S * j;
+        const int kk = (2 * q + h) * 32;
+        const bool ok = ok_t && q < KG && kk + 8 * g < K;
+        b[2 * j + h] = ok ? load16_stream(src + kk) : u32x4{0u, 0u, 0u, 0u};
+      }
+  };
+  auto compute_publish = [&](u32x4 (&b)[KBW], int buf) {
+    f32x4 acc[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = mfma_16x16x32(afr[kb][f], b[kb], acc[f]);
+#pragma unroll
+    for (int f = 0; f < F; ++f) red[((buf * NW + w) * F + f) * kWave + lane] = acc[f];
+  };
+  auto reduce_store = [&](int buf, int r) {
+    constexpr int ROWS = PACK ? 8 : 16;
+    const float* rf = reinterpret_cast<const float*>(red);
+    for (int it = tid; it < P * ROWS * 16; it += NW * kWave) {
+      const int col = it & 15, m = (it >> 4) % ROWS, pp = (it >> 4) / ROWS;
+      const int tile = t0 + r * P + pp;
+      const int n = tile * 16 + col;
+      if (tile >= t1 || m >= M || n >= N) continue;
+      const int fh = 0, fl = PACK ? 0 : 1, rh = m, rl = PACK ? m + 8 : m;
+      float hi = 0.f, lo = 0.f;
+      for (int ss = 0; ss < S; ++ss) {
+        const int wv = pp * S + ss;
+        hi += rf[(((buf * NW + wv) * F + fh) * kWave + 16 * (rh >> 2) + col) * 4 + (rh & 3)];
+        lo += rf[(((buf * NW + wv) * F + fl) * kWave + 16 * (rl >> 2) + col) * 4 + (rl & 3)];
+      }
+      p.Y[static_cast<size_t>(m) * p.ldy + n] = hi + lo;
+    }
+  };
+
+  u32x4 b0[KBW], b1[KBW];
+  load(b0, 0);
+  load(b1, 1);
+  for (int r = 0; r < rounds; r += 2) {
+    compute_publish(b0, 0);
+    load(b0, r + 2);
+    __syncthreads();
+    reduce_store(0, r);
+    if (r + 1 < rounds) {
+      compute_publish(b1, 1);
+      load(b1, r + 3);
+      __syncthreads();
+      reduce_store(1, r + 1);
+    }
+  }
+}
+
 struct Plan {
+  bool stream;  // gemv_stream_kernel
+  int GPW;      // granules per wave (stream variant)
   int NA;
   bool pack;
   int NW;
@@ -259,6 +374,22 @@ Plan make_plan(int M, int N, int K, int cus) {
   }
   const int F = pl.pack ? 1 : 2 * pl.NA;
   const int tiles = (N + 15) / 16, KG = (K + 63) / 64;
+  if (M <= 16) {
+    int S = 16;
+    while (S > KG) S >>= 1;
+    const int gpw = (KG + S - 1) / S;
+    if (gpw <= (pl.pack ? 4 : 2)) {
+      pl.stream = true;
+      pl.GPW = gpw;
+      pl.S = S;
+      pl.TB = 1;
+      pl.KGC = KG;
+      const int P = 16 / S;
+      pl.grid = std::max(1, std::min(cus, (tiles + P - 1) / P));
+      pl.lds = static_cast<size_t>(2) * 16 * F * kWave * 16;
+      return pl;
+    }
+  }
   const int cap = cus * pl.NW;
   int S = 1;
   if (2 * tiles < cap)
@@ -296,7 +427,27 @@ hipError_t launch_inst(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   return hipLaunchKernel(fn, dim3(pl.grid), dim3(NW * kWave), args, pl.lds, st);
 }
 
+template <bool PACK, int GPW>
+hipError_t launch_stream(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_stream_kernel<PACK, GPW>);
+  GemvParams a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
+}
+
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  if (pl.stream) {
+    if (pl.pack) {
+      switch (pl.GPW) {
+        case 1: return launch_stream<true, 1>(prm, pl, st);
+        case 2: return launch_stream<true, 2>(prm, pl, st);
+        case 3: return launch_stream<true, 3>(prm, pl, st);
+        default: return launch_stream<true, 4>(prm, pl, st);
+      }
+    }
+    if (pl.GPW == 1) return launch_stream<false, 1>(prm, pl, st);
+    return launch_stream<false, 2>(prm, pl, st);
+  }
   if (pl.NA == 1) {
     if (pl.pack) {
       if (pl.TB == 1) return launch_inst<1, true, 16, 1>(prm, pl, st);

@@ -5,24 +5,35 @@
 // step's base-logit row, takes the argmax with the lowest index winning
 // ties, maps it through d2t, and the previous token never leaves the device;
 // only the final [num_reqs, k] ids are read back. Section "W7 LANDED":
-// markov_w2 is [draft_vocab, markov_rank] bf16 and each step's bias GEMV
-// reads all of it, so a step costs one pass over markov_w2.
+// markov_w2 is [draft_vocab, markov_rank] bf16 and the bias GEMV of every
+// step covers all of it, which the page treats as an irreducible per-step
+// re-read.
 //
-// Design on gfx950 (one kernel per step, all on the caller's stream):
-//  * Step kernel: each workgroup owns a contiguous range of 16-row tiles of
-//    markov_w2. A wave streams a tile with 16-byte loads straight into the
-//    B operand of v_mfma_f32_16x16x32_bf16; the A operand holds the gathered
-//    markov_w1 rows of up to 16 requests (exact bf16, so no splitting is
-//    needed), giving bias[request][vocab] for a whole tile in r/32 MFMAs.
-//    The score add and a running (score, index) maximum are fused into the
-//    same pass; s never reaches memory.
-//  * Argmax: every candidate is packed into a 64-bit key whose unsigned
-//    order is (score, then lower index), so the reduction is a plain max:
-//    lanes, then waves through LDS, then one key per workgroup written to
-//    the workspace. No atomics; the result is independent of scheduling.
-//  * prev: the next step's kernel reduces the previous step's per-workgroup
-//    keys itself (a few KB from cache) while its first markov_w2 loads are
-//    already in flight. A last tiny kernel turns every step's keys into ids.
+// Design on gfx950: one persistent kernel runs all k steps.
+//  * Grid = one workgroup per compute unit, launched cooperatively so every
+//    workgroup is resident. Workgroup b owns a contiguous range of 16-row
+//    tiles of markov_w2 and loads it ONCE per call into on-chip storage:
+//    the first tiles stay in VGPRs (RT tiles per wave, already in MFMA
+//    B-operand layout), the next ones in LDS, and only what does not fit
+//    (very large vocabularies) is re-read from memory at each step. On
+//    MI355X the register files and LDS of 256 CUs hold ~168 MB, so the
+//    78 MB markov_w2 of a 151936 x 256 draft vocabulary is read from HBM
+//    once per call instead of once per step.
+//  * Per step, the A operand of v_mfma_f32_16x16x32_bf16 holds the gathered
+//    markov_w1 rows of up to 16 requests (exact bf16), so one tile's bias for
+//    every request is r/32 MFMAs; the base-row add and a running maximum of
+//    packed (score, index) keys are fused into the same pass. Keys order by
+//    score, then by lower index, so a plain max gives the greedy pick with
+//    the lowest index winning ties, independent of reduction order.
+//  * Steps are separated by a key exchange that doubles as the grid barrier:
+//    a small kernel first clears this call's key slots; every workgroup then
+//    publishes its best key per request into its own slot (a valid key is
+//    never zero) and polls the G slots of that step with coherent loads until
+//    all are present (bounded spin), taking their maximum as it goes. Every
+//    workgroup thus learns prev without a counter or a second round trip.
+//    Workgroup 0 writes the ids. The next step's base values are fetched
+//    before the exchange, so only the markov_w1 gather follows it.
+//  * No floating-point atomics anywhere; results do not depend on timing.
 #include "dspark_internal.h"
 
 #include <algorithm>
@@ -30,20 +41,27 @@
 namespace dspark {
 namespace {
 
-constexpr int kMarkovThreads = 256;           // 4 waves
-constexpr int kMarkovWaves = kMarkovThreads / kWave;
-constexpr int kMaxGroups = 1024;              // upper bound of the step grid
 constexpr int kMaxReqs = 16;
+constexpr int kMaxGroups = 256;          // grid cap: one workgroup per CU
+constexpr int kLoopWaves = 8;
+constexpr int kLoopThreads = kLoopWaves * kWave;
+constexpr size_t kCtlBytes = 256;          // watchdog flag
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr uint32_t kSpinLimit = 1u << 18;  // watchdog (~0.3 s of polling): far beyond any legitimate wait
 
 struct MarkovParams {
-  const float* base;       // [R, B, V]
-  const uint16_t* w1;      // [V, r]
-  const uint16_t* w2;      // [V, r]
-  const int64_t* prev0;    // [R]
-  const int64_t* d2t;      // [V] or null
-  int64_t* ids;            // [R, k]
-  uint64_t* part;          // [k][R][G] per-workgroup best keys
+  const float* base;     // [R, B, V]
+  const uint16_t* w1;    // [V, r]
+  const uint16_t* w2;    // [V, r]
+  const int64_t* prev0;  // [R]
+  const int64_t* d2t;    // [V] or null
+  int64_t* ids;          // [R, k]
+  uint32_t* ctl;         // [0] watchdog flag
+  uint64_t* part;        // [k][R][G] per-workgroup best keys, cleared per call
   int R, B, V, r, k, G, tiles;
+  int lds_tiles;         // markov_w2 tiles held in LDS per workgroup
+  int bstride;           // floats per request in the LDS base slice (>= 16 * tiles per workgroup)
+  int base_in_lds;       // 0: base values are read straight from memory (slice too large)
 };
 
 __device__ __forceinline__ bool prev0_ok(const MarkovParams& p, int m) {
@@ -51,158 +69,274 @@ __device__ __forceinline__ bool prev0_ok(const MarkovParams& p, int m) {
   return v >= 0 && v < p.V;
 }
 
-// Reduce the G per-workgroup keys of (step, request) with one wave.
-__device__ __forceinline__ uint64_t wave_reduce_keys(const uint64_t* keys, int G, int lane) {
-  uint64_t best = 0;
-  for (int j = lane; j < G; j += kWave) best = umax64(best, keys[j]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) best = umax64(best, __shfl_xor(best, off));
-  return best;
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int KBMAX>
-__global__ __launch_bounds__(kMarkovThreads) void markov_step_kernel(MarkovParams p, int step) {
-  __shared__ uint64_t red[kMarkovWaves][kMaxReqs];
-  __shared__ int prev_s[kMaxReqs];
+// Clears the watchdog flag and the key slots of this call (n slots).
+__global__ void markov_init_kernel(uint32_t* ctl, uint64_t* part, int n) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t == 0) ctl[0] = 0u;
+  for (int j = t; j < n; j += gridDim.x * blockDim.x) part[j] = 0ull;
+}
+
+constexpr int kMaxPoll = kMaxGroups / kWave;  // slots per lane when polling
+
+template <int KB, int RT>
+__global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams p) {
+  constexpr int NW = kLoopWaves;
+  extern __shared__ __align__(16) unsigned char smem[];
+  u32x4* w2l = reinterpret_cast<u32x4*>(smem);                                         // [lds_tiles][KB][64]
+  uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * 1024);  // [NW][16]
+  int* prev_s = reinterpret_cast<int*>(keys_s + NW * kMaxReqs);                           // [16]
+  float* basel = reinterpret_cast<float*>(prev_s + kMaxReqs);                             // [R][bstride]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
-  const int R = p.R, V = p.V, r = p.r;
-  const int KB = (r + 31) / 32;
+  const int R = p.R, V = p.V, r = p.r, G = p.G;
+  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / G);
+  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / G);
+  const int nt = t1 - t0;
+  const int nreg = min(nt, NW * RT);
+  const int nheld = nreg + min(nt - nreg, p.lds_tiles);
 
-  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
-  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
-
-  // First tile of this wave: issue its markov_w2 loads before resolving prev.
-  int t = t0 + w;
-  u32x4 bcur[KBMAX];
-  auto load_tile = [&](u32x4 (&b)[KBMAX], int tt) {
-    const int row = min(tt * 16 + i, V - 1);
-    const uint16_t* src = p.w2 + static_cast<size_t>(row) * r + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < KBMAX; ++kb) {
-      const bool ok = kb < KB && (kb * 32 + 8 * g) < r && tt < t1;
-      b[kb] = ok ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
+  auto w2_row = [&](int j, int lrow) {
+    const int row = min((t0 + j) * 16 + lrow, V - 1);
+    return p.w2 + static_cast<size_t>(row) * r;
   };
-  load_tile(bcur, t);
 
-  // prev of every request for this step.
-  for (int m = w; m < R; m += kMarkovWaves) {
-    int pv;
-    if (step == 0) {
-      pv = prev0_ok(p, m) ? static_cast<int>(p.prev0[m]) : 0;
-    } else {
-      const uint64_t key = wave_reduce_keys(p.part + (static_cast<size_t>(step - 1) * R + m) * p.G, p.G, lane);
-      pv = static_cast<int>(key_index(key));
-      if (pv < 0 || pv >= V) pv = 0;  // defensive: keys always hold an index < V
-    }
-    if (lane == 0) prev_s[m] = pv;
+  // ---- load this workgroup's markov_w2 tiles once: registers, then LDS
+  u32x4 wreg[RT > 0 ? RT : 1][KB];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const int j = w + NW * u;
+    const uint16_t* src = w2_row(j, i) + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      wreg[u][kb] = (j < nreg && kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
   }
-  __syncthreads();
-
-  // A operand: markov_w1[prev of request i], zero for absent requests.
-  u32x4 afr[KBMAX];
-  {
-    const bool live = i < R && prev0_ok(p, i < R ? i : 0);
-    const int pv = live ? prev_s[i] : 0;
-    const uint16_t* src = p.w1 + static_cast<size_t>(pv) * r + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < KBMAX; ++kb) {
-      const bool ok = live && kb < KB && (kb * 32 + 8 * g) < r;
-      afr[kb] = ok ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int e = tid; e < (nheld - nreg) * KB * kWave; e += kLoopThreads) {
+    const int ln = e & 63, kb = (e >> 6) % KB, jj = (e >> 6) / KB;
+    const int gg = ln >> 4;
+    w2l[e] = (kb * 32 + 8 * gg < r) ? load16(w2_row(nreg + jj, ln & 15) + kb * 32 + 8 * gg)
+                                    : u32x4{0u, 0u, 0u, 0u};
   }
+  if (tid < R) prev_s[tid] = prev0_ok(p, tid) ? static_cast<int>(p.prev0[tid]) : 0;
 
-  uint64_t best[4] = {0, 0, 0, 0};
-  const size_t row_stride = static_cast<size_t>(p.B) * V;
-  const float* base_step = p.base + static_cast<size_t>(step) * V;
-
-  auto score_tile = [&](u32x4 (&b)[KBMAX], int tt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bool bl = p.base_in_lds != 0;
+  const int nb = bl ? R * nt * 16 : 0;  // base values of this workgroup staged per step
+  constexpr int kPre = 4;               // prefetched base values per thread
+  float pre[kPre];
+  auto fetch_base = [&](int st) {
 #pragma unroll
-    for (int kb = 0; kb < KBMAX; ++kb)
-      if (kb < KB) acc = mfma_16x16x32(afr[kb], b[kb], acc);
-    const int n = tt * 16 + i;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g + v;
-      if (m < R && n < V) {
-        const float sc = base_step[m * row_stride + n] + acc[v];
-        best[v] = umax64(best[v], score_key(sc, static_cast<uint32_t>(n)));
+    for (int u = 0; u < kPre; ++u) {
+      const int e = tid + u * kLoopThreads;
+      pre[u] = 0.f;
+      if (e < nb) {
+        const int m = e / (nt * 16), nl = e - m * (nt * 16);
+        const int n = t0 * 16 + nl;
+        if (n < V) pre[u] = p.base[(static_cast<size_t>(m) * p.B + st) * V + n];
       }
     }
   };
-
-  u32x4 bnext[KBMAX];
-  for (; t < t1; t += 2 * kMarkovWaves) {
-    load_tile(bnext, t + kMarkovWaves);
-    score_tile(bcur, t);
-    if (t + kMarkovWaves >= t1) break;
-    load_tile(bcur, t + 2 * kMarkovWaves);
-    score_tile(bnext, t + kMarkovWaves);
-  }
-
-  // Lanes of one 16-lane group hold the same requests: reduce across them.
+  auto stage_base = [&](int st) {  // prefetched values, then any remainder straight from memory
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) best[v] = umax64(best[v], __shfl_xor(best[v], off));
-  if (i == 0)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[w][4 * g + v] = best[v];
-  __syncthreads();
-  if (tid < R) {
-    uint64_t k = red[0][tid];
-#pragma unroll
-    for (int ww = 1; ww < kMarkovWaves; ++ww) k = umax64(k, red[ww][tid]);
-    p.part[(static_cast<size_t>(step) * R + tid) * p.G + blockIdx.x] = k;
-  }
-}
-
-// One wave per (request, step): reduce the step's keys, map through d2t.
-__global__ __launch_bounds__(kWave) void markov_ids_kernel(MarkovParams p) {
-  const int m = blockIdx.x / p.k, step = blockIdx.x % p.k, lane = threadIdx.x;
-  const uint64_t key = wave_reduce_keys(p.part + (static_cast<size_t>(step) * p.R + m) * p.G, p.G, lane);
-  if (lane == 0) {
-    int64_t id = -1;
-    if (prev0_ok(p, m)) {
-      const int64_t tok = static_cast<int64_t>(key_index(key));
-      id = p.d2t ? p.d2t[tok] : tok;
+    for (int u = 0; u < kPre; ++u) {
+      const int e = tid + u * kLoopThreads;
+      if (e < nb) {
+        const int m = e / (nt * 16), nl = e - m * (nt * 16);
+        basel[m * p.bstride + nl] = pre[u];
+      }
     }
-    p.ids[static_cast<size_t>(m) * p.k + step] = id;
+    for (int e = tid + kPre * kLoopThreads; e < nb; e += kLoopThreads) {
+      const int m = e / (nt * 16), nl = e - m * (nt * 16);
+      const int n = t0 * 16 + nl;
+      basel[m * p.bstride + nl] = n < V ? p.base[(static_cast<size_t>(m) * p.B + st) * V + n] : 0.f;
+    }
+  };
+  fetch_base(0);
+
+  for (int step = 0; step < p.k; ++step) {
+    __syncthreads();  // prev_s written; the previous step is done with basel
+    stage_base(step);
+    // ---- A operand: markov_w1[prev] of request i (zero for absent or invalid requests)
+    u32x4 afr[KB];
+    {
+      const bool live = i < R && prev0_ok(p, i < R ? i : 0);
+      const uint16_t* src = p.w1 + static_cast<size_t>(live ? prev_s[i] : 0) * r + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        afr[kb] = (live && kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();  // basel ready
+
+    uint64_t best[4] = {0, 0, 0, 0};
+    auto score = [&](int j, f32x4 acc) {
+      const int n = (t0 + j) * 16 + i;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * g + v;
+        if (m < R && n < V) {
+          const float bv = bl ? basel[m * p.bstride + j * 16 + i]
+                              : p.base[(static_cast<size_t>(m) * p.B + step) * V + n];
+          best[v] = umax64(best[v], score_key(bv + acc[v], static_cast<uint32_t>(n)));
+        }
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int j = w + NW * u;
+      if (j < nreg) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(afr[kb], wreg[u][kb], acc);
+        score(j, acc);
+      }
+    }
+    for (int j = nreg + w; j < nt; j += NW) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (j < nheld) {
+        const u32x4* src = w2l + static_cast<size_t>(j - nreg) * KB * kWave + lane;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(afr[kb], src[kb * kWave], acc);
+      } else {
+        const uint16_t* src = w2_row(j, i) + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 b = (kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+          acc = mfma_16x16x32(afr[kb], b, acc);
+        }
+      }
+      score(j, acc);
+    }
+    const bool last = step == p.k - 1;
+    if (!last) fetch_base(step + 1);  // independent of this step's winner
+
+    // ---- workgroup maximum per request (lanes of a 16-lane group share requests 4g..4g+3)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v >= R) break;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) best[v] = umax64(best[v], __shfl_xor(best[v], off));
+    }
+    if (i == 0)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) keys_s[w * kMaxReqs + 4 * g + v] = best[v];
+    __syncthreads();
+
+    // ---- publish this workgroup's key of every request
+    if (tid < R) {
+      uint64_t kk = keys_s[tid];
+      for (int ww = 1; ww < NW; ++ww) kk = umax64(kk, keys_s[ww * kMaxReqs + tid]);
+      __hip_atomic_store(p.part + (static_cast<size_t>(step) * R + tid) * G + blockIdx.x, kk, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (last && blockIdx.x != 0) return;  // only workgroup 0 needs the final step's winner
+
+    // ---- exchange: poll the G slots of each request until all are published
+    for (int m = w; m < R; m += NW) {
+      const uint64_t* src = p.part + (static_cast<size_t>(step) * R + m) * G;
+      uint64_t kk = 0;
+      uint32_t spins = 0;
+      for (;;) {
+        uint64_t slot[kMaxPoll];
+        bool have = true;
+#pragma unroll
+        for (int u = 0; u < kMaxPoll; ++u) {
+          const int j = lane + u * kWave;
+          slot[u] = j < G ? load_coherent(src + j) : ~0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kMaxPoll; ++u) have = have && slot[u] != 0ull;
+        if (__all(have)) {
+#pragma unroll
+          for (int u = 0; u < kMaxPoll; ++u) {
+            const int j = lane + u * kWave;
+            if (j < G) kk = umax64(kk, slot[u]);
+          }
+          break;
+        }
+        if (++spins > kSpinLimit) {
+          if (lane == 0) __hip_atomic_store(p.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int u = 0; u < kMaxPoll; ++u) {
+            const int j = lane + u * kWave;
+            if (j < G) kk = umax64(kk, slot[u]);
+          }
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) kk = umax64(kk, __shfl_xor(kk, off));
+      if (lane == 0) {
+        int tok = static_cast<int>(key_index(kk));
+        if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
+        prev_s[m] = tok;
+        if (blockIdx.x == 0) {
+          int64_t id = -1;
+          if (prev0_ok(p, m)) id = p.d2t ? p.d2t[tok] : static_cast<int64_t>(tok);
+          if (__hip_atomic_load(p.ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) id = -2;
+          p.ids[static_cast<size_t>(m) * p.k + step] = id;
+        }
+      }
+    }
   }
 }
 
-int step_grid(int V) {
+struct LoopPlan {
+  int G, KB, RT, lds_tiles, bstride, base_in_lds;
+  size_t lds;
+};
+
+constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straight from memory
+
+int reg_tiles(int KB) { return KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0); }
+
+LoopPlan make_loop_plan(int R, int V, int r, int cus) {
+  LoopPlan pl{};
   const int tiles = (V + 15) / 16;
-  const int cus = device_cu_count();
-  int G = std::min((tiles + kMarkovWaves - 1) / kMarkovWaves, std::max(1, cus) * 4);
-  return std::max(1, std::min(G, kMaxGroups));
+  pl.G = std::max(1, std::min({cus, tiles, kMaxGroups}));
+  const int kb = (r + 31) / 32;
+  pl.KB = kb <= 1 ? 1 : kb <= 2 ? 2 : kb <= 4 ? 4 : kb <= 8 ? 8 : kb <= 16 ? 16 : 32;
+  pl.RT = reg_tiles(pl.KB);
+  const int ntmax = (tiles + pl.G - 1) / pl.G;
+  pl.bstride = ntmax * 16;
+  const size_t base_bytes = static_cast<size_t>(R) * pl.bstride * 4;
+  pl.base_in_lds = base_bytes <= kBaseLdsMax ? 1 : 0;
+  const size_t fixed = static_cast<size_t>(kLoopWaves) * kMaxReqs * 8 + kMaxReqs * 4 +
+                       (pl.base_in_lds ? base_bytes : 0);
+  const size_t tile_bytes = static_cast<size_t>(pl.KB) * 1024;
+  const int want = std::max(0, ntmax - kLoopWaves * pl.RT);
+  const int fit = fixed < kLdsBytes ? static_cast<int>((kLdsBytes - fixed) / tile_bytes) : 0;
+  pl.lds_tiles = std::min(want, fit);
+  pl.lds = pl.lds_tiles * tile_bytes + fixed;
+  return pl;
 }
 
-template <int KBMAX>
-hipError_t launch_steps(const MarkovParams& prm, hipStream_t st) {
-  for (int step = 0; step < prm.k; ++step) {
-    MarkovParams a = prm;
-    int sv = step;
-    void* args[] = {&a, &sv};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&markov_step_kernel<KBMAX>),
-                                         dim3(prm.G), dim3(kMarkovThreads), args, 0, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+template <int KB>
+hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, hipStream_t st) {
+  constexpr int RT = KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
+  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<KB, RT>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (attr != hipSuccess) return attr;
+  void* args[] = {&prm};
+  return hipLaunchCooperativeKernel(fn, dim3(pl.G), dim3(kLoopThreads), args, static_cast<unsigned>(pl.lds), st);
 }
 
 }  // namespace
 
 size_t markov_workspace_bytes(int num_reqs, int k, int V) {
   if (num_reqs < 1 || num_reqs > kMaxReqs || k < 1 || V < 1) return 0;
-  return static_cast<size_t>(k) * num_reqs * kMaxGroups * sizeof(uint64_t);
+  return kCtlBytes + static_cast<size_t>(k) * num_reqs * kMaxGroups * sizeof(uint64_t);
 }
 
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
                          int k, int64_t* ids, void* workspace, hipStream_t stream) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorNoDevice;
+  const LoopPlan pl = make_loop_plan(R, V, r, cus);
   MarkovParams prm{};
   prm.base = base;
   prm.w1 = w1;
@@ -210,26 +344,34 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.prev0 = prev0;
   prm.d2t = d2t;
   prm.ids = ids;
-  prm.part = static_cast<uint64_t*>(workspace);
+  prm.ctl = static_cast<uint32_t*>(workspace);
+  prm.part = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(workspace) + kCtlBytes);
   prm.R = R;
   prm.B = B;
   prm.V = V;
   prm.r = r;
   prm.k = k;
-  prm.G = step_grid(V);
+  prm.G = pl.G;
   prm.tiles = (V + 15) / 16;
-  const int KB = (r + 31) / 32;
-  hipError_t e;
-  if (KB <= 2) e = launch_steps<2>(prm, stream);
-  else if (KB <= 4) e = launch_steps<4>(prm, stream);
-  else if (KB <= 8) e = launch_steps<8>(prm, stream);
-  else if (KB <= 16) e = launch_steps<16>(prm, stream);
-  else e = launch_steps<32>(prm, stream);
-  if (e != hipSuccess) return e;
-  MarkovParams a = prm;
-  void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&markov_ids_kernel), dim3(R * k), dim3(kWave),
-                         args, 0, stream);
+  prm.lds_tiles = pl.lds_tiles;
+  prm.bstride = pl.bstride;
+  prm.base_in_lds = pl.base_in_lds;
+  {
+    int nslots = k * R * pl.G;
+    void* args[] = {&prm.ctl, &prm.part, &nslots};
+    const int blocks = std::max(1, std::min(64, (nslots + 255) / 256));
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&markov_init_kernel), dim3(blocks),
+                                         dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  switch (pl.KB) {
+    case 1: return launch_loop<1>(prm, pl, stream);
+    case 2: return launch_loop<2>(prm, pl, stream);
+    case 4: return launch_loop<4>(prm, pl, stream);
+    case 8: return launch_loop<8>(prm, pl, stream);
+    case 16: return launch_loop<16>(prm, pl, stream);
+    default: return launch_loop<32>(prm, pl, stream);
+  }
 }
 
 }  // namespace dspark

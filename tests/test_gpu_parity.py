@@ -86,25 +86,29 @@ def test_lm_head_full_size_sampled(dev):
     logits_close(y[:, pick], oracle.gemv_rows(W, H, pick), "lm_head sampled")
 
 
-def test_gemv_invariants(dev):
-    """Deterministic reruns; a row's output independent of the other rows
-    (M = 1, 7, 15 give bit-identical rows); equal weight rows give equal
-    outputs wherever they sit."""
-    N, K = 9000, 4096
+@pytest.mark.parametrize("N,K", [(9000, 4096), (151936, 4096), (4096, 12288), (248320, 5120)])
+def test_gemv_invariants(dev, N, K):
+    """Deterministic reruns; a row's output does not depend on the other rows
+    (bit-identical for every M within a row class: 1..8 and 9..16); equal
+    weight rows give equal outputs wherever they sit."""
     say(f"[gemv invariants] N={N} K={K}")
-    W, X = synth.gemv_inputs(15, N, K, 99)
-    W[5000] = W[17]
-    W[8999] = W[17]
+    W, X = synth.gemv_inputs(16, N, K, 99)
+    W[N // 2 + 5] = W[17]
+    W[N - 1] = W[17]
     Wd, Xd = _bf(W, dev), _up(X, dev)
-    y15a = _ops().lm_head(Wd, Xd)
-    y15b = _ops().lm_head(Wd, Xd)
-    y7 = _ops().lm_head(Wd, Xd[:7].contiguous())
-    y1 = _ops().lm_head(Wd, Xd[3:4].contiguous())
+    ops = _ops()
+    y8a, y8b = ops.lm_head(Wd, Xd[:8].contiguous()), ops.lm_head(Wd, Xd[:8].contiguous())
+    y7 = ops.lm_head(Wd, Xd[:7].contiguous())
+    y1 = ops.lm_head(Wd, Xd[3:4].contiguous())
+    y16 = ops.lm_head(Wd, Xd)
+    y9 = ops.lm_head(Wd, Xd[:9].contiguous())
     torch.cuda.synchronize()
-    assert torch.equal(y15a, y15b)
-    assert torch.equal(y7, y15a[:7])
-    assert torch.equal(y1[0], y15a[3])
-    assert torch.equal(y15a[:, 5000], y15a[:, 17]) and torch.equal(y15a[:, 8999], y15a[:, 17])
+    assert torch.equal(y8a, y8b)
+    assert torch.equal(y7, y8a[:7])
+    assert torch.equal(y1[0], y8a[3])
+    assert torch.equal(y9, y16[:9])
+    for y in (y8a, y16):
+        assert torch.equal(y[:, N // 2 + 5], y[:, 17]) and torch.equal(y[:, N - 1], y[:, 17])
 
 
 # ---------------------------------------------------------------------------
@@ -115,7 +119,7 @@ MARKOV_CASES = [
     # (R, B, k, V, r)
     (1, 4, 4, 4096, 32), (1, 7, 7, 1, 8), (1, 3, 2, 5, 8), (2, 5, 5, 17, 16), (1, 7, 7, 20011, 256),
     (3, 6, 4, 4099, 264), (8, 9, 9, 32000 + 7, 256), (16, 2, 2, 3001, 64), (5, 3, 3, 2000, 1024),
-    (1, 15, 15, 9000, 128),
+    (1, 15, 15, 9000, 128), (16, 3, 2, 300000, 32),
 ]
 
 
