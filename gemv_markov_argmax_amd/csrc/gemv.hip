@@ -348,7 +348,121 @@ __global__ __launch_bounds__(16 * kWave) void gemv_stream_kernel(GemvParams p) {
   }
 }
 
+// Transposing stream variant for M <= 8 and 1024 < K <= 4096: 16 waves,
+// KBW = 4 or 8 k-blocks of 32 per wave. Wave w owns the contiguous K
+// segment [32*KBW*w, 32*KBW*(w+1)) of every tile. Its weight loads are
+// contiguous runs (each instruction covers 16/KBW rows x 64*KBW bytes, i.e.
+// whole 128-byte lines), which the memory system serves noticeably faster
+// than the 16-rows x 64-bytes pattern of direct B-operand loads. The wave
+// transposes its segment through a private LDS area (rows padded by 16
+// bytes, so the row writes and the B-operand reads are both free of bank
+// conflicts) and runs the MFMAs from there. The 16 partial tiles are added
+// in LDS in wave order.
+template <int KBW>
+__global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) {
+  constexpr int NW = 16;
+  constexpr int SEG = 64 * KBW;                 // bytes of a row segment
+  constexpr int RS = SEG + 16;                  // padded LDS row stride
+  constexpr int LPR = SEG / 16;                 // lanes per row in a load instruction
+  constexpr int RPI = kWave / LPR;              // rows per load instruction
+  constexpr int NLD = 16 / RPI;                 // load instructions per tile
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* tr = smem;                                                         // [NW][16][RS]
+  f32x4* red = reinterpret_cast<f32x4*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [NW][64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int N = p.N, K = p.K, M = p.M;
+  const int kseg = 32 * KBW * w;  // first k of this wave's segment
+
+  // A fragments (rows 0..7: bf16 hi part of X, rows 8..15: lo part); k-block
+  // kb of the segment covers k = kseg + 32*kb + 8*g + (0..7).
+  u32x4 afr[KBW];
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) {
+    const int k = kseg + 32 * kb + 8 * g;
+    const int m = i & 7, half = i >> 3;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (m < M && k < K) {
+      const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
+      const float4 x0 = xp[0], x1 = xp[1];
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t hb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t hv = bf16_bits_rne(xs[e]);
+        hb[e] = half ? bf16_bits_rne(xs[e] - bf16_bits_to_f32(hv)) : hv;
+      }
+      v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+    }
+    afr[kb] = v;
+  }
+
+  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
+  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
+  const int rounds = t1 - t0;
+
+  // Load instruction q of a tile: row RPI*q + lane/LPR, bytes 16*(lane%LPR) of the segment.
+  const int lrow = lane / LPR, lchunk = lane % LPR;
+  const bool lk_ok = kseg + 8 * lchunk < K;
+  auto load = [&](u32x4 (&b)[NLD], int rr) {
+    const int row0 = (t0 + rr) * 16 + lrow;
+    const bool ok = rr < rounds && lk_ok;
+    const uint16_t* src = p.W + static_cast<size_t>(ok ? row0 : 0) * K + kseg + 8 * lchunk;
+    const size_t step = static_cast<size_t>(RPI) * K;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q)
+      b[q] = (ok && row0 + RPI * q < N) ? load16_stream(src + q * step) : u32x4{0u, 0u, 0u, 0u};
+  };
+  unsigned char* wtr = tr + w * 16 * RS;
+  unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;   // + RPI*q*RS
+  const unsigned char* rd_base = wtr + i * RS + 16 * g;    // + 64*kb
+  auto compute_publish = [&](u32x4 (&b)[NLD]) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb)
+      acc = mfma_16x16x32(afr[kb], *reinterpret_cast<const u32x4*>(rd_base + 64 * kb), acc);
+    red[w * kWave + lane] = acc;
+  };
+  auto reduce_store = [&](int rr) {
+    const float* rf = reinterpret_cast<const float*>(red);
+    if (tid < 128) {
+      const int col = tid & 15, m = tid >> 4;
+      const int n = (t0 + rr) * 16 + col;
+      if (m < M && n < N) {
+        float hi = 0.f, lo = 0.f;
+        for (int ww = 0; ww < NW; ++ww) {
+          hi += rf[(ww * kWave + 16 * (m >> 2) + col) * 4 + (m & 3)];
+          lo += rf[(ww * kWave + 16 * ((m + 8) >> 2) + col) * 4 + (m & 3)];
+        }
+        p.Y[static_cast<size_t>(m) * p.ldy + n] = hi + lo;
+      }
+    }
+  };
+
+  u32x4 b0[NLD], b1[NLD];
+  load(b0, 0);
+  load(b1, 1);
+  for (int rr = 0; rr < rounds; rr += 2) {
+    compute_publish(b0);
+    load(b0, rr + 2);
+    __syncthreads();
+    reduce_store(rr);
+    __syncthreads();
+    if (rr + 1 < rounds) {
+      compute_publish(b1);
+      load(b1, rr + 3);
+      __syncthreads();
+      reduce_store(rr + 1);
+      __syncthreads();
+    }
+  }
+}
+
 struct Plan {
+  int tkbw;     // gemv_tstream_kernel k-blocks per wave (0: not used)
   bool stream;  // gemv_stream_kernel
   int GPW;      // granules per wave (stream variant)
   int NA;
@@ -374,6 +488,15 @@ Plan make_plan(int M, int N, int K, int cus) {
   }
   const int F = pl.pack ? 1 : 2 * pl.NA;
   const int tiles = (N + 15) / 16, KG = (K + 63) / 64;
+  if (M <= 8 && K > 1024 && K <= 4096) {
+    pl.tkbw = K > 2048 ? 8 : 4;
+    pl.S = 16;
+    pl.TB = 1;
+    pl.KGC = KG;
+    pl.grid = std::max(1, std::min(cus, tiles));
+    pl.lds = static_cast<size_t>(16) * 16 * (64 * pl.tkbw + 16) + static_cast<size_t>(16) * kWave * 16;
+    return pl;
+  }
   if (M <= 16) {
     int S = 16;
     while (S > KG) S >>= 1;
@@ -435,7 +558,20 @@ hipError_t launch_stream(const GemvParams& prm, const Plan& pl, hipStream_t st) 
   return hipLaunchKernel(fn, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
 }
 
+template <int KBW>
+hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_tstream_kernel<KBW>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (attr != hipSuccess) return attr;
+  GemvParams a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
+}
+
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  if (pl.tkbw == 8) return launch_tstream<8>(prm, pl, st);
+  if (pl.tkbw == 4) return launch_tstream<4>(prm, pl, st);
   if (pl.stream) {
     if (pl.pack) {
       switch (pl.GPW) {

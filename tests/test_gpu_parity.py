@@ -46,6 +46,7 @@ GEMV_CASES = [
     (1, 1, 8), (4, 4096, 256), (7, 4096 + 8, 264), (7, 17, 4096), (8, 1000, 520),
     (9, 333, 264), (15, 4096, 5120), (16, 2049, 1032), (17, 515, 264), (33, 1024, 512),
     (72, 3203, 640), (130, 300, 136), (7, 4096, 7424), (3, 32000 + 3, 256),
+    (5, 1000, 1032), (8, 777, 3000), (2, 4099, 2048), (7, 16, 1096),
 ]
 
 
