@@ -161,14 +161,27 @@ def main():
     def pr():
         ops.conf_probe(H, pw, bias, thr, logit_out=plog, pass_out=ppass)
 
+    # The probe reads only the hidden states, so it runs on a second stream
+    # (default priority) beside the lm_head and the Markov loop; the round's
+    # single D2H copy waits for both.
+    main_stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    start_ev = torch.cuda.Event()
+    probe_done = torch.cuda.Event()
+
     def one_round(ev=None):
+        start_ev.record(main_stream)
+        side.wait_event(start_ev)
+        with torch.cuda.stream(side):
+            pr()
+            probe_done.record(side)
         if ev is not None:
-            ev[0].record()
+            ev[0].record(main_stream)
         lm()
         if ev is not None:
-            ev[1].record()
+            ev[1].record(main_stream)
         mk()
-        pr()
+        main_stream.wait_event(probe_done)
         out_host.copy_(out_dev, non_blocking=True)
 
     if args.copy_calibration_mib > 0:
@@ -186,14 +199,16 @@ def main():
     torch.cuda.synchronize()
     first_ids = out_host[: R * k * 8].view(torch.int64).view(R, k).numpy().copy()
 
-    # Timed region: K whole rounds; HIP events bracket each lm_head launch on
-    # the stream it runs on (the kernel the roofline entry is about).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # Timed region: K whole rounds. HIP events bracket the lm_head launch (the
+    # kernel the roofline entry is about) on the stream it runs on, in every
+    # EVERY-th round; an event record adds a few microseconds of idle time.
+    EVERY = 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(0, args.steps, EVERY)]
     log(f"[bench] timing {args.steps} rounds")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        one_round(evs[s])
+        one_round(evs[s // EVERY] if s % EVERY == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0

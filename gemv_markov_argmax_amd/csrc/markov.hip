@@ -10,8 +10,9 @@
 // re-read.
 //
 // Design on gfx950: one persistent kernel runs all k steps.
-//  * Grid = one workgroup per compute unit, launched cooperatively so every
-//    workgroup is resident. Workgroup b owns a contiguous range of 16-row
+//  * Grid = at most one workgroup per compute unit, and the host checks that
+//    the whole grid fits on the device at once, so every workgroup is
+//    resident (the steps exchange keys between all of them). Workgroup b owns a contiguous range of 16-row
 //    tiles of markov_w2 and loads it ONCE per call into on-chip storage:
 //    the first tiles stay in VGPRs (RT tiles per wave, already in MFMA
 //    B-operand layout), the next ones in LDS, and only what does not fit
@@ -314,14 +315,22 @@ LoopPlan make_loop_plan(int R, int V, int r, int cus) {
 }
 
 template <int KB>
-hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, hipStream_t st) {
+hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
   constexpr int RT = KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
   const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<KB, RT>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
+  // Every workgroup must be resident at once (the steps exchange keys). A
+  // cooperative launch would enforce that but costs ~17 us of extra launch
+  // latency on MI355X, so the same condition is checked here instead: the
+  // grid never exceeds one workgroup per CU times the per-CU occupancy.
+  int per_cu = 0;
+  const hipError_t oe = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kLoopThreads, pl.lds);
+  if (oe != hipSuccess) return oe;
+  if (per_cu < 1 || pl.G > per_cu * cus) return hipErrorCooperativeLaunchTooLarge;
   void* args[] = {&prm};
-  return hipLaunchCooperativeKernel(fn, dim3(pl.G), dim3(kLoopThreads), args, static_cast<unsigned>(pl.lds), st);
+  return hipLaunchKernel(fn, dim3(pl.G), dim3(kLoopThreads), args, pl.lds, st);
 }
 
 }  // namespace
@@ -365,12 +374,12 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
     if (e != hipSuccess) return e;
   }
   switch (pl.KB) {
-    case 1: return launch_loop<1>(prm, pl, stream);
-    case 2: return launch_loop<2>(prm, pl, stream);
-    case 4: return launch_loop<4>(prm, pl, stream);
-    case 8: return launch_loop<8>(prm, pl, stream);
-    case 16: return launch_loop<16>(prm, pl, stream);
-    default: return launch_loop<32>(prm, pl, stream);
+    case 1: return launch_loop<1>(prm, pl, cus, stream);
+    case 2: return launch_loop<2>(prm, pl, cus, stream);
+    case 4: return launch_loop<4>(prm, pl, cus, stream);
+    case 8: return launch_loop<8>(prm, pl, cus, stream);
+    case 16: return launch_loop<16>(prm, pl, cus, stream);
+    default: return launch_loop<32>(prm, pl, cus, stream);
   }
 }
 
