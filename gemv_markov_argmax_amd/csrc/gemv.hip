@@ -235,38 +235,120 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvParams p) {
   }
 }
 
-// Streaming variant for M <= 16 and K <= 64*16*GPW (F = 1) or 64*16*2 (F = 2):
-// every 16-row tile is split along K over S = min(16, KG) waves (P = 16/S
-// tiles side by side), so all waves of a workgroup do the same amount of work
-// on every tile. Each wave converts its own K slice of X into A fragments
-// once and keeps them in registers; LDS only holds the partial tiles, double
-// buffered, so one barrier per tile suffices. The weight loads of the next
-// two tiles are always in flight while a tile is being reduced.
-template <bool PACK, int GPW>
-__global__ __launch_bounds__(16 * kWave) void gemv_stream_kernel(GemvParams p) {
-  constexpr int NW = 16, F = PACK ? 1 : 2, KBW = 2 * GPW;
+// Streaming variant for M <= 16 (the small-M GEMVs of a draft round).
+//
+// Every 16-row tile is split along K over the 16 waves of a workgroup: wave w
+// owns k-blocks [P*16*KBW + w*KBW, +KBW) of phase P (k-block = 32 values),
+// so all waves do equal work on every tile and the A fragments of a wave
+// (its K slice of X, split into bf16 hi/lo) fit in registers. K longer than
+// 16*KBW k-blocks is covered in phases; phase P > 0 adds into Y, in order.
+//
+// Weight loads are contiguous runs: each instruction covers 16/KBW rows x
+// 64*KBW bytes (whole 128-byte lines for KBW >= 2), which the memory system
+// serves noticeably faster than the 16-rows x 64-bytes pattern of loading
+// the MFMA B operand directly. The wave transposes its segment through a
+// private LDS area (rows padded by 16 bytes: conflict-free writes and B
+// reads) and runs the MFMAs from there. Loads run two tiles ahead.
+//
+// M <= 8 (PACK): rows 0..7 of the A block hold the hi parts, rows 8..15 the
+// lo parts, one MFMA per k-block; each wave folds lo onto hi. 8 < M <= 16:
+// hi and lo are two A blocks with their own accumulators, added per wave.
+// The 16 per-wave partial tiles are summed in LDS in wave order (double
+// buffered, one barrier per tile).
+template <bool PACK, int KBW>
+__global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) {
+  constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
+  constexpr int SEG = 64 * KBW;                 // bytes of a row segment
+  constexpr int RS = SEG + 16;                  // padded LDS row stride
+  constexpr int LPR = SEG / 16;                 // lanes per row in a load instruction
+  constexpr int RPI = kWave / LPR;              // rows per load instruction
+  constexpr int NLD = 16 / RPI;                 // load instructions per tile
   extern __shared__ __align__(16) unsigned char smem[];
-  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [2][NW][F][64]
+  unsigned char* tr = smem;                                                          // [NW][16][RS]
+  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [2][NW][ROWS][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
-  const int S = p.S, P = NW / S, pw = w / S, s = w - pw * S;
-  const int N = p.N, K = p.K, M = p.M, KG = p.KG;
+  const int N = p.N, K = p.K, M = p.M;
+  const int KB = (K + 31) / 32;
+  const int phases = (KB + 16 * KBW - 1) / (16 * KBW);
 
-  // A fragments of this wave's granules q = s + S*j.
-  u32x4 afr[KBW][F];
+  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
+  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
+  const int rounds = t1 - t0;
+  const int lrow = lane / LPR, lchunk = lane % LPR;
+  unsigned char* wtr = tr + w * 16 * RS;
+  unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
+  const unsigned char* rd_base = wtr + i * RS + 16 * g;   // + 64*kb
+
+  for (int ph = 0; ph < phases; ++ph) {
+    const int kseg = 32 * KBW * (ph * NW + w);  // first k of this wave's segment
+    const bool lk_ok = kseg + 8 * lchunk < K;
+    u32x4 afr[KBW][F];
+
+    auto load = [&](u32x4 (&b)[NLD], int rr) {
+      const int row0 = (t0 + rr) * 16 + lrow;
+      const bool ok = rr < rounds && lk_ok;
+      const uint16_t* src = p.W + static_cast<size_t>(ok ? row0 : 0) * K + kseg + 8 * lchunk;
+      const size_t step = static_cast<size_t>(RPI) * K;
 #pragma unroll
-  for (int j = 0; j < GPW; ++j)
+      for (int q = 0; q < NLD; ++q)
+        b[q] = (ok && row0 + RPI * q < N) ? load16_stream(src + q * step) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto compute_publish = [&](u32x4 (&b)[NLD], int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = s + S * j;
-      const int k = (2 * q + h) * 32 + 8 * g;
+      for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+      f32x4 acc[F];
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(rd_base + 64 * kb);
+#pragma unroll
+        for (int f = 0; f < F; ++f) acc[f] = mfma_16x16x32(afr[kb][f], bv, acc[f]);
+      }
+      float* dst = red + (buf * NW + w) * ROWS * 16;
+      if (PACK) {
+        // lanes 0..31 hold rows 0..7 (hi), lanes 32..63 rows 8..15 (lo) of the same columns
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float lo = __shfl_down(acc[0][v], 32);
+          if (g < 2) dst[(4 * g + v) * 16 + i] = acc[0][v] + lo;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dst[(4 * g + v) * 16 + i] = acc[0][v] + acc[F - 1][v];
+      }
+    };
+    auto reduce_store = [&](int buf, int rr) {
+      for (int it = tid; it < ROWS * 16; it += NW * kWave) {
+        const int col = it & 15, m = it >> 4;
+        const int n = (t0 + rr) * 16 + col;
+        if (m < M && n < N) {
+          float y = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) y += red[((buf * NW + ww) * ROWS + m) * 16 + col];
+          float* yp = p.Y + static_cast<size_t>(m) * p.ldy + n;
+          *yp = ph == 0 ? y : *yp + y;  // the same thread wrote it in the previous phase
+        }
+      }
+    };
+
+    // The first two tiles' weight loads go out before the A fragments are
+    // built: they do not depend on X, so the two memory latencies overlap.
+    u32x4 b0[NLD], b1[NLD];
+    load(b0, 0);
+    load(b1, 1);
+    // A fragments: k-block kb of the segment covers k = kseg + 32*kb + 8*g + (0..7).
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const int k = kseg + 32 * kb + 8 * g;
 #pragma unroll
       for (int f = 0; f < F; ++f) {
         const int m = PACK ? (i & 7) : i;
         const int half = PACK ? (i >> 3) : f;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (q < KG && m < M && k < K) {
+        if (m < M && k < K) {
           const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
           const float4 x0 = xp[0], x1 = xp[1];
           const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -278,184 +360,23 @@ __global__ __launch_bounds__(16 * kWave) void gemv_stream_kernel(GemvParams p) {
           }
           v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
         }
-        afr[2 * j + h][f] = v;
+        afr[kb][f] = v;
       }
     }
-
-  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
-  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
-  const int rounds = (t1 - t0 + P - 1) / P;
-
-  auto load = [&](u32x4 (&b)[KBW], int r) {
-    const int tile = t0 + r * P + pw;
-    const bool ok_t = r < rounds && tile < t1;
-    const int row = min(tile * 16 + i, N - 1);
-    const uint16_t* src = p.W + static_cast<size_t>(row) * K + 8 * g;
-#pragma unroll
-    for (int j = 0; j < GPW; ++j)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = s + S * j;
-        const int kk = (2 * q + h) * 32;
-        const bool ok = ok_t && q < KG && kk + 8 * g < K;
-        b[2 * j + h] = ok ? load16_stream(src + kk) : u32x4{0u, 0u, 0u, 0u};
-      }
-  };
-  auto compute_publish = [&](u32x4 (&b)[KBW], int buf) {
-    f32x4 acc[F];
-#pragma unroll
-    for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-      for (int f = 0; f < F; ++f) acc[f] = mfma_16x16x32(afr[kb][f], b[kb], acc[f]);
-#pragma unroll
-    for (int f = 0; f < F; ++f) red[((buf * NW + w) * F + f) * kWave + lane] = acc[f];
-  };
-  auto reduce_store = [&](int buf, int r) {
-    constexpr int ROWS = PACK ? 8 : 16;
-    const float* rf = reinterpret_cast<const float*>(red);
-    for (int it = tid; it < P * ROWS * 16; it += NW * kWave) {
-      const int col = it & 15, m = (it >> 4) % ROWS, pp = (it >> 4) / ROWS;
-      const int tile = t0 + r * P + pp;
-      const int n = tile * 16 + col;
-      if (tile >= t1 || m >= M || n >= N) continue;
-      const int fh = 0, fl = PACK ? 0 : 1, rh = m, rl = PACK ? m + 8 : m;
-      float hi = 0.f, lo = 0.f;
-      for (int ss = 0; ss < S; ++ss) {
-        const int wv = pp * S + ss;
-        hi += rf[(((buf * NW + wv) * F + fh) * kWave + 16 * (rh >> 2) + col) * 4 + (rh & 3)];
-        lo += rf[(((buf * NW + wv) * F + fl) * kWave + 16 * (rl >> 2) + col) * 4 + (rl & 3)];
-      }
-      p.Y[static_cast<size_t>(m) * p.ldy + n] = hi + lo;
-    }
-  };
-
-  u32x4 b0[KBW], b1[KBW];
-  load(b0, 0);
-  load(b1, 1);
-  for (int r = 0; r < rounds; r += 2) {
-    compute_publish(b0, 0);
-    load(b0, r + 2);
-    __syncthreads();
-    reduce_store(0, r);
-    if (r + 1 < rounds) {
-      compute_publish(b1, 1);
-      load(b1, r + 3);
+    for (int rr = 0; rr < rounds; rr += 2) {
+      compute_publish(b0, 0);
+      load(b0, rr + 2);
       __syncthreads();
-      reduce_store(1, r + 1);
-    }
-  }
-}
-
-// Transposing stream variant for M <= 8 and 1024 < K <= 4096: 16 waves,
-// KBW = 4 or 8 k-blocks of 32 per wave. Wave w owns the contiguous K
-// segment [32*KBW*w, 32*KBW*(w+1)) of every tile. Its weight loads are
-// contiguous runs (each instruction covers 16/KBW rows x 64*KBW bytes, i.e.
-// whole 128-byte lines), which the memory system serves noticeably faster
-// than the 16-rows x 64-bytes pattern of direct B-operand loads. The wave
-// transposes its segment through a private LDS area (rows padded by 16
-// bytes, so the row writes and the B-operand reads are both free of bank
-// conflicts) and runs the MFMAs from there. The 16 partial tiles are added
-// in LDS in wave order.
-template <int KBW>
-__global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) {
-  constexpr int NW = 16;
-  constexpr int SEG = 64 * KBW;                 // bytes of a row segment
-  constexpr int RS = SEG + 16;                  // padded LDS row stride
-  constexpr int LPR = SEG / 16;                 // lanes per row in a load instruction
-  constexpr int RPI = kWave / LPR;              // rows per load instruction
-  constexpr int NLD = 16 / RPI;                 // load instructions per tile
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* tr = smem;                                                         // [NW][16][RS]
-  f32x4* red = reinterpret_cast<f32x4*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [NW][64]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
-  const int N = p.N, K = p.K, M = p.M;
-  const int kseg = 32 * KBW * w;  // first k of this wave's segment
-
-  // A fragments (rows 0..7: bf16 hi part of X, rows 8..15: lo part); k-block
-  // kb of the segment covers k = kseg + 32*kb + 8*g + (0..7).
-  u32x4 afr[KBW];
-#pragma unroll
-  for (int kb = 0; kb < KBW; ++kb) {
-    const int k = kseg + 32 * kb + 8 * g;
-    const int m = i & 7, half = i >> 3;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (m < M && k < K) {
-      const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
-      const float4 x0 = xp[0], x1 = xp[1];
-      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      uint32_t hb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t hv = bf16_bits_rne(xs[e]);
-        hb[e] = half ? bf16_bits_rne(xs[e] - bf16_bits_to_f32(hv)) : hv;
-      }
-      v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-    }
-    afr[kb] = v;
-  }
-
-  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
-  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
-  const int rounds = t1 - t0;
-
-  // Load instruction q of a tile: row RPI*q + lane/LPR, bytes 16*(lane%LPR) of the segment.
-  const int lrow = lane / LPR, lchunk = lane % LPR;
-  const bool lk_ok = kseg + 8 * lchunk < K;
-  auto load = [&](u32x4 (&b)[NLD], int rr) {
-    const int row0 = (t0 + rr) * 16 + lrow;
-    const bool ok = rr < rounds && lk_ok;
-    const uint16_t* src = p.W + static_cast<size_t>(ok ? row0 : 0) * K + kseg + 8 * lchunk;
-    const size_t step = static_cast<size_t>(RPI) * K;
-#pragma unroll
-    for (int q = 0; q < NLD; ++q)
-      b[q] = (ok && row0 + RPI * q < N) ? load16_stream(src + q * step) : u32x4{0u, 0u, 0u, 0u};
-  };
-  unsigned char* wtr = tr + w * 16 * RS;
-  unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;   // + RPI*q*RS
-  const unsigned char* rd_base = wtr + i * RS + 16 * g;    // + 64*kb
-  auto compute_publish = [&](u32x4 (&b)[NLD]) {
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
-      acc = mfma_16x16x32(afr[kb], *reinterpret_cast<const u32x4*>(rd_base + 64 * kb), acc);
-    red[w * kWave + lane] = acc;
-  };
-  auto reduce_store = [&](int rr) {
-    const float* rf = reinterpret_cast<const float*>(red);
-    if (tid < 128) {
-      const int col = tid & 15, m = tid >> 4;
-      const int n = (t0 + rr) * 16 + col;
-      if (m < M && n < N) {
-        float hi = 0.f, lo = 0.f;
-        for (int ww = 0; ww < NW; ++ww) {
-          hi += rf[(ww * kWave + 16 * (m >> 2) + col) * 4 + (m & 3)];
-          lo += rf[(ww * kWave + 16 * ((m + 8) >> 2) + col) * 4 + (m & 3)];
-        }
-        p.Y[static_cast<size_t>(m) * p.ldy + n] = hi + lo;
+      reduce_store(0, rr);
+      if (rr + 1 < rounds) {
+        compute_publish(b1, 1);
+        load(b1, rr + 3);
+        __syncthreads();
+        reduce_store(1, rr + 1);
       }
     }
-  };
-
-  u32x4 b0[NLD], b1[NLD];
-  load(b0, 0);
-  load(b1, 1);
-  for (int rr = 0; rr < rounds; rr += 2) {
-    compute_publish(b0);
-    load(b0, rr + 2);
-    __syncthreads();
-    reduce_store(rr);
-    __syncthreads();
-    if (rr + 1 < rounds) {
-      compute_publish(b1);
-      load(b1, rr + 3);
-      __syncthreads();
-      reduce_store(rr + 1);
+    if (phases > 1) {
+      __threadfence_block();  // this phase's Y stores complete before the next phase reads them
       __syncthreads();
     }
   }
@@ -463,8 +384,6 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
 
 struct Plan {
   int tkbw;     // gemv_tstream_kernel k-blocks per wave (0: not used)
-  bool stream;  // gemv_stream_kernel
-  int GPW;      // granules per wave (stream variant)
   int NA;
   bool pack;
   int NW;
@@ -488,30 +407,20 @@ Plan make_plan(int M, int N, int K, int cus) {
   }
   const int F = pl.pack ? 1 : 2 * pl.NA;
   const int tiles = (N + 15) / 16, KG = (K + 63) / 64;
-  if (M <= 8 && K > 1024 && K <= 4096) {
-    pl.tkbw = K > 2048 ? 8 : 4;
+  if (M <= 16) {
+    // gemv_tstream_kernel: K slices of 32*KBW per wave, phases for longer K.
+    const int KB = (K + 31) / 32;
+    const int kbw_max = pl.pack ? 8 : 4;
+    int kbw = 1;
+    while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
+    pl.tkbw = kbw;
     pl.S = 16;
     pl.TB = 1;
     pl.KGC = KG;
     pl.grid = std::max(1, std::min(cus, tiles));
-    pl.lds = static_cast<size_t>(16) * 16 * (64 * pl.tkbw + 16) + static_cast<size_t>(16) * kWave * 16;
+    const int rows = pl.pack ? 8 : 16;
+    pl.lds = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
     return pl;
-  }
-  if (M <= 16) {
-    int S = 16;
-    while (S > KG) S >>= 1;
-    const int gpw = (KG + S - 1) / S;
-    if (gpw <= (pl.pack ? 4 : 2)) {
-      pl.stream = true;
-      pl.GPW = gpw;
-      pl.S = S;
-      pl.TB = 1;
-      pl.KGC = KG;
-      const int P = 16 / S;
-      pl.grid = std::max(1, std::min(cus, (tiles + P - 1) / P));
-      pl.lds = static_cast<size_t>(2) * 16 * F * kWave * 16;
-      return pl;
-    }
   }
   const int cap = cus * pl.NW;
   int S = 1;
@@ -550,17 +459,9 @@ hipError_t launch_inst(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   return hipLaunchKernel(fn, dim3(pl.grid), dim3(NW * kWave), args, pl.lds, st);
 }
 
-template <bool PACK, int GPW>
-hipError_t launch_stream(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_stream_kernel<PACK, GPW>);
-  GemvParams a = prm;
-  void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
-}
-
-template <int KBW>
+template <bool PACK, int KBW>
 hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_tstream_kernel<KBW>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_tstream_kernel<PACK, KBW>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
@@ -570,29 +471,20 @@ hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st)
 }
 
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  if (pl.tkbw == 8) return launch_tstream<8>(prm, pl, st);
-  if (pl.tkbw == 4) return launch_tstream<4>(prm, pl, st);
-  if (pl.stream) {
+  if (pl.tkbw > 0) {
     if (pl.pack) {
-      switch (pl.GPW) {
-        case 1: return launch_stream<true, 1>(prm, pl, st);
-        case 2: return launch_stream<true, 2>(prm, pl, st);
-        case 3: return launch_stream<true, 3>(prm, pl, st);
-        default: return launch_stream<true, 4>(prm, pl, st);
+      switch (pl.tkbw) {
+        case 1: return launch_tstream<true, 1>(prm, pl, st);
+        case 2: return launch_tstream<true, 2>(prm, pl, st);
+        case 4: return launch_tstream<true, 4>(prm, pl, st);
+        default: return launch_tstream<true, 8>(prm, pl, st);
       }
     }
-    if (pl.GPW == 1) return launch_stream<false, 1>(prm, pl, st);
-    return launch_stream<false, 2>(prm, pl, st);
-  }
-  if (pl.NA == 1) {
-    if (pl.pack) {
-      if (pl.TB == 1) return launch_inst<1, true, 16, 1>(prm, pl, st);
-      if (pl.TB == 2) return launch_inst<1, true, 16, 2>(prm, pl, st);
-      return launch_inst<1, true, 16, 4>(prm, pl, st);
+    switch (pl.tkbw) {
+      case 1: return launch_tstream<false, 1>(prm, pl, st);
+      case 2: return launch_tstream<false, 2>(prm, pl, st);
+      default: return launch_tstream<false, 4>(prm, pl, st);
     }
-    if (pl.TB == 1) return launch_inst<1, false, 16, 1>(prm, pl, st);
-    if (pl.TB == 2) return launch_inst<1, false, 16, 2>(prm, pl, st);
-    return launch_inst<1, false, 16, 4>(prm, pl, st);
   }
   switch (pl.NA) {
     case 2: return launch_inst<2, false, 8, 1>(prm, pl, st);
