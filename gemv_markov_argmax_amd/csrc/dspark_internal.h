@@ -60,6 +60,25 @@ __device__ __forceinline__ uint32_t key_index(uint64_t key) {
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// A 64-bit value moved across lanes by a DPP pattern (both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Maximum over each row of 16 lanes, left in every lane of the row: quad
+// swaps (lane ^ 1, lane ^ 2), then the half-row and row mirrors, which
+// pair each quad with one in the other half and each half with the other.
+__device__ __forceinline__ uint64_t row_max64(uint64_t v) {
+  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
+  v = umax64(v, dpp64<0x140>(v));  // row_mirror
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------

@@ -273,9 +273,14 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
   const int KB = (K + 31) / 32;
   const int phases = (KB + 16 * KBW - 1) / (16 * KBW);
 
-  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
-  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
-  const int rounds = t1 - t0;
+  // Contiguous row range [r0, r1) of this workgroup, balanced to 2 rows (the
+  // granularity of a load instruction); tiles are 16 rows from r0, the last
+  // one masked at r1.
+  const int r0 = static_cast<int>((static_cast<long long>(blockIdx.x) * (N / 2)) / gridDim.x) * 2;
+  const int r1 = blockIdx.x + 1 == gridDim.x
+                     ? N
+                     : static_cast<int>((static_cast<long long>(blockIdx.x + 1) * (N / 2)) / gridDim.x) * 2;
+  const int rounds = (r1 - r0 + 15) / 16;
   const int lrow = lane / LPR, lchunk = lane % LPR;
   unsigned char* wtr = tr + w * 16 * RS;
   unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
@@ -287,13 +292,13 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
     u32x4 afr[KBW][F];
 
     auto load = [&](u32x4 (&b)[NLD], int rr) {
-      const int row0 = (t0 + rr) * 16 + lrow;
+      const int row0 = r0 + rr * 16 + lrow;
       const bool ok = rr < rounds && lk_ok;
       const uint16_t* src = p.W + static_cast<size_t>(ok ? row0 : 0) * K + kseg + 8 * lchunk;
       const size_t step = static_cast<size_t>(RPI) * K;
 #pragma unroll
       for (int q = 0; q < NLD; ++q)
-        b[q] = (ok && row0 + RPI * q < N) ? load16_stream(src + q * step) : u32x4{0u, 0u, 0u, 0u};
+        b[q] = (ok && row0 + RPI * q < r1) ? load16_stream(src + q * step) : u32x4{0u, 0u, 0u, 0u};
     };
     auto compute_publish = [&](u32x4 (&b)[NLD], int buf) {
 #pragma unroll
@@ -323,8 +328,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
     auto reduce_store = [&](int buf, int rr) {
       for (int it = tid; it < ROWS * 16; it += NW * kWave) {
         const int col = it & 15, m = it >> 4;
-        const int n = (t0 + rr) * 16 + col;
-        if (m < M && n < N) {
+        const int n = r0 + rr * 16 + col;
+        if (m < M && n < r1) {
           float y = 0.f;
 #pragma unroll
           for (int ww = 0; ww < NW; ++ww) y += red[((buf * NW + ww) * ROWS + m) * 16 + col];
@@ -417,7 +422,7 @@ Plan make_plan(int M, int N, int K, int cus) {
     pl.S = 16;
     pl.TB = 1;
     pl.KGC = KG;
-    pl.grid = std::max(1, std::min(cus, tiles));
+    pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
     const int rows = pl.pack ? 8 : 16;
     pl.lds = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
     return pl;

@@ -126,28 +126,29 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
   const bool bl = p.base_in_lds != 0;
   const int nb = bl ? R * nt * 16 : 0;  // base values of this workgroup staged per step
   constexpr int kPre = 4;               // prefetched base values per thread
+  // Entries e = tid + u*threads of the slice: LDS slot and base offset (step 0), fixed for the call.
+  int pre_lds[kPre];
+  size_t pre_src[kPre];
+  bool pre_ok[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int e = tid + u * kLoopThreads;
+    const int m = e < nb ? e / (nt * 16) : 0, nl = e - m * (nt * 16);
+    const int n = t0 * 16 + nl;
+    pre_lds[u] = m * p.bstride + nl;
+    pre_src[u] = static_cast<size_t>(m) * p.B * V + n;
+    pre_ok[u] = e < nb && n < V;
+  }
   float pre[kPre];
   auto fetch_base = [&](int st) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const int e = tid + u * kLoopThreads;
-      pre[u] = 0.f;
-      if (e < nb) {
-        const int m = e / (nt * 16), nl = e - m * (nt * 16);
-        const int n = t0 * 16 + nl;
-        if (n < V) pre[u] = p.base[(static_cast<size_t>(m) * p.B + st) * V + n];
-      }
-    }
+    for (int u = 0; u < kPre; ++u)
+      pre[u] = pre_ok[u] ? p.base[pre_src[u] + static_cast<size_t>(st) * V] : 0.f;
   };
   auto stage_base = [&](int st) {  // prefetched values, then any remainder straight from memory
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const int e = tid + u * kLoopThreads;
-      if (e < nb) {
-        const int m = e / (nt * 16), nl = e - m * (nt * 16);
-        basel[m * p.bstride + nl] = pre[u];
-      }
-    }
+    for (int u = 0; u < kPre; ++u)
+      if (tid + u * kLoopThreads < nb) basel[pre_lds[u]] = pre[u];
     for (int e = tid + kPre * kLoopThreads; e < nb; e += kLoopThreads) {
       const int m = e / (nt * 16), nl = e - m * (nt * 16);
       const int n = t0 * 16 + nl;
@@ -158,8 +159,8 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
 
   for (int step = 0; step < p.k; ++step) {
     __syncthreads();  // prev_s written; the previous step is done with basel
-    stage_base(step);
-    // ---- A operand: markov_w1[prev] of request i (zero for absent or invalid requests)
+    // ---- A operand: markov_w1[prev] of request i (zero for absent or invalid
+    // requests); issued first, it is the only load on this step's critical path
     u32x4 afr[KB];
     {
       const bool live = i < R && prev0_ok(p, i < R ? i : 0);
@@ -168,6 +169,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
       for (int kb = 0; kb < KB; ++kb)
         afr[kb] = (live && kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
     }
+    stage_base(step);
     __syncthreads();  // basel ready
 
     uint64_t best[4] = {0, 0, 0, 0};
@@ -216,8 +218,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       if (v >= R) break;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) best[v] = umax64(best[v], __shfl_xor(best[v], off));
+      best[v] = row_max64(best[v]);
     }
     if (i == 0)
 #pragma unroll
@@ -267,8 +268,9 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
         }
         __builtin_amdgcn_s_sleep(1);
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) kk = umax64(kk, __shfl_xor(kk, off));
+      kk = row_max64(kk);
+      kk = umax64(kk, __shfl_xor(kk, 16));
+      kk = umax64(kk, __shfl_xor(kk, 32));
       if (lane == 0) {
         int tok = static_cast<int>(key_index(kk));
         if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
