@@ -209,6 +209,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ops.lib()
+    if args.copy_calibration_mib > 0:
+        nflt = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(nflt, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     if args.config == "draft_layer":
         return bench_layer(args, dev)
     log(f"[bench] generating {args.config} inputs")
@@ -265,15 +274,6 @@ def main():
         mk()
         main_stream.wait_event(probe_done)
         out_host.copy_(out_dev, non_blocking=True)
-
-    if args.copy_calibration_mib > 0:
-        nflt = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(nflt, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     log(f"[bench] warmup {args.warmup} rounds")
     for _ in range(args.warmup):

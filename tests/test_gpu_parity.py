@@ -237,7 +237,7 @@ def _run_round(inp, t, logits=None, ids=None, ws=None, lg=None, ps=None):
     return logits, ids, lg, ps
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head", "reduced_vocab_batched"])
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head", "reduced_vocab_batched", "lane27b"])
 def test_round_chained(dev, name):
     inp, t = _round_tensors(name, dev)
     say(f"[round {name}] seed={inp['seed']}")
