@@ -2,9 +2,10 @@
 """Draft-round benchmark of the DSpark hot path on one MI355X.
 
 One step = one draft round of the chosen head workload, every row of the hot
-path: lm_head GEMV over all drafted rows -> k-step on-device Markov loop ->
-confidence probe on every drafted row -> asynchronous copy of the drafted
-ids and probe logits into pinned host memory. Inputs are seeded synthetic
+path, in order on one stream: lm_head GEMV over all drafted rows -> k-step
+on-device Markov loop -> confidence probe on every drafted row -> one
+asynchronous copy of the drafted ids and probe logits into pinned host
+memory. Inputs are seeded synthetic
 tensors already resident in HBM when timing starts.
 
 Prints one JSON line (stdout). Progress goes to stderr.
@@ -252,27 +253,20 @@ def main():
     def pr():
         ops.conf_probe(H, pw, bias, thr, logit_out=plog, pass_out=ppass)
 
-    # The probe reads only the hidden states, so it runs on a second stream
-    # (default priority) beside the lm_head and the Markov loop; the round's
-    # single D2H copy waits for both.
+    # Everything runs in order on one stream: lm_head, Markov loop, probe, then
+    # one asynchronous copy of the ids and probe logits. (Running the 3 us
+    # probe on a second stream beside the lm_head was measured ~10 us per
+    # round slower: the cross-stream event waits cost more than the probe.)
     main_stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    start_ev = torch.cuda.Event()
-    probe_done = torch.cuda.Event()
 
     def one_round(ev=None):
-        start_ev.record(main_stream)
-        side.wait_event(start_ev)
-        with torch.cuda.stream(side):
-            pr()
-            probe_done.record(side)
         if ev is not None:
             ev[0].record(main_stream)
         lm()
         if ev is not None:
             ev[1].record(main_stream)
         mk()
-        main_stream.wait_event(probe_done)
+        pr()
         out_host.copy_(out_dev, non_blocking=True)
 
     log(f"[bench] warmup {args.warmup} rounds")

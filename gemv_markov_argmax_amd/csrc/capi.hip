@@ -80,7 +80,7 @@ dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V
                                    const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0, int k,
                                    int64_t* ids_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!base || !w1 || !w2 || !prev0 || !ids_out) return DSPARK_ERR_NULL;
-  if (num_reqs < 1 || num_reqs > 16 || B < 1 || V < 1 || k < 1 || k > B || r < 8 || r > 1024 || (r % 8) != 0)
+  if (num_reqs < 1 || num_reqs > 16 || B < 1 || V < 1 || k < 1 || k > B || k > 32 || r < 8 || r > 1024 || (r % 8) != 0)
     return DSPARK_ERR_SHAPE;
   if (!aligned(base, 4) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(prev0, 8) ||
       !aligned(ids_out, 8) || (d2t && !aligned(d2t, 8)))

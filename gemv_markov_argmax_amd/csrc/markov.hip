@@ -27,13 +27,20 @@
 //    score, then by lower index, so a plain max gives the greedy pick with
 //    the lowest index winning ties, independent of reduction order.
 //  * Steps are separated by a key exchange that doubles as the grid barrier:
-//    a small kernel first clears this call's key slots; every workgroup then
-//    publishes its best key per request into its own slot (a valid key is
-//    never zero) and polls the G slots of that step with coherent loads until
-//    all are present (bounded spin), taking their maximum as it goes. Every
-//    workgroup thus learns prev without a counter or a second round trip.
-//    Workgroup 0 writes the ids. The next step's base values are fetched
-//    before the exchange, so only the markov_w1 gather follows it.
+//    every workgroup publishes its best key per request into its own slot (a
+//    valid key is never zero) and polls the G slots of that step with
+//    coherent loads until all are present (bounded spin), taking their
+//    maximum as it goes. Every workgroup thus learns prev without a counter
+//    or a second round trip. Workgroup 0 writes the ids. The next step's base
+//    values are fetched before the exchange, so only the markov_w1 gather
+//    follows it.
+//  * The key slots must read zero when a call starts, without a clearing
+//    launch in front of every call. The workspace holds two slot buffers and
+//    a call sequence number whose parity picks the active one; a call clears
+//    the entries the previous call used in the other buffer, and the last
+//    workgroup to leave advances the sequence number. Only a stream-ordered
+//    next call uses that buffer, so it is clean by then, even if a poll gave
+//    up. The workspace must therefore be zero-filled once before first use.
 //  * No floating-point atomics anywhere; results do not depend on timing.
 #include "dspark_internal.h"
 
@@ -43,10 +50,17 @@ namespace dspark {
 namespace {
 
 constexpr int kMaxReqs = 16;
+constexpr int kMaxSteps = 32;
 constexpr int kMaxGroups = 256;          // grid cap: one workgroup per CU
 constexpr int kLoopWaves = 8;
 constexpr int kLoopThreads = kLoopWaves * kWave;
-constexpr size_t kCtlBytes = 256;          // watchdog flag
+constexpr size_t kCtlBytes = 256;        // control words, then two slot buffers
+constexpr size_t kSlotsPerBuffer = static_cast<size_t>(kMaxSteps) * kMaxReqs * kMaxGroups;
+// Control words (uint32) at the start of the workspace.
+constexpr int kCtlWatchdog = 0;  // nonzero: a poll of this call gave up
+constexpr int kCtlSeq = 1;       // call sequence number; its parity selects the active slot buffer
+constexpr int kCtlExit = 2;      // workgroups of this call that are done with the slots
+constexpr int kCtlUsed = 4;      // [4 + b]: slots the last call that used buffer b wrote
 constexpr size_t kLdsBytes = 160 * 1024;
 constexpr uint32_t kSpinLimit = 1u << 18;  // watchdog (~0.3 s of polling): far beyond any legitimate wait
 
@@ -57,8 +71,8 @@ struct MarkovParams {
   const int64_t* prev0;  // [R]
   const int64_t* d2t;    // [V] or null
   int64_t* ids;          // [R, k]
-  uint32_t* ctl;         // [0] watchdog flag
-  uint64_t* part;        // [k][R][G] per-workgroup best keys, cleared per call
+  uint32_t* ctl;         // control words (kCtl*)
+  uint64_t* slots;       // [2][kSlotsPerBuffer]; active buffer: [k][R][G] per-workgroup best keys
   int R, B, V, r, k, G, tiles;
   int lds_tiles;         // markov_w2 tiles held in LDS per workgroup
   int bstride;           // floats per request in the LDS base slice (>= 16 * tiles per workgroup)
@@ -74,11 +88,8 @@ __device__ __forceinline__ uint64_t load_coherent(const uint64_t* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Clears the watchdog flag and the key slots of this call (n slots).
-__global__ void markov_init_kernel(uint32_t* ctl, uint64_t* part, int n) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t == 0) ctl[0] = 0u;
-  for (int j = t; j < n; j += gridDim.x * blockDim.x) part[j] = 0ull;
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kMaxPoll = kMaxGroups / kWave;  // slots per lane when polling
@@ -99,6 +110,8 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
   const int nt = t1 - t0;
   const int nreg = min(nt, NW * RT);
   const int nheld = nreg + min(nt - nreg, p.lds_tiles);
+  // Active slot buffer of this call (issued first: the reply arrives while markov_w2 loads).
+  const uint32_t seq = load_coherent(p.ctl + kCtlSeq);
 
   auto w2_row = [&](int j, int lrow) {
     const int row = min((t0 + j) * 16 + lrow, V - 1);
@@ -122,6 +135,29 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
                                     : u32x4{0u, 0u, 0u, 0u};
   }
   if (tid < R) prev_s[tid] = prev0_ok(p, tid) ? static_cast<int>(p.prev0[tid]) : 0;
+
+  const int cur = static_cast<int>(seq & 1u);
+  uint64_t* part = p.slots + cur * kSlotsPerBuffer;
+  {
+    // Clear what the previous call left in the other buffer; the next call uses it.
+    uint64_t* other = p.slots + (cur ^ 1) * kSlotsPerBuffer;
+    const uint32_t used = min(load_coherent(p.ctl + kCtlUsed + (cur ^ 1)), static_cast<uint32_t>(kSlotsPerBuffer));
+    for (uint32_t e = blockIdx.x * kLoopThreads + tid; e < used; e += G * kLoopThreads)
+      __hip_atomic_store(other + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && tid == 0)
+      __hip_atomic_store(p.ctl + kCtlUsed + cur, static_cast<uint32_t>(p.k * R * G), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Called once per workgroup when it is done reading slots; the last one
+  // out resets the exit count and the watchdog flag and advances the sequence.
+  auto leave = [&]() {
+    const uint32_t n = __hip_atomic_fetch_add(p.ctl + kCtlExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (n == static_cast<uint32_t>(G) - 1u) {
+      __hip_atomic_store(p.ctl + kCtlExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctl + kCtlWatchdog, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctl + kCtlSeq, seq + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   const bool bl = p.base_in_lds != 0;
   const int nb = bl ? R * nt * 16 : 0;  // base values of this workgroup staged per step
@@ -229,14 +265,17 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
     if (tid < R) {
       uint64_t kk = keys_s[tid];
       for (int ww = 1; ww < NW; ++ww) kk = umax64(kk, keys_s[ww * kMaxReqs + tid]);
-      __hip_atomic_store(p.part + (static_cast<size_t>(step) * R + tid) * G + blockIdx.x, kk, __ATOMIC_RELAXED,
+      __hip_atomic_store(part + (static_cast<size_t>(step) * R + tid) * G + blockIdx.x, kk, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (last && blockIdx.x != 0) return;  // only workgroup 0 needs the final step's winner
+    if (last && blockIdx.x != 0) {  // only workgroup 0 needs the final step's winner
+      if (tid == 0) leave();        // this workgroup's last poll ended before this step began
+      return;
+    }
 
     // ---- exchange: poll the G slots of each request until all are published
     for (int m = w; m < R; m += NW) {
-      const uint64_t* src = p.part + (static_cast<size_t>(step) * R + m) * G;
+      const uint64_t* src = part + (static_cast<size_t>(step) * R + m) * G;
       uint64_t kk = 0;
       uint32_t spins = 0;
       for (;;) {
@@ -258,7 +297,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
           break;
         }
         if (++spins > kSpinLimit) {
-          if (lane == 0) __hip_atomic_store(p.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) __hip_atomic_store(p.ctl + kCtlWatchdog, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
           for (int u = 0; u < kMaxPoll; ++u) {
             const int j = lane + u * kWave;
@@ -278,12 +317,14 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
         if (blockIdx.x == 0) {
           int64_t id = -1;
           if (prev0_ok(p, m)) id = p.d2t ? p.d2t[tok] : static_cast<int64_t>(tok);
-          if (__hip_atomic_load(p.ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) id = -2;
+          if (load_coherent(p.ctl + kCtlWatchdog) != 0u) id = -2;
           p.ids[static_cast<size_t>(m) * p.k + step] = id;
         }
       }
     }
   }
+  __syncthreads();  // workgroup 0: every poll of the final step is over
+  if (tid == 0) leave();
 }
 
 struct LoopPlan {
@@ -338,8 +379,8 @@ hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream
 }  // namespace
 
 size_t markov_workspace_bytes(int num_reqs, int k, int V) {
-  if (num_reqs < 1 || num_reqs > kMaxReqs || k < 1 || V < 1) return 0;
-  return kCtlBytes + static_cast<size_t>(k) * num_reqs * kMaxGroups * sizeof(uint64_t);
+  if (num_reqs < 1 || num_reqs > kMaxReqs || k < 1 || k > kMaxSteps || V < 1) return 0;
+  return kCtlBytes + 2 * kSlotsPerBuffer * sizeof(uint64_t);  // one layout for every size
 }
 
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
@@ -356,7 +397,7 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.d2t = d2t;
   prm.ids = ids;
   prm.ctl = static_cast<uint32_t*>(workspace);
-  prm.part = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(workspace) + kCtlBytes);
+  prm.slots = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(workspace) + kCtlBytes);
   prm.R = R;
   prm.B = B;
   prm.V = V;
@@ -367,14 +408,6 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.lds_tiles = pl.lds_tiles;
   prm.bstride = pl.bstride;
   prm.base_in_lds = pl.base_in_lds;
-  {
-    int nslots = k * R * pl.G;
-    void* args[] = {&prm.ctl, &prm.part, &nslots};
-    const int blocks = std::max(1, std::min(64, (nslots + 255) / 256));
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&markov_init_kernel), dim3(blocks),
-                                         dim3(256), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
   switch (pl.KB) {
     case 1: return launch_loop<1>(prm, pl, cus, stream);
     case 2: return launch_loop<2>(prm, pl, cus, stream);

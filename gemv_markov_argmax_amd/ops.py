@@ -108,10 +108,11 @@ def markov_workspace_bytes(num_reqs: int, k: int, V: int) -> int:
 
 
 def markov_workspace(num_reqs: int, k: int, V: int, device) -> torch.Tensor:
+    """A zero-filled workspace for dspark_markov_sample; reusable for calls of any shape."""
     n = markov_workspace_bytes(num_reqs, k, V)
     if n == 0:
         raise ValueError("sizes out of range for the Markov loop")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor, k: int,

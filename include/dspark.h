@@ -33,8 +33,9 @@
  *    BEFORE any HIP call is made and nothing is enqueued. A failed launch
  *    returns DSPARK_ERR_HIP. Faults during execution surface at the caller's
  *    next synchronization, as usual in HIP.
- *  - Calls are stateless and reentrant. Calls that share a workspace must
- *    not run concurrently.
+ *  - The library keeps no host-side state and every call is reentrant. The
+ *    Markov workspace carries device-side state from one call to the next,
+ *    so calls that share a workspace must not run concurrently.
  *  - Results are deterministic: no floating-point atomics are used, and the
  *    summation order of every output is fixed by the shapes alone.
  */
@@ -100,7 +101,8 @@ dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H,
 
 /*
  * Bytes of device workspace dspark_markov_sample needs for these sizes
- * (0 when a size is out of range).
+ * (0 when a size is out of range). The layout is the same for every valid
+ * size (about 2 MiB), so one workspace serves calls of any shape.
  */
 size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V);
 
@@ -127,8 +129,13 @@ size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V);
  *   prev0     int64 [num_reqs], draft-vocabulary ids
  *   ids_out   int64 [num_reqs, k], overwritten
  *   workspace >= dspark_markov_workspace_bytes(num_reqs, k, V) bytes,
- *             8-byte aligned; contents undefined between calls
- * Sizes: 1 <= num_reqs <= 16, 1 <= k <= B, V >= 1, 8 <= r <= 1024 with
+ *             8-byte aligned, owned by the caller. It must be ZERO-FILLED
+ *             ONCE before its first use; every call leaves it ready for the
+ *             next one (the loop keeps its own state there: key slots of the
+ *             grid-wide exchange and a call counter), so no clearing launch
+ *             precedes a call. Calls that share a workspace must be ordered
+ *             (one stream, or event dependencies).
+ * Sizes: 1 <= num_reqs <= 16, 1 <= k <= min(B, 32), V >= 1, 8 <= r <= 1024 with
  * r % 8 == 0. A request whose prev0 lies outside [0, V) gets -1 in every
  * entry of its ids row (a device-side check; nothing out of range is read).
  */

@@ -83,6 +83,7 @@ def test_markov_errors(L):
     assert call(R=17) == ERR_SHAPE
     assert call(k=8) == ERR_SHAPE          # k > B
     assert call(k=0) == ERR_SHAPE
+    assert call(B=40, k=33) == ERR_SHAPE   # k > 32
     assert call(r=12) == ERR_SHAPE         # r % 8 != 0
     assert call(r=2048) == ERR_SHAPE
     assert call(V=0) == ERR_SHAPE
@@ -96,7 +97,9 @@ def test_markov_errors(L):
 def test_markov_workspace_bytes(L):
     f = L.dspark_markov_workspace_bytes
     assert f(0, 7, 100) == 0 and f(17, 7, 100) == 0 and f(1, 0, 100) == 0 and f(1, 7, 0) == 0
-    assert f(8, 9, 32000) >= f(1, 9, 32000) > 0
+    assert f(1, 33, 100) == 0
+    # one layout for every valid shape, so a workspace can be reused across shapes
+    assert f(8, 9, 32000) == f(1, 9, 32000) == f(16, 32, 300000) == f(1, 1, 1) > 0
 
 
 def test_probe_errors(L):

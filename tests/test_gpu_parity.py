@@ -134,6 +134,22 @@ def test_markov_matches_oracle(dev, R, B, k, V, r):
     check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
 
 
+def test_markov_workspace_reused_across_shapes(dev):
+    """One zero-filled workspace serves a sequence of calls whose step
+    count, request count and grid size go up and down: the loop leaves its
+    key slots clean for the next call without a clearing launch."""
+    ws = _ops().markov_workspace(1, 1, 1, dev)
+    seq = [(1, 7, 7, 20011, 256), (16, 2, 2, 3001, 64), (1, 15, 15, 9000, 128), (2, 5, 5, 17, 16),
+           (8, 9, 9, 32007, 256), (1, 3, 2, 5, 8), (1, 15, 15, 9000, 128), (3, 6, 4, 4099, 264)]
+    for n, (R, B, k, V, r) in enumerate(seq):
+        seed = 4100 + n
+        say(f"[markov reuse {n}] R={R} B={B} k={k} V={V} r={r} seed={seed}")
+        base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, seed)
+        ids = _ops().markov_sample(_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k, workspace=ws)
+        torch.cuda.synchronize()
+        check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
+
+
 def test_markov_d2t_and_sentinel(dev):
     R, B, k, V, r = 4, 5, 5, 3000, 64
     say(f"[markov d2t+sentinel] R={R} V={V} r={r}")
