@@ -34,6 +34,30 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Raw buffer resource over [base, base + bytes) (bytes < 2^31). A load whose
+// offset is at or past `bytes` returns zeros from the hardware range check
+// and touches no memory, so edge lanes need neither a branch nor a clamp.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+constexpr uint32_t kBufOutOfRange = 0x80000000u;  // an offset past every range used here
+constexpr int kBufFlags = 0x00020000;             // word 3 of a raw 32-bit-element resource on gfx9
+
+__device__ __forceinline__ BufRes buf_res(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufFlags);
+}
+
+// 16 bytes, non-temporal (read once: a weight stream).
+__device__ __forceinline__ u32x4 buf_load16_nt(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2));
+}
+
+__device__ __forceinline__ float4 buf_load_f32x4(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
+__device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+
 // Round a finite float to bf16, nearest-even, returning the 16-bit pattern.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   uint32_t u = __float_as_uint(f);

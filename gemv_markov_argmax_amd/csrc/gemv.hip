@@ -46,6 +46,7 @@ struct GemvParams {
   int KG;        // 64-element granules in K
   int KGC;       // granules per LDS chunk
   int tiles;     // ceil(N / 16)
+  int chunk;     // gemv_tstream_kernel: tiles whose outputs are staged in LDS at once (even)
 };
 
 template <int NA, bool PACK, int NW, int TB>
@@ -235,7 +236,12 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvParams p) {
   }
 }
 
-// Streaming variant for M <= 16 (the small-M GEMVs of a draft round).
+// Short variant for M <= 16: at most two 16-row tiles per workgroup (the
+// small projections of a draft layer). It follows the same plan as
+// gemv_tstream_kernel below but with the shortest dependency chain: plain
+// guarded loads and a direct store of each output tile. (The store makes the
+// wave wait for every load in flight before its next tile, which only
+// matters when there are many tiles per workgroup.)
 //
 // Every 16-row tile is split along K over the 16 waves of a workgroup: wave w
 // owns k-blocks [P*16*KBW + w*KBW, +KBW) of phase P (k-block = 32 values),
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvParams p) {
 // The 16 per-wave partial tiles are summed in LDS in wave order (double
 // buffered, one barrier per tile).
 template <bool PACK, int KBW>
-__global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) {
+__global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
   constexpr int SEG = 64 * KBW;                 // bytes of a row segment
   constexpr int RS = SEG + 16;                  // padded LDS row stride
@@ -387,8 +393,236 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
   }
 }
 
+// Streaming variant for M <= 16 (the small-M GEMVs of a draft round).
+//
+// Every 16-row tile is split along K over the 16 waves of a workgroup: wave w
+// owns k-blocks [P*16*KBW + w*KBW, +KBW) of phase P (k-block = 32 values),
+// so all waves do equal work on every tile and the A fragments of a wave
+// (its K slice of X, split into bf16 hi/lo) fit in registers. K longer than
+// 16*KBW k-blocks is covered in phases.
+//
+// Weight loads are contiguous runs: each instruction covers 16/KBW rows x
+// 64*KBW bytes (whole 128-byte lines for KBW >= 2), which the memory system
+// serves noticeably faster than the 16-rows x 64-bytes pattern of loading
+// the MFMA B operand directly. The wave transposes its segment through a
+// private LDS area (rows padded by 16 bytes: conflict-free writes and B
+// reads) and runs the MFMAs from there. Loads run two tiles ahead.
+//
+// The loop issues no global store. On gfx9 loads and stores share one
+// counter and may complete out of order with respect to each other, so a
+// wave that has a store outstanding must drain every prefetched load before
+// it may use one. The outputs of a chunk of tiles are therefore summed into
+// LDS (phases add there) and written out, as whole rows, once per chunk.
+// All global loads are raw buffer loads over the workgroup's own rows (and
+// over X): a lane past the end of its range gets zeros from the hardware
+// range check instead of a branch, so the loop body is straight code and
+// the compiler counts the loads in flight exactly.
+//
+// M <= 8 (PACK): rows 0..7 of the A block hold the hi parts, rows 8..15 the
+// lo parts, one MFMA per k-block; each wave folds lo onto hi. 8 < M <= 16:
+// hi and lo are two A blocks with their own accumulators, added per wave.
+// The 16 per-wave partial tiles are summed in wave order (double buffered,
+// one barrier per tile).
+template <bool PACK, int KBW, bool MULTI>
+__global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) {
+  constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
+  constexpr int SEG = 64 * KBW;                 // bytes of a row segment
+  constexpr int RS = SEG + 16;                  // padded LDS row stride
+  constexpr int LPR = SEG / 16;                 // lanes per row in a load instruction
+  constexpr int RPI = kWave / LPR;              // rows per load instruction
+  constexpr int NLD = 16 / RPI;                 // load instructions per tile
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* tr = smem;                                                          // [NW][16][RS]
+  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [2][NW][ROWS][16]
+  float* ylds = red + 2 * NW * ROWS * 16;                                            // [chunk][M][16]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int N = p.N, K = p.K, M = p.M;
+  const int KB = (K + 31) / 32;
+  const int phases = (KB + 16 * KBW - 1) / (16 * KBW);
+
+  // Contiguous row range [r0, r1) of this workgroup, balanced to 2 rows (the
+  // granularity of a load instruction); tiles are 16 rows from r0, the last
+  // one masked at r1.
+  const int r0 = static_cast<int>((static_cast<long long>(blockIdx.x) * (N / 2)) / gridDim.x) * 2;
+  const int r1 = blockIdx.x + 1 == gridDim.x
+                     ? N
+                     : static_cast<int>((static_cast<long long>(blockIdx.x + 1) * (N / 2)) / gridDim.x) * 2;
+  const int rounds = (r1 - r0 + 15) / 16;
+  // Chunks of this workgroup's tiles, balanced, even sized (but the last).
+  const int nchunks = (rounds + p.chunk - 1) / p.chunk;
+  const int csize = (((rounds + nchunks - 1) / nchunks) + 1) & ~1;
+  const int lrow = lane / LPR, lchunk = lane % LPR;
+  unsigned char* wtr = tr + w * 16 * RS;
+  unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
+  const unsigned char* rd_base = wtr + i * RS + 16 * g;   // + 64*kb
+
+  const uint32_t rowb = static_cast<uint32_t>(K) * 2;     // bytes per weight row
+  const BufRes wres = buf_res(p.W + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
+  const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+
+  u32x4 afr[KBW][F];
+  u32x4 b0[NLD], b1[NLD];
+  int ph = 0, c0 = 0, c1 = 0, lim = 0;
+  uint32_t lane_off = 0;
+
+  // Phase ph: this wave's segment starts at k = kseg. A lane whose k lies
+  // past K starts out of range, so it reads zeros (the added tile offsets
+  // stay below 2^31 and cannot wrap it back in).
+  auto set_phase = [&](int phase) {
+    ph = phase;
+    const int kseg = 32 * KBW * (ph * NW + w);
+    lane_off = kseg + 8 * lchunk < K
+                   ? static_cast<uint32_t>(lrow) * rowb + static_cast<uint32_t>(kseg + 8 * lchunk) * 2
+                   : kBufOutOfRange;
+  };
+  // A fragments of phase ph: k-block kb covers k = kseg + 32*kb + 8*g + (0..7);
+  // lanes past M or K load zeros. The activation loads go out at once, or in
+  // two batches where registers are short, and are split into bf16 hi/lo.
+  auto build_a = [&]() {
+    const int kseg = 32 * KBW * (ph * NW + w);
+    constexpr int KH = KBW * F * 8 > 32 ? KBW / 2 : KBW;
+#pragma unroll
+    for (int k0 = 0; k0 < KBW; k0 += KH) {
+      float4 xr[KH][F][2];
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk)
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          const int m = PACK ? (i & 7) : i, k = kseg + 32 * (k0 + kk) + 8 * g;
+          const uint32_t off = m < M && k < K ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
+          xr[kk][f][0] = buf_load_f32x4(xres, off);
+          xr[kk][f][1] = buf_load_f32x4(xres, off + 16);
+        }
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk)
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          const int half = PACK ? (i >> 3) : f;
+          const float4 x0 = xr[kk][f][0], x1 = xr[kk][f][1];
+          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          uint32_t hb[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t hv = bf16_bits_rne(xs[e]);
+            hb[e] = half ? bf16_bits_rne(xs[e] - bf16_bits_to_f32(hv)) : hv;
+          }
+          afr[k0 + kk][f] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                                  hb[6] | (hb[7] << 16)};
+        }
+    }
+  };
+  // Tile rr of this workgroup; rows past r1 and tiles past lim read zeros.
+  auto load = [&](u32x4 (&b)[NLD], int rr) {
+    const uint32_t off = rr < lim ? lane_off + static_cast<uint32_t>(rr) * 16 * rowb : kBufOutOfRange;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(wres, off + static_cast<uint32_t>(q * RPI) * rowb);
+  };
+  // b0 must stay the older group (the loop waits for it with b1 still in
+  // flight), so the scheduler may not move the prologue loads. The first
+  // tile's loads go out before the A fragments are built: they do not depend
+  // on X, so the two memory latencies overlap.
+  auto prologue = [&](bool with_a) {
+    load(b0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (with_a) build_a();
+    load(b1, c0 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_publish = [&](u32x4 (&b)[NLD], int buf) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+    f32x4 acc[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(rd_base + 64 * kb);
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = mfma_16x16x32(afr[kb][f], bv, acc[f]);
+    }
+    float* dst = red + (buf * NW + w) * ROWS * 16;
+    if (PACK) {
+      // lanes 0..31 hold rows 0..7 (hi), lanes 32..63 rows 8..15 (lo) of the same columns
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float lo = __shfl_down(acc[0][v], 32);
+        if (g < 2) dst[(4 * g + v) * 16 + i] = acc[0][v] + lo;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[(4 * g + v) * 16 + i] = acc[0][v] + acc[F - 1][v];
+    }
+  };
+  // Wave-order sum of tile rr into the chunk's LDS outputs (phases add).
+  auto reduce = [&](int buf, int rr) {
+    if (tid < M * 16) {
+      float y = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) y += red[((buf * NW + ww) * ROWS + (tid >> 4)) * 16 + (tid & 15)];
+      float* yl = ylds + (rr - c0) * M * 16 + tid;
+      *yl = ph == 0 ? y : *yl + y;
+    }
+  };
+  // Tiles [c0, c1), two per iteration with a single exit: the back edge
+  // always carries b0 older than b1, so the head waits for b0 alone. Chunks
+  // are even sized but the last; its odd tail runs the second half on the
+  // zeros of tile c1 and keeps nothing.
+  auto run_tiles = [&]() {
+    for (int rr = c0; rr < c1; rr += 2) {
+      compute_publish(b0, 0);
+      load(b0, rr + 2);
+      __syncthreads();
+      reduce(0, rr);
+      compute_publish(b1, 1);
+      load(b1, rr + 3);
+      __syncthreads();
+      if (rr + 1 < c1) reduce(1, rr + 1);
+    }
+  };
+  // The chunk's outputs, row by row: columns [r0 + 16*c0, min(r1, r0 + 16*c1)).
+  auto write_out = [&]() {
+    __syncthreads();
+    const int n0 = r0 + 16 * c0, cols = min(r1, r0 + 16 * c1) - n0;
+    for (int m = 0; m < M; ++m)
+      for (int j = tid; j < cols; j += NW * kWave)
+        p.Y[static_cast<size_t>(m) * p.ldy + n0 + j] = ylds[(j >> 4) * M * 16 + m * 16 + (j & 15)];
+    __syncthreads();  // the next chunk reuses the LDS outputs
+  };
+
+  if (!MULTI) {
+    // One phase: the A fragments are built once and the prefetch runs on
+    // across chunk boundaries, so a chunk's outputs go out while the next
+    // chunk's first tiles are already on their way.
+    set_phase(0);
+    lim = rounds;
+    c0 = 0;
+    prologue(true);
+    for (; c0 < rounds; c0 += csize) {
+      c1 = min(rounds, c0 + csize);
+      run_tiles();
+      write_out();
+    }
+  } else {
+    // Each chunk runs every phase; tiles past the chunk read zeros.
+    for (c0 = 0; c0 < rounds; c0 += csize) {
+      c1 = min(rounds, c0 + csize);
+      lim = c1;
+      for (int q = 0; q < phases; ++q) {
+        set_phase(q);
+        prologue(true);
+        run_tiles();
+      }
+      write_out();
+    }
+  }
+}
+
 struct Plan {
-  int tkbw;     // gemv_tstream_kernel k-blocks per wave (0: not used)
+  int tkbw;     // gemv_tstream_kernel / gemv_short_kernel k-blocks per wave (0: neither)
+  bool shortk;  // gemv_short_kernel (at most two tiles per workgroup)
+  int chunk;    // gemv_tstream_kernel tiles per LDS output chunk
   int NA;
   bool pack;
   int NW;
@@ -413,18 +647,34 @@ Plan make_plan(int M, int N, int K, int cus) {
   const int F = pl.pack ? 1 : 2 * pl.NA;
   const int tiles = (N + 15) / 16, KG = (K + 63) / 64;
   if (M <= 16) {
-    // gemv_tstream_kernel: K slices of 32*KBW per wave, phases for longer K.
+    // K slices of 32*KBW per wave, phases for longer K. Workgroups with at
+    // most two tiles take the short kernel (up to 8 k-blocks per wave with
+    // packed rows); longer ones the LDS-staged streaming kernel, whose
+    // registers allow 4.
     const int KB = (K + 31) / 32;
-    const int kbw_max = pl.pack ? 8 : 4;
+    pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
+    const int rows_max = 2 * ((N / 2 + pl.grid - 1) / pl.grid) + 1;  // rows of the largest workgroup
+    const int rounds = (rows_max + 15) / 16;
+    pl.shortk = rounds <= 2;
+    const int kbw_max = pl.shortk && pl.pack ? 8 : 4;
     int kbw = 1;
     while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
     pl.tkbw = kbw;
     pl.S = 16;
     pl.TB = 1;
     pl.KGC = KG;
-    pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
     const int rows = pl.pack ? 8 : 16;
-    pl.lds = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
+    const size_t fixed = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
+    if (pl.shortk) {
+      pl.chunk = 0;
+      pl.lds = fixed;
+      return pl;
+    }
+    const size_t per_tile = static_cast<size_t>(M) * 16 * 4;
+    int chunk = static_cast<int>((kLdsBytes - fixed) / per_tile) & ~1;
+    chunk = std::max(2, std::min(chunk, (rounds + 1) & ~1));
+    pl.chunk = chunk;
+    pl.lds = fixed + chunk * per_tile;
     return pl;
   }
   const int cap = cus * pl.NW;
@@ -466,7 +716,24 @@ hipError_t launch_inst(const GemvParams& prm, const Plan& pl, hipStream_t st) {
 
 template <bool PACK, int KBW>
 hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_tstream_kernel<PACK, KBW>);
+  const void* one = reinterpret_cast<const void*>(&gemv_tstream_kernel<PACK, KBW, false>);
+  const void* multi = reinterpret_cast<const void*>(&gemv_tstream_kernel<PACK, KBW, true>);
+  static const hipError_t attr = [&] {
+    const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+    return e != hipSuccess ? e
+                           : hipFuncSetAttribute(multi, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kLdsBytes));
+  }();
+  if (attr != hipSuccess) return attr;
+  const bool phased = (prm.K + 32 * 16 * KBW - 1) / (32 * 16 * KBW) > 1;  // more than one K phase
+  GemvParams a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(phased ? multi : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
+}
+
+template <bool PACK, int KBW>
+hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
@@ -476,13 +743,27 @@ hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st)
 }
 
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  if (pl.tkbw > 0 && pl.shortk) {
+    if (pl.pack) {
+      switch (pl.tkbw) {
+        case 1: return launch_short<true, 1>(prm, pl, st);
+        case 2: return launch_short<true, 2>(prm, pl, st);
+        case 4: return launch_short<true, 4>(prm, pl, st);
+        default: return launch_short<true, 8>(prm, pl, st);
+      }
+    }
+    switch (pl.tkbw) {
+      case 1: return launch_short<false, 1>(prm, pl, st);
+      case 2: return launch_short<false, 2>(prm, pl, st);
+      default: return launch_short<false, 4>(prm, pl, st);
+    }
+  }
   if (pl.tkbw > 0) {
     if (pl.pack) {
       switch (pl.tkbw) {
         case 1: return launch_tstream<true, 1>(prm, pl, st);
         case 2: return launch_tstream<true, 2>(prm, pl, st);
-        case 4: return launch_tstream<true, 4>(prm, pl, st);
-        default: return launch_tstream<true, 8>(prm, pl, st);
+        default: return launch_tstream<true, 4>(prm, pl, st);
       }
     }
     switch (pl.tkbw) {
@@ -524,6 +805,7 @@ hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, f
     prm.KG = (K + 63) / 64;
     prm.KGC = pl.KGC;
     prm.tiles = (N + 15) / 16;
+    prm.chunk = pl.chunk;
     const hipError_t e = dispatch(prm, pl, stream);
     if (e != hipSuccess) return e;
   }
