@@ -329,7 +329,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.config, "num_reqs": R, "B": B, "k": k, "d": d, "V": V, "r": r},
-        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (gemv_tstream_kernel<true, 8>)", "achieved": lm_gbs,
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head)", "achieved": lm_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
                      "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3},
         "round_hbm": {"achieved": round_gbs, "unit": "GB/s", "frac": round_gbs / HBM_PEAK_GBS,

@@ -36,11 +36,18 @@
 //    follows it.
 //  * The key slots must read zero when a call starts, without a clearing
 //    launch in front of every call. The workspace holds two slot buffers and
-//    a call sequence number whose parity picks the active one; a call clears
-//    the entries the previous call used in the other buffer, and the last
-//    workgroup to leave advances the sequence number. Only a stream-ordered
-//    next call uses that buffer, so it is clean by then, even if a poll gave
-//    up. The workspace must therefore be zero-filled once before first use.
+//    a call sequence number whose parity picks the active one; while a call
+//    runs, its workgroups clear the entries the previous call used in the
+//    other buffer, and workgroup 0, the last to read any slot, advances the
+//    sequence number at the end. Only a stream-ordered next call uses that
+//    buffer, so it is clean by then. The workspace must therefore be
+//    zero-filled once before first use. A poll that gives up (which the
+//    residency check rules out on an otherwise idle device) leaves a sticky
+//    flag: that call and every later one on the workspace return -2 ids
+//    until it is zero-filled again.
+//  * Nothing but the exchange sits on the per-step path of workgroup 0: the
+//    drafted tokens stay in LDS and the ids (d2t applied) are written once,
+//    after the last step.
 //  * No floating-point atomics anywhere; results do not depend on timing.
 #include "dspark_internal.h"
 
@@ -57,9 +64,8 @@ constexpr int kLoopThreads = kLoopWaves * kWave;
 constexpr size_t kCtlBytes = 256;        // control words, then two slot buffers
 constexpr size_t kSlotsPerBuffer = static_cast<size_t>(kMaxSteps) * kMaxReqs * kMaxGroups;
 // Control words (uint32) at the start of the workspace.
-constexpr int kCtlWatchdog = 0;  // nonzero: a poll of this call gave up
+constexpr int kCtlWatchdog = 0;  // nonzero: a poll gave up; sticky until the workspace is zero-filled
 constexpr int kCtlSeq = 1;       // call sequence number; its parity selects the active slot buffer
-constexpr int kCtlExit = 2;      // workgroups of this call that are done with the slots
 constexpr int kCtlUsed = 4;      // [4 + b]: slots the last call that used buffer b wrote
 constexpr size_t kLdsBytes = 160 * 1024;
 constexpr uint32_t kSpinLimit = 1u << 18;  // watchdog (~0.3 s of polling): far beyond any legitimate wait
@@ -101,7 +107,8 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
   u32x4* w2l = reinterpret_cast<u32x4*>(smem);                                         // [lds_tiles][KB][64]
   uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * 1024);  // [NW][16]
   int* prev_s = reinterpret_cast<int*>(keys_s + NW * kMaxReqs);                           // [16]
-  float* basel = reinterpret_cast<float*>(prev_s + kMaxReqs);                             // [R][bstride]
+  int* tok_s = prev_s + kMaxReqs;                                                         // [k][R] drafted tokens
+  float* basel = reinterpret_cast<float*>(tok_s + kMaxSteps * kMaxReqs);                  // [R][bstride]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
   const int R = p.R, V = p.V, r = p.r, G = p.G;
@@ -110,8 +117,10 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
   const int nt = t1 - t0;
   const int nreg = min(nt, NW * RT);
   const int nheld = nreg + min(nt - nreg, p.lds_tiles);
-  // Active slot buffer of this call (issued first: the reply arrives while markov_w2 loads).
+  // Active slot buffer of this call, and the sticky watchdog flag (issued
+  // first: the replies arrive while markov_w2 loads).
   const uint32_t seq = load_coherent(p.ctl + kCtlSeq);
+  const uint32_t dead = load_coherent(p.ctl + kCtlWatchdog);
 
   auto w2_row = [&](int j, int lrow) {
     const int row = min((t0 + j) * 16 + lrow, V - 1);
@@ -138,23 +147,37 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
 
   const int cur = static_cast<int>(seq & 1u);
   uint64_t* part = p.slots + cur * kSlotsPerBuffer;
-  {
-    // Clear what the previous call left in the other buffer; the next call uses it.
+  const uint32_t used_other = load_coherent(p.ctl + kCtlUsed + (cur ^ 1));
+  // Clears what the previous call left in the other buffer (which the next
+  // call uses), shared by the workgroups that finish early: all but 0, or 0
+  // alone. These stores stay out of the step loop: a store in flight would
+  // make a wave drain its outstanding loads before it may use any of them.
+  auto clear_other = [&]() {
     uint64_t* other = p.slots + (cur ^ 1) * kSlotsPerBuffer;
-    const uint32_t used = min(load_coherent(p.ctl + kCtlUsed + (cur ^ 1)), static_cast<uint32_t>(kSlotsPerBuffer));
-    for (uint32_t e = blockIdx.x * kLoopThreads + tid; e < used; e += G * kLoopThreads)
+    const uint32_t used = min(used_other, static_cast<uint32_t>(kSlotsPerBuffer));
+    const uint32_t nwg = G > 1 ? G - 1 : 1, wg = G > 1 ? blockIdx.x - 1 : 0;
+    for (uint32_t e = wg * kLoopThreads + tid; e < used; e += nwg * kLoopThreads)
       __hip_atomic_store(other + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (blockIdx.x == 0 && tid == 0)
+  };
+  // Workgroup 0 after the last step (every other workgroup has published
+  // every step, so none reads a slot any more): the ids of all steps, the
+  // slots used, and the next sequence number. A poll that gave up in this
+  // call or an earlier one turns every id into -2.
+  auto finish = [&]() {
+    if (G == 1) clear_other();
+    const bool bad = dead != 0u || load_coherent(p.ctl + kCtlWatchdog) != 0u;
+    for (int e = tid; e < R * p.k; e += kLoopThreads) {
+      const int m = e / p.k, st = e - m * p.k;
+      int64_t id = -1;
+      if (dead == 0u && prev0_ok(p, m)) {  // tok_s holds this call's tokens (each in [0, V))
+        const int tok = tok_s[st * kMaxReqs + m];
+        id = p.d2t ? p.d2t[tok] : static_cast<int64_t>(tok);
+      }
+      p.ids[e] = bad ? -2 : id;
+    }
+    if (tid == 0) {
       __hip_atomic_store(p.ctl + kCtlUsed + cur, static_cast<uint32_t>(p.k * R * G), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // Called once per workgroup when it is done reading slots; the last one
-  // out resets the exit count and the watchdog flag and advances the sequence.
-  auto leave = [&]() {
-    const uint32_t n = __hip_atomic_fetch_add(p.ctl + kCtlExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (n == static_cast<uint32_t>(G) - 1u) {
-      __hip_atomic_store(p.ctl + kCtlExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.ctl + kCtlWatchdog, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctl + kCtlSeq, seq + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
@@ -192,6 +215,11 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
     }
   };
   fetch_base(0);
+
+  if (dead != 0u) {  // an earlier call gave up: report it and touch no slot
+    if (blockIdx.x == 0) finish();
+    return;
+  }
 
   for (int step = 0; step < p.k; ++step) {
     __syncthreads();  // prev_s written; the previous step is done with basel
@@ -269,7 +297,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
                          __HIP_MEMORY_SCOPE_AGENT);
     }
     if (last && blockIdx.x != 0) {  // only workgroup 0 needs the final step's winner
-      if (tid == 0) leave();        // this workgroup's last poll ended before this step began
+      clear_other();
       return;
     }
 
@@ -314,17 +342,12 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
         int tok = static_cast<int>(key_index(kk));
         if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
         prev_s[m] = tok;
-        if (blockIdx.x == 0) {
-          int64_t id = -1;
-          if (prev0_ok(p, m)) id = p.d2t ? p.d2t[tok] : static_cast<int64_t>(tok);
-          if (load_coherent(p.ctl + kCtlWatchdog) != 0u) id = -2;
-          p.ids[static_cast<size_t>(m) * p.k + step] = id;
-        }
+        tok_s[step * kMaxReqs + m] = tok;
       }
     }
   }
-  __syncthreads();  // workgroup 0: every poll of the final step is over
-  if (tid == 0) leave();
+  __syncthreads();  // workgroup 0: every poll of the final step is over, tok_s complete
+  finish();
 }
 
 struct LoopPlan {
@@ -348,7 +371,7 @@ LoopPlan make_loop_plan(int R, int V, int r, int cus) {
   const size_t base_bytes = static_cast<size_t>(R) * pl.bstride * 4;
   pl.base_in_lds = base_bytes <= kBaseLdsMax ? 1 : 0;
   const size_t fixed = static_cast<size_t>(kLoopWaves) * kMaxReqs * 8 + kMaxReqs * 4 +
-                       (pl.base_in_lds ? base_bytes : 0);
+                       static_cast<size_t>(kMaxSteps) * kMaxReqs * 4 + (pl.base_in_lds ? base_bytes : 0);
   const size_t tile_bytes = static_cast<size_t>(pl.KB) * 1024;
   const int want = std::max(0, ntmax - kLoopWaves * pl.RT);
   const int fit = fixed < kLdsBytes ? static_cast<int>((kLdsBytes - fixed) / tile_bytes) : 0;

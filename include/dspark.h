@@ -135,6 +135,12 @@ size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V);
  *             grid-wide exchange and a call counter), so no clearing launch
  *             precedes a call. Calls that share a workspace must be ordered
  *             (one stream, or event dependencies).
+ * The loop's workgroups exchange one key per step and must all be resident
+ * at once; the call checks that the grid fits the device
+ * (DSPARK_ERR_HIP otherwise). Should a grid-wide wait still time out (other
+ * work holding the compute units for a long time), every id of that call is
+ * -2, and so is every id of later calls on the same workspace until it is
+ * zero-filled again.
  * Sizes: 1 <= num_reqs <= 16, 1 <= k <= min(B, 32), V >= 1, 8 <= r <= 1024 with
  * r % 8 == 0. A request whose prev0 lies outside [0, V) gets -1 in every
  * entry of its ids row (a device-side check; nothing out of range is read).

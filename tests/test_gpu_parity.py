@@ -150,6 +150,28 @@ def test_markov_workspace_reused_across_shapes(dev):
         check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
 
 
+def test_markov_sticky_watchdog_flag(dev):
+    """A workspace whose watchdog word is set (as a timed-out grid-wide wait
+    leaves it; set here from the host) makes every id -2 without touching a
+    key slot, call after call, until the workspace is zero-filled again."""
+    R, B, k, V, r = 2, 5, 5, 3000, 64
+    say(f"[markov watchdog flag] R={R} V={V} r={r}")
+    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, 91)
+    args = (_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k)
+    ws = _ops().markov_workspace(R, k, V, dev)
+    good = _ops().markov_sample(*args, workspace=ws).clone()
+    ws[0] = 1  # low byte of the watchdog word
+    for _ in range(2):
+        ids = _ops().markov_sample(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(ids == -2)
+    ws.zero_()
+    ids = _ops().markov_sample(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, good)
+    check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
+
+
 def test_markov_d2t_and_sentinel(dev):
     R, B, k, V, r = 4, 5, 5, 3000, 64
     say(f"[markov d2t+sentinel] R={R} V={V} r={r}")
