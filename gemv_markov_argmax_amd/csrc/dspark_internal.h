@@ -58,6 +58,18 @@ __device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Exact-to-2^-17 split of two fp32 values into bf16 pairs: hi = bf16(x),
+// lo = bf16(x - hi), both nearest-even (v_cvt_pk_bf16_f32 on gfx950), so
+// x = hi + lo + O(2^-17 |x|). Returns {hi pair, lo pair}, a in the low halves.
+__device__ __forceinline__ uint2 split_bf16x2(float a, float b) {
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  const f32x2 r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u)};
+  return uint2{hi, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
+}
+
 // Round a finite float to bf16, nearest-even, returning the 16-bit pattern.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   uint32_t u = __float_as_uint(f);

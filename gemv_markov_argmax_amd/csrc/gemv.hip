@@ -8,27 +8,26 @@
 // weight-stationary matvec that reads every weight row once for all rows.
 //
 // Design on gfx950:
-//  * The weights stream from HBM exactly once, 16 bytes per lane per load,
-//    straight into the B operand of v_mfma_f32_16x16x32_bf16: lane l loads
-//    8 consecutive bf16 of weight row (16*tile + l%16), so one instruction
-//    covers 16 rows x 64 contiguous bytes and no repacking is needed.
+//  * Every weight byte is read from HBM exactly once, with contiguous 16-byte
+//    loads (whole 128-byte lines per row where the shape allows) and the
+//    non-temporal hint.
 //  * The activations are fp32. Each is split exactly into two bf16 terms,
-//    x = hi + lo + O(2^-17 |x|), and both terms enter the A operand, so the
-//    product keeps ~16 bits of the activation against the bf16 weight and
-//    accumulates in fp32. For M <= 8 the hi and lo rows share one 16-row A
-//    block (rows 0..7 hi, 8..15 lo): one MFMA per 1 KB of weights.
-//    The A fragments of a K-chunk sit in LDS, built once per chunk by the
-//    whole workgroup.
-//  * With M <= 16 the MFMA work per weight byte is tiny (an MFMA per KB),
-//    so the kernel is bound by HBM: the design goal is bytes in flight.
-//    Each wave keeps two stages of 8 outstanding 16-byte loads per lane.
-//  * Work split: 16-row tiles are dealt to workgroups in contiguous ranges.
-//    When there are few tiles (small N), a tile's K range is split over S
-//    waves of one workgroup in 64-element granules (granule q goes to
-//    segment q mod S) and the S partial tiles are added in LDS in a fixed
-//    order. The summation order of an output depends on (K, S) only, never
-//    on M or on the tile's position, so equal weight rows give bit-equal
-//    outputs and a row's result does not depend on the other rows.
+//    x = hi + lo + O(2^-17 |x|), and both terms enter the A operand of
+//    v_mfma_f32_16x16x32_bf16 against the bf16 weights, accumulating in
+//    fp32. The expected logit error is ~1e-5. For M <= 8 the hi and lo rows
+//    share one 16-row A block (rows 0..7 hi, 8..15 lo): one MFMA per 1 KB of
+//    weights.
+//  * Three kernels, chosen by shape:
+//      - gemv_short_kernel: M <= 16, at most two 16-row tiles per workgroup
+//        (the projections of a draft layer): the shortest dependency chain.
+//      - gemv_tstream_kernel: M <= 16, many tiles per workgroup (the
+//        lm_heads): K split over 16 waves, two tiles of loads in flight,
+//        outputs summed in LDS and written once per chunk of tiles.
+//      - gemv_mrows_kernel: 16 < M <= 80 per launch (batched requests): a
+//        small GEMM streaming K chunks of weights and A through LDS.
+//  * Summation order depends on the shape only (never on timing), so reruns
+//    are bit-identical; for M <= 16 an output row does not depend on the
+//    other rows, and equal weight rows give equal outputs.
 #include "dspark_internal.h"
 
 #include <algorithm>
@@ -42,199 +41,8 @@ struct GemvParams {
   float* Y;
   int N, K, M;   // M rows in this launch
   int ldy;       // row stride of Y
-  int S;         // K segments per tile
-  int KG;        // 64-element granules in K
-  int KGC;       // granules per LDS chunk
-  int tiles;     // ceil(N / 16)
   int chunk;     // gemv_tstream_kernel: tiles whose outputs are staged in LDS at once (even)
 };
-
-template <int NA, bool PACK, int NW, int TB>
-__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvParams p) {
-  constexpr int F = PACK ? 1 : 2 * NA;           // A fragments per k-block (= accumulators per tile)
-  constexpr int GU = TB >= 4 ? 1 : 4 / TB;       // granules per pipeline stage
-  extern __shared__ __align__(16) unsigned char smem[];
-  u32x4* Alds = reinterpret_cast<u32x4*>(smem);  // [KGC*2][F][64]
-  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(p.KGC) * 2 * F * kWave * 16);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
-  const int S = p.S, P = NW / S, pw = w / S, s = w - pw * S;
-  const int N = p.N, K = p.K, M = p.M, KGC = p.KGC, KG = p.KG;
-  const int nchunks = (KG + KGC - 1) / KGC;
-
-  const int t0 = static_cast<int>((static_cast<long long>(blockIdx.x) * p.tiles) / gridDim.x);
-  const int t1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * p.tiles) / gridDim.x);
-  const int per_round = P * TB;
-  const int rounds = (t1 - t0 + per_round - 1) / per_round;
-
-  for (int rd = 0; rd < rounds; ++rd) {
-    int tile[TB];
-    bool tvalid[TB];
-    const uint16_t* wrow[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      tile[tb] = t0 + (rd * P + pw) * TB + tb;
-      tvalid[tb] = tile[tb] < t1;
-      const int row = min(tile[tb] * 16 + i, N - 1);  // out-of-range rows read a valid row, never stored
-      wrow[tb] = p.W + static_cast<size_t>(row) * K + 8 * g;
-    }
-    f32x4 acc[TB][F];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int f = 0; f < F; ++f) acc[tb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = 0; c < nchunks; ++c) {
-      const int q0 = c * KGC, q1 = min(KG, q0 + KGC);
-      if (nchunks > 1 || rd == 0) {
-        if (!(rd == 0 && c == 0)) __syncthreads();  // previous chunk fully consumed
-        // Build the A fragments of granules [q0, q1): entry e = (kbl*F + f)*64 + lane.
-        const int nent = (q1 - q0) * 2 * F * kWave;
-        for (int e = tid; e < nent; e += NW * kWave) {
-          const int ln = e & 63, fk = e >> 6, f = fk % F, kbl = fk / F;
-          const int ii = ln & 15, gg = ln >> 4;
-          const int k = (q0 * 2 + kbl) * 32 + 8 * gg;
-          int m, half;
-          if (PACK) {
-            m = ii & 7;
-            half = ii >> 3;
-          } else {
-            m = 16 * (f >> 1) + ii;
-            half = f & 1;
-          }
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (m < M && k < K) {
-            const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
-            const float4 x0 = xp[0], x1 = xp[1];
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint32_t hb[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const uint32_t h = bf16_bits_rne(xs[j]);
-              hb[j] = half ? bf16_bits_rne(xs[j] - bf16_bits_to_f32(h)) : h;
-            }
-            v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                      hb[6] | (hb[7] << 16)};
-          }
-          Alds[e] = v;
-        }
-        __syncthreads();
-      }
-
-      // This wave's granules of the chunk: q = qs + j*S, j < nq.
-      const int qs = q0 + ((s - q0 % S) % S + S) % S;
-      const int nq = qs < q1 ? (q1 - qs + S - 1) / S : 0;
-
-      auto load_stage = [&](u32x4 (&buf)[GU][TB][2], int j0) {
-#pragma unroll
-        for (int u = 0; u < GU; ++u) {
-          const int j = j0 + u;
-          const int q = qs + j * S;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int kk = (2 * q + h) * 32;
-            const bool ok = (j < nq) && (kk + 8 * g < K);
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-              buf[u][tb][h] = ok ? load16_stream(wrow[tb] + kk) : u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      };
-      auto compute_stage = [&](u32x4 (&buf)[GU][TB][2], int j0) {
-#pragma unroll
-        for (int u = 0; u < GU; ++u) {
-          const int j = j0 + u;
-          if (j < nq) {
-            const int ql = qs + j * S - q0;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-              for (int f = 0; f < F; ++f) {
-                const u32x4 av = Alds[((ql * 2 + h) * F + f) * kWave + lane];
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) acc[tb][f] = mfma_16x16x32(av, buf[u][tb][h], acc[tb][f]);
-              }
-            }
-          }
-        }
-      };
-
-      u32x4 bufA[GU][TB][2], bufB[GU][TB][2];
-      load_stage(bufA, 0);
-      for (int j0 = 0; j0 < nq; j0 += 2 * GU) {
-        load_stage(bufB, j0 + GU);
-        compute_stage(bufA, j0);
-        load_stage(bufA, j0 + 2 * GU);
-        compute_stage(bufB, j0 + GU);
-      }
-    }
-
-    // ---- epilogue: y = (sum of hi products) + (sum of lo products)
-    if (S == 1) {
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        if (!tvalid[tb]) continue;
-        const int n = tile[tb] * 16 + i;
-        if (PACK) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float lo = __shfl_down(acc[tb][0][v], 32);
-            const int m = 4 * g + v;
-            if (g < 2 && m < M && n < N) p.Y[static_cast<size_t>(m) * p.ldy + n] = acc[tb][0][v] + lo;
-          }
-        } else {
-#pragma unroll
-          for (int a = 0; a < NA; ++a)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int m = 16 * a + 4 * g + v;
-              if (m < M && n < N)
-                p.Y[static_cast<size_t>(m) * p.ldy + n] = acc[tb][2 * a][v] + acc[tb][2 * a + 1][v];
-            }
-        }
-      }
-    } else {
-      // Partial tiles of the S segments -> LDS, then a fixed-order sum.
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int f = 0; f < F; ++f)
-          reinterpret_cast<f32x4*>(red)[((w * TB + tb) * F + f) * kWave + lane] = acc[tb][f];
-      __syncthreads();
-      constexpr int ROWS = PACK ? 8 : 16 * NA;
-      const int items = P * TB * ROWS * 16;
-      for (int it = tid; it < items; it += NW * kWave) {
-        const int col = it & 15;
-        const int rest = it >> 4;
-        const int m = rest % ROWS;
-        const int tb = (rest / ROWS) % TB;
-        const int pp = rest / (ROWS * TB);
-        const int t = t0 + (rd * P + pp) * TB + tb;
-        const int n = t * 16 + col;
-        if (t >= t1 || m >= M || n >= N) continue;
-        int fh, fl, rh, rl;
-        if (PACK) {
-          fh = fl = 0;
-          rh = m;
-          rl = m + 8;
-        } else {
-          fh = 2 * (m >> 4);
-          fl = fh + 1;
-          rh = rl = m & 15;
-        }
-        float hi = 0.f, lo = 0.f;
-        for (int ss = 0; ss < S; ++ss) {
-          const int wv = pp * S + ss;
-          hi += red[(((wv * TB + tb) * F + fh) * kWave + 16 * (rh >> 2) + col) * 4 + (rh & 3)];
-          lo += red[(((wv * TB + tb) * F + fl) * kWave + 16 * (rl >> 2) + col) * 4 + (rl & 3)];
-        }
-        p.Y[static_cast<size_t>(m) * p.ldy + n] = hi + lo;
-      }
-      __syncthreads();
-    }
-  }
-}
 
 // Short variant for M <= 16: at most two 16-row tiles per workgroup (the
 // small projections of a draft layer). It follows the same plan as
@@ -362,6 +170,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
         if (m < M && k < K) {
           const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
           const float4 x0 = xp[0], x1 = xp[1];
+          // (software rounding: the same nearest-even split as split_bf16x2,
+          // in fewer registers, which this kernel is short of)
           const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           uint32_t hb[8];
 #pragma unroll
@@ -501,15 +311,10 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
         for (int f = 0; f < F; ++f) {
           const int half = PACK ? (i >> 3) : f;
           const float4 x0 = xr[kk][f][0], x1 = xr[kk][f][1];
-          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          uint32_t hb[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t hv = bf16_bits_rne(xs[e]);
-            hb[e] = half ? bf16_bits_rne(xs[e] - bf16_bits_to_f32(hv)) : hv;
-          }
-          afr[k0 + kk][f] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                                  hb[6] | (hb[7] << 16)};
+          const uint2 s0 = split_bf16x2(x0.x, x0.y), s1 = split_bf16x2(x0.z, x0.w);
+          const uint2 s2 = split_bf16x2(x1.x, x1.y), s3 = split_bf16x2(x1.z, x1.w);
+          const u32x4 h = {s0.x, s1.x, s2.x, s3.x}, l = {s0.y, s1.y, s2.y, s3.y};
+          afr[k0 + kk][f] = half ? l : h;
         }
     }
   };
@@ -619,99 +424,199 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
   }
 }
 
+// Medium-M variant, 16 < M <= 80 (the batched lm_head of several requests):
+// a small GEMM. With the hi/lo split the A side has 2M rows, too many to
+// keep per wave, so the workgroup streams K in chunks through LDS: a chunk
+// holds 128 weight rows and all 2M A rows (hi parts in rows 0..M-1, lo parts
+// in rows M..2M-1), each 4 k-blocks long. Eight waves split the
+// 8 x ceil(M/8) output tiles of the workgroup 4 x 2 (32 weight rows by half
+// the A blocks), so each B fragment read from LDS feeds up to 5 MFMAs and
+// each A fragment 2, which keeps LDS traffic under its bandwidth at the HBM
+// rate and the registers of a wave under 256.
+// Loads run two chunks ahead in registers (weights first, then X, in the
+// order they are consumed), and there is no global store before the end, so
+// the compiler never drains the prefetch. The output tile is assembled in
+// LDS and y = hi + lo is written row by row.
+constexpr int kMrRows = 128;                    // weight rows per workgroup
+constexpr int kMrKC = 4;                        // k-blocks per K chunk
+constexpr int kMrStride = kMrKC * 64 + 16;      // bytes per LDS row of a chunk (padded)
+constexpr int kMrMaxM = 80;                     // activation rows per launch
+constexpr int kMrWaves = 8;
+constexpr int kMrThreads = kMrWaves * kWave;
+constexpr int kMrBQ = kMrRows * 16 / kMrThreads;                 // weight loads per thread per chunk
+constexpr int kMrAQ = (kMrMaxM * 32 + kMrThreads - 1) / kMrThreads;  // X float4 loads per thread per chunk
+
+template <int MB2>
+__global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int M = p.M, N = p.N, K = p.K;
+  const int MB = (2 * M + 15) / 16;  // 16-row A blocks
+  const int arows = 16 * MB;
+  const int bufbytes = (kMrRows + arows) * kMrStride;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int ng = w & 3, mg = w >> 2;  // 32-row weight group, A block group
+  const int mb0 = mg == 0 ? 0 : (MB + 1) / 2;
+  const int nmb = mg == 0 ? (MB + 1) / 2 : MB / 2;
+  const int n0 = blockIdx.x * kMrRows;
+  const int nrows = min(kMrRows, N - n0);
+  const int nchunks = (K + 32 * kMrKC - 1) / (32 * kMrKC);
+  const uint32_t rowb = static_cast<uint32_t>(K) * 2;
+  const BufRes wres = buf_res(p.W + static_cast<size_t>(n0) * K, static_cast<uint32_t>(nrows) * rowb);
+  const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+
+  // Rows of the last A block past 2M stay zero in both buffers.
+  for (int e = tid; e < (arows - 2 * M) * kMrStride / 16; e += kMrThreads) {
+    const int off = (kMrRows + 2 * M) * kMrStride + 16 * e;
+    *reinterpret_cast<u32x4*>(smem + off) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(smem + bufbytes + off) = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Chunk c: weight piece q of thread t is row 32q + t/16, bytes 16*(t%16) of
+  // the chunk; X float4 q is f = t + 512q: row f/32, floats 4*(f%32).
+  // Anything past N, K, M or the last chunk reads zeros.
+  const int brow = tid >> 4, bpc = tid & 15;
+  u32x4 bq[2][kMrBQ];
+  float4 aq[2][kMrAQ];
+  auto issue = [&](int set, int c) {
+    const int kc = 32 * kMrKC * c;
+    const int kb = kc + 8 * bpc;
+#pragma unroll
+    for (int q = 0; q < kMrBQ; ++q) {
+      const uint32_t off = c < nchunks && kb < K
+                               ? static_cast<uint32_t>(32 * q + brow) * rowb + static_cast<uint32_t>(kb) * 2
+                               : kBufOutOfRange;
+      bq[set][q] = buf_load16_nt(wres, off);
+    }
+#pragma unroll
+    for (int q = 0; q < kMrAQ; ++q) {
+      const int f = tid + kMrThreads * q, m = f >> 5, k = kc + 4 * (f & 31);
+      const uint32_t off =
+          c < nchunks && m < M && k < K ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
+      aq[set][q] = buf_load_f32x4(xres, off);
+    }
+  };
+  // Register set -> LDS buffer b; X is split into its bf16 hi and lo rows.
+  auto stage = [&](int set, int b) {
+    unsigned char* Bs = smem + b * bufbytes;
+    unsigned char* As = Bs + kMrRows * kMrStride;
+#pragma unroll
+    for (int q = 0; q < kMrBQ; ++q)
+      *reinterpret_cast<u32x4*>(Bs + (32 * q + brow) * kMrStride + 16 * bpc) = bq[set][q];
+#pragma unroll
+    for (int q = 0; q < kMrAQ; ++q) {
+      const int f = tid + kMrThreads * q, m = f >> 5, col = f & 31;
+      if (m < M) {
+        const float4 x = aq[set][q];
+        const uint2 s0 = split_bf16x2(x.x, x.y), s1 = split_bf16x2(x.z, x.w);
+        *reinterpret_cast<uint2*>(As + m * kMrStride + 8 * col) = uint2{s0.x, s1.x};
+        *reinterpret_cast<uint2*>(As + (M + m) * kMrStride + 8 * col) = uint2{s0.y, s1.y};
+      }
+    }
+  };
+  f32x4 acc[2][MB2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mb = 0; mb < MB2; ++mb) acc[nt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int b) {
+    const unsigned char* Bs = smem + b * bufbytes + (32 * ng + i) * kMrStride + 16 * g;
+    const unsigned char* As = smem + b * bufbytes + (kMrRows + 16 * mb0 + i) * kMrStride + 16 * g;
+#pragma unroll
+    for (int kb = 0; kb < kMrKC; ++kb) {
+      u32x4 bf[2], af[MB2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) bf[nt] = *reinterpret_cast<const u32x4*>(Bs + 16 * nt * kMrStride + 64 * kb);
+#pragma unroll
+      for (int mb = 0; mb < MB2; ++mb)
+        af[mb] = mb < nmb ? *reinterpret_cast<const u32x4*>(As + 16 * mb * kMrStride + 64 * kb)
+                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int mb = 0; mb < MB2; ++mb)
+        if (mb < nmb)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt][mb] = mfma_16x16x32(af[mb], bf[nt], acc[nt][mb]);
+    }
+  };
+
+  // Chunk j lives in register set j%2 and LDS buffer j%2; two chunks are in
+  // flight while one is computed. Two chunks per iteration and a single exit
+  // (an odd count computes one chunk of zeros at the end).
+  issue(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  stage(0, 0);
+  issue(0, 2);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    compute(0);
+    stage(1, 1);
+    issue(1, c + 3);
+    __syncthreads();
+    compute(1);
+    stage(0, 0);
+    issue(0, c + 4);
+    __syncthreads();
+  }
+
+  // Output tile [2M x 128] in LDS, then y[m] = hi row m + lo row M+m.
+  float* L = reinterpret_cast<float*>(smem);  // [arows][kMrRows]
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mb = 0; mb < MB2; ++mb)
+      if (mb < nmb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          L[(16 * (mb0 + mb) + 4 * g + v) * kMrRows + 32 * ng + 16 * nt + i] = acc[nt][mb][v];
+  __syncthreads();
+  for (int e = tid; e < M * kMrRows; e += kMrThreads) {
+    const int m = e / kMrRows, col = e - m * kMrRows;
+    if (col < nrows) p.Y[static_cast<size_t>(m) * p.ldy + n0 + col] = L[m * kMrRows + col] + L[(M + m) * kMrRows + col];
+  }
+}
+
 struct Plan {
-  int tkbw;     // gemv_tstream_kernel / gemv_short_kernel k-blocks per wave (0: neither)
+  int tkbw;     // k-blocks per wave
+  bool pack;    // M <= 8: hi and lo rows share one A block
   bool shortk;  // gemv_short_kernel (at most two tiles per workgroup)
   int chunk;    // gemv_tstream_kernel tiles per LDS output chunk
-  int NA;
-  bool pack;
-  int NW;
-  int TB;
-  int S;
-  int KGC;
   int grid;
   size_t lds;
 };
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
+// M <= 16: K slices of 32*KBW per wave, phases for longer K. Workgroups with
+// at most two tiles take the short kernel (up to 8 k-blocks per wave with
+// packed rows); longer ones the LDS-staged streaming kernel, whose registers
+// allow 4.
 Plan make_plan(int M, int N, int K, int cus) {
   Plan pl{};
-  if (M <= 8) {
-    pl.NA = 1, pl.pack = true, pl.NW = 16;
-  } else if (M <= 16) {
-    pl.NA = 1, pl.pack = false, pl.NW = 16;
-  } else {
-    pl.NA = (M + 15) / 16, pl.pack = false, pl.NW = 8;
-  }
-  const int F = pl.pack ? 1 : 2 * pl.NA;
-  const int tiles = (N + 15) / 16, KG = (K + 63) / 64;
-  if (M <= 16) {
-    // K slices of 32*KBW per wave, phases for longer K. Workgroups with at
-    // most two tiles take the short kernel (up to 8 k-blocks per wave with
-    // packed rows); longer ones the LDS-staged streaming kernel, whose
-    // registers allow 4.
-    const int KB = (K + 31) / 32;
-    pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
-    const int rows_max = 2 * ((N / 2 + pl.grid - 1) / pl.grid) + 1;  // rows of the largest workgroup
-    const int rounds = (rows_max + 15) / 16;
-    pl.shortk = rounds <= 2;
-    const int kbw_max = pl.shortk && pl.pack ? 8 : 4;
-    int kbw = 1;
-    while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
-    pl.tkbw = kbw;
-    pl.S = 16;
-    pl.TB = 1;
-    pl.KGC = KG;
-    const int rows = pl.pack ? 8 : 16;
-    const size_t fixed = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
-    if (pl.shortk) {
-      pl.chunk = 0;
-      pl.lds = fixed;
-      return pl;
-    }
-    const size_t per_tile = static_cast<size_t>(M) * 16 * 4;
-    int chunk = static_cast<int>((kLdsBytes - fixed) / per_tile) & ~1;
-    chunk = std::max(2, std::min(chunk, (rounds + 1) & ~1));
-    pl.chunk = chunk;
-    pl.lds = fixed + chunk * per_tile;
+  pl.pack = M <= 8;
+  const int tiles = (N + 15) / 16;
+  const int KB = (K + 31) / 32;
+  pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
+  const int rows_max = 2 * ((N / 2 + pl.grid - 1) / pl.grid) + 1;  // rows of the largest workgroup
+  const int rounds = (rows_max + 15) / 16;
+  pl.shortk = rounds <= 2;
+  const int kbw_max = pl.shortk && pl.pack ? 8 : 4;
+  int kbw = 1;
+  while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
+  pl.tkbw = kbw;
+  const int rows = pl.pack ? 8 : 16;
+  const size_t fixed = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
+  if (pl.shortk) {
+    pl.chunk = 0;
+    pl.lds = fixed;
     return pl;
   }
-  const int cap = cus * pl.NW;
-  int S = 1;
-  if (2 * tiles < cap)
-    while (S < pl.NW && S < KG && tiles * S < cap) S *= 2;
-  pl.S = S;
-  const int P = pl.NW / S;
-  const size_t gran = static_cast<size_t>(2) * F * kWave * 16;
-  const size_t red1 = S > 1 ? static_cast<size_t>(pl.NW) * F * kWave * 16 : 0;
-  if (static_cast<size_t>(KG) * gran + red1 <= kLdsBytes) {
-    pl.TB = 1;
-    pl.KGC = KG;
-    pl.grid = std::min(cus, (tiles + P - 1) / P);
-    pl.lds = KG * gran + red1;
-    return pl;
-  }
-  const int tbmax = F <= 2 ? 4 : 1;
-  int tb = (tiles + P * cus - 1) / (P * cus);
-  tb = tb <= 1 ? 1 : (tb <= 2 ? 2 : 4);
-  pl.TB = std::min(tb, tbmax);
-  const size_t red = S > 1 ? static_cast<size_t>(pl.NW) * pl.TB * F * kWave * 16 : 0;
-  pl.KGC = std::max<int>(1, static_cast<int>((kLdsBytes - red) / gran));
-  pl.grid = (tiles + P * pl.TB - 1) / (P * pl.TB);
-  pl.lds = pl.KGC * gran + red;
+  const size_t per_tile = static_cast<size_t>(M) * 16 * 4;
+  int chunk = static_cast<int>((kLdsBytes - fixed) / per_tile) & ~1;
+  chunk = std::max(2, std::min(chunk, (rounds + 1) & ~1));
+  pl.chunk = chunk;
+  pl.lds = fixed + chunk * per_tile;
   return pl;
-}
-
-template <int NA, bool PACK, int NW, int TB>
-hipError_t launch_inst(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<NA, PACK, NW, TB>);
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
-  if (attr != hipSuccess) return attr;
-  GemvParams a = prm;
-  void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3(pl.grid), dim3(NW * kWave), args, pl.lds, st);
 }
 
 template <bool PACK, int KBW>
@@ -772,15 +677,20 @@ hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
       default: return launch_tstream<false, 4>(prm, pl, st);
     }
   }
-  switch (pl.NA) {
-    case 2: return launch_inst<2, false, 8, 1>(prm, pl, st);
-    case 3: return launch_inst<3, false, 8, 1>(prm, pl, st);
-    case 4: return launch_inst<4, false, 8, 1>(prm, pl, st);
-    case 5: return launch_inst<5, false, 8, 1>(prm, pl, st);
-    case 6: return launch_inst<6, false, 8, 1>(prm, pl, st);
-    case 7: return launch_inst<7, false, 8, 1>(prm, pl, st);
-    default: return launch_inst<8, false, 8, 1>(prm, pl, st);
-  }
+  return hipErrorInvalidValue;
+}
+
+template <int MB2>
+hipError_t launch_mrows(const GemvParams& prm, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_mrows_kernel<MB2>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (attr != hipSuccess) return attr;
+  const int arows = 16 * ((2 * prm.M + 15) / 16);
+  const size_t lds = 2 * static_cast<size_t>(kMrRows + arows) * kMrStride;
+  GemvParams a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3((prm.N + kMrRows - 1) / kMrRows), dim3(kMrThreads), args, lds, st);
 }
 
 }  // namespace
@@ -789,24 +699,33 @@ hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, f
                        hipStream_t stream) {
   const int cus = device_cu_count();
   if (cus <= 0) return hipErrorNoDevice;
-  constexpr int kMaxRows = 128;  // 8 row groups of 16 per launch
-  for (int m0 = 0; m0 < M; m0 += kMaxRows) {
-    const int mc = std::min(kMaxRows, M - m0);
-    const Plan pl = make_plan(mc, N, K, cus);
-    GemvParams prm{};
-    prm.W = W;
+  GemvParams prm{};
+  prm.W = W;
+  prm.N = N;
+  prm.K = K;
+  prm.ldy = N;
+  if (M <= 16) {
+    const Plan pl = make_plan(M, N, K, cus);
+    prm.X = X;
+    prm.Y = Y;
+    prm.M = M;
+    prm.chunk = pl.chunk;
+    return dispatch(prm, pl, stream);
+  }
+  // More rows: balanced parts of at most kMrMaxM rows (each above 16).
+  const int parts = (M + kMrMaxM - 1) / kMrMaxM;
+  for (int part = 0; part < parts; ++part) {
+    const int m0 = M * part / parts, mc = M * (part + 1) / parts - m0;
     prm.X = X + static_cast<size_t>(m0) * K;
     prm.Y = Y + static_cast<size_t>(m0) * N;
-    prm.N = N;
-    prm.K = K;
     prm.M = mc;
-    prm.ldy = N;
-    prm.S = pl.S;
-    prm.KG = (K + 63) / 64;
-    prm.KGC = pl.KGC;
-    prm.tiles = (N + 15) / 16;
-    prm.chunk = pl.chunk;
-    const hipError_t e = dispatch(prm, pl, stream);
+    hipError_t e;
+    switch (((mc + 7) / 8 + 1) / 2) {
+      case 2: e = launch_mrows<2>(prm, stream); break;
+      case 3: e = launch_mrows<3>(prm, stream); break;
+      case 4: e = launch_mrows<4>(prm, stream); break;
+      default: e = launch_mrows<5>(prm, stream); break;
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
