@@ -31,6 +31,7 @@
 #include "dspark_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dspark {
 namespace {
@@ -450,13 +451,13 @@ template <int MB2>
 __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int M = p.M, N = p.N, K = p.K;
-  const int MB = (2 * M + 15) / 16;  // 16-row A blocks
-  const int arows = 16 * MB;
-  const int bufbytes = (kMrRows + arows) * kMrStride;
+  // 2*MB2 A blocks of 16 rows (rows past 2M are zero), MB2 per wave group,
+  // then one scratch row that takes the writes of lanes past M.
+  constexpr int arows = 32 * MB2;
+  constexpr int bufbytes = (kMrRows + arows + 1) * kMrStride;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
   const int ng = w & 3, mg = w >> 2;  // 32-row weight group, A block group
-  const int mb0 = mg == 0 ? 0 : (MB + 1) / 2;
-  const int nmb = mg == 0 ? (MB + 1) / 2 : MB / 2;
+  const int mb0 = mg * MB2;
   const int n0 = blockIdx.x * kMrRows;
   const int nrows = min(kMrRows, N - n0);
   const int nchunks = (K + 32 * kMrKC - 1) / (32 * kMrKC);
@@ -475,8 +476,8 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   // the chunk; X float4 q is f = t + 512q: row f/32, floats 4*(f%32).
   // Anything past N, K, M or the last chunk reads zeros.
   const int brow = tid >> 4, bpc = tid & 15;
-  u32x4 bq[2][kMrBQ];
-  float4 aq[2][kMrAQ];
+  u32x4 bq[3][kMrBQ];
+  float4 aq[3][kMrAQ];
   auto issue = [&](int set, int c) {
     const int kc = 32 * kMrKC * c;
     const int kb = kc + 8 * bpc;
@@ -505,12 +506,11 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
 #pragma unroll
     for (int q = 0; q < kMrAQ; ++q) {
       const int f = tid + kMrThreads * q, m = f >> 5, col = f & 31;
-      if (m < M) {
-        const float4 x = aq[set][q];
-        const uint2 s0 = split_bf16x2(x.x, x.y), s1 = split_bf16x2(x.z, x.w);
-        *reinterpret_cast<uint2*>(As + m * kMrStride + 8 * col) = uint2{s0.x, s1.x};
-        *reinterpret_cast<uint2*>(As + (M + m) * kMrStride + 8 * col) = uint2{s0.y, s1.y};
-      }
+      const float4 x = aq[set][q];
+      const uint2 s0 = split_bf16x2(x.x, x.y), s1 = split_bf16x2(x.z, x.w);
+      const int rh = m < M ? m : arows, rl = m < M ? M + m : arows;  // no branch: scratch row
+      *reinterpret_cast<uint2*>(As + rh * kMrStride + 8 * col) = uint2{s0.x, s1.x};
+      *reinterpret_cast<uint2*>(As + rl * kMrStride + 8 * col) = uint2{s0.y, s1.y};
     }
   };
   f32x4 acc[2][MB2];
@@ -527,37 +527,56 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) bf[nt] = *reinterpret_cast<const u32x4*>(Bs + 16 * nt * kMrStride + 64 * kb);
 #pragma unroll
-      for (int mb = 0; mb < MB2; ++mb)
-        af[mb] = mb < nmb ? *reinterpret_cast<const u32x4*>(As + 16 * mb * kMrStride + 64 * kb)
-                          : u32x4{0u, 0u, 0u, 0u};
+      for (int mb = 0; mb < MB2; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(As + 16 * mb * kMrStride + 64 * kb);
 #pragma unroll
       for (int mb = 0; mb < MB2; ++mb)
-        if (mb < nmb)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[nt][mb] = mfma_16x16x32(af[mb], bf[nt], acc[nt][mb]);
+        for (int nt = 0; nt < 2; ++nt) acc[nt][mb] = mfma_16x16x32(af[mb], bf[nt], acc[nt][mb]);
     }
   };
 
-  // Chunk j lives in register set j%2 and LDS buffer j%2; two chunks are in
-  // flight while one is computed. Two chunks per iteration and a single exit
-  // (an odd count computes one chunk of zeros at the end).
+  // Chunk j lives in register set j%3 and LDS buffer j%2: three chunks are
+  // in flight while one is computed. Step j of an iteration stages chunk
+  // c+j+1, computes chunk c+j and issues chunk c+j+4 into the set just
+  // freed, all straight code so that the conversion and LDS writes of one
+  // chunk interleave with the MFMAs of the other; six steps per iteration
+  // keep every index static, and the main loop has a single exit (the tail
+  // after it may wait more conservatively).
+  auto step = [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    stage((j + 1) % 3, (j + 1) % 2);
+    compute(j % 2);
+    return j;
+  };
   issue(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   issue(1, 1);
   __builtin_amdgcn_sched_barrier(0);
+  issue(2, 2);
+  __builtin_amdgcn_sched_barrier(0);
   stage(0, 0);
-  issue(0, 2);
+  issue(0, 3);
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    compute(0);
-    stage(1, 1);
-    issue(1, c + 3);
-    __syncthreads();
-    compute(1);
-    stage(0, 0);
-    issue(0, c + 4);
-    __syncthreads();
+  int c = 0;
+#define DSPARK_MR_STEP(J)                                        \
+  step(std::integral_constant<int, J>{});                        \
+  issue((J + 1) % 3, c + J + 4);                                 \
+  __syncthreads();
+  for (; c + 6 <= nchunks; c += 6) {
+    DSPARK_MR_STEP(0)
+    DSPARK_MR_STEP(1)
+    DSPARK_MR_STEP(2)
+    DSPARK_MR_STEP(3)
+    DSPARK_MR_STEP(4)
+    DSPARK_MR_STEP(5)
   }
+  const int rest = nchunks - c;
+  if (rest > 0) { DSPARK_MR_STEP(0) }
+  if (rest > 1) { DSPARK_MR_STEP(1) }
+  if (rest > 2) { DSPARK_MR_STEP(2) }
+  if (rest > 3) { DSPARK_MR_STEP(3) }
+  if (rest > 4) { DSPARK_MR_STEP(4) }
+#undef DSPARK_MR_STEP
 
   // Output tile [2M x 128] in LDS, then y[m] = hi row m + lo row M+m.
   float* L = reinterpret_cast<float*>(smem);  // [arows][kMrRows]
@@ -565,7 +584,6 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int mb = 0; mb < MB2; ++mb)
-      if (mb < nmb)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           L[(16 * (mb0 + mb) + 4 * g + v) * kMrRows + 32 * ng + 16 * nt + i] = acc[nt][mb][v];
@@ -686,8 +704,7 @@ hipError_t launch_mrows(const GemvParams& prm, hipStream_t st) {
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
-  const int arows = 16 * ((2 * prm.M + 15) / 16);
-  const size_t lds = 2 * static_cast<size_t>(kMrRows + arows) * kMrStride;
+  const size_t lds = 2 * static_cast<size_t>(kMrRows + 32 * MB2 + 1) * kMrStride;
   GemvParams a = prm;
   void* args[] = {&a};
   return hipLaunchKernel(fn, dim3((prm.N + kMrRows - 1) / kMrRows), dim3(kMrThreads), args, lds, st);
