@@ -449,12 +449,15 @@ constexpr int kMrAQ = (kMrMaxM * 32 + kMrThreads - 1) / kMrThreads;  // X float4
 
 template <int MB2>
 __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int M = p.M, N = p.N, K = p.K;
   // 2*MB2 A blocks of 16 rows (rows past 2M are zero), MB2 per wave group,
-  // then one scratch row that takes the writes of lanes past M.
+  // then one scratch row that takes the writes of lanes past M. The two
+  // chunk buffers are separate arrays, so the compiler can see that staging
+  // one never touches what the MFMAs read from the other.
   constexpr int arows = 32 * MB2;
   constexpr int bufbytes = (kMrRows + arows + 1) * kMrStride;
+  __shared__ __align__(16) unsigned char lds0[bufbytes];
+  __shared__ __align__(16) unsigned char lds1[bufbytes];
+  const int M = p.M, N = p.N, K = p.K;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
   const int ng = w & 3, mg = w >> 2;  // 32-row weight group, A block group
   const int mb0 = mg * MB2;
@@ -468,19 +471,18 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   // Rows of the last A block past 2M stay zero in both buffers.
   for (int e = tid; e < (arows - 2 * M) * kMrStride / 16; e += kMrThreads) {
     const int off = (kMrRows + 2 * M) * kMrStride + 16 * e;
-    *reinterpret_cast<u32x4*>(smem + off) = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(smem + bufbytes + off) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds0 + off) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds1 + off) = u32x4{0u, 0u, 0u, 0u};
   }
 
   // Chunk c: weight piece q of thread t is row 32q + t/16, bytes 16*(t%16) of
   // the chunk; X float4 q is f = t + 512q: row f/32, floats 4*(f%32).
   // Anything past N, K, M or the last chunk reads zeros.
   const int brow = tid >> 4, bpc = tid & 15;
-  u32x4 bq[3][kMrBQ];
-  float4 aq[3][kMrAQ];
-  auto issue = [&](int set, int c) {
-    const int kc = 32 * kMrKC * c;
-    const int kb = kc + 8 * bpc;
+  u32x4 bq[3][kMrBQ];   // weights of chunk j: set j%3
+  float4 aq[2][kMrAQ];  // X of chunk j: set j%2 (from L2, so one chunk less ahead)
+  auto issue_b = [&](int set, int c) {
+    const int kb = 32 * kMrKC * c + 8 * bpc;
 #pragma unroll
     for (int q = 0; q < kMrBQ; ++q) {
       const uint32_t off = c < nchunks && kb < K
@@ -488,6 +490,9 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
                                : kBufOutOfRange;
       bq[set][q] = buf_load16_nt(wres, off);
     }
+  };
+  auto issue_a = [&](int set, int c) {
+    const int kc = 32 * kMrKC * c;
 #pragma unroll
     for (int q = 0; q < kMrAQ; ++q) {
       const int f = tid + kMrThreads * q, m = f >> 5, k = kc + 4 * (f & 31);
@@ -496,31 +501,41 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
       aq[set][q] = buf_load_f32x4(xres, off);
     }
   };
-  // Register set -> LDS buffer b; X is split into its bf16 hi and lo rows.
-  auto stage = [&](int set, int b) {
-    unsigned char* Bs = smem + b * bufbytes;
+  // Part `part` (of kMrKC) of moving register set -> LDS buffer b; X is
+  // split into its bf16 hi and lo rows.
+  auto stage_part = [&](int bset, int aset, int b, int part) {
+    unsigned char* Bs = b ? lds1 : lds0;
     unsigned char* As = Bs + kMrRows * kMrStride;
 #pragma unroll
     for (int q = 0; q < kMrBQ; ++q)
-      *reinterpret_cast<u32x4*>(Bs + (32 * q + brow) * kMrStride + 16 * bpc) = bq[set][q];
+      if (q % kMrKC == part) *reinterpret_cast<u32x4*>(Bs + (32 * q + brow) * kMrStride + 16 * bpc) = bq[bset][q];
 #pragma unroll
     for (int q = 0; q < kMrAQ; ++q) {
+      if (q % kMrKC != part) continue;
       const int f = tid + kMrThreads * q, m = f >> 5, col = f & 31;
-      const float4 x = aq[set][q];
+      const float4 x = aq[aset][q];
       const uint2 s0 = split_bf16x2(x.x, x.y), s1 = split_bf16x2(x.z, x.w);
       const int rh = m < M ? m : arows, rl = m < M ? M + m : arows;  // no branch: scratch row
       *reinterpret_cast<uint2*>(As + rh * kMrStride + 8 * col) = uint2{s0.x, s1.x};
       *reinterpret_cast<uint2*>(As + rl * kMrStride + 8 * col) = uint2{s0.y, s1.y};
     }
   };
+  auto stage = [&](int bset, int aset, int b) {
+#pragma unroll
+    for (int part = 0; part < kMrKC; ++part) stage_part(bset, aset, b, part);
+  };
   f32x4 acc[2][MB2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int mb = 0; mb < MB2; ++mb) acc[nt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int b) {
-    const unsigned char* Bs = smem + b * bufbytes + (32 * ng + i) * kMrStride + 16 * g;
-    const unsigned char* As = smem + b * bufbytes + (kMrRows + 16 * mb0 + i) * kMrStride + 16 * g;
+  // Computes the chunk in buffer b; part kb of staging register sets
+  // (bset, aset) into buffer 1-b is placed after each k-block, so the
+  // conversions and LDS writes sit between the MFMAs in program order.
+  auto compute_stage = [&](int b, int bset, int aset) {
+    const unsigned char* base = b ? lds1 : lds0;
+    const unsigned char* Bs = base + (32 * ng + i) * kMrStride + 16 * g;
+    const unsigned char* As = base + (kMrRows + 16 * mb0 + i) * kMrStride + 16 * g;
 #pragma unroll
     for (int kb = 0; kb < kMrKC; ++kb) {
       u32x4 bf[2], af[MB2];
@@ -532,35 +547,39 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
       for (int mb = 0; mb < MB2; ++mb)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[nt][mb] = mfma_16x16x32(af[mb], bf[nt], acc[nt][mb]);
+      stage_part(bset, aset, 1 - b, kb);
     }
   };
 
-  // Chunk j lives in register set j%3 and LDS buffer j%2: three chunks are
-  // in flight while one is computed. Step j of an iteration stages chunk
-  // c+j+1, computes chunk c+j and issues chunk c+j+4 into the set just
-  // freed, all straight code so that the conversion and LDS writes of one
-  // chunk interleave with the MFMAs of the other; six steps per iteration
-  // keep every index static, and the main loop has a single exit (the tail
-  // after it may wait more conservatively).
+  // Chunk j: weights in register set j%3, X in set j%2, LDS buffer j%2.
+  // While chunk j is computed, the weights of chunks j+1..j+3 and the X of
+  // j+1..j+2 are in flight. Step j stages chunk j+1 (interleaved with the
+  // MFMAs of chunk j), then issues X of chunk j+3 and weights of chunk j+4,
+  // in that order, so that each wait covers exactly the loads it needs.
+  // Six steps per iteration keep every index static; the main loop has a
+  // single exit (the tail after it may wait more conservatively).
   auto step = [&](auto J) {
     constexpr int j = decltype(J)::value;
-    stage((j + 1) % 3, (j + 1) % 2);
-    compute(j % 2);
+    compute_stage(j % 2, (j + 1) % 3, (j + 1) % 2);
     return j;
   };
-  issue(0, 0);
+  issue_a(0, 0);
+  issue_b(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  issue(1, 1);
+  issue_a(1, 1);
+  issue_b(1, 1);
   __builtin_amdgcn_sched_barrier(0);
-  issue(2, 2);
+  issue_b(2, 2);
   __builtin_amdgcn_sched_barrier(0);
-  stage(0, 0);
-  issue(0, 3);
+  stage(0, 0, 0);
+  issue_a(0, 2);
+  issue_b(0, 3);
   __syncthreads();
   int c = 0;
 #define DSPARK_MR_STEP(J)                                        \
   step(std::integral_constant<int, J>{});                        \
-  issue((J + 1) % 3, c + J + 4);                                 \
+  issue_a((J + 1) % 2, c + J + 3);                               \
+  issue_b((J + 1) % 3, c + J + 4);                               \
   __syncthreads();
   for (; c + 6 <= nchunks; c += 6) {
     DSPARK_MR_STEP(0)
@@ -578,19 +597,25 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   if (rest > 4) { DSPARK_MR_STEP(4) }
 #undef DSPARK_MR_STEP
 
-  // Output tile [2M x 128] in LDS, then y[m] = hi row m + lo row M+m.
-  float* L = reinterpret_cast<float*>(smem);  // [arows][kMrRows]
+  // Output tile [2M x 128] through LDS in two halves of 64 columns (one
+  // half fits in a chunk buffer), then y[m] = hi row m + lo row M+m.
+  float* L = reinterpret_cast<float*>(lds0);  // [arows][64]
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int half = 0; half < 2; ++half) {
+    if ((ng >> 1) == half)
 #pragma unroll
-    for (int mb = 0; mb < MB2; ++mb)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          L[(16 * (mb0 + mb) + 4 * g + v) * kMrRows + 32 * ng + 16 * nt + i] = acc[nt][mb][v];
-  __syncthreads();
-  for (int e = tid; e < M * kMrRows; e += kMrThreads) {
-    const int m = e / kMrRows, col = e - m * kMrRows;
-    if (col < nrows) p.Y[static_cast<size_t>(m) * p.ldy + n0 + col] = L[m * kMrRows + col] + L[(M + m) * kMrRows + col];
+        for (int mb = 0; mb < MB2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            L[(16 * (mb0 + mb) + 4 * g + v) * 64 + 32 * (ng & 1) + 16 * nt + i] = acc[nt][mb][v];
+    __syncthreads();
+    for (int e = tid; e < M * 64; e += kMrThreads) {
+      const int m = e >> 6, col = 64 * half + (e & 63);
+      if (col < nrows) p.Y[static_cast<size_t>(m) * p.ldy + n0 + col] = L[m * 64 + (e & 63)] + L[(M + m) * 64 + (e & 63)];
+    }
+    __syncthreads();
   }
 }
 
@@ -700,14 +725,10 @@ hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
 
 template <int MB2>
 hipError_t launch_mrows(const GemvParams& prm, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_mrows_kernel<MB2>);
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
-  if (attr != hipSuccess) return attr;
-  const size_t lds = 2 * static_cast<size_t>(kMrRows + 32 * MB2 + 1) * kMrStride;
+  const void* fn = reinterpret_cast<const void*>(&gemv_mrows_kernel<MB2>);  // static LDS only
   GemvParams a = prm;
   void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3((prm.N + kMrRows - 1) / kMrRows), dim3(kMrThreads), args, lds, st);
+  return hipLaunchKernel(fn, dim3((prm.N + kMrRows - 1) / kMrRows), dim3(kMrThreads), args, 0, st);
 }
 
 }  // namespace
