@@ -359,10 +359,11 @@ constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straig
 
 int reg_tiles(int KB) { return KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0); }
 
-LoopPlan make_loop_plan(int R, int V, int r, int cus) {
+// Plan for G workgroups (G <= min(tiles, kMaxGroups)).
+LoopPlan make_loop_plan(int R, int V, int r, int G) {
   LoopPlan pl{};
   const int tiles = (V + 15) / 16;
-  pl.G = std::max(1, std::min({cus, tiles, kMaxGroups}));
+  pl.G = G;
   const int kb = (r + 31) / 32;
   pl.KB = kb <= 1 ? 1 : kb <= 2 ? 2 : kb <= 4 ? 4 : kb <= 8 ? 8 : kb <= 16 ? 16 : 32;
   pl.RT = reg_tiles(pl.KB);
@@ -411,7 +412,13 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
                          int k, int64_t* ids, void* workspace, hipStream_t stream) {
   const int cus = device_cu_count();
   if (cus <= 0) return hipErrorNoDevice;
-  const LoopPlan pl = make_loop_plan(R, V, r, cus);
+  // Workgroups: one per CU, but at least ~16 tiles each. With fewer tiles a
+  // workgroup's step is all latency, and more workgroups only lengthen the
+  // exchange (measured: 32000 x 256 with 8 requests 74 -> 67 us per call at
+  // 128 instead of 256 workgroups; 4096 x 32 17 -> 14 us at 16).
+  const int tiles = (V + 15) / 16;
+  const int G = std::max(1, std::min({cus, kMaxGroups, (tiles + 15) / 16}));
+  const LoopPlan pl = make_loop_plan(R, V, r, G);
   MarkovParams prm{};
   prm.base = base;
   prm.w1 = w1;
@@ -427,7 +434,7 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.r = r;
   prm.k = k;
   prm.G = pl.G;
-  prm.tiles = (V + 15) / 16;
+  prm.tiles = tiles;
   prm.lds_tiles = pl.lds_tiles;
   prm.bstride = pl.bstride;
   prm.base_in_lds = pl.base_in_lds;
