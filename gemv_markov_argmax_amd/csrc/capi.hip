@@ -35,7 +35,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 dspark_status gemv_checks(const uint16_t* W, int N, int K, const float* X, int M, const float* Y) {
   if (!W || !X || !Y) return DSPARK_ERR_NULL;
-  if (N < 1 || K < 8 || (K % 8) != 0 || M < 1) return DSPARK_ERR_SHAPE;
+  if (N < 1 || K < 8 || (K % 8) != 0 || M < 1 || !dspark::gemv_shape_fits(N, K, M)) return DSPARK_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return DSPARK_ERR_ALIGN;
   return DSPARK_OK;
 }

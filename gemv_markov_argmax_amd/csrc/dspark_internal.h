@@ -70,6 +70,23 @@ __device__ __forceinline__ uint2 split_bf16x2(float a, float b) {
   return uint2{hi, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
 }
 
+// The packed A block (M <= 8) holds the hi parts of row m in lane i = m and
+// the lo parts in lane i = m + 8 of each 16-lane row, both over the same 8
+// activations. Each of the two lanes loads one half of them (lane i >> 3
+// picks which) and takes the other half from its partner i ^ 8 through DPP
+// row_ror:8, so the activations are read once rather than twice. Returns the
+// eight values in k order.
+__device__ __forceinline__ void pair_halves(float4 mine, int i, float4& x0, float4& x1) {
+  float4 other;
+  other.x = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mine.x), 0x128, 0xF, 0xF, false));
+  other.y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mine.y), 0x128, 0xF, 0xF, false));
+  other.z = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mine.z), 0x128, 0xF, 0xF, false));
+  other.w = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mine.w), 0x128, 0xF, 0xF, false));
+  const bool upper = (i >> 3) != 0;
+  x0 = upper ? other : mine;
+  x1 = upper ? mine : other;
+}
+
 // Round a finite float to bf16, nearest-even, returning the 16-bit pattern.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -118,6 +135,11 @@ __device__ __forceinline__ uint64_t row_max64(uint64_t v) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------
+
+// Whether the GEMV kernels can address this shape: every buffer range they
+// build (a workgroup's weight rows, the activation rows of a launch) must
+// stay below 2^31 bytes.
+bool gemv_shape_fits(int N, int K, int M);
 
 // Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,

@@ -43,34 +43,57 @@ struct GemvParams {
   int N, K, M;   // M rows in this launch
   int ldy;       // row stride of Y
   int chunk;     // gemv_tstream_kernel: tiles whose outputs are staged in LDS at once (even)
+  int pq, prem;  // row pairs per workgroup: N/2 = pq * gridDim.x + prem (the first prem get one more)
 };
 
+// Contiguous row range [r0, r1) of workgroup b: a balanced share of the N/2
+// row pairs (a load instruction covers 2 rows); the last workgroup also takes
+// an odd last row. Plain 32-bit arithmetic (the quotients come from the host).
+__device__ __forceinline__ int2 wg_rows(const GemvParams& p) {
+  const int b = blockIdx.x;
+  const int r0 = 2 * (b * p.pq + min(b, p.prem));
+  const int r1 = b + 1 == static_cast<int>(gridDim.x) ? p.N : 2 * ((b + 1) * p.pq + min(b + 1, p.prem));
+  return int2{r0, r1};
+}
+
+// Rows of the largest workgroup under wg_rows with `grid` workgroups.
+inline int wg_rows_max(int N, int grid) {
+  const int q = (N / 2) / grid, rem = (N / 2) % grid;
+  return std::max(2 * (q + (rem > 0 ? 1 : 0)), 2 * q + (N & 1));
+}
+
 // Short variant for M <= 16: at most two 16-row tiles per workgroup (the
-// small projections of a draft layer). It follows the same plan as
-// gemv_tstream_kernel below but with the shortest dependency chain: plain
-// guarded loads and a direct store of each output tile. (The store makes the
-// wave wait for every load in flight before its next tile, which only
-// matters when there are many tiles per workgroup.)
+// projections of a draft layer). Nothing is amortized over a long tile
+// stream here, so the order of the first memory round trip decides the
+// time: each wave issues its activation loads first (they come from L2),
+// then the weight loads of its first tile (from HBM), and splits the
+// activations into bf16 hi/lo while the weights are still on their way.
+// The second tile's weights follow the split, when its registers are free.
 //
 // Every 16-row tile is split along K over the 16 waves of a workgroup: wave w
 // owns k-blocks [P*16*KBW + w*KBW, +KBW) of phase P (k-block = 32 values),
 // so all waves do equal work on every tile and the A fragments of a wave
 // (its K slice of X, split into bf16 hi/lo) fit in registers. K longer than
-// 16*KBW k-blocks is covered in phases; phase P > 0 adds into Y, in order.
+// 16*KBW k-blocks is covered in phases, which add into an LDS copy of the
+// outputs; Y is written once, after the last phase. (A global store between
+// phases would make the wave drain the next phase's weight loads before it
+// could use its activations: loads and stores share one counter on gfx9.)
 //
 // Weight loads are contiguous runs: each instruction covers 16/KBW rows x
 // 64*KBW bytes (whole 128-byte lines for KBW >= 2), which the memory system
 // serves noticeably faster than the 16-rows x 64-bytes pattern of loading
 // the MFMA B operand directly. The wave transposes its segment through a
 // private LDS area (rows padded by 16 bytes: conflict-free writes and B
-// reads) and runs the MFMAs from there. Loads run two tiles ahead.
+// reads) and runs the MFMAs from there. All global loads are raw buffer
+// loads: lanes past M, K or the workgroup's rows get zeros from the range
+// check, so the code is straight and the loads in flight are counted exactly.
 //
 // M <= 8 (PACK): rows 0..7 of the A block hold the hi parts, rows 8..15 the
 // lo parts, one MFMA per k-block; each wave folds lo onto hi. 8 < M <= 16:
 // hi and lo are two A blocks with their own accumulators, added per wave.
 // The 16 per-wave partial tiles are summed in LDS in wave order (double
 // buffered, one barrier per tile).
-template <bool PACK, int KBW>
+template <bool PACK, int KBW, bool TWO>
 __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
   constexpr int SEG = 64 * KBW;                 // bytes of a row segment
@@ -81,6 +104,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* tr = smem;                                                          // [NW][16][RS]
   float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [2][NW][ROWS][16]
+  float* ysum = red + 2 * NW * ROWS * 16;                                            // [2][ROWS][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
@@ -88,119 +112,177 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   const int KB = (K + 31) / 32;
   const int phases = (KB + 16 * KBW - 1) / (16 * KBW);
 
-  // Contiguous row range [r0, r1) of this workgroup, balanced to 2 rows (the
-  // granularity of a load instruction); tiles are 16 rows from r0, the last
-  // one masked at r1.
-  const int r0 = static_cast<int>((static_cast<long long>(blockIdx.x) * (N / 2)) / gridDim.x) * 2;
-  const int r1 = blockIdx.x + 1 == gridDim.x
-                     ? N
-                     : static_cast<int>((static_cast<long long>(blockIdx.x + 1) * (N / 2)) / gridDim.x) * 2;
+  // Row range of this workgroup; tiles are 16 rows from r0, the last one
+  // masked at r1.
+  const int2 rows = wg_rows(p);
+  const int r0 = rows.x, r1 = rows.y;
   const int rounds = (r1 - r0 + 15) / 16;
   const int lrow = lane / LPR, lchunk = lane % LPR;
   unsigned char* wtr = tr + w * 16 * RS;
   unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
   const unsigned char* rd_base = wtr + i * RS + 16 * g;   // + 64*kb
 
-  for (int ph = 0; ph < phases; ++ph) {
-    const int kseg = 32 * KBW * (ph * NW + w);  // first k of this wave's segment
-    const bool lk_ok = kseg + 8 * lchunk < K;
-    u32x4 afr[KBW][F];
+  const uint32_t rowb = static_cast<uint32_t>(K) * 2;  // bytes per weight row
+  const BufRes wres = buf_res(p.W + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
+  const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
 
-    auto load = [&](u32x4 (&b)[NLD], int rr) {
-      const int row0 = r0 + rr * 16 + lrow;
-      const bool ok = rr < rounds && lk_ok;
-      const uint16_t* src = p.W + static_cast<size_t>(ok ? row0 : 0) * K + kseg + 8 * lchunk;
-      const size_t step = static_cast<size_t>(RPI) * K;
+  auto load = [&](u32x4 (&b)[NLD], uint32_t off) {
 #pragma unroll
-      for (int q = 0; q < NLD; ++q)
-        b[q] = (ok && row0 + RPI * q < r1) ? load16_stream(src + q * step) : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto compute_publish = [&](u32x4 (&b)[NLD], int buf) {
+    for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(wres, off + static_cast<uint32_t>(q * RPI) * rowb);
+  };
+  // A tile's weights into this wave's private LDS area (row-major segments).
+  auto stage = [&](const u32x4 (&b)[NLD]) {
 #pragma unroll
-      for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
-      f32x4 acc[F];
+    for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+  };
+  // B fragments from the staged tile, the MFMAs, and the wave's partial tile
+  // into red[buf].
+  auto mma_publish = [&](const u32x4 (&afr)[KBW][F], int buf) {
+    f32x4 acc[F];
 #pragma unroll
-      for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(rd_base + 64 * kb);
+    for (int kb = 0; kb < KBW; ++kb) {
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(rd_base + 64 * kb);
 #pragma unroll
-        for (int f = 0; f < F; ++f) acc[f] = mfma_16x16x32(afr[kb][f], bv, acc[f]);
+      for (int f = 0; f < F; ++f) acc[f] = mfma_16x16x32(afr[kb][f], bv, acc[f]);
+    }
+    float* dst = red + (buf * NW + w) * ROWS * 16;
+    if (PACK) {
+      // lanes 0..31 hold rows 0..7 (hi), lanes 32..63 rows 8..15 (lo) of the same columns
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float lo = __shfl_down(acc[0][v], 32);
+        if (g < 2) dst[(4 * g + v) * 16 + i] = acc[0][v] + lo;
       }
-      float* dst = red + (buf * NW + w) * ROWS * 16;
-      if (PACK) {
-        // lanes 0..31 hold rows 0..7 (hi), lanes 32..63 rows 8..15 (lo) of the same columns
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float lo = __shfl_down(acc[0][v], 32);
-          if (g < 2) dst[(4 * g + v) * 16 + i] = acc[0][v] + lo;
-        }
-      } else {
+      for (int v = 0; v < 4; ++v) dst[(4 * g + v) * 16 + i] = acc[0][v] + acc[F - 1][v];
+    }
+  };
+  // Wave-order sum of tile t into the LDS outputs (phases add, in order).
+  auto reduce = [&](int buf, int t, int ph) {
+    if (tid < ROWS * 16) {
+      float y = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dst[(4 * g + v) * 16 + i] = acc[0][v] + acc[F - 1][v];
-      }
-    };
-    auto reduce_store = [&](int buf, int rr) {
-      for (int it = tid; it < ROWS * 16; it += NW * kWave) {
-        const int col = it & 15, m = it >> 4;
-        const int n = r0 + rr * 16 + col;
-        if (m < M && n < r1) {
-          float y = 0.f;
-#pragma unroll
-          for (int ww = 0; ww < NW; ++ww) y += red[((buf * NW + ww) * ROWS + m) * 16 + col];
-          float* yp = p.Y + static_cast<size_t>(m) * p.ldy + n;
-          *yp = ph == 0 ? y : *yp + y;  // the same thread wrote it in the previous phase
-        }
-      }
-    };
+      for (int ww = 0; ww < NW; ++ww) y += red[(buf * NW + ww) * ROWS * 16 + tid];
+      float* ys = ysum + t * ROWS * 16 + tid;
+      *ys = ph == 0 ? y : *ys + y;
+    }
+  };
 
-    // The first two tiles' weight loads go out before the A fragments are
-    // built: they do not depend on X, so the two memory latencies overlap.
-    u32x4 b0[NLD], b1[NLD];
-    load(b0, 0);
-    load(b1, 1);
-    // A fragments: k-block kb of the segment covers k = kseg + 32*kb + 8*g + (0..7).
+  // Activations of phase ph, k-block kb: k = kseg + 32*kb + 8*g + (0..7) of
+  // row m (packed rows: each lane of a hi/lo pair loads one half). A phase
+  // past the last reads nothing.
+  constexpr int XH = PACK ? 1 : 2;
+  const int m = PACK ? (i & 7) : i;
+  const bool mrow = m < M;
+  const uint32_t xrow = static_cast<uint32_t>(m) * K * 4;
+  // (the conditions combine with & rather than &&: no short-circuit, so the
+  // compiler selects offsets instead of branching around the address math)
+  auto load_x = [&](float4 (&xr)[KBW][XH], int ph) {
+    const int kseg = 32 * KBW * (ph * NW + w);
+    const bool live = (ph < phases) & mrow;
 #pragma unroll
     for (int kb = 0; kb < KBW; ++kb) {
       const int k = kseg + 32 * kb + 8 * g;
-#pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const int m = PACK ? (i & 7) : i;
-        const int half = PACK ? (i >> 3) : f;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (m < M && k < K) {
-          const float4* xp = reinterpret_cast<const float4*>(p.X + static_cast<size_t>(m) * K + k);
-          const float4 x0 = xp[0], x1 = xp[1];
-          // (software rounding: the same nearest-even split as split_bf16x2,
-          // in fewer registers, which this kernel is short of)
-          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          uint32_t hb[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t hv = bf16_bits_rne(xs[e]);
-            hb[e] = half ? bf16_bits_rne(xs[e] - bf16_bits_to_f32(hv)) : hv;
-          }
-          v = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-        }
-        afr[kb][f] = v;
+      const uint32_t off = live & (k < K) ? xrow + static_cast<uint32_t>(k) * 4 : kBufOutOfRange;
+      if (PACK) {
+        xr[kb][0] = buf_load_f32x4(xres, off + 16 * (i >> 3));
+      } else {
+        xr[kb][0] = buf_load_f32x4(xres, off);
+        xr[kb][XH - 1] = buf_load_f32x4(xres, off + 16);
       }
     }
-    for (int rr = 0; rr < rounds; rr += 2) {
-      compute_publish(b0, 0);
-      load(b0, rr + 2);
+  };
+  // Offset of this lane's first weight load in phase ph (tile 0). A lane
+  // whose k lies past K, or a phase past the last, starts out of range (the
+  // added row offsets stay below 2^31 and cannot wrap it back).
+  auto w_off = [&](int ph) -> uint32_t {
+    const int kseg = 32 * KBW * (ph * NW + w);
+    return (ph < phases) & (kseg + 8 * lchunk < K)
+               ? static_cast<uint32_t>(lrow) * rowb + static_cast<uint32_t>(kseg + 8 * lchunk) * 2
+               : kBufOutOfRange;
+  };
+  auto split = [&](const float4 (&xr)[KBW][XH], u32x4 (&afr)[KBW][F]) {
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      float4 x0 = xr[kb][0], x1 = xr[kb][XH - 1];
+      if (PACK) pair_halves(xr[kb][0], i, x0, x1);
+      const uint2 s0 = split_bf16x2(x0.x, x0.y), s1 = split_bf16x2(x0.z, x0.w);
+      const uint2 s2 = split_bf16x2(x1.x, x1.y), s3 = split_bf16x2(x1.z, x1.w);
+      const u32x4 h = {s0.x, s1.x, s2.x, s3.x}, l = {s0.y, s1.y, s2.y, s3.y};
+      if (PACK) {
+        afr[kb][0] = (i >> 3) ? l : h;
+      } else {
+        afr[kb][0] = h;
+        afr[kb][F - 1] = l;
+      }
+    }
+  };
+
+  if (!TWO) {
+    // One tile per workgroup: the loads of phase ph + 1 go out while phase
+    // ph is still being computed (activations before its MFMAs, weights right
+    // after them, when their registers are free), so they overlap its
+    // reduction and the next split.
+    float4 xr[KBW][XH];
+    u32x4 b[NLD], afr[KBW][F];
+    // (the scheduling barriers keep each step's registers apart: the
+    // activations become A fragments, the weights go to LDS, and only then
+    // do the next phase's loads reuse those registers; the last phase is
+    // peeled so that no load is issued for a phase that does not exist)
+    auto phase = [&](int ph, auto more) {
+      __builtin_amdgcn_sched_barrier(0);
+      split(xr, afr);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(b);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(more)::value) load_x(xr, ph + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_publish(afr, ph & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(more)::value) load(b, w_off(ph + 1));
       __syncthreads();
-      reduce_store(0, rr);
-      if (rr + 1 < rounds) {
-        compute_publish(b1, 1);
-        load(b1, rr + 3);
+      reduce(ph & 1, 0, ph);
+    };
+    load_x(xr, 0);
+    load(b, w_off(0));
+    int ph = 0;
+    for (; ph + 1 < phases; ++ph) phase(ph, std::true_type{});
+    phase(ph, std::false_type{});
+  } else {
+    for (int ph = 0; ph < phases; ++ph) {
+      float4 xr[KBW][XH];
+      u32x4 b0[NLD], b1[NLD], afr[KBW][F];
+      load_x(xr, ph);
+      const uint32_t off = w_off(ph);
+      load(b0, off);
+      __builtin_amdgcn_sched_barrier(0);
+      split(xr, afr);
+      // The second tile, if the workgroup has one (else the loads read
+      // nothing: issuing them unconditionally keeps the code straight and the
+      // registers of the two tiles apart).
+      load(b1, rounds > 1 ? off + 16 * rowb : kBufOutOfRange);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(b0);
+      mma_publish(afr, 0);
+      __syncthreads();
+      reduce(0, 0, ph);
+      if (rounds > 1) {
+        stage(b1);
+        mma_publish(afr, 1);
         __syncthreads();
-        reduce_store(1, rr + 1);
+        reduce(1, 1, ph);
       }
     }
-    if (phases > 1) {
-      __threadfence_block();  // this phase's Y stores complete before the next phase reads them
-      __syncthreads();
-    }
+  }
+  __syncthreads();
+  // Outputs, once: tile t covers columns r0 + 16t + (0..15).
+  for (int e = tid; e < rounds * M * 16; e += NW * kWave) {
+    const int t = e / (M * 16), rem = e - t * M * 16, mm = rem >> 4, col = rem & 15;
+    const int n = r0 + 16 * t + col;
+    if (n < r1) p.Y[static_cast<size_t>(mm) * p.ldy + n] = ysum[(t * ROWS + mm) * 16 + col];
   }
 }
 
@@ -253,13 +335,10 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
   const int KB = (K + 31) / 32;
   const int phases = (KB + 16 * KBW - 1) / (16 * KBW);
 
-  // Contiguous row range [r0, r1) of this workgroup, balanced to 2 rows (the
-  // granularity of a load instruction); tiles are 16 rows from r0, the last
-  // one masked at r1.
-  const int r0 = static_cast<int>((static_cast<long long>(blockIdx.x) * (N / 2)) / gridDim.x) * 2;
-  const int r1 = blockIdx.x + 1 == gridDim.x
-                     ? N
-                     : static_cast<int>((static_cast<long long>(blockIdx.x + 1) * (N / 2)) / gridDim.x) * 2;
+  // Row range of this workgroup; tiles are 16 rows from r0, the last one
+  // masked at r1.
+  const int2 rows = wg_rows(p);
+  const int r0 = rows.x, r1 = rows.y;
   const int rounds = (r1 - r0 + 15) / 16;
   // Chunks of this workgroup's tiles, balanced, even sized (but the last).
   const int nchunks = (rounds + p.chunk - 1) / p.chunk;
@@ -293,30 +372,37 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
   // two batches where registers are short, and are split into bf16 hi/lo.
   auto build_a = [&]() {
     const int kseg = 32 * KBW * (ph * NW + w);
-    constexpr int KH = KBW * F * 8 > 32 ? KBW / 2 : KBW;
+    constexpr int XH = PACK ? 1 : 2;  // float4 loads per lane and k-block (packed rows: one half each)
+    constexpr int KH = KBW * XH * 4 > 32 ? KBW / 2 : KBW;
+    const int m = PACK ? (i & 7) : i;
 #pragma unroll
     for (int k0 = 0; k0 < KBW; k0 += KH) {
-      float4 xr[KH][F][2];
+      float4 xr[KH][XH];
 #pragma unroll
-      for (int kk = 0; kk < KH; ++kk)
-#pragma unroll
-        for (int f = 0; f < F; ++f) {
-          const int m = PACK ? (i & 7) : i, k = kseg + 32 * (k0 + kk) + 8 * g;
-          const uint32_t off = m < M && k < K ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
-          xr[kk][f][0] = buf_load_f32x4(xres, off);
-          xr[kk][f][1] = buf_load_f32x4(xres, off + 16);
+      for (int kk = 0; kk < KH; ++kk) {
+        const int k = kseg + 32 * (k0 + kk) + 8 * g;
+        const uint32_t off = (m < M) & (k < K) ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
+        if (PACK) {
+          xr[kk][0] = buf_load_f32x4(xres, off + 16 * (i >> 3));
+        } else {
+          xr[kk][0] = buf_load_f32x4(xres, off);
+          xr[kk][XH - 1] = buf_load_f32x4(xres, off + 16);
         }
+      }
 #pragma unroll
-      for (int kk = 0; kk < KH; ++kk)
-#pragma unroll
-        for (int f = 0; f < F; ++f) {
-          const int half = PACK ? (i >> 3) : f;
-          const float4 x0 = xr[kk][f][0], x1 = xr[kk][f][1];
-          const uint2 s0 = split_bf16x2(x0.x, x0.y), s1 = split_bf16x2(x0.z, x0.w);
-          const uint2 s2 = split_bf16x2(x1.x, x1.y), s3 = split_bf16x2(x1.z, x1.w);
-          const u32x4 h = {s0.x, s1.x, s2.x, s3.x}, l = {s0.y, s1.y, s2.y, s3.y};
-          afr[k0 + kk][f] = half ? l : h;
+      for (int kk = 0; kk < KH; ++kk) {
+        float4 x0 = xr[kk][0], x1 = xr[kk][XH - 1];
+        if (PACK) pair_halves(xr[kk][0], i, x0, x1);
+        const uint2 s0 = split_bf16x2(x0.x, x0.y), s1 = split_bf16x2(x0.z, x0.w);
+        const uint2 s2 = split_bf16x2(x1.x, x1.y), s3 = split_bf16x2(x1.z, x1.w);
+        const u32x4 h = {s0.x, s1.x, s2.x, s3.x}, l = {s0.y, s1.y, s2.y, s3.y};
+        if (PACK) {
+          afr[k0 + kk][0] = (i >> 3) ? l : h;
+        } else {
+          afr[k0 + kk][0] = h;
+          afr[k0 + kk][F - 1] = l;
         }
+      }
     }
   };
   // Tile rr of this workgroup; rows past r1 and tiles past lim read zeros.
@@ -623,6 +709,7 @@ struct Plan {
   int tkbw;     // k-blocks per wave
   bool pack;    // M <= 8: hi and lo rows share one A block
   bool shortk;  // gemv_short_kernel (at most two tiles per workgroup)
+  bool two;     // some workgroup has two tiles
   int chunk;    // gemv_tstream_kernel tiles per LDS output chunk
   int grid;
   size_t lds;
@@ -640,9 +727,9 @@ Plan make_plan(int M, int N, int K, int cus) {
   const int tiles = (N + 15) / 16;
   const int KB = (K + 31) / 32;
   pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
-  const int rows_max = 2 * ((N / 2 + pl.grid - 1) / pl.grid) + 1;  // rows of the largest workgroup
-  const int rounds = (rows_max + 15) / 16;
+  const int rounds = (wg_rows_max(N, pl.grid) + 15) / 16;
   pl.shortk = rounds <= 2;
+  pl.two = rounds == 2;
   const int kbw_max = pl.shortk && pl.pack ? 8 : 4;
   int kbw = 1;
   while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
@@ -651,7 +738,7 @@ Plan make_plan(int M, int N, int K, int cus) {
   const size_t fixed = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
   if (pl.shortk) {
     pl.chunk = 0;
-    pl.lds = fixed;
+    pl.lds = fixed + static_cast<size_t>(2) * rows * 16 * 4;  // + the LDS outputs of two tiles
     return pl;
   }
   const size_t per_tile = static_cast<size_t>(M) * 16 * 4;
@@ -681,13 +768,18 @@ hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st)
 
 template <bool PACK, int KBW>
 hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW>);
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  const void* one = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, false>);
+  const void* two = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true>);
+  static const hipError_t attr = [&] {
+    const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+    return e != hipSuccess ? e
+                           : hipFuncSetAttribute(two, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kLdsBytes));
+  }();
   if (attr != hipSuccess) return attr;
   GemvParams a = prm;
   void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
+  return hipLaunchKernel(pl.two ? two : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
 }
 
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
@@ -733,6 +825,15 @@ hipError_t launch_mrows(const GemvParams& prm, hipStream_t st) {
 
 }  // namespace
 
+bool gemv_shape_fits(int N, int K, int M) {
+  if (K > (1 << 22)) return false;  // X of a launch part: <= 80 rows * K * 4 bytes; W: 128 rows * 2K
+  if (M > 16) return true;
+  const int cus = device_cu_count();
+  if (cus <= 0) return true;  // the launch reports the missing device
+  const Plan pl = make_plan(M, N, K, cus);
+  return static_cast<long long>(wg_rows_max(N, pl.grid)) * K * 2 < (1LL << 31);
+}
+
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
                        hipStream_t stream) {
   const int cus = device_cu_count();
@@ -748,6 +849,8 @@ hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, f
     prm.Y = Y;
     prm.M = M;
     prm.chunk = pl.chunk;
+    prm.pq = (N / 2) / pl.grid;
+    prm.prem = (N / 2) % pl.grid;
     return dispatch(prm, pl, stream);
   }
   // More rows: balanced parts of at most kMrMaxM rows (each above 16).

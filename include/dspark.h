@@ -74,8 +74,11 @@ const char* dspark_status_string(dspark_status status);
  *   W  bf16 [N, K]  row n produces output column n    16-byte aligned
  *   X  fp32 [M, K]  activations                        16-byte aligned
  *   Y  fp32 [M, N]  output, overwritten                 4-byte aligned
- * Sizes: N >= 1, K >= 8 and K % 8 == 0, M >= 1. The weight is streamed once
- * per group of 128 rows of X. Accumulation is fp32; each fp32 activation is
+ * Sizes: N >= 1, K >= 8 and K % 8 == 0, K <= 4194304, M >= 1; for M <= 16
+ * the weight rows one workgroup streams (about N / CUs + 1) times 2K bytes
+ * must stay below 2 GiB (DSPARK_ERR_SHAPE otherwise: the kernels address a
+ * workgroup's share with 32-bit buffer offsets). The weight is streamed once
+ * per group of at most 80 rows of X. Accumulation is fp32; each fp32 activation is
  * split exactly-to-2^-17 into two bf16 terms, so |error| stays far below
  * 1e-3 + 1e-3 |Y| at every size in use.
  */

@@ -60,6 +60,7 @@ def test_gemv_errors(L):
         assert fn(A, 16, 0, A, 7, A2, None) == ERR_SHAPE
         assert fn(A, 16, 12, A, 7, A2, None) == ERR_SHAPE      # K % 8 != 0
         assert fn(A, 16, 64, A, 0, A2, None) == ERR_SHAPE
+        assert fn(A, 16, (1 << 22) + 8, A, 7, A2, None) == ERR_SHAPE  # K past the 32-bit buffer ranges
         assert fn(MIS, 16, 64, A, 7, A2, None) == ERR_ALIGN
         assert fn(A, 16, 64, MIS, 7, A2, None) == ERR_ALIGN
         assert fn(A, 16, 64, A, 7, A2 + 1, None) == ERR_ALIGN
