@@ -105,10 +105,14 @@ def cpu_baseline(inp, seconds):
 
 
 def bench_layer(args, dev):
-    """One step = the seven projections of one draft layer at M = 7 (q, k, v, o,
-    gate, up, down; each with its own activations) plus the 7424-wide probe on
-    the 7 drafted rows. Steps cycle through --layer-copies distinct weight sets,
-    like a multi-layer drafter, so no weight is served from the Infinity Cache."""
+    """One step = one draft layer at M = 7 plus the 7424-wide probe on the 7
+    drafted rows. The layer's projections run as a transformer layer runs
+    them: q, k and v share their input and go as one GEMV over the
+    concatenated [3 * 4096, 4096] weight, gate and up likewise over
+    [2 * 12288, 4096]; o and down on their own (4 launches, every weight byte
+    read once, as with 7 separate GEMVs). The seven separate GEMVs are timed
+    too. Steps cycle through --layer-copies distinct weight sets, like a
+    multi-layer drafter, so no weight is served from the Infinity Cache."""
     import numpy as np
     import torch
 
@@ -118,65 +122,97 @@ def bench_layer(args, dev):
     inp = synth.layer_inputs(copies=args.layer_copies)
     names = list(inp["layers"][0].keys())
     Ws = [{nm: ops.bf16_from_bits(lw[nm], dev) for nm in names} for lw in inp["layers"]]
+    fnames = list(synth.FUSED_INPUT.keys())
+    Wf = [{nm: ops.bf16_from_bits(w, dev) for nm, w in synth.fused_layer(lw).items()} for lw in inp["layers"]]
     Xs = {nm: torch.from_numpy(inp["X"][nm]).to(dev) for nm in names}
+    Xf = {nm: Xs[synth.FUSED_INPUT[nm]] for nm in fnames}
     Ys = {nm: torch.empty(inp["M"], Ws[0][nm].shape[0], device=dev) for nm in names}
+    Yf = {nm: torch.empty(inp["M"], Wf[0][nm].shape[0], device=dev) for nm in fnames}
     px = torch.from_numpy(inp["probe_x"]).to(dev)
     pw = ops.bf16_from_bits(inp["probe_w"], dev)
     plog = torch.empty(inp["M"], device=dev)
     ppass = torch.empty(inp["M"], dtype=torch.int32, device=dev)
     M = inp["M"]
-    wbytes = {nm: Ws[0][nm].numel() * 2 for nm in names}
-    gemv_bytes = {nm: wbytes[nm] + M * Ws[0][nm].shape[1] * 4 + M * Ws[0][nm].shape[0] * 4 for nm in names}
-    layer_bytes = sum(gemv_bytes.values()) + M * inp["probe_width"] * 4 + inp["probe_width"] * 2 + M * 8
 
-    def step(c):
+    def gbytes(W):
+        return W.numel() * 2 + M * W.shape[1] * 4 + M * W.shape[0] * 4
+
+    gemv_bytes = {nm: gbytes(Ws[0][nm]) for nm in names}
+    fused_bytes = {nm: gbytes(Wf[0][nm]) for nm in fnames}
+    probe_bytes = M * inp["probe_width"] * 4 + inp["probe_width"] * 2 + M * 8
+    layer_bytes = sum(fused_bytes.values()) + probe_bytes
+
+    def step_fused(c):
+        for nm in fnames:
+            ops.proj_smallm(Wf[c][nm], Xf[nm], out=Yf[nm])
+        ops.conf_probe(px, pw, 0.0, 0.0, logit_out=plog, pass_out=ppass)
+
+    def step_separate(c):
         for nm in names:
             ops.proj_smallm(Ws[c][nm], Xs[nm], out=Ys[nm])
         ops.conf_probe(px, pw, 0.0, 0.0, logit_out=plog, pass_out=ppass)
 
-    for s_ in range(args.warmup):
-        step(s_ % args.layer_copies)
-    torch.cuda.synchronize()
-    # Timed region: whole layers back to back, one pair of events around all.
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    a.record()
-    for s_ in range(args.steps):
-        step(s_ % args.layer_copies)
-    b.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    layer_us = a.elapsed_time(b) * 1e3 / args.steps
+
+    def timed_layers(step):
+        for s_ in range(args.warmup):
+            step(s_ % args.layer_copies)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record()
+        for s_ in range(args.steps):
+            step(s_ % args.layer_copies)
+        b.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, a.elapsed_time(b) * 1e3 / args.steps
+
+    # Timed region: whole layers back to back, one pair of events around all.
+    elapsed, layer_us = timed_layers(step_fused)
+    elapsed_sep, layer_us_sep = timed_layers(step_separate)
 
     # Per projection (outside the timed region): the same GEMV launched back to
     # back over the weight copies, one pair of events around the batch.
-    per = {}
-    for nm in names:
-        n = 8 * args.layer_copies
-        a.record()
-        for j in range(n):
-            ops.proj_smallm(Ws[j % args.layer_copies][nm], Xs[nm], out=Ys[nm])
-        b.record()
-        torch.cuda.synchronize()
-        per[nm] = a.elapsed_time(b) * 1e3 / n
-    gbs = {nm: gemv_bytes[nm] / (per[nm] * 1e-6) / 1e9 for nm in names}
-    tot_us = sum(per.values())
-    agg = sum(gemv_bytes.values()) / (tot_us * 1e-6) / 1e9
+    def per_gemv(Wsets, Xd, Yd, nms):
+        per = {}
+        for nm in nms:
+            n = 8 * args.layer_copies
+            a.record()
+            for j in range(n):
+                ops.proj_smallm(Wsets[j % args.layer_copies][nm], Xd[nm], out=Yd[nm])
+            b.record()
+            torch.cuda.synchronize()
+            per[nm] = a.elapsed_time(b) * 1e3 / n
+        return per
+
+    per_f = per_gemv(Wf, Xf, Yf, fnames)
+    per_s = per_gemv(Ws, Xs, Ys, names)
+    gbs_f = {nm: fused_bytes[nm] / (per_f[nm] * 1e-6) / 1e9 for nm in fnames}
+    gbs_s = {nm: gemv_bytes[nm] / (per_s[nm] * 1e-6) / 1e9 for nm in names}
+    tot_f, tot_s = sum(per_f.values()), sum(per_s.values())
+    agg = sum(fused_bytes.values()) / (tot_f * 1e-6) / 1e9
+    agg_s = sum(gemv_bytes.values()) / (tot_s * 1e-6) / 1e9
     log(f"[bench] draft_layer: {args.steps / elapsed:.1f} layers/s ({layer_us:.1f} us per layer incl. probe); "
-        f"GEMV sum {tot_us:.1f} us = {agg:.0f} GB/s; "
-        + ", ".join(f"{nm} {per[nm]:.1f} us ({gbs[nm]:.0f} GB/s)" for nm in names))
+        f"GEMV sum {tot_f:.1f} us = {agg:.0f} GB/s; "
+        + ", ".join(f"{nm} {per_f[nm]:.1f} us ({gbs_f[nm]:.0f} GB/s)" for nm in fnames))
+    log(f"[bench] seven separate GEMVs: {args.steps / elapsed_sep:.1f} layers/s ({layer_us_sep:.1f} us per layer); "
+        f"GEMV sum {tot_s:.1f} us = {agg_s:.0f} GB/s; "
+        + ", ".join(f"{nm} {per_s[nm]:.1f} us ({gbs_s[nm]:.0f} GB/s)" for nm in names))
     out = {
         "metric": "draft layers/s + achieved HBM GB/s of the M=7 projections",
         "value": args.steps / elapsed, "unit": "layers/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "draft_layer", "M": M, "d": inp["d"], "ffn": inp["ffn"],
-                   "probe_width": inp["probe_width"], "weight_copies": args.layer_copies},
-        "roofline": {"bound": "hbm", "kernel": "proj_smallm GEMVs (7 per layer)", "achieved": agg,
+                   "probe_width": inp["probe_width"], "weight_copies": args.layer_copies,
+                   "projections": "qkv [12288,4096], o [4096,4096], gate_up [24576,4096], down [4096,12288]"},
+        "roofline": {"bound": "hbm", "kernel": "proj_smallm GEMVs (4 per layer)", "achieved": agg,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": agg / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_layer": sum(gemv_bytes.values()), "gemv_us_per_layer": tot_us},
-        "per_gemv": {nm: {"us": per[nm], "GB/s": gbs[nm], "bytes": gemv_bytes[nm]} for nm in names},
+                     "algorithmic_bytes_per_layer": sum(fused_bytes.values()), "gemv_us_per_layer": tot_f},
+        "per_gemv": {nm: {"us": per_f[nm], "GB/s": gbs_f[nm], "bytes": fused_bytes[nm]} for nm in fnames},
         "step_hbm": {"achieved": layer_bytes / (layer_us * 1e-6) / 1e9, "unit": "GB/s", "layer_us": layer_us},
+        "separate_gemvs": {"layers_per_s": args.steps / elapsed_sep, "layer_us": layer_us_sep, "gemv_us": tot_s,
+                           "GB/s": agg_s,
+                           "per_gemv": {nm: {"us": per_s[nm], "GB/s": gbs_s[nm]} for nm in names}},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

@@ -18,7 +18,7 @@
 //    share one 16-row A block (rows 0..7 hi, 8..15 lo): one MFMA per 1 KB of
 //    weights.
 //  * Three kernels, chosen by shape:
-//      - gemv_short_kernel: M <= 16, at most two 16-row tiles per workgroup
+//      - gemv_short_kernel: M <= 16, at most 16 tiles of 16 rows per workgroup
 //        (the projections of a draft layer): the shortest dependency chain.
 //      - gemv_tstream_kernel: M <= 16, many tiles per workgroup (the
 //        lm_heads): K split over 16 waves, two tiles of loads in flight,
@@ -62,13 +62,12 @@ inline int wg_rows_max(int N, int grid) {
   return std::max(2 * (q + (rem > 0 ? 1 : 0)), 2 * q + (N & 1));
 }
 
-// Short variant for M <= 16: at most two 16-row tiles per workgroup (the
-// projections of a draft layer). Nothing is amortized over a long tile
+// Short variant for M <= 16: at most 16 tiles of 16 rows per workgroup (the
+// projections of a draft layer). Little is amortized over a long tile
 // stream here, so the order of the first memory round trip decides the
 // time: each wave issues its activation loads first (they come from L2),
 // then the weight loads of its first tile (from HBM), and splits the
 // activations into bf16 hi/lo while the weights are still on their way.
-// The second tile's weights follow the split, when its registers are free.
 //
 // Every 16-row tile is split along K over the 16 waves of a workgroup: wave w
 // owns k-blocks [P*16*KBW + w*KBW, +KBW) of phase P (k-block = 32 values),
@@ -93,7 +92,7 @@ inline int wg_rows_max(int N, int grid) {
 // hi and lo are two A blocks with their own accumulators, added per wave.
 // The 16 per-wave partial tiles are summed in LDS in wave order (double
 // buffered, one barrier per tile).
-template <bool PACK, int KBW, bool TWO>
+template <bool PACK, int KBW, bool MANY>
 __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
   constexpr int SEG = 64 * KBW;                 // bytes of a row segment
@@ -104,7 +103,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* tr = smem;                                                          // [NW][16][RS]
   float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [2][NW][ROWS][16]
-  float* ysum = red + 2 * NW * ROWS * 16;                                            // [2][ROWS][16]
+  float* ysum = red + 2 * NW * ROWS * 16;                                            // [tiles][ROWS][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     }
   };
 
-  if (!TWO) {
+  if (!MANY) {
     // One tile per workgroup: the loads of phase ph + 1 go out while phase
     // ph is still being computed (activations before its MFMAs, weights right
     // after them, when their registers are free), so they overlap its
@@ -252,28 +251,33 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     for (; ph + 1 < phases; ++ph) phase(ph, std::true_type{});
     phase(ph, std::false_type{});
   } else {
+    // Several tiles per workgroup: one tile of weights in flight per wave,
+    // the next issued as soon as the current one is in LDS (so it overlaps
+    // the MFMAs, the reduction and the barrier); the activations and their
+    // split once per phase. 16 waves x one tile keep enough bytes in flight
+    // per CU to cover the memory latency.
+    float4 xr[KBW][XH];
+    u32x4 b[NLD], afr[KBW][F];
+    load_x(xr, 0);
+    load(b, w_off(0));
+    __builtin_amdgcn_sched_barrier(0);
+    split(xr, afr);
+    int j = 0;  // items so far: parity of the reduction buffer
     for (int ph = 0; ph < phases; ++ph) {
-      float4 xr[KBW][XH];
-      u32x4 b0[NLD], b1[NLD], afr[KBW][F];
-      load_x(xr, ph);
       const uint32_t off = w_off(ph);
-      load(b0, off);
-      __builtin_amdgcn_sched_barrier(0);
-      split(xr, afr);
-      // The second tile, if the workgroup has one (else the loads read
-      // nothing: issuing them unconditionally keeps the code straight and the
-      // registers of the two tiles apart).
-      load(b1, rounds > 1 ? off + 16 * rowb : kBufOutOfRange);
-      __builtin_amdgcn_sched_barrier(0);
-      stage(b0);
-      mma_publish(afr, 0);
-      __syncthreads();
-      reduce(0, 0, ph);
-      if (rounds > 1) {
-        stage(b1);
-        mma_publish(afr, 1);
+      for (int t = 0; t < rounds; ++t, ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        stage(b);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool last_t = t + 1 == rounds;
+        const bool more = !last_t || ph + 1 < phases;
+        if (last_t && more) load_x(xr, ph + 1);
+        if (more) load(b, last_t ? w_off(ph + 1) : off + static_cast<uint32_t>(t + 1) * 16 * rowb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_publish(afr, j & 1);
         __syncthreads();
-        reduce(1, 1, ph);
+        reduce(j & 1, t, ph);
+        if (last_t && more) split(xr, afr);
       }
     }
   }
@@ -708,19 +712,19 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
 struct Plan {
   int tkbw;     // k-blocks per wave
   bool pack;    // M <= 8: hi and lo rows share one A block
-  bool shortk;  // gemv_short_kernel (at most two tiles per workgroup)
-  bool two;     // some workgroup has two tiles
+  bool shortk;  // gemv_short_kernel (at most kShortTiles tiles per workgroup)
+  bool many;    // some workgroup has more than one tile
   int chunk;    // gemv_tstream_kernel tiles per LDS output chunk
   int grid;
   size_t lds;
 };
 
 constexpr size_t kLdsBytes = 160 * 1024;
+constexpr int kShortTiles = 16;  // workgroups with at most this many tiles take gemv_short_kernel
 
 // M <= 16: K slices of 32*KBW per wave, phases for longer K. Workgroups with
-// at most two tiles take the short kernel (up to 8 k-blocks per wave with
-// packed rows); longer ones the LDS-staged streaming kernel, whose registers
-// allow 4.
+// at most kShortTiles tiles take the short kernel, longer ones the streaming
+// kernel with its LDS output chunks.
 Plan make_plan(int M, int N, int K, int cus) {
   Plan pl{};
   pl.pack = M <= 8;
@@ -728,9 +732,12 @@ Plan make_plan(int M, int N, int K, int cus) {
   const int KB = (K + 31) / 32;
   pl.grid = std::max(1, std::min(cus, std::min(tiles, N / 2)));
   const int rounds = (wg_rows_max(N, pl.grid) + 15) / 16;
-  pl.shortk = rounds <= 2;
-  pl.two = rounds == 2;
-  const int kbw_max = pl.shortk && pl.pack ? 8 : 4;
+  pl.shortk = rounds <= kShortTiles;
+  pl.many = rounds > 1;
+  // Measured on MI355X (M = 7 and 15, K = 4096 and 12288): one tile per
+  // workgroup runs fastest with 2 k-blocks per wave and phase, several tiles
+  // with 4, and the short kernel beats the streaming one up to 16 tiles.
+  const int kbw_max = pl.shortk ? (pl.many ? 4 : 2) : 4;
   int kbw = 1;
   while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
   pl.tkbw = kbw;
@@ -738,7 +745,7 @@ Plan make_plan(int M, int N, int K, int cus) {
   const size_t fixed = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
   if (pl.shortk) {
     pl.chunk = 0;
-    pl.lds = fixed + static_cast<size_t>(2) * rows * 16 * 4;  // + the LDS outputs of two tiles
+    pl.lds = fixed + static_cast<size_t>(rounds) * rows * 16 * 4;  // + the LDS outputs of its tiles
     return pl;
   }
   const size_t per_tile = static_cast<size_t>(M) * 16 * 4;
@@ -769,17 +776,17 @@ hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st)
 template <bool PACK, int KBW>
 hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   const void* one = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, false>);
-  const void* two = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true>);
+  const void* many = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true>);
   static const hipError_t attr = [&] {
     const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
     return e != hipSuccess ? e
-                           : hipFuncSetAttribute(two, hipFuncAttributeMaxDynamicSharedMemorySize,
+                           : hipFuncSetAttribute(many, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  static_cast<int>(kLdsBytes));
   }();
   if (attr != hipSuccess) return attr;
   GemvParams a = prm;
   void* args[] = {&a};
-  return hipLaunchKernel(pl.two ? two : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
+  return hipLaunchKernel(pl.many ? many : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
 }
 
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
@@ -788,8 +795,7 @@ hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
       switch (pl.tkbw) {
         case 1: return launch_short<true, 1>(prm, pl, st);
         case 2: return launch_short<true, 2>(prm, pl, st);
-        case 4: return launch_short<true, 4>(prm, pl, st);
-        default: return launch_short<true, 8>(prm, pl, st);
+        default: return launch_short<true, 4>(prm, pl, st);
       }
     }
     switch (pl.tkbw) {

@@ -211,8 +211,10 @@ def round_inputs(name: str, seed: int | None = None, with_base: bool = False):
 
 def layer_inputs(seed: int | None = None, copies: int = 1):
     """One draft layer at M = 7 (q/k/v/o [4096, 4096], gate/up [12288, 4096],
-    down [4096, 12288], bf16 ~ N(0, 0.02^2)), per-projection inputs
-    X [7, K] ~ N(0, 1), and a 7424-wide probe (w ~ N(0, 0.02^2), x ~ N(0, 1)).
+    down [4096, 12288], bf16 ~ N(0, 0.02^2)), inputs X [7, K] ~ N(0, 1), and
+    a 7424-wide probe (w ~ N(0, 0.02^2), x ~ N(0, 1)). As in a transformer
+    layer, q, k and v read the same input, and so do gate and up; o and down
+    have their own.
 
     ``copies`` > 1 draws that many independent weight sets.
     """
@@ -226,7 +228,22 @@ def layer_inputs(seed: int | None = None, copies: int = 1):
         for j, (nm, shp) in enumerate(shapes.items()):
             ws[nm] = normal_bf16(seed, S_LAYER + 16 * c + j, shp)
         layers.append(ws)
-    xs = {nm: normal_f32(seed, S_LAYER + 15 * 16 + j, (M, shp[1])) for j, (nm, shp) in enumerate(shapes.items())}
+    xs = {nm: normal_f32(seed, S_LAYER + 15 * 16 + j, (M, shp[1])) for j, (nm, shp) in enumerate(shapes.items())
+          if nm in ("q", "o", "gate", "down")}
+    xs["k"] = xs["v"] = xs["q"]
+    xs["up"] = xs["gate"]
     px, pw = probe_inputs(M, cfg["probe_width"], seed)
     return dict(cfg, seed=seed, layers=layers, X=xs, probe_x=px, probe_w=pw,
                 probe_bias=np.float32(0.0), probe_threshold=np.float32(0.0))
+
+
+def fused_layer(ws: dict) -> dict:
+    """The same layer with the projections that share an input concatenated
+    along N: qkv [3 * 4096, 4096] (rows q, then k, then v) and gate_up
+    [2 * 12288, 4096]; o and down unchanged. Output columns follow the same
+    order, so y_qkv[:, :4096] is q, and so on."""
+    return dict(qkv=np.concatenate([ws["q"], ws["k"], ws["v"]]), o=ws["o"],
+                gate_up=np.concatenate([ws["gate"], ws["up"]]), down=ws["down"])
+
+
+FUSED_INPUT = dict(qkv="q", o="o", gate_up="gate", down="down")  # fused projection -> its input's name

@@ -72,6 +72,27 @@ def test_draft_layer_projections(dev, name):
         logits_close(y.cpu().numpy(), oracle.gemv(Wb, X), f"proj {proj}")
 
 
+def test_draft_layer_fused_projections(dev):
+    """q/k/v as one GEMV over the concatenated weight (and gate/up likewise):
+    each slice of the output matches the oracle of its own projection."""
+    inp = synth.layer_inputs()
+    ws = inp["layers"][0]
+    fused = synth.fused_layer(ws)
+    parts = dict(qkv=["q", "k", "v"], o=["o"], gate_up=["gate", "up"], down=["down"])
+    for nm, Wb in fused.items():
+        X = inp["X"][synth.FUSED_INPUT[nm]]
+        say(f"[proj fused {nm}] W {Wb.shape} X {X.shape} seed={inp['seed']}")
+        y = _ops().proj_smallm(_bf(Wb, dev), _up(X, dev))
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        col = 0
+        for part in parts[nm]:
+            n = ws[part].shape[0]
+            logits_close(y[:, col:col + n], oracle.gemv(ws[part], inp["X"][part]), f"proj {nm}/{part}")
+            col += n
+        assert col == y.shape[1]
+
+
 def test_lm_head_full_size_sampled(dev):
     """Qwen3-8B-shaped head at full size in the benchmark's launch
     configuration; oracle on sampled vocabulary rows incl. the ragged tail."""
