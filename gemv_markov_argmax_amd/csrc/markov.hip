@@ -100,15 +100,16 @@ __device__ __forceinline__ uint32_t load_coherent(const uint32_t* a) {
 
 constexpr int kMaxPoll = kMaxGroups / kWave;  // slots per lane when polling
 
-template <int KB, int RT>
+template <int KB, int RT, int LT, bool BL>
 __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams p) {
   constexpr int NW = kLoopWaves;
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* w2l = reinterpret_cast<u32x4*>(smem);                                         // [lds_tiles][KB][64]
   uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * 1024);  // [NW][16]
-  int* prev_s = reinterpret_cast<int*>(keys_s + NW * kMaxReqs);                           // [16]
+  int* prev_s = reinterpret_cast<int*>(keys_s + NW * kMaxReqs);                           // [16] prev0 (valid or 0)
   int* tok_s = prev_s + kMaxReqs;                                                         // [k][R] drafted tokens
-  float* basel = reinterpret_cast<float*>(tok_s + kMaxSteps * kMaxReqs);                  // [R][bstride]
+  unsigned char* a_lds = reinterpret_cast<unsigned char*>(tok_s + kMaxSteps * kMaxReqs);  // [16][KB*64 + 16]
+  float* basel = reinterpret_cast<float*>(a_lds + 16 * (KB * 64 + 16));                   // [R][bstride]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
   const int R = p.R, V = p.V, r = p.r, G = p.G;
@@ -182,101 +183,176 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
     }
   };
 
-  const bool bl = p.base_in_lds != 0;
-  const int nb = bl ? R * nt * 16 : 0;  // base values of this workgroup staged per step
-  constexpr int kPre = 4;               // prefetched base values per thread
-  // Entries e = tid + u*threads of the slice: LDS slot and base offset (step 0), fixed for the call.
-  int pre_lds[kPre];
-  size_t pre_src[kPre];
-  bool pre_ok[kPre];
+  // ---- base values of this workgroup's slice, staged in LDS per step by
+  // the stager threads: during the exchange, by the waves that do not poll
+  // (w >= R), or after the polls when every wave polls (R >= waves). Loads
+  // first, then the LDS writes, so a thread's loads are in flight together.
+  const int nb = BL ? R * nt * 16 : 0;
+  const int stage_w0 = R < NW ? R : 0;
+  const int sthreads = (NW - stage_w0) * kWave;
+  const int stid = tid - stage_w0 * kWave;  // < 0: not a stager
+  constexpr int kPre = 4;
+  float sv[kPre];
+  // (the thread index is made opaque per call, so the slice addresses are
+  // recomputed here rather than held in registers across the whole step)
+  auto stage_fetch = [&](int st) {
+    if (!BL || stid < 0) return;
+    int so = stid;
+    asm volatile("" : "+v"(so));
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    const int e = tid + u * kLoopThreads;
-    const int m = e < nb ? e / (nt * 16) : 0, nl = e - m * (nt * 16);
-    const int n = t0 * 16 + nl;
-    pre_lds[u] = m * p.bstride + nl;
-    pre_src[u] = static_cast<size_t>(m) * p.B * V + n;
-    pre_ok[u] = e < nb && n < V;
-  }
-  float pre[kPre];
-  auto fetch_base = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < kPre; ++u)
-      pre[u] = pre_ok[u] ? p.base[pre_src[u] + static_cast<size_t>(st) * V] : 0.f;
-  };
-  auto stage_base = [&](int st) {  // prefetched values, then any remainder straight from memory
-#pragma unroll
-    for (int u = 0; u < kPre; ++u)
-      if (tid + u * kLoopThreads < nb) basel[pre_lds[u]] = pre[u];
-    for (int e = tid + kPre * kLoopThreads; e < nb; e += kLoopThreads) {
-      const int m = e / (nt * 16), nl = e - m * (nt * 16);
-      const int n = t0 * 16 + nl;
-      basel[m * p.bstride + nl] = n < V ? p.base[(static_cast<size_t>(m) * p.B + st) * V + n] : 0.f;
+    for (int u = 0; u < kPre; ++u) {
+      const int e = so + u * sthreads;
+      const int m = e < nb ? e / (nt * 16) : 0, n = t0 * 16 + (e - m * (nt * 16));
+      // (always issued, to entry 0 for an unused slot: straight code)
+      sv[u] = p.base[e < nb && n < V ? (static_cast<size_t>(m) * p.B + st) * V + n : 0];
     }
   };
-  fetch_base(0);
+  auto stage_store = [&](int st) {
+    if (!BL || stid < 0) return;
+    int so = stid;
+    asm volatile("" : "+v"(so));
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int e = so + u * sthreads;
+      const int m = e / (nt * 16);
+      if (e < nb) basel[m * p.bstride + (e - m * (nt * 16))] = sv[u];
+    }
+    for (int e = so + kPre * sthreads; e < nb; e += sthreads) {  // large slices only
+      const int m = e / (nt * 16), n = t0 * 16 + (e - m * (nt * 16));
+      basel[m * p.bstride + (e - m * (nt * 16))] = n < V ? p.base[(static_cast<size_t>(m) * p.B + st) * V + n] : 0.f;
+    }
+  };
+
+  // ---- the A operand of the next step, in LDS: row m holds markov_w1[prev]
+  // of request m (rows padded by 16 bytes, so the fragment reads of the 16
+  // rows fall in different banks). A polling wave gathers its request's row
+  // as soon as it knows the token (r <= 1024: at most two 16-byte loads per
+  // lane); the LDS writes follow once the stagers' loads are out too.
+  constexpr int kARow = KB * 64 + 16;
+  auto gather_fetch = [&](int tok, u32x4 (&gv)[2]) {
+    const uint16_t* src = p.w1 + static_cast<size_t>(tok) * r;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + q * kWave;  // 16-byte chunk of the row
+      gv[q] = load16(src + 8 * (c < r / 8 ? c : 0));
+    }
+  };
+  auto gather_store = [&](int m, const u32x4 (&gv)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + q * kWave;
+      if (c < r / 8) *reinterpret_cast<u32x4*>(a_lds + m * kARow + 16 * c) = gv[q];
+    }
+  };
 
   if (dead != 0u) {  // an earlier call gave up: report it and touch no slot
     if (blockIdx.x == 0) finish();
     return;
   }
 
-  for (int step = 0; step < p.k; ++step) {
-    __syncthreads();  // prev_s written; the previous step is done with basel
-    // ---- A operand: markov_w1[prev] of request i (zero for absent or invalid
-    // requests); issued first, it is the only load on this step's critical path
-    u32x4 afr[KB];
-    {
-      const bool live = i < R && prev0_ok(p, i < R ? i : 0);
-      const uint16_t* src = p.w1 + static_cast<size_t>(live ? prev_s[i] : 0) * r + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        afr[kb] = (live && kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
-    stage_base(step);
-    __syncthreads();  // basel ready
+  // Prologue: zero the A block (columns past r stay zero: the markov_w2
+  // fragments are zero there too, and uninitialized LDS could hold NaNs),
+  // then the rows of step 0 and the base slice of step 0.
+  for (int e = tid; e < 16 * kARow / 16; e += kLoopThreads)
+    reinterpret_cast<u32x4*>(a_lds)[e] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  for (int m = w; m < R; m += NW) {
+    u32x4 gv[2];
+    gather_fetch(prev_s[m], gv);
+    gather_store(m, gv);
+  }
+  stage_fetch(0);
+  stage_store(0);
+  __syncthreads();
 
+  for (int step = 0; step < p.k; ++step) {
+    const bool last = step == p.k - 1;
+    // Lane coordinates made opaque once per step, so the compiler recomputes
+    // the addresses derived from them (a few VALU ops) instead of keeping
+    // dozens of loop-invariant addresses live next to the register tiles.
+    int ll = lane;
+    asm volatile("" : "+v"(ll));
+    const int li = ll & 15, lg = ll >> 4;
+
+    // Scores of tile j: lane (i, g) holds rows m = 4g..4g+3 at column
+    // n = 16 (t0 + j) + i. Branch-free: the four base values are read at
+    // once (clamped to a valid entry) and a key counts only where the tile,
+    // the request and the column exist.
     uint64_t best[4] = {0, 0, 0, 0};
-    auto score = [&](int j, f32x4 acc) {
-      const int n = (t0 + j) * 16 + i;
+    auto score = [&](int j, bool tile_ok, f32x4 acc) {
+      const int jj = tile_ok ? j : 0;
+      const int n = (t0 + jj) * 16 + li;
+      float bv[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = 4 * g + v;
-        if (m < R && n < V) {
-          const float bv = bl ? basel[m * p.bstride + j * 16 + i]
-                              : p.base[(static_cast<size_t>(m) * p.B + step) * V + n];
-          best[v] = umax64(best[v], score_key(bv + acc[v], static_cast<uint32_t>(n)));
-        }
+        const int m = min(4 * lg + v, R - 1);
+        bv[v] = BL ? basel[m * p.bstride + jj * 16 + li]
+                   : p.base[(static_cast<size_t>(m) * p.B + step) * V + min(n, V - 1)];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint64_t key = score_key(bv[v] + acc[v], static_cast<uint32_t>(n));
+        const bool ok = tile_ok && 4 * lg + v < R && n < V;
+        best[v] = ok && key > best[v] ? key : best[v];
       }
     };
+    // A fragment kb of this lane: k = 32*kb + 8*g + (0..7) of row i, read
+    // from LDS where it is needed (it feeds every tile of the k-block).
+    const u32x4* a_frag = reinterpret_cast<const u32x4*>(a_lds + li * kARow + 16 * lg);  // + 4*kb
+
+    // Register tiles and the wave's first LT LDS tiles, all accumulation
+    // chains interleaved per k-block, so one chain's MFMAs overlap the
+    // others' latency and the LDS reads of a k-block go out together. An
+    // absent tile computes on zeros (or on LDS tile 0) and is not scored.
+    {
+      f32x4 accr[RT > 0 ? RT : 1], accl[LT];
+      int jl[LT];
+      const u32x4* srcl[LT];
 #pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      const int j = w + NW * u;
-      if (j < nreg) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(afr[kb], wreg[u][kb], acc);
-        score(j, acc);
+      for (int t = 0; t < LT; ++t) {
+        jl[t] = nreg + w + NW * t;
+        srcl[t] = w2l + static_cast<size_t>(jl[t] < nheld ? jl[t] - nreg : 0) * KB * kWave + ll;
+        accl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    for (int j = nreg + w; j < nt; j += NW) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (j < nheld) {
-        const u32x4* src = w2l + static_cast<size_t>(j - nreg) * KB * kWave + lane;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(afr[kb], src[kb * kWave], acc);
-      } else {
-        const uint16_t* src = w2_row(j, i) + 8 * g;
+      for (int u = 0; u < RT; ++u) accr[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 a = a_frag[4 * kb];
+        u32x4 bl[LT];
+#pragma unroll
+        for (int t = 0; t < LT; ++t) bl[t] = srcl[t][kb * kWave];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) accr[u] = mfma_16x16x32(a, wreg[u][kb], accr[u]);
+#pragma unroll
+        for (int t = 0; t < LT; ++t) accl[t] = mfma_16x16x32(a, bl[t], accl[t]);
+      }
+#pragma unroll
+      for (int u = 0; u < RT; ++u) score(w + NW * u, w + NW * u < nreg, accr[u]);
+#pragma unroll
+      for (int t = 0; t < LT; ++t) score(jl[t], jl[t] < nheld, accl[t]);
+    }
+    // Further LDS tiles of this wave, if any.
+    for (int j = nreg + w + NW * LT; j < nheld; j += NW) {
+      const u32x4* src = w2l + static_cast<size_t>(j - nreg) * KB * kWave + ll;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(a_frag[4 * kb], src[kb * kWave], acc);
+      score(j, true, acc);
+    }
+    // Tiles beyond on-chip capacity are read from memory at every step.
+    for (int j = nheld + (((nreg + w - nheld) % NW) + NW) % NW; j < nt; j += NW) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      {
+        const uint16_t* src = w2_row(j, li) + 8 * lg;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 b = (kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
-          acc = mfma_16x16x32(afr[kb], b, acc);
+          const u32x4 b = (kb * 32 + 8 * lg < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+          acc = mfma_16x16x32(a_frag[4 * kb], b, acc);
         }
       }
-      score(j, acc);
+      score(j, true, acc);
     }
-    const bool last = step == p.k - 1;
-    if (!last) fetch_base(step + 1);  // independent of this step's winner
 
     // ---- workgroup maximum per request (lanes of a 16-lane group share requests 4g..4g+3)
 #pragma unroll
@@ -287,7 +363,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
     if (i == 0)
 #pragma unroll
       for (int v = 0; v < 4; ++v) keys_s[w * kMaxReqs + 4 * g + v] = best[v];
-    __syncthreads();
+    __syncthreads();  // keys complete; every wave is done with this step's A block and base slice
 
     // ---- publish this workgroup's key of every request
     if (tid < R) {
@@ -300,9 +376,20 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
       clear_other();
       return;
     }
+    // The next step's base slice: waves that do not poll fetch and store it
+    // while the pollers wait; when every wave polls, the loads go out before
+    // the polls (so they arrive during them) and the stores follow the polls.
+    if (!last) stage_fetch(step + 1);
+    if (!last && stage_w0 > 0) stage_store(step + 1);
 
-    // ---- exchange: poll the G slots of each request until all are published
-    for (int m = w; m < R; m += NW) {
+    // ---- exchange: poll the G slots of each request until all are published;
+    // the winner's markov_w1 row is the next step's A row (wave w polls
+    // request w, and then w + 8, whose row goes to LDS at once)
+    u32x4 gv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = w + h * NW;
+      if (m >= R) break;
       const uint64_t* src = part + (static_cast<size_t>(step) * R + m) * G;
       uint64_t kk = 0;
       uint32_t spins = 0;
@@ -311,7 +398,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
         bool have = true;
 #pragma unroll
         for (int u = 0; u < kMaxPoll; ++u) {
-          const int j = lane + u * kWave;
+          const int j = ll + u * kWave;
           slot[u] = j < G ? load_coherent(src + j) : ~0ull;
         }
 #pragma unroll
@@ -319,7 +406,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
         if (__all(have)) {
 #pragma unroll
           for (int u = 0; u < kMaxPoll; ++u) {
-            const int j = lane + u * kWave;
+            const int j = ll + u * kWave;
             if (j < G) kk = umax64(kk, slot[u]);
           }
           break;
@@ -338,15 +425,22 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
       kk = row_max64(kk);
       kk = umax64(kk, __shfl_xor(kk, 16));
       kk = umax64(kk, __shfl_xor(kk, 32));
-      if (lane == 0) {
-        int tok = static_cast<int>(key_index(kk));
-        if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
-        prev_s[m] = tok;
-        tok_s[step * kMaxReqs + m] = tok;
+      int tok = static_cast<int>(key_index(kk));
+      if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
+      if (lane == 0) tok_s[step * kMaxReqs + m] = tok;
+      if (!last && h == 0) gather_fetch(tok, gv);
+      if (!last && h == 1) {
+        u32x4 gv1[2];
+        gather_fetch(tok, gv1);
+        gather_store(m, gv1);
       }
     }
+    if (!last) {
+      if (w < R) gather_store(w, gv);
+      if (stage_w0 == 0) stage_store(step + 1);
+    }
+    __syncthreads();  // the next step's A block and base slice are in LDS (and tok_s complete)
   }
-  __syncthreads();  // workgroup 0: every poll of the final step is over, tok_s complete
   finish();
 }
 
@@ -357,7 +451,7 @@ struct LoopPlan {
 
 constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straight from memory
 
-int reg_tiles(int KB) { return KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0); }
+constexpr int reg_tiles(int KB) { return KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0); }
 
 // Plan for G workgroups (G <= min(tiles, kMaxGroups)).
 LoopPlan make_loop_plan(int R, int V, int r, int G) {
@@ -371,7 +465,7 @@ LoopPlan make_loop_plan(int R, int V, int r, int G) {
   pl.bstride = ntmax * 16;
   const size_t base_bytes = static_cast<size_t>(R) * pl.bstride * 4;
   pl.base_in_lds = base_bytes <= kBaseLdsMax ? 1 : 0;
-  const size_t fixed = static_cast<size_t>(kLoopWaves) * kMaxReqs * 8 + kMaxReqs * 4 +
+  const size_t fixed = static_cast<size_t>(kLoopWaves) * kMaxReqs * 8 + kMaxReqs * 4 + 16 * (pl.KB * 64 + 16) +
                        static_cast<size_t>(kMaxSteps) * kMaxReqs * 4 + (pl.base_in_lds ? base_bytes : 0);
   const size_t tile_bytes = static_cast<size_t>(pl.KB) * 1024;
   const int want = std::max(0, ntmax - kLoopWaves * pl.RT);
@@ -381,10 +475,11 @@ LoopPlan make_loop_plan(int R, int V, int r, int G) {
   return pl;
 }
 
-template <int KB>
+template <int KB, bool BL>
 hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
-  constexpr int RT = KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
-  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<KB, RT>);
+  constexpr int RT = reg_tiles(KB);
+  constexpr int LT = KB >= 16 ? 1 : 2;
+  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<KB, RT, LT, BL>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
@@ -438,13 +533,23 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.lds_tiles = pl.lds_tiles;
   prm.bstride = pl.bstride;
   prm.base_in_lds = pl.base_in_lds;
+  if (pl.base_in_lds) {
+    switch (pl.KB) {
+      case 1: return launch_loop<1, true>(prm, pl, cus, stream);
+      case 2: return launch_loop<2, true>(prm, pl, cus, stream);
+      case 4: return launch_loop<4, true>(prm, pl, cus, stream);
+      case 8: return launch_loop<8, true>(prm, pl, cus, stream);
+      case 16: return launch_loop<16, true>(prm, pl, cus, stream);
+      default: return launch_loop<32, true>(prm, pl, cus, stream);
+    }
+  }
   switch (pl.KB) {
-    case 1: return launch_loop<1>(prm, pl, cus, stream);
-    case 2: return launch_loop<2>(prm, pl, cus, stream);
-    case 4: return launch_loop<4>(prm, pl, cus, stream);
-    case 8: return launch_loop<8>(prm, pl, cus, stream);
-    case 16: return launch_loop<16>(prm, pl, cus, stream);
-    default: return launch_loop<32>(prm, pl, cus, stream);
+    case 1: return launch_loop<1, false>(prm, pl, cus, stream);
+    case 2: return launch_loop<2, false>(prm, pl, cus, stream);
+    case 4: return launch_loop<4, false>(prm, pl, cus, stream);
+    case 8: return launch_loop<8, false>(prm, pl, cus, stream);
+    case 16: return launch_loop<16, false>(prm, pl, cus, stream);
+    default: return launch_loop<32, false>(prm, pl, cus, stream);
   }
 }
 
