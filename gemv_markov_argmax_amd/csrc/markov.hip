@@ -59,8 +59,11 @@ namespace {
 constexpr int kMaxReqs = 16;
 constexpr int kMaxSteps = 32;
 constexpr int kMaxGroups = 256;          // grid cap: one workgroup per CU
-constexpr int kLoopWaves = 8;
-constexpr int kLoopThreads = kLoopWaves * kWave;
+// Waves per workgroup: 8 (two per SIMD) by default; 4 (one per SIMD, half
+// of each SIMD's registers in AGPRs) when eight would leave markov_w2 tiles
+// to be re-read from memory at every step: a single wave per SIMD may hold
+// 10 tiles of r = 256 instead of 3.
+constexpr int kLoopWavesMax = 8;
 constexpr size_t kCtlBytes = 256;        // control words, then two slot buffers
 constexpr size_t kSlotsPerBuffer = static_cast<size_t>(kMaxSteps) * kMaxReqs * kMaxGroups;
 // Control words (uint32) at the start of the workspace.
@@ -100,9 +103,9 @@ __device__ __forceinline__ uint32_t load_coherent(const uint32_t* a) {
 
 constexpr int kMaxPoll = kMaxGroups / kWave;  // slots per lane when polling
 
-template <int KB, int RT, int LT, bool BL>
-__global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams p) {
-  constexpr int NW = kLoopWaves;
+template <int NW, int KB, int RT, int LT, bool BL>
+__global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p) {
+  constexpr int kLoopThreads = NW * kWave;
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* w2l = reinterpret_cast<u32x4*>(smem);                                         // [lds_tiles][KB][64]
   uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * 1024);  // [NW][16]
@@ -384,10 +387,10 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
 
     // ---- exchange: poll the G slots of each request until all are published;
     // the winner's markov_w1 row is the next step's A row (wave w polls
-    // request w, and then w + 8, whose row goes to LDS at once)
+    // request w, and then w + NW, ..., whose rows go to LDS at once)
     u32x4 gv[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kMaxReqs / NW; ++h) {
       const int m = w + h * NW;
       if (m >= R) break;
       const uint64_t* src = part + (static_cast<size_t>(step) * R + m) * G;
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
       if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
       if (lane == 0) tok_s[step * kMaxReqs + m] = tok;
       if (!last && h == 0) gather_fetch(tok, gv);
-      if (!last && h == 1) {
+      if (!last && h > 0) {
         u32x4 gv1[2];
         gather_fetch(tok, gv1);
         gather_store(m, gv1);
@@ -445,41 +448,49 @@ __global__ __launch_bounds__(kLoopThreads) void markov_loop_kernel(MarkovParams 
 }
 
 struct LoopPlan {
-  int G, KB, RT, lds_tiles, bstride, base_in_lds;
+  int G, NW, KB, RT, lds_tiles, bstride, base_in_lds;
   size_t lds;
+  bool streams;  // some tiles are re-read from memory at every step
 };
 
 constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straight from memory
 
-constexpr int reg_tiles(int KB) { return KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0); }
+// markov_w2 tiles held in registers per wave (the largest counts that leave
+// no register spills; one wave per SIMD is built for r = 256 only).
+constexpr int reg_tiles(int NW, int KB) {
+  return NW == 4 ? (KB == 8 ? 10 : 0) : KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
+}
 
-// Plan for G workgroups (G <= min(tiles, kMaxGroups)).
-LoopPlan make_loop_plan(int R, int V, int r, int G) {
+// Plan for G workgroups (G <= min(tiles, kMaxGroups)) of NW waves.
+LoopPlan make_loop_plan(int R, int V, int r, int G, int NW) {
   LoopPlan pl{};
   const int tiles = (V + 15) / 16;
   pl.G = G;
+  pl.NW = NW;
   const int kb = (r + 31) / 32;
   pl.KB = kb <= 1 ? 1 : kb <= 2 ? 2 : kb <= 4 ? 4 : kb <= 8 ? 8 : kb <= 16 ? 16 : 32;
-  pl.RT = reg_tiles(pl.KB);
+  pl.RT = reg_tiles(NW, pl.KB);
   const int ntmax = (tiles + pl.G - 1) / pl.G;
   pl.bstride = ntmax * 16;
   const size_t base_bytes = static_cast<size_t>(R) * pl.bstride * 4;
   pl.base_in_lds = base_bytes <= kBaseLdsMax ? 1 : 0;
-  const size_t fixed = static_cast<size_t>(kLoopWaves) * kMaxReqs * 8 + kMaxReqs * 4 + 16 * (pl.KB * 64 + 16) +
+  const size_t fixed = static_cast<size_t>(NW) * kMaxReqs * 8 + kMaxReqs * 4 + 16 * (pl.KB * 64 + 16) +
                        static_cast<size_t>(kMaxSteps) * kMaxReqs * 4 + (pl.base_in_lds ? base_bytes : 0);
   const size_t tile_bytes = static_cast<size_t>(pl.KB) * 1024;
-  const int want = std::max(0, ntmax - kLoopWaves * pl.RT);
+  const int want = std::max(0, ntmax - NW * pl.RT);
   const int fit = fixed < kLdsBytes ? static_cast<int>((kLdsBytes - fixed) / tile_bytes) : 0;
   pl.lds_tiles = std::min(want, fit);
   pl.lds = pl.lds_tiles * tile_bytes + fixed;
+  pl.streams = want > fit;
   return pl;
 }
 
-template <int KB, bool BL>
+template <int NW, int KB, bool BL>
 hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
-  constexpr int RT = reg_tiles(KB);
+  constexpr int RT = reg_tiles(NW, KB);
   constexpr int LT = KB >= 16 ? 1 : 2;
-  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<KB, RT, LT, BL>);
+  constexpr int kLoopThreads = NW * kWave;
+  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<NW, KB, RT, LT, BL>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
@@ -513,7 +524,11 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   // 128 instead of 256 workgroups; 4096 x 32 17 -> 14 us at 16).
   const int tiles = (V + 15) / 16;
   const int G = std::max(1, std::min({cus, kMaxGroups, (tiles + 15) / 16}));
-  const LoopPlan pl = make_loop_plan(R, V, r, G);
+  LoopPlan pl = make_loop_plan(R, V, r, G, kLoopWavesMax);
+  if (pl.streams && pl.KB == 8) {  // one wave per SIMD holds more of markov_w2 on chip
+    const LoopPlan p4 = make_loop_plan(R, V, r, G, 4);
+    if (p4.lds_tiles + 4 * p4.RT > pl.lds_tiles + kLoopWavesMax * pl.RT) pl = p4;
+  }
   MarkovParams prm{};
   prm.base = base;
   prm.w1 = w1;
@@ -533,23 +548,27 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.lds_tiles = pl.lds_tiles;
   prm.bstride = pl.bstride;
   prm.base_in_lds = pl.base_in_lds;
+  if (pl.NW == 4) {  // r = 256 only
+    return pl.base_in_lds ? launch_loop<4, 8, true>(prm, pl, cus, stream)
+                          : launch_loop<4, 8, false>(prm, pl, cus, stream);
+  }
   if (pl.base_in_lds) {
     switch (pl.KB) {
-      case 1: return launch_loop<1, true>(prm, pl, cus, stream);
-      case 2: return launch_loop<2, true>(prm, pl, cus, stream);
-      case 4: return launch_loop<4, true>(prm, pl, cus, stream);
-      case 8: return launch_loop<8, true>(prm, pl, cus, stream);
-      case 16: return launch_loop<16, true>(prm, pl, cus, stream);
-      default: return launch_loop<32, true>(prm, pl, cus, stream);
+      case 1: return launch_loop<8, 1, true>(prm, pl, cus, stream);
+      case 2: return launch_loop<8, 2, true>(prm, pl, cus, stream);
+      case 4: return launch_loop<8, 4, true>(prm, pl, cus, stream);
+      case 8: return launch_loop<8, 8, true>(prm, pl, cus, stream);
+      case 16: return launch_loop<8, 16, true>(prm, pl, cus, stream);
+      default: return launch_loop<8, 32, true>(prm, pl, cus, stream);
     }
   }
   switch (pl.KB) {
-    case 1: return launch_loop<1, false>(prm, pl, cus, stream);
-    case 2: return launch_loop<2, false>(prm, pl, cus, stream);
-    case 4: return launch_loop<4, false>(prm, pl, cus, stream);
-    case 8: return launch_loop<8, false>(prm, pl, cus, stream);
-    case 16: return launch_loop<16, false>(prm, pl, cus, stream);
-    default: return launch_loop<32, false>(prm, pl, cus, stream);
+    case 1: return launch_loop<8, 1, false>(prm, pl, cus, stream);
+    case 2: return launch_loop<8, 2, false>(prm, pl, cus, stream);
+    case 4: return launch_loop<8, 4, false>(prm, pl, cus, stream);
+    case 8: return launch_loop<8, 8, false>(prm, pl, cus, stream);
+    case 16: return launch_loop<8, 16, false>(prm, pl, cus, stream);
+    default: return launch_loop<8, 32, false>(prm, pl, cus, stream);
   }
 }
 

@@ -244,6 +244,25 @@ def test_markov_full_size_and_invariants(dev):
     check_markov(a.cpu().numpy(), base, w1, w2, prev0, B)
 
 
+@pytest.mark.parametrize("R,B", [(1, 15), (9, 6)])
+def test_markov_lane27b_size(dev, R, B):
+    """The 27B lane's vocabulary (248320 x 256): markov_w2 does not fit on
+    chip with eight waves per workgroup, so the loop runs one wave per SIMD
+    with tiles in AGPRs; R = 9 has waves poll several requests each. Exact
+    ids (near-ties reported), 5% tie rows with exactly equal scores."""
+    cfg = synth.CONFIGS["lane27b"]
+    V, r = cfg["V"], cfg["r"]
+    seed = synth.config_seed("lane27b") + R
+    say(f"[markov lane27b] R={R} B={B} V={V} r={r} seed={seed}")
+    base, w1, w2, prev0, ties = synth.markov_inputs(R, B, V, r, seed, tie_frac=cfg["tie_frac"])
+    bd, w1d, w2d, pd = _up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev)
+    ids = _ops().markov_sample(bd, w1d, w2d, pd, B)
+    again = _ops().markov_sample(bd, w1d, w2d, pd, B)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, again)
+    check_markov(ids.cpu().numpy(), base, w1, w2, prev0, B)
+
+
 # ---------------------------------------------------------------------------
 # Probe
 # ---------------------------------------------------------------------------
