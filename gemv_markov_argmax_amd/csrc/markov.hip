@@ -109,10 +109,11 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* w2l = reinterpret_cast<u32x4*>(smem);                                         // [lds_tiles][KB][64]
   uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * 1024);  // [NW][16]
-  int* prev_s = reinterpret_cast<int*>(keys_s + NW * kMaxReqs);                           // [16] prev0 (valid or 0)
-  int* tok_s = prev_s + kMaxReqs;                                                         // [k][R] drafted tokens
-  unsigned char* a_lds = reinterpret_cast<unsigned char*>(tok_s + kMaxSteps * kMaxReqs);  // [16][KB*64 + 16]
-  float* basel = reinterpret_cast<float*>(a_lds + 16 * (KB * 64 + 16));                   // [R][bstride]
+  // A block: R rows, then a zero row read by the lanes of absent requests.
+  unsigned char* a_lds = reinterpret_cast<unsigned char*>(keys_s + NW * kMaxReqs);       // [R + 1][KB*64 + 16]
+  int* prev_s = reinterpret_cast<int*>(a_lds + (p.R + 1) * (KB * 64 + 16));             // [16] prev0 (valid or 0)
+  int* tok_s = prev_s + kMaxReqs;                                                       // [k][R] drafted tokens
+  float* basel = reinterpret_cast<float*>(tok_s + p.k * p.R);                           // [R][bstride]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
   const int R = p.R, V = p.V, r = p.r, G = p.G;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       const int m = e / p.k, st = e - m * p.k;
       int64_t id = -1;
       if (dead == 0u && prev0_ok(p, m)) {  // tok_s holds this call's tokens (each in [0, V))
-        const int tok = tok_s[st * kMaxReqs + m];
+        const int tok = tok_s[st * R + m];
         id = p.d2t ? p.d2t[tok] : static_cast<int64_t>(tok);
       }
       p.ids[e] = bad ? -2 : id;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   // Prologue: zero the A block (columns past r stay zero: the markov_w2
   // fragments are zero there too, and uninitialized LDS could hold NaNs),
   // then the rows of step 0 and the base slice of step 0.
-  for (int e = tid; e < 16 * kARow / 16; e += kLoopThreads)
+  for (int e = tid; e < (R + 1) * kARow / 16; e += kLoopThreads)
     reinterpret_cast<u32x4*>(a_lds)[e] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   for (int m = w; m < R; m += NW) {
@@ -301,39 +302,54 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     };
     // A fragment kb of this lane: k = 32*kb + 8*g + (0..7) of row i, read
     // from LDS where it is needed (it feeds every tile of the k-block).
-    const u32x4* a_frag = reinterpret_cast<const u32x4*>(a_lds + li * kARow + 16 * lg);  // + 4*kb
+    const u32x4* a_frag = reinterpret_cast<const u32x4*>(a_lds + min(li, R) * kARow + 16 * lg);  // + 4*kb
 
     // Register tiles and the wave's first LT LDS tiles, all accumulation
     // chains interleaved per k-block, so one chain's MFMAs overlap the
     // others' latency and the LDS reads of a k-block go out together. An
     // absent tile computes on zeros (or on LDS tile 0) and is not scored.
-    {
-      f32x4 accr[RT > 0 ? RT : 1], accl[LT];
-      int jl[LT];
-      const u32x4* srcl[LT];
+    // With many register tiles (one wave per SIMD) they go in two passes,
+    // which halves the accumulators held at once; the LDS tiles ride along
+    // with the first pass.
+    constexpr int RG = RT > 6 ? (RT + 1) / 2 : (RT > 0 ? RT : 1);  // register tiles per pass
 #pragma unroll
-      for (int t = 0; t < LT; ++t) {
+    for (int u0 = 0; u0 < (RT > 0 ? RT : 1); u0 += RG) {
+      constexpr int L1 = LT;
+      const bool first = u0 == 0;
+      f32x4 accr[RG], accl[L1];
+      int jl[L1];
+      const u32x4* srcl[L1];
+#pragma unroll
+      for (int t = 0; t < L1; ++t) {
         jl[t] = nreg + w + NW * t;
         srcl[t] = w2l + static_cast<size_t>(jl[t] < nheld ? jl[t] - nreg : 0) * KB * kWave + ll;
         accl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int u = 0; u < RT; ++u) accr[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < RG; ++u) accr[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const u32x4 a = a_frag[4 * kb];
-        u32x4 bl[LT];
+        u32x4 bl[L1];
+        if (first)
 #pragma unroll
-        for (int t = 0; t < LT; ++t) bl[t] = srcl[t][kb * kWave];
+          for (int t = 0; t < L1; ++t) bl[t] = srcl[t][kb * kWave];
 #pragma unroll
-        for (int u = 0; u < RT; ++u) accr[u] = mfma_16x16x32(a, wreg[u][kb], accr[u]);
+        for (int u = 0; u < RG; ++u)
+          if (RT > 0 && u0 + u < RT) accr[u] = mfma_16x16x32(a, wreg[u0 + u < RT ? u0 + u : 0][kb], accr[u]);
+        if (first)
 #pragma unroll
-        for (int t = 0; t < LT; ++t) accl[t] = mfma_16x16x32(a, bl[t], accl[t]);
+          for (int t = 0; t < L1; ++t) accl[t] = mfma_16x16x32(a, bl[t], accl[t]);
+        // (one wave per SIMD: keep each k-block's fragment reads next to its
+        // MFMAs, so that they do not pile up in registers ahead of them)
+        if (NW == 4 && (kb & 1)) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int u = 0; u < RT; ++u) score(w + NW * u, w + NW * u < nreg, accr[u]);
+      for (int u = 0; u < RG; ++u)
+        if (RT > 0 && u0 + u < RT) score(w + NW * (u0 + u), w + NW * (u0 + u) < nreg, accr[u]);
+      if (first)
 #pragma unroll
-      for (int t = 0; t < LT; ++t) score(jl[t], jl[t] < nheld, accl[t]);
+        for (int t = 0; t < L1; ++t) score(jl[t], jl[t] < nheld, accl[t]);
     }
     // Further LDS tiles of this wave, if any.
     for (int j = nreg + w + NW * LT; j < nheld; j += NW) {
@@ -389,7 +405,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     // the winner's markov_w1 row is the next step's A row (wave w polls
     // request w, and then w + NW, ..., whose rows go to LDS at once)
     u32x4 gv[2];
-#pragma unroll
+#pragma unroll 1
     for (int h = 0; h < kMaxReqs / NW; ++h) {
       const int m = w + h * NW;
       if (m >= R) break;
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       kk = umax64(kk, __shfl_xor(kk, 32));
       int tok = static_cast<int>(key_index(kk));
       if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
-      if (lane == 0) tok_s[step * kMaxReqs + m] = tok;
+      if (lane == 0) tok_s[step * R + m] = tok;
       if (!last && h == 0) gather_fetch(tok, gv);
       if (!last && h > 0) {
         u32x4 gv1[2];
@@ -462,7 +478,7 @@ constexpr int reg_tiles(int NW, int KB) {
 }
 
 // Plan for G workgroups (G <= min(tiles, kMaxGroups)) of NW waves.
-LoopPlan make_loop_plan(int R, int V, int r, int G, int NW) {
+LoopPlan make_loop_plan(int R, int V, int r, int k, int G, int NW) {
   LoopPlan pl{};
   const int tiles = (V + 15) / 16;
   pl.G = G;
@@ -474,8 +490,8 @@ LoopPlan make_loop_plan(int R, int V, int r, int G, int NW) {
   pl.bstride = ntmax * 16;
   const size_t base_bytes = static_cast<size_t>(R) * pl.bstride * 4;
   pl.base_in_lds = base_bytes <= kBaseLdsMax ? 1 : 0;
-  const size_t fixed = static_cast<size_t>(NW) * kMaxReqs * 8 + kMaxReqs * 4 + 16 * (pl.KB * 64 + 16) +
-                       static_cast<size_t>(kMaxSteps) * kMaxReqs * 4 + (pl.base_in_lds ? base_bytes : 0);
+  const size_t fixed = static_cast<size_t>(NW) * kMaxReqs * 8 + static_cast<size_t>(R + 1) * (pl.KB * 64 + 16) +
+                       kMaxReqs * 4 + static_cast<size_t>(k) * R * 4 + (pl.base_in_lds ? base_bytes : 0);
   const size_t tile_bytes = static_cast<size_t>(pl.KB) * 1024;
   const int want = std::max(0, ntmax - NW * pl.RT);
   const int fit = fixed < kLdsBytes ? static_cast<int>((kLdsBytes - fixed) / tile_bytes) : 0;
@@ -524,9 +540,9 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   // 128 instead of 256 workgroups; 4096 x 32 17 -> 14 us at 16).
   const int tiles = (V + 15) / 16;
   const int G = std::max(1, std::min({cus, kMaxGroups, (tiles + 15) / 16}));
-  LoopPlan pl = make_loop_plan(R, V, r, G, kLoopWavesMax);
+  LoopPlan pl = make_loop_plan(R, V, r, k, G, kLoopWavesMax);
   if (pl.streams && pl.KB == 8) {  // one wave per SIMD holds more of markov_w2 on chip
-    const LoopPlan p4 = make_loop_plan(R, V, r, G, 4);
+    const LoopPlan p4 = make_loop_plan(R, V, r, k, G, 4);
     if (p4.lds_tiles + 4 * p4.RT > pl.lds_tiles + kLoopWavesMax * pl.RT) pl = p4;
   }
   MarkovParams prm{};
