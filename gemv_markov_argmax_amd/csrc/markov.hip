@@ -142,11 +142,29 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     for (int kb = 0; kb < KB; ++kb)
       wreg[u][kb] = (j < nreg && kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
   }
-  for (int e = tid; e < (nheld - nreg) * KB * kWave; e += kLoopThreads) {
-    const int ln = e & 63, kb = (e >> 6) % KB, jj = (e >> 6) / KB;
-    const int gg = ln >> 4;
-    w2l[e] = (kb * 32 + 8 * gg < r) ? load16(w2_row(nreg + jj, ln & 15) + kb * 32 + 8 * gg)
-                                    : u32x4{0u, 0u, 0u, 0u};
+  // LDS tiles: eight loads per thread in flight at a time, then their LDS
+  // writes (one load and write after the other would serialize the latency).
+  {
+    constexpr int kBatch = 8;
+    const int nl = (nheld - nreg) * KB * kWave;
+    for (int e0 = 0; e0 < nl; e0 += kBatch * kLoopThreads) {
+      u32x4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = min(e0 + u * kLoopThreads + tid, nl - 1);
+        const int ln = e & 63, kb = (e >> 6) % KB, jj = (e >> 6) / KB;
+        const int gg = ln >> 4;
+        // (lanes past r read column 0 and store zeros: straight code)
+        const bool kok = kb * 32 + 8 * gg < r;
+        v[u] = load16(w2_row(nreg + jj, ln & 15) + (kok ? kb * 32 + 8 * gg : 0));
+        v[u] = kok ? v[u] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + u * kLoopThreads + tid;
+        if (e < nl) w2l[e] = v[u];
+      }
+    }
   }
   if (tid < R) prev_s[tid] = prev0_ok(p, tid) ? static_cast<int>(p.prev0[tid]) : 0;
 
