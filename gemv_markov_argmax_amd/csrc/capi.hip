@@ -76,9 +76,13 @@ size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V) {
   return dspark::markov_workspace_bytes(num_reqs, k, V);
 }
 
-dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V, const uint16_t* w1,
-                                   const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0, int k,
-                                   int64_t* ids_out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dspark_status markov_checks(const float* base, int num_reqs, int B, int V, const uint16_t* w1, const uint16_t* w2,
+                            int r, const int64_t* d2t, const int64_t* prev0, int k, const int64_t* ids_out,
+                            const void* workspace, size_t workspace_bytes) {
   if (!base || !w1 || !w2 || !prev0 || !ids_out) return DSPARK_ERR_NULL;
   if (num_reqs < 1 || num_reqs > 16 || B < 1 || V < 1 || k < 1 || k > B || k > 32 || r < 8 || r > 1024 || (r % 8) != 0)
     return DSPARK_ERR_SHAPE;
@@ -88,18 +92,73 @@ dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V
   const size_t need = dspark::markov_workspace_bytes(num_reqs, k, V);
   if (!workspace || workspace_bytes < need) return DSPARK_ERR_WORKSPACE;
   if (!aligned(workspace, 8)) return DSPARK_ERR_ALIGN;
-  return from_hip(dspark::launch_markov(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,
-                                        static_cast<hipStream_t>(stream)));
+  return DSPARK_OK;
 }
 
-dspark_status dspark_conf_probe(const float* x, int M, int D, const uint16_t* w, float bias, float threshold,
-                                float* logit_out, int32_t* pass_out, void* stream) {
+dspark_status probe_checks(const float* x, int M, int D, const uint16_t* w, const float* logit_out,
+                           const int32_t* pass_out) {
   if (!x || !w || !logit_out) return DSPARK_ERR_NULL;
   if (M < 1 || D < 8 || (D % 8) != 0) return DSPARK_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(logit_out, 4) || (pass_out && !aligned(pass_out, 4)))
     return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V, const uint16_t* w1,
+                                   const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0, int k,
+                                   int64_t* ids_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const dspark_status st =
+      markov_checks(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace, workspace_bytes);
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_markov(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,
+                                        nullptr, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_conf_probe(const float* x, int M, int D, const uint16_t* w, float bias, float threshold,
+                                float* logit_out, int32_t* pass_out, void* stream) {
+  const dspark_status st = probe_checks(x, M, D, w, logit_out, pass_out);
+  if (st != DSPARK_OK) return st;
   return from_hip(dspark::launch_probe(x, M, D, w, bias, threshold, logit_out, pass_out,
                                        static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B, int V, const uint16_t* w1,
+                                         const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0, int k,
+                                         int64_t* ids_out, void* workspace, size_t workspace_bytes,
+                                         const float* probe_x, int probe_M, int probe_D, const uint16_t* probe_w,
+                                         float probe_bias, float probe_threshold, float* logit_out,
+                                         int32_t* pass_out, void* stream) {
+  dspark_status st =
+      markov_checks(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace, workspace_bytes);
+  if (st == DSPARK_OK) st = probe_checks(probe_x, probe_M, probe_D, probe_w, logit_out, pass_out);
+  if (st != DSPARK_OK) return st;
+  const dspark::ProbeArgs pa{probe_x, probe_M, probe_D, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
+  return from_hip(dspark::launch_markov(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace, &pa,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float* H, int num_reqs, int B,
+                                 const uint16_t* w1, const uint16_t* w2, int r, const int64_t* d2t,
+                                 const int64_t* prev0, int k, const uint16_t* probe_w, float probe_bias,
+                                 float probe_threshold, float* base_out, int64_t* ids_out, float* logit_out,
+                                 int32_t* pass_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_reqs < 1 || num_reqs > 16 || B < 1 || B > (1 << 20)) return DSPARK_ERR_SHAPE;
+  const int rows = num_reqs * B;
+  dspark_status st = gemv_checks(W_lm, V, d, H, rows, base_out);
+  if (st == DSPARK_OK)
+    st = markov_checks(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace, workspace_bytes);
+  if (st == DSPARK_OK && probe_w) st = probe_checks(H, rows, d, probe_w, logit_out, pass_out);
+  if (st != DSPARK_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dspark::launch_gemv(W_lm, V, d, H, rows, base_out, s);
+  if (e != hipSuccess) return DSPARK_ERR_HIP;
+  const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
+  return from_hip(dspark::launch_markov(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,
+                                        probe_w ? &pa : nullptr, s));
 }
 
 }  // extern "C"

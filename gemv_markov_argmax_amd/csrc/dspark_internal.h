@@ -87,6 +87,49 @@ __device__ __forceinline__ void pair_halves(float4 mine, int i, float4& x0, floa
   x1 = upper ? mine : other;
 }
 
+// Chain h (0..3) of the confidence probe's sum over one row of D entries
+// (D % 8 == 0): lane l of a wave accumulates t = 8l + 512h + 2048j,
+// j = 0, 1, ..., eight terms at a time in t order, in one fp32 FMA chain;
+// the lanes are then combined by a fixed butterfly, so every lane ends with
+// the chain's total. A row's sum is (c0 + c1) + (c2 + c3) over its four
+// chains, an order fixed by D alone, whichever waves compute the chains.
+// Up to NIN iterations' loads are in flight at once (NIN = 4: rows up to
+// 8192 entries are a single round trip).
+template <int NIN>
+__device__ __forceinline__ float probe_chain(const float* __restrict__ x, int D, const uint16_t* __restrict__ w,
+                                             int lane, int h) {
+  float acc = 0.f;
+  for (int t0 = 8 * lane + 512 * h; t0 < D; t0 += NIN * 2048) {
+    u32x4 wb[NIN];
+    float4 xa[NIN], xb[NIN];
+#pragma unroll
+    for (int u = 0; u < NIN; ++u) {
+      const int t = min(t0 + 2048 * u, D - 8);  // (clamped: a load past D is issued but never used)
+      wb[u] = load16(w + t);
+      xa[u] = *reinterpret_cast<const float4*>(x + t);
+      xb[u] = *reinterpret_cast<const float4*>(x + t + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < NIN; ++u) {
+      if (t0 + 2048 * u >= D) break;
+      acc = __builtin_fmaf(xa[u].x, __uint_as_float(wb[u].x << 16), acc);
+      acc = __builtin_fmaf(xa[u].y, __uint_as_float(wb[u].x & 0xFFFF0000u), acc);
+      acc = __builtin_fmaf(xa[u].z, __uint_as_float(wb[u].y << 16), acc);
+      acc = __builtin_fmaf(xa[u].w, __uint_as_float(wb[u].y & 0xFFFF0000u), acc);
+      acc = __builtin_fmaf(xb[u].x, __uint_as_float(wb[u].z << 16), acc);
+      acc = __builtin_fmaf(xb[u].y, __uint_as_float(wb[u].z & 0xFFFF0000u), acc);
+      acc = __builtin_fmaf(xb[u].z, __uint_as_float(wb[u].w << 16), acc);
+      acc = __builtin_fmaf(xb[u].w, __uint_as_float(wb[u].w & 0xFFFF0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  return acc;
+}
+
+// The probe's logit from the four chain totals.
+__device__ __forceinline__ float probe_logit(const float* c, float bias) { return ((c[0] + c[1]) + (c[2] + c[3])) + bias; }
+
 // Round a finite float to bf16, nearest-even, returning the 16-bit pattern.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -145,11 +188,23 @@ bool gemv_shape_fits(int N, int K, int M);
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
                        hipStream_t stream);
 
-// Markov loop; see dspark_markov_sample.
+// The confidence probe's arguments (see dspark_conf_probe).
+struct ProbeArgs {
+  const float* x;  // [M, D]
+  int M, D;
+  const uint16_t* w;  // [D]
+  float bias, threshold;
+  float* logit;   // [M]
+  int32_t* pass;  // [M] or null
+};
+
+// Markov loop; see dspark_markov_sample. With `probe` non-null the same
+// launch also computes the confidence probe, bit-identical to launch_probe.
 size_t markov_workspace_bytes(int num_reqs, int k, int V);
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
-                         int k, int64_t* ids, void* workspace, hipStream_t stream);
+                         int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
+                         hipStream_t stream);
 
 hipError_t launch_probe(const float* x, int M, int D, const uint16_t* w, float bias,
                         float threshold, float* logit, int32_t* pass, hipStream_t stream);

@@ -86,6 +86,8 @@ struct MarkovParams {
   int lds_tiles;         // markov_w2 tiles held in LDS per workgroup
   int bstride;           // floats per request in the LDS base slice (>= 16 * tiles per workgroup)
   int base_in_lds;       // 0: base values are read straight from memory (slice too large)
+  int probe_on;          // nonzero: also compute the confidence probe described by `probe`
+  ProbeArgs probe;
 };
 
 __device__ __forceinline__ bool prev0_ok(const MarkovParams& p, int m) {
@@ -267,8 +269,38 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     }
   };
 
+  // The confidence probe, when asked for: it depends on nothing the loop
+  // computes, so it runs on the workgroups that are otherwise idle at the
+  // end, those that leave after publishing the last step (all but
+  // workgroup 0, or workgroup 0 alone when it is the only one). Each row
+  // goes to four waves, which compute its four chains exactly as the
+  // standalone probe kernel does, so the logits are the same bits. Called
+  // by whole workgroups only (it has barriers); the chain totals go to
+  // prev_s, which nothing reads after the prologue.
+  auto probe_rows = [&]() {
+    if (!p.probe_on) return;
+    const ProbeArgs& a = p.probe;
+    constexpr int kRowsPerWg = NW / 4;
+    const int wg = G > 1 ? static_cast<int>(blockIdx.x) - 1 : 0, nwg = G > 1 ? G - 1 : 1;
+    float* ctot = reinterpret_cast<float*>(prev_s);
+    __syncthreads();
+    for (int m0 = wg * kRowsPerWg; m0 < a.M; m0 += nwg * kRowsPerWg) {
+      const int m = m0 + w / 4;
+      const float c = m < a.M ? probe_chain<4>(a.x + static_cast<size_t>(m) * a.D, a.D, a.w, lane, w & 3) : 0.f;
+      if (lane == 0) ctot[w] = c;
+      __syncthreads();
+      if (tid < kRowsPerWg && m0 + tid < a.M) {
+        const float l = probe_logit(ctot + 4 * tid, a.bias);
+        a.logit[m0 + tid] = l;
+        if (a.pass) a.pass[m0 + tid] = l >= a.threshold ? 1 : 0;
+      }
+      __syncthreads();
+    }
+  };
+
   if (dead != 0u) {  // an earlier call gave up: report it and touch no slot
     if (blockIdx.x == 0) finish();
+    if (blockIdx.x != 0 || G == 1) probe_rows();
     return;
   }
 
@@ -411,6 +443,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     }
     if (last && blockIdx.x != 0) {  // only workgroup 0 needs the final step's winner
       clear_other();
+      probe_rows();
       return;
     }
     // The next step's base slice: waves that do not poll fetch and store it
@@ -479,6 +512,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     __syncthreads();  // the next step's A block and base slice are in LDS (and tok_s complete)
   }
   finish();
+  if (G == 1) probe_rows();
 }
 
 struct LoopPlan {
@@ -549,7 +583,8 @@ size_t markov_workspace_bytes(int num_reqs, int k, int V) {
 
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
-                         int k, int64_t* ids, void* workspace, hipStream_t stream) {
+                         int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
+                         hipStream_t stream) {
   const int cus = device_cu_count();
   if (cus <= 0) return hipErrorNoDevice;
   // Workgroups: one per CU, but at least ~16 tiles each. With fewer tiles a
@@ -582,6 +617,10 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
   prm.lds_tiles = pl.lds_tiles;
   prm.bstride = pl.bstride;
   prm.base_in_lds = pl.base_in_lds;
+  if (probe) {
+    prm.probe_on = 1;
+    prm.probe = *probe;
+  }
   if (pl.NW == 4) {  // r = 256 only
     return pl.base_in_lds ? launch_loop<4, 8, true>(prm, pl, cus, stream)
                           : launch_loop<4, 8, false>(prm, pl, cus, stream);

@@ -6,49 +6,28 @@
 // Section "Performance": GPU and CPU evaluations differ only in summation
 // order and make the same gating decisions.
 //
-// One workgroup per row. Each lane reads 8 bf16 weights (16 bytes) and 8
-// fp32 activations per iteration and accumulates them in one fp32 FMA
-// chain; lanes are then combined by a fixed butterfly and waves in index
-// order, so the result is deterministic.
+// One workgroup of four waves per row: wave h computes chain h of the sum
+// (lane l takes entries 8l + 512h + 2048j, eight at a time, in one fp32 FMA
+// chain, then a fixed butterfly), and the four chain totals are added in a
+// fixed order, so the result is deterministic and depends on D alone. A
+// row of up to 8192 entries is one round trip to memory. The Markov loop
+// computes the same chains in the same order when a draft round asks it
+// for the probe.
 #include "dspark_internal.h"
 
 namespace dspark {
 namespace {
 
-constexpr int kProbeThreads = 256;
-
-__global__ __launch_bounds__(kProbeThreads) void probe_kernel(const float* __restrict__ x, int D,
-                                                              const uint16_t* __restrict__ w, float bias,
-                                                              float threshold, float* __restrict__ logit,
-                                                              int32_t* __restrict__ pass) {
-  __shared__ float part[kProbeThreads / kWave];
-  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float* xr = x + static_cast<size_t>(m) * D;
-  float acc = 0.f;
-  for (int t = tid * 8; t < D; t += kProbeThreads * 8) {
-    const u32x4 wb = load16(w + t);
-    const float4 x0 = *reinterpret_cast<const float4*>(xr + t);
-    const float4 x1 = *reinterpret_cast<const float4*>(xr + t + 4);
-    acc = __builtin_fmaf(x0.x, __uint_as_float(wb.x << 16), acc);
-    acc = __builtin_fmaf(x0.y, __uint_as_float(wb.x & 0xFFFF0000u), acc);
-    acc = __builtin_fmaf(x0.z, __uint_as_float(wb.y << 16), acc);
-    acc = __builtin_fmaf(x0.w, __uint_as_float(wb.y & 0xFFFF0000u), acc);
-    acc = __builtin_fmaf(x1.x, __uint_as_float(wb.z << 16), acc);
-    acc = __builtin_fmaf(x1.y, __uint_as_float(wb.z & 0xFFFF0000u), acc);
-    acc = __builtin_fmaf(x1.z, __uint_as_float(wb.w << 16), acc);
-    acc = __builtin_fmaf(x1.w, __uint_as_float(wb.w & 0xFFFF0000u), acc);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) part[wv] = acc;
+__global__ __launch_bounds__(4 * kWave) void probe_kernel(ProbeArgs a) {
+  __shared__ float part[4];
+  const int m = blockIdx.x, lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+  const float c = probe_chain<4>(a.x + static_cast<size_t>(m) * a.D, a.D, a.w, lane, h);
+  if (lane == 0) part[h] = c;
   __syncthreads();
-  if (tid == 0) {
-    float s = part[0];
-#pragma unroll
-    for (int j = 1; j < kProbeThreads / kWave; ++j) s += part[j];
-    const float l = s + bias;
-    logit[m] = l;
-    if (pass) pass[m] = l >= threshold ? 1 : 0;
+  if (threadIdx.x == 0) {
+    const float l = probe_logit(part, a.bias);
+    a.logit[m] = l;
+    if (a.pass) a.pass[m] = l >= a.threshold ? 1 : 0;
   }
 }
 
@@ -56,9 +35,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_kernel(const float* __res
 
 hipError_t launch_probe(const float* x, int M, int D, const uint16_t* w, float bias, float threshold,
                         float* logit, int32_t* pass, hipStream_t stream) {
-  void* args[] = {&x, &D, &w, &bias, &threshold, &logit, &pass};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&probe_kernel), dim3(M), dim3(kProbeThreads), args, 0,
-                         stream);
+  ProbeArgs a{x, M, D, w, bias, threshold, logit, pass};
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&probe_kernel), dim3(M), dim3(4 * kWave), args, 0, stream);
 }
 
 }  // namespace dspark

@@ -27,6 +27,10 @@ SIGNATURES = {
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
+    "dspark_markov_sample_probe": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
+                                        _p, _i, _i, _p, _f, _f, _p, _p, _p]),
+    "dspark_draft_round": (_i, [_p, _i, _i, _p, _i, _i, _p, _p, _i, _p, _p, _i, _p, _f, _f,
+                                _p, _p, _p, _p, _p, _sz, _p]),
 }
 
 
@@ -117,10 +121,15 @@ def markov_workspace(num_reqs: int, k: int, V: int, device) -> torch.Tensor:
 
 def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor, k: int,
                   d2t: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+                  workspace: torch.Tensor | None = None, probe: dict | None = None) -> torch.Tensor:
     """Drafted ids [R, k] int64 of the on-device Markov loop (dspark_markov_sample).
 
     base fp32 [R, B, V]; w1, w2 bf16 [V, r]; prev0 int64 [R]; d2t int64 [V] or None.
+    ``probe``, when given, is a dict with the arguments of conf_probe (x, w,
+    and optionally bias, threshold, logit_out, pass_out): the probe then runs
+    in the same launch (dspark_markov_sample_probe) and its outputs are
+    written to probe["logit_out"] and probe["pass_out"] (allocated here when
+    absent).
     """
     _dev(base, torch.float32, "base", 3)
     _dev(w1, torch.bfloat16, "w1", 2)
@@ -144,16 +153,23 @@ def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0:
     if workspace is None:
         workspace = markov_workspace(R, k, V, base.device)
     _dev(workspace, torch.uint8, "workspace", 1)
-    _check(lib().dspark_markov_sample(base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr,
-                                      prev0.data_ptr(), k, out.data_ptr(), workspace.data_ptr(),
-                                      workspace.numel(), _stream(base)))
+    if probe is None:
+        _check(lib().dspark_markov_sample(base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr,
+                                          prev0.data_ptr(), k, out.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream(base)))
+        return out
+    x, pw = probe["x"], probe["w"]
+    lo, pa = _probe_outputs(x, pw, probe.get("logit_out"), probe.get("pass_out"), probe.get("want_pass", True))
+    probe["logit_out"], probe["pass_out"] = lo, pa
+    _check(lib().dspark_markov_sample_probe(
+        base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr, prev0.data_ptr(), k, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), x.data_ptr(), x.shape[0], x.shape[1], pw.data_ptr(),
+        float(probe.get("bias", 0.0)), float(probe.get("threshold", 0.0)), lo.data_ptr(),
+        None if pa is None else pa.data_ptr(), _stream(base)))
     return out
 
 
-def conf_probe(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, threshold: float = 0.0,
-               logit_out: torch.Tensor | None = None, pass_out: torch.Tensor | None = None,
-               want_pass: bool = True):
-    """(logit fp32 [M], pass int32 [M] or None) of the confidence probe (dspark_conf_probe)."""
+def _probe_outputs(x, w, logit_out, pass_out, want_pass):
     _dev(x, torch.float32, "x", 2)
     _dev(w, torch.bfloat16, "w", 1)
     M, D = x.shape
@@ -166,10 +182,92 @@ def conf_probe(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, threshold: f
         pass_out = torch.empty(M, dtype=torch.int32, device=x.device)
     if pass_out is not None:
         _dev(pass_out, torch.int32, "pass_out", 1)
+    if logit_out.shape[0] != M or (pass_out is not None and pass_out.shape[0] != M):
+        raise ValueError("logit_out and pass_out must have M entries")
+    return logit_out, pass_out
+
+
+def conf_probe(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, threshold: float = 0.0,
+               logit_out: torch.Tensor | None = None, pass_out: torch.Tensor | None = None,
+               want_pass: bool = True):
+    """(logit fp32 [M], pass int32 [M] or None) of the confidence probe (dspark_conf_probe)."""
+    logit_out, pass_out = _probe_outputs(x, w, logit_out, pass_out, want_pass)
+    M, D = x.shape
     _check(lib().dspark_conf_probe(x.data_ptr(), M, D, w.data_ptr(), float(bias), float(threshold),
                                    logit_out.data_ptr(), None if pass_out is None else pass_out.data_ptr(),
                                    _stream(x)))
     return logit_out, pass_out
+
+
+def draft_round(W_lm: torch.Tensor, H: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor,
+                B: int, k: int, probe_w: torch.Tensor | None = None, probe_bias: float = 0.0,
+                probe_threshold: float = 0.0, d2t: torch.Tensor | None = None,
+                base_out: torch.Tensor | None = None, ids_out: torch.Tensor | None = None,
+                logit_out: torch.Tensor | None = None, pass_out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, want_pass: bool = True) -> dict:
+    """One draft round (dspark_draft_round): lm_head, Markov loop and, when
+    probe_w is given, the probe on every row of H. Returns a dict with base
+    fp32 [R, B, V], ids int64 [R, k], logit fp32 [R*B] and pass int32 [R*B]
+    (the last two None without a probe).
+
+    W_lm bf16 [V, d]; H fp32 [R*B, d]; w1, w2 bf16 [V, r]; prev0 int64 [R].
+    """
+    _dev(W_lm, torch.bfloat16, "W_lm", 2)
+    _dev(H, torch.float32, "H", 2)
+    _dev(w1, torch.bfloat16, "w1", 2)
+    _dev(w2, torch.bfloat16, "w2", 2)
+    _dev(prev0, torch.int64, "prev0", 1)
+    V, d = W_lm.shape
+    R = prev0.shape[0]
+    r = w1.shape[1]
+    if tuple(H.shape) != (R * B, d):
+        raise ValueError("H must be [num_reqs * B, d]")
+    if tuple(w1.shape) != (V, r) or tuple(w2.shape) != (V, r):
+        raise ValueError("w1 and w2 must both be [V, r]")
+    dev = H.device
+    d2t_ptr = None
+    if d2t is not None:
+        _dev(d2t, torch.int64, "d2t", 1)
+        if d2t.shape[0] != V:
+            raise ValueError("d2t must have V entries")
+        d2t_ptr = d2t.data_ptr()
+    if base_out is None:
+        base_out = torch.empty((R, B, V), dtype=torch.float32, device=dev)
+    _dev(base_out, torch.float32, "base_out", 3)
+    if tuple(base_out.shape) != (R, B, V):
+        raise ValueError("base_out must be [num_reqs, B, V]")
+    if ids_out is None:
+        ids_out = torch.empty((R, k), dtype=torch.int64, device=dev)
+    _dev(ids_out, torch.int64, "ids_out", 2)
+    if tuple(ids_out.shape) != (R, k):
+        raise ValueError("ids_out must be [num_reqs, k]")
+    pw_ptr = lo_ptr = pa_ptr = None
+    if probe_w is not None:
+        _dev(probe_w, torch.bfloat16, "probe_w", 1)
+        if probe_w.shape[0] != d:
+            raise ValueError("probe_w must have d entries")
+        pw_ptr = probe_w.data_ptr()
+        if logit_out is None:
+            logit_out = torch.empty(R * B, dtype=torch.float32, device=dev)
+        _dev(logit_out, torch.float32, "logit_out", 1)
+        if pass_out is None and want_pass:
+            pass_out = torch.empty(R * B, dtype=torch.int32, device=dev)
+        if pass_out is not None:
+            _dev(pass_out, torch.int32, "pass_out", 1)
+            pa_ptr = pass_out.data_ptr()
+        if logit_out.shape[0] != R * B or (pass_out is not None and pass_out.shape[0] != R * B):
+            raise ValueError("logit_out and pass_out must have num_reqs * B entries")
+        lo_ptr = logit_out.data_ptr()
+    else:
+        logit_out = pass_out = None
+    if workspace is None:
+        workspace = markov_workspace(R, k, V, dev)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    _check(lib().dspark_draft_round(W_lm.data_ptr(), V, d, H.data_ptr(), R, B, w1.data_ptr(), w2.data_ptr(), r,
+                                    d2t_ptr, prev0.data_ptr(), k, pw_ptr, float(probe_bias), float(probe_threshold),
+                                    base_out.data_ptr(), ids_out.data_ptr(), lo_ptr, pa_ptr, workspace.data_ptr(),
+                                    workspace.numel(), _stream(H)))
+    return dict(base=base_out, ids=ids_out, logit=logit_out, passed=pass_out)
 
 
 def bf16_from_bits(bits, device) -> torch.Tensor:

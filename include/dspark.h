@@ -7,7 +7,10 @@
  * verify pass:
  *   1. weight-stationary small-M GEMVs (draft projections, lm_head),
  *   2. the k-step Markov-biased greedy sampling loop, entirely on device,
- *   3. the confidence probe.
+ *   3. the confidence probe,
+ * each as its own entry point, the loop and probe in one launch
+ * (dspark_markov_sample_probe), and the lm_head, loop and probe together as
+ * one round (dspark_draft_round).
  *
  * Sources cited below (a reader has the pages themselves):
  *   [DS772]  ds4 #772, "dspark: cut per-cycle CUDA overheads (single-draft
@@ -173,6 +176,72 @@ dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V
 dspark_status dspark_conf_probe(const float* x, int M, int D, const uint16_t* w, float bias,
                                 float threshold, float* logit_out, int32_t* pass_out,
                                 void* stream);
+
+/*
+ * dspark_markov_sample_probe -- dspark_markov_sample and dspark_conf_probe
+ * in one launch.
+ *
+ * [W7] "The fix" for the loop and [DS772] "Summary" for the probe, as in
+ * the two calls it replaces. The probe depends on nothing the loop computes;
+ * it runs on the waves that finish the loop early (every workgroup but the
+ * one that waits for the last step's winner), so it adds no launch and
+ * almost no time to the round. Use it where the base logits come from
+ * elsewhere (another lm_head implementation); dspark_draft_round is
+ * dspark_lm_head followed by this call.
+ *
+ * Arguments: those of dspark_markov_sample, then those of dspark_conf_probe
+ * (probe_x fp32 [probe_M, probe_D], probe_w bf16 [probe_D], ...), with the
+ * same layouts, sizes, alignment and errors. Results are bit-identical to
+ * the two separate calls.
+ */
+dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B, int V,
+                                         const uint16_t* w1, const uint16_t* w2, int r,
+                                         const int64_t* d2t, const int64_t* prev0, int k,
+                                         int64_t* ids_out, void* workspace, size_t workspace_bytes,
+                                         const float* probe_x, int probe_M, int probe_D,
+                                         const uint16_t* probe_w, float probe_bias,
+                                         float probe_threshold, float* logit_out, int32_t* pass_out,
+                                         void* stream);
+
+/*
+ * dspark_draft_round -- one whole draft round: lm_head, the Markov loop and
+ * the confidence probe on every drafted row, in two launches.
+ *
+ * [W7] "The fix": the round is a composition of device primitives in which
+ * only the final ids leave the device; the base logits stay in device
+ * memory between the lm_head and the loop. [DS772] "Summary": the probe of
+ * each drafted row is computed on the device as well and only its 4-byte
+ * logit goes back.
+ *
+ * Equivalent to, in this order on `stream`,
+ *   dspark_lm_head(W_lm, V, d, H, num_reqs * B, base_out)
+ *   dspark_markov_sample(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, ...)
+ *   dspark_conf_probe(H, num_reqs * B, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out)
+ * and bit-identical to those three calls. The probe runs inside the Markov
+ * loop's launch (as in dspark_markov_sample_probe), so the round is two
+ * kernels instead of three.
+ *
+ *   W_lm      bf16  [V, d]                 16-byte aligned
+ *   H         fp32  [num_reqs * B, d]      16-byte aligned (hidden states, also the probe's x)
+ *   w1, w2    bf16  [V, r]                 16-byte aligned
+ *   d2t       int64 [V] or NULL
+ *   prev0     int64 [num_reqs]
+ *   probe_w   bf16  [d] or NULL (no probe; logit_out and pass_out are then ignored)
+ *   base_out  fp32  [num_reqs, B, V]       4-byte aligned, overwritten (the base logits)
+ *   ids_out   int64 [num_reqs, k]          overwritten
+ *   logit_out fp32  [num_reqs * B]         overwritten (required when probe_w is given)
+ *   pass_out  int32 [num_reqs * B] or NULL
+ *   workspace as for dspark_markov_sample (zero-filled once before first use)
+ * Sizes and errors: those of the three calls above; every check is made
+ * before anything is enqueued.
+ */
+dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float* H, int num_reqs,
+                                 int B, const uint16_t* w1, const uint16_t* w2, int r,
+                                 const int64_t* d2t, const int64_t* prev0, int k,
+                                 const uint16_t* probe_w, float probe_bias, float probe_threshold,
+                                 float* base_out, int64_t* ids_out, float* logit_out,
+                                 int32_t* pass_out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,8 @@ def declared():
 def test_header_declares_the_entry_points():
     names = declared()
     for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
-              "dspark_markov_workspace_bytes", "dspark_status_string"]:
+              "dspark_markov_sample_probe", "dspark_draft_round", "dspark_markov_workspace_bytes",
+              "dspark_status_string"]:
         assert n in names
 
 
@@ -112,6 +113,58 @@ def test_probe_errors(L):
     assert f(A, 7, 60, A, 0.0, 0.0, A2, None, None) == ERR_SHAPE
     assert f(MIS, 7, 64, A, 0.0, 0.0, A2, None, None) == ERR_ALIGN
     assert f(A, 7, 64, A, 0.0, 0.0, A2, A2 + 2, None) == ERR_ALIGN
+
+
+def test_markov_sample_probe_errors(L):
+    f = L.dspark_markov_sample_probe
+    ws = L.dspark_markov_workspace_bytes(1, 7, 151936)
+    good = dict(base=A, R=1, B=7, V=151936, w1=A, w2=A2, r=256, d2t=None, prev0=A, k=7, ids=A2, ws=A, wsb=ws,
+                x=A2, M=7, D=4096, pw=A, logit=A2, ps=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["base"], a["R"], a["B"], a["V"], a["w1"], a["w2"], a["r"], a["d2t"], a["prev0"], a["k"],
+                 a["ids"], a["ws"], a["wsb"], a["x"], a["M"], a["D"], a["pw"], 0.0, 0.0, a["logit"], a["ps"], None)
+    assert call(base=None) == ERR_NULL
+    assert call(x=None) == ERR_NULL
+    assert call(pw=None) == ERR_NULL
+    assert call(logit=None) == ERR_NULL
+    assert call(k=8) == ERR_SHAPE
+    assert call(M=0) == ERR_SHAPE
+    assert call(D=12) == ERR_SHAPE
+    assert call(x=MIS) == ERR_ALIGN
+    assert call(ps=A + 2) == ERR_ALIGN
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+
+
+def test_draft_round_errors(L):
+    f = L.dspark_draft_round
+    ws = L.dspark_markov_workspace_bytes(1, 7, 151936)
+    good = dict(W=A, V=151936, d=4096, H=A2, R=1, B=7, w1=A, w2=A2, r=256, d2t=None, prev0=A, k=7, pw=A,
+                base=A2, ids=A, logit=A2, ps=None, ws=A, wsb=ws)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["W"], a["V"], a["d"], a["H"], a["R"], a["B"], a["w1"], a["w2"], a["r"], a["d2t"], a["prev0"],
+                 a["k"], a["pw"], 0.0, 0.0, a["base"], a["ids"], a["logit"], a["ps"], a["ws"], a["wsb"], None)
+    assert call(W=None) == ERR_NULL
+    assert call(H=None) == ERR_NULL
+    assert call(base=None) == ERR_NULL
+    assert call(w2=None) == ERR_NULL
+    assert call(ids=None) == ERR_NULL
+    assert call(logit=None) == ERR_NULL                 # a probe needs its output
+    assert call(R=0) == ERR_SHAPE
+    assert call(R=17) == ERR_SHAPE
+    assert call(B=0) == ERR_SHAPE
+    assert call(d=4100) == ERR_SHAPE                    # d % 8 != 0
+    assert call(k=8) == ERR_SHAPE                       # k > B
+    assert call(r=2048) == ERR_SHAPE
+    assert call(H=MIS) == ERR_ALIGN
+    assert call(base=A + 2) == ERR_ALIGN
+    assert call(pw=MIS) == ERR_ALIGN
+    assert call(ps=A + 2) == ERR_ALIGN
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
 
 
 def test_binding_has_no_cpu_path(L):

@@ -330,6 +330,136 @@ def test_round_chained(dev, name):
     probe_close(lg.cpu().numpy(), ps.cpu().numpy(), ref["logit"], ref["passed"], float(inp["probe_threshold"]))
 
 
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head", "reduced_vocab_batched", "lane27b"])
+def test_draft_round_fused(dev, name):
+    """dspark_draft_round (the probe inside the Markov launch) gives the same
+    bits as the three separate calls, and matches the oracle."""
+    inp, t = _round_tensors(name, dev)
+    say(f"[draft_round {name}] seed={inp['seed']}")
+    R, B, k = inp["num_reqs"], inp["B"], inp["k"]
+    sep = [x.clone() for x in _run_round(inp, t)]
+    out = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, probe_w=t["pw"],
+                             probe_bias=float(inp["probe_bias"]), probe_threshold=float(inp["probe_threshold"]))
+    torch.cuda.synchronize()
+    assert torch.equal(out["base"].view(R * B, -1), sep[0])
+    assert torch.equal(out["ids"], sep[1])
+    assert torch.equal(out["logit"], sep[2])
+    assert torch.equal(out["passed"], sep[3])
+    if name in ("tiny", "reduced_vocab_batched"):
+        ref = oracle.draft_round(inp["W_lm"], inp["H"], inp["w1"], inp["w2"], inp["prev0"], R, B, k,
+                                 inp["probe_w"], inp["probe_bias"], inp["probe_threshold"])
+        logits_close(out["base"].view(R * B, -1).cpu().numpy(), ref["base"], f"draft_round {name} logits")
+        check_markov(out["ids"].cpu().numpy(), ref["base32"], inp["w1"], inp["w2"], inp["prev0"], k)
+        probe_close(out["logit"].cpu().numpy(), out["passed"].cpu().numpy(), ref["logit"], ref["passed"],
+                    float(inp["probe_threshold"]))
+
+
+# (R, B, k, V, d, r): one workgroup (V <= 256: the probe runs after workgroup
+# 0's last step), and more probe rows than the waves that compute them.
+SMALL_ROUNDS = [(2, 3, 3, 200, 64, 16), (16, 2, 2, 600, 136, 64), (3, 5, 4, 1000, 8, 8)]
+
+
+@pytest.mark.parametrize("R,B,k,V,d,r", SMALL_ROUNDS)
+def test_draft_round_small_grids(dev, R, B, k, V, d, r):
+    seed = 5100 + V + d
+    say(f"[draft_round small] R={R} B={B} k={k} V={V} d={d} r={r} seed={seed}")
+    W, H = synth.gemv_inputs(R * B, V, d, seed)
+    _, w1, w2, prev0, _ = synth.markov_inputs(R, 1, V, r, seed)
+    _, pw = synth.probe_inputs(1, d, seed)
+    thr = 0.01
+    out = _ops().draft_round(_bf(W, dev), _up(H, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), B, k,
+                             probe_w=_bf(pw, dev), probe_bias=-0.02, probe_threshold=thr)
+    torch.cuda.synchronize()
+    ref = oracle.draft_round(W, H, w1, w2, prev0, R, B, k, pw, -0.02, thr)
+    logits_close(out["base"].view(R * B, -1).cpu().numpy(), ref["base"], "draft_round small logits")
+    check_markov(out["ids"].cpu().numpy(), ref["base32"], w1, w2, prev0, k)
+    probe_close(out["logit"].cpu().numpy(), out["passed"].cpu().numpy(), ref["logit"], ref["passed"], thr)
+    lg, ps = _ops().conf_probe(_up(H, dev), _bf(pw, dev), -0.02, thr)
+    torch.cuda.synchronize()
+    assert torch.equal(out["logit"], lg) and torch.equal(out["passed"], ps)
+
+
+@pytest.mark.parametrize("R,B,k,V,r,M,D", [(1, 7, 7, 151936, 256, 7, 7424), (8, 9, 9, 32000, 256, 3, 7432),
+                                             (2, 3, 2, 200, 16, 40, 64)])
+def test_markov_sample_probe(dev, R, B, k, V, r, M, D):
+    """The loop and a probe of unrelated shape in one launch: the same bits as
+    dspark_markov_sample and dspark_conf_probe called separately."""
+    seed = 7300 + M
+    say(f"[markov_sample_probe] R={R} B={B} k={k} V={V} r={r} probe M={M} D={D} seed={seed}")
+    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, seed)
+    x, pw = synth.probe_inputs(M, D, seed)
+    args = (_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k)
+    probe = dict(x=_up(x, dev), w=_bf(pw, dev), bias=0.125, threshold=0.0)
+    ids = _ops().markov_sample(*args, probe=probe)
+    ids_sep = _ops().markov_sample(*args)
+    lg, ps = _ops().conf_probe(probe["x"], probe["w"], 0.125, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_sep)
+    assert torch.equal(probe["logit_out"], lg) and torch.equal(probe["pass_out"], ps)
+    ref_l, ref_p = oracle.conf_probe(x, pw, 0.125, 0.0)
+    probe_close(lg.cpu().numpy(), ps.cpu().numpy(), ref_l, ref_p, 0.0)
+    if V <= 32000:
+        check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
+
+
+def test_draft_round_without_probe_and_watchdog(dev):
+    """Without probe_w the round writes no probe output; with the watchdog
+    word set the ids are -2 and the probe is still computed."""
+    inp, t = _round_tensors("tiny", dev)
+    say("[draft_round no probe / watchdog] tiny")
+    R, B, V, k = inp["num_reqs"], inp["B"], inp["V"], inp["k"]
+    ws = _ops().markov_workspace(R, k, V, dev)
+    lg = torch.full((R * B,), 7.0, device=dev)
+    out = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws, logit_out=lg)
+    torch.cuda.synchronize()
+    assert out["logit"] is None and torch.all(lg == 7.0)
+    good = out["ids"].clone()
+    ws[0] = 1  # the watchdog word, as a timed-out wait leaves it
+    out = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, probe_w=t["pw"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(out["ids"] == -2)
+    ref_lg, ref_ps = _ops().conf_probe(t["H"], t["pw"])
+    torch.cuda.synchronize()
+    assert torch.equal(out["logit"], ref_lg) and torch.equal(out["passed"], ref_ps)
+    ws.zero_()
+    out = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out["ids"], good)
+
+
+def test_draft_round_graph_replay(dev):
+    """dspark_draft_round recorded in a HIP graph and replayed with eager work
+    between replays: every replay equals the eager result."""
+    inp, t = _round_tensors("reduced_vocab_batched", dev)
+    say("[draft_round graph replay] reduced_vocab_batched")
+    R, B, V, k = inp["num_reqs"], inp["B"], inp["V"], inp["k"]
+    ops = _ops()
+    bufs = dict(base_out=torch.empty(R, B, V, device=dev), ids_out=torch.empty(R, k, dtype=torch.int64, device=dev),
+                logit_out=torch.empty(R * B, device=dev), pass_out=torch.empty(R * B, dtype=torch.int32, device=dev),
+                workspace=ops.markov_workspace(R, k, V, dev))
+
+    def run():
+        return ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, probe_w=t["pw"], **bufs)
+    eager = {n: x.clone() for n, x in run().items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        for n in ("base_out", "ids_out", "logit_out"):
+            bufs[n].fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, b in zip(("base_out", "ids_out", "logit_out", "pass_out"), ("base", "ids", "logit", "passed")):
+            assert torch.equal(bufs[n], eager[b]), f"replay {rep}: {n} differs"
+        _ = ops.lm_head(t["W"], t["H"])  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_round_graph_replay(dev):
     """The whole round recorded once in a HIP graph and replayed, with eager
     work between replays: every replay equals the eager result."""
