@@ -4,9 +4,9 @@
 One step = one draft round of the chosen head workload, every row of the hot
 path, in order on one stream (dspark_draft_round): lm_head GEMV over all
 drafted rows -> k-step on-device Markov loop, with the confidence probe on
-every drafted row computed in the same launch -> one asynchronous copy of
-the drafted ids and probe logits into pinned host memory. Inputs are seeded
-synthetic tensors already resident in HBM when timing starts.
+every drafted row computed in the same launch; the drafted ids and probe
+logits are stored by the kernels straight into pinned host memory. Inputs
+are seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints one JSON line (stdout). Progress goes to stderr.
 
@@ -270,13 +270,13 @@ def main():
     pw = ops.bf16_from_bits(inp["probe_w"], dev)
     logits = torch.empty(rows, V, device=dev)
     ws = ops.markov_workspace(R, k, V, dev)
-    # Drafted ids and probe logits share one device buffer so that a single
-    # asynchronous copy brings the round's results to pinned host memory.
-    out_dev = torch.empty(R * k * 8 + rows * 4, dtype=torch.uint8, device=dev)
-    ids = out_dev[: R * k * 8].view(torch.int64).view(R, k)
-    plog = out_dev[R * k * 8:].view(torch.float32)
-    ppass = torch.empty(rows, dtype=torch.int32, device=dev)
-    out_host = torch.empty(out_dev.numel(), dtype=torch.uint8, pin_memory=True)
+    # The round's results (drafted ids, probe logits and gates) are stored by
+    # the kernels straight into pinned host memory mapped for the device: no
+    # copy follows the round.
+    out_host = torch.empty(R * k * 8 + rows * 8, dtype=torch.uint8, pin_memory=True)
+    ids = out_host[: R * k * 8].view(torch.int64).view(R, k)
+    plog = out_host[R * k * 8: R * k * 8 + rows * 4].view(torch.float32)
+    ppass = out_host[R * k * 8 + rows * 4:].view(torch.int32)
     bias, thr = float(inp["probe_bias"]), float(inp["probe_threshold"])
     torch.cuda.synchronize()
 
@@ -295,11 +295,11 @@ def main():
         ops.conf_probe(H, pw, bias, thr, logit_out=plog, pass_out=ppass)
 
     # A round is dspark_draft_round: the lm_head launch, then the Markov loop
-    # with the probe on its idle waves, in order on one stream; then one
-    # asynchronous copy of the ids and probe logits. In the rounds that carry
-    # HIP events around the lm_head, the same two launches are issued by
-    # their own entry points (dspark_lm_head, dspark_markov_sample_probe),
-    # so that the events can sit between them.
+    # with the probe on its idle waves, in order on one stream, the results
+    # landing in host memory. In the rounds that carry HIP events around the
+    # lm_head, the same two launches are issued by their own entry points
+    # (dspark_lm_head, dspark_markov_sample_probe), so that the events can
+    # sit between them.
     main_stream = torch.cuda.current_stream()
 
     def one_round(ev=None):
@@ -312,18 +312,18 @@ def main():
             lm()
             ev[1].record(main_stream)
             mk()
-        out_host.copy_(out_dev, non_blocking=True)
 
     log(f"[bench] warmup {args.warmup} rounds")
     for _ in range(args.warmup):
         one_round()
     torch.cuda.synchronize()
-    first_ids = out_host[: R * k * 8].view(torch.int64).view(R, k).numpy().copy()
+    first_ids = ids.numpy().copy()
 
     # Timed region: K whole rounds. HIP events bracket the lm_head launch (the
     # kernel the roofline entry is about) on the stream it runs on, in every
-    # EVERY-th round; an event record adds a few microseconds of idle time.
-    EVERY = 4
+    # EVERY-th round; a pair of event records costs the round ~20 us of idle
+    # time, so only a sample of the rounds carries them.
+    EVERY = 10
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(0, args.steps, EVERY)]
     log(f"[bench] timing {args.steps} rounds")
     torch.cuda.synchronize()

@@ -81,6 +81,36 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None
     return t
 
 
+_hip = None
+
+
+def _host_device_ptr(t: torch.Tensor) -> int:
+    """The device address of a pinned host tensor (hipHostGetDevicePointer of
+    the HIP runtime this process already uses)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    p = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(p), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not p.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({err}): the host tensor is not mapped for the device")
+    return p.value
+
+
+def _out_ptr(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None) -> int:
+    """Address of a small result array: a GPU tensor, or a pinned host tensor
+    (the kernel then stores the results straight into host memory)."""
+    if isinstance(t, torch.Tensor) and not t.is_cuda and t.is_pinned():
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous() or (ndim is not None and t.dim() != ndim):
+            raise ValueError(f"{name} must be contiguous with {ndim} dims")
+        return _host_device_ptr(t)
+    return _dev(t, dtype, name, ndim).data_ptr()
+
+
 def _gemv(entry, W, X, out):
     _dev(W, torch.bfloat16, "W", 2)
     _dev(X, torch.float32, "X", 2)
@@ -149,23 +179,25 @@ def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0:
         d2t_ptr = d2t.data_ptr()
     if out is None:
         out = torch.empty((R, k), dtype=torch.int64, device=base.device)
-    _dev(out, torch.int64, "out", 2)
+    if tuple(out.shape) != (R, k):
+        raise ValueError("out must be [num_reqs, k]")
+    out_ptr = _out_ptr(out, torch.int64, "out", 2)
     if workspace is None:
         workspace = markov_workspace(R, k, V, base.device)
     _dev(workspace, torch.uint8, "workspace", 1)
     if probe is None:
         _check(lib().dspark_markov_sample(base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr,
-                                          prev0.data_ptr(), k, out.data_ptr(), workspace.data_ptr(),
+                                          prev0.data_ptr(), k, out_ptr, workspace.data_ptr(),
                                           workspace.numel(), _stream(base)))
         return out
     x, pw = probe["x"], probe["w"]
-    lo, pa = _probe_outputs(x, pw, probe.get("logit_out"), probe.get("pass_out"), probe.get("want_pass", True))
+    lo, pa, lo_ptr, pa_ptr = _probe_outputs(x, pw, probe.get("logit_out"), probe.get("pass_out"),
+                                            probe.get("want_pass", True))
     probe["logit_out"], probe["pass_out"] = lo, pa
     _check(lib().dspark_markov_sample_probe(
-        base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr, prev0.data_ptr(), k, out.data_ptr(),
+        base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr, prev0.data_ptr(), k, out_ptr,
         workspace.data_ptr(), workspace.numel(), x.data_ptr(), x.shape[0], x.shape[1], pw.data_ptr(),
-        float(probe.get("bias", 0.0)), float(probe.get("threshold", 0.0)), lo.data_ptr(),
-        None if pa is None else pa.data_ptr(), _stream(base)))
+        float(probe.get("bias", 0.0)), float(probe.get("threshold", 0.0)), lo_ptr, pa_ptr, _stream(base)))
     return out
 
 
@@ -177,25 +209,23 @@ def _probe_outputs(x, w, logit_out, pass_out, want_pass):
         raise ValueError("w must have D entries")
     if logit_out is None:
         logit_out = torch.empty(M, dtype=torch.float32, device=x.device)
-    _dev(logit_out, torch.float32, "logit_out", 1)
+    lo_ptr = _out_ptr(logit_out, torch.float32, "logit_out", 1)
     if pass_out is None and want_pass:
         pass_out = torch.empty(M, dtype=torch.int32, device=x.device)
-    if pass_out is not None:
-        _dev(pass_out, torch.int32, "pass_out", 1)
+    pa_ptr = None if pass_out is None else _out_ptr(pass_out, torch.int32, "pass_out", 1)
     if logit_out.shape[0] != M or (pass_out is not None and pass_out.shape[0] != M):
         raise ValueError("logit_out and pass_out must have M entries")
-    return logit_out, pass_out
+    return logit_out, pass_out, lo_ptr, pa_ptr
 
 
 def conf_probe(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, threshold: float = 0.0,
                logit_out: torch.Tensor | None = None, pass_out: torch.Tensor | None = None,
                want_pass: bool = True):
     """(logit fp32 [M], pass int32 [M] or None) of the confidence probe (dspark_conf_probe)."""
-    logit_out, pass_out = _probe_outputs(x, w, logit_out, pass_out, want_pass)
+    logit_out, pass_out, lo_ptr, pa_ptr = _probe_outputs(x, w, logit_out, pass_out, want_pass)
     M, D = x.shape
     _check(lib().dspark_conf_probe(x.data_ptr(), M, D, w.data_ptr(), float(bias), float(threshold),
-                                   logit_out.data_ptr(), None if pass_out is None else pass_out.data_ptr(),
-                                   _stream(x)))
+                                   lo_ptr, pa_ptr, _stream(x)))
     return logit_out, pass_out
 
 
@@ -238,26 +268,15 @@ def draft_round(W_lm: torch.Tensor, H: torch.Tensor, w1: torch.Tensor, w2: torch
         raise ValueError("base_out must be [num_reqs, B, V]")
     if ids_out is None:
         ids_out = torch.empty((R, k), dtype=torch.int64, device=dev)
-    _dev(ids_out, torch.int64, "ids_out", 2)
     if tuple(ids_out.shape) != (R, k):
         raise ValueError("ids_out must be [num_reqs, k]")
+    ids_ptr = _out_ptr(ids_out, torch.int64, "ids_out", 2)
     pw_ptr = lo_ptr = pa_ptr = None
     if probe_w is not None:
-        _dev(probe_w, torch.bfloat16, "probe_w", 1)
         if probe_w.shape[0] != d:
             raise ValueError("probe_w must have d entries")
+        logit_out, pass_out, lo_ptr, pa_ptr = _probe_outputs(H, probe_w, logit_out, pass_out, want_pass)
         pw_ptr = probe_w.data_ptr()
-        if logit_out is None:
-            logit_out = torch.empty(R * B, dtype=torch.float32, device=dev)
-        _dev(logit_out, torch.float32, "logit_out", 1)
-        if pass_out is None and want_pass:
-            pass_out = torch.empty(R * B, dtype=torch.int32, device=dev)
-        if pass_out is not None:
-            _dev(pass_out, torch.int32, "pass_out", 1)
-            pa_ptr = pass_out.data_ptr()
-        if logit_out.shape[0] != R * B or (pass_out is not None and pass_out.shape[0] != R * B):
-            raise ValueError("logit_out and pass_out must have num_reqs * B entries")
-        lo_ptr = logit_out.data_ptr()
     else:
         logit_out = pass_out = None
     if workspace is None:
@@ -265,7 +284,7 @@ def draft_round(W_lm: torch.Tensor, H: torch.Tensor, w1: torch.Tensor, w2: torch
     _dev(workspace, torch.uint8, "workspace", 1)
     _check(lib().dspark_draft_round(W_lm.data_ptr(), V, d, H.data_ptr(), R, B, w1.data_ptr(), w2.data_ptr(), r,
                                     d2t_ptr, prev0.data_ptr(), k, pw_ptr, float(probe_bias), float(probe_threshold),
-                                    base_out.data_ptr(), ids_out.data_ptr(), lo_ptr, pa_ptr, workspace.data_ptr(),
+                                    base_out.data_ptr(), ids_ptr, lo_ptr, pa_ptr, workspace.data_ptr(),
                                     workspace.numel(), _stream(H)))
     return dict(base=base_out, ids=ids_out, logit=logit_out, passed=pass_out)
 

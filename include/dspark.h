@@ -26,6 +26,11 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller. The
  *    library never allocates, frees or copies memory between host and device.
+ *    The small result arrays (ids_out, logit_out, pass_out) may instead be
+ *    pinned host memory mapped for the device (hipHostMalloc; pass the
+ *    address hipHostGetDevicePointer returns): the kernels then store the
+ *    results straight into host memory and no copy follows the call. The
+ *    host may read them once the stream has been synchronized.
  *  - Tensors are dense and row-major; there are no stride arguments.
  *  - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.

@@ -427,6 +427,32 @@ def test_draft_round_without_probe_and_watchdog(dev):
     assert torch.equal(out["ids"], good)
 
 
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head"])
+def test_draft_round_pinned_host_outputs(dev, name):
+    """ids, probe logits and gates stored by the kernels straight into pinned
+    host memory (slices of one buffer) equal the device-memory results."""
+    inp, t = _round_tensors(name, dev)
+    say(f"[draft_round pinned outputs] {name}")
+    R, B, k = inp["num_reqs"], inp["B"], inp["k"]
+    rows = R * B
+    host = torch.zeros(R * k * 8 + rows * 8, dtype=torch.uint8, pin_memory=True)
+    ids = host[: R * k * 8].view(torch.int64).view(R, k)
+    lg = host[R * k * 8: R * k * 8 + rows * 4].view(torch.float32)
+    ps = host[R * k * 8 + rows * 4:].view(torch.int32)
+    kw = dict(probe_w=t["pw"], probe_bias=float(inp["probe_bias"]), probe_threshold=float(inp["probe_threshold"]))
+    ref = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, **kw)
+    _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, ids_out=ids, logit_out=lg, pass_out=ps,
+                       **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ref["ids"].cpu())
+    assert torch.equal(lg, ref["logit"].cpu()) and torch.equal(ps, ref["passed"].cpu())
+    lg2 = torch.zeros(rows, dtype=torch.float32, pin_memory=True)
+    _ops().conf_probe(t["H"], t["pw"], float(inp["probe_bias"]), float(inp["probe_threshold"]), logit_out=lg2,
+                      want_pass=False)
+    torch.cuda.synchronize()
+    assert torch.equal(lg2, ref["logit"].cpu())
+
+
 def test_draft_round_graph_replay(dev):
     """dspark_draft_round recorded in a HIP graph and replayed with eager work
     between replays: every replay equals the eager result."""
