@@ -114,6 +114,39 @@ def normal_bf16(seed: int, stream: int, shape, std: float = W_STD) -> np.ndarray
     return out.reshape(shape)
 
 
+def q8_0_quantize(x: np.ndarray):
+    """Round float32 rows to Q8_0 blocks (32 entries along the last axis):
+    per block d = max|x| / 127, stored as IEEE binary16 (nearest), and
+    q = x / d rounded half away from zero, in [-127, 127]; an all-zero block
+    gets d = 0 and q = 0. This is how such weights are usually produced;
+    here it only prepares inputs. Returns (q int8 [..., K], d bits uint16
+    [..., K / 32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    K = x.shape[-1]
+    if K % 32:
+        raise ValueError("Q8_0 needs K % 32 == 0")
+    xb = x.reshape(x.shape[:-1] + (K // 32, 32))
+    d = np.abs(xb).max(axis=-1) / np.float32(127.0)
+    inv = np.where(d > 0, np.float32(1.0) / np.where(d > 0, d, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    v = xb * inv[..., None]
+    q = np.clip(np.sign(v) * np.floor(np.abs(v) + np.float32(0.5)), -127, 127).astype(np.int8)
+    return q.reshape(x.shape), d.astype(np.float16).view(np.uint16)
+
+
+def normal_q8(seed: int, stream: int, shape, std: float = W_STD):
+    """Q8_0 form (q int8, d bits uint16) of N(0, std^2) float32 draws."""
+    n = int(np.prod(shape))
+    x = np.empty(n, dtype=np.float32)
+
+    def fill(b, lo, hi):
+        v = _gen(seed, stream, b).standard_normal(hi - lo, dtype=np.float32)
+        v *= np.float32(std)
+        x[lo:hi] = v
+
+    _fill_blocks(n, fill)
+    return q8_0_quantize(x.reshape(shape))
+
+
 def uniform_index(seed: int, stream: int, n: int, high: int) -> np.ndarray:
     """int64 draws uniform in [0, high)."""
     return _gen(seed, stream).integers(0, high, size=n, dtype=np.int64)
@@ -178,6 +211,23 @@ def markov_inputs(num_reqs: int, B: int, V: int, r: int, seed: int,
                 w2[b, :] = w2[a, :]
             ties.append((req, i, a, b))
     return base, w1, w2, prev0, ties
+
+
+def gemv_q8_inputs(M: int, N: int, K: int, seed: int, w_std: float = W_STD):
+    """W as Q8_0 (q int8 [N, K], d bits [N, K/32]) of N(0, w_std^2) draws; X float32 [M, K] ~ N(0, 1)."""
+    Wq, Wd = normal_q8(seed, S_W_LM, (N, K), w_std)
+    X = normal_f32(seed, S_H, (M, K))
+    return Wq, Wd, X
+
+
+def markov_q8_inputs(num_reqs: int, B: int, V: int, r: int, seed: int, base_std: float = 1.28):
+    """The Markov loop's inputs with markov_w1 and markov_w2 as Q8_0 of
+    N(0, 0.02^2) draws (r % 32 == 0). Returns (base, w1q, w1d, w2q, w2d, prev0)."""
+    base = normal_f32(seed, S_BASE, (num_reqs, B, V), base_std)
+    w1q, w1d = normal_q8(seed, S_W1, (V, r))
+    w2q, w2d = normal_q8(seed, S_W2, (V, r))
+    prev0 = uniform_index(seed, S_PREV0, num_reqs, V)
+    return base, w1q, w1d, w2q, w2d, prev0
 
 
 def d2t_map(V: int, seed: int, offset: int = 1000) -> np.ndarray:

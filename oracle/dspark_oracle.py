@@ -42,6 +42,35 @@ def bf16_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def fp16_to_f64(bits) -> np.ndarray:
+    """Exact value of IEEE 754 binary16 bit patterns (numpy's half-precision
+    decode, widened exactly)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+QK8_0 = 32  # entries per Q8_0 block
+
+
+def q8_0_to_f64(q, d_bits) -> np.ndarray:
+    """Exact values of Q8_0 weights.
+
+    [DS772] "Summary": the GPU confidence path takes Q8_0 markov weights
+    (any other format falls back to the CPU). The pages do not spell the
+    format out; the reading taken is the Q8_0 block format of the GGUF files
+    that project loads: each run of 32 consecutive entries of a row shares
+    one IEEE binary16 scale d, and entry j of the block is d * q[j] with q a
+    signed 8-bit integer. Here the quants and the scales are passed as two
+    arrays: q int8 [..., K] and d_bits uint16 [..., K / 32] (binary16 bit
+    patterns); block b of a row covers entries 32b .. 32b + 31.
+    """
+    q = np.asarray(q, dtype=np.int8)
+    d = fp16_to_f64(d_bits)
+    if q.shape[-1] % QK8_0 != 0 or d.shape != q.shape[:-1] + (q.shape[-1] // QK8_0,):
+        raise ValueError("Q8_0: q [..., K] with K % 32 == 0 and d [..., K / 32] required")
+    _finite(d)
+    return q.astype(np.float64) * np.repeat(d, QK8_0, axis=-1)
+
+
 def _finite(*arrays):
     for a in arrays:
         if not np.all(np.isfinite(a)):
@@ -79,6 +108,28 @@ proj_smallm = gemv
 lm_head = gemv
 
 
+def gemv_q8(Wq, Wd_bits, X) -> np.ndarray:
+    """Y[m, n] = sum_t X[m, t] * W[n, t] with W given as Q8_0 blocks.
+
+    The same definition as gemv ([SI441] "Observation"), over weights stored
+    in the quantized form whose weight-stationary matvec [SI441] "Proposed
+    work" cites as the existing quantized kernels: W = q8_0_to_f64(Wq, Wd),
+    Wq int8 [N, K], Wd binary16 [N, K / 32]; X float32 [M, K]; in float64.
+    """
+    W = q8_0_to_f64(Wq, Wd_bits)
+    X64 = np.asarray(X, dtype=np.float32).astype(np.float64)
+    _finite(X64)
+    if W.ndim != 2 or X64.ndim != 2 or W.shape[1] != X64.shape[1]:
+        raise ValueError("gemv_q8: W [N, K] and X [M, K] required")
+    return X64 @ W.T
+
+
+def gemv_q8_rows(Wq, Wd_bits, X, rows) -> np.ndarray:
+    """gemv_q8 evaluated only for the output columns ``rows``."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return gemv_q8(np.asarray(Wq)[rows], np.asarray(Wd_bits)[rows], X)
+
+
 # ---------------------------------------------------------------------------
 # Markov-biased greedy sampling loop
 # ---------------------------------------------------------------------------
@@ -91,20 +142,25 @@ class StepResult:
     s: np.ndarray     # fp64 scores of the step
 
 
+def _decoded(w) -> np.ndarray:
+    return w if (isinstance(w, np.ndarray) and w.dtype == np.float64) else bf16_to_f64(w)
+
+
 def markov_scores(base_row, w1_bits, w2, prev: int) -> np.ndarray:
     """Scores of one step: s[v] = base_row[v] + sum_j W2[v, j] * W1[prev, j].
 
     [W7] "The fix": gather the markov_w1 row of the previous token, multiply
     markov_w2 [V, r] by it, add the step's base-logit row. No scale,
     temperature or nonlinearity appears on the page, so none is applied.
-    ``w2`` may be bf16 bits or an already decoded float64 array.
+    ``w1_bits`` and ``w2`` may be bf16 bits or already decoded float64
+    arrays (the values of weights in any storage format).
     """
     w1 = np.asarray(w1_bits)
     V = w1.shape[0]
     if not (0 <= prev < V):
         raise ValueError(f"prev {prev} outside [0, {V})")
-    e = bf16_to_f64(w1[prev])
-    W2 = w2 if (isinstance(w2, np.ndarray) and w2.dtype == np.float64) else bf16_to_f64(w2)
+    e = _decoded(w1[prev])
+    W2 = _decoded(w2)
     b = np.asarray(base_row, dtype=np.float32).astype(np.float64)
     _finite(b)
     return b + W2 @ e
@@ -148,12 +204,28 @@ def markov_sample(base, w1_bits, w2_bits, prev0, k: int, d2t=None) -> dict:
     Returns dict(ids [R, k] int64, tok [R, k], margin [R, k] float64,
     runner_up [R, k]).
     """
+    return _markov_loop(base, bf16_to_f64(w1_bits), bf16_to_f64(w2_bits), prev0, k, d2t)
+
+
+def markov_sample_q8(base, w1q, w1d_bits, w2q, w2d_bits, prev0, k: int, d2t=None) -> dict:
+    """The same loop with markov_w1 and markov_w2 given as Q8_0 blocks.
+
+    [DS772] "Summary": the GPU path takes Q8_0 markov weights. Reading: both
+    markov tensors are Q8_0 (blocks along the rank dimension, r % 32 == 0);
+    the loop is unchanged and runs on their exact values (q8_0_to_f64).
+    w1q, w2q int8 [V, r]; w1d_bits, w2d_bits binary16 [V, r / 32].
+    """
+    return _markov_loop(base, q8_0_to_f64(w1q, w1d_bits), q8_0_to_f64(w2q, w2d_bits), prev0, k, d2t)
+
+
+def _markov_loop(base, W1, W2, prev0, k: int, d2t=None) -> dict:
     base = np.asarray(base, dtype=np.float32)
     R, B, V = base.shape
     if not (1 <= k <= B):
         raise ValueError("need 1 <= k <= B")
-    W2 = bf16_to_f64(w2_bits)
-    _finite(W2)
+    if W1.shape != W2.shape or W1.shape[0] != V:
+        raise ValueError("markov_w1 and markov_w2 must both be [V, r]")
+    _finite(W1, W2)
     ids = np.empty((R, k), np.int64)
     tok = np.empty((R, k), np.int64)
     margin = np.empty((R, k), np.float64)
@@ -161,7 +233,7 @@ def markov_sample(base, w1_bits, w2_bits, prev0, k: int, d2t=None) -> dict:
     for req in range(R):
         prev = int(prev0[req])
         for i in range(k):
-            st = markov_step(base[req, i], w1_bits, W2, prev)
+            st = markov_step(base[req, i], W1, W2, prev)
             tok[req, i] = st.tok
             margin[req, i] = st.margin
             runner[req, i] = st.runner_up

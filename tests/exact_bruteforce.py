@@ -21,6 +21,40 @@ def frac_f32(x) -> Fraction:
     return Fraction(v)
 
 
+def frac_f16(bits: int) -> Fraction:
+    """Exact value of an IEEE binary16 bit pattern (struct's 'e' format)."""
+    (v,) = struct.unpack("<e", struct.pack("<H", int(bits) & 0xFFFF))
+    return Fraction(v)
+
+
+def frac_q8(q_row, d_row):
+    """Exact values of one Q8_0 row: entry j is d[j // 32] * q[j]."""
+    return [Fraction(int(q_row[j])) * frac_f16(d_row[j // 32]) for j in range(len(q_row))]
+
+
+def exact_gemv_q8(Wq, Wd, X):
+    Wf = [frac_q8(Wq[n], Wd[n]) for n in range(len(Wq))]
+    K = len(Wf[0])
+    return [[sum((frac_f32(xr[t]) * Wf[n][t] for t in range(K)), Fraction(0)) for n in range(len(Wf))] for xr in X]
+
+
+def exact_markov_values(base, W1f, W2f, prev0, k):
+    """exact_markov over already exact weight values (lists of Fractions)."""
+    out = []
+    for req in range(len(base)):
+        prev = int(prev0[req])
+        steps = []
+        for i in range(k):
+            e = W1f[prev]
+            s = [frac_f32(base[req][i][v]) + sum((W2f[v][j] * e[j] for j in range(len(e))), Fraction(0))
+                 for v in range(len(base[req][i]))]
+            tok, margin, _ = exact_argmax(s)
+            steps.append((tok, margin, s))
+            prev = tok
+        out.append(steps)
+    return out
+
+
 def exact_gemv(W_bits, X):
     N, K = len(W_bits), len(W_bits[0])
     Wf = [[frac_bf16(W_bits[n][t]) for t in range(K)] for n in range(N)]

@@ -13,7 +13,8 @@ import os
 
 import numpy as np
 
-from exact_bruteforce import exact_argmax, exact_gemv, exact_markov, exact_probe
+from exact_bruteforce import (exact_argmax, exact_gemv, exact_gemv_q8, exact_markov, exact_markov_values,
+                              exact_probe, frac_q8)
 from gemv_markov_argmax_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -289,4 +290,187 @@ def probe_pins(conf_probe):
     return pins
 
 
-__all__ = ["markov_pins", "gemv_pins", "probe_pins", "exact_argmax"]
+# ---------------------------------------------------------------------------
+# Q8_0 weights: the GEMV and the Markov loop
+# ---------------------------------------------------------------------------
+
+def _q8_rows(nonzero, K):
+    q = np.zeros((len(nonzero), K), np.int8)
+    for n, pairs in enumerate(nonzero):
+        for j, v in pairs:
+            q[n, j] = v
+    return q
+
+
+def _hex16(vals):
+    return np.array([int(v, 16) for v in vals], np.uint16)
+
+
+def _rand_q8(g, rows, K, d_kind="mixed"):
+    q = g.integers(-128, 128, size=(rows, K)).astype(np.int8)
+    nb = K // 32
+    if d_kind == "one":
+        d = np.full((rows, nb), 0x3C00, np.uint16)
+    else:  # finite binary16 patterns of either sign, normals and subnormals
+        e = g.integers(0, 31, size=(rows, nb))
+        f = g.integers(0, 1024, size=(rows, nb))
+        sgn = g.integers(0, 2, size=(rows, nb))
+        d = ((sgn << 15) | (e << 10) | f).astype(np.uint16)
+    return q, d
+
+
+def gemv_q8_pins(gemv_q8, gemv_bf16=None):
+    pins = []
+    fx = _load("q8_hand.json")
+    gx = fx["gemv"]
+
+    def hand():
+        K = gx["K"]
+        Wq = _q8_rows(gx["W_q_nonzero"], K)
+        Wd = np.stack([_hex16(r) for r in gx["W_d_bits"]])
+        X = np.zeros((2, K), np.float32)
+        for j, v in gx["X_nonzero"][0]:
+            X[0, j] = v
+        X[1, :] = 1.0
+        y = gemv_q8(Wq, Wd, X)
+        return np.array_equal(y, gx["expected_Y"]), f"{np.asarray(y).tolist()}"
+    pins.append(_run("hand two-block example (scales per 32-entry block, signed quants)", hand))
+
+    def fp16_scales():
+        bad = []
+        for bits, val, why in fx["fp16"]["cases"]:
+            q = np.zeros((1, 32), np.int8)
+            q[0, 0] = 1
+            y = gemv_q8(q, _hex16([bits]).reshape(1, 1), np.ones((1, 32), np.float32))
+            got = float(np.asarray(y)[0, 0])
+            if got != val:  # (a zero scale gives a zero sum, whose sign the pin leaves open)
+                bad.append((bits, got, val))
+        return not bad, f"{bad}"
+    pins.append(_run("binary16 scales decode to their IEEE 754 values", fp16_scales))
+
+    def block_boundary():
+        K = 96
+        X = np.arange(1, K + 1, dtype=np.float32).reshape(1, K)
+        Wd = _hex16(["0x3c00", "0x4000", "0x4400"]).reshape(1, 3)  # 1, 2, 4
+        want = {0: 1.0, 31: 32.0, 32: 2 * 33.0, 63: 2 * 64.0, 64: 4 * 65.0, 95: 4 * 96.0}
+        bad = []
+        for j, v in want.items():
+            q = np.zeros((1, K), np.int8)
+            q[0, j] = 1
+            got = float(np.asarray(gemv_q8(q, Wd, X))[0, 0])
+            if got != v:
+                bad.append((j, got, v))
+        return not bad, f"{bad}"
+    pins.append(_run("entries 32b..32b+31 take scale b", block_boundary))
+
+    def brute():
+        bad = 0
+        for seed in range(40):
+            g = np.random.default_rng(500 + seed)
+            M, N, K = int(g.integers(1, 4)), int(g.integers(1, 5)), 32 * int(g.integers(1, 3))
+            X = g.standard_normal((M, K)).astype(np.float32)
+            q, d = _rand_q8(g, N, K)
+            y = np.asarray(gemv_q8(q, d, X))
+            ex = exact_gemv_q8(q.tolist(), d.tolist(), X.tolist())
+            Wf = np.array([[float(v) for v in frac_q8(q[n], d[n])] for n in range(N)])
+            mag = np.abs(X.astype(np.float64)) @ np.abs(Wf).T
+            err = np.abs(y - np.array([[float(v) for v in row] for row in ex]))
+            bad += int(np.any(err > 1e-14 * np.maximum(mag, 1e-300) + 1e-300))
+        return bad == 0, f"{bad} problems off the exact value"
+    pins.append(_run("exact rational brute force, tiny random Q8_0 problems", brute))
+
+    if gemv_bf16 is not None:
+        def unit_scales():
+            g = np.random.default_rng(9)
+            q, d = _rand_q8(g, 6, 64, "one")
+            X = g.standard_normal((3, 64)).astype(np.float32)
+            wb = _bits(q.astype(np.float32))  # small integers are exact in bf16
+            return np.allclose(gemv_q8(q, d, X), gemv_bf16(wb, X), rtol=1e-14, atol=0), "d = 1 vs bf16 weights q"
+        pins.append(_run("unit scales reduce to the bf16 GEMV on weights q", unit_scales))
+    return pins
+
+
+def markov_q8_pins(markov_sample_q8, markov_sample_bf16=None, n_brute=60):
+    pins = []
+    fx = _load("markov_hand_3tok.json")
+    d_half = int(_load("q8_hand.json")["markov"]["d_bits"], 16)
+
+    def q8_of(w):
+        w = np.asarray(w, np.float64)
+        q = np.zeros((w.shape[0], 32), np.int8)
+        q[:, : w.shape[1]] = (2 * w).astype(np.int8)
+        return q, np.full((w.shape[0], 1), d_half, np.uint16)
+
+    def hand():
+        base = np.asarray(fx["base"], np.float32)
+        (q1, d1), (q2, d2) = q8_of(fx["w1"]), q8_of(fx["w2"])
+        out = markov_sample_q8(base, q1, d1, q2, d2, fx["prev0"], fx["k"])
+        ok = np.array_equal(out["ids"], fx["expected_ids"]) and np.array_equal(out["margin"], fx["expected_margin"])
+        out2 = markov_sample_q8(base, q1, d1, q2, d2, fx["prev0"], fx["k"], d2t=np.asarray(fx["d2t"]))
+        ok = ok and np.array_equal(out2["ids"], fx["expected_ids_d2t"])
+        return ok, f"ids {out['ids'].tolist()} margin {out['margin'].tolist()}"
+    pins.append(_run("hand 3-token example in Q8_0 form", hand))
+
+    def brute():
+        bad = []
+        for seed in range(n_brute):
+            g = np.random.default_rng(900 + seed)
+            V, k, r = int(g.integers(2, 40)), int(g.integers(1, 4)), 32 * int(g.integers(1, 3))
+            base = g.standard_normal((1, k, V)).astype(np.float32)
+            q1, d1 = _rand_q8(g, V, r)
+            q2, d2 = _rand_q8(g, V, r)
+            # keep the scores in a modest range: scales 2^-12 .. 2^-6
+            d1 = ((g.integers(3, 9, size=d1.shape) << 10) | (d1 & 0x83FF)).astype(np.uint16)
+            d2 = ((g.integers(3, 9, size=d2.shape) << 10) | (d2 & 0x83FF)).astype(np.uint16)
+            p0 = g.integers(0, V, size=1)
+            out = markov_sample_q8(base, q1, d1, q2, d2, p0, k)
+            W1f = [frac_q8(q1[v], d1[v]) for v in range(V)]
+            W2f = [frac_q8(q2[v], d2[v]) for v in range(V)]
+            ex = exact_markov_values(base.tolist(), W1f, W2f, p0, k)[0]
+            for i, (tok, margin, sc) in enumerate(ex):
+                scale = max(1.0, float(max(abs(x) for x in sc)))
+                if float(margin) > 1e-6 * scale and int(out["tok"][0, i]) != tok:
+                    bad.append((seed, i, int(out["tok"][0, i]), tok))
+                    break
+                if abs(float(out["margin"][0, i]) - float(margin)) > 1e-12 * scale:
+                    bad.append((seed, i, "margin"))
+                    break
+                if int(out["tok"][0, i]) != tok:
+                    break
+        return not bad, f"{len(bad)} mismatching problems, first {bad[:1]}"
+    pins.append(_run("exact rational brute force, tiny random Q8_0 problems", brute))
+
+    def block_scales():
+        # r = 64, W1[prev] = 1 everywhere with scales (1, 1); W2 row v holds a
+        # single quant 1 at column c_v, scales (1, 8): the bias of row v is 1
+        # when c_v < 32 and 8 otherwise, so the draft is the row with c_v in
+        # the second block.
+        V, r = 6, 64
+        cols = [0, 31, 33, 30, 5, 12]
+        q2 = np.zeros((V, r), np.int8)
+        for v, c in enumerate(cols):
+            q2[v, c] = 1
+        d2 = np.tile(_hex16(["0x3c00", "0x4800"]), (V, 1))
+        q1 = np.ones((V, r), np.int8)
+        d1 = np.tile(_hex16(["0x3c00", "0x3c00"]), (V, 1))
+        base = np.zeros((1, 1, V), np.float32)
+        out = markov_sample_q8(base, q1, d1, q2, d2, [0], 1)
+        return int(out["tok"][0, 0]) == 2 and float(out["margin"][0, 0]) == 7.0, f"{out['tok'].tolist()} {out['margin'].tolist()}"
+    pins.append(_run("the second 32-entry block takes the second scale", block_scales))
+
+    if markov_sample_bf16 is not None:
+        def unit_scales():
+            b, _, _, p0, _ = synth.markov_inputs(2, 4, 120, 32, seed=31)
+            g = np.random.default_rng(41)
+            q1, d1 = _rand_q8(g, 120, 32, "one")
+            q2, d2 = _rand_q8(g, 120, 32, "one")
+            q1 = (q1 // 16).astype(np.int8)  # small bias terms: scores stay comparable to the base
+            q2 = (q2 // 16).astype(np.int8)
+            a = markov_sample_q8(b, q1, d1, q2, d2, p0, 4)
+            c = markov_sample_bf16(b, _bits(q1.astype(np.float32)), _bits(q2.astype(np.float32)), p0, 4)
+            return np.array_equal(a["ids"], c["ids"]) and np.array_equal(a["margin"], c["margin"]), "d = 1 vs bf16"
+        pins.append(_run("unit scales reduce to the bf16 loop on weights q", unit_scales))
+    return pins
+
+
+__all__ = ["markov_pins", "gemv_pins", "probe_pins", "gemv_q8_pins", "markov_q8_pins", "exact_argmax"]

@@ -6,8 +6,8 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.dspark_oracle import bf16_to_f64
-from oracle_pins import gemv_pins, markov_pins, probe_pins
+from oracle.dspark_oracle import _markov_loop, bf16_to_f64, fp16_to_f64
+from oracle_pins import gemv_pins, gemv_q8_pins, markov_pins, markov_q8_pins, probe_pins
 
 
 def _markov_mutant(kind):
@@ -93,4 +93,46 @@ def _probe_mutant(kind):
 @pytest.mark.parametrize("kind", ["no_bias", "bias_sign", "ignore_w", "strict_gate"])
 def test_probe_mutant_is_caught(kind):
     results = probe_pins(_probe_mutant(kind))
+    assert any(not ok for _, ok, _ in results), f"mutant {kind} passed every pin"
+
+
+def _q8_dequant_mutant(kind):
+    def deq(q, d_bits):
+        q = np.asarray(q, np.int8)
+        d_bits = np.asarray(d_bits, np.uint16)
+        d = fp16_to_f64(d_bits)
+        qv = q.astype(np.uint8).astype(np.float64) if kind == "unsigned_q" else q.astype(np.float64)
+        if kind == "scale_as_bf16":
+            d = bf16_to_f64(d_bits)
+        if kind == "no_scale":
+            d = np.ones_like(d)
+        if kind == "scale_shift":
+            d = np.roll(d, 1, axis=-1)
+        K = q.shape[-1]
+        idx = np.arange(K) // (16 if kind == "block16" else 32)
+        idx = idx % d.shape[-1]
+        return qv * d[..., idx]
+    return deq
+
+
+Q8_MUTANTS = ["unsigned_q", "scale_as_bf16", "no_scale", "scale_shift", "block16"]
+
+
+@pytest.mark.parametrize("kind", Q8_MUTANTS)
+def test_gemv_q8_mutant_is_caught(kind):
+    deq = _q8_dequant_mutant(kind)
+
+    def gemv_q8(Wq, Wd, X):
+        return np.asarray(X, np.float32).astype(np.float64) @ deq(Wq, Wd).T
+    results = gemv_q8_pins(gemv_q8)
+    assert any(not ok for _, ok, _ in results), f"mutant {kind} passed every pin"
+
+
+@pytest.mark.parametrize("kind", Q8_MUTANTS)
+def test_markov_q8_mutant_is_caught(kind):
+    deq = _q8_dequant_mutant(kind)
+
+    def sample(base, w1q, w1d, w2q, w2d, prev0, k, d2t=None):
+        return _markov_loop(base, deq(w1q, w1d), deq(w2q, w2d), prev0, k, d2t)
+    results = markov_q8_pins(sample, n_brute=30)
     assert any(not ok for _, ok, _ in results), f"mutant {kind} passed every pin"

@@ -3,7 +3,7 @@ special cases with textbook answers and invariants (no GPU)."""
 import pytest
 
 import oracle
-from oracle_pins import gemv_pins, markov_pins, probe_pins
+from oracle_pins import gemv_pins, gemv_q8_pins, markov_pins, markov_q8_pins, probe_pins
 
 
 def _ids(pins):
@@ -18,6 +18,12 @@ def _ids(pins):
 def test_oracle_meets_every_pin(suite, fn):
     results = suite(fn)
     failed = [(n, d) for n, ok, d in results if not ok]
+    assert not failed, failed
+
+
+def test_q8_oracle_meets_every_pin():
+    failed = [(n, d) for n, ok, d in gemv_q8_pins(oracle.gemv_q8, oracle.gemv) if not ok]
+    failed += [(n, d) for n, ok, d in markov_q8_pins(oracle.markov_sample_q8, oracle.markov_sample) if not ok]
     assert not failed, failed
 
 
