@@ -40,6 +40,14 @@ dspark_status gemv_checks(const uint16_t* W, int N, int K, const float* X, int M
   return DSPARK_OK;
 }
 
+dspark_status gemv_q8_checks(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M,
+                            const float* Y) {
+  if (!Wq || !Wd || !X || !Y) return DSPARK_ERR_NULL;
+  if (N < 1 || K < 32 || (K % 32) != 0 || M < 1 || !dspark::gemv_q8_shape_fits(N, K, M)) return DSPARK_ERR_SHAPE;
+  if (!aligned(Wq, 16) || !aligned(Wd, 2) || !aligned(X, 16) || !aligned(Y, 4)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
 dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
 }  // namespace
@@ -70,6 +78,20 @@ dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H,
   const dspark_status st = gemv_checks(W_lm, V, d, H, rows, logits);
   if (st != DSPARK_OK) return st;
   return from_hip(dspark::launch_gemv(W_lm, V, d, H, rows, logits, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_proj_smallm_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M,
+                                    float* Y, void* stream) {
+  const dspark_status st = gemv_q8_checks(Wq, Wd, N, K, X, M, Y);
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv_q8(Wq, Wd, N, K, X, M, Y, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_lm_head_q8(const int8_t* Wq, const uint16_t* Wd, int V, int d, const float* H, int rows,
+                                float* logits, void* stream) {
+  const dspark_status st = gemv_q8_checks(Wq, Wd, V, d, H, rows, logits);
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv_q8(Wq, Wd, V, d, H, rows, logits, static_cast<hipStream_t>(stream)));
 }
 
 size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V) {

@@ -184,6 +184,11 @@ __device__ __forceinline__ uint64_t row_max64(uint64_t v) {
 // stay below 2^31 bytes.
 bool gemv_shape_fits(int N, int K, int M);
 
+// Small-M GEMV over Q8_0 weights; see dspark_proj_smallm_q8.
+bool gemv_q8_shape_fits(int N, int K, int M);
+hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M, float* Y,
+                          hipStream_t stream);
+
 // Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
                        hipStream_t stream);

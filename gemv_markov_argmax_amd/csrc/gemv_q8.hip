@@ -1,0 +1,330 @@
+// Weight-stationary small-M GEMV over Q8_0 weights on gfx950 matrix cores.
+//
+// Y[m, n] = sum_t X[m, t] * W[n, t], with W in Q8_0 blocks: entries
+// 32b .. 32b + 31 of row n are d[n, b] * q[n, t], q int8 [N, K], d IEEE
+// binary16 [N, K / 32]; X fp32 [M, K], Y fp32 [M, N].
+//
+// SharpInference #441, "Proposed work": the weight-stationary matvec it
+// would reuse targets quantized weights; ds4 #772, "Summary": the GPU path
+// takes Q8_0 weights. A Q8_0 weight costs 1.0625 bytes instead of 2.
+//
+// Design on gfx950 (the bf16 streaming kernel's structure, one byte per
+// weight):
+//  * 16 waves per workgroup, one workgroup per CU over a balanced contiguous
+//    row range; every 16-row tile is split along K over the waves (4 blocks
+//    of 32 entries per wave and phase), two tiles of loads in flight.
+//  * Each wave loads its 16 x 128-byte segment of a tile in whole 128-byte
+//    lines (non-temporal raw buffer loads; zeros past the range), together
+//    with the tile's 16 x 4 scales, and stages both in a private LDS area.
+//  * B fragments: 8 quants per lane, converted exactly to bf16 (a signed
+//    byte has at most 8 significant bits: one sign-extending convert per
+//    value and a byte permute per pair). A fragments: X split exactly into
+//    bf16 hi and lo (residual <= 2^-17 |x|), as in the bf16 kernel.
+//  * Each 32-entry block is one v_mfma_f32_16x16x32_bf16 on a fresh
+//    accumulator, scaled by its block's scale and added in fp32. The 16
+//    per-wave partial tiles are summed in LDS in wave order; phases add
+//    there; outputs go out once per chunk of tiles. The summation order
+//    depends on the shape only.
+#include "dspark_internal.h"
+
+#include <algorithm>
+
+namespace dspark {
+namespace {
+
+struct Q8Params {
+  const int8_t* Wq;
+  const uint16_t* Wd;
+  const float* X;
+  float* Y;
+  int N, K, M;  // M rows in this launch (<= 16)
+  int ldy;
+  int chunk;    // tiles whose outputs are staged in LDS at once (even)
+  int pq, prem; // row pairs per workgroup: N/2 = pq * gridDim.x + prem
+};
+
+constexpr int kQNW = 16;                 // waves per workgroup
+constexpr int kQKBW = 4;                 // 32-entry blocks per wave and phase
+constexpr int kQSeg = 32 * kQKBW;        // quant bytes of a row segment (one 128-byte line)
+constexpr int kQRS = kQSeg + 16;         // padded LDS row stride
+constexpr int kQLPR = kQSeg / 16;        // lanes per row in a load instruction
+constexpr int kQRPI = kWave / kQLPR;     // rows per load instruction
+constexpr int kQNLD = 16 / kQRPI;        // load instructions per tile
+constexpr size_t kQLds = 160 * 1024;
+
+__device__ __forceinline__ int2 q8_rows(const Q8Params& p) {
+  const int b = blockIdx.x;
+  const int r0 = 2 * (b * p.pq + min(b, p.prem));
+  const int r1 = b + 1 == static_cast<int>(gridDim.x) ? p.N : 2 * ((b + 1) * p.pq + min(b + 1, p.prem));
+  return int2{r0, r1};
+}
+
+inline int q8_rows_max(int N, int grid) {
+  const int q = (N / 2) / grid, rem = (N / 2) % grid;
+  return std::max(2 * (q + (rem > 0 ? 1 : 0)), 2 * q + (N & 1));
+}
+
+// Eight signed bytes (two dwords, entry order) as eight bf16 values, exactly.
+__device__ __forceinline__ u32x4 q8x8_to_bf16(uint2 v) {
+  auto cv = [](uint32_t w, int byte) { return __builtin_bit_cast(uint32_t, static_cast<float>(static_cast<int8_t>(w >> (8 * byte)))); };
+  auto pk = [](uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x07060302u); };
+  return u32x4{pk(cv(v.x, 0), cv(v.x, 1)), pk(cv(v.x, 2), cv(v.x, 3)), pk(cv(v.y, 0), cv(v.y, 1)),
+               pk(cv(v.y, 2), cv(v.y, 3))};
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// MULTI: more than one K phase (the chunk loop runs every phase per chunk).
+template <bool PACK, bool MULTI>
+__global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
+  constexpr int NW = kQNW, KBW = kQKBW, RS = kQRS, LPR = kQLPR, RPI = kQRPI, NLD = kQNLD;
+  constexpr int F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* tr = smem;                                                           // [NW][16][RS] quants
+  uint16_t* sc = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [NW][16][KBW] scales
+  float* red = reinterpret_cast<float*>(sc + NW * 16 * KBW);                         // [2][NW][ROWS][16]
+  float* ylds = red + 2 * NW * ROWS * 16;                                            // [chunk][M][16]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int K = p.K, M = p.M;
+  const int KB = K / 32;
+  const int phases = (KB + NW * KBW - 1) / (NW * KBW);
+
+  const int2 rows = q8_rows(p);
+  const int r0 = rows.x, r1 = rows.y;
+  const int rounds = (r1 - r0 + 15) / 16;
+  const int nchunks = (rounds + p.chunk - 1) / p.chunk;
+  const int csize = (((rounds + nchunks - 1) / nchunks) + 1) & ~1;
+  const int lrow = lane / LPR, lchunk = lane % LPR;
+  unsigned char* wtr = tr + w * 16 * RS;
+  unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
+  const unsigned char* rd_base = wtr + i * RS + 8 * g;    // + 32*kb
+  uint16_t* wsc = sc + w * 16 * KBW;
+
+  const uint32_t rowb = static_cast<uint32_t>(K);       // quant bytes per row
+  const uint32_t drow = static_cast<uint32_t>(KB) * 2;  // scale bytes per row
+  const BufRes qres = buf_res(p.Wq + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
+  const BufRes dres = buf_res(p.Wd + static_cast<size_t>(r0) * KB, static_cast<uint32_t>(r1 - r0) * drow);
+  const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+
+  u32x4 afr[KBW][F];
+  u32x4 b0[NLD], b1[NLD];
+  uint32_t s0 = 0, s1 = 0;  // the scale half of this lane (row i, block g of the segment)
+  int ph = 0, c0 = 0, c1 = 0, lim = 0;
+  uint32_t lane_off = 0, sc_off = 0;
+
+  // Phase ph: this wave's segment starts at entry kseg (block kseg / 32).
+  // Lanes past K start out of range and read zeros.
+  auto set_phase = [&](int phase) {
+    ph = phase;
+    const int kseg = 32 * KBW * (ph * NW + w);
+    lane_off = kseg + 16 * lchunk < K ? static_cast<uint32_t>(lrow) * rowb + static_cast<uint32_t>(kseg + 16 * lchunk)
+                                      : kBufOutOfRange;
+    const int blk = kseg / 32 + g;
+    sc_off = blk < KB ? static_cast<uint32_t>(i) * drow + static_cast<uint32_t>(blk) * 2 : kBufOutOfRange;
+  };
+  // A fragments of phase ph: block kb covers k = kseg + 32*kb + 8*g + (0..7).
+  auto build_a = [&]() {
+    const int kseg = 32 * KBW * (ph * NW + w);
+    constexpr int XH = PACK ? 1 : 2;
+    constexpr int KH = KBW * XH * 4 > 32 ? KBW / 2 : KBW;
+    const int m = PACK ? (i & 7) : i;
+#pragma unroll
+    for (int k0 = 0; k0 < KBW; k0 += KH) {
+      float4 xr[KH][XH];
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk) {
+        const int k = kseg + 32 * (k0 + kk) + 8 * g;
+        const uint32_t off = (m < M) & (k < K) ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
+        if (PACK) {
+          xr[kk][0] = buf_load_f32x4(xres, off + 16 * (i >> 3));
+        } else {
+          xr[kk][0] = buf_load_f32x4(xres, off);
+          xr[kk][XH - 1] = buf_load_f32x4(xres, off + 16);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk) {
+        float4 x0 = xr[kk][0], x1 = xr[kk][XH - 1];
+        if (PACK) pair_halves(xr[kk][0], i, x0, x1);
+        const uint2 sa = split_bf16x2(x0.x, x0.y), sb = split_bf16x2(x0.z, x0.w);
+        const uint2 sc2 = split_bf16x2(x1.x, x1.y), sd = split_bf16x2(x1.z, x1.w);
+        const u32x4 h = {sa.x, sb.x, sc2.x, sd.x}, l = {sa.y, sb.y, sc2.y, sd.y};
+        if (PACK) {
+          afr[k0 + kk][0] = (i >> 3) ? l : h;
+        } else {
+          afr[k0 + kk][0] = h;
+          afr[k0 + kk][F - 1] = l;
+        }
+      }
+    }
+  };
+  // Tile rr: quants and scales; rows past r1 and tiles past lim read zeros.
+  auto load = [&](u32x4 (&b)[NLD], uint32_t& s, int rr) {
+    const bool live = rr < lim;
+    const uint32_t off = live ? lane_off + static_cast<uint32_t>(rr) * 16 * rowb : kBufOutOfRange;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(qres, off + static_cast<uint32_t>(q * RPI) * rowb);
+    s = __builtin_amdgcn_raw_buffer_load_b16(dres, static_cast<int>(live ? sc_off + static_cast<uint32_t>(rr) * 16 * drow
+                                                                          : kBufOutOfRange),
+                                             0, 0);
+  };
+  auto prologue = [&](bool with_a) {
+    load(b0, s0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (with_a) build_a();
+    load(b1, s1, c0 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_publish = [&](u32x4 (&b)[NLD], uint32_t s, int buf) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+    wsc[i * KBW + g] = static_cast<uint16_t>(s);
+    const uint2 sh = *reinterpret_cast<const uint2*>(wsc + i * KBW);  // the 4 scales of row i
+    const float scale[KBW] = {half_bits_to_float(sh.x & 0xffffu), half_bits_to_float(sh.x >> 16),
+                              half_bits_to_float(sh.y & 0xffffu), half_bits_to_float(sh.y >> 16)};
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const u32x4 bv = q8x8_to_bf16(*reinterpret_cast<const uint2*>(rd_base + 32 * kb));
+      f32x4 acc = mfma_16x16x32(afr[kb][0], bv, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (!PACK) acc = mfma_16x16x32(afr[kb][F - 1], bv, acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot[v] = __builtin_fmaf(acc[v], scale[kb], tot[v]);
+    }
+    float* dst = red + (buf * NW + w) * ROWS * 16;
+    if (PACK) {
+      // lanes 0..31 hold rows 0..7 (hi), lanes 32..63 rows 8..15 (lo) of the same columns
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float lo = __shfl_down(tot[v], 32);
+        if (g < 2) dst[(4 * g + v) * 16 + i] = tot[v] + lo;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[(4 * g + v) * 16 + i] = tot[v];
+    }
+  };
+  auto reduce = [&](int buf, int rr) {
+    if (tid < M * 16) {
+      float y = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) y += red[((buf * NW + ww) * ROWS + (tid >> 4)) * 16 + (tid & 15)];
+      float* yl = ylds + (rr - c0) * M * 16 + tid;
+      *yl = ph == 0 ? y : *yl + y;
+    }
+  };
+  // Tiles [c0, c1), two per iteration; the back edge carries b0 older than b1.
+  auto run_tiles = [&]() {
+    for (int rr = c0; rr < c1; rr += 2) {
+      compute_publish(b0, s0, 0);
+      load(b0, s0, rr + 2);
+      __syncthreads();
+      reduce(0, rr);
+      compute_publish(b1, s1, 1);
+      load(b1, s1, rr + 3);
+      __syncthreads();
+      if (rr + 1 < c1) reduce(1, rr + 1);
+    }
+  };
+  auto write_out = [&]() {
+    __syncthreads();
+    const int n0 = r0 + 16 * c0, cols = min(r1, r0 + 16 * c1) - n0;
+    for (int m = 0; m < M; ++m)
+      for (int j = tid; j < cols; j += NW * kWave)
+        p.Y[static_cast<size_t>(m) * p.ldy + n0 + j] = ylds[(j >> 4) * M * 16 + m * 16 + (j & 15)];
+    __syncthreads();
+  };
+
+  if (!MULTI) {
+    set_phase(0);
+    lim = rounds;
+    c0 = 0;
+    prologue(true);
+    for (; c0 < rounds; c0 += csize) {
+      c1 = min(rounds, c0 + csize);
+      run_tiles();
+      write_out();
+    }
+  } else {
+    for (c0 = 0; c0 < rounds; c0 += csize) {
+      c1 = min(rounds, c0 + csize);
+      lim = c1;
+      for (int q = 0; q < phases; ++q) {
+        set_phase(q);
+        prologue(true);
+        run_tiles();
+      }
+      write_out();
+    }
+  }
+}
+
+template <bool PACK>
+hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
+  const void* one = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, false>);
+  const void* many = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, true>);
+  static const hipError_t attr = [&] {
+    const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kQLds));
+    return e != hipSuccess ? e
+                           : hipFuncSetAttribute(many, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kQLds));
+  }();
+  if (attr != hipSuccess) return attr;
+  Q8Params a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(multi ? many : one, dim3(grid), dim3(kQNW * kWave), args, lds, st);
+}
+
+}  // namespace
+
+bool gemv_q8_shape_fits(int N, int K, int M) {
+  if (N < 1 || K < 32 || (K % 32) != 0 || M < 1 || K > (1 << 22)) return false;  // X of a launch: <= 16 * K * 4 bytes
+  const int cus = device_cu_count();
+  if (cus <= 0) return true;  // the launch reports the missing device
+  const int grid = std::max(1, std::min(cus, std::min((N + 15) / 16, std::max(1, N / 2))));
+  return static_cast<long long>(q8_rows_max(N, grid)) * K < (1LL << 31);
+}
+
+hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M, float* Y,
+                          hipStream_t stream) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorNoDevice;
+  const int tiles = (N + 15) / 16;
+  const int grid = std::max(1, std::min(cus, std::min(tiles, std::max(1, N / 2))));
+  const int rounds = (q8_rows_max(N, grid) + 15) / 16;
+  const int KB = K / 32;
+  const bool multi = (KB + kQNW * kQKBW - 1) / (kQNW * kQKBW) > 1;
+  // Launches of at most 16 rows of X each (the weights are read once per launch).
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    const int mm = std::min(16, M - m0);
+    const bool pack = mm <= 8;
+    const int rowsl = pack ? 8 : 16;
+    const size_t fixed = static_cast<size_t>(kQNW) * 16 * kQRS + static_cast<size_t>(kQNW) * 16 * kQKBW * 2 +
+                         static_cast<size_t>(2) * kQNW * rowsl * 16 * 4;
+    const size_t per_tile = static_cast<size_t>(mm) * 16 * 4;
+    int chunk = static_cast<int>((kQLds - fixed) / per_tile) & ~1;
+    chunk = std::max(2, std::min(chunk, (rounds + 1) & ~1));
+    Q8Params prm{};
+    prm.Wq = Wq;
+    prm.Wd = Wd;
+    prm.X = X + static_cast<size_t>(m0) * K;
+    prm.Y = Y + static_cast<size_t>(m0) * N;
+    prm.N = N;
+    prm.K = K;
+    prm.M = mm;
+    prm.ldy = N;
+    prm.chunk = chunk;
+    prm.pq = (N / 2) / grid;
+    prm.prem = (N / 2) % grid;
+    const size_t lds = fixed + chunk * per_tile;
+    const hipError_t e = pack ? launch_q8<true>(prm, grid, lds, multi, stream)
+                              : launch_q8<false>(prm, grid, lds, multi, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dspark

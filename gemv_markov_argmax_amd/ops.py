@@ -24,6 +24,8 @@ SIGNATURES = {
     "dspark_status_string": (ctypes.c_char_p, [_i]),
     "dspark_proj_smallm": (_i, [_p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head": (_i, [_p, _i, _i, _p, _i, _p, _p]),
+    "dspark_proj_smallm_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
+    "dspark_lm_head_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -135,6 +137,42 @@ def proj_smallm(W: torch.Tensor, X: torch.Tensor, out: torch.Tensor | None = Non
 def lm_head(W_lm: torch.Tensor, H: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Base logits [rows, V] = H @ W_lm^T (dspark_lm_head)."""
     return _gemv(lib().dspark_lm_head, W_lm, H, out)
+
+
+def _gemv_q8(entry, Wq, Wd, X, out):
+    _dev(Wq, torch.int8, "Wq", 2)
+    _dev(Wd, torch.float16, "Wd", 2)
+    _dev(X, torch.float32, "X", 2)
+    N, K = Wq.shape
+    M = X.shape[0]
+    if X.shape[1] != K or K % 32 != 0 or tuple(Wd.shape) != (N, K // 32):
+        raise ValueError("Wq [N, K] (K % 32 == 0), Wd [N, K / 32] and X [M, K] required")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _dev(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check(entry(Wq.data_ptr(), Wd.data_ptr(), N, K, X.data_ptr(), M, out.data_ptr(), _stream(Wq)))
+    return out
+
+
+def proj_smallm_q8(Wq: torch.Tensor, Wd: torch.Tensor, X: torch.Tensor, out: torch.Tensor | None = None):
+    """Y = X @ dequant(W).T for Q8_0 weights (dspark_proj_smallm_q8): Wq int8 [N, K],
+    Wd float16 [N, K / 32] (the block scales), X fp32 [M, K]."""
+    return _gemv_q8(lib().dspark_proj_smallm_q8, Wq, Wd, X, out)
+
+
+def lm_head_q8(Wq: torch.Tensor, Wd: torch.Tensor, H: torch.Tensor, out: torch.Tensor | None = None):
+    """Base logits from a Q8_0 lm_head (dspark_lm_head_q8)."""
+    return _gemv_q8(lib().dspark_lm_head_q8, Wq, Wd, H, out)
+
+
+def q8_from_numpy(q, d_bits, device):
+    """Upload Q8_0 weights (int8 quants, uint16 binary16 scale bits) as torch tensors."""
+    import numpy as np
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.int8)).to(device)
+    dt = torch.from_numpy(np.ascontiguousarray(d_bits, dtype=np.uint16).view(np.float16)).to(device)
+    return qt, dt
 
 
 def markov_workspace_bytes(num_reqs: int, k: int, V: int) -> int:

@@ -111,6 +111,36 @@ dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H,
                              float* logits, void* stream);
 
 /*
+ * dspark_proj_smallm_q8, dspark_lm_head_q8 -- the same products over Q8_0
+ * weights.
+ *
+ * [SI441] "Proposed work": the weight-stationary batched matvec it would
+ * reuse targets quantized weights. [DS772] "Summary": the GPU path takes
+ * Q8_0 weights. Q8_0 is read as the GGUF block format: entries 32b..32b+31
+ * of a weight row share one IEEE binary16 scale d[n, b], and entry t is
+ * d[n, t / 32] * q[n, t] with q a signed 8-bit integer. Here quants and
+ * scales are two arrays (a GGUF tensor, whose blocks interleave them, is
+ * split once when it is loaded).
+ *
+ *   Y[m, n] = sum_{t < K} X[m, t] * d[n, t / 32] * q[n, t]
+ *
+ *   Wq  int8   [N, K]       16-byte aligned
+ *   Wd  binary16 bits [N, K / 32]  2-byte aligned
+ *   X   fp32   [M, K]       16-byte aligned
+ *   Y   fp32   [M, N]        4-byte aligned, overwritten
+ * Sizes: N >= 1, K >= 32 with K % 32 == 0, K <= 4194304, M >= 1, and a
+ * workgroup's quant rows (about N / CUs) times K bytes below 2 GiB
+ * (DSPARK_ERR_SHAPE otherwise). The weights are read once per 16 rows of X.
+ * Accuracy: X is split exactly into two bf16 terms (residual <= 2^-17 |x|),
+ * the quants are exact in bf16, and each block's product is scaled and
+ * added in fp32; the summation order depends on the shape only.
+ */
+dspark_status dspark_proj_smallm_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M,
+                                    float* Y, void* stream);
+dspark_status dspark_lm_head_q8(const int8_t* Wq, const uint16_t* Wd, int V, int d, const float* H, int rows,
+                                float* logits, void* stream);
+
+/*
  * Bytes of device workspace dspark_markov_sample needs for these sizes
  * (0 when a size is out of range). The layout is the same for every valid
  * size (about 2 MiB), so one workspace serves calls of any shape.

@@ -24,13 +24,14 @@ def declared():
     code = open(HEADER).read()
     code = re.sub(r"/\*.*?\*/", "", code, flags=re.S)
     code = re.sub(r"//[^\n]*", "", code)
-    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", code)))
+    return sorted(set(re.findall(r"\b(dspark_[a-z0-9_]+)\s*\(", code)))
 
 
 def test_header_declares_the_entry_points():
     names = declared()
     for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
-              "dspark_markov_sample_probe", "dspark_draft_round", "dspark_markov_workspace_bytes",
+              "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
+              "dspark_markov_workspace_bytes",
               "dspark_status_string"]:
         assert n in names
 
@@ -65,6 +66,22 @@ def test_gemv_errors(L):
         assert fn(MIS, 16, 64, A, 7, A2, None) == ERR_ALIGN
         assert fn(A, 16, 64, MIS, 7, A2, None) == ERR_ALIGN
         assert fn(A, 16, 64, A, 7, A2 + 1, None) == ERR_ALIGN
+
+
+def test_gemv_q8_errors(L):
+    for fn in (L.dspark_proj_smallm_q8, L.dspark_lm_head_q8):
+        assert fn(None, A, 16, 64, A, 7, A2, None) == ERR_NULL
+        assert fn(A, None, 16, 64, A, 7, A2, None) == ERR_NULL
+        assert fn(A, A, 16, 64, None, 7, A2, None) == ERR_NULL
+        assert fn(A, A, 16, 64, A, 7, None, None) == ERR_NULL
+        assert fn(A, A, 0, 64, A, 7, A2, None) == ERR_SHAPE
+        assert fn(A, A, 16, 16, A, 7, A2, None) == ERR_SHAPE      # K < 32
+        assert fn(A, A, 16, 80, A, 7, A2, None) == ERR_SHAPE      # K % 32 != 0
+        assert fn(A, A, 16, 64, A, 0, A2, None) == ERR_SHAPE
+        assert fn(A, A, 16, (1 << 22) + 32, A, 7, A2, None) == ERR_SHAPE
+        assert fn(A + 8, A, 16, 64, A, 7, A2, None) == ERR_ALIGN  # quants need 16 bytes
+        assert fn(A, A + 1, 16, 64, A, 7, A2, None) == ERR_ALIGN  # scales need 2
+        assert fn(A, A, 16, 64, MIS, 7, A2, None) == ERR_ALIGN
 
 
 def test_markov_errors(L):

@@ -108,6 +108,75 @@ def test_lm_head_full_size_sampled(dev):
     logits_close(y[:, pick], oracle.gemv_rows(W, H, pick), "lm_head sampled")
 
 
+# ---------------------------------------------------------------------------
+# GEMV over Q8_0 weights
+# ---------------------------------------------------------------------------
+
+GEMV_Q8_CASES = [
+    # (M, N, K): one block, K not a multiple of the 128-entry wave segment,
+    # several phases with a partial last one, ragged N, both row packings,
+    # more than 16 rows (several launches)
+    (1, 1, 32), (7, 4096, 4096), (7, 4099, 96), (15, 1000, 160), (16, 2049, 4128), (3, 300, 7424),
+    (8, 33, 64), (9, 777, 2080), (20, 515, 256), (4, 65, 5120), (7, 16, 12288),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_Q8_CASES)
+@pytest.mark.parametrize("entry", ["proj_smallm_q8", "lm_head_q8"])
+def test_gemv_q8_matches_oracle(dev, entry, M, N, K):
+    seed = 7100 + M * 31 + N + K
+    say(f"[gemv {entry}] M={M} N={N} K={K} seed={seed}")
+    Wq, Wd, X = synth.gemv_q8_inputs(M, N, K, seed)
+    q, d = _ops().q8_from_numpy(Wq, Wd, dev)
+    y = getattr(_ops(), entry)(q, d, _up(X, dev))
+    torch.cuda.synchronize()
+    logits_close(y.cpu().numpy(), oracle.gemv_q8(Wq, Wd, X), f"{entry} M={M} N={N} K={K}")
+
+
+def test_gemv_q8_scale_edge_values(dev):
+    """Scales of either sign, subnormal and the largest binary16, quants at
+    -128 and 127: every block's scale lands on its own 32 entries."""
+    M, N, K = 5, 70, 192
+    g = np.random.default_rng(77)
+    say(f"[gemv q8 edge scales] M={M} N={N} K={K}")
+    Wq = g.integers(-128, 128, size=(N, K)).astype(np.int8)
+    Wq[0, :] = -128
+    Wq[1, :] = 127
+    e = g.integers(1, 22, size=(N, K // 32))
+    Wd = ((g.integers(0, 2, size=e.shape) << 15) | (e << 10) | g.integers(0, 1024, size=e.shape)).astype(np.uint16)
+    Wd[2, :] = 0x0001  # least subnormal
+    Wd[3, :] = 0x7BFF  # 65504
+    Wd[4, :] = 0x8000  # -0
+    X = (g.standard_normal((M, K)) * 0.01).astype(np.float32)
+    q, d = _ops().q8_from_numpy(Wq, Wd, dev)
+    y = _ops().proj_smallm_q8(q, d, _up(X, dev))
+    torch.cuda.synchronize()
+    logits_close(y.cpu().numpy(), oracle.gemv_q8(Wq, Wd, X), "q8 edge scales")
+
+
+def test_lm_head_q8_full_size_sampled(dev):
+    """Qwen3-8B-shaped head with Q8_0 weights at full size; oracle on sampled
+    rows incl. the ragged tail; reruns bit-identical; a row's output does not
+    depend on the other rows (M = 7 vs M = 1, same packing)."""
+    cfg = synth.CONFIGS["qwen3_8b_head"]
+    V, d, rows = cfg["V"], cfg["d"], cfg["B"]
+    seed = synth.config_seed("qwen3_8b_head")
+    say(f"[lm_head q8 full] V={V} d={d} rows={rows} seed={seed}")
+    Wq, Wd, H = synth.gemv_q8_inputs(rows, V, d, seed)
+    q, dd = _ops().q8_from_numpy(Wq, Wd, dev)
+    Hd = _up(H, dev)
+    y = _ops().lm_head_q8(q, dd, Hd)
+    y2 = _ops().lm_head_q8(q, dd, Hd)
+    y1 = _ops().lm_head_q8(q, dd, Hd[3:4].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "rerun differs"
+    assert torch.equal(y[3:4], y1), "row 3 depends on the other rows"
+    y = y.cpu().numpy()
+    pick = np.unique(np.concatenate([np.arange(32), np.arange(V - 48, V),
+                                     np.random.default_rng(1).choice(V, 3000, replace=False)]))
+    logits_close(y[:, pick], oracle.gemv_q8_rows(Wq, Wd, H, pick), "lm_head q8 sampled")
+
+
 @pytest.mark.parametrize("N,K", [(9000, 4096), (151936, 4096), (4096, 12288), (248320, 5120)])
 def test_gemv_invariants(dev, N, K):
     """Deterministic reruns; a row's output does not depend on the other rows
