@@ -11,11 +11,12 @@
 // Design on gfx950 (the bf16 streaming kernel's structure, one byte per
 // weight):
 //  * 16 waves per workgroup, one workgroup per CU over a balanced contiguous
-//    row range; every 16-row tile is split along K over the waves (4 blocks
-//    of 32 entries per wave and phase), two tiles of loads in flight.
-//  * Each wave loads its 16 x 128-byte segment of a tile in whole 128-byte
-//    lines (non-temporal raw buffer loads; zeros past the range), together
-//    with the tile's 16 x 4 scales, and stages both in a private LDS area.
+//    row range; every 16-row tile is split along K over the waves (8 blocks
+//    of 32 entries per wave and phase, 4 for more than 8 rows of X), two
+//    tiles of loads in flight.
+//  * Each wave loads its 16 x 256-byte (128-byte) segment of a tile in whole
+//    128-byte lines (non-temporal raw buffer loads; zeros past the range),
+//    together with the tile's scales, and stages both in a private LDS area.
 //  * B fragments: 8 quants per lane, converted exactly to bf16 (a signed
 //    byte has at most 8 significant bits: one sign-extending convert per
 //    value and a byte permute per pair). A fragments: X split exactly into
@@ -43,13 +44,7 @@ struct Q8Params {
   int pq, prem; // row pairs per workgroup: N/2 = pq * gridDim.x + prem
 };
 
-constexpr int kQNW = 16;                 // waves per workgroup
-constexpr int kQKBW = 4;                 // 32-entry blocks per wave and phase
-constexpr int kQSeg = 32 * kQKBW;        // quant bytes of a row segment (one 128-byte line)
-constexpr int kQRS = kQSeg + 16;         // padded LDS row stride
-constexpr int kQLPR = kQSeg / 16;        // lanes per row in a load instruction
-constexpr int kQRPI = kWave / kQLPR;     // rows per load instruction
-constexpr int kQNLD = 16 / kQRPI;        // load instructions per tile
+constexpr int kQNW = 16;  // waves per workgroup
 constexpr size_t kQLds = 160 * 1024;
 
 __device__ __forceinline__ int2 q8_rows(const Q8Params& p) {
@@ -76,10 +71,18 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
-// MULTI: more than one K phase (the chunk loop runs every phase per chunk).
-template <bool PACK, bool MULTI>
+// KBW: 32-entry blocks per wave and phase (4 or 8: 128 or 256 quant bytes
+// of each row per wave). MULTI: more than one K phase (the chunk loop runs
+// every phase per chunk).
+template <bool PACK, bool MULTI, int KBW>
 __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
-  constexpr int NW = kQNW, KBW = kQKBW, RS = kQRS, LPR = kQLPR, RPI = kQRPI, NLD = kQNLD;
+  constexpr int NW = kQNW;
+  constexpr int SEG = 32 * KBW;     // quant bytes of a row segment
+  constexpr int RS = SEG + 16;      // padded LDS row stride
+  constexpr int LPR = SEG / 16;     // lanes per row in a load instruction
+  constexpr int RPI = kWave / LPR;  // rows per load instruction
+  constexpr int NLD = 16 / RPI;     // load instructions per tile
+  constexpr int SPL = KBW / 4;      // scale loads per lane and tile
   constexpr int F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* tr = smem;                                                           // [NW][16][RS] quants
@@ -112,9 +115,9 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
 
   u32x4 afr[KBW][F];
   u32x4 b0[NLD], b1[NLD];
-  uint32_t s0 = 0, s1 = 0;  // the scale half of this lane (row i, block g of the segment)
+  uint32_t s0[SPL], s1[SPL];  // scale halves of this lane: row i, blocks g + 4j of the segment
   int ph = 0, c0 = 0, c1 = 0, lim = 0;
-  uint32_t lane_off = 0, sc_off = 0;
+  uint32_t lane_off = 0, sc_off[SPL];
 
   // Phase ph: this wave's segment starts at entry kseg (block kseg / 32).
   // Lanes past K start out of range and read zeros.
@@ -123,8 +126,11 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
     const int kseg = 32 * KBW * (ph * NW + w);
     lane_off = kseg + 16 * lchunk < K ? static_cast<uint32_t>(lrow) * rowb + static_cast<uint32_t>(kseg + 16 * lchunk)
                                       : kBufOutOfRange;
-    const int blk = kseg / 32 + g;
-    sc_off = blk < KB ? static_cast<uint32_t>(i) * drow + static_cast<uint32_t>(blk) * 2 : kBufOutOfRange;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int blk = kseg / 32 + g + 4 * j;
+      sc_off[j] = blk < KB ? static_cast<uint32_t>(i) * drow + static_cast<uint32_t>(blk) * 2 : kBufOutOfRange;
+    }
   };
   // A fragments of phase ph: block kb covers k = kseg + 32*kb + 8*g + (0..7).
   auto build_a = [&]() {
@@ -163,14 +169,15 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
     }
   };
   // Tile rr: quants and scales; rows past r1 and tiles past lim read zeros.
-  auto load = [&](u32x4 (&b)[NLD], uint32_t& s, int rr) {
+  auto load = [&](u32x4 (&b)[NLD], uint32_t (&s)[SPL], int rr) {
     const bool live = rr < lim;
     const uint32_t off = live ? lane_off + static_cast<uint32_t>(rr) * 16 * rowb : kBufOutOfRange;
 #pragma unroll
     for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(qres, off + static_cast<uint32_t>(q * RPI) * rowb);
-    s = __builtin_amdgcn_raw_buffer_load_b16(dres, static_cast<int>(live ? sc_off + static_cast<uint32_t>(rr) * 16 * drow
-                                                                          : kBufOutOfRange),
-                                             0, 0);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j)
+      s[j] = __builtin_amdgcn_raw_buffer_load_b16(
+          dres, static_cast<int>(live ? sc_off[j] + static_cast<uint32_t>(rr) * 16 * drow : kBufOutOfRange), 0, 0);
   };
   auto prologue = [&](bool with_a) {
     load(b0, s0, c0);
@@ -179,13 +186,20 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
     load(b1, s1, c0 + 1);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute_publish = [&](u32x4 (&b)[NLD], uint32_t s, int buf) {
+  auto compute_publish = [&](u32x4 (&b)[NLD], const uint32_t (&s)[SPL], int buf) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
-    wsc[i * KBW + g] = static_cast<uint16_t>(s);
-    const uint2 sh = *reinterpret_cast<const uint2*>(wsc + i * KBW);  // the 4 scales of row i
-    const float scale[KBW] = {half_bits_to_float(sh.x & 0xffffu), half_bits_to_float(sh.x >> 16),
-                              half_bits_to_float(sh.y & 0xffffu), half_bits_to_float(sh.y >> 16)};
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) wsc[i * KBW + g + 4 * j] = static_cast<uint16_t>(s[j]);
+    float scale[KBW];  // the KBW scales of row i
+#pragma unroll
+    for (int j = 0; j < KBW / 4; ++j) {
+      const uint2 sh = *reinterpret_cast<const uint2*>(wsc + i * KBW + 4 * j);
+      scale[4 * j] = half_bits_to_float(sh.x & 0xffffu);
+      scale[4 * j + 1] = half_bits_to_float(sh.x >> 16);
+      scale[4 * j + 2] = half_bits_to_float(sh.y & 0xffffu);
+      scale[4 * j + 3] = half_bits_to_float(sh.y >> 16);
+    }
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KBW; ++kb) {
@@ -263,10 +277,10 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
   }
 }
 
-template <bool PACK>
+template <bool PACK, int KBW>
 hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
-  const void* one = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, false>);
-  const void* many = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, true>);
+  const void* one = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, false, KBW>);
+  const void* many = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, true, KBW>);
   static const hipError_t attr = [&] {
     const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kQLds));
     return e != hipSuccess ? e
@@ -296,13 +310,16 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
   const int grid = std::max(1, std::min(cus, std::min(tiles, std::max(1, N / 2))));
   const int rounds = (q8_rows_max(N, grid) + 15) / 16;
   const int KB = K / 32;
-  const bool multi = (KB + kQNW * kQKBW - 1) / (kQNW * kQKBW) > 1;
   // Launches of at most 16 rows of X each (the weights are read once per launch).
   for (int m0 = 0; m0 < M; m0 += 16) {
     const int mm = std::min(16, M - m0);
     const bool pack = mm <= 8;
     const int rowsl = pack ? 8 : 16;
-    const size_t fixed = static_cast<size_t>(kQNW) * 16 * kQRS + static_cast<size_t>(kQNW) * 16 * kQKBW * 2 +
+    // 8 blocks (256 quant bytes of a row) per wave and phase keep twice the
+    // bytes in flight of 4; rows of 9..16 activations take 4 (registers).
+    const int kbw = pack ? 8 : 4;
+    const bool multi = (KB + kQNW * kbw - 1) / (kQNW * kbw) > 1;
+    const size_t fixed = static_cast<size_t>(kQNW) * 16 * (32 * kbw + 16) + static_cast<size_t>(kQNW) * 16 * kbw * 2 +
                          static_cast<size_t>(2) * kQNW * rowsl * 16 * 4;
     const size_t per_tile = static_cast<size_t>(mm) * 16 * 4;
     int chunk = static_cast<int>((kQLds - fixed) / per_tile) & ~1;
@@ -320,8 +337,8 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
     prm.pq = (N / 2) / grid;
     prm.prem = (N / 2) % grid;
     const size_t lds = fixed + chunk * per_tile;
-    const hipError_t e = pack ? launch_q8<true>(prm, grid, lds, multi, stream)
-                              : launch_q8<false>(prm, grid, lds, multi, stream);
+    const hipError_t e = pack ? launch_q8<true, 8>(prm, grid, lds, multi, stream)
+                              : launch_q8<false, 4>(prm, grid, lds, multi, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
