@@ -117,6 +117,22 @@ dspark_status markov_checks(const float* base, int num_reqs, int B, int V, const
   return DSPARK_OK;
 }
 
+dspark_status markov_q8_checks(const float* base, int num_reqs, int B, int V, const int8_t* w1q, const uint16_t* w1d,
+                               const int8_t* w2q, const uint16_t* w2d, int r, const int64_t* d2t,
+                               const int64_t* prev0, int k, const int64_t* ids_out, const void* workspace,
+                               size_t workspace_bytes) {
+  if (!base || !w1q || !w1d || !w2q || !w2d || !prev0 || !ids_out) return DSPARK_ERR_NULL;
+  if (num_reqs < 1 || num_reqs > 16 || B < 1 || V < 1 || k < 1 || k > B || k > 32 || r < 32 || r > 256 || (r % 32) != 0)
+    return DSPARK_ERR_SHAPE;
+  if (!aligned(base, 4) || !aligned(w1q, 16) || !aligned(w2q, 16) || !aligned(w1d, 2) || !aligned(w2d, 2) ||
+      !aligned(prev0, 8) || !aligned(ids_out, 8) || (d2t && !aligned(d2t, 8)))
+    return DSPARK_ERR_ALIGN;
+  const size_t need = dspark::markov_workspace_bytes(num_reqs, k, V);
+  if (!workspace || workspace_bytes < need) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
 dspark_status probe_checks(const float* x, int M, int D, const uint16_t* w, const float* logit_out,
                            const int32_t* pass_out) {
   if (!x || !w || !logit_out) return DSPARK_ERR_NULL;
@@ -181,6 +197,42 @@ dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float
   const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
   return from_hip(dspark::launch_markov(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,
                                         probe_w ? &pa : nullptr, s));
+}
+
+dspark_status dspark_markov_sample_q8(const float* base, int num_reqs, int B, int V, const int8_t* w1q,
+                                      const uint16_t* w1d, const int8_t* w2q, const uint16_t* w2d, int r,
+                                      const int64_t* d2t, const int64_t* prev0, int k, int64_t* ids_out,
+                                      void* workspace, size_t workspace_bytes, const float* probe_x, int probe_M,
+                                      int probe_D, const uint16_t* probe_w, float probe_bias, float probe_threshold,
+                                      float* logit_out, int32_t* pass_out, void* stream) {
+  dspark_status st = markov_q8_checks(base, num_reqs, B, V, w1q, w1d, w2q, w2d, r, d2t, prev0, k, ids_out, workspace,
+                                      workspace_bytes);
+  if (st == DSPARK_OK && probe_x) st = probe_checks(probe_x, probe_M, probe_D, probe_w, logit_out, pass_out);
+  if (st != DSPARK_OK) return st;
+  const dspark::ProbeArgs pa{probe_x, probe_M, probe_D, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
+  return from_hip(dspark::launch_markov_q8(base, num_reqs, B, V, w1q, w1d, w2q, w2d, r, d2t, prev0, k, ids_out,
+                                           workspace, probe_x ? &pa : nullptr, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_draft_round_q8(const int8_t* Wq_lm, const uint16_t* Wd_lm, int V, int d, const float* H,
+                                    int num_reqs, int B, const int8_t* w1q, const uint16_t* w1d, const int8_t* w2q,
+                                    const uint16_t* w2d, int r, const int64_t* d2t, const int64_t* prev0, int k,
+                                    const uint16_t* probe_w, float probe_bias, float probe_threshold, float* base_out,
+                                    int64_t* ids_out, float* logit_out, int32_t* pass_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (num_reqs < 1 || num_reqs > 16 || B < 1 || B > (1 << 20)) return DSPARK_ERR_SHAPE;
+  const int rows = num_reqs * B;
+  dspark_status st = gemv_q8_checks(Wq_lm, Wd_lm, V, d, H, rows, base_out);
+  if (st == DSPARK_OK)
+    st = markov_q8_checks(base_out, num_reqs, B, V, w1q, w1d, w2q, w2d, r, d2t, prev0, k, ids_out, workspace,
+                          workspace_bytes);
+  if (st == DSPARK_OK && probe_w) st = probe_checks(H, rows, d, probe_w, logit_out, pass_out);
+  if (st != DSPARK_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dspark::launch_gemv_q8(Wq_lm, Wd_lm, V, d, H, rows, base_out, s) != hipSuccess) return DSPARK_ERR_HIP;
+  const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
+  return from_hip(dspark::launch_markov_q8(base_out, num_reqs, B, V, w1q, w1d, w2q, w2d, r, d2t, prev0, k, ids_out,
+                                           workspace, probe_w ? &pa : nullptr, s));
 }
 
 }  // extern "C"

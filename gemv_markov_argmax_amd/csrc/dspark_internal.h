@@ -10,6 +10,7 @@ namespace dspark {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -211,6 +212,11 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
                          int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
                          hipStream_t stream);
 
+// The same loop over Q8_0 markov weights (r % 32 == 0); see dspark_markov_sample_q8.
+hipError_t launch_markov_q8(const float* base, int R, int B, int V, const int8_t* w1q, const uint16_t* w1d,
+                            const int8_t* w2q, const uint16_t* w2d, int r, const int64_t* d2t,
+                            const int64_t* prev0, int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
+                            hipStream_t stream);
 hipError_t launch_probe(const float* x, int M, int D, const uint16_t* w, float bias,
                         float threshold, float* logit, int32_t* pass, hipStream_t stream);
 

@@ -52,6 +52,7 @@
 #include "dspark_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dspark {
 namespace {
@@ -88,6 +89,11 @@ struct MarkovParams {
   int base_in_lds;       // 0: base values are read straight from memory (slice too large)
   int probe_on;          // nonzero: also compute the confidence probe described by `probe`
   ProbeArgs probe;
+  // Q8_0 weights (the Q8 kernels): quants [V, r] and binary16 block scales [V, r / 32]
+  const int8_t* w1q;
+  const uint16_t* w1d;
+  const int8_t* w2q;
+  const uint16_t* w2d;
 };
 
 __device__ __forceinline__ bool prev0_ok(const MarkovParams& p, int m) {
@@ -105,15 +111,46 @@ __device__ __forceinline__ uint32_t load_coherent(const uint32_t* a) {
 
 constexpr int kMaxPoll = kMaxGroups / kWave;  // slots per lane when polling
 
-template <int NW, int KB, int RT, int LT, bool BL>
+// One k-block (32 entries of the rank) of a lane's MFMA operand: 8 bf16
+// values, or 8 int8 quants for Q8_0 weights.
+template <bool Q8>
+using Frag = std::conditional_t<Q8, uint2, u32x4>;
+
+// Q8_0 block scales are kept in LDS as rows of an even number of halves
+// (two per 32-bit word, so every word read is aligned).
+constexpr int scale_row(int KB) { return 2 * ((KB + 1) / 2); }
+// LDS bytes of one markov_w2 tile held in LDS: the fragments of KB k-blocks
+// for 64 lanes, and with Q8_0 weights the 16 rows' block scales.
+constexpr size_t lds_tile_bytes(int KB, bool Q8) {
+  return static_cast<size_t>(KB) * kWave * (Q8 ? 8 : 16) + (Q8 ? static_cast<size_t>(16) * scale_row(KB) * 2 : 0);
+}
+// LDS bytes of the A block: R + 1 rows (padded by 16 bytes), then with Q8_0
+// weights the rows' block scales (rounded up to 16 bytes).
+constexpr size_t a_row_bytes(int KB, bool Q8) { return static_cast<size_t>(KB) * (Q8 ? 32 : 64) + 16; }
+constexpr size_t a_block_bytes(int R, int KB, bool Q8) {
+  return static_cast<size_t>(R + 1) * a_row_bytes(KB, Q8) +
+         (Q8 ? (static_cast<size_t>(R + 1) * scale_row(KB) * 2 + 15) / 16 * 16 : 0);
+}
+
+__device__ __forceinline__ float half_lo(uint32_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v))); }
+__device__ __forceinline__ float half_hi(uint32_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16))); }
+
+template <int NW, int KB, int RT, int LT, bool BL, bool Q8>
 __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p) {
   constexpr int kLoopThreads = NW * kWave;
+  using BF = Frag<Q8>;
+  constexpr int kSH = (KB + 1) / 2;  // packed scale pairs of a row (Q8)
+  constexpr int kSR = 2 * kSH;       // halves per LDS scale row (Q8)
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4* w2l = reinterpret_cast<u32x4*>(smem);                                         // [lds_tiles][KB][64]
-  uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * 1024);  // [NW][16]
-  // A block: R rows, then a zero row read by the lanes of absent requests.
-  unsigned char* a_lds = reinterpret_cast<unsigned char*>(keys_s + NW * kMaxReqs);       // [R + 1][KB*64 + 16]
-  int* prev_s = reinterpret_cast<int*>(a_lds + (p.R + 1) * (KB * 64 + 16));             // [16] prev0 (valid or 0)
+  BF* w2l = reinterpret_cast<BF*>(smem);                                               // [lds_tiles][KB][64]
+  uint16_t* w2ls = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(p.lds_tiles) * KB * kWave * sizeof(BF));  // [lds_tiles][16][kSR] (Q8)
+  uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + static_cast<size_t>(p.lds_tiles) * lds_tile_bytes(KB, Q8));  // [NW][16]
+  // A block: R rows, then a zero row read by the lanes of absent requests
+  // (with Q8_0 weights followed by the rows' block scales).
+  constexpr int kARow = static_cast<int>(a_row_bytes(KB, Q8));
+  unsigned char* a_lds = reinterpret_cast<unsigned char*>(keys_s + NW * kMaxReqs);       // [R + 1][kARow]
+  uint16_t* a_sc = reinterpret_cast<uint16_t*>(a_lds + (p.R + 1) * kARow);              // [R + 1][kSR] (Q8)
+  int* prev_s = reinterpret_cast<int*>(a_lds + a_block_bytes(p.R, KB, Q8));            // [16] prev0 (valid or 0)
   int* tok_s = prev_s + kMaxReqs;                                                       // [k][R] drafted tokens
   float* basel = reinterpret_cast<float*>(tok_s + p.k * p.R);                           // [R][bstride]
 
@@ -133,16 +170,48 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     const int row = min((t0 + j) * 16 + lrow, V - 1);
     return p.w2 + static_cast<size_t>(row) * r;
   };
+  const int KBr = r / 32;  // Q8_0 blocks per row
+  auto w2q_row = [&](int j, int lrow) {
+    const int row = min((t0 + j) * 16 + lrow, V - 1);
+    return p.w2q + static_cast<size_t>(row) * r;
+  };
+  auto w2d_row = [&](int j, int lrow) {
+    const int row = min((t0 + j) * 16 + lrow, V - 1);
+    return p.w2d + static_cast<size_t>(row) * KBr;
+  };
+  // Lane fragment of k-block kb of tile j (row = 16 (t0 + j) + i, entries
+  // 32 kb + 8 g .. + 7), zeros past the rank.
+  auto frag_of = [&](int j, int kb, int lrow, int lg) -> BF {
+    if constexpr (Q8) {
+      return kb * 32 + 8 * lg < r ? *reinterpret_cast<const uint2*>(w2q_row(j, lrow) + kb * 32 + 8 * lg) : uint2{0u, 0u};
+    } else {
+      return kb * 32 + 8 * lg < r ? load16(w2_row(j, lrow) + kb * 32 + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // Q8_0: the block scales of row lrow of tile j, two per word (zeros past the rank).
+  auto scales_of = [&](int j, int lrow, uint32_t (&sc)[kSH]) {
+    const uint16_t* sd = w2d_row(j, lrow);
+#pragma unroll
+    for (int h = 0; h < kSH; ++h) {
+      const uint32_t lo = 2 * h < KBr ? sd[2 * h] : 0u, hi = 2 * h + 1 < KBr ? sd[2 * h + 1] : 0u;
+      sc[h] = lo | (hi << 16);
+    }
+  };
 
   // ---- load this workgroup's markov_w2 tiles once: registers, then LDS
-  u32x4 wreg[RT > 0 ? RT : 1][KB];
+  BF wreg[RT > 0 ? RT : 1][KB];
+  uint32_t wsc[Q8 && RT > 0 ? RT : 1][Q8 ? kSH : 1];  // Q8_0: block scales of the register tiles
 #pragma unroll
   for (int u = 0; u < RT; ++u) {
     const int j = w + NW * u;
-    const uint16_t* src = w2_row(j, i) + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      wreg[u][kb] = (j < nreg && kb * 32 + 8 * g < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < KB; ++kb) wreg[u][kb] = j < nreg ? frag_of(j, kb, i, g) : BF{};
+    if constexpr (Q8) {
+      scales_of(j, i, wsc[u]);
+      if (j >= nreg)
+#pragma unroll
+        for (int h = 0; h < kSH; ++h) wsc[u][h] = 0u;
+    }
   }
   // LDS tiles: eight loads per thread in flight at a time, then their LDS
   // writes (one load and write after the other would serialize the latency).
@@ -150,7 +219,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     constexpr int kBatch = 8;
     const int nl = (nheld - nreg) * KB * kWave;
     for (int e0 = 0; e0 < nl; e0 += kBatch * kLoopThreads) {
-      u32x4 v[kBatch];
+      BF v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int e = min(e0 + u * kLoopThreads + tid, nl - 1);
@@ -158,13 +227,25 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
         const int gg = ln >> 4;
         // (lanes past r read column 0 and store zeros: straight code)
         const bool kok = kb * 32 + 8 * gg < r;
-        v[u] = load16(w2_row(nreg + jj, ln & 15) + (kok ? kb * 32 + 8 * gg : 0));
-        v[u] = kok ? v[u] : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (Q8) {
+          v[u] = *reinterpret_cast<const uint2*>(w2q_row(nreg + jj, ln & 15) + (kok ? kb * 32 + 8 * gg : 0));
+          v[u] = kok ? v[u] : uint2{0u, 0u};
+        } else {
+          v[u] = load16(w2_row(nreg + jj, ln & 15) + (kok ? kb * 32 + 8 * gg : 0));
+          v[u] = kok ? v[u] : u32x4{0u, 0u, 0u, 0u};
+        }
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int e = e0 + u * kLoopThreads + tid;
         if (e < nl) w2l[e] = v[u];
+      }
+    }
+    if constexpr (Q8) {  // the LDS tiles' block scales: [tile][row][kSR]
+      const int ns = (nheld - nreg) * 16 * kSR;
+      for (int e = tid; e < ns; e += kLoopThreads) {
+        const int kb = e % kSR, row = (e / kSR) % 16, jj = e / (16 * kSR);
+        w2ls[e] = kb < KBr ? w2d_row(nreg + jj, row)[kb] : static_cast<uint16_t>(0);
       }
     }
   }
@@ -252,21 +333,28 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   // rows fall in different banks). A polling wave gathers its request's row
   // as soon as it knows the token (r <= 1024: at most two 16-byte loads per
   // lane); the LDS writes follow once the stagers' loads are out too.
-  constexpr int kARow = KB * 64 + 16;
-  auto gather_fetch = [&](int tok, u32x4 (&gv)[2]) {
-    const uint16_t* src = p.w1 + static_cast<size_t>(tok) * r;
+  // (Q8_0: the row's quants, r bytes, and its r / 32 block scales.)
+  constexpr int kRowChunks = Q8 ? 1 : 2;  // 16-byte loads per lane (r <= 1024)
+  const int nchunk = Q8 ? r / 16 : r / 8;  // 16-byte chunks of a row
+  auto gather_fetch = [&](int tok, u32x4 (&gv)[2], uint32_t& gs) {
+    const unsigned char* src = Q8 ? reinterpret_cast<const unsigned char*>(p.w1q + static_cast<size_t>(tok) * r)
+                                  : reinterpret_cast<const unsigned char*>(p.w1 + static_cast<size_t>(tok) * r);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kRowChunks; ++q) {
       const int c = lane + q * kWave;  // 16-byte chunk of the row
-      gv[q] = load16(src + 8 * (c < r / 8 ? c : 0));
+      gv[q] = load16(src + 16 * (c < nchunk ? c : 0));
     }
+    gs = 0u;
+    if constexpr (Q8) gs = p.w1d[static_cast<size_t>(tok) * KBr + (lane < KBr ? lane : 0)];
   };
-  auto gather_store = [&](int m, const u32x4 (&gv)[2]) {
+  auto gather_store = [&](int m, const u32x4 (&gv)[2], uint32_t gs) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kRowChunks; ++q) {
       const int c = lane + q * kWave;
-      if (c < r / 8) *reinterpret_cast<u32x4*>(a_lds + m * kARow + 16 * c) = gv[q];
+      if (c < nchunk) *reinterpret_cast<u32x4*>(a_lds + m * kARow + 16 * c) = gv[q];
     }
+    if constexpr (Q8)
+      if (lane < KBr) a_sc[m * kSR + lane] = static_cast<uint16_t>(gs);
   };
 
   // The confidence probe, when asked for: it depends on nothing the loop
@@ -307,13 +395,14 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   // Prologue: zero the A block (columns past r stay zero: the markov_w2
   // fragments are zero there too, and uninitialized LDS could hold NaNs),
   // then the rows of step 0 and the base slice of step 0.
-  for (int e = tid; e < (R + 1) * kARow / 16; e += kLoopThreads)
+  for (int e = tid; e < static_cast<int>(a_block_bytes(R, KB, Q8) / 16); e += kLoopThreads)
     reinterpret_cast<u32x4*>(a_lds)[e] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   for (int m = w; m < R; m += NW) {
     u32x4 gv[2];
-    gather_fetch(prev_s[m], gv);
-    gather_store(m, gv);
+    uint32_t gs;
+    gather_fetch(prev_s[m], gv, gs);
+    gather_store(m, gv, gs);
   }
   stage_fetch(0);
   stage_store(0);
@@ -352,7 +441,47 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     };
     // A fragment kb of this lane: k = 32*kb + 8*g + (0..7) of row i, read
     // from LDS where it is needed (it feeds every tile of the k-block).
-    const u32x4* a_frag = reinterpret_cast<const u32x4*>(a_lds + min(li, R) * kARow + 16 * lg);  // + 4*kb
+    const BF* a_frag = reinterpret_cast<const BF*>(a_lds + min(li, R) * kARow + sizeof(BF) * lg);  // + 4*kb
+    // Q8_0: the block scales of the A rows of this lane's outputs (rows
+    // 4 lg + v; past R the zero row): up to 8 blocks held in registers, two
+    // per word, read once per step; longer rows read them per k-block.
+    constexpr bool kAscReg = Q8 && KB <= 8;
+    uint32_t asc[kAscReg ? 4 : 1][kAscReg ? kSH : 1];
+    if constexpr (kAscReg) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h = 0; h < kSH; ++h)
+          asc[v][h] = reinterpret_cast<const uint32_t*>(a_sc + min(4 * lg + v, R) * kSR)[h];
+    }
+    auto a_scales = [&](int kb, float (&s1)[4]) {
+      if constexpr (kAscReg) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s1[v] = (kb & 1) ? half_hi(asc[v][kb >> 1]) : half_lo(asc[v][kb >> 1]);
+      } else if constexpr (Q8) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          s1[v] = static_cast<float>(__builtin_bit_cast(_Float16, a_sc[min(4 * lg + v, R) * kSR + kb]));
+      }
+    };
+    // One k-block of a tile into its accumulator. bf16: an MFMA chain.
+    // Q8_0: the block's exact integer dot products (int8 MFMA), scaled by
+    // the A row's and the tile row's block scales and added in fp32, for the
+    // A rows that exist (v < R for every lane group).
+    auto mac = [&](f32x4& acc, BF a, BF b, const uint32_t* bsc, int kb, const float (&s1)[4]) {
+      if constexpr (Q8) {
+        const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
+                                                             i32x4{0, 0, 0, 0}, 0, 0, 0);
+        const float s2 = (kb & 1) ? half_hi(bsc[kb >> 1]) : half_lo(bsc[kb >> 1]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (v == 0 || v < R) acc[v] = __builtin_fmaf(static_cast<float>(d[v]), s1[v] * s2, acc[v]);
+      } else {
+        (void)bsc;
+        (void)s1;
+        acc = mfma_16x16x32(a, b, acc);
+      }
+    };
 
     // Register tiles and the wave's first LT LDS tiles, all accumulation
     // chains interleaved per k-block, so one chain's MFMAs overlap the
@@ -368,28 +497,41 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       const bool first = u0 == 0;
       f32x4 accr[RG], accl[L1];
       int jl[L1];
-      const u32x4* srcl[L1];
+      const BF* srcl[L1];
+      uint32_t lsc[L1][Q8 ? kSH : 1];  // Q8_0: block scales of those LDS tiles (row li)
 #pragma unroll
       for (int t = 0; t < L1; ++t) {
         jl[t] = nreg + w + NW * t;
-        srcl[t] = w2l + static_cast<size_t>(jl[t] < nheld ? jl[t] - nreg : 0) * KB * kWave + ll;
+        const int lt = jl[t] < nheld ? jl[t] - nreg : 0;
+        srcl[t] = w2l + static_cast<size_t>(lt) * KB * kWave + ll;
         accl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (Q8) {
+          if (first)
+#pragma unroll
+            for (int h = 0; h < kSH; ++h)
+              lsc[t][h] = reinterpret_cast<const uint32_t*>(w2ls + (static_cast<size_t>(lt) * 16 + li) * kSR)[h];
+        }
       }
 #pragma unroll
       for (int u = 0; u < RG; ++u) accr[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 a = a_frag[4 * kb];
-        u32x4 bl[L1];
+        const BF a = a_frag[4 * kb];
+        float s1[4];
+        a_scales(kb, s1);
+        BF bl[L1];
         if (first)
 #pragma unroll
           for (int t = 0; t < L1; ++t) bl[t] = srcl[t][kb * kWave];
 #pragma unroll
         for (int u = 0; u < RG; ++u)
-          if (RT > 0 && u0 + u < RT) accr[u] = mfma_16x16x32(a, wreg[u0 + u < RT ? u0 + u : 0][kb], accr[u]);
+          if (RT > 0 && u0 + u < RT) {
+            const int uu = u0 + u < RT ? u0 + u : 0;
+            mac(accr[u], a, wreg[uu][kb], wsc[Q8 ? uu : 0], kb, s1);
+          }
         if (first)
 #pragma unroll
-          for (int t = 0; t < L1; ++t) accl[t] = mfma_16x16x32(a, bl[t], accl[t]);
+          for (int t = 0; t < L1; ++t) mac(accl[t], a, bl[t], lsc[t], kb, s1);
         // (one wave per SIMD: keep each k-block's fragment reads next to its
         // MFMAs, so that they do not pile up in registers ahead of them)
         if (NW == 4 && (kb & 1)) __builtin_amdgcn_sched_barrier(0);
@@ -403,22 +545,31 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     }
     // Further LDS tiles of this wave, if any.
     for (int j = nreg + w + NW * LT; j < nheld; j += NW) {
-      const u32x4* src = w2l + static_cast<size_t>(j - nreg) * KB * kWave + ll;
+      const BF* src = w2l + static_cast<size_t>(j - nreg) * KB * kWave + ll;
+      uint32_t sc1[Q8 ? kSH : 1];
+      if constexpr (Q8)
+#pragma unroll
+        for (int h = 0; h < kSH; ++h)
+          sc1[h] = reinterpret_cast<const uint32_t*>(w2ls + (static_cast<size_t>(j - nreg) * 16 + li) * kSR)[h];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(a_frag[4 * kb], src[kb * kWave], acc);
+      for (int kb = 0; kb < KB; ++kb) {
+        float s1[4];
+        a_scales(kb, s1);
+        mac(acc, a_frag[4 * kb], src[kb * kWave], sc1, kb, s1);
+      }
       score(j, true, acc);
     }
     // Tiles beyond on-chip capacity are read from memory at every step.
     for (int j = nheld + (((nreg + w - nheld) % NW) + NW) % NW; j < nt; j += NW) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      {
-        const uint16_t* src = w2_row(j, li) + 8 * lg;
+      uint32_t sc1[Q8 ? kSH : 1];
+      if constexpr (Q8) scales_of(j, li, sc1);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 b = (kb * 32 + 8 * lg < r) ? load16(src + kb * 32) : u32x4{0u, 0u, 0u, 0u};
-          acc = mfma_16x16x32(a_frag[4 * kb], b, acc);
-        }
+      for (int kb = 0; kb < KB; ++kb) {
+        float s1[4];
+        a_scales(kb, s1);
+        mac(acc, a_frag[4 * kb], frag_of(j, kb, li, lg), sc1, kb, s1);
       }
       score(j, true, acc);
     }
@@ -456,6 +607,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     // the winner's markov_w1 row is the next step's A row (wave w polls
     // request w, and then w + NW, ..., whose rows go to LDS at once)
     u32x4 gv[2];
+    uint32_t gs = 0u;
 #pragma unroll 1
     for (int h = 0; h < kMaxReqs / NW; ++h) {
       const int m = w + h * NW;
@@ -498,15 +650,16 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       int tok = static_cast<int>(key_index(kk));
       if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
       if (lane == 0) tok_s[step * R + m] = tok;
-      if (!last && h == 0) gather_fetch(tok, gv);
+      if (!last && h == 0) gather_fetch(tok, gv, gs);
       if (!last && h > 0) {
         u32x4 gv1[2];
-        gather_fetch(tok, gv1);
-        gather_store(m, gv1);
+        uint32_t gs1;
+        gather_fetch(tok, gv1, gs1);
+        gather_store(m, gv1, gs1);
       }
     }
     if (!last) {
-      if (w < R) gather_store(w, gv);
+      if (w < R) gather_store(w, gv, gs);
       if (stage_w0 == 0) stage_store(step + 1);
     }
     __syncthreads();  // the next step's A block and base slice are in LDS (and tok_s complete)
@@ -524,27 +677,29 @@ struct LoopPlan {
 constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straight from memory
 
 // markov_w2 tiles held in registers per wave (the largest counts that leave
-// no register spills; one wave per SIMD is built for r = 256 only).
-constexpr int reg_tiles(int NW, int KB) {
+// no register spills; one wave per SIMD is built for bf16 at r = 256 only).
+// A Q8_0 tile takes half the registers of a bf16 one, plus its scales.
+constexpr int reg_tiles(int NW, int KB, bool Q8, bool BL = true) {
+  if (Q8) return NW != 8 ? 0 : KB <= 2 ? 6 : KB == 4 ? 5 : KB == 8 ? (BL ? 3 : 2) : KB == 16 ? 1 : 0;
   return NW == 4 ? (KB == 8 ? 10 : 0) : KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
 }
 
 // Plan for G workgroups (G <= min(tiles, kMaxGroups)) of NW waves.
-LoopPlan make_loop_plan(int R, int V, int r, int k, int G, int NW) {
+LoopPlan make_loop_plan(int R, int V, int r, int k, int G, int NW, bool q8) {
   LoopPlan pl{};
   const int tiles = (V + 15) / 16;
   pl.G = G;
   pl.NW = NW;
   const int kb = (r + 31) / 32;
   pl.KB = kb <= 1 ? 1 : kb <= 2 ? 2 : kb <= 4 ? 4 : kb <= 8 ? 8 : kb <= 16 ? 16 : 32;
-  pl.RT = reg_tiles(NW, pl.KB);
   const int ntmax = (tiles + pl.G - 1) / pl.G;
   pl.bstride = ntmax * 16;
   const size_t base_bytes = static_cast<size_t>(R) * pl.bstride * 4;
   pl.base_in_lds = base_bytes <= kBaseLdsMax ? 1 : 0;
-  const size_t fixed = static_cast<size_t>(NW) * kMaxReqs * 8 + static_cast<size_t>(R + 1) * (pl.KB * 64 + 16) +
-                       kMaxReqs * 4 + static_cast<size_t>(k) * R * 4 + (pl.base_in_lds ? base_bytes : 0);
-  const size_t tile_bytes = static_cast<size_t>(pl.KB) * 1024;
+  pl.RT = reg_tiles(NW, pl.KB, q8, pl.base_in_lds != 0);
+  const size_t fixed = static_cast<size_t>(NW) * kMaxReqs * 8 + a_block_bytes(R, pl.KB, q8) + kMaxReqs * 4 +
+                       static_cast<size_t>(k) * R * 4 + (pl.base_in_lds ? base_bytes : 0);
+  const size_t tile_bytes = lds_tile_bytes(pl.KB, q8);
   const int want = std::max(0, ntmax - NW * pl.RT);
   const int fit = fixed < kLdsBytes ? static_cast<int>((kLdsBytes - fixed) / tile_bytes) : 0;
   pl.lds_tiles = std::min(want, fit);
@@ -553,12 +708,12 @@ LoopPlan make_loop_plan(int R, int V, int r, int k, int G, int NW) {
   return pl;
 }
 
-template <int NW, int KB, bool BL>
+template <int NW, int KB, bool BL, bool Q8>
 hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
-  constexpr int RT = reg_tiles(NW, KB);
+  constexpr int RT = reg_tiles(NW, KB, Q8, BL);
   constexpr int LT = KB >= 16 ? 1 : 2;
   constexpr int kLoopThreads = NW * kWave;
-  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<NW, KB, RT, LT, BL>);
+  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<NW, KB, RT, LT, BL, Q8>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
@@ -574,6 +729,78 @@ hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream
   return hipLaunchKernel(fn, dim3(pl.G), dim3(kLoopThreads), args, pl.lds, st);
 }
 
+template <bool Q8>
+hipError_t dispatch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
+  const bool bl = pl.base_in_lds != 0;
+  if constexpr (Q8) {
+    // Q8_0 weights: r <= 256 (at 512 and more the block scales of the A rows
+    // and the int8 products do not fit beside the tiles without spills)
+    switch (pl.KB) {
+      case 1: return bl ? launch_loop<8, 1, true, true>(prm, pl, cus, st) : launch_loop<8, 1, false, true>(prm, pl, cus, st);
+      case 2: return bl ? launch_loop<8, 2, true, true>(prm, pl, cus, st) : launch_loop<8, 2, false, true>(prm, pl, cus, st);
+      case 4: return bl ? launch_loop<8, 4, true, true>(prm, pl, cus, st) : launch_loop<8, 4, false, true>(prm, pl, cus, st);
+      case 8: return bl ? launch_loop<8, 8, true, true>(prm, pl, cus, st) : launch_loop<8, 8, false, true>(prm, pl, cus, st);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    if (pl.NW == 4)  // r = 256 only
+      return bl ? launch_loop<4, 8, true, false>(prm, pl, cus, st) : launch_loop<4, 8, false, false>(prm, pl, cus, st);
+    switch (pl.KB) {
+      case 1: return bl ? launch_loop<8, 1, true, false>(prm, pl, cus, st) : launch_loop<8, 1, false, false>(prm, pl, cus, st);
+      case 2: return bl ? launch_loop<8, 2, true, false>(prm, pl, cus, st) : launch_loop<8, 2, false, false>(prm, pl, cus, st);
+      case 4: return bl ? launch_loop<8, 4, true, false>(prm, pl, cus, st) : launch_loop<8, 4, false, false>(prm, pl, cus, st);
+      case 8: return bl ? launch_loop<8, 8, true, false>(prm, pl, cus, st) : launch_loop<8, 8, false, false>(prm, pl, cus, st);
+      case 16: return bl ? launch_loop<8, 16, true, false>(prm, pl, cus, st) : launch_loop<8, 16, false, false>(prm, pl, cus, st);
+      default: return bl ? launch_loop<8, 32, true, false>(prm, pl, cus, st) : launch_loop<8, 32, false, false>(prm, pl, cus, st);
+    }
+  }
+}
+
+// Shared by both weight formats: the grid, the plan and the parameters.
+hipError_t launch_markov_any(MarkovParams prm, bool q8, const ProbeArgs* probe, hipStream_t stream) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorNoDevice;
+  // Workgroups: one per CU, but at least ~16 tiles each. With fewer tiles a
+  // workgroup's step is all latency, and more workgroups only lengthen the
+  // exchange (measured: 32000 x 256 with 8 requests 74 -> 67 us per call at
+  // 128 instead of 256 workgroups; 4096 x 32 17 -> 14 us at 16).
+  const int R = prm.R, V = prm.V, r = prm.r, k = prm.k;
+  const int tiles = (V + 15) / 16;
+  const int G = std::max(1, std::min({cus, kMaxGroups, (tiles + 15) / 16}));
+  LoopPlan pl = make_loop_plan(R, V, r, k, G, kLoopWavesMax, q8);
+  if (!q8 && pl.streams && pl.KB == 8) {  // one wave per SIMD holds more of markov_w2 on chip
+    const LoopPlan p4 = make_loop_plan(R, V, r, k, G, 4, false);
+    if (p4.lds_tiles + 4 * p4.RT > pl.lds_tiles + kLoopWavesMax * pl.RT) pl = p4;
+  }
+  prm.G = pl.G;
+  prm.tiles = tiles;
+  prm.lds_tiles = pl.lds_tiles;
+  prm.bstride = pl.bstride;
+  prm.base_in_lds = pl.base_in_lds;
+  if (probe) {
+    prm.probe_on = 1;
+    prm.probe = *probe;
+  }
+  return q8 ? dispatch_loop<true>(prm, pl, cus, stream) : dispatch_loop<false>(prm, pl, cus, stream);
+}
+
+MarkovParams common_params(const float* base, int R, int B, int V, int r, const int64_t* d2t, const int64_t* prev0,
+                           int k, int64_t* ids, void* workspace) {
+  MarkovParams prm{};
+  prm.base = base;
+  prm.prev0 = prev0;
+  prm.d2t = d2t;
+  prm.ids = ids;
+  prm.ctl = static_cast<uint32_t*>(workspace);
+  prm.slots = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(workspace) + kCtlBytes);
+  prm.R = R;
+  prm.B = B;
+  prm.V = V;
+  prm.r = r;
+  prm.k = k;
+  return prm;
+}
+
 }  // namespace
 
 size_t markov_workspace_bytes(int num_reqs, int k, int V) {
@@ -585,64 +812,22 @@ hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t*
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
                          int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
                          hipStream_t stream) {
-  const int cus = device_cu_count();
-  if (cus <= 0) return hipErrorNoDevice;
-  // Workgroups: one per CU, but at least ~16 tiles each. With fewer tiles a
-  // workgroup's step is all latency, and more workgroups only lengthen the
-  // exchange (measured: 32000 x 256 with 8 requests 74 -> 67 us per call at
-  // 128 instead of 256 workgroups; 4096 x 32 17 -> 14 us at 16).
-  const int tiles = (V + 15) / 16;
-  const int G = std::max(1, std::min({cus, kMaxGroups, (tiles + 15) / 16}));
-  LoopPlan pl = make_loop_plan(R, V, r, k, G, kLoopWavesMax);
-  if (pl.streams && pl.KB == 8) {  // one wave per SIMD holds more of markov_w2 on chip
-    const LoopPlan p4 = make_loop_plan(R, V, r, k, G, 4);
-    if (p4.lds_tiles + 4 * p4.RT > pl.lds_tiles + kLoopWavesMax * pl.RT) pl = p4;
-  }
-  MarkovParams prm{};
-  prm.base = base;
+  MarkovParams prm = common_params(base, R, B, V, r, d2t, prev0, k, ids, workspace);
   prm.w1 = w1;
   prm.w2 = w2;
-  prm.prev0 = prev0;
-  prm.d2t = d2t;
-  prm.ids = ids;
-  prm.ctl = static_cast<uint32_t*>(workspace);
-  prm.slots = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(workspace) + kCtlBytes);
-  prm.R = R;
-  prm.B = B;
-  prm.V = V;
-  prm.r = r;
-  prm.k = k;
-  prm.G = pl.G;
-  prm.tiles = tiles;
-  prm.lds_tiles = pl.lds_tiles;
-  prm.bstride = pl.bstride;
-  prm.base_in_lds = pl.base_in_lds;
-  if (probe) {
-    prm.probe_on = 1;
-    prm.probe = *probe;
-  }
-  if (pl.NW == 4) {  // r = 256 only
-    return pl.base_in_lds ? launch_loop<4, 8, true>(prm, pl, cus, stream)
-                          : launch_loop<4, 8, false>(prm, pl, cus, stream);
-  }
-  if (pl.base_in_lds) {
-    switch (pl.KB) {
-      case 1: return launch_loop<8, 1, true>(prm, pl, cus, stream);
-      case 2: return launch_loop<8, 2, true>(prm, pl, cus, stream);
-      case 4: return launch_loop<8, 4, true>(prm, pl, cus, stream);
-      case 8: return launch_loop<8, 8, true>(prm, pl, cus, stream);
-      case 16: return launch_loop<8, 16, true>(prm, pl, cus, stream);
-      default: return launch_loop<8, 32, true>(prm, pl, cus, stream);
-    }
-  }
-  switch (pl.KB) {
-    case 1: return launch_loop<8, 1, false>(prm, pl, cus, stream);
-    case 2: return launch_loop<8, 2, false>(prm, pl, cus, stream);
-    case 4: return launch_loop<8, 4, false>(prm, pl, cus, stream);
-    case 8: return launch_loop<8, 8, false>(prm, pl, cus, stream);
-    case 16: return launch_loop<8, 16, false>(prm, pl, cus, stream);
-    default: return launch_loop<8, 32, false>(prm, pl, cus, stream);
-  }
+  return launch_markov_any(prm, false, probe, stream);
+}
+
+hipError_t launch_markov_q8(const float* base, int R, int B, int V, const int8_t* w1q, const uint16_t* w1d,
+                            const int8_t* w2q, const uint16_t* w2d, int r, const int64_t* d2t,
+                            const int64_t* prev0, int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
+                            hipStream_t stream) {
+  MarkovParams prm = common_params(base, R, B, V, r, d2t, prev0, k, ids, workspace);
+  prm.w1q = w1q;
+  prm.w1d = w1d;
+  prm.w2q = w2q;
+  prm.w2d = w2d;
+  return launch_markov_any(prm, true, probe, stream);
 }
 
 }  // namespace dspark

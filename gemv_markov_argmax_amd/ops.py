@@ -26,6 +26,10 @@ SIGNATURES = {
     "dspark_lm_head": (_i, [_p, _i, _i, _p, _i, _p, _p]),
     "dspark_proj_smallm_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
+    "dspark_markov_sample_q8": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
+                                     _p, _i, _i, _p, _f, _f, _p, _p, _p]),
+    "dspark_draft_round_q8": (_i, [_p, _p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _f, _f,
+                                   _p, _p, _p, _p, _p, _sz, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -324,6 +328,114 @@ def draft_round(W_lm: torch.Tensor, H: torch.Tensor, w1: torch.Tensor, w2: torch
                                     d2t_ptr, prev0.data_ptr(), k, pw_ptr, float(probe_bias), float(probe_threshold),
                                     base_out.data_ptr(), ids_ptr, lo_ptr, pa_ptr, workspace.data_ptr(),
                                     workspace.numel(), _stream(H)))
+    return dict(base=base_out, ids=ids_out, logit=logit_out, passed=pass_out)
+
+
+def _q8_pair(q, d, V, r, name):
+    _dev(q, torch.int8, name + "q", 2)
+    _dev(d, torch.float16, name + "d", 2)
+    if tuple(q.shape) != (V, r) or tuple(d.shape) != (V, r // 32):
+        raise ValueError(f"{name}: quants [V, r] and scales [V, r / 32] required")
+
+
+def markov_sample_q8(base: torch.Tensor, w1q: torch.Tensor, w1d: torch.Tensor, w2q: torch.Tensor,
+                     w2d: torch.Tensor, prev0: torch.Tensor, k: int, d2t: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     probe: dict | None = None) -> torch.Tensor:
+    """Drafted ids [R, k] of the Markov loop over Q8_0 markov weights
+    (dspark_markov_sample_q8): w1q, w2q int8 [V, r]; w1d, w2d float16
+    [V, r / 32]. ``probe`` as in markov_sample (same launch)."""
+    _dev(base, torch.float32, "base", 3)
+    _dev(prev0, torch.int64, "prev0", 1)
+    R, B, V = base.shape
+    r = w1q.shape[1]
+    _q8_pair(w1q, w1d, V, r, "w1")
+    _q8_pair(w2q, w2d, V, r, "w2")
+    if prev0.shape[0] != R:
+        raise ValueError("prev0 must have num_reqs entries")
+    d2t_ptr = None
+    if d2t is not None:
+        _dev(d2t, torch.int64, "d2t", 1)
+        if d2t.shape[0] != V:
+            raise ValueError("d2t must have V entries")
+        d2t_ptr = d2t.data_ptr()
+    if out is None:
+        out = torch.empty((R, k), dtype=torch.int64, device=base.device)
+    if tuple(out.shape) != (R, k):
+        raise ValueError("out must be [num_reqs, k]")
+    out_ptr = _out_ptr(out, torch.int64, "out", 2)
+    if workspace is None:
+        workspace = markov_workspace(R, k, V, base.device)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    px = pw = lo_ptr = pa_ptr = None
+    pm = pd = 0
+    bias = thr = 0.0
+    if probe is not None:
+        x, w = probe["x"], probe["w"]
+        lo, pa, lo_ptr, pa_ptr = _probe_outputs(x, w, probe.get("logit_out"), probe.get("pass_out"),
+                                                probe.get("want_pass", True))
+        probe["logit_out"], probe["pass_out"] = lo, pa
+        px, pw, pm, pd = x.data_ptr(), w.data_ptr(), x.shape[0], x.shape[1]
+        bias, thr = float(probe.get("bias", 0.0)), float(probe.get("threshold", 0.0))
+    _check(lib().dspark_markov_sample_q8(base.data_ptr(), R, B, V, w1q.data_ptr(), w1d.data_ptr(), w2q.data_ptr(),
+                                         w2d.data_ptr(), r, d2t_ptr, prev0.data_ptr(), k, out_ptr,
+                                         workspace.data_ptr(), workspace.numel(), px, pm, pd, pw, bias, thr,
+                                         lo_ptr, pa_ptr, _stream(base)))
+    return out
+
+
+def draft_round_q8(Wq: torch.Tensor, Wd: torch.Tensor, H: torch.Tensor, w1q: torch.Tensor, w1d: torch.Tensor,
+                   w2q: torch.Tensor, w2d: torch.Tensor, prev0: torch.Tensor, B: int, k: int,
+                   probe_w: torch.Tensor | None = None, probe_bias: float = 0.0, probe_threshold: float = 0.0,
+                   d2t: torch.Tensor | None = None, base_out: torch.Tensor | None = None,
+                   ids_out: torch.Tensor | None = None, logit_out: torch.Tensor | None = None,
+                   pass_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   want_pass: bool = True) -> dict:
+    """One draft round over Q8_0 weights (dspark_draft_round_q8); returns the
+    dict of draft_round."""
+    _dev(Wq, torch.int8, "Wq", 2)
+    _dev(Wd, torch.float16, "Wd", 2)
+    _dev(H, torch.float32, "H", 2)
+    _dev(prev0, torch.int64, "prev0", 1)
+    V, d = Wq.shape
+    R = prev0.shape[0]
+    r = w1q.shape[1]
+    if tuple(Wd.shape) != (V, d // 32) or tuple(H.shape) != (R * B, d):
+        raise ValueError("Wq [V, d], Wd [V, d / 32] and H [num_reqs * B, d] required")
+    _q8_pair(w1q, w1d, V, r, "w1")
+    _q8_pair(w2q, w2d, V, r, "w2")
+    dev = H.device
+    d2t_ptr = None
+    if d2t is not None:
+        _dev(d2t, torch.int64, "d2t", 1)
+        if d2t.shape[0] != V:
+            raise ValueError("d2t must have V entries")
+        d2t_ptr = d2t.data_ptr()
+    if base_out is None:
+        base_out = torch.empty((R, B, V), dtype=torch.float32, device=dev)
+    _dev(base_out, torch.float32, "base_out", 3)
+    if tuple(base_out.shape) != (R, B, V):
+        raise ValueError("base_out must be [num_reqs, B, V]")
+    if ids_out is None:
+        ids_out = torch.empty((R, k), dtype=torch.int64, device=dev)
+    if tuple(ids_out.shape) != (R, k):
+        raise ValueError("ids_out must be [num_reqs, k]")
+    ids_ptr = _out_ptr(ids_out, torch.int64, "ids_out", 2)
+    pw_ptr = lo_ptr = pa_ptr = None
+    if probe_w is not None:
+        if probe_w.shape[0] != d:
+            raise ValueError("probe_w must have d entries")
+        logit_out, pass_out, lo_ptr, pa_ptr = _probe_outputs(H, probe_w, logit_out, pass_out, want_pass)
+        pw_ptr = probe_w.data_ptr()
+    else:
+        logit_out = pass_out = None
+    if workspace is None:
+        workspace = markov_workspace(R, k, V, dev)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    _check(lib().dspark_draft_round_q8(Wq.data_ptr(), Wd.data_ptr(), V, d, H.data_ptr(), R, B, w1q.data_ptr(),
+                                       w1d.data_ptr(), w2q.data_ptr(), w2d.data_ptr(), r, d2t_ptr, prev0.data_ptr(),
+                                       k, pw_ptr, float(probe_bias), float(probe_threshold), base_out.data_ptr(),
+                                       ids_ptr, lo_ptr, pa_ptr, workspace.data_ptr(), workspace.numel(), _stream(H)))
     return dict(base=base_out, ids=ids_out, logit=logit_out, passed=pass_out)
 
 

@@ -19,6 +19,8 @@ models, prompts or weights exist here):
 * ``draft_layer`` -- one draft transformer layer's projections at M = 7
   (SharpInference #441, "Hypothesis") plus a 7424-wide confidence probe
   (ds4 #772, "Summary").
+* ``qwen3_8b_head_q8``, ``lane27b_q8`` -- the two single-request heads with
+  the lm_head and markov weights in Q8_0 (ds4 #772, "Summary").
 
 Every tensor is drawn from its own PCG64 stream, keyed by (seed, stream id,
 block index), so a value never depends on how many threads fill the array.
@@ -46,6 +48,10 @@ CONFIGS = {
     "lane27b": dict(num_reqs=1, B=15, k=15, d=5120, V=248320, r=256, tie_frac=0.05),
     "reduced_vocab_batched": dict(num_reqs=8, B=9, k=9, d=5120, V=32000, r=256),
     "draft_layer": dict(M=7, d=4096, ffn=12288, probe_width=7424),
+    # The two R = 1 heads with Q8_0 lm_head and markov weights (ds4 #772,
+    # "Summary": the GPU path takes Q8_0 markov weights).
+    "qwen3_8b_head_q8": dict(num_reqs=1, B=7, k=7, d=4096, V=151936, r=256, weights="q8_0"),
+    "lane27b_q8": dict(num_reqs=1, B=15, k=15, d=5120, V=248320, r=256, weights="q8_0"),
 }
 CONFIG_SEED_INDEX = {name: i + 1 for i, name in enumerate(CONFIGS)}
 
@@ -248,10 +254,15 @@ def round_inputs(name: str, seed: int | None = None, with_base: bool = False):
     seed = config_seed(name) if seed is None else seed
     R, B, d, V, r = cfg["num_reqs"], cfg["B"], cfg["d"], cfg["V"], cfg["r"]
     out = dict(cfg, seed=seed, name=name)
-    out["W_lm"] = normal_bf16(seed, S_W_LM, (V, d))
+    if cfg.get("weights") == "q8_0":  # lm_head and markov weights as Q8_0 (q int8, d binary16 bits)
+        out["Wq_lm"], out["Wd_lm"] = normal_q8(seed, S_W_LM, (V, d))
+        out["w1q"], out["w1d"] = normal_q8(seed, S_W1, (V, r))
+        out["w2q"], out["w2d"] = normal_q8(seed, S_W2, (V, r))
+    else:
+        out["W_lm"] = normal_bf16(seed, S_W_LM, (V, d))
+        out["w1"] = normal_bf16(seed, S_W1, (V, r))
+        out["w2"] = normal_bf16(seed, S_W2, (V, r))
     out["H"] = normal_f32(seed, S_H, (R * B, d))
-    out["w1"] = normal_bf16(seed, S_W1, (V, r))
-    out["w2"] = normal_bf16(seed, S_W2, (V, r))
     out["prev0"] = uniform_index(seed, S_PREV0, R, V)
     out["probe_w"] = normal_bf16(seed, S_PROBE_W, (d,))
     out["probe_bias"] = np.float32(0.0)

@@ -10,7 +10,8 @@
  *   3. the confidence probe,
  * each as its own entry point, the loop and probe in one launch
  * (dspark_markov_sample_probe), and the lm_head, loop and probe together as
- * one round (dspark_draft_round).
+ * one round (dspark_draft_round); and the same over Q8_0 weights (the *_q8
+ * entry points).
  *
  * Sources cited below (a reader has the pages themselves):
  *   [DS772]  ds4 #772, "dspark: cut per-cycle CUDA overheads (single-draft
@@ -277,6 +278,48 @@ dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float
                                  float* base_out, int64_t* ids_out, float* logit_out,
                                  int32_t* pass_out, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * dspark_markov_sample_q8 -- the Markov loop over Q8_0 markov weights, with
+ * the confidence probe optionally in the same launch.
+ *
+ * [DS772] "Summary": the GPU path takes Q8_0 markov weights. Both markov_w1
+ * and markov_w2 are Q8_0 with blocks along the rank: entry j of row v is
+ * d[v, j / 32] * q[v, j] (IEEE binary16 scale, signed 8-bit quant). The loop
+ * is that of dspark_markov_sample ([W7] "The fix") on these exact values:
+ * each block's dot product is exact in integers (int8 matrix cores), then
+ * scaled by the two block scales and added in fp32.
+ *
+ *   w1q, w2q  int8     [V, r]       16-byte aligned
+ *   w1d, w2d  binary16 [V, r / 32]   2-byte aligned
+ *   probe_x   NULL (no probe) or the probe's x as in dspark_conf_probe, with
+ *             probe_M, probe_D, probe_w, probe_bias, probe_threshold,
+ *             logit_out, pass_out (results bit-identical to that call)
+ * Every other argument, the workspace rules and the errors are those of
+ * dspark_markov_sample. Sizes: 32 <= r <= 256 with r % 32 == 0 (the register
+ * and LDS budget of the int8 path); other limits as dspark_markov_sample.
+ */
+dspark_status dspark_markov_sample_q8(const float* base, int num_reqs, int B, int V, const int8_t* w1q,
+                                      const uint16_t* w1d, const int8_t* w2q, const uint16_t* w2d, int r,
+                                      const int64_t* d2t, const int64_t* prev0, int k, int64_t* ids_out,
+                                      void* workspace, size_t workspace_bytes, const float* probe_x,
+                                      int probe_M, int probe_D, const uint16_t* probe_w, float probe_bias,
+                                      float probe_threshold, float* logit_out, int32_t* pass_out,
+                                      void* stream);
+
+/*
+ * dspark_draft_round_q8 -- dspark_draft_round with a Q8_0 lm_head and Q8_0
+ * markov weights: dspark_lm_head_q8, then dspark_markov_sample_q8 with the
+ * probe (bf16 weights, optional as in dspark_draft_round) in the same
+ * launch. Arguments, sizes and errors are those of the calls it composes.
+ */
+dspark_status dspark_draft_round_q8(const int8_t* Wq_lm, const uint16_t* Wd_lm, int V, int d, const float* H,
+                                    int num_reqs, int B, const int8_t* w1q, const uint16_t* w1d,
+                                    const int8_t* w2q, const uint16_t* w2d, int r, const int64_t* d2t,
+                                    const int64_t* prev0, int k, const uint16_t* probe_w, float probe_bias,
+                                    float probe_threshold, float* base_out, int64_t* ids_out,
+                                    float* logit_out, int32_t* pass_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -281,3 +281,15 @@ def draft_round(W_lm_bits, H, w1_bits, w2_bits, prev0, num_reqs: int, B: int, k:
     mk = markov_sample(base32, w1_bits, w2_bits, prev0, k, d2t)
     logit, passed = conf_probe(H, probe_w_bits, probe_bias, probe_threshold)
     return dict(base=base64, base32=base32, logit=logit, passed=passed, **mk)
+
+
+def draft_round_q8(Wq_lm, Wd_lm_bits, H, w1q, w1d_bits, w2q, w2d_bits, prev0, num_reqs: int, B: int, k: int,
+                   probe_w_bits, probe_bias: float, probe_threshold: float, d2t=None) -> dict:
+    """draft_round with a Q8_0 lm_head and Q8_0 markov weights ([DS772]
+    "Summary"); the probe weights stay bf16."""
+    base64 = gemv_q8(Wq_lm, Wd_lm_bits, H)
+    V = base64.shape[1]
+    base32 = base64.astype(np.float32).reshape(num_reqs, B, V)
+    mk = markov_sample_q8(base32, w1q, w1d_bits, w2q, w2d_bits, prev0, k, d2t)
+    logit, passed = conf_probe(H, probe_w_bits, probe_bias, probe_threshold)
+    return dict(base=base64, base32=base32, logit=logit, passed=passed, **mk)

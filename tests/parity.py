@@ -59,14 +59,17 @@ def probe_close(gpu_logit, gpu_pass, ref_logit, ref_pass, threshold):
 
 def check_markov(gpu_ids, base, w1, w2, prev0, k, d2t=None, report=None):
     """Compare drafted ids with the oracle; return the list of near-tie
-    records (request, step, gpu tok, oracle tok, runner-up, margin)."""
+    records (request, step, gpu tok, oracle tok, runner-up, margin).
+    w1, w2: bf16 bits, or float64 values (e.g. oracle.q8_0_to_f64 of Q8_0
+    weights)."""
     gpu_ids = np.asarray(gpu_ids)
     R = base.shape[0]
     V = base.shape[2]
     inv = None
     if d2t is not None:
         inv = {int(t): v for v, t in enumerate(np.asarray(d2t))}
-    W2 = oracle.bf16_to_f64(w2)
+    # (weights as bf16 bits, or already decoded float64 values of any format)
+    W2 = w2 if (isinstance(w2, np.ndarray) and w2.dtype == np.float64) else oracle.bf16_to_f64(w2)
     near = []
     for q in range(R):
         p0 = int(prev0[q])

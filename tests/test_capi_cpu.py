@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared()
     for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
               "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
+              "dspark_markov_sample_q8", "dspark_draft_round_q8",
               "dspark_markov_workspace_bytes",
               "dspark_status_string"]:
         assert n in names
@@ -152,6 +153,51 @@ def test_markov_sample_probe_errors(L):
     assert call(x=MIS) == ERR_ALIGN
     assert call(ps=A + 2) == ERR_ALIGN
     assert call(wsb=ws - 1) == ERR_WORKSPACE
+
+
+def test_markov_q8_errors(L):
+    f = L.dspark_markov_sample_q8
+    ws = L.dspark_markov_workspace_bytes(1, 7, 151936)
+    good = dict(base=A, R=1, B=7, V=151936, w1q=A, w1d=A2, w2q=A2, w2d=A, r=256, d2t=None, prev0=A, k=7, ids=A2,
+                ws=A, wsb=ws, px=None, pm=0, pd=0, pw=None, lo=None, ps=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["base"], a["R"], a["B"], a["V"], a["w1q"], a["w1d"], a["w2q"], a["w2d"], a["r"], a["d2t"],
+                 a["prev0"], a["k"], a["ids"], a["ws"], a["wsb"], a["px"], a["pm"], a["pd"], a["pw"], 0.0, 0.0,
+                 a["lo"], a["ps"], None)
+    assert call(w1q=None) == ERR_NULL
+    assert call(w2d=None) == ERR_NULL
+    assert call(px=A, pm=7, pd=64, pw=None, lo=A2) == ERR_NULL   # a probe needs its weights
+    assert call(r=48) == ERR_SHAPE                                # r % 32 != 0
+    assert call(r=512) == ERR_SHAPE                               # r > 256
+    assert call(r=16) == ERR_SHAPE
+    assert call(k=8) == ERR_SHAPE
+    assert call(R=17) == ERR_SHAPE
+    assert call(px=A, pm=7, pd=60, pw=A, lo=A2) == ERR_SHAPE      # probe D % 8 != 0
+    assert call(w1q=A + 8) == ERR_ALIGN
+    assert call(w2d=A + 1) == ERR_ALIGN
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+
+
+def test_draft_round_q8_errors(L):
+    f = L.dspark_draft_round_q8
+    ws = L.dspark_markov_workspace_bytes(1, 7, 151936)
+    good = dict(Wq=A, Wd=A2, V=151936, d=4096, H=A2, R=1, B=7, w1q=A, w1d=A2, w2q=A2, w2d=A, r=256, d2t=None,
+                prev0=A, k=7, pw=A, base=A2, ids=A, lo=A2, ps=None, ws=A, wsb=ws)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["Wq"], a["Wd"], a["V"], a["d"], a["H"], a["R"], a["B"], a["w1q"], a["w1d"], a["w2q"], a["w2d"],
+                 a["r"], a["d2t"], a["prev0"], a["k"], a["pw"], 0.0, 0.0, a["base"], a["ids"], a["lo"], a["ps"],
+                 a["ws"], a["wsb"], None)
+    assert call(Wq=None) == ERR_NULL
+    assert call(lo=None) == ERR_NULL
+    assert call(d=4100) == ERR_SHAPE      # d % 32 != 0
+    assert call(r=1024) == ERR_SHAPE
+    assert call(R=0) == ERR_SHAPE
+    assert call(Wd=A + 1) == ERR_ALIGN
+    assert call(ws=None) == ERR_WORKSPACE
 
 
 def test_draft_round_errors(L):

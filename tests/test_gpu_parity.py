@@ -555,6 +555,157 @@ def test_draft_round_graph_replay(dev):
         torch.cuda.synchronize()
 
 
+# ---------------------------------------------------------------------------
+# The Markov loop and the round over Q8_0 weights
+# ---------------------------------------------------------------------------
+
+def _q8(q, d, dev):
+    return _ops().q8_from_numpy(q, d, dev)
+
+
+MARKOV_Q8_CASES = [
+    # (R, B, k, V, r): one block; one workgroup with 3 blocks of a 4-block
+    # k-loop; 16 requests over 3 workgroups; the batched lane; the
+    # Qwen3-8B head at full size
+    (1, 4, 4, 4096, 32), (3, 5, 5, 3000, 64), (2, 3, 3, 200, 96), (16, 2, 2, 600, 128),
+    (8, 9, 9, 32000, 256), (1, 7, 7, 151936, 256),
+]
+
+
+@pytest.mark.parametrize("R,B,k,V,r", MARKOV_Q8_CASES)
+def test_markov_q8_matches_oracle(dev, R, B, k, V, r):
+    seed = 8100 + R * 7 + V + r
+    say(f"[markov q8] R={R} B={B} k={k} V={V} r={r} seed={seed}")
+    base, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, B, V, r, seed)
+    ids = _ops().markov_sample_q8(_up(base, dev), *_q8(w1q, w1d, dev), *_q8(w2q, w2d, dev), _up(prev0, dev), k)
+    ids2 = _ops().markov_sample_q8(_up(base, dev), *_q8(w1q, w1d, dev), *_q8(w2q, w2d, dev), _up(prev0, dev), k)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2), "rerun differs"
+    check_markov(ids.cpu().numpy(), base, oracle.q8_0_to_f64(w1q, w1d), oracle.q8_0_to_f64(w2q, w2d), prev0, k)
+
+
+@pytest.mark.parametrize("R,B", [(1, 15), (9, 6)])
+def test_markov_q8_lane27b_size(dev, R, B):
+    """The 27B lane's draft vocabulary (248320 x 256): in Q8_0 every
+    markov_w2 tile of a workgroup fits on chip."""
+    V, r, k = 248320, 256, B
+    seed = 8200 + R
+    say(f"[markov q8 lane27b] R={R} B={B} V={V} seed={seed}")
+    base, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, B, V, r, seed)
+    ids = _ops().markov_sample_q8(_up(base, dev), *_q8(w1q, w1d, dev), *_q8(w2q, w2d, dev), _up(prev0, dev), k)
+    torch.cuda.synchronize()
+    check_markov(ids.cpu().numpy(), base, oracle.q8_0_to_f64(w1q, w1d), oracle.q8_0_to_f64(w2q, w2d), prev0, k)
+
+
+def test_markov_q8_constructed_ties(dev):
+    """Exact ties in Q8_0: tie rows' pair (a, b) share the top base value and
+    markov_w2 row b is a copy of row a (quants and scales): index a wins."""
+    R, B, V, r = 2, 6, 5000, 64
+    say(f"[markov q8 ties] R={R} V={V} r={r}")
+    base, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, B, V, r, 93)
+    g = np.random.default_rng(5)
+    ties = []
+    for q in range(R):
+        for i in range(B):
+            a, b = sorted(int(x) for x in g.choice(V, 2, replace=False))
+            base[q, i, a] = base[q, i, b] = synth.TIE_VALUE
+            w2q[b], w2d[b] = w2q[a], w2d[a]
+            ties.append((q, i, a))
+    ids = _ops().markov_sample_q8(_up(base, dev), *_q8(w1q, w1d, dev), *_q8(w2q, w2d, dev), _up(prev0, dev), B)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    for q, i, a in ties:
+        assert ids[q, i] == a, f"request {q} step {i}: {ids[q, i]} instead of {a}"
+
+
+def test_markov_q8_and_bf16_share_a_workspace(dev):
+    """bf16 and Q8_0 calls alternate on one workspace (the key slots and the
+    call counter are shared): each equals its result on a fresh workspace."""
+    R, B, k, V, r = 3, 5, 5, 3000, 64
+    say("[markov q8/bf16 shared workspace]")
+    base, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, B, V, r, 97)
+    _, w1, w2, _, _ = synth.markov_inputs(R, B, V, r, 97)
+    bq = (_up(base, dev), *_q8(w1q, w1d, dev), *_q8(w2q, w2d, dev), _up(prev0, dev), k)
+    bb = (_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k)
+    ref_q = _ops().markov_sample_q8(*bq).clone()
+    ref_b = _ops().markov_sample(*bb).clone()
+    ws = _ops().markov_workspace(R, k, V, dev)
+    for _ in range(3):
+        a = _ops().markov_sample_q8(*bq, workspace=ws)
+        b = _ops().markov_sample(*bb, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, ref_q) and torch.equal(b, ref_b)
+
+
+def test_markov_q8_fused_probe(dev):
+    R, B, k, V, r = 1, 7, 7, 151936, 256
+    say("[markov q8 + probe] qwen3_8b_head shape, probe 7 x 4096")
+    base, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, B, V, r, 99)
+    x, pw = synth.probe_inputs(7, 4096, 99)
+    probe = dict(x=_up(x, dev), w=_bf(pw, dev), bias=0.25, threshold=0.0)
+    args = (_up(base, dev), *_q8(w1q, w1d, dev), *_q8(w2q, w2d, dev), _up(prev0, dev), k)
+    ids = _ops().markov_sample_q8(*args, probe=probe)
+    ids2 = _ops().markov_sample_q8(*args)
+    lg, ps = _ops().conf_probe(probe["x"], probe["w"], 0.25, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    assert torch.equal(probe["logit_out"], lg) and torch.equal(probe["pass_out"], ps)
+
+
+def _round_q8_tensors(inp, dev):
+    return dict(Wq=_q8(inp["Wq_lm"], inp["Wd_lm"], dev), w1=_q8(inp["w1q"], inp["w1d"], dev),
+                w2=_q8(inp["w2q"], inp["w2d"], dev), H=_up(inp["H"], dev), prev0=_up(inp["prev0"], dev),
+                pw=_bf(inp["probe_w"], dev))
+
+
+def test_draft_round_q8_small(dev):
+    """A small Q8_0 round against the oracle and against the separate calls."""
+    R, B, k, V, d, r = 2, 4, 3, 3000, 256, 64
+    seed = 8300
+    say(f"[draft_round q8 small] R={R} B={B} k={k} V={V} d={d} r={r}")
+    Wq, Wd, H = synth.gemv_q8_inputs(R * B, V, d, seed)
+    _, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, 1, V, r, seed)
+    _, pw = synth.probe_inputs(1, d, seed)
+    inp = dict(Wq_lm=Wq, Wd_lm=Wd, H=H, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d, prev0=prev0, probe_w=pw)
+    t = _round_q8_tensors(inp, dev)
+    out = _ops().draft_round_q8(*t["Wq"], t["H"], *t["w1"], *t["w2"], t["prev0"], B, k, probe_w=t["pw"],
+                                probe_threshold=0.01)
+    base = _ops().lm_head_q8(*t["Wq"], t["H"])
+    ids = _ops().markov_sample_q8(base.view(R, B, V), *t["w1"], *t["w2"], t["prev0"], k)
+    lg, ps = _ops().conf_probe(t["H"], t["pw"], 0.0, 0.01)
+    torch.cuda.synchronize()
+    assert torch.equal(out["base"].view(R * B, V), base) and torch.equal(out["ids"], ids)
+    assert torch.equal(out["logit"], lg) and torch.equal(out["passed"], ps)
+    ref = oracle.draft_round_q8(Wq, Wd, H, w1q, w1d, w2q, w2d, prev0, R, B, k, pw, 0.0, 0.01)
+    logits_close(base.cpu().numpy(), ref["base"], "draft_round_q8 logits")
+    check_markov(out["ids"].cpu().numpy(), ref["base32"], oracle.q8_0_to_f64(w1q, w1d),
+                 oracle.q8_0_to_f64(w2q, w2d), prev0, k)
+    probe_close(lg.cpu().numpy(), ps.cpu().numpy(), ref["logit"], ref["passed"], 0.01)
+
+
+def test_draft_round_q8_full_size(dev):
+    """The Qwen3-8B head in Q8_0 at full size: the fused round equals the
+    separate calls bit for bit; the loop is checked against the oracle on the
+    GPU's own base logits, the base logits on sampled rows."""
+    inp = synth.round_inputs("qwen3_8b_head_q8")
+    R, B, k, V = inp["num_reqs"], inp["B"], inp["k"], inp["V"]
+    say(f"[draft_round q8 full] qwen3_8b_head_q8 seed={inp['seed']}")
+    t = _round_q8_tensors(inp, dev)
+    out = _ops().draft_round_q8(*t["Wq"], t["H"], *t["w1"], *t["w2"], t["prev0"], B, k, probe_w=t["pw"])
+    base = _ops().lm_head_q8(*t["Wq"], t["H"])
+    ids = _ops().markov_sample_q8(base.view(R, B, V), *t["w1"], *t["w2"], t["prev0"], k)
+    torch.cuda.synchronize()
+    assert torch.equal(out["base"].view(R * B, V), base) and torch.equal(out["ids"], ids)
+    b = base.cpu().numpy()
+    pick = np.unique(np.concatenate([np.arange(16), np.arange(V - 16, V),
+                                     np.random.default_rng(2).choice(V, 1500, replace=False)]))
+    logits_close(b[:, pick], oracle.gemv_q8_rows(inp["Wq_lm"], inp["Wd_lm"], inp["H"], pick), "q8 round logits")
+    check_markov(out["ids"].cpu().numpy(), b.reshape(R, B, V), oracle.q8_0_to_f64(inp["w1q"], inp["w1d"]),
+                 oracle.q8_0_to_f64(inp["w2q"], inp["w2d"]), inp["prev0"], k)
+    ref_l, ref_p = oracle.conf_probe(inp["H"], inp["probe_w"], 0.0, 0.0)
+    probe_close(out["logit"].cpu().numpy(), out["passed"].cpu().numpy(), ref_l, ref_p, 0.0)
+
+
 def test_round_graph_replay(dev):
     """The whole round recorded once in a HIP graph and replayed, with eager
     work between replays: every replay equals the eager result."""
