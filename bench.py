@@ -34,6 +34,7 @@ def log(*a):
 
 COUNTERS = os.path.join(ROOT, "profiles", "counters_lm_head_{workload}.json")
 GEMV_SRC = os.path.join(ROOT, "gemv_markov_argmax_amd", "csrc", "gemv.hip")
+GEMV_Q8_SRC = os.path.join(ROOT, "gemv_markov_argmax_amd", "csrc", "gemv_q8.hip")
 
 
 def measured_traffic(workload):
@@ -46,7 +47,7 @@ def measured_traffic(workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(GEMV_SRC, "rb") as f:
+    with open(GEMV_Q8_SRC if workload.endswith("_q8") else GEMV_SRC, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     if rec.get("gemv_source_sha256") != sha:
         return None
@@ -54,11 +55,14 @@ def measured_traffic(workload):
 
 
 def round_bytes(cfg):
-    """Algorithmic HBM bytes of one round (each weight once per use; W2 once per step)."""
+    """Algorithmic HBM bytes of one round (each weight once per use; W2 once
+    per step). A bf16 weight is 2 bytes, a Q8_0 one 34/32 (a binary16 scale
+    per 32 int8 quants)."""
     R, B, k, d, V, r = cfg["num_reqs"], cfg["B"], cfg["k"], cfg["d"], cfg["V"], cfg["r"]
+    wb = 34 / 32 if cfg.get("weights") == "q8_0" else 2
     rows = R * B
-    lm = V * d * 2 + rows * d * 4 + rows * V * 4
-    mk = k * (V * r * 2 + R * r * 2 + R * V * 4) + R * k * 8 + R * 8
+    lm = int(V * d * wb) + rows * d * 4 + rows * V * 4
+    mk = int(k * (V * r * wb + R * r * wb) + k * R * V * 4) + R * k * 8 + R * 8
     pr = rows * d * 4 + d * 2 + rows * 8
     return lm, mk, pr
 
@@ -84,12 +88,19 @@ def cpu_baseline(inp, seconds):
     slices = max(1, V // 16384)
     rows = np.arange(V // slices)
     base = synth.normal_f32(inp["seed"], synth.S_BASE, (R, B, V), 1.28)
+    q8 = inp.get("weights") == "q8_0"
     t_lm, t_mk, t_pr, n = 0.0, 0.0, 0.0, 0
     while True:
         a = time.perf_counter()
-        oracle.gemv_rows(inp["W_lm"], inp["H"], rows)
+        if q8:
+            oracle.gemv_q8_rows(inp["Wq_lm"], inp["Wd_lm"], inp["H"], rows)
+        else:
+            oracle.gemv_rows(inp["W_lm"], inp["H"], rows)
         b = time.perf_counter()
-        oracle.markov_sample(base, inp["w1"], inp["w2"], inp["prev0"], k)
+        if q8:
+            oracle.markov_sample_q8(base, inp["w1q"], inp["w1d"], inp["w2q"], inp["w2d"], inp["prev0"], k)
+        else:
+            oracle.markov_sample(base, inp["w1"], inp["w2"], inp["prev0"], k)
         c = time.perf_counter()
         oracle.conf_probe(inp["H"], inp["probe_w"], float(inp["probe_bias"]), float(inp["probe_threshold"]))
         d = time.perf_counter()
@@ -224,7 +235,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="qwen3_8b_head",
-                    choices=["tiny", "qwen3_8b_head", "lane27b", "reduced_vocab_batched", "draft_layer"])
+                    choices=["tiny", "qwen3_8b_head", "lane27b", "reduced_vocab_batched", "draft_layer",
+                             "qwen3_8b_head_q8", "lane27b_q8"])
     ap.add_argument("--layer-copies", type=int, default=4,
                     help="draft_layer: distinct weight copies cycled through (defeats the 256 MB Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
@@ -262,10 +274,16 @@ def main():
     R, B, k, d, V, r = (inp[x] for x in ("num_reqs", "B", "k", "d", "V", "r"))
     rows = R * B
 
-    W = ops.bf16_from_bits(inp["W_lm"], dev)
+    q8 = inp.get("weights") == "q8_0"
+    if q8:  # Q8_0 lm_head and markov weights: (quants, scales) pairs
+        W = ops.q8_from_numpy(inp["Wq_lm"], inp["Wd_lm"], dev)
+        w1 = ops.q8_from_numpy(inp["w1q"], inp["w1d"], dev)
+        w2 = ops.q8_from_numpy(inp["w2q"], inp["w2d"], dev)
+    else:
+        W = ops.bf16_from_bits(inp["W_lm"], dev)
+        w1 = ops.bf16_from_bits(inp["w1"], dev)
+        w2 = ops.bf16_from_bits(inp["w2"], dev)
     H = torch.from_numpy(inp["H"]).to(dev)
-    w1 = ops.bf16_from_bits(inp["w1"], dev)
-    w2 = ops.bf16_from_bits(inp["w2"], dev)
     prev0 = torch.from_numpy(inp["prev0"]).to(dev)
     pw = ops.bf16_from_bits(inp["probe_w"], dev)
     logits = torch.empty(rows, V, device=dev)
@@ -281,15 +299,24 @@ def main():
     torch.cuda.synchronize()
 
     def lm():
-        ops.lm_head(W, H, out=logits)
+        if q8:
+            ops.lm_head_q8(*W, H, out=logits)
+        else:
+            ops.lm_head(W, H, out=logits)
 
     probe = dict(x=H, w=pw, bias=bias, threshold=thr, logit_out=plog, pass_out=ppass)
 
     def mk():  # the Markov loop with the probe in the same launch
-        ops.markov_sample(logits.view(R, B, V), w1, w2, prev0, k, out=ids, workspace=ws, probe=probe)
+        if q8:
+            ops.markov_sample_q8(logits.view(R, B, V), *w1, *w2, prev0, k, out=ids, workspace=ws, probe=probe)
+        else:
+            ops.markov_sample(logits.view(R, B, V), w1, w2, prev0, k, out=ids, workspace=ws, probe=probe)
 
     def mk_alone():
-        ops.markov_sample(logits.view(R, B, V), w1, w2, prev0, k, out=ids, workspace=ws)
+        if q8:
+            ops.markov_sample_q8(logits.view(R, B, V), *w1, *w2, prev0, k, out=ids, workspace=ws)
+        else:
+            ops.markov_sample(logits.view(R, B, V), w1, w2, prev0, k, out=ids, workspace=ws)
 
     def pr():
         ops.conf_probe(H, pw, bias, thr, logit_out=plog, pass_out=ppass)
@@ -303,7 +330,11 @@ def main():
     main_stream = torch.cuda.current_stream()
 
     def one_round(ev=None):
-        if ev is None:
+        if ev is None and q8:
+            ops.draft_round_q8(*W, H, *w1, *w2, prev0, B, k, probe_w=pw, probe_bias=bias, probe_threshold=thr,
+                               base_out=logits.view(R, B, V), ids_out=ids, logit_out=plog, pass_out=ppass,
+                               workspace=ws)
+        elif ev is None:
             ops.draft_round(W, H, w1, w2, prev0, B, k, probe_w=pw, probe_bias=bias, probe_threshold=thr,
                             base_out=logits.view(R, B, V), ids_out=ids, logit_out=plog, pass_out=ppass,
                             workspace=ws)
@@ -372,10 +403,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "q8_0" if q8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": args.config, "num_reqs": R, "B": B, "k": k, "d": d, "V": V, "r": r},
-        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head)", "achieved": lm_gbs,
+        "config": {"workload": args.config, "num_reqs": R, "B": B, "k": k, "d": d, "V": V, "r": r,
+                   "weights": "q8_0" if q8 else "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head_q8)" if q8 else "lm_head GEMV (dspark_lm_head)",
+                     "achieved": lm_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
                      "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3},
         "round_hbm": {"achieved": round_gbs, "unit": "GB/s", "frac": round_gbs / HBM_PEAK_GBS,

@@ -135,7 +135,9 @@ constexpr size_t a_block_bytes(int R, int KB, bool Q8) {
 __device__ __forceinline__ float half_lo(uint32_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v))); }
 __device__ __forceinline__ float half_hi(uint32_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16))); }
 
-template <int NW, int KB, int RT, int LT, bool BL, bool Q8>
+// NV (Q8_0 only): request rows a lane's outputs can hold, 1 when there is a
+// single request (R = 1), else 4.
+template <int NW, int KB, int RT, int LT, bool BL, bool Q8, int NV = 4>
 __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p) {
   constexpr int kLoopThreads = NW * kWave;
   using BF = Frag<Q8>;
@@ -446,10 +448,10 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     // 4 lg + v; past R the zero row): up to 8 blocks held in registers, two
     // per word, read once per step; longer rows read them per k-block.
     constexpr bool kAscReg = Q8 && KB <= 8;
-    uint32_t asc[kAscReg ? 4 : 1][kAscReg ? kSH : 1];
+    uint32_t asc[kAscReg ? NV : 1][kAscReg ? kSH : 1];
     if constexpr (kAscReg) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int h = 0; h < kSH; ++h)
           asc[v][h] = reinterpret_cast<const uint32_t*>(a_sc + min(4 * lg + v, R) * kSR)[h];
@@ -457,25 +459,36 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     auto a_scales = [&](int kb, float (&s1)[4]) {
       if constexpr (kAscReg) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s1[v] = (kb & 1) ? half_hi(asc[v][kb >> 1]) : half_lo(asc[v][kb >> 1]);
+        for (int v = 0; v < NV; ++v) s1[v] = (kb & 1) ? half_hi(asc[v][kb >> 1]) : half_lo(asc[v][kb >> 1]);
       } else if constexpr (Q8) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < NV; ++v)
           s1[v] = static_cast<float>(__builtin_bit_cast(_Float16, a_sc[min(4 * lg + v, R) * kSR + kb]));
       }
     };
     // One k-block of a tile into its accumulator. bf16: an MFMA chain.
-    // Q8_0: the block's exact integer dot products (int8 MFMA), scaled by
-    // the A row's and the tile row's block scales and added in fp32, for the
-    // A rows that exist (v < R for every lane group).
+    // Q8_0: the block's exact integer dot products (int8 MFMA), then scaled
+    // by the A row's and the tile row's block scales and added in fp32, for
+    // the NV request rows a lane's outputs can hold. The two halves are separate so that a k-block's
+    // MFMAs for all tiles go out before any of their results is scaled.
+    auto mma8 = [&](BF a, BF b) -> i32x4 {
+      if constexpr (Q8) {
+        return __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
+                                                     i32x4{0, 0, 0, 0}, 0, 0, 0);
+      } else {
+        (void)a;
+        (void)b;
+        return i32x4{0, 0, 0, 0};
+      }
+    };
+    auto scale_add = [&](f32x4& acc, i32x4 d, const uint32_t* bsc, int kb, const float (&s1)[4]) {
+      const float s2 = (kb & 1) ? half_hi(bsc[kb >> 1]) : half_lo(bsc[kb >> 1]);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = __builtin_fmaf(static_cast<float>(d[v]), s1[v] * s2, acc[v]);
+    };
     auto mac = [&](f32x4& acc, BF a, BF b, const uint32_t* bsc, int kb, const float (&s1)[4]) {
       if constexpr (Q8) {
-        const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
-                                                             i32x4{0, 0, 0, 0}, 0, 0, 0);
-        const float s2 = (kb & 1) ? half_hi(bsc[kb >> 1]) : half_lo(bsc[kb >> 1]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (v == 0 || v < R) acc[v] = __builtin_fmaf(static_cast<float>(d[v]), s1[v] * s2, acc[v]);
+        scale_add(acc, mma8(a, b), bsc, kb, s1);
       } else {
         (void)bsc;
         (void)s1;
@@ -483,6 +496,8 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       }
     };
 
+    // The scores of every tile of this workgroup.
+    {
     // Register tiles and the wave's first LT LDS tiles, all accumulation
     // chains interleaved per k-block, so one chain's MFMAs overlap the
     // others' latency and the LDS reads of a k-block go out together. An
@@ -523,18 +538,34 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
         if (first)
 #pragma unroll
           for (int t = 0; t < L1; ++t) bl[t] = srcl[t][kb * kWave];
+        if constexpr (Q8) {
+          i32x4 dr[RG], dl[L1];
 #pragma unroll
-        for (int u = 0; u < RG; ++u)
-          if (RT > 0 && u0 + u < RT) {
-            const int uu = u0 + u < RT ? u0 + u : 0;
-            mac(accr[u], a, wreg[uu][kb], wsc[Q8 ? uu : 0], kb, s1);
-          }
-        if (first)
+          for (int u = 0; u < RG; ++u)
+            if (RT > 0 && u0 + u < RT) dr[u] = mma8(a, wreg[u0 + u < RT ? u0 + u : 0][kb]);
+          if (first)
 #pragma unroll
-          for (int t = 0; t < L1; ++t) mac(accl[t], a, bl[t], lsc[t], kb, s1);
+            for (int t = 0; t < L1; ++t) dl[t] = mma8(a, bl[t]);
+#pragma unroll
+          for (int u = 0; u < RG; ++u)
+            if (RT > 0 && u0 + u < RT) scale_add(accr[u], dr[u], wsc[u0 + u < RT ? u0 + u : 0], kb, s1);
+          if (first)
+#pragma unroll
+            for (int t = 0; t < L1; ++t) scale_add(accl[t], dl[t], lsc[t], kb, s1);
+        } else {
+#pragma unroll
+          for (int u = 0; u < RG; ++u)
+            if (RT > 0 && u0 + u < RT) mac(accr[u], a, wreg[u0 + u < RT ? u0 + u : 0][kb], wsc[0], kb, s1);
+          if (first)
+#pragma unroll
+            for (int t = 0; t < L1; ++t) mac(accl[t], a, bl[t], lsc[t], kb, s1);
+        }
         // (one wave per SIMD: keep each k-block's fragment reads next to its
         // MFMAs, so that they do not pile up in registers ahead of them)
         if (NW == 4 && (kb & 1)) __builtin_amdgcn_sched_barrier(0);
+        // (Q8_0: one k-block at a time, its MFMAs ahead of their scaling;
+        // loads of later k-blocks may not pile up ahead of them)
+        if (Q8) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int u = 0; u < RG; ++u)
@@ -572,6 +603,8 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
         mac(acc, a_frag[4 * kb], frag_of(j, kb, li, lg), sc1, kb, s1);
       }
       score(j, true, acc);
+    }
+
     }
 
     // ---- workgroup maximum per request (lanes of a 16-lane group share requests 4g..4g+3)
@@ -680,7 +713,7 @@ constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straig
 // no register spills; one wave per SIMD is built for bf16 at r = 256 only).
 // A Q8_0 tile takes half the registers of a bf16 one, plus its scales.
 constexpr int reg_tiles(int NW, int KB, bool Q8, bool BL = true) {
-  if (Q8) return NW != 8 ? 0 : KB <= 2 ? 6 : KB == 4 ? 5 : KB == 8 ? (BL ? 3 : 2) : KB == 16 ? 1 : 0;
+  if (Q8) return NW != 8 ? 0 : KB <= 2 ? 6 : KB == 4 ? 5 : KB == 8 ? (BL ? 3 : 1) : KB == 16 ? 1 : 0;
   return NW == 4 ? (KB == 8 ? 10 : 0) : KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
 }
 
@@ -708,12 +741,12 @@ LoopPlan make_loop_plan(int R, int V, int r, int k, int G, int NW, bool q8) {
   return pl;
 }
 
-template <int NW, int KB, bool BL, bool Q8>
+template <int NW, int KB, bool BL, bool Q8, int NV = 4>
 hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
   constexpr int RT = reg_tiles(NW, KB, Q8, BL);
   constexpr int LT = KB >= 16 ? 1 : 2;
   constexpr int kLoopThreads = NW * kWave;
-  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<NW, KB, RT, LT, BL, Q8>);
+  const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<NW, KB, RT, LT, BL, Q8, NV>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (attr != hipSuccess) return attr;
@@ -734,7 +767,17 @@ hipError_t dispatch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStre
   const bool bl = pl.base_in_lds != 0;
   if constexpr (Q8) {
     // Q8_0 weights: r <= 256 (at 512 and more the block scales of the A rows
-    // and the int8 products do not fit beside the tiles without spills)
+    // and the int8 products do not fit beside the tiles without spills);
+    // a single request scales one output row per lane instead of four.
+    if (prm.R == 1) {
+      switch (pl.KB) {
+        case 1: return bl ? launch_loop<8, 1, true, true, 1>(prm, pl, cus, st) : launch_loop<8, 1, false, true, 1>(prm, pl, cus, st);
+        case 2: return bl ? launch_loop<8, 2, true, true, 1>(prm, pl, cus, st) : launch_loop<8, 2, false, true, 1>(prm, pl, cus, st);
+        case 4: return bl ? launch_loop<8, 4, true, true, 1>(prm, pl, cus, st) : launch_loop<8, 4, false, true, 1>(prm, pl, cus, st);
+        case 8: return bl ? launch_loop<8, 8, true, true, 1>(prm, pl, cus, st) : launch_loop<8, 8, false, true, 1>(prm, pl, cus, st);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (pl.KB) {
       case 1: return bl ? launch_loop<8, 1, true, true>(prm, pl, cus, st) : launch_loop<8, 1, false, true>(prm, pl, cus, st);
       case 2: return bl ? launch_loop<8, 2, true, true>(prm, pl, cus, st) : launch_loop<8, 2, false, true>(prm, pl, cus, st);
