@@ -135,8 +135,8 @@ constexpr size_t a_block_bytes(int R, int KB, bool Q8) {
 __device__ __forceinline__ float half_lo(uint32_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v))); }
 __device__ __forceinline__ float half_hi(uint32_t v) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16))); }
 
-// NV (Q8_0 only): request rows a lane's outputs can hold, 1 when there is a
-// single request (R = 1), else 4.
+// NV: request rows a lane's outputs can hold, 1 when there is a single
+// request (R = 1), else 4.
 template <int NW, int KB, int RT, int LT, bool BL, bool Q8, int NV = 4>
 __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p) {
   constexpr int kLoopThreads = NW * kWave;
@@ -427,15 +427,16 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     auto score = [&](int j, bool tile_ok, f32x4 acc) {
       const int jj = tile_ok ? j : 0;
       const int n = (t0 + jj) * 16 + li;
+      // (a single request: only row 0 of each lane group exists)
       float bv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < NV; ++v) {
         const int m = min(4 * lg + v, R - 1);
         bv[v] = BL ? basel[m * p.bstride + jj * 16 + li]
                    : p.base[(static_cast<size_t>(m) * p.B + step) * V + min(n, V - 1)];
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < NV; ++v) {
         const uint64_t key = score_key(bv[v] + acc[v], static_cast<uint32_t>(n));
         const bool ok = tile_ok && 4 * lg + v < R && n < V;
         best[v] = ok && key > best[v] ? key : best[v];
@@ -787,7 +788,12 @@ hipError_t dispatch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStre
     }
   } else {
     if (pl.NW == 4)  // r = 256 only
-      return bl ? launch_loop<4, 8, true, false>(prm, pl, cus, st) : launch_loop<4, 8, false, false>(prm, pl, cus, st);
+      return prm.R == 1 ? (bl ? launch_loop<4, 8, true, false, 1>(prm, pl, cus, st)
+                              : launch_loop<4, 8, false, false, 1>(prm, pl, cus, st))
+                        : (bl ? launch_loop<4, 8, true, false>(prm, pl, cus, st)
+                              : launch_loop<4, 8, false, false>(prm, pl, cus, st));
+    if (prm.R == 1 && pl.KB == 8)  // the single-request heads at r = 256
+      return bl ? launch_loop<8, 8, true, false, 1>(prm, pl, cus, st) : launch_loop<8, 8, false, false, 1>(prm, pl, cus, st);
     switch (pl.KB) {
       case 1: return bl ? launch_loop<8, 1, true, false>(prm, pl, cus, st) : launch_loop<8, 1, false, false>(prm, pl, cus, st);
       case 2: return bl ? launch_loop<8, 2, true, false>(prm, pl, cus, st) : launch_loop<8, 2, false, false>(prm, pl, cus, st);
