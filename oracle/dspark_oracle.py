@@ -293,3 +293,68 @@ def draft_round_q8(Wq_lm, Wd_lm_bits, H, w1q, w1d_bits, w2q, w2d_bits, prev0, nu
     mk = markov_sample_q8(base32, w1q, w1d_bits, w2q, w2d_bits, prev0, k, d2t)
     logit, passed = conf_probe(H, probe_w_bits, probe_bias, probe_threshold)
     return dict(base=base64, base32=base32, logit=logit, passed=passed, **mk)
+
+
+# ---------------------------------------------------------------------------
+# The rest of the draft block forward at small M
+# ---------------------------------------------------------------------------
+#
+# [SI441] "Observation" lists the draft block's operations: the fc, q/k/v/o
+# and gate/up/down projections, the lm_head, and AttentionBatchedRagged over
+# a short context. The pages name no norm, activation or position encoding;
+# the readings taken (a pre-norm transformer layer with RMSNorm, a SiLU-gated
+# MLP, multi-head attention without a position encoding, each draft position
+# attending to its request's context and to its own block) are listed in the
+# design notes.
+
+def rmsnorm(x, gamma_bits, eps: float):
+    """y[m, t] = x[m, t] / sqrt(mean_t x[m, t]^2 + eps) * gamma[t]; gamma bf16, x fp32."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    g = bf16_to_f64(gamma_bits)
+    _finite(x64, g)
+    ms = np.mean(x64 * x64, axis=-1, keepdims=True)
+    return x64 / np.sqrt(ms + float(np.float32(eps))) * g
+
+
+def silu_gate(gu, F: int):
+    """a[m, j] = silu(g) * u with g = gu[m, j], u = gu[m, F + j], silu(g) = g / (1 + exp(-g))."""
+    gu64 = np.asarray(gu, dtype=np.float32).astype(np.float64)
+    _finite(gu64)
+    g, u = gu64[:, :F], gu64[:, F:2 * F]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def attention_ragged(q, k_blk, v_blk, R: int, B: int, H: int, Dh: int, k_ctx_bits, v_ctx_bits, ctx_len,
+                     block_causal: bool = False):
+    """Multi-head attention of the B draft positions of each request.
+
+    Position i of request r, head h, attends to the request's first
+    ctx_len[r] context positions (k_ctx, v_ctx: bf16 [R, Lmax, H * Dh]) and
+    to the positions of its own block (k_blk, v_blk: fp32 [R * B, H * Dh]),
+    all of them, or those j <= i when block_causal. Scores are q . k /
+    sqrt(Dh); softmax over those keys; the output is the weighted sum of the
+    values. q, k_blk, v_blk, out: [R * B, H * Dh], row r * B + i.
+    """
+    q64 = np.asarray(q, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+    kb = np.asarray(k_blk, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+    vb = np.asarray(v_blk, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+    kc = bf16_to_f64(k_ctx_bits)
+    vc = bf16_to_f64(v_ctx_bits)
+    Lmax = kc.shape[1]
+    kc = kc.reshape(R, Lmax, H, Dh)
+    vc = vc.reshape(R, Lmax, H, Dh)
+    _finite(q64, kb, vb, kc, vc)
+    out = np.empty((R, B, H, Dh))
+    for r in range(R):
+        L = int(ctx_len[r])
+        if not (0 <= L <= Lmax):
+            raise ValueError("ctx_len outside [0, Lmax]")
+        for i in range(B):
+            nb = i + 1 if block_causal else B
+            for h in range(H):
+                keys = np.concatenate([kc[r, :L, h], kb[r, :nb, h]])
+                vals = np.concatenate([vc[r, :L, h], vb[r, :nb, h]])
+                s = keys @ q64[r, i, h] / np.sqrt(Dh)
+                w = np.exp(s - s.max())
+                out[r, i, h] = (w / w.sum()) @ vals
+    return out.reshape(R * B, H * Dh)

@@ -1,0 +1,82 @@
+"""The oracle's block-forward functions against their pins, and planted
+mistakes that the pins must catch (no GPU)."""
+import numpy as np
+import pytest
+
+import oracle
+from block_pins import attention_pins, rmsnorm_pins, silu_gate_pins
+from oracle.dspark_oracle import bf16_to_f64
+
+
+@pytest.mark.parametrize("suite,fn", [(rmsnorm_pins, oracle.rmsnorm), (silu_gate_pins, oracle.silu_gate),
+                                      (attention_pins, oracle.attention_ragged)],
+                         ids=["rmsnorm", "silu_gate", "attention_ragged"])
+def test_block_oracle_meets_every_pin(suite, fn):
+    failed = [(n, d) for n, ok, d in suite(fn) if not ok]
+    assert not failed, failed
+
+
+def _rms_mutant(kind):
+    def f(x, gamma_bits, eps):
+        x64 = np.asarray(x, np.float32).astype(np.float64)
+        g = bf16_to_f64(gamma_bits)
+        ms = np.sum(x64 * x64, axis=-1, keepdims=True) if kind == "sum" else np.mean(x64 * x64, axis=-1, keepdims=True)
+        den = np.sqrt(ms) + eps if kind == "eps_outside" else np.sqrt(ms + eps)
+        y = x64 / den
+        return y if kind == "no_gamma" else y * g
+    return f
+
+
+@pytest.mark.parametrize("kind", ["sum", "eps_outside", "no_gamma"])
+def test_rmsnorm_mutant_is_caught(kind):
+    assert any(not ok for _, ok, _ in rmsnorm_pins(_rms_mutant(kind))), kind
+
+
+def _silu_mutant(kind):
+    def f(gu, F):
+        gu64 = np.asarray(gu, np.float32).astype(np.float64)
+        g, u = gu64[:, :F], gu64[:, F:2 * F]
+        if kind == "swap":
+            g, u = u, g
+        sig = 1.0 / (1.0 + np.exp(-g))
+        return sig * u if kind == "sigmoid_only" else g * sig * u if kind != "tanh" else np.tanh(g) * u
+    return f
+
+
+@pytest.mark.parametrize("kind", ["swap", "sigmoid_only", "tanh"])
+def test_silu_gate_mutant_is_caught(kind):
+    assert any(not ok for _, ok, _ in silu_gate_pins(_silu_mutant(kind))), kind
+
+
+def _attn_mutant(kind):
+    def f(q, k_blk, v_blk, R, B, H, Dh, k_ctx_bits, v_ctx_bits, ctx_len, block_causal=False):
+        q64 = np.asarray(q, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+        kb = np.asarray(k_blk, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+        vb = np.asarray(v_blk, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+        kc = bf16_to_f64(k_ctx_bits)
+        Lmax = kc.shape[1]
+        kc = kc.reshape(R, Lmax, H, Dh)
+        vc = bf16_to_f64(v_ctx_bits).reshape(R, Lmax, H, Dh)
+        out = np.empty((R, B, H, Dh))
+        for r in range(R):
+            L = Lmax if kind == "ignore_len" else int(ctx_len[r])
+            for i in range(B):
+                nb = (i if kind == "causal_off_by_one" else i + 1) if block_causal else B
+                if kind == "no_block":
+                    nb = 0 if L > 0 else nb
+                for h in range(H):
+                    keys = np.concatenate([kc[r, :L, h], kb[r, :nb, h]])
+                    vals = np.concatenate([vc[r, :L, h], vb[r, :nb, h]])
+                    if len(keys) == 0:
+                        out[r, i, h] = 0
+                        continue
+                    s = keys @ q64[r, i, h] / (1.0 if kind == "no_scale" else np.sqrt(Dh))
+                    w = np.exp(s - s.max())
+                    out[r, i, h] = (w / (1.0 if kind == "no_normalize" else w.sum())) @ vals
+        return out.reshape(R * B, H * Dh)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["ignore_len", "causal_off_by_one", "no_block", "no_scale", "no_normalize"])
+def test_attention_mutant_is_caught(kind):
+    assert any(not ok for _, ok, _ in attention_pins(_attn_mutant(kind))), kind
