@@ -235,4 +235,40 @@ dspark_status dspark_draft_round_q8(const int8_t* Wq_lm, const uint16_t* Wd_lm, 
                                            workspace, probe_w ? &pa : nullptr, s));
 }
 
+dspark_status dspark_rmsnorm(const float* x, int M, int D, const uint16_t* gamma, float eps, float* y,
+                             void* stream) {
+  if (!x || !gamma || !y) return DSPARK_ERR_NULL;
+  if (M < 1 || D < 1 || !(eps >= 0.f)) return DSPARK_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(gamma, 2) || !aligned(y, 4)) return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_rmsnorm(x, M, D, gamma, eps, y, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_silu_gate(const float* gu, int M, int F, float* a, void* stream) {
+  if (!gu || !a) return DSPARK_ERR_NULL;
+  if (M < 1 || F < 1) return DSPARK_ERR_SHAPE;
+  if (!aligned(gu, 4) || !aligned(a, 4)) return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_silu_gate(gu, M, F, a, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_proj_smallm_add(const uint16_t* W, int N, int K, const float* X, int M, const float* residual,
+                                     float* Y, void* stream) {
+  dspark_status st = gemv_checks(W, N, K, X, M, Y);
+  if (st == DSPARK_OK && !residual) st = DSPARK_ERR_NULL;
+  if (st == DSPARK_OK && !aligned(residual, 4)) st = DSPARK_ERR_ALIGN;
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv(W, N, K, X, M, Y, static_cast<hipStream_t>(stream), residual));
+}
+
+dspark_status dspark_attention_ragged(const float* q, const float* k, const float* v, int ld, int R, int B, int H,
+                                      int Dh, const uint16_t* k_ctx, const uint16_t* v_ctx, int Lmax,
+                                      const int32_t* ctx_len, int block_causal, float* out, void* stream) {
+  if (!q || !k || !v || !ctx_len || !out || (Lmax > 0 && (!k_ctx || !v_ctx))) return DSPARK_ERR_NULL;
+  if (R < 1 || !dspark::attention_shape_fits(B, H, Dh, Lmax) || ld < H * Dh || (ld % 4) != 0) return DSPARK_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4) || !aligned(ctx_len, 4) ||
+      (k_ctx && !aligned(k_ctx, 16)) || (v_ctx && !aligned(v_ctx, 16)))
+    return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_attention(q, k, v, ld, R, B, H, Dh, k_ctx, v_ctx, Lmax, ctx_len, block_causal ? 1 : 0,
+                                           out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

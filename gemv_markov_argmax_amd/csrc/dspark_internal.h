@@ -185,6 +185,15 @@ __device__ __forceinline__ uint64_t row_max64(uint64_t v) {
 // stay below 2^31 bytes.
 bool gemv_shape_fits(int N, int K, int M);
 
+// The rest of the draft block: see dspark_rmsnorm, dspark_silu_gate,
+// dspark_attention_ragged.
+hipError_t launch_rmsnorm(const float* x, int M, int D, const uint16_t* gamma, float eps, float* y, hipStream_t st);
+hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t st);
+bool attention_shape_fits(int B, int H, int Dh, int Lmax);
+hipError_t launch_attention(const float* q, const float* kb, const float* vb, int ld, int R, int B, int H, int Dh,
+                            const uint16_t* kc, const uint16_t* vc, int Lmax, const int32_t* ctx_len, int causal,
+                            float* out, hipStream_t st);
+
 // Small-M GEMV over Q8_0 weights; see dspark_proj_smallm_q8.
 bool gemv_q8_shape_fits(int N, int K, int M);
 hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M, float* Y,
@@ -192,7 +201,7 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
 
 // Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
-                       hipStream_t stream);
+                       hipStream_t stream, const float* res = nullptr);
 
 // The confidence probe's arguments (see dspark_conf_probe).
 struct ProbeArgs {

@@ -44,7 +44,12 @@ struct GemvParams {
   int ldy;       // row stride of Y
   int chunk;     // gemv_tstream_kernel: tiles whose outputs are staged in LDS at once (even)
   int pq, prem;  // row pairs per workgroup: N/2 = pq * gridDim.x + prem (the first prem get one more)
+  const float* res;  // null, or [M, N] (row stride ldy) added to the outputs; may be Y itself
 };
+
+// The output value of (m, n), plus the residual when there is one (read and
+// written by the same thread, so the residual may be Y itself).
+__device__ __forceinline__ float with_res(const GemvParams& p, size_t idx, float y) { return p.res ? p.res[idx] + y : y; }
 
 // Contiguous row range [r0, r1) of workgroup b: a balanced share of the N/2
 // row pairs (a load instruction covers 2 rows); the last workgroup also takes
@@ -286,7 +291,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   for (int e = tid; e < rounds * M * 16; e += NW * kWave) {
     const int t = e / (M * 16), rem = e - t * M * 16, mm = rem >> 4, col = rem & 15;
     const int n = r0 + 16 * t + col;
-    if (n < r1) p.Y[static_cast<size_t>(mm) * p.ldy + n] = ysum[(t * ROWS + mm) * 16 + col];
+    const size_t idx = static_cast<size_t>(mm) * p.ldy + n;
+    if (n < r1) p.Y[idx] = with_res(p, idx, ysum[(t * ROWS + mm) * 16 + col]);
   }
 }
 
@@ -483,7 +489,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
     const int n0 = r0 + 16 * c0, cols = min(r1, r0 + 16 * c1) - n0;
     for (int m = 0; m < M; ++m)
       for (int j = tid; j < cols; j += NW * kWave)
-        p.Y[static_cast<size_t>(m) * p.ldy + n0 + j] = ylds[(j >> 4) * M * 16 + m * 16 + (j & 15)];
+        p.Y[static_cast<size_t>(m) * p.ldy + n0 + j] =
+            with_res(p, static_cast<size_t>(m) * p.ldy + n0 + j, ylds[(j >> 4) * M * 16 + m * 16 + (j & 15)]);
     __syncthreads();  // the next chunk reuses the LDS outputs
   };
 
@@ -703,7 +710,8 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
     __syncthreads();
     for (int e = tid; e < M * 64; e += kMrThreads) {
       const int m = e >> 6, col = 64 * half + (e & 63);
-      if (col < nrows) p.Y[static_cast<size_t>(m) * p.ldy + n0 + col] = L[m * 64 + (e & 63)] + L[(M + m) * 64 + (e & 63)];
+      const size_t idx = static_cast<size_t>(m) * p.ldy + n0 + col;
+      if (col < nrows) p.Y[idx] = with_res(p, idx, L[m * 64 + (e & 63)] + L[(M + m) * 64 + (e & 63)]);
     }
     __syncthreads();
   }
@@ -841,11 +849,12 @@ bool gemv_shape_fits(int N, int K, int M) {
 }
 
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float* res) {
   const int cus = device_cu_count();
   if (cus <= 0) return hipErrorNoDevice;
   GemvParams prm{};
   prm.W = W;
+  prm.res = res;
   prm.N = N;
   prm.K = K;
   prm.ldy = N;
@@ -865,6 +874,7 @@ hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, f
     const int m0 = M * part / parts, mc = M * (part + 1) / parts - m0;
     prm.X = X + static_cast<size_t>(m0) * K;
     prm.Y = Y + static_cast<size_t>(m0) * N;
+    prm.res = res ? res + static_cast<size_t>(m0) * N : nullptr;
     prm.M = mc;
     hipError_t e;
     switch (((mc + 7) / 8 + 1) / 2) {

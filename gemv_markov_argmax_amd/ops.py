@@ -30,6 +30,10 @@ SIGNATURES = {
                                      _p, _i, _i, _p, _f, _f, _p, _p, _p]),
     "dspark_draft_round_q8": (_i, [_p, _p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _f, _f,
                                    _p, _p, _p, _p, _p, _sz, _p]),
+    "dspark_rmsnorm": (_i, [_p, _i, _i, _p, _f, _p, _p]),
+    "dspark_silu_gate": (_i, [_p, _i, _i, _p, _p]),
+    "dspark_proj_smallm_add": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
+    "dspark_attention_ragged": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -169,6 +173,100 @@ def proj_smallm_q8(Wq: torch.Tensor, Wd: torch.Tensor, X: torch.Tensor, out: tor
 def lm_head_q8(Wq: torch.Tensor, Wd: torch.Tensor, H: torch.Tensor, out: torch.Tensor | None = None):
     """Base logits from a Q8_0 lm_head (dspark_lm_head_q8)."""
     return _gemv_q8(lib().dspark_lm_head_q8, Wq, Wd, H, out)
+
+
+def proj_smallm_add(W: torch.Tensor, X: torch.Tensor, residual: torch.Tensor, out: torch.Tensor | None = None):
+    """Y = residual + X @ W.T (dspark_proj_smallm_add); out may be residual itself."""
+    _dev(W, torch.bfloat16, "W", 2)
+    _dev(X, torch.float32, "X", 2)
+    _dev(residual, torch.float32, "residual", 2)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K or tuple(residual.shape) != (M, N):
+        raise ValueError("W [N, K], X [M, K] and residual [M, N] required")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _dev(out, torch.float32, "out", 2)
+    _check(lib().dspark_proj_smallm_add(W.data_ptr(), N, K, X.data_ptr(), M, residual.data_ptr(), out.data_ptr(),
+                                        _stream(W)))
+    return out
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out: torch.Tensor | None = None):
+    """x / sqrt(mean(x^2) + eps) * gamma per row (dspark_rmsnorm); gamma bf16 [D]."""
+    _dev(x, torch.float32, "x", 2)
+    _dev(gamma, torch.bfloat16, "gamma", 1)
+    M, D = x.shape
+    if gamma.shape[0] != D:
+        raise ValueError("gamma must have D entries")
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, torch.float32, "out", 2)
+    _check(lib().dspark_rmsnorm(x.data_ptr(), M, D, gamma.data_ptr(), float(eps), out.data_ptr(), _stream(x)))
+    return out
+
+
+def silu_gate(gu: torch.Tensor, out: torch.Tensor | None = None):
+    """silu(gu[:, :F]) * gu[:, F:] (dspark_silu_gate)."""
+    _dev(gu, torch.float32, "gu", 2)
+    M, F2 = gu.shape
+    if F2 % 2:
+        raise ValueError("gu must have an even number of columns")
+    if out is None:
+        out = torch.empty((M, F2 // 2), dtype=torch.float32, device=gu.device)
+    _dev(out, torch.float32, "out", 2)
+    _check(lib().dspark_silu_gate(gu.data_ptr(), M, F2 // 2, out.data_ptr(), _stream(gu)))
+    return out
+
+
+def attention_ragged(qkv: torch.Tensor, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor, v_ctx: torch.Tensor,
+                     ctx_len: torch.Tensor, block_causal: bool = False, out: torch.Tensor | None = None):
+    """Attention of the draft positions (dspark_attention_ragged). qkv fp32
+    [R * B, 3 H Dh] holds q, k and v as three column blocks (the fused qkv
+    projection's output); k_ctx, v_ctx bf16 [R, Lmax, H Dh]; ctx_len int32 [R]."""
+    _dev(qkv, torch.float32, "qkv", 2)
+    _dev(k_ctx, torch.bfloat16, "k_ctx", 3)
+    _dev(v_ctx, torch.bfloat16, "v_ctx", 3)
+    _dev(ctx_len, torch.int32, "ctx_len", 1)
+    HD = H * Dh
+    if tuple(qkv.shape) != (R * B, 3 * HD) or k_ctx.shape[0] != R or k_ctx.shape[2] != HD or v_ctx.shape != k_ctx.shape:
+        raise ValueError("qkv [R * B, 3 H Dh] and k_ctx, v_ctx [R, Lmax, H Dh] required")
+    if out is None:
+        out = torch.empty((R * B, HD), dtype=torch.float32, device=qkv.device)
+    _dev(out, torch.float32, "out", 2)
+    base = qkv.data_ptr()
+    _check(lib().dspark_attention_ragged(base, base + HD * 4, base + 2 * HD * 4, 3 * HD, R, B, H, Dh,
+                                         k_ctx.data_ptr(), v_ctx.data_ptr(), k_ctx.shape[1], ctx_len.data_ptr(),
+                                         1 if block_causal else 0, out.data_ptr(), _stream(qkv)))
+    return out
+
+
+def draft_block_forward(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor,
+                        v_ctx: torch.Tensor, ctx_len: torch.Tensor, eps: float, block_causal: bool = False,
+                        scratch: dict | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One draft block (layer) as seven C-ABI calls: rmsnorm, the fused qkv
+    projection, attention, o with the residual, rmsnorm, the fused gate/up
+    projection, the SiLU gate, and down with the residual. w holds bf16
+    tensors qkv [3d, d], o [d, d], gate_up [2F, d], down [d, F], ln1, ln2 [d].
+    ``scratch`` (dict of fp32 buffers x, qkv, attn, h2, gu, act) is reused
+    when given; ``out`` may be h itself."""
+    M, d = h.shape
+    F = w["down"].shape[1]
+    sc = scratch if scratch is not None else {}
+    dev = h.device
+
+    def buf(name, shape):
+        if name not in sc or tuple(sc[name].shape) != shape:
+            sc[name] = torch.empty(shape, dtype=torch.float32, device=dev)
+        return sc[name]
+    x = rmsnorm(h, w["ln1"], eps, out=buf("x", (M, d)))
+    qkv = proj_smallm(w["qkv"], x, out=buf("qkv", (M, 3 * d)))
+    attn = attention_ragged(qkv, R, B, H, Dh, k_ctx, v_ctx, ctx_len, block_causal, out=buf("attn", (M, d)))
+    h2 = proj_smallm_add(w["o"], attn, h, out=buf("h2", (M, d)))
+    x2 = rmsnorm(h2, w["ln2"], eps, out=buf("x", (M, d)))
+    gu = proj_smallm(w["gate_up"], x2, out=buf("gu", (M, 2 * F)))
+    act = silu_gate(gu, out=buf("act", (M, F)))
+    return proj_smallm_add(w["down"], act, h2, out=out if out is not None else torch.empty_like(h))
 
 
 def q8_from_numpy(q, d_bits, device):

@@ -298,6 +298,28 @@ def layer_inputs(seed: int | None = None, copies: int = 1):
                 probe_bias=np.float32(0.0), probe_threshold=np.float32(0.0))
 
 
+def block_inputs(R: int, B: int, H: int, Dh: int, F: int, Lmax: int, ctx_len, seed: int, copies: int = 1):
+    """A draft block (layer) at M = R * B: weights bf16 ~ N(0, 0.02^2) of
+    qkv [3 H Dh, d], o [d, H Dh], gate_up [2F, d], down [d, F] (d = H Dh),
+    norm gains ln1, ln2 ~ 1 + N(0, 0.1^2) in bf16; hidden states h [R * B, d]
+    ~ N(0, 1); context keys and values bf16 [R, Lmax, d] ~ N(0, 1); the given
+    context lengths. ``copies`` > 1 draws that many weight sets (layers)."""
+    d = H * Dh
+    layers = []
+    for c in range(copies):
+        base = S_LAYER + 16 * (20 + c)
+        w = dict(qkv=normal_bf16(seed, base, (3 * d, d)), o=normal_bf16(seed, base + 1, (d, d)),
+                 gate_up=normal_bf16(seed, base + 2, (2 * F, d)), down=normal_bf16(seed, base + 3, (d, F)))
+        w["ln1"] = bf16_bits_rne(1.0 + normal_f32(seed, base + 4, (d,), 0.1))
+        w["ln2"] = bf16_bits_rne(1.0 + normal_f32(seed, base + 5, (d,), 0.1))
+        layers.append(w)
+    h = normal_f32(seed, S_LAYER + 16 * 19, (R * B, d))
+    k_ctx = normal_bf16(seed, S_LAYER + 16 * 19 + 1, (R, Lmax, d), 1.0)
+    v_ctx = normal_bf16(seed, S_LAYER + 16 * 19 + 2, (R, Lmax, d), 1.0)
+    return dict(h=h, layers=layers, k_ctx=k_ctx, v_ctx=v_ctx, ctx_len=np.asarray(ctx_len, np.int32),
+                R=R, B=B, H=H, Dh=Dh, F=F, d=d, Lmax=Lmax, eps=np.float32(1e-6))
+
+
 def fused_layer(ws: dict) -> dict:
     """The same layer with the projections that share an input concatenated
     along N: qkv [3 * 4096, 4096] (rows q, then k, then v) and gate_up

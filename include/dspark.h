@@ -321,6 +321,70 @@ dspark_status dspark_draft_round_q8(const int8_t* Wq_lm, const uint16_t* Wd_lm, 
                                     float* logit_out, int32_t* pass_out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * The rest of the draft block forward at small M.
+ *
+ * [SI441] "Observation": a draft block runs its projections (q/k/v/o,
+ * gate/up/down: dspark_proj_smallm) and an attention over a short context
+ * (AttentionBatchedRagged). The pages name nothing else of the block; these
+ * entry points take the plainest reading of a transformer drafter derived
+ * from Qwen3: RMSNorm before the attention and before the MLP, a SiLU-gated
+ * MLP, residual additions, and multi-head attention without a position
+ * encoding in which each draft position attends to its request's context and
+ * to its own block. Each computes in fp32 with a fixed summation order.
+ */
+
+/*
+ * dspark_rmsnorm: y[m, t] = x[m, t] / sqrt(mean_t x[m, t]^2 + eps) * gamma[t].
+ *   x     fp32 [M, D]   16-byte aligned
+ *   gamma bf16 [D]       2-byte aligned
+ *   y     fp32 [M, D]   overwritten (may be x)
+ * Sizes: M >= 1, D >= 1. eps >= 0.
+ */
+dspark_status dspark_rmsnorm(const float* x, int M, int D, const uint16_t* gamma, float eps, float* y,
+                             void* stream);
+
+/*
+ * dspark_silu_gate: a[m, j] = silu(g) * u, g = gu[m, j], u = gu[m, F + j],
+ * silu(g) = g / (1 + exp(-g)) (gu is the output of the fused gate/up
+ * projection: gate columns first).
+ *   gu fp32 [M, 2F];  a fp32 [M, F], overwritten.  Sizes: M >= 1, F >= 1.
+ */
+dspark_status dspark_silu_gate(const float* gu, int M, int F, float* a, void* stream);
+
+/*
+ * dspark_proj_smallm_add: Y = residual + X W^T (the o and down projections
+ * with the block's residual addition in the same launch). Arguments, sizes
+ * and errors are those of dspark_proj_smallm; residual fp32 [M, N], 4-byte
+ * aligned, may be Y itself (each element is read before it is written).
+ */
+dspark_status dspark_proj_smallm_add(const uint16_t* W, int N, int K, const float* X, int M,
+                                     const float* residual, float* Y, void* stream);
+
+/*
+ * dspark_attention_ragged -- attention of the B draft positions of each of
+ * R requests, H heads of Dh dimensions.
+ *
+ * Position i of request r, head h, attends to the request's first
+ * ctx_len[r] context positions and to the positions of its own block (all B
+ * of them, or j <= i when block_causal): scores q . k / sqrt(Dh), softmax
+ * over those keys, output the weighted sum of their values.
+ *
+ *   q, k, v   fp32 [R * B, ld]: row r * B + i, head h at columns h * Dh ..
+ *             (e.g. the three column blocks of the fused qkv projection with
+ *             ld = 3 H Dh); 16-byte aligned, ld % 4 == 0
+ *   k_ctx, v_ctx  bf16 [R, Lmax, H * Dh], 16-byte aligned (the context cache)
+ *   ctx_len   int32 [R], each in [0, Lmax]
+ *   out       fp32 [R * B, H * Dh], overwritten
+ * Sizes: R >= 1, 1 <= B <= 16, H >= 1, 8 <= Dh <= 256 with Dh % 8 == 0,
+ * Lmax >= 0 and B * (Lmax + B) * 4 <= 96 KiB (the scores of one request and
+ * head are kept on chip: a short context).
+ */
+dspark_status dspark_attention_ragged(const float* q, const float* k, const float* v, int ld, int R, int B,
+                                      int H, int Dh, const uint16_t* k_ctx, const uint16_t* v_ctx,
+                                      int Lmax, const int32_t* ctx_len, int block_causal, float* out,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

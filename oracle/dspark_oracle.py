@@ -358,3 +358,55 @@ def attention_ragged(q, k_blk, v_blk, R: int, B: int, H: int, Dh: int, k_ctx_bit
                 w = np.exp(s - s.max())
                 out[r, i, h] = (w / w.sum()) @ vals
     return out.reshape(R * B, H * Dh)
+
+
+def draft_block_forward(h, w: dict, R: int, B: int, H: int, Dh: int, k_ctx_bits, v_ctx_bits, ctx_len,
+                        eps: float, block_causal: bool = False):
+    """One draft block (layer) forward at small M = R * B, in float64, as
+    the readings above compose it:
+      x1 = rmsnorm(h, ln1); qkv = x1 W_qkv^T; a = attention(qkv);
+      h2 = h + a W_o^T; x2 = rmsnorm(h2, ln2); gu = x2 W_gate_up^T;
+      h3 = h2 + silu_gate(gu) W_down^T.
+    w: bf16 bits of qkv [3 H Dh, d], o [d, H Dh], gate_up [2 F, d], down
+    [d, F], ln1 and ln2 [d]. Intermediate values stay in float64 here."""
+    HD = H * Dh
+    x1 = rmsnorm(h, w["ln1"], eps)
+    qkv = x1 @ bf16_to_f64(w["qkv"]).T
+    a = _attention64(qkv, R, B, H, Dh, k_ctx_bits, v_ctx_bits, ctx_len, block_causal)
+    h2 = np.asarray(h, np.float32).astype(np.float64) + a @ bf16_to_f64(w["o"]).T
+    x2 = rmsnorm_f64(h2, w["ln2"], eps)
+    gu = x2 @ bf16_to_f64(w["gate_up"]).T
+    F = gu.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    return h2 + (g / (1.0 + np.exp(-g)) * u) @ bf16_to_f64(w["down"]).T
+
+
+def rmsnorm_f64(x64, gamma_bits, eps: float):
+    """rmsnorm on float64 inputs (the block's second norm reads a float64 sum)."""
+    g = bf16_to_f64(gamma_bits)
+    ms = np.mean(x64 * x64, axis=-1, keepdims=True)
+    return x64 / np.sqrt(ms + float(np.float32(eps))) * g
+
+
+def _attention64(qkv, R, B, H, Dh, k_ctx_bits, v_ctx_bits, ctx_len, block_causal):
+    """attention_ragged on float64 q, k, v (same definition, no float32 rounding of the inputs)."""
+    HD = H * Dh
+    q = qkv[:, :HD].reshape(R, B, H, Dh)
+    kb = qkv[:, HD:2 * HD].reshape(R, B, H, Dh)
+    vb = qkv[:, 2 * HD:].reshape(R, B, H, Dh)
+    kc = bf16_to_f64(k_ctx_bits)
+    Lmax = kc.shape[1]
+    kc = kc.reshape(R, Lmax, H, Dh)
+    vc = bf16_to_f64(v_ctx_bits).reshape(R, Lmax, H, Dh)
+    out = np.empty((R, B, H, Dh))
+    for r in range(R):
+        L = int(ctx_len[r])
+        for i in range(B):
+            nb = i + 1 if block_causal else B
+            for hh in range(H):
+                keys = np.concatenate([kc[r, :L, hh], kb[r, :nb, hh]])
+                vals = np.concatenate([vc[r, :L, hh], vb[r, :nb, hh]])
+                sc = keys @ q[r, i, hh] / np.sqrt(Dh)
+                e = np.exp(sc - sc.max())
+                out[r, i, hh] = (e / e.sum()) @ vals
+    return out.reshape(R * B, HD)

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = declared()
     for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
               "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
-              "dspark_markov_sample_q8", "dspark_draft_round_q8",
+              "dspark_markov_sample_q8", "dspark_draft_round_q8", "dspark_rmsnorm", "dspark_silu_gate",
+              "dspark_proj_smallm_add", "dspark_attention_ragged",
               "dspark_markov_workspace_bytes",
               "dspark_status_string"]:
         assert n in names
@@ -228,6 +229,33 @@ def test_draft_round_errors(L):
     assert call(ps=A + 2) == ERR_ALIGN
     assert call(ws=None) == ERR_WORKSPACE
     assert call(wsb=ws - 1) == ERR_WORKSPACE
+
+
+def test_block_errors(L):
+    assert L.dspark_rmsnorm(None, 7, 64, A, 1e-6, A2, None) == ERR_NULL
+    assert L.dspark_rmsnorm(A, 0, 64, A, 1e-6, A2, None) == ERR_SHAPE
+    assert L.dspark_rmsnorm(A, 7, 64, A, -1.0, A2, None) == ERR_SHAPE
+    assert L.dspark_rmsnorm(MIS, 7, 64, A, 1e-6, A2, None) == ERR_ALIGN
+    assert L.dspark_silu_gate(None, 7, 64, A2, None) == ERR_NULL
+    assert L.dspark_silu_gate(A, 7, 0, A2, None) == ERR_SHAPE
+    assert L.dspark_proj_smallm_add(A, 16, 64, A, 7, None, A2, None) == ERR_NULL
+    assert L.dspark_proj_smallm_add(A, 16, 12, A, 7, A, A2, None) == ERR_SHAPE
+    assert L.dspark_proj_smallm_add(A, 16, 64, A, 7, A + 2, A2, None) == ERR_ALIGN
+    f = L.dspark_attention_ragged
+    ok = dict(q=A, k=A2, v=A, ld=3 * 4096, R=1, B=7, H=32, Dh=128, kc=A, vc=A2, Lmax=512, lens=A, c=0, out=A2)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["ld"], a["R"], a["B"], a["H"], a["Dh"], a["kc"], a["vc"], a["Lmax"],
+                 a["lens"], a["c"], a["out"], None)
+    assert call(q=None) == ERR_NULL
+    assert call(kc=None) == ERR_NULL
+    assert call(B=17) == ERR_SHAPE
+    assert call(Dh=100) == ERR_SHAPE                 # Dh % 8 != 0
+    assert call(Dh=512) == ERR_SHAPE
+    assert call(Lmax=4000) == ERR_SHAPE              # scores of a head beyond 96 KiB
+    assert call(ld=4094) == ERR_SHAPE
+    assert call(k=A2 + 4) == ERR_ALIGN
 
 
 def test_binding_has_no_cpu_path(L):

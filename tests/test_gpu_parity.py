@@ -706,6 +706,106 @@ def test_draft_round_q8_full_size(dev):
     probe_close(out["logit"].cpu().numpy(), out["passed"].cpu().numpy(), ref_l, ref_p, 0.0)
 
 
+# ---------------------------------------------------------------------------
+# The rest of the draft block: RMSNorm, SiLU gate, residual GEMV, attention
+# ---------------------------------------------------------------------------
+
+def _close(a, b, what, rtol=1e-5, atol=1e-5):
+    a = np.asarray(a, np.float64)
+    err = np.abs(a - b)
+    ok = err <= atol + rtol * np.abs(b)
+    assert ok.all(), f"{what}: max err {err.max():.3e} at {np.unravel_index(np.argmax(err), err.shape)}"
+
+
+@pytest.mark.parametrize("M,D", [(7, 4096), (3, 7424), (1, 5), (16, 4100), (72, 5120)])
+def test_rmsnorm_matches_oracle(dev, M, D):
+    say(f"[rmsnorm] M={M} D={D}")
+    g = np.random.default_rng(M + D)
+    x = (g.standard_normal((M, D)) * 2).astype(np.float32)
+    gamma = synth.bf16_bits_rne((1 + 0.1 * g.standard_normal(D)).astype(np.float32))
+    y = _ops().rmsnorm(_up(x, dev), _bf(gamma, dev), 1e-6)
+    torch.cuda.synchronize()
+    _close(y.cpu().numpy(), oracle.rmsnorm(x, gamma, 1e-6), f"rmsnorm M={M} D={D}")
+
+
+@pytest.mark.parametrize("M,F", [(7, 12288), (1, 3), (9, 1000)])
+def test_silu_gate_matches_oracle(dev, M, F):
+    say(f"[silu gate] M={M} F={F}")
+    g = np.random.default_rng(M * F)
+    gu = (g.standard_normal((M, 2 * F)) * 4).astype(np.float32)
+    a = _ops().silu_gate(_up(gu, dev))
+    torch.cuda.synchronize()
+    _close(a.cpu().numpy(), oracle.silu_gate(gu, F), f"silu gate M={M} F={F}", rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 4096, 4096), (7, 4096, 12288), (3, 1000, 264), (20, 515, 256)])
+def test_proj_smallm_add(dev, M, N, K):
+    """Y = residual + X W^T, also in place (residual = Y)."""
+    seed = 7300 + M + N + K
+    say(f"[proj add] M={M} N={N} K={K} seed={seed}")
+    W, X = synth.gemv_inputs(M, N, K, seed)
+    res = synth.normal_f32(seed, synth.S_BASE, (M, N))
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    y = _ops().proj_smallm_add(Wd, Xd, _up(res, dev))
+    r2 = _up(res, dev)
+    _ops().proj_smallm_add(Wd, Xd, r2, out=r2)
+    plain = _ops().proj_smallm(Wd, Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, r2), "in-place result differs"
+    assert torch.equal(y, _up(res, dev) + plain), "residual epilogue is not y + residual in fp32"
+    logits_close(y.cpu().numpy(), oracle.gemv(W, X) + res.astype(np.float64), f"proj add M={M} N={N} K={K}")
+
+
+ATTN_CASES = [
+    # (R, B, H, Dh, Lmax, ctx_len, causal)
+    (1, 7, 32, 128, 512, [512], False), (1, 7, 32, 128, 512, [300], True), (2, 3, 4, 64, 128, [0, 100], False),
+    (2, 16, 2, 256, 100, [100, 37], True), (1, 1, 1, 8, 0, [0], False), (3, 5, 3, 32, 40, [40, 0, 17], True),
+]
+
+
+@pytest.mark.parametrize("R,B,H,Dh,Lmax,lens,causal", ATTN_CASES)
+def test_attention_ragged_matches_oracle(dev, R, B, H, Dh, Lmax, lens, causal):
+    seed = 7400 + R * B * H + Dh + Lmax
+    say(f"[attention] R={R} B={B} H={H} Dh={Dh} Lmax={Lmax} lens={lens} causal={causal}")
+    g = np.random.default_rng(seed)
+    HD = H * Dh
+    qkv = g.standard_normal((R * B, 3 * HD)).astype(np.float32)
+    kc = synth.bf16_bits_rne(g.standard_normal((R, max(Lmax, 1), HD)).astype(np.float32))[:, :Lmax]
+    vc = synth.bf16_bits_rne(g.standard_normal((R, max(Lmax, 1), HD)).astype(np.float32))[:, :Lmax]
+    kcd = _bf(np.ascontiguousarray(kc), dev).view(R, Lmax, HD) if Lmax else torch.zeros((R, 0, HD), dtype=torch.bfloat16, device=dev)
+    vcd = _bf(np.ascontiguousarray(vc), dev).view(R, Lmax, HD) if Lmax else torch.zeros((R, 0, HD), dtype=torch.bfloat16, device=dev)
+    out = _ops().attention_ragged(_up(qkv, dev), R, B, H, Dh, kcd, vcd,
+                                  torch.tensor(lens, dtype=torch.int32, device=dev), causal)
+    out2 = _ops().attention_ragged(_up(qkv, dev), R, B, H, Dh, kcd, vcd,
+                                   torch.tensor(lens, dtype=torch.int32, device=dev), causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "rerun differs"
+    kc_ = kc if Lmax else np.zeros((R, 0, HD), np.uint16)
+    vc_ = vc if Lmax else np.zeros((R, 0, HD), np.uint16)
+    ref = oracle.attention_ragged(qkv[:, :HD], qkv[:, HD:2 * HD], qkv[:, 2 * HD:], R, B, H, Dh, kc_, vc_, lens, causal)
+    _close(out.cpu().numpy(), ref, "attention", rtol=1e-4, atol=1e-5)
+
+
+@pytest.mark.parametrize("R,B,H,Dh,F,Lmax,lens", [(1, 7, 2, 128, 512, 64, [64]), (1, 7, 32, 128, 12288, 512, [512]),
+                                                  (2, 4, 4, 64, 1024, 96, [96, 20])])
+def test_draft_block_forward_matches_oracle(dev, R, B, H, Dh, F, Lmax, lens):
+    """One whole draft block (rmsnorm, qkv, attention, o + residual, rmsnorm,
+    gate/up, SiLU gate, down + residual) through the C ABI, against the fp64
+    composition."""
+    seed = 7500 + H * Dh + F
+    say(f"[draft block] R={R} B={B} H={H} Dh={Dh} F={F} Lmax={Lmax} lens={lens} seed={seed}")
+    inp = synth.block_inputs(R, B, H, Dh, F, Lmax, lens, seed)
+    w = {k: _bf(v, dev) for k, v in inp["layers"][0].items()}
+    kc = _bf(inp["k_ctx"], dev).view(R, Lmax, H * Dh)
+    vc = _bf(inp["v_ctx"], dev).view(R, Lmax, H * Dh)
+    y = _ops().draft_block_forward(_up(inp["h"], dev), w, R, B, H, Dh, kc, vc,
+                                   torch.tensor(lens, dtype=torch.int32, device=dev), float(inp["eps"]))
+    torch.cuda.synchronize()
+    ref = oracle.draft_block_forward(inp["h"], inp["layers"][0], R, B, H, Dh, inp["k_ctx"], inp["v_ctx"],
+                                     inp["ctx_len"], float(inp["eps"]))
+    logits_close(y.cpu().numpy(), ref, f"draft block d={H * Dh}")
+
+
 def test_round_graph_replay(dev):
     """The whole round recorded once in a HIP graph and replayed, with eager
     work between replays: every replay equals the eager result."""

@@ -80,3 +80,23 @@ def _attn_mutant(kind):
 @pytest.mark.parametrize("kind", ["ignore_len", "causal_off_by_one", "no_block", "no_scale", "no_normalize"])
 def test_attention_mutant_is_caught(kind):
     assert any(not ok for _, ok, _ in attention_pins(_attn_mutant(kind))), kind
+
+
+def test_block_forward_pins():
+    """The composed block: with o and down zero it returns h exactly (the
+    residual path); the MLP branch is linear in W_down (doubling W_down
+    doubles h3 - h2, with h2 the output at W_down = 0); the attention branch
+    does not see W_down."""
+    from gemv_markov_argmax_amd import synth
+    inp = synth.block_inputs(2, 3, 2, 16, 48, 10, [4, 10], 11)
+    w = dict(inp["layers"][0])
+    args = (2, 3, 2, 16, inp["k_ctx"], inp["v_ctx"], inp["ctx_len"], 1e-6)
+    zero = dict(w, o=np.zeros_like(w["o"]), down=np.zeros_like(w["down"]))
+    y0 = oracle.draft_block_forward(inp["h"], zero, *args)
+    assert np.array_equal(y0, inp["h"].astype(np.float64))
+    nodown = dict(w, down=np.zeros_like(w["down"]))
+    h2 = oracle.draft_block_forward(inp["h"], nodown, *args)
+    y1 = oracle.draft_block_forward(inp["h"], w, *args)
+    dbl = synth.bf16_bits_rne(((w["down"].astype(np.uint32) << 16).view(np.float32) * 2).astype(np.float32))
+    y2 = oracle.draft_block_forward(inp["h"], dict(w, down=dbl), *args)
+    assert np.allclose(y2 - h2, 2 * (y1 - h2), rtol=1e-12, atol=1e-12)
