@@ -229,6 +229,102 @@ def bench_layer(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_block(args, dev, layers: int, with_head: bool):
+    """draft_block: one step = one draft block forward (rmsnorm, fused qkv,
+    attention over 512 context positions, o + residual, rmsnorm, fused
+    gate/up, SiLU gate, down + residual) at M = 7, d = 4096, 32 heads of 128,
+    F = 12288, cycling over 4 weight copies so that no weight is served from
+    the Infinity Cache.
+    draft_round_8l: one step = a whole draft round of an 8-layer drafter
+    (8 x 436 MB of layer weights, each with its own context cache) followed
+    by the Qwen3-8B head round (dspark_draft_round: lm_head, Markov loop,
+    probe): 4.7 GB of weights, the size of the drafter SharpInference #441
+    streams per round."""
+    import numpy as np
+    import torch
+
+    from gemv_markov_argmax_amd import ops, synth
+
+    R, B, H, Dh, F, L = 1, 7, 32, 128, 12288, 512
+    M, d = R * B, H * Dh
+    n_w = layers if with_head else 4
+    log(f"[bench] generating {n_w} draft blocks (d={d}, F={F}, context {L})")
+    blocks = []
+    for c in range(n_w):
+        inp = synth.block_inputs(R, B, H, Dh, F, L, [L], synth.config_seed("draft_layer") + 100 * c)
+        blocks.append(dict(w={k: ops.bf16_from_bits(v, dev) for k, v in inp["layers"][0].items()},
+                           kc=ops.bf16_from_bits(inp["k_ctx"], dev).view(R, L, d),
+                           vc=ops.bf16_from_bits(inp["v_ctx"], dev).view(R, L, d)))
+        if c == 0:
+            h0 = torch.from_numpy(inp["h"]).to(dev)
+            eps = float(inp["eps"])
+        del inp
+    ctx_len = torch.tensor([L], dtype=torch.int32, device=dev)
+    scratch = {}
+    h = h0.clone()
+    hb = torch.empty_like(h0)
+    block_bytes = (3 * d * d + d * d + 2 * F * d + d * F) * 2 + 2 * d * 2 + 2 * R * L * d * 2 + M * d * 4 * 2
+
+    head = None
+    if with_head:
+        hinp = synth.round_inputs("qwen3_8b_head")
+        V, k, r = hinp["V"], hinp["k"], hinp["r"]
+        head = dict(W=ops.bf16_from_bits(hinp["W_lm"], dev), w1=ops.bf16_from_bits(hinp["w1"], dev),
+                    w2=ops.bf16_from_bits(hinp["w2"], dev), prev0=torch.from_numpy(hinp["prev0"]).to(dev),
+                    pw=ops.bf16_from_bits(hinp["probe_w"], dev), base=torch.empty(R, B, V, device=dev),
+                    ws=ops.markov_workspace(R, k, V, dev), k=k)
+        out_host = torch.empty(R * k * 8 + M * 8, dtype=torch.uint8, pin_memory=True)
+        ids = out_host[: R * k * 8].view(torch.int64).view(R, k)
+        plog = out_host[R * k * 8: R * k * 8 + M * 4].view(torch.float32)
+        ppass = out_host[R * k * 8 + M * 4:].view(torch.int32)
+        lm_b, mk_b, pr_b = round_bytes(hinp)
+        del hinp
+
+    def step(s_):
+        x, y = h, hb
+        for li in range(layers if with_head else 1):
+            blk = blocks[li if with_head else s_ % n_w]
+            ops.draft_block_forward(x, blk["w"], R, B, H, Dh, blk["kc"], blk["vc"], ctx_len, eps, scratch=scratch, out=y)
+            x, y = y, x
+        if with_head:
+            ops.draft_round(head["W"], x, head["w1"], head["w2"], head["prev0"], B, head["k"], probe_w=head["pw"],
+                            base_out=head["base"], ids_out=ids, logit_out=plog, pass_out=ppass, workspace=head["ws"])
+
+    for s_ in range(args.warmup):
+        step(s_)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    a.record()
+    for s_ in range(args.steps):
+        step(s_)
+    b.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_us = a.elapsed_time(b) * 1e3 / args.steps
+    n_blocks = layers if with_head else 1
+    step_bytes = n_blocks * block_bytes + ((lm_b + mk_b + pr_b) if with_head else 0)
+    gbs = step_bytes / (step_us * 1e-6) / 1e9
+    name = "draft_round_8l" if with_head else "draft_block"
+    log(f"[bench] {name}: {args.steps / elapsed:.1f} steps/s, {step_us:.1f} us per step, "
+        f"{step_bytes / 1e9:.3f} GB algorithmic -> {gbs:.0f} GB/s")
+    out = {
+        "metric": ("draft rounds/s of an 8-layer drafter + Qwen3-8B head round" if with_head
+                   else "draft blocks/s (one full layer at M=7) + achieved HBM GB/s"),
+        "value": args.steps / elapsed, "unit": "rounds/s" if with_head else "blocks/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "layers": n_blocks, "M": M, "d": d, "heads": H, "head_dim": Dh, "ffn": F,
+                   "context": L},
+        "roofline": {"bound": "hbm", "kernel": "whole step (its GEMVs carry 98% of the bytes)", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_step": step_bytes, "step_us": step_us},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,7 +332,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="qwen3_8b_head",
                     choices=["tiny", "qwen3_8b_head", "lane27b", "reduced_vocab_batched", "draft_layer",
-                             "qwen3_8b_head_q8", "lane27b_q8"])
+                             "qwen3_8b_head_q8", "lane27b_q8", "draft_block", "draft_round_8l"])
     ap.add_argument("--layer-copies", type=int, default=4,
                     help="draft_layer: distinct weight copies cycled through (defeats the 256 MB Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
@@ -269,6 +365,10 @@ def main():
 
     if args.config == "draft_layer":
         return bench_layer(args, dev)
+    if args.config == "draft_block":
+        return bench_block(args, dev, 1, False)
+    if args.config == "draft_round_8l":
+        return bench_block(args, dev, 8, True)
     log(f"[bench] generating {args.config} inputs")
     inp = synth.round_inputs(args.config)
     R, B, k, d, V, r = (inp[x] for x in ("num_reqs", "B", "k", "d", "V", "r"))

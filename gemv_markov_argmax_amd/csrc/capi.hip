@@ -259,16 +259,23 @@ dspark_status dspark_proj_smallm_add(const uint16_t* W, int N, int K, const floa
   return from_hip(dspark::launch_gemv(W, N, K, X, M, Y, static_cast<hipStream_t>(stream), residual));
 }
 
+size_t dspark_attention_workspace_bytes(int num_reqs, int B, int H, int Dh, int Lmax) {
+  if (!dspark::attention_shape_fits(num_reqs, B, H, Dh, Lmax)) return 0;
+  return dspark::attention_workspace_bytes(num_reqs, B, H, Dh, Lmax);
+}
+
 dspark_status dspark_attention_ragged(const float* q, const float* k, const float* v, int ld, int R, int B, int H,
                                       int Dh, const uint16_t* k_ctx, const uint16_t* v_ctx, int Lmax,
-                                      const int32_t* ctx_len, int block_causal, float* out, void* stream) {
+                                      const int32_t* ctx_len, int block_causal, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !ctx_len || !out || (Lmax > 0 && (!k_ctx || !v_ctx))) return DSPARK_ERR_NULL;
-  if (R < 1 || !dspark::attention_shape_fits(B, H, Dh, Lmax) || ld < H * Dh || (ld % 4) != 0) return DSPARK_ERR_SHAPE;
+  if (!dspark::attention_shape_fits(R, B, H, Dh, Lmax) || ld < H * Dh || (ld % 4) != 0) return DSPARK_ERR_SHAPE;
+  if (!workspace || workspace_bytes < dspark::attention_workspace_bytes(R, B, H, Dh, Lmax)) return DSPARK_ERR_WORKSPACE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4) || !aligned(ctx_len, 4) ||
-      (k_ctx && !aligned(k_ctx, 16)) || (v_ctx && !aligned(v_ctx, 16)))
+      !aligned(workspace, 16) || (k_ctx && !aligned(k_ctx, 16)) || (v_ctx && !aligned(v_ctx, 16)))
     return DSPARK_ERR_ALIGN;
   return from_hip(dspark::launch_attention(q, k, v, ld, R, B, H, Dh, k_ctx, v_ctx, Lmax, ctx_len, block_causal ? 1 : 0,
-                                           out, static_cast<hipStream_t>(stream)));
+                                           out, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

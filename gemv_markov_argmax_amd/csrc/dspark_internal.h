@@ -189,10 +189,11 @@ bool gemv_shape_fits(int N, int K, int M);
 // dspark_attention_ragged.
 hipError_t launch_rmsnorm(const float* x, int M, int D, const uint16_t* gamma, float eps, float* y, hipStream_t st);
 hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t st);
-bool attention_shape_fits(int B, int H, int Dh, int Lmax);
+bool attention_shape_fits(int R, int B, int H, int Dh, int Lmax);
+size_t attention_workspace_bytes(int R, int B, int H, int Dh, int Lmax);
 hipError_t launch_attention(const float* q, const float* kb, const float* vb, int ld, int R, int B, int H, int Dh,
                             const uint16_t* kc, const uint16_t* vc, int Lmax, const int32_t* ctx_len, int causal,
-                            float* out, hipStream_t st);
+                            float* out, float* ws, hipStream_t st);
 
 // Small-M GEMV over Q8_0 weights; see dspark_proj_smallm_q8.
 bool gemv_q8_shape_fits(int N, int K, int M);

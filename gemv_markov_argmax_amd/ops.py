@@ -33,7 +33,8 @@ SIGNATURES = {
     "dspark_rmsnorm": (_i, [_p, _i, _i, _p, _f, _p, _p]),
     "dspark_silu_gate": (_i, [_p, _i, _i, _p, _p]),
     "dspark_proj_smallm_add": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
-    "dspark_attention_ragged": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p, _p]),
+    "dspark_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "dspark_attention_ragged": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p, _p, _sz, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -219,11 +220,18 @@ def silu_gate(gu: torch.Tensor, out: torch.Tensor | None = None):
     return out
 
 
+def attention_workspace_bytes(R: int, B: int, H: int, Dh: int, Lmax: int) -> int:
+    return int(lib().dspark_attention_workspace_bytes(R, B, H, Dh, Lmax))
+
+
 def attention_ragged(qkv: torch.Tensor, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor, v_ctx: torch.Tensor,
-                     ctx_len: torch.Tensor, block_causal: bool = False, out: torch.Tensor | None = None):
+                     ctx_len: torch.Tensor, block_causal: bool = False, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
     """Attention of the draft positions (dspark_attention_ragged). qkv fp32
     [R * B, 3 H Dh] holds q, k and v as three column blocks (the fused qkv
-    projection's output); k_ctx, v_ctx bf16 [R, Lmax, H Dh]; ctx_len int32 [R]."""
+    projection's output); k_ctx, v_ctx bf16 [R, Lmax, H Dh]; ctx_len int32 [R].
+    ``workspace`` (uint8, at least attention_workspace_bytes) is allocated when
+    not given."""
     _dev(qkv, torch.float32, "qkv", 2)
     _dev(k_ctx, torch.bfloat16, "k_ctx", 3)
     _dev(v_ctx, torch.bfloat16, "v_ctx", 3)
@@ -234,10 +242,15 @@ def attention_ragged(qkv: torch.Tensor, R: int, B: int, H: int, Dh: int, k_ctx: 
     if out is None:
         out = torch.empty((R * B, HD), dtype=torch.float32, device=qkv.device)
     _dev(out, torch.float32, "out", 2)
+    if workspace is None:
+        workspace = torch.empty(max(attention_workspace_bytes(R, B, H, Dh, k_ctx.shape[1]), 16), dtype=torch.uint8,
+                                device=qkv.device)
+    _dev(workspace, torch.uint8, "workspace", 1)
     base = qkv.data_ptr()
     _check(lib().dspark_attention_ragged(base, base + HD * 4, base + 2 * HD * 4, 3 * HD, R, B, H, Dh,
                                          k_ctx.data_ptr(), v_ctx.data_ptr(), k_ctx.shape[1], ctx_len.data_ptr(),
-                                         1 if block_causal else 0, out.data_ptr(), _stream(qkv)))
+                                         1 if block_causal else 0, out.data_ptr(), workspace.data_ptr(),
+                                         workspace.numel(), _stream(qkv)))
     return out
 
 
@@ -248,8 +261,8 @@ def draft_block_forward(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: in
     projection, attention, o with the residual, rmsnorm, the fused gate/up
     projection, the SiLU gate, and down with the residual. w holds bf16
     tensors qkv [3d, d], o [d, d], gate_up [2F, d], down [d, F], ln1, ln2 [d].
-    ``scratch`` (dict of fp32 buffers x, qkv, attn, h2, gu, act) is reused
-    when given; ``out`` may be h itself."""
+    ``scratch`` (dict of fp32 buffers x, qkv, attn, h2, gu, act and the
+    attention workspace) is reused when given; ``out`` may be h itself."""
     M, d = h.shape
     F = w["down"].shape[1]
     sc = scratch if scratch is not None else {}
@@ -261,7 +274,11 @@ def draft_block_forward(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: in
         return sc[name]
     x = rmsnorm(h, w["ln1"], eps, out=buf("x", (M, d)))
     qkv = proj_smallm(w["qkv"], x, out=buf("qkv", (M, 3 * d)))
-    attn = attention_ragged(qkv, R, B, H, Dh, k_ctx, v_ctx, ctx_len, block_causal, out=buf("attn", (M, d)))
+    nws = max(attention_workspace_bytes(R, B, H, Dh, k_ctx.shape[1]), 16)
+    if "attn_ws" not in sc or sc["attn_ws"].numel() < nws:
+        sc["attn_ws"] = torch.empty(nws, dtype=torch.uint8, device=dev)
+    attn = attention_ragged(qkv, R, B, H, Dh, k_ctx, v_ctx, ctx_len, block_causal, out=buf("attn", (M, d)),
+                            workspace=sc["attn_ws"])
     h2 = proj_smallm_add(w["o"], attn, h, out=buf("h2", (M, d)))
     x2 = rmsnorm(h2, w["ln2"], eps, out=buf("x", (M, d)))
     gu = proj_smallm(w["gate_up"], x2, out=buf("gu", (M, 2 * F)))

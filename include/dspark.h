@@ -376,14 +376,23 @@ dspark_status dspark_proj_smallm_add(const uint16_t* W, int N, int K, const floa
  *   k_ctx, v_ctx  bf16 [R, Lmax, H * Dh], 16-byte aligned (the context cache)
  *   ctx_len   int32 [R], each in [0, Lmax]
  *   out       fp32 [R * B, H * Dh], overwritten
+ *   workspace device memory of at least dspark_attention_workspace_bytes(R,
+ *             B, H, Dh, Lmax) bytes, 16-byte aligned: per-chunk partial
+ *             results, fully written before they are read (no clearing
+ *             needed); calls that share it must be ordered on one stream
  * Sizes: R >= 1, 1 <= B <= 16, H >= 1, 8 <= Dh <= 256 with Dh % 8 == 0,
- * Lmax >= 0 and B * (Lmax + B) * 4 <= 96 KiB (the scores of one request and
- * head are kept on chip: a short context).
+ * 0 <= Lmax <= 2^30, R * H * ceil((Lmax + B) / 64) < 2^31.
+ * The keys are taken 64 at a time (one workgroup each); each chunk's softmax
+ * uses its own maximum and the chunks are merged in order with the exact
+ * rescaling, so the context length is limited by the workspace only.
+ * Errors: DSPARK_ERR_NULL, _SHAPE, _WORKSPACE, _ALIGN; nothing is launched
+ * then.
  */
+size_t dspark_attention_workspace_bytes(int num_reqs, int B, int H, int Dh, int Lmax);
 dspark_status dspark_attention_ragged(const float* q, const float* k, const float* v, int ld, int R, int B,
                                       int H, int Dh, const uint16_t* k_ctx, const uint16_t* v_ctx,
                                       int Lmax, const int32_t* ctx_len, int block_causal, float* out,
-                                      void* stream);
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -242,18 +242,26 @@ def test_block_errors(L):
     assert L.dspark_proj_smallm_add(A, 16, 12, A, 7, A, A2, None) == ERR_SHAPE
     assert L.dspark_proj_smallm_add(A, 16, 64, A, 7, A + 2, A2, None) == ERR_ALIGN
     f = L.dspark_attention_ragged
-    ok = dict(q=A, k=A2, v=A, ld=3 * 4096, R=1, B=7, H=32, Dh=128, kc=A, vc=A2, Lmax=512, lens=A, c=0, out=A2)
+    need = L.dspark_attention_workspace_bytes(1, 7, 32, 128, 512)
+    assert need == 32 * 9 * 7 * 130 * 4                       # 9 chunks of 64 keys, m, l and o per chunk
+    assert L.dspark_attention_workspace_bytes(1, 17, 32, 128, 512) == 0
+    ok = dict(q=A, k=A2, v=A, ld=3 * 4096, R=1, B=7, H=32, Dh=128, kc=A, vc=A2, Lmax=512, lens=A, c=0, out=A2,
+              ws=A, nws=need)
 
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["q"], a["k"], a["v"], a["ld"], a["R"], a["B"], a["H"], a["Dh"], a["kc"], a["vc"], a["Lmax"],
-                 a["lens"], a["c"], a["out"], None)
+                 a["lens"], a["c"], a["out"], a["ws"], a["nws"], None)
     assert call(q=None) == ERR_NULL
     assert call(kc=None) == ERR_NULL
     assert call(B=17) == ERR_SHAPE
     assert call(Dh=100) == ERR_SHAPE                 # Dh % 8 != 0
     assert call(Dh=512) == ERR_SHAPE
-    assert call(Lmax=4000) == ERR_SHAPE              # scores of a head beyond 96 KiB
+    assert call(Lmax=-1) == ERR_SHAPE
+    assert call(Lmax=4000) == ERR_WORKSPACE          # more chunks than the workspace holds
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(nws=need - 1) == ERR_WORKSPACE
+    assert call(ws=A + 8) == ERR_ALIGN
     assert call(ld=4094) == ERR_SHAPE
     assert call(k=A2 + 4) == ERR_ALIGN
 

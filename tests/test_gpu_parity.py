@@ -760,6 +760,9 @@ ATTN_CASES = [
     # (R, B, H, Dh, Lmax, ctx_len, causal)
     (1, 7, 32, 128, 512, [512], False), (1, 7, 32, 128, 512, [300], True), (2, 3, 4, 64, 128, [0, 100], False),
     (2, 16, 2, 256, 100, [100, 37], True), (1, 1, 1, 8, 0, [0], False), (3, 5, 3, 32, 40, [40, 0, 17], True),
+    # keys come in chunks of 64: Lk = 64 and 65 exactly, two full chunks, a long context, Dh = 24 (three 8-dim groups)
+    (2, 7, 2, 128, 58, [57, 58], True), (1, 7, 3, 64, 121, [121], False), (2, 7, 4, 128, 4000, [4000, 1234], True),
+    (2, 4, 3, 24, 70, [70, 1], True),
 ]
 
 
@@ -784,6 +787,26 @@ def test_attention_ragged_matches_oracle(dev, R, B, H, Dh, Lmax, lens, causal):
     vc_ = vc if Lmax else np.zeros((R, 0, HD), np.uint16)
     ref = oracle.attention_ragged(qkv[:, :HD], qkv[:, HD:2 * HD], qkv[:, 2 * HD:], R, B, H, Dh, kc_, vc_, lens, causal)
     _close(out.cpu().numpy(), ref, "attention", rtol=1e-4, atol=1e-5)
+
+
+def test_attention_workspace_needs_no_clearing(dev):
+    """Every partial result is written before it is read: a workspace full of
+    NaN bit patterns, shared by a large and then a smaller call, gives the
+    results of fresh workspaces bit for bit."""
+    say("[attention] dirty shared workspace")
+    ops = _ops()
+    g = np.random.default_rng(7411)
+    ws = torch.full((ops.attention_workspace_bytes(2, 7, 4, 128, 700),), 0xFF, dtype=torch.uint8, device=dev)
+    for (R, B, H, Dh, Lmax, lens, causal) in [(2, 7, 4, 128, 700, [700, 3], True), (1, 5, 2, 64, 90, [80], False)]:
+        HD = H * Dh
+        qkv = _up(g.standard_normal((R * B, 3 * HD)).astype(np.float32), dev)
+        kc = _bf(synth.bf16_bits_rne(g.standard_normal((R, Lmax, HD)).astype(np.float32)), dev).view(R, Lmax, HD)
+        vc = _bf(synth.bf16_bits_rne(g.standard_normal((R, Lmax, HD)).astype(np.float32)), dev).view(R, Lmax, HD)
+        ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+        a = ops.attention_ragged(qkv, R, B, H, Dh, kc, vc, ln, causal, workspace=ws)
+        b = ops.attention_ragged(qkv, R, B, H, Dh, kc, vc, ln, causal)
+        torch.cuda.synchronize()
+        assert torch.isfinite(a).all() and torch.equal(a, b), f"shared workspace changed the result R={R} Lmax={Lmax}"
 
 
 @pytest.mark.parametrize("R,B,H,Dh,F,Lmax,lens", [(1, 7, 2, 128, 512, 64, [64]), (1, 7, 32, 128, 12288, 512, [512]),
