@@ -235,11 +235,12 @@ def bench_block(args, dev, layers: int, with_head: bool):
     gate/up, SiLU gate, down + residual) at M = 7, d = 4096, 32 heads of 128,
     F = 12288, cycling over 4 weight copies so that no weight is served from
     the Infinity Cache.
-    draft_round_8l: one step = a whole draft round of an 8-layer drafter
-    (8 x 436 MB of layer weights, each with its own context cache) followed
-    by the Qwen3-8B head round (dspark_draft_round: lm_head, Markov loop,
-    probe): 4.7 GB of weights, the size of the drafter SharpInference #441
-    streams per round."""
+    draft_round_8l: one step = a whole draft round: the fc projection
+    ([4096, 4096]), 8 blocks (8 x 436 MB of layer weights, each block with
+    its own context cache), the final norm, then the Qwen3-8B head round
+    (dspark_draft_round: lm_head, Markov loop, probe): 4.8 GB of weights,
+    about the ~4.7 GB SharpInference #441 says its drafter streams per round.
+    Each block is one dspark_draft_block call."""
     import numpy as np
     import torch
 
@@ -267,6 +268,11 @@ def bench_block(args, dev, layers: int, with_head: bool):
 
     head = None
     if with_head:
+        fcw = ops.bf16_from_bits(synth.normal_bf16(synth.config_seed("draft_layer"), 7001, (d, d)), dev)
+        x_in = torch.from_numpy(synth.normal_f32(synth.config_seed("draft_layer"), 7002, (M, d))).to(dev)
+        fnorm = ops.bf16_from_bits(synth.bf16_bits_rne(
+            1.0 + synth.normal_f32(synth.config_seed("draft_layer"), 7003, (d,), 0.1)), dev)
+        hid = torch.empty(M, d, device=dev)
         hinp = synth.round_inputs("qwen3_8b_head")
         V, k, r = hinp["V"], hinp["k"], hinp["r"]
         head = dict(W=ops.bf16_from_bits(hinp["W_lm"], dev), w1=ops.bf16_from_bits(hinp["w1"], dev),
@@ -281,14 +287,15 @@ def bench_block(args, dev, layers: int, with_head: bool):
         del hinp
 
     def step(s_):
-        x, y = h, hb
-        for li in range(layers if with_head else 1):
-            blk = blocks[li if with_head else s_ % n_w]
-            ops.draft_block_forward(x, blk["w"], R, B, H, Dh, blk["kc"], blk["vc"], ctx_len, eps, scratch=scratch, out=y)
-            x, y = y, x
-        if with_head:
-            ops.draft_round(head["W"], x, head["w1"], head["w2"], head["prev0"], B, head["k"], probe_w=head["pw"],
-                            base_out=head["base"], ids_out=ids, logit_out=plog, pass_out=ppass, workspace=head["ws"])
+        if not with_head:
+            blk = blocks[s_ % n_w]
+            ops.draft_block_forward(h, blk["w"], R, B, H, Dh, blk["kc"], blk["vc"], ctx_len, eps, scratch=scratch,
+                                    out=hb)
+            return
+        ops.draft_forward(x_in, fcw, [b_["w"] for b_ in blocks], [b_["kc"] for b_ in blocks],
+                          [b_["vc"] for b_ in blocks], R, B, H, Dh, ctx_len, fnorm, eps, scratch=scratch, out=hid)
+        ops.draft_round(head["W"], hid, head["w1"], head["w2"], head["prev0"], B, head["k"], probe_w=head["pw"],
+                        base_out=head["base"], ids_out=ids, logit_out=plog, pass_out=ppass, workspace=head["ws"])
 
     for s_ in range(args.warmup):
         step(s_)
@@ -304,13 +311,14 @@ def bench_block(args, dev, layers: int, with_head: bool):
     elapsed = time.perf_counter() - t0
     step_us = a.elapsed_time(b) * 1e3 / args.steps
     n_blocks = layers if with_head else 1
-    step_bytes = n_blocks * block_bytes + ((lm_b + mk_b + pr_b) if with_head else 0)
+    fc_bytes = (d * d * 2 + 2 * M * d * 4 + d * 2 + 2 * M * d * 4) if with_head else 0  # fc and the final norm
+    step_bytes = n_blocks * block_bytes + fc_bytes + ((lm_b + mk_b + pr_b) if with_head else 0)
     gbs = step_bytes / (step_us * 1e-6) / 1e9
     name = "draft_round_8l" if with_head else "draft_block"
     log(f"[bench] {name}: {args.steps / elapsed:.1f} steps/s, {step_us:.1f} us per step, "
         f"{step_bytes / 1e9:.3f} GB algorithmic -> {gbs:.0f} GB/s")
     out = {
-        "metric": ("draft rounds/s of an 8-layer drafter + Qwen3-8B head round" if with_head
+        "metric": ("draft rounds/s of an 8-layer drafter (fc, blocks, norm) + Qwen3-8B head round" if with_head
                    else "draft blocks/s (one full layer at M=7) + achieved HBM GB/s"),
         "value": args.steps / elapsed, "unit": "rounds/s" if with_head else "blocks/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,

@@ -278,4 +278,80 @@ dspark_status dspark_attention_ragged(const float* q, const float* k, const floa
                                            out, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
+// The draft block's intermediate buffers, carved out of the caller's
+// workspace at 256-byte boundaries.
+struct BlockLayout {
+  size_t x, qkv, attn, h2, gu, act, attn_ws, total;
+};
+
+static BlockLayout block_layout(int R, int B, int H, int Dh, int d, int F, int Lmax) {
+  const size_t M = static_cast<size_t>(R) * B, HD = static_cast<size_t>(H) * Dh;
+  auto up = [](size_t n) { return (n + 255) & ~static_cast<size_t>(255); };
+  BlockLayout l{};
+  size_t off = 0;
+  l.x = off; off += up(M * d * 4);
+  l.qkv = off; off += up(M * 3 * HD * 4);
+  l.attn = off; off += up(M * HD * 4);
+  l.h2 = off; off += up(M * d * 4);
+  l.gu = off; off += up(M * 2 * static_cast<size_t>(F) * 4);
+  l.act = off; off += up(M * static_cast<size_t>(F) * 4);
+  l.attn_ws = off; off += up(dspark::attention_workspace_bytes(R, B, H, Dh, Lmax));
+  l.total = off;
+  return l;
+}
+
+static bool block_shape_fits(int R, int B, int H, int Dh, int d, int F, int Lmax) {
+  if (R < 1 || d < 8 || (d % 8) != 0 || F < 8 || (F % 8) != 0) return false;
+  if (!dspark::attention_shape_fits(R, B, H, Dh, Lmax)) return false;
+  const long long M = static_cast<long long>(R) * B, HD = static_cast<long long>(H) * Dh;
+  if (M > (1 << 20) || 3 * HD > (1LL << 30) || 2LL * F > (1LL << 30)) return false;
+  return dspark::gemv_shape_fits(static_cast<int>(3 * HD), d, static_cast<int>(M)) &&
+         dspark::gemv_shape_fits(d, static_cast<int>(HD), static_cast<int>(M)) &&
+         dspark::gemv_shape_fits(2 * F, d, static_cast<int>(M)) && dspark::gemv_shape_fits(d, F, static_cast<int>(M));
+}
+
+size_t dspark_draft_block_workspace_bytes(int num_reqs, int B, int H, int Dh, int d, int F, int Lmax) {
+  if (!block_shape_fits(num_reqs, B, H, Dh, d, F, Lmax)) return 0;
+  return block_layout(num_reqs, B, H, Dh, d, F, Lmax).total;
+}
+
+dspark_status dspark_draft_block(const uint16_t* w_qkv, const uint16_t* w_o, const uint16_t* w_gate_up,
+                                 const uint16_t* w_down, const uint16_t* ln1, const uint16_t* ln2, int d, int F,
+                                 int H, int Dh, int num_reqs, int B, const float* h_in, float* h_out,
+                                 const uint16_t* k_ctx, const uint16_t* v_ctx, int Lmax, const int32_t* ctx_len,
+                                 float eps, int block_causal, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!w_qkv || !w_o || !w_gate_up || !w_down || !ln1 || !ln2 || !h_in || !h_out || !ctx_len ||
+      (Lmax > 0 && (!k_ctx || !v_ctx)))
+    return DSPARK_ERR_NULL;
+  if (!block_shape_fits(num_reqs, B, H, Dh, d, F, Lmax) || !(eps >= 0.f)) return DSPARK_ERR_SHAPE;
+  const BlockLayout l = block_layout(num_reqs, B, H, Dh, d, F, Lmax);
+  if (!workspace || workspace_bytes < l.total) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) ||
+      !aligned(ln1, 2) || !aligned(ln2, 2) || !aligned(h_in, 16) || !aligned(h_out, 16) || !aligned(ctx_len, 4) ||
+      !aligned(workspace, 256) || (k_ctx && !aligned(k_ctx, 16)) || (v_ctx && !aligned(v_ctx, 16)))
+    return DSPARK_ERR_ALIGN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  float* x = reinterpret_cast<float*>(base + l.x);
+  float* qkv = reinterpret_cast<float*>(base + l.qkv);
+  float* attn = reinterpret_cast<float*>(base + l.attn);
+  float* h2 = reinterpret_cast<float*>(base + l.h2);
+  float* gu = reinterpret_cast<float*>(base + l.gu);
+  float* act = reinterpret_cast<float*>(base + l.act);
+  float* aws = reinterpret_cast<float*>(base + l.attn_ws);
+  const int M = num_reqs * B, HD = H * Dh;
+  hipError_t e = dspark::launch_rmsnorm(h_in, M, d, ln1, eps, x, st);
+  if (e == hipSuccess) e = dspark::launch_gemv(w_qkv, 3 * HD, d, x, M, qkv, st);
+  if (e == hipSuccess)
+    e = dspark::launch_attention(qkv, qkv + HD, qkv + 2 * HD, 3 * HD, num_reqs, B, H, Dh, k_ctx, v_ctx, Lmax, ctx_len,
+                                 block_causal ? 1 : 0, attn, aws, st);
+  if (e == hipSuccess) e = dspark::launch_gemv(w_o, d, HD, attn, M, h2, st, h_in);
+  if (e == hipSuccess) e = dspark::launch_rmsnorm(h2, M, d, ln2, eps, x, st);
+  if (e == hipSuccess) e = dspark::launch_gemv(w_gate_up, 2 * F, d, x, M, gu, st);
+  if (e == hipSuccess) e = dspark::launch_silu_gate(gu, M, F, act, st);
+  if (e == hipSuccess) e = dspark::launch_gemv(w_down, d, F, act, M, h_out, st, h2);
+  return from_hip(e);
+}
+
 }  // extern "C"

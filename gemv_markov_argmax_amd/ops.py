@@ -35,6 +35,9 @@ SIGNATURES = {
     "dspark_proj_smallm_add": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "dspark_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_attention_ragged": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p, _p, _sz, _p]),
+    "dspark_draft_block_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "dspark_draft_block": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _f, _i,
+                                _p, _sz, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -254,35 +257,79 @@ def attention_ragged(qkv: torch.Tensor, R: int, B: int, H: int, Dh: int, k_ctx: 
     return out
 
 
+def draft_block_workspace_bytes(R: int, B: int, H: int, Dh: int, d: int, F: int, Lmax: int) -> int:
+    return int(lib().dspark_draft_block_workspace_bytes(R, B, H, Dh, d, F, Lmax))
+
+
 def draft_block_forward(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor,
                         v_ctx: torch.Tensor, ctx_len: torch.Tensor, eps: float, block_causal: bool = False,
                         scratch: dict | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """One draft block (layer) as seven C-ABI calls: rmsnorm, the fused qkv
-    projection, attention, o with the residual, rmsnorm, the fused gate/up
-    projection, the SiLU gate, and down with the residual. w holds bf16
-    tensors qkv [3d, d], o [d, d], gate_up [2F, d], down [d, F], ln1, ln2 [d].
-    ``scratch`` (dict of fp32 buffers x, qkv, attn, h2, gu, act and the
-    attention workspace) is reused when given; ``out`` may be h itself."""
+    """One draft block (layer) in one C-ABI call (dspark_draft_block): rmsnorm,
+    the fused qkv projection, attention, o with the residual, rmsnorm, the
+    fused gate/up projection, the SiLU gate, and down with the residual. w
+    holds bf16 tensors qkv [3 H Dh, d], o [d, H Dh], gate_up [2F, d],
+    down [d, F], ln1, ln2 [d]. ``scratch`` (a dict) keeps the workspace
+    between calls; ``out`` may be h itself."""
     M, d = h.shape
     F = w["down"].shape[1]
+    _dev(h, torch.float32, "h", 2)
+    for name in ("qkv", "o", "gate_up", "down", "ln1", "ln2"):
+        _dev(w[name], torch.bfloat16, name, 2 if name not in ("ln1", "ln2") else 1)
+    _dev(k_ctx, torch.bfloat16, "k_ctx", 3)
+    _dev(v_ctx, torch.bfloat16, "v_ctx", 3)
+    _dev(ctx_len, torch.int32, "ctx_len", 1)
+    if M != R * B or k_ctx.shape[0] != R or v_ctx.shape != k_ctx.shape or k_ctx.shape[2] != H * Dh:
+        raise ValueError("h [R * B, d] and k_ctx, v_ctx [R, Lmax, H Dh] required")
+    Lmax = k_ctx.shape[1]
+    n = draft_block_workspace_bytes(R, B, H, Dh, d, F, Lmax)
     sc = scratch if scratch is not None else {}
-    dev = h.device
+    if "ws" not in sc or sc["ws"].numel() < n + 256:
+        sc["ws"] = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device=h.device)
+    ws = sc["ws"]
+    off = (-ws.data_ptr()) % 256
+    if out is None:
+        out = torch.empty_like(h)
+    _dev(out, torch.float32, "out", 2)
+    _check(lib().dspark_draft_block(w["qkv"].data_ptr(), w["o"].data_ptr(), w["gate_up"].data_ptr(),
+                                    w["down"].data_ptr(), w["ln1"].data_ptr(), w["ln2"].data_ptr(), d, F, H, Dh, R,
+                                    B, h.data_ptr(), out.data_ptr(), k_ctx.data_ptr(), v_ctx.data_ptr(), Lmax,
+                                    ctx_len.data_ptr(), float(eps), 1 if block_causal else 0, ws.data_ptr() + off,
+                                    ws.numel() - off, _stream(h)))
+    return out
 
-    def buf(name, shape):
-        if name not in sc or tuple(sc[name].shape) != shape:
-            sc[name] = torch.empty(shape, dtype=torch.float32, device=dev)
-        return sc[name]
-    x = rmsnorm(h, w["ln1"], eps, out=buf("x", (M, d)))
-    qkv = proj_smallm(w["qkv"], x, out=buf("qkv", (M, 3 * d)))
-    nws = max(attention_workspace_bytes(R, B, H, Dh, k_ctx.shape[1]), 16)
-    if "attn_ws" not in sc or sc["attn_ws"].numel() < nws:
-        sc["attn_ws"] = torch.empty(nws, dtype=torch.uint8, device=dev)
-    attn = attention_ragged(qkv, R, B, H, Dh, k_ctx, v_ctx, ctx_len, block_causal, out=buf("attn", (M, d)),
-                            workspace=sc["attn_ws"])
-    h2 = proj_smallm_add(w["o"], attn, h, out=buf("h2", (M, d)))
-    x2 = rmsnorm(h2, w["ln2"], eps, out=buf("x", (M, d)))
-    gu = proj_smallm(w["gate_up"], x2, out=buf("gu", (M, 2 * F)))
-    act = silu_gate(gu, out=buf("act", (M, F)))
+
+def draft_forward(x_in: torch.Tensor, fc: torch.Tensor, layers: list, k_ctx: list, v_ctx: list, R: int, B: int,
+                  H: int, Dh: int, ctx_len: torch.Tensor, norm: torch.Tensor, eps: float, block_causal: bool = False,
+                  scratch: dict | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The drafter's forward up to the lm_head's input: h = x_in fc^T
+    (dspark_proj_smallm), each block in order (dspark_draft_block, with its
+    own context cache), then the final norm (dspark_rmsnorm). Returns the
+    normed hidden states [R * B, d]."""
+    sc = scratch if scratch is not None else {}
+    M, d = x_in.shape[0], fc.shape[0]
+    if "h" not in sc or tuple(sc["h"].shape) != (M, d):
+        sc["h"] = torch.empty((M, d), dtype=torch.float32, device=x_in.device)
+    h = proj_smallm(fc, x_in, out=sc["h"])
+    for w, kc, vc in zip(layers, k_ctx, v_ctx):
+        draft_block_forward(h, w, R, B, H, Dh, kc, vc, ctx_len, eps, block_causal, scratch=sc, out=h)
+    return rmsnorm(h, norm, eps, out=out)
+
+
+def draft_block_forward_calls(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor,
+                              v_ctx: torch.Tensor, ctx_len: torch.Tensor, eps: float, block_causal: bool = False,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    """The same block as eight separate C-ABI calls (rmsnorm, proj_smallm,
+    attention_ragged, proj_smallm_add, rmsnorm, proj_smallm, silu_gate,
+    proj_smallm_add); dspark_draft_block must match it bit for bit."""
+    M, d = h.shape
+    F = w["down"].shape[1]
+    x = rmsnorm(h, w["ln1"], eps)
+    qkv = proj_smallm(w["qkv"], x)
+    attn = attention_ragged(qkv, R, B, H, Dh, k_ctx, v_ctx, ctx_len, block_causal)
+    h2 = proj_smallm_add(w["o"], attn, h)
+    x2 = rmsnorm(h2, w["ln2"], eps)
+    gu = proj_smallm(w["gate_up"], x2)
+    act = silu_gate(gu)
     return proj_smallm_add(w["down"], act, h2, out=out if out is not None else torch.empty_like(h))
 
 

@@ -320,6 +320,23 @@ def block_inputs(R: int, B: int, H: int, Dh: int, F: int, Lmax: int, ctx_len, se
                 R=R, B=B, H=H, Dh=Dh, F=F, d=d, Lmax=Lmax, eps=np.float32(1e-6))
 
 
+def draft_forward_inputs(R: int, B: int, H: int, Dh: int, F: int, Lmax: int, ctx_len, layers: int, n_fc: int,
+                         seed: int) -> dict:
+    """A drafter of ``layers`` blocks at M = R * B: the blocks of block_inputs
+    (weights and a context cache per block), fc bf16 [d, n_fc d] ~ N(0, 0.02^2)
+    and its input x_in [R * B, n_fc d] ~ N(0, 1), and a final norm gain
+    norm [d] ~ 1 + N(0, 0.1^2) in bf16."""
+    d = H * Dh
+    blk = block_inputs(R, B, H, Dh, F, Lmax, ctx_len, seed, copies=layers)
+    k_ctx = [blk["k_ctx"]] + [normal_bf16(seed, S_LAYER + 16 * (60 + c), (R, Lmax, d), 1.0) for c in range(1, layers)]
+    v_ctx = [blk["v_ctx"]] + [normal_bf16(seed, S_LAYER + 16 * (60 + c) + 1, (R, Lmax, d), 1.0)
+                              for c in range(1, layers)]
+    fc = normal_bf16(seed, S_LAYER + 16 * 58, (d, n_fc * d))
+    x_in = normal_f32(seed, S_LAYER + 16 * 58 + 1, (R * B, n_fc * d))
+    norm = bf16_bits_rne(1.0 + normal_f32(seed, S_LAYER + 16 * 58 + 2, (d,), 0.1))
+    return dict(blk, k_ctx=k_ctx, v_ctx=v_ctx, fc=fc, x_in=x_in, norm=norm, n_fc=n_fc)
+
+
 def fused_layer(ws: dict) -> dict:
     """The same layer with the projections that share an input concatenated
     along N: qkv [3 * 4096, 4096] (rows q, then k, then v) and gate_up

@@ -394,6 +394,47 @@ dspark_status dspark_attention_ragged(const float* q, const float* k, const floa
                                       int Lmax, const int32_t* ctx_len, int block_causal, float* out,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dspark_draft_block -- one whole draft block (layer) at small M, as the
+ * composition of the entry points above on one stream:
+ *   x    = rmsnorm(h_in, ln1)                       (dspark_rmsnorm)
+ *   qkv  = x W_qkv^T                                (dspark_proj_smallm)
+ *   a    = attention(qkv, context)                  (dspark_attention_ragged)
+ *   h2   = h_in + a W_o^T                           (dspark_proj_smallm_add)
+ *   x    = rmsnorm(h2, ln2)
+ *   gu   = x W_gate_up^T
+ *   act  = silu(gu[:, :F]) * gu[:, F:]              (dspark_silu_gate)
+ *   h_out = h2 + act W_down^T
+ * [SI441] "Observation" lists the block's projections (q/k/v/o, gate/up/down)
+ * and its attention over a short context; the norms, the gated MLP and the
+ * residuals are the plainest reading of a Qwen3-derived drafter. Results are
+ * bit-identical to making the eight calls one by one.
+ *
+ *   w_qkv      bf16 [3 H Dh, d]: q rows, then k rows, then v rows
+ *   w_o        bf16 [d, H Dh]
+ *   w_gate_up  bf16 [2F, d]: gate rows, then up rows
+ *   w_down     bf16 [d, F]
+ *   ln1, ln2   bf16 [d]
+ *   h_in       fp32 [num_reqs * B, d]; h_out fp32 [num_reqs * B, d], may be h_in
+ *   k_ctx, v_ctx, Lmax, ctx_len, block_causal   as for dspark_attention_ragged
+ *   workspace  at least dspark_draft_block_workspace_bytes(...) bytes, 256-byte
+ *              aligned, caller-owned; holds the intermediate activations, no
+ *              clearing needed; calls that share it must be ordered
+ * Alignment: weights, h_in, h_out, k_ctx, v_ctx 16 bytes; ln1, ln2 2 bytes.
+ * Sizes: d % 8 == 0, F % 8 == 0, the attention's limits, and every
+ * projection within dspark_proj_smallm's. eps >= 0.
+ * Errors: DSPARK_ERR_NULL, _SHAPE, _WORKSPACE, _ALIGN before anything is
+ * enqueued; DSPARK_ERR_HIP if a launch fails (earlier launches of the call
+ * stay enqueued).
+ */
+size_t dspark_draft_block_workspace_bytes(int num_reqs, int B, int H, int Dh, int d, int F, int Lmax);
+dspark_status dspark_draft_block(const uint16_t* w_qkv, const uint16_t* w_o, const uint16_t* w_gate_up,
+                                 const uint16_t* w_down, const uint16_t* ln1, const uint16_t* ln2, int d,
+                                 int F, int H, int Dh, int num_reqs, int B, const float* h_in, float* h_out,
+                                 const uint16_t* k_ctx, const uint16_t* v_ctx, int Lmax,
+                                 const int32_t* ctx_len, float eps, int block_causal, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

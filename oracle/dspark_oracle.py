@@ -381,6 +381,23 @@ def draft_block_forward(h, w: dict, R: int, B: int, H: int, Dh: int, k_ctx_bits,
     return h2 + (g / (1.0 + np.exp(-g)) * u) @ bf16_to_f64(w["down"]).T
 
 
+def draft_forward(x_in, fc_bits, layers, k_ctx_list, v_ctx_list, ctx_len, norm_bits, eps: float, R: int, B: int,
+                  H: int, Dh: int, block_causal: bool = False):
+    """The drafter's forward at small M = R * B, up to the hidden states the
+    lm_head reads: h = x_in fc^T, then each block in order (each with its own
+    context cache), then a final rmsnorm.
+
+    [SI441] "Observation" lists fc among the drafter's projections and the
+    block stack around it; the final norm is the plainest reading of a
+    Qwen3-derived drafter. The hidden state handed from one block to the
+    next is float32 (the blocks' input type), rounded once per hand-over;
+    inside a block everything stays float64."""
+    h = gemv(fc_bits, x_in)
+    for w, kc, vc in zip(layers, k_ctx_list, v_ctx_list):
+        h = draft_block_forward(h.astype(np.float32), w, R, B, H, Dh, kc, vc, ctx_len, eps, block_causal)
+    return rmsnorm(h.astype(np.float32), norm_bits, eps)
+
+
 def rmsnorm_f64(x64, gamma_bits, eps: float):
     """rmsnorm on float64 inputs (the block's second norm reads a float64 sum)."""
     g = bf16_to_f64(gamma_bits)

@@ -275,3 +275,28 @@ def test_binding_has_no_cpu_path(L):
         ops.proj_smallm(W, X)
     with pytest.raises(ValueError, match="GPU tensor"):
         ops.conf_probe(X, torch.zeros(64, dtype=torch.bfloat16))
+
+
+def test_draft_block_rejects_bad_arguments(L):
+    need = L.dspark_draft_block_workspace_bytes(1, 7, 32, 128, 4096, 12288, 512)
+    assert need > 0
+    assert L.dspark_draft_block_workspace_bytes(1, 7, 32, 128, 4096, 12283, 512) == 0     # F % 8 != 0
+    ok = dict(wqkv=A, wo=A2, wgu=A, wd=A2, ln1=A, ln2=A2, d=4096, F=12288, H=32, Dh=128, R=1, B=7, hin=A, hout=A2,
+              kc=A, vc=A2, Lmax=512, lens=A, eps=1e-6, c=0, ws=A, nws=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.dspark_draft_block(a["wqkv"], a["wo"], a["wgu"], a["wd"], a["ln1"], a["ln2"], a["d"], a["F"], a["H"],
+                                    a["Dh"], a["R"], a["B"], a["hin"], a["hout"], a["kc"], a["vc"], a["Lmax"],
+                                    a["lens"], a["eps"], a["c"], a["ws"], a["nws"], None)
+    assert call(wo=None) == ERR_NULL
+    assert call(ln2=None) == ERR_NULL
+    assert call(vc=None) == ERR_NULL
+    assert call(d=4092) == ERR_SHAPE
+    assert call(B=17) == ERR_SHAPE
+    assert call(eps=-1.0) == ERR_SHAPE
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(nws=need - 1) == ERR_WORKSPACE
+    assert call(ws=A + 16) == ERR_ALIGN                  # the workspace needs 256-byte alignment
+    assert call(hin=A + 4) == ERR_ALIGN
+    assert call(ln1=A + 1) == ERR_ALIGN

@@ -829,6 +829,63 @@ def test_draft_block_forward_matches_oracle(dev, R, B, H, Dh, F, Lmax, lens):
     logits_close(y.cpu().numpy(), ref, f"draft block d={H * Dh}")
 
 
+@pytest.mark.parametrize("R,B,H,Dh,F,Lmax,lens,causal", [(1, 7, 32, 128, 12288, 512, [512], False),
+                                                         (2, 4, 4, 64, 1024, 96, [96, 20], True)])
+def test_draft_block_single_call_equals_calls(dev, R, B, H, Dh, F, Lmax, lens, causal):
+    """dspark_draft_block gives the bits of its eight entry points called one
+    by one, also when h_out is h_in."""
+    seed = 7600 + H * Dh + F
+    say(f"[draft block one call] R={R} B={B} H={H} Dh={Dh} F={F} Lmax={Lmax} lens={lens} causal={causal} seed={seed}")
+    ops = _ops()
+    inp = synth.block_inputs(R, B, H, Dh, F, Lmax, lens, seed)
+    w = {k: _bf(v, dev) for k, v in inp["layers"][0].items()}
+    kc = _bf(inp["k_ctx"], dev).view(R, Lmax, H * Dh)
+    vc = _bf(inp["v_ctx"], dev).view(R, Lmax, H * Dh)
+    ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+    h = _up(inp["h"], dev)
+    eps = float(inp["eps"])
+    one = ops.draft_block_forward(h, w, R, B, H, Dh, kc, vc, ln, eps, causal)
+    calls = ops.draft_block_forward_calls(h, w, R, B, H, Dh, kc, vc, ln, eps, causal)
+    inplace = h.clone()
+    ops.draft_block_forward(inplace, w, R, B, H, Dh, kc, vc, ln, eps, causal, out=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(one, calls)
+    assert torch.equal(one, inplace)
+
+
+@pytest.mark.parametrize("R,B,H,Dh,F,Lmax,lens,layers,n_fc,V,r", [(2, 3, 2, 64, 256, 40, [40, 9], 3, 2, 1000, 16),
+                                                                 (1, 7, 32, 128, 12288, 512, [512], 2, 1, 4096, 256)])
+def test_draft_forward_round_matches_oracle(dev, R, B, H, Dh, F, Lmax, lens, layers, n_fc, V, r):
+    """A whole synthetic draft round: fc, the blocks (each with its own
+    context cache), the final norm, then dspark_draft_round on the result;
+    hidden states, logits, ids and probe against the fp64 oracle."""
+    seed = 7700 + layers * 10 + n_fc
+    d = H * Dh
+    k = B
+    say(f"[draft forward + round] R={R} B={B} d={d} F={F} layers={layers} n_fc={n_fc} V={V} r={r} seed={seed}")
+    ops = _ops()
+    inp = synth.draft_forward_inputs(R, B, H, Dh, F, Lmax, lens, layers, n_fc, seed)
+    W_lm, _ = synth.gemv_inputs(1, V, d, seed)
+    _, w1, w2, prev0, _ = synth.markov_inputs(R, 1, V, r, seed)
+    _, pw = synth.probe_inputs(1, d, seed)
+    eps = float(inp["eps"])
+    hid = ops.draft_forward(_up(inp["x_in"], dev), _bf(inp["fc"], dev),
+                            [{kk: _bf(v, dev) for kk, v in w.items()} for w in inp["layers"]],
+                            [_bf(c, dev).view(R, Lmax, d) for c in inp["k_ctx"]],
+                            [_bf(c, dev).view(R, Lmax, d) for c in inp["v_ctx"]], R, B, H, Dh,
+                            torch.tensor(lens, dtype=torch.int32, device=dev), _bf(inp["norm"], dev), eps)
+    out = ops.draft_round(_bf(W_lm, dev), hid, _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), B, k,
+                          probe_w=_bf(pw, dev), probe_bias=0.0, probe_threshold=0.0)
+    torch.cuda.synchronize()
+    ref_h = oracle.draft_forward(inp["x_in"], inp["fc"], inp["layers"], inp["k_ctx"], inp["v_ctx"], inp["ctx_len"],
+                                 inp["norm"], eps, R, B, H, Dh)
+    logits_close(hid.cpu().numpy(), ref_h, f"draft forward hidden ({layers} blocks)")
+    ref = oracle.draft_round(W_lm, ref_h.astype(np.float32), w1, w2, prev0, R, B, k, pw, 0.0, 0.0)
+    logits_close(out["base"].view(R * B, -1).cpu().numpy(), ref["base"], "draft forward round logits")
+    check_markov(out["ids"].cpu().numpy(), ref["base32"], w1, w2, prev0, k)
+    probe_close(out["logit"].cpu().numpy(), out["passed"].cpu().numpy(), ref["logit"], ref["passed"], 0.0)
+
+
 def test_round_graph_replay(dev):
     """The whole round recorded once in a HIP graph and replayed, with eager
     work between replays: every replay equals the eager result."""

@@ -100,3 +100,31 @@ def test_block_forward_pins():
     dbl = synth.bf16_bits_rne(((w["down"].astype(np.uint32) << 16).view(np.float32) * 2).astype(np.float32))
     y2 = oracle.draft_block_forward(inp["h"], dict(w, down=dbl), *args)
     assert np.allclose(y2 - h2, 2 * (y1 - h2), rtol=1e-12, atol=1e-12)
+
+
+def test_draft_forward_pins():
+    """The drafter's forward: with fc the identity and no blocks it is the
+    final rmsnorm of its input; a block whose o and down are zero passes its
+    input through, so prepending one changes nothing, and the blocks after it
+    still read their own context caches in order; the output is linear in the
+    final norm's gain."""
+    from gemv_markov_argmax_amd import synth
+    R, B, H, Dh, F, Lmax = 2, 3, 2, 8, 24, 6
+    inp = synth.draft_forward_inputs(R, B, H, Dh, F, Lmax, [6, 2], layers=2, n_fc=1, seed=21)
+    d = H * Dh
+    eye = synth.bf16_bits_rne(np.eye(d, dtype=np.float32))
+    x = inp["x_in"]
+    y = oracle.draft_forward(x, eye, [], [], [], inp["ctx_len"], inp["norm"], 1e-6, R, B, H, Dh)
+    assert np.array_equal(y, oracle.rmsnorm(x, inp["norm"], 1e-6))
+    w0, w1 = inp["layers"]
+    ident = dict(w0, o=np.zeros_like(w0["o"]), down=np.zeros_like(w0["down"]))
+    args = (inp["ctx_len"], inp["norm"], 1e-6, R, B, H, Dh)
+    one = oracle.draft_forward(x, inp["fc"], [w1], [inp["k_ctx"][1]], [inp["v_ctx"][1]], *args)
+    two = oracle.draft_forward(x, inp["fc"], [ident, w1], inp["k_ctx"], inp["v_ctx"], *args)
+    assert np.array_equal(one, two)
+    swapped = oracle.draft_forward(x, inp["fc"], [ident, w1], inp["k_ctx"][::-1], inp["v_ctx"][::-1], *args)
+    assert not np.allclose(one, swapped)
+    dbl = synth.bf16_bits_rne(2 * (inp["norm"].astype(np.uint32) << 16).view(np.float32))
+    twice = oracle.draft_forward(x, inp["fc"], [w1], [inp["k_ctx"][1]], [inp["v_ctx"][1]], inp["ctx_len"], dbl,
+                                 1e-6, R, B, H, Dh)
+    assert np.array_equal(twice, 2 * one)
