@@ -94,7 +94,9 @@ struct AttnParams {
   float* out;  // [R * B, H * Dh]
 };
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 256;                     // merge kernel
+constexpr int kChunkWaves = 8;                        // chunk kernel: eight waves share a chunk's work
+constexpr int kChunkThreads = kChunkWaves * 64;
 constexpr int kAttnMaxB = 16;
 constexpr int kAttnMaxDh = 256;
 constexpr int kAttnChunk = 64;  // keys per workgroup: one per lane of a wave
@@ -153,20 +155,21 @@ __device__ __forceinline__ void convert_kv8(const Raw8& raw, bool ctx, bool live
 //     together and coalesced: unit e = tid + 256 u is (key e / (Dh / 8),
 //     8-dim group e % (Dh / 8)), so consecutive lanes read consecutive bytes
 //     of a key's row. q and the keys go to LDS (key rows padded by 4 floats).
-//  2. Scores: lane l of wave w takes key 64c + l and sums the dims of groups
-//     w, w + 4, ... (8 dims each, in order) against every position (q
-//     broadcast from LDS); the four wave partials are added as
-//     (w0 + w1) + (w2 + w3). The values then replace the keys in LDS.
-//  3. Per position (wave w takes positions w, w + 4, ...): chunk maximum and
-//     the sum of exp over visible keys, a fixed butterfly over the lanes.
-//  4. o_c: thread (d, kg) sums keys kg, kg + KG, ... in order (KG = 256 / Dh
+//  2. Scores: lane l of wave w (eight waves) takes key 64c + l and sums the
+//     dims of groups w, w + 8, ... (8 dims each, in order) against every
+//     position (q broadcast from LDS); the wave partials are added pairwise,
+//     ((w0 + w1) + (w2 + w3)) + ((w4 + w5) + (w6 + w7)). The values then
+//     replace the keys in LDS.
+//  3. Per position (wave w takes positions w, w + 8): chunk maximum and the
+//     sum of exp over visible keys, a fixed butterfly over the lanes.
+//  4. o_c: thread (d, kg) sums keys kg, kg + KG, ... in order (KG = 512 / Dh
 //     key groups), the groups then in kg order.
-__global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParams p, float* __restrict__ ws, int NC) {
+__global__ __launch_bounds__(kChunkThreads) void attention_chunk_kernel(AttnParams p, float* __restrict__ ws, int NC) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int B = p.B, Dh = p.Dh, NG = Dh / 8, KS = Dh + 4;
   float* qs = reinterpret_cast<float*>(smem);   // [B][Dh]
-  float* Sp = qs + B * Dh;                      // [4][B][64] score partials, later [KG][B][Dh]
-  float* Pt = Sp + 4 * B * kAttnChunk;          // [64][16]: probabilities, key-major
+  float* Sp = qs + B * Dh;                      // [8][B][64] score partials, later [KG][B][Dh]
+  float* Pt = Sp + kChunkWaves * B * kAttnChunk;  // [64][16]: probabilities, key-major
   float* KV = Pt + kAttnChunk * kAttnMaxB;      // [64][Dh + 4]: keys, then values
   const int c = blockIdx.x % NC, rh = blockIdx.x / NC, r = rh / p.H, h = rh - r * p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -176,20 +179,20 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
   const int nj = min(kAttnChunk, Lk - j0);
 
   // 1. loads: keys and values (all in flight together), then q into LDS
-  constexpr int kU = kAttnChunk * kAttnMaxDh / 8 / kAttnThreads;  // units per thread, at most
+  constexpr int kU = kAttnChunk * kAttnMaxDh / 8 / kChunkThreads;  // units per thread, at most
   Raw8 kraw[kU], vraw[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const int e = tid + u * kAttnThreads, jj = e / NG, g = e - jj * NG;
+    const int e = tid + u * kChunkThreads, jj = e / NG, g = e - jj * NG;
     kraw[u] = issue_kv8(p.kc, p.kb, p, r, h, L, j0 + jj, g, jj < nj);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const int e = tid + u * kAttnThreads, jj = e / NG, g = e - jj * NG;
+    const int e = tid + u * kChunkThreads, jj = e / NG, g = e - jj * NG;
     vraw[u] = issue_kv8(p.vc, p.vb, p, r, h, L, j0 + jj, g, jj < nj);
   }
   const int D4 = Dh / 4;
-  for (int e0 = 0; e0 < B * D4; e0 += kAttnThreads) {  // one pass per 256 float4 units of q
+  for (int e0 = 0; e0 < B * D4; e0 += kChunkThreads) {  // one pass per 512 float4 units of q
     const int e = e0 + tid;
     if (e < B * D4) {
       const int i = e / D4, d4 = e - i * D4;
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
   auto stage = [&](const Raw8* raw) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int e = tid + u * kAttnThreads, jj = e / NG, g = e - jj * NG;
+      const int e = tid + u * kChunkThreads, jj = e / NG, g = e - jj * NG;
       if (jj < kAttnChunk) {
         float f[8];
         convert_kv8(raw[u], j0 + jj < L, jj < nj, f);
@@ -219,24 +222,35 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
 #pragma unroll
     for (int i = 0; i < kAttnMaxB; ++i) s[i] = 0.f;
     const float* kr = KV + lane * KS;
-    for (int g = w; g < NG; g += 4) {
+    for (int g = w; g < NG; g += kChunkWaves) {
       const float4 ka = *reinterpret_cast<const float4*>(kr + 8 * g);
       const float4 kb = *reinterpret_cast<const float4*>(kr + 8 * g + 4);
-      // Positions are guarded, not broken out of, so that the loop unrolls
-      // with s[] in fixed registers.
+      // Positions in batches of four: one uniform branch per batch, whose
+      // eight LDS reads are issued together, and s[] in fixed registers.
+      // Slots past B in the last batch read past q (still inside this
+      // workgroup's LDS) and are never stored.
 #pragma unroll
-      for (int i = 0; i < kAttnMaxB; ++i) {
-        if (i < B) {  // uniform
-          const float4 qa = *reinterpret_cast<const float4*>(qs + i * Dh + 8 * g);
-          const float4 qb = *reinterpret_cast<const float4*>(qs + i * Dh + 8 * g + 4);
-          s[i] = __builtin_fmaf(qa.x, ka.x, s[i]);
-          s[i] = __builtin_fmaf(qa.y, ka.y, s[i]);
-          s[i] = __builtin_fmaf(qa.z, ka.z, s[i]);
-          s[i] = __builtin_fmaf(qa.w, ka.w, s[i]);
-          s[i] = __builtin_fmaf(qb.x, kb.x, s[i]);
-          s[i] = __builtin_fmaf(qb.y, kb.y, s[i]);
-          s[i] = __builtin_fmaf(qb.z, kb.z, s[i]);
-          s[i] = __builtin_fmaf(qb.w, kb.w, s[i]);
+      for (int i0 = 0; i0 < kAttnMaxB; i0 += 4) {
+        if (i0 < B) {
+          float4 qa[4], qb[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            qa[u] = *reinterpret_cast<const float4*>(qs + (i0 + u) * Dh + 8 * g);
+            qb[u] = *reinterpret_cast<const float4*>(qs + (i0 + u) * Dh + 8 * g + 4);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float t = s[i0 + u];
+            t = __builtin_fmaf(qa[u].x, ka.x, t);
+            t = __builtin_fmaf(qa[u].y, ka.y, t);
+            t = __builtin_fmaf(qa[u].z, ka.z, t);
+            t = __builtin_fmaf(qa[u].w, ka.w, t);
+            t = __builtin_fmaf(qb[u].x, kb.x, t);
+            t = __builtin_fmaf(qb[u].y, kb.y, t);
+            t = __builtin_fmaf(qb[u].z, kb.z, t);
+            t = __builtin_fmaf(qb[u].w, kb.w, t);
+            s[i0 + u] = t;
+          }
         }
       }
     }
@@ -250,11 +264,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
   // 3. chunk softmax statistics
   const float scale = 1.0f / sqrtf(static_cast<float>(Dh));
   const size_t wbase = attn_ws_index(r, h, c, p.H, NC, B, Dh);
-  for (int i = w; i < B; i += kAttnThreads / kWave) {
+  for (int i = w; i < B; i += kChunkThreads / kWave) {
     const int jj = lane, j = j0 + jj;
     const bool vis = jj < nj && (!p.causal || j <= L + i);
-    const float sc = ((Sp[(0 * B + i) * kAttnChunk + jj] + Sp[(1 * B + i) * kAttnChunk + jj]) +
-                      (Sp[(2 * B + i) * kAttnChunk + jj] + Sp[(3 * B + i) * kAttnChunk + jj])) * scale;
+    const float* si = Sp + i * kAttnChunk + jj;
+    const int wstride = B * kAttnChunk;
+    const float sc = (((si[0] + si[wstride]) + (si[2 * wstride] + si[3 * wstride])) +
+                      ((si[4 * wstride] + si[5 * wstride]) + (si[6 * wstride] + si[7 * wstride]))) * scale;
     float mx = vis ? sc : -INFINITY;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -271,8 +287,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
   __syncthreads();
 
   // 4. o_c
-  const int KG = kAttnThreads / Dh;
-  float* Op = Sp;  // [KG][B][Dh]: KG * Dh <= 256, so it fits the partials' space
+  const int KG = kChunkThreads / Dh;
+  float* Op = Sp;  // [KG][B][Dh]: KG * Dh <= 512, so it fits the partials' space
   if (tid < KG * Dh) {
     const int d = tid % Dh, kg = tid / Dh;
     float o[kAttnMaxB];
@@ -283,14 +299,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
       const float v = KV[jj * KS + d];
       const float* pj = Pt + jj * kAttnMaxB;  // the key's probabilities, read 4 positions at a time
 #pragma unroll
-      for (int i4 = 0; i4 < kAttnMaxB; i4 += 4) {
-        if (i4 < B) {  // uniform; lanes of positions past B hold unused values
-          const float4 pv = *reinterpret_cast<const float4*>(pj + i4);
-          o[i4] = __builtin_fmaf(pv.x, v, o[i4]);
-          o[i4 + 1] = __builtin_fmaf(pv.y, v, o[i4 + 1]);
-          o[i4 + 2] = __builtin_fmaf(pv.z, v, o[i4 + 2]);
-          o[i4 + 3] = __builtin_fmaf(pv.w, v, o[i4 + 3]);
-        }
+      for (int i4 = 0; i4 < kAttnMaxB; i4 += 4) {  // all 16 slots, no branch; slots past B are never stored
+        const float4 pv = *reinterpret_cast<const float4*>(pj + i4);
+        o[i4] = __builtin_fmaf(pv.x, v, o[i4]);
+        o[i4 + 1] = __builtin_fmaf(pv.y, v, o[i4 + 1]);
+        o[i4 + 2] = __builtin_fmaf(pv.z, v, o[i4 + 2]);
+        o[i4 + 3] = __builtin_fmaf(pv.w, v, o[i4 + 3]);
       }
     }
 #pragma unroll
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(AttnParam
       if (i < B) Op[(kg * B + i) * Dh + d] = o[i];
   }
   __syncthreads();
-  for (int e = tid; e < B * Dh; e += kAttnThreads) {
+  for (int e = tid; e < B * Dh; e += kChunkThreads) {
     float t = Op[e];
     for (int kg = 1; kg < KG; ++kg) t += Op[kg * B * Dh + e];
     ws[wbase + 2 * B + e] = t;
@@ -362,7 +376,7 @@ hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t
 int attention_chunks(int B, int Lmax) { return (Lmax + B + kAttnChunk - 1) / kAttnChunk; }
 
 size_t attention_lds_bytes(int B, int Dh) {
-  return static_cast<size_t>(B * Dh + 4 * B * kAttnChunk + kAttnChunk * kAttnMaxB + kAttnChunk * (Dh + 4)) * 4;
+  return static_cast<size_t>(B * Dh + kChunkWaves * B * kAttnChunk + kAttnChunk * kAttnMaxB + kAttnChunk * (Dh + 4)) * 4;
 }
 
 bool attention_shape_fits(int R, int B, int H, int Dh, int Lmax) {
@@ -386,7 +400,7 @@ hipError_t launch_attention(const float* q, const float* kb, const float* vb, in
   int NC = attention_chunks(B, Lmax);
   void* args[] = {&a, &ws, &NC};
   const long long grid = static_cast<long long>(R) * H * NC;
-  hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), args,
+  hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), args,
                                  attention_lds_bytes(B, Dh), st);
   if (e != hipSuccess) return e;
   const long long mgrid = static_cast<long long>(R) * H * ((B * Dh + kAttnThreads - 1) / kAttnThreads);
