@@ -149,30 +149,65 @@ __device__ __forceinline__ void convert_kv8(const Raw8& raw, bool ctx, bool live
   }
 }
 
-// One workgroup per (request, head, chunk of 64 keys); chunks past the
-// request's Lk exit at once.
+// LDS row strides (floats) of the chunk kernel, chosen so that the MFMA
+// operand reads below hit 64 distinct banks: q and the keys are read with
+// 16 lanes on 16 rows (stride = 4 mod 64), the values with 4 lanes groups on
+// 4 rows of 16 columns (stride = 16 mod 64, whole 16-column tiles).
+__host__ __device__ constexpr int attn_ks(int Dh) { return Dh + ((4 - Dh) % 64 + 64) % 64; }
+__host__ __device__ constexpr int attn_vs(int Dh) {
+  return (Dh + 15) / 16 * 16 + ((16 - (Dh + 15) / 16 * 16) % 64 + 64) % 64;
+}
+
+// Reductions over a wave on DPP moves (no LDS round trip): pairs, quads, half
+// rows and rows through lane permutes within a row of 16 (every lane of a
+// row then holds the row's result), then row 0 into row 1 and row 2 into
+// row 3, then rows 0-1 into rows 2-3; lane 63 holds the result, which is
+// read back as a scalar. The order is fixed, so the result is deterministic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+  const float id = MAX ? -INFINITY : 0.f;
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_move<0xb1, 0xf>(v, id));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_move<0x4e, 0xf>(v, id));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_move<0x141, 0xf>(v, id));  // row_half_mirror
+  v = op(v, dpp_move<0x140, 0xf>(v, id));  // row_mirror
+  v = op(v, dpp_move<0x142, 0xa>(v, id));  // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_move<0x143, 0xc>(v, id));  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// One workgroup of eight waves per (request, head, chunk of 64 keys); chunks
+// past the request's Lk exit at once. The chunk's two products run on
+// v_mfma_f32_16x16x4f32 (fp32 operands and accumulation; positions padded to
+// 16 rows, rows past B never stored):
 //  1. The chunk's keys and values and q are loaded first, all in flight
-//     together and coalesced: unit e = tid + 256 u is (key e / (Dh / 8),
+//     together and coalesced: unit e = tid + 512 u is (key e / (Dh / 8),
 //     8-dim group e % (Dh / 8)), so consecutive lanes read consecutive bytes
-//     of a key's row. q and the keys go to LDS (key rows padded by 4 floats).
-//  2. Scores: lane l of wave w (eight waves) takes key 64c + l and sums the
-//     dims of groups w, w + 8, ... (8 dims each, in order) against every
-//     position (q broadcast from LDS); the wave partials are added pairwise,
-//     ((w0 + w1) + (w2 + w3)) + ((w4 + w5) + (w6 + w7)). The values then
-//     replace the keys in LDS.
-//  3. Per position (wave w takes positions w, w + 8): chunk maximum and the
-//     sum of exp over visible keys, a fixed butterfly over the lanes.
-//  4. o_c: thread (d, kg) sums keys kg, kg + KG, ... in order (KG = 512 / Dh
-//     key groups), the groups then in kg order.
+//     of a key's row. q and the keys go to LDS.
+//  2. Scores S[16 x 64] = q k^T: wave w takes the 16 keys of tile w % 4 and
+//     half of the dims (w / 4), Dh / 8 MFMA steps of 4 dims in order; the two
+//     halves are added in step 3. The values then replace the keys in LDS.
+//  3. Per position (wave w takes positions w, w + 8): s = (half 0 + half 1)
+//     / sqrt(Dh), the chunk maximum and the sum of exp over visible keys
+//     (wave_reduce); the probabilities go to LDS.
+//  4. o_c[16 x Dh] = P V: wave w takes the 16-column tiles w, w + 8, ..., 16
+//     MFMA steps of 4 keys in order, stored straight to the workspace.
 __global__ __launch_bounds__(kChunkThreads) void attention_chunk_kernel(AttnParams p, float* __restrict__ ws, int NC) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int B = p.B, Dh = p.Dh, NG = Dh / 8, KS = Dh + 4;
-  float* qs = reinterpret_cast<float*>(smem);   // [B][Dh]
-  float* Sp = qs + B * Dh;                      // [8][B][64] score partials, later [KG][B][Dh]
-  float* Pt = Sp + kChunkWaves * B * kAttnChunk;  // [64][16]: probabilities, key-major
-  float* KV = Pt + kAttnChunk * kAttnMaxB;      // [64][Dh + 4]: keys, then values
+  const int B = p.B, Dh = p.Dh, NG = Dh / 8, KS = attn_ks(Dh), VS = attn_vs(Dh);
+  float* qs = reinterpret_cast<float*>(smem);      // [16][KS]: q rows (rows past B unused)
+  float* Sp = qs + kAttnMaxB * KS;                 // [2][16][64] score halves
+  float* Pt = Sp + 2 * kAttnMaxB * kAttnChunk;     // [64][16]: probabilities, key-major
+  float* KV = Pt + kAttnChunk * kAttnMaxB;         // [64][KS] keys, then [64][VS] values
   const int c = blockIdx.x % NC, rh = blockIdx.x / NC, r = rh / p.H, h = rh - r * p.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index as a scalar, so that the loops over a wave's share are
+  // uniform (scalar-controlled and unrolled, not exec-masked)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = min(max(p.ctx_len[r], 0), p.Lmax);
   const int Lk = L + B, j0 = c * kAttnChunk;
   if (j0 >= Lk) return;  // uniform over the workgroup
@@ -196,88 +231,62 @@ __global__ __launch_bounds__(kChunkThreads) void attention_chunk_kernel(AttnPara
     const int e = e0 + tid;
     if (e < B * D4) {
       const int i = e / D4, d4 = e - i * D4;
-      *reinterpret_cast<float4*>(qs + 4 * e) =
+      *reinterpret_cast<float4*>(qs + i * KS + 4 * d4) =
           *reinterpret_cast<const float4*>(p.q + static_cast<size_t>(r * B + i) * p.ld + h * Dh + 4 * d4);
     }
   }
-  auto stage = [&](const Raw8* raw) {
+  auto stage = [&](const Raw8* raw, int stride) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int e = tid + u * kChunkThreads, jj = e / NG, g = e - jj * NG;
       if (jj < kAttnChunk) {
         float f[8];
         convert_kv8(raw[u], j0 + jj < L, jj < nj, f);
-        float* dst = KV + jj * KS + 8 * g;
+        float* dst = KV + jj * stride + 8 * g;
         *reinterpret_cast<float4*>(dst) = float4{f[0], f[1], f[2], f[3]};
         *reinterpret_cast<float4*>(dst + 4) = float4{f[4], f[5], f[6], f[7]};
       }
     }
   };
-  stage(kraw);
+  stage(kraw, KS);
   __syncthreads();
 
-  // 2. score partials
+  // 2. scores: A = q [16 x 4] (lane: row l % 16, dim l / 16), B = k^T [4 x 16]
+  //    (lane: dim l / 16, key l % 16); D rows 4 (l / 16) + v, key l % 16
+  const int li = lane & 15, lk = lane >> 4;
   {
-    float s[kAttnMaxB];
+    const int t = w & 3, half = w >> 2, steps = Dh / 8, s0 = half * steps;
+    const float* qa = qs + li * KS + lk;
+    const float* kb = KV + (16 * t + li) * KS + lk;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int st = s0;
+    for (; st + 4 <= s0 + steps; st += 4) {  // four steps' operands read before their MFMAs
+      float a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < kAttnMaxB; ++i) s[i] = 0.f;
-    const float* kr = KV + lane * KS;
-    for (int g = w; g < NG; g += kChunkWaves) {
-      const float4 ka = *reinterpret_cast<const float4*>(kr + 8 * g);
-      const float4 kb = *reinterpret_cast<const float4*>(kr + 8 * g + 4);
-      // Positions in batches of four: one uniform branch per batch, whose
-      // eight LDS reads are issued together, and s[] in fixed registers.
-      // Slots past B in the last batch read past q (still inside this
-      // workgroup's LDS) and are never stored.
-#pragma unroll
-      for (int i0 = 0; i0 < kAttnMaxB; i0 += 4) {
-        if (i0 < B) {
-          float4 qa[4], qb[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            qa[u] = *reinterpret_cast<const float4*>(qs + (i0 + u) * Dh + 8 * g);
-            qb[u] = *reinterpret_cast<const float4*>(qs + (i0 + u) * Dh + 8 * g + 4);
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float t = s[i0 + u];
-            t = __builtin_fmaf(qa[u].x, ka.x, t);
-            t = __builtin_fmaf(qa[u].y, ka.y, t);
-            t = __builtin_fmaf(qa[u].z, ka.z, t);
-            t = __builtin_fmaf(qa[u].w, ka.w, t);
-            t = __builtin_fmaf(qb[u].x, kb.x, t);
-            t = __builtin_fmaf(qb[u].y, kb.y, t);
-            t = __builtin_fmaf(qb[u].z, kb.z, t);
-            t = __builtin_fmaf(qb[u].w, kb.w, t);
-            s[i0 + u] = t;
-          }
-        }
+      for (int u = 0; u < 4; ++u) {
+        a[u] = qa[4 * (st + u)];
+        b[u] = kb[4 * (st + u)];
       }
-    }
 #pragma unroll
-    for (int i = 0; i < kAttnMaxB; ++i)
-      if (i < B) Sp[(w * B + i) * kAttnChunk + lane] = s[i];
+      for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc, 0, 0, 0);
+    }
+    for (; st < s0 + steps; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * st], kb[4 * st], acc, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Sp[(half * kAttnMaxB + 4 * lk + v) * kAttnChunk + 16 * t + li] = acc[v];
   }
   __syncthreads();  // the keys are consumed
-  stage(vraw);
+  stage(vraw, VS);
 
   // 3. chunk softmax statistics
   const float scale = 1.0f / sqrtf(static_cast<float>(Dh));
   const size_t wbase = attn_ws_index(r, h, c, p.H, NC, B, Dh);
-  for (int i = w; i < B; i += kChunkThreads / kWave) {
+  for (int i = w; i < B; i += kChunkWaves) {
     const int jj = lane, j = j0 + jj;
     const bool vis = jj < nj && (!p.causal || j <= L + i);
-    const float* si = Sp + i * kAttnChunk + jj;
-    const int wstride = B * kAttnChunk;
-    const float sc = (((si[0] + si[wstride]) + (si[2 * wstride] + si[3 * wstride])) +
-                      ((si[4 * wstride] + si[5 * wstride]) + (si[6 * wstride] + si[7 * wstride]))) * scale;
-    float mx = vis ? sc : -INFINITY;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float sc = (Sp[i * kAttnChunk + jj] + Sp[(kAttnMaxB + i) * kAttnChunk + jj]) * scale;
+    const float mx = wave_reduce<true>(vis ? sc : -INFINITY);
     const float e = vis ? expf(sc - mx) : 0.f;
-    float sum = e;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    const float sum = wave_reduce<false>(e);
     Pt[jj * kAttnMaxB + i] = e;
     if (lane == 0) {
       ws[wbase + i] = mx;
@@ -286,36 +295,22 @@ __global__ __launch_bounds__(kChunkThreads) void attention_chunk_kernel(AttnPara
   }
   __syncthreads();
 
-  // 4. o_c
-  const int KG = kChunkThreads / Dh;
-  float* Op = Sp;  // [KG][B][Dh]: KG * Dh <= 512, so it fits the partials' space
-  if (tid < KG * Dh) {
-    const int d = tid % Dh, kg = tid / Dh;
-    float o[kAttnMaxB];
+  // 4. o_c = P V: A = P [16 x 4] (lane: row l % 16, key l / 16: Pt[64 st + l]),
+  //    B = V [4 x 16] (lane: key l / 16, column l % 16)
+  const int NT = (Dh + 15) / 16;
+  for (int t = w; t < NT; t += kChunkWaves) {
+    const float* pa = Pt + lane;
+    const float* vb = KV + lk * VS + 16 * t + li;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kAttnMaxB; ++i) o[i] = 0.f;
-#pragma unroll 4
-    for (int jj = kg; jj < nj; jj += KG) {
-      const float v = KV[jj * KS + d];
-      const float* pj = Pt + jj * kAttnMaxB;  // the key's probabilities, read 4 positions at a time
+    for (int st = 0; st < kAttnChunk / 4; ++st)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[64 * st], vb[4 * st * VS], acc, 0, 0, 0);
+    const int col = 16 * t + li;
 #pragma unroll
-      for (int i4 = 0; i4 < kAttnMaxB; i4 += 4) {  // all 16 slots, no branch; slots past B are never stored
-        const float4 pv = *reinterpret_cast<const float4*>(pj + i4);
-        o[i4] = __builtin_fmaf(pv.x, v, o[i4]);
-        o[i4 + 1] = __builtin_fmaf(pv.y, v, o[i4 + 1]);
-        o[i4 + 2] = __builtin_fmaf(pv.z, v, o[i4 + 2]);
-        o[i4 + 3] = __builtin_fmaf(pv.w, v, o[i4 + 3]);
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int i = 4 * lk + v;
+      if (i < B && col < Dh) ws[wbase + 2 * B + i * Dh + col] = acc[v];
     }
-#pragma unroll
-    for (int i = 0; i < kAttnMaxB; ++i)
-      if (i < B) Op[(kg * B + i) * Dh + d] = o[i];
-  }
-  __syncthreads();
-  for (int e = tid; e < B * Dh; e += kChunkThreads) {
-    float t = Op[e];
-    for (int kg = 1; kg < KG; ++kg) t += Op[kg * B * Dh + e];
-    ws[wbase + 2 * B + e] = t;
   }
 }
 
@@ -376,7 +371,10 @@ hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t
 int attention_chunks(int B, int Lmax) { return (Lmax + B + kAttnChunk - 1) / kAttnChunk; }
 
 size_t attention_lds_bytes(int B, int Dh) {
-  return static_cast<size_t>(B * Dh + kChunkWaves * B * kAttnChunk + kAttnChunk * kAttnMaxB + kAttnChunk * (Dh + 4)) * 4;
+  (void)B;
+  const int ks = attn_ks(Dh), vs = attn_vs(Dh);
+  return static_cast<size_t>(kAttnMaxB * ks + 2 * kAttnMaxB * kAttnChunk + kAttnChunk * kAttnMaxB +
+                             kAttnChunk * (ks > vs ? ks : vs)) * 4;
 }
 
 bool attention_shape_fits(int R, int B, int H, int Dh, int Lmax) {
