@@ -738,7 +738,7 @@ def test_silu_gate_matches_oracle(dev, M, F):
     _close(a.cpu().numpy(), oracle.silu_gate(gu, F), f"silu gate M={M} F={F}", rtol=2e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("M,N,K", [(7, 4096, 4096), (7, 4096, 12288), (3, 1000, 264), (20, 515, 256)])
+@pytest.mark.parametrize("M,N,K", [(7, 4096, 4096), (7, 4096, 12288), (3, 1000, 264), (20, 515, 256), (90, 600, 512)])
 def test_proj_smallm_add(dev, M, N, K):
     """Y = residual + X W^T, also in place (residual = Y)."""
     seed = 7300 + M + N + K
@@ -810,7 +810,10 @@ def test_attention_workspace_needs_no_clearing(dev):
 
 
 @pytest.mark.parametrize("R,B,H,Dh,F,Lmax,lens", [(1, 7, 2, 128, 512, 64, [64]), (1, 7, 32, 128, 12288, 512, [512]),
-                                                  (2, 4, 4, 64, 1024, 96, [96, 20])])
+                                                  (2, 4, 4, 64, 1024, 96, [96, 20]),
+                                                  # M = 21 and M = 84: the small-GEMM path and its split launches
+                                                  (3, 7, 4, 64, 512, 80, [80, 33, 0]),
+                                                  (12, 7, 2, 64, 256, 40, [40, 1, 7, 13, 0, 40, 39, 2, 25, 31, 8, 16])])
 def test_draft_block_forward_matches_oracle(dev, R, B, H, Dh, F, Lmax, lens):
     """One whole draft block (rmsnorm, qkv, attention, o + residual, rmsnorm,
     gate/up, SiLU gate, down + residual) through the C ABI, against the fp64
