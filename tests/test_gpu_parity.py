@@ -920,3 +920,57 @@ def test_round_graph_replay(dev):
             assert torch.equal(a, b), f"replay {rep} differs"
         _ = ops.lm_head(t["W"], t["H"])  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_draft_forward_graph_replay(dev):
+    """fc, two blocks, the final norm and the round recorded once in a HIP
+    graph and replayed, with eager work between replays: every replay equals
+    the eager result (the attention and the block record no memset)."""
+    R, B, H, Dh, F, Lmax, lens, V, r = 2, 3, 2, 64, 256, 40, [40, 9], 1000, 16
+    seed = 7801
+    say(f"[draft forward graph replay] R={R} B={B} d={H * Dh} seed={seed}")
+    ops = _ops()
+    inp = synth.draft_forward_inputs(R, B, H, Dh, F, Lmax, lens, 2, 1, seed)
+    W_lm, _ = synth.gemv_inputs(1, V, H * Dh, seed)
+    _, w1, w2, prev0, _ = synth.markov_inputs(R, 1, V, r, seed)
+    _, pw = synth.probe_inputs(1, H * Dh, seed)
+    x_in, fc, norm = _up(inp["x_in"], dev), _bf(inp["fc"], dev), _bf(inp["norm"], dev)
+    layers = [{kk: _bf(v, dev) for kk, v in w.items()} for w in inp["layers"]]
+    kcs = [_bf(c, dev).view(R, Lmax, H * Dh) for c in inp["k_ctx"]]
+    vcs = [_bf(c, dev).view(R, Lmax, H * Dh) for c in inp["v_ctx"]]
+    ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+    Wl, w1d, w2d, p0, pwd = _bf(W_lm, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), _bf(pw, dev)
+    scratch = {}
+    hid = torch.empty(R * B, H * Dh, device=dev)
+    base = torch.empty(R, B, V, device=dev)
+    ids = torch.empty(R, B, dtype=torch.int64, device=dev)
+    lg = torch.empty(R * B, device=dev)
+    ps = torch.empty(R * B, dtype=torch.int32, device=dev)
+    mws = ops.markov_workspace(R, B, V, dev)
+
+    def run():
+        ops.draft_forward(x_in, fc, layers, kcs, vcs, R, B, H, Dh, ln, norm, float(inp["eps"]), scratch=scratch,
+                          out=hid)
+        ops.draft_round(Wl, hid, w1d, w2d, p0, B, B, probe_w=pwd, base_out=base, ids_out=ids, logit_out=lg,
+                        pass_out=ps, workspace=mws)
+    run()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in (hid, base, ids, lg, ps)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        for x in (hid, base, lg):
+            x.fill_(7.0)
+        ids.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((hid, base, ids, lg, ps), eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = ops.proj_smallm(fc, x_in)  # eager work between replays
+        torch.cuda.synchronize()
