@@ -348,8 +348,7 @@ dspark_status dspark_draft_block(const uint16_t* w_qkv, const uint16_t* w_o, con
                                  block_causal ? 1 : 0, attn, aws, st);
   if (e == hipSuccess) e = dspark::launch_gemv(w_o, d, HD, attn, M, h2, st, h_in);
   if (e == hipSuccess) e = dspark::launch_rmsnorm(h2, M, d, ln2, eps, x, st);
-  if (e == hipSuccess) e = dspark::launch_gemv(w_gate_up, 2 * F, d, x, M, gu, st);
-  if (e == hipSuccess) e = dspark::launch_silu_gate(gu, M, F, act, st);
+  if (e == hipSuccess) e = dspark::launch_gemv_gated(w_gate_up, F, d, x, M, act, gu, st);
   if (e == hipSuccess) e = dspark::launch_gemv(w_down, d, F, act, M, h_out, st, h2);
   return from_hip(e);
 }

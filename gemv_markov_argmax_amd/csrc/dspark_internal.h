@@ -188,6 +188,11 @@ bool gemv_shape_fits(int N, int K, int M);
 // The rest of the draft block: see dspark_rmsnorm, dspark_silu_gate,
 // dspark_attention_ragged.
 hipError_t launch_rmsnorm(const float* x, int M, int D, const uint16_t* gamma, float eps, float* y, hipStream_t st);
+// act = silu(X W_gate^T) * (X W_up^T) for W = [gate rows; up rows] bf16 [2F, K]:
+// one GEMV with the gate in its epilogue where the short kernel takes the
+// shape, else the GEMV into gu [M, 2F] followed by launch_silu_gate.
+hipError_t launch_gemv_gated(const uint16_t* W, int F, int K, const float* X, int M, float* act, float* gu,
+                             hipStream_t stream);
 hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t st);
 bool attention_shape_fits(int R, int B, int H, int Dh, int Lmax);
 size_t attention_workspace_bytes(int R, int B, int H, int Dh, int Lmax);

@@ -97,7 +97,12 @@ inline int wg_rows_max(int N, int grid) {
 // hi and lo are two A blocks with their own accumulators, added per wave.
 // The 16 per-wave partial tiles are summed in LDS in wave order (double
 // buffered, one barrier per tile).
-template <bool PACK, int KBW, bool MANY>
+// GATED (the fused gate/up projection of an MLP, W = [gate rows; up rows],
+// N = 2F): output row 2j is gate row j and row 2j + 1 is up row j, so both
+// halves of activation j land in the same workgroup (rows come in pairs), and
+// the epilogue writes act[m, j] = silu(g) * u, silu(g) = g / (1 + exp(-g)),
+// into Y [M, F]; each row's own value is computed exactly as without GATED.
+template <bool PACK, int KBW, bool MANY, bool GATED = false>
 __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
   constexpr int SEG = 64 * KBW;                 // bytes of a row segment
@@ -127,12 +132,20 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   const unsigned char* rd_base = wtr + i * RS + 16 * g;   // + 64*kb
 
   const uint32_t rowb = static_cast<uint32_t>(K) * 2;  // bytes per weight row
-  const BufRes wres = buf_res(p.W + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
+  // Weight rows: this workgroup's range, or (GATED) the whole matrix, lane
+  // row lrow of a tile being gate or up row (r0 + lrow) / 2 by its parity
+  // (r0, RPI and 16 are even, so the parity is that of lrow); rows past the
+  // matrix read zeros, rows past r1 are computed and not stored.
+  const BufRes wres = GATED ? buf_res(p.W, static_cast<uint32_t>(N) * rowb)
+                            : buf_res(p.W + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
   const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+  const uint32_t row_off = GATED ? static_cast<uint32_t>((lrow & 1) * (N >> 1) + (r0 >> 1) + (lrow >> 1)) * rowb
+                                 : static_cast<uint32_t>(lrow) * rowb;
+  const uint32_t tile_step = (GATED ? 8u : 16u) * rowb;  // 16 rows further
 
   auto load = [&](u32x4 (&b)[NLD], uint32_t off) {
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(wres, off + static_cast<uint32_t>(q * RPI) * rowb);
+    for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(wres, off + static_cast<uint32_t>(q * (GATED ? RPI / 2 : RPI)) * rowb);
   };
   // A tile's weights into this wave's private LDS area (row-major segments).
   auto stage = [&](const u32x4 (&b)[NLD]) {
@@ -204,9 +217,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   // added row offsets stay below 2^31 and cannot wrap it back).
   auto w_off = [&](int ph) -> uint32_t {
     const int kseg = 32 * KBW * (ph * NW + w);
-    return (ph < phases) & (kseg + 8 * lchunk < K)
-               ? static_cast<uint32_t>(lrow) * rowb + static_cast<uint32_t>(kseg + 8 * lchunk) * 2
-               : kBufOutOfRange;
+    return (ph < phases) & (kseg + 8 * lchunk < K) ? row_off + static_cast<uint32_t>(kseg + 8 * lchunk) * 2
+                                                   : kBufOutOfRange;
   };
   auto split = [&](const float4 (&xr)[KBW][XH], u32x4 (&afr)[KBW][F]) {
 #pragma unroll
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
         const bool last_t = t + 1 == rounds;
         const bool more = !last_t || ph + 1 < phases;
         if (last_t && more) load_x(xr, ph + 1);
-        if (more) load(b, last_t ? w_off(ph + 1) : off + static_cast<uint32_t>(t + 1) * 16 * rowb);
+        if (more) load(b, last_t ? w_off(ph + 1) : off + static_cast<uint32_t>(t + 1) * tile_step);
         __builtin_amdgcn_sched_barrier(0);
         mma_publish(afr, j & 1);
         __syncthreads();
@@ -287,6 +299,18 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     }
   }
   __syncthreads();
+  if constexpr (GATED) {
+    // Activations, once: row pair (n, n + 1) of tile t is (gate, up) of j = n / 2.
+    for (int e = tid; e < rounds * M * 8; e += NW * kWave) {
+      const int t = e / (M * 8), rem = e - t * M * 8, mm = rem >> 3, pc = rem & 7;
+      const int n = r0 + 16 * t + 2 * pc;
+      if (n < r1) {
+        const float g = ysum[(t * ROWS + mm) * 16 + 2 * pc], u = ysum[(t * ROWS + mm) * 16 + 2 * pc + 1];
+        p.Y[static_cast<size_t>(mm) * p.ldy + (n >> 1)] = g / (1.0f + expf(-g)) * u;
+      }
+    }
+    return;
+  }
   // Outputs, once: tile t covers columns r0 + 16t + (0..15).
   for (int e = tid; e < rounds * M * 16; e += NW * kWave) {
     const int t = e / (M * 16), rem = e - t * M * 16, mm = rem >> 4, col = rem & 15;
@@ -781,10 +805,10 @@ hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st)
   return hipLaunchKernel(phased ? multi : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
 }
 
-template <bool PACK, int KBW>
+template <bool PACK, int KBW, bool GATED = false>
 hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* one = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, false>);
-  const void* many = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true>);
+  const void* one = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, false, GATED>);
+  const void* many = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true, GATED>);
   static const hipError_t attr = [&] {
     const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
     return e != hipSuccess ? e
@@ -795,6 +819,21 @@ hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   GemvParams a = prm;
   void* args[] = {&a};
   return hipLaunchKernel(pl.many ? many : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
+}
+
+hipError_t dispatch_gated(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+  if (pl.pack) {
+    switch (pl.tkbw) {
+      case 1: return launch_short<true, 1, true>(prm, pl, st);
+      case 2: return launch_short<true, 2, true>(prm, pl, st);
+      default: return launch_short<true, 4, true>(prm, pl, st);
+    }
+  }
+  switch (pl.tkbw) {
+    case 1: return launch_short<false, 1, true>(prm, pl, st);
+    case 2: return launch_short<false, 2, true>(prm, pl, st);
+    default: return launch_short<false, 4, true>(prm, pl, st);
+  }
 }
 
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
@@ -886,6 +925,33 @@ hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, f
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemv_gated(const uint16_t* W, int F, int K, const float* X, int M, float* act, float* gu,
+                             hipStream_t stream) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorNoDevice;
+  const int N = 2 * F;
+  if (M <= 16 && static_cast<long long>(N) * K * 2 < (1LL << 31)) {
+    const Plan pl = make_plan(M, N, K, cus);
+    if (pl.shortk && pl.tkbw > 0) {
+      GemvParams prm{};
+      prm.W = W;
+      prm.X = X;
+      prm.Y = act;
+      prm.N = N;
+      prm.K = K;
+      prm.M = M;
+      prm.ldy = F;
+      prm.pq = (N / 2) / pl.grid;
+      prm.prem = (N / 2) % pl.grid;
+      return dispatch_gated(prm, pl, stream);
+    }
+  }
+  // Other shapes: the projection into gu [M, 2F], then the gate.
+  hipError_t e = launch_gemv(W, N, K, X, M, gu, stream);
+  if (e != hipSuccess) return e;
+  return launch_silu_gate(gu, M, F, act, stream);
 }
 
 }  // namespace dspark
