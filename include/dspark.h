@@ -408,7 +408,9 @@ dspark_status dspark_attention_ragged(const float* q, const float* k, const floa
  * [SI441] "Observation" lists the block's projections (q/k/v/o, gate/up/down)
  * and its attention over a short context; the norms, the gated MLP and the
  * residuals are the plainest reading of a Qwen3-derived drafter. Results are
- * bit-identical to making the eight calls one by one.
+ * bit-identical to making the eight calls one by one (where the shape allows,
+ * the gate runs in the gate/up projection's epilogue instead of a launch of
+ * its own, computing the same values).
  *
  *   w_qkv      bf16 [3 H Dh, d]: q rows, then k rows, then v rows
  *   w_o        bf16 [d, H Dh]
