@@ -315,10 +315,14 @@ __global__ __launch_bounds__(kChunkThreads) void attention_chunk_kernel(AttnPara
 }
 
 // Thread per output element (request, head, position i, dim d); a workgroup
-// covers 256 consecutive elements of one (request, head). It reads the m_c of
-// every chunk of the request (M), then l_c and o_c, the chunks in order.
+// covers 256 consecutive elements of one (request, head). The request's chunks
+// are read 16 at a time (m, l and o together, one memory round trip per
+// batch) and merged in chunk order; a later batch with a larger maximum
+// rescales what is summed so far by exp(M_old - M_new). With at most 16
+// chunks this is exactly out = sum_c w_c o_c as defined above.
 __global__ __launch_bounds__(kAttnThreads) void attention_merge_kernel(AttnParams p, const float* __restrict__ ws,
                                                                        int NC) {
+  constexpr int kBatch = 16;
   const int B = p.B, Dh = p.Dh;
   const int EB = (B * Dh + kAttnThreads - 1) / kAttnThreads;
   const int rh = blockIdx.x / EB, r = rh / p.H, h = rh - r * p.H;
@@ -329,21 +333,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_merge_kernel(AttnParam
   const int nc = (L + B + kAttnChunk - 1) / kAttnChunk;
   const float* base = ws + attn_ws_index(r, h, 0, p.H, NC, B, Dh);
   const size_t stride = static_cast<size_t>(B) * (Dh + 2);
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * stride + i]);
-  float l = 0.f, t = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += 8) {
-    float m[8], lc[8], oc[8];
+  float M = -INFINITY, l = 0.f, t = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += kBatch) {
+    float m[kBatch], lc[kBatch], oc[kBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // clamped indexes: the batch's loads are issued together
-      const float* b = base + min(c0 + u, nc - 1) * stride;
-      m[u] = b[i];
-      lc[u] = b[B + i];
-      oc[u] = b[2 * B + e];
+    for (int u = 0; u < kBatch; ++u) {  // clamped indexes: the batch's loads are issued together
+      const float* bp = base + min(c0 + u, nc - 1) * stride;
+      m[u] = bp[i];
+      lc[u] = bp[B + i];
+      oc[u] = bp[2 * B + e];
     }
+    float Mb = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kBatch; ++u)
+      if (c0 + u < nc) Mb = fmaxf(Mb, m[u]);
+    if (Mb != M && M != -INFINITY) {  // rescale the earlier batches
+      const float sc = expf(M - Mb);
+      l *= sc;
+      t *= sc;
+    }
+    M = Mb;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
       if (c0 + u < nc) {
         const float a = m[u] == -INFINITY ? 0.f : expf(m[u] - M);  // a chunk with no visible key adds nothing
         l = __builtin_fmaf(lc[u], a, l);
