@@ -381,8 +381,7 @@ hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t
 
 int attention_chunks(int B, int Lmax) { return (Lmax + B + kAttnChunk - 1) / kAttnChunk; }
 
-size_t attention_lds_bytes(int B, int Dh) {
-  (void)B;
+size_t attention_lds_bytes(int Dh) {  // q rows and score halves sized for 16 positions
   const int ks = attn_ks(Dh), vs = attn_vs(Dh);
   return static_cast<size_t>(kAttnMaxB * ks + 2 * kAttnMaxB * kAttnChunk + kAttnChunk * kAttnMaxB +
                              kAttnChunk * (ks > vs ? ks : vs)) * 4;
@@ -410,7 +409,7 @@ hipError_t launch_attention(const float* q, const float* kb, const float* vb, in
   void* args[] = {&a, &ws, &NC};
   const long long grid = static_cast<long long>(R) * H * NC;
   hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), args,
-                                 attention_lds_bytes(B, Dh), st);
+                                 attention_lds_bytes(Dh), st);
   if (e != hipSuccess) return e;
   const long long mgrid = static_cast<long long>(R) * H * ((B * Dh + kAttnThreads - 1) / kAttnThreads);
   return hipLaunchKernel(reinterpret_cast<const void*>(&attention_merge_kernel), dim3(static_cast<unsigned>(mgrid)),
