@@ -128,3 +128,23 @@ def test_draft_forward_pins():
     twice = oracle.draft_forward(x, inp["fc"], [w1], [inp["k_ctx"][1]], [inp["v_ctx"][1]], inp["ctx_len"], dbl,
                                  1e-6, R, B, H, Dh)
     assert np.array_equal(twice, 2 * one)
+
+
+def test_block_forward_norm_placement():
+    """Each norm gain feeds only its own branch: with W_o = 0 the block is
+    h + MLP(rmsnorm(h, ln2)) and must not depend on ln1; with W_down = 0 it
+    is h + attention(rmsnorm(h, ln1)) W_o and must not depend on ln2; and each
+    gain does change its own branch."""
+    from gemv_markov_argmax_amd import synth
+    inp = synth.block_inputs(2, 3, 2, 16, 48, 10, [4, 10], 13)
+    w = dict(inp["layers"][0])
+    args = (2, 3, 2, 16, inp["k_ctx"], inp["v_ctx"], inp["ctx_len"], 1e-6)
+    other = synth.bf16_bits_rne(np.linspace(0.5, 1.5, w["ln1"].shape[0]).astype(np.float32))
+    no_o = dict(w, o=np.zeros_like(w["o"]))
+    a = oracle.draft_block_forward(inp["h"], no_o, *args)
+    assert np.array_equal(a, oracle.draft_block_forward(inp["h"], dict(no_o, ln1=other), *args))
+    assert not np.allclose(a, oracle.draft_block_forward(inp["h"], dict(no_o, ln2=other), *args))
+    no_down = dict(w, down=np.zeros_like(w["down"]))
+    b = oracle.draft_block_forward(inp["h"], no_down, *args)
+    assert np.array_equal(b, oracle.draft_block_forward(inp["h"], dict(no_down, ln2=other), *args))
+    assert not np.allclose(b, oracle.draft_block_forward(inp["h"], dict(no_down, ln1=other), *args))
