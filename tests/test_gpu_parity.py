@@ -974,3 +974,30 @@ def test_draft_forward_graph_replay(dev):
             assert torch.equal(a, b), f"replay {rep} differs"
         _ = ops.proj_smallm(fc, x_in)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("R,B,H,Dh,F,Lmax,lens,causal", [(1, 7, 2, 64, 256, 0, [0], False),
+                                                         (2, 5, 2, 64, 256, 0, [0, 0], True),
+                                                         (2, 7, 4, 64, 512, 70, [70, 3], True)])
+def test_draft_block_edges_match_oracle(dev, R, B, H, Dh, F, Lmax, lens, causal):
+    """Whole blocks with no context at all (the block attends to itself only)
+    and with causal block attention, against the fp64 composition."""
+    seed = 7900 + Lmax + 10 * R + (1 if causal else 0)
+    say(f"[draft block edges] R={R} B={B} H={H} Dh={Dh} F={F} Lmax={Lmax} lens={lens} causal={causal} seed={seed}")
+    inp = synth.block_inputs(R, B, H, Dh, F, Lmax, lens, seed)
+    w = {k: _bf(v, dev) for k, v in inp["layers"][0].items()}
+    d = H * Dh
+    if Lmax:
+        kc = _bf(inp["k_ctx"], dev).view(R, Lmax, d)
+        vc = _bf(inp["v_ctx"], dev).view(R, Lmax, d)
+    else:
+        kc = torch.zeros((R, 0, d), dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros((R, 0, d), dtype=torch.bfloat16, device=dev)
+    y = _ops().draft_block_forward(_up(inp["h"], dev), w, R, B, H, Dh, kc, vc,
+                                   torch.tensor(lens, dtype=torch.int32, device=dev), float(inp["eps"]), causal)
+    torch.cuda.synchronize()
+    kc_ = inp["k_ctx"] if Lmax else np.zeros((R, 0, d), np.uint16)
+    vc_ = inp["v_ctx"] if Lmax else np.zeros((R, 0, d), np.uint16)
+    ref = oracle.draft_block_forward(inp["h"], inp["layers"][0], R, B, H, Dh, kc_, vc_, inp["ctx_len"],
+                                     float(inp["eps"]), causal)
+    logits_close(y.cpu().numpy(), ref, f"draft block edge Lmax={Lmax} causal={causal}")
