@@ -77,6 +77,17 @@ def _finite(*arrays):
             raise ValueError("oracle inputs must be finite")
 
 
+def _values(x) -> np.ndarray:
+    """Exact float64 values of an activation input: a float64 array is taken
+    as it is (a value the oracle computed itself, e.g. inside the draft
+    block), anything else is read as float32 (the type the path hands
+    between its steps) and widened exactly."""
+    a = np.asarray(x)
+    if a.dtype == np.float64:
+        return a
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
 # ---------------------------------------------------------------------------
 # Small-M projections and the lm_head
 # ---------------------------------------------------------------------------
@@ -87,10 +98,10 @@ def gemv(W_bits, X) -> np.ndarray:
     [SI441] "Observation": every draft projection and the lm_head multiplies
     the B drafted positions' activations by one weight matrix, reading the
     weight once for all B rows. W is [N, K] bf16 (row n is output n), X is
-    [M, K] float32, Y is [M, N].
+    [M, K] float32 (or float64 values, taken exactly), Y is [M, N].
     """
     W = bf16_to_f64(W_bits)
-    X64 = np.asarray(X, dtype=np.float32).astype(np.float64)
+    X64 = _values(X)
     _finite(W, X64)
     if W.ndim != 2 or X64.ndim != 2 or W.shape[1] != X64.shape[1]:
         raise ValueError("gemv: W [N, K] and X [M, K] required")
@@ -308,8 +319,10 @@ def draft_round_q8(Wq_lm, Wd_lm_bits, H, w1q, w1d_bits, w2q, w2d_bits, prev0, nu
 # design notes.
 
 def rmsnorm(x, gamma_bits, eps: float):
-    """y[m, t] = x[m, t] / sqrt(mean_t x[m, t]^2 + eps) * gamma[t]; gamma bf16, x fp32."""
-    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    """y[m, t] = x[m, t] / sqrt(mean_t x[m, t]^2 + eps) * gamma[t]; gamma bf16,
+    x float32 (or float64 values, taken exactly: the block's second norm reads
+    the float64 residual sum)."""
+    x64 = _values(x)
     g = bf16_to_f64(gamma_bits)
     _finite(x64, g)
     ms = np.mean(x64 * x64, axis=-1, keepdims=True)
@@ -317,8 +330,9 @@ def rmsnorm(x, gamma_bits, eps: float):
 
 
 def silu_gate(gu, F: int):
-    """a[m, j] = silu(g) * u with g = gu[m, j], u = gu[m, F + j], silu(g) = g / (1 + exp(-g))."""
-    gu64 = np.asarray(gu, dtype=np.float32).astype(np.float64)
+    """a[m, j] = silu(g) * u with g = gu[m, j], u = gu[m, F + j], silu(g) = g / (1 + exp(-g)).
+    gu float32 (or float64 values, taken exactly)."""
+    gu64 = _values(gu)
     _finite(gu64)
     g, u = gu64[:, :F], gu64[:, F:2 * F]
     return g / (1.0 + np.exp(-g)) * u
@@ -333,11 +347,12 @@ def attention_ragged(q, k_blk, v_blk, R: int, B: int, H: int, Dh: int, k_ctx_bit
     to the positions of its own block (k_blk, v_blk: fp32 [R * B, H * Dh]),
     all of them, or those j <= i when block_causal. Scores are q . k /
     sqrt(Dh); softmax over those keys; the output is the weighted sum of the
-    values. q, k_blk, v_blk, out: [R * B, H * Dh], row r * B + i.
+    values. q, k_blk, v_blk, out: [R * B, H * Dh], row r * B + i; q, k_blk
+    and v_blk float32 (or float64 values, taken exactly).
     """
-    q64 = np.asarray(q, np.float32).astype(np.float64).reshape(R, B, H, Dh)
-    kb = np.asarray(k_blk, np.float32).astype(np.float64).reshape(R, B, H, Dh)
-    vb = np.asarray(v_blk, np.float32).astype(np.float64).reshape(R, B, H, Dh)
+    q64 = _values(q).reshape(R, B, H, Dh)
+    kb = _values(k_blk).reshape(R, B, H, Dh)
+    vb = _values(v_blk).reshape(R, B, H, Dh)
     kc = bf16_to_f64(k_ctx_bits)
     vc = bf16_to_f64(v_ctx_bits)
     Lmax = kc.shape[1]
@@ -364,21 +379,24 @@ def draft_block_forward(h, w: dict, R: int, B: int, H: int, Dh: int, k_ctx_bits,
                         eps: float, block_causal: bool = False):
     """One draft block (layer) forward at small M = R * B, in float64, as
     the readings above compose it:
-      x1 = rmsnorm(h, ln1); qkv = x1 W_qkv^T; a = attention(qkv);
+      x1 = rmsnorm(h, ln1); [q | k | v] = x1 W_qkv^T; a = attention(q, k, v);
       h2 = h + a W_o^T; x2 = rmsnorm(h2, ln2); gu = x2 W_gate_up^T;
       h3 = h2 + silu_gate(gu) W_down^T.
-    w: bf16 bits of qkv [3 H Dh, d], o [d, H Dh], gate_up [2 F, d], down
-    [d, F], ln1 and ln2 [d]. Intermediate values stay in float64 here."""
+    w: bf16 bits of qkv [3 H Dh, d] (q rows, then k rows, then v rows), o
+    [d, H Dh], gate_up [2 F, d] (gate rows, then up rows), down [d, F], ln1
+    and ln2 [d]. Every step is the module's own function for it (gemv,
+    rmsnorm, attention_ragged, silu_gate) applied to the float64 values of
+    the step before; h is float32."""
     HD = H * Dh
-    x1 = rmsnorm(h, w["ln1"], eps)
-    qkv = x1 @ bf16_to_f64(w["qkv"]).T
-    a = _attention64(qkv, R, B, H, Dh, k_ctx_bits, v_ctx_bits, ctx_len, block_causal)
-    h2 = np.asarray(h, np.float32).astype(np.float64) + a @ bf16_to_f64(w["o"]).T
-    x2 = rmsnorm_f64(h2, w["ln2"], eps)
-    gu = x2 @ bf16_to_f64(w["gate_up"]).T
-    F = gu.shape[1] // 2
-    g, u = gu[:, :F], gu[:, F:]
-    return h2 + (g / (1.0 + np.exp(-g)) * u) @ bf16_to_f64(w["down"]).T
+    h64 = _values(np.asarray(h, dtype=np.float32))
+    x1 = rmsnorm(h64, w["ln1"], eps)
+    qkv = gemv(w["qkv"], x1)
+    a = attention_ragged(qkv[:, :HD], qkv[:, HD:2 * HD], qkv[:, 2 * HD:], R, B, H, Dh, k_ctx_bits, v_ctx_bits,
+                         ctx_len, block_causal)
+    h2 = h64 + gemv(w["o"], a)
+    x2 = rmsnorm(h2, w["ln2"], eps)
+    gu = gemv(w["gate_up"], x2)
+    return h2 + gemv(w["down"], silu_gate(gu, gu.shape[1] // 2))
 
 
 def draft_forward(x_in, fc_bits, layers, k_ctx_list, v_ctx_list, ctx_len, norm_bits, eps: float, R: int, B: int,
@@ -396,34 +414,3 @@ def draft_forward(x_in, fc_bits, layers, k_ctx_list, v_ctx_list, ctx_len, norm_b
     for w, kc, vc in zip(layers, k_ctx_list, v_ctx_list):
         h = draft_block_forward(h.astype(np.float32), w, R, B, H, Dh, kc, vc, ctx_len, eps, block_causal)
     return rmsnorm(h.astype(np.float32), norm_bits, eps)
-
-
-def rmsnorm_f64(x64, gamma_bits, eps: float):
-    """rmsnorm on float64 inputs (the block's second norm reads a float64 sum)."""
-    g = bf16_to_f64(gamma_bits)
-    ms = np.mean(x64 * x64, axis=-1, keepdims=True)
-    return x64 / np.sqrt(ms + float(np.float32(eps))) * g
-
-
-def _attention64(qkv, R, B, H, Dh, k_ctx_bits, v_ctx_bits, ctx_len, block_causal):
-    """attention_ragged on float64 q, k, v (same definition, no float32 rounding of the inputs)."""
-    HD = H * Dh
-    q = qkv[:, :HD].reshape(R, B, H, Dh)
-    kb = qkv[:, HD:2 * HD].reshape(R, B, H, Dh)
-    vb = qkv[:, 2 * HD:].reshape(R, B, H, Dh)
-    kc = bf16_to_f64(k_ctx_bits)
-    Lmax = kc.shape[1]
-    kc = kc.reshape(R, Lmax, H, Dh)
-    vc = bf16_to_f64(v_ctx_bits).reshape(R, Lmax, H, Dh)
-    out = np.empty((R, B, H, Dh))
-    for r in range(R):
-        L = int(ctx_len[r])
-        for i in range(B):
-            nb = i + 1 if block_causal else B
-            for hh in range(H):
-                keys = np.concatenate([kc[r, :L, hh], kb[r, :nb, hh]])
-                vals = np.concatenate([vc[r, :L, hh], vb[r, :nb, hh]])
-                sc = keys @ q[r, i, hh] / np.sqrt(Dh)
-                e = np.exp(sc - sc.max())
-                out[r, i, hh] = (e / e.sum()) @ vals
-    return out.reshape(R * B, HD)

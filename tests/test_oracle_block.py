@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 
 import oracle
-from block_pins import attention_pins, rmsnorm_pins, silu_gate_pins
+from block_pins import attention_pins, block_forward_pins, draft_forward_pins, rmsnorm_pins, silu_gate_pins
+from oracle import dspark_oracle
 from oracle.dspark_oracle import bf16_to_f64
 
 
@@ -82,69 +83,106 @@ def test_attention_mutant_is_caught(kind):
     assert any(not ok for _, ok, _ in attention_pins(_attn_mutant(kind))), kind
 
 
-def test_block_forward_pins():
-    """The composed block: with o and down zero it returns h exactly (the
-    residual path); the MLP branch is linear in W_down (doubling W_down
-    doubles h3 - h2, with h2 the output at W_down = 0); the attention branch
-    does not see W_down."""
-    from gemv_markov_argmax_amd import synth
-    inp = synth.block_inputs(2, 3, 2, 16, 48, 10, [4, 10], 11)
-    w = dict(inp["layers"][0])
-    args = (2, 3, 2, 16, inp["k_ctx"], inp["v_ctx"], inp["ctx_len"], 1e-6)
-    zero = dict(w, o=np.zeros_like(w["o"]), down=np.zeros_like(w["down"]))
-    y0 = oracle.draft_block_forward(inp["h"], zero, *args)
-    assert np.array_equal(y0, inp["h"].astype(np.float64))
-    nodown = dict(w, down=np.zeros_like(w["down"]))
-    h2 = oracle.draft_block_forward(inp["h"], nodown, *args)
-    y1 = oracle.draft_block_forward(inp["h"], w, *args)
-    dbl = synth.bf16_bits_rne(((w["down"].astype(np.uint32) << 16).view(np.float32) * 2).astype(np.float32))
-    y2 = oracle.draft_block_forward(inp["h"], dict(w, down=dbl), *args)
-    assert np.allclose(y2 - h2, 2 * (y1 - h2), rtol=1e-12, atol=1e-12)
+def test_block_forward_meets_every_pin():
+    failed = [(n, d) for n, ok, d in block_forward_pins(oracle.draft_block_forward) if not ok]
+    assert not failed, failed
 
 
-def test_draft_forward_pins():
-    """The drafter's forward: with fc the identity and no blocks it is the
-    final rmsnorm of its input; a block whose o and down are zero passes its
-    input through, so prepending one changes nothing, and the blocks after it
-    still read their own context caches in order; the output is linear in the
-    final norm's gain."""
-    from gemv_markov_argmax_amd import synth
-    R, B, H, Dh, F, Lmax = 2, 3, 2, 8, 24, 6
-    inp = synth.draft_forward_inputs(R, B, H, Dh, F, Lmax, [6, 2], layers=2, n_fc=1, seed=21)
-    d = H * Dh
-    eye = synth.bf16_bits_rne(np.eye(d, dtype=np.float32))
-    x = inp["x_in"]
-    y = oracle.draft_forward(x, eye, [], [], [], inp["ctx_len"], inp["norm"], 1e-6, R, B, H, Dh)
-    assert np.array_equal(y, oracle.rmsnorm(x, inp["norm"], 1e-6))
-    w0, w1 = inp["layers"]
-    ident = dict(w0, o=np.zeros_like(w0["o"]), down=np.zeros_like(w0["down"]))
-    args = (inp["ctx_len"], inp["norm"], 1e-6, R, B, H, Dh)
-    one = oracle.draft_forward(x, inp["fc"], [w1], [inp["k_ctx"][1]], [inp["v_ctx"][1]], *args)
-    two = oracle.draft_forward(x, inp["fc"], [ident, w1], inp["k_ctx"], inp["v_ctx"], *args)
-    assert np.array_equal(one, two)
-    swapped = oracle.draft_forward(x, inp["fc"], [ident, w1], inp["k_ctx"][::-1], inp["v_ctx"][::-1], *args)
-    assert not np.allclose(one, swapped)
-    dbl = synth.bf16_bits_rne(2 * (inp["norm"].astype(np.uint32) << 16).view(np.float32))
-    twice = oracle.draft_forward(x, inp["fc"], [w1], [inp["k_ctx"][1]], [inp["v_ctx"][1]], inp["ctx_len"], dbl,
-                                 1e-6, R, B, H, Dh)
-    assert np.array_equal(twice, 2 * one)
+def test_draft_forward_meets_every_pin():
+    failed = [(n, d) for n, ok, d in draft_forward_pins(oracle.draft_forward, oracle.draft_block_forward) if not ok]
+    assert not failed, failed
 
 
-def test_block_forward_norm_placement():
-    """Each norm gain feeds only its own branch: with W_o = 0 the block is
-    h + MLP(rmsnorm(h, ln2)) and must not depend on ln1; with W_down = 0 it
-    is h + attention(rmsnorm(h, ln1)) W_o and must not depend on ln2; and each
-    gain does change its own branch."""
-    from gemv_markov_argmax_amd import synth
-    inp = synth.block_inputs(2, 3, 2, 16, 48, 10, [4, 10], 13)
-    w = dict(inp["layers"][0])
-    args = (2, 3, 2, 16, inp["k_ctx"], inp["v_ctx"], inp["ctx_len"], 1e-6)
-    other = synth.bf16_bits_rne(np.linspace(0.5, 1.5, w["ln1"].shape[0]).astype(np.float32))
-    no_o = dict(w, o=np.zeros_like(w["o"]))
-    a = oracle.draft_block_forward(inp["h"], no_o, *args)
-    assert np.array_equal(a, oracle.draft_block_forward(inp["h"], dict(no_o, ln1=other), *args))
-    assert not np.allclose(a, oracle.draft_block_forward(inp["h"], dict(no_o, ln2=other), *args))
-    no_down = dict(w, down=np.zeros_like(w["down"]))
-    b = oracle.draft_block_forward(inp["h"], no_down, *args)
-    assert np.array_equal(b, oracle.draft_block_forward(inp["h"], dict(no_down, ln2=other), *args))
-    assert not np.allclose(b, oracle.draft_block_forward(inp["h"], dict(no_down, ln1=other), *args))
+def _block_mutant(kind):
+    """The block composed from the oracle's pinned steps with one planted
+    mistake in how they are put together."""
+    O = dspark_oracle
+
+    def f(h, w, R, B, H, Dh, k_ctx, v_ctx, ctx_len, eps, block_causal=False):
+        HD = H * Dh
+        h64 = np.asarray(h, np.float32).astype(np.float64)
+        x1 = O.rmsnorm(h64, w["ln2" if kind == "ln_swap" else "ln1"], eps)
+        qkv = O.gemv(w["qkv"], x1)
+        q, k, v = qkv[:, :HD], qkv[:, HD:2 * HD], qkv[:, 2 * HD:]
+        if kind == "qk_swap":
+            q, k = k, q
+        if kind == "v_from_k":
+            v = k
+        causal = False if kind == "causal_ignored" else block_causal
+        a = O.attention_ragged(q, k, v, R, B, H, Dh, k_ctx, v_ctx, ctx_len, causal)
+        Wo = w["o"]
+        if kind == "o_transposed":
+            Wo = np.ascontiguousarray(np.asarray(Wo).T)
+        h2 = (0 if kind == "no_res1" else h64) + O.gemv(Wo, a)
+        x2 = O.rmsnorm(h64 if kind == "x2_from_h" else h2, w["ln1" if kind == "ln_swap" else "ln2"], eps)
+        gu = O.gemv(w["gate_up"], x2)
+        F = gu.shape[1] // 2
+        if kind == "gate_up_swap":
+            gu = np.concatenate([gu[:, F:], gu[:, :F]], axis=1)
+        mlp = O.gemv(w["down"], O.silu_gate(gu, F))
+        return (h64 if kind == "res2_from_h" else h2) + mlp
+    return f
+
+
+BLOCK_MUTANTS = ["qk_swap", "v_from_k", "causal_ignored", "o_transposed", "no_res1", "x2_from_h", "ln_swap",
+                 "gate_up_swap", "res2_from_h"]
+
+
+@pytest.mark.parametrize("kind", BLOCK_MUTANTS)
+def test_block_composition_mutant_is_caught(kind):
+    assert any(not ok for _, ok, _ in block_forward_pins(_block_mutant(kind))), kind
+
+
+def test_block_mutant_harness_is_faithful():
+    """Without a planted mistake the hand-composed block is the oracle's."""
+    assert not [n for n, ok, _ in block_forward_pins(_block_mutant("none")) if not ok]
+
+
+def _forward_mutant(kind):
+    O = dspark_oracle
+
+    def f(x_in, fc, layers, kcs, vcs, ctx_len, norm, eps, R, B, H, Dh, block_causal=False):
+        if kind == "fc_transposed":
+            fc = np.ascontiguousarray(np.asarray(fc).T)
+        h = O.gemv(fc, x_in)
+        order = list(zip(layers, kcs, vcs))
+        if kind == "reversed":
+            order = order[::-1]
+        if kind == "shared_cache" and order:
+            order = [(w, kcs[0], vcs[0]) for w, _, _ in order]
+        for w, kc, vc in order:
+            h = O.draft_block_forward(h.astype(np.float32), w, R, B, H, Dh, kc, vc, ctx_len, eps, block_causal)
+        return h if kind == "no_final_norm" else O.rmsnorm(h.astype(np.float32), norm, eps)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["fc_transposed", "reversed", "shared_cache", "no_final_norm"])
+def test_forward_composition_mutant_is_caught(kind):
+    assert any(not ok for _, ok, _ in draft_forward_pins(_forward_mutant(kind), oracle.draft_block_forward)), kind
+
+
+def _rms_dropped_mean(x, gamma_bits, eps):
+    x64 = np.asarray(x).astype(np.float64)
+    return x64 / np.sqrt(np.sum(x64 * x64, axis=-1, keepdims=True) + eps) * bf16_to_f64(gamma_bits)
+
+
+def _rms_eps_outside(x, gamma_bits, eps):
+    x64 = np.asarray(x).astype(np.float64)
+    return x64 / (np.sqrt(np.mean(x64 * x64, axis=-1, keepdims=True)) + eps) * bf16_to_f64(gamma_bits)
+
+
+@pytest.mark.parametrize("name,mutant,pins", [
+    ("rmsnorm", _rms_dropped_mean, rmsnorm_pins), ("rmsnorm", _rms_eps_outside, rmsnorm_pins),
+    ("attention_ragged", _attn_mutant("no_scale"), attention_pins),
+], ids=["rms_sum_for_mean", "rms_eps_outside_root", "attention_dropped_scale"])
+def test_block_runs_through_the_pinned_steps(monkeypatch, name, mutant, pins):
+    """A mistake planted in one of the pinned steps changes the block's
+    output (the block has no private copy of that step), and the step's own
+    pins catch it."""
+    inp = __import__("gemv_markov_argmax_amd.synth", fromlist=["x"]).block_inputs(2, 3, 2, 16, 48, 10, [4, 10], 19)
+    args = (inp["h"], inp["layers"][0], 2, 3, 2, 16, inp["k_ctx"], inp["v_ctx"], inp["ctx_len"], 1e-6)
+    good = oracle.draft_block_forward(*args)
+    monkeypatch.setattr(dspark_oracle, name, mutant)
+    bad = dspark_oracle.draft_block_forward(*args)
+    assert not np.allclose(good, bad, rtol=1e-9, atol=1e-12), f"block ignores {name}"
+    assert any(not ok for _, ok, _ in pins(mutant)), f"{name} pins miss the mutant"
