@@ -98,6 +98,8 @@ size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V) {
   return dspark::markov_workspace_bytes(num_reqs, k, V);
 }
 
+uint32_t dspark_markov_set_spin_limit(uint32_t polls) { return dspark::markov_set_spin_limit(polls); }
+
 }  // extern "C"
 
 namespace {

@@ -222,6 +222,9 @@ struct ProbeArgs {
 // Markov loop; see dspark_markov_sample. With `probe` non-null the same
 // launch also computes the confidence probe, bit-identical to launch_probe.
 size_t markov_workspace_bytes(int num_reqs, int k, int V);
+// Polls before a grid-wide wait of the loop gives up (0: the default);
+// returns the previous setting. Applies to launches enqueued afterwards.
+uint32_t markov_set_spin_limit(uint32_t polls);
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
                          int k, int64_t* ids, void* workspace, const ProbeArgs* probe,

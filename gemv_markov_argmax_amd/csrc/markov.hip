@@ -41,10 +41,21 @@
 //    other buffer, and workgroup 0, the last to read any slot, advances the
 //    sequence number at the end. Only a stream-ordered next call uses that
 //    buffer, so it is clean by then. The workspace must therefore be
-//    zero-filled once before first use. A poll that gives up (which the
-//    residency check rules out on an otherwise idle device) leaves a sticky
-//    flag: that call and every later one on the workspace return -2 ids
-//    until it is zero-filled again.
+//    zero-filled once before first use.
+//  * The polls are bounded. A poll that gives up (all workgroups resident is
+//    checked on the host, but another stream's kernels could hold compute
+//    units for longer than the bound) marks the workspace: that call's ids
+//    are -2, and it leaves the sequence number and the slot counts alone,
+//    so that a workgroup of it that starts late still sees the state every
+//    other workgroup of the call saw. The next call finds the mark and
+//    repairs the workspace instead of sampling: all of its workgroups clear
+//    both slot buffers, its ids are -2 too, and workgroup 0 records the
+//    repair together with the call's launch number. A workgroup that finds
+//    a repair recorded under its own launch number is a late one of the
+//    repairing launch (or a replay of the same captured launch): it only
+//    clears and leaves. Every call after that samples normally, and the
+//    first one that completes removes the repair record. No caller action
+//    is needed.
 //  * Nothing but the exchange sits on the per-step path of workgroup 0: the
 //    drafted tokens stay in LDS and the ids (d2t applied) are written once,
 //    after the last step.
@@ -52,6 +63,7 @@
 #include "dspark_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace dspark {
@@ -68,11 +80,17 @@ constexpr int kLoopWavesMax = 8;
 constexpr size_t kCtlBytes = 256;        // control words, then two slot buffers
 constexpr size_t kSlotsPerBuffer = static_cast<size_t>(kMaxSteps) * kMaxReqs * kMaxGroups;
 // Control words (uint32) at the start of the workspace.
-constexpr int kCtlWatchdog = 0;  // nonzero: a poll gave up; sticky until the workspace is zero-filled
-constexpr int kCtlSeq = 1;       // call sequence number; its parity selects the active slot buffer
-constexpr int kCtlUsed = 4;      // [4 + b]: slots the last call that used buffer b wrote
+constexpr int kCtlState = 0;       // kStateOk, kStateTimedOut (a poll gave up) or kStateRepaired
+constexpr int kCtlSeq = 1;         // call sequence number; its parity selects the active slot buffer
+constexpr int kCtlRepairedBy = 2;  // launch number of the call that repaired the workspace
+constexpr int kCtlUsed = 4;        // [4 + b]: slots the last call that used buffer b wrote
+constexpr uint32_t kStateOk = 0;
+constexpr uint32_t kStateTimedOut = 1;  // any value but kStateOk and kStateRepaired is treated so
+constexpr uint32_t kStateRepaired = 2;
 constexpr size_t kLdsBytes = 160 * 1024;
-constexpr uint32_t kSpinLimit = 1u << 18;  // watchdog (~0.3 s of polling): far beyond any legitimate wait
+constexpr uint32_t kDefaultSpinLimit = 1u << 18;  // ~0.3 s of polling: far beyond any legitimate wait
+std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+std::atomic<uint32_t> g_launches{0};
 
 struct MarkovParams {
   const float* base;     // [R, B, V]
@@ -88,6 +106,8 @@ struct MarkovParams {
   int bstride;           // floats per request in the LDS base slice (>= 16 * tiles per workgroup)
   int base_in_lds;       // 0: base values are read straight from memory (slice too large)
   int probe_on;          // nonzero: also compute the confidence probe described by `probe`
+  uint32_t nonce;        // launch number (never 0): tells a late workgroup of a repairing launch
+  uint32_t spin_limit;   // polls before a grid-wide wait gives up
   ProbeArgs probe;
   // Q8_0 weights (the Q8 kernels): quants [V, r] and binary16 block scales [V, r / 32]
   const int8_t* w1q;
@@ -163,10 +183,14 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   const int nt = t1 - t0;
   const int nreg = min(nt, NW * RT);
   const int nheld = nreg + min(nt - nreg, p.lds_tiles);
-  // Active slot buffer of this call, and the sticky watchdog flag (issued
-  // first: the replies arrive while markov_w2 loads).
+  // Active slot buffer of this call and the workspace state (issued first:
+  // the replies arrive while markov_w2 loads).
   const uint32_t seq = load_coherent(p.ctl + kCtlSeq);
-  const uint32_t dead = load_coherent(p.ctl + kCtlWatchdog);
+  const uint32_t state = load_coherent(p.ctl + kCtlState);
+  const uint32_t repaired_by = load_coherent(p.ctl + kCtlRepairedBy);
+  // kStateRepaired under this launch's number: a late workgroup of the
+  // repairing launch, or a replay of that captured launch.
+  const bool repair = !(state == kStateOk || (state == kStateRepaired && repaired_by != p.nonce));
 
   auto w2_row = [&](int j, int lrow) {
     const int row = min((t0 + j) * 16 + lrow, V - 1);
@@ -269,24 +293,47 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   };
   // Workgroup 0 after the last step (every other workgroup has published
   // every step, so none reads a slot any more): the ids of all steps, the
-  // slots used, and the next sequence number. A poll that gave up in this
-  // call or an earlier one turns every id into -2.
+  // slots used, and the next sequence number. When a poll of this call gave
+  // up, every id is -2 and the state stays as it is (the next call repairs).
   auto finish = [&]() {
     if (G == 1) clear_other();
-    const bool bad = dead != 0u || load_coherent(p.ctl + kCtlWatchdog) != 0u;
+    const bool bad = load_coherent(p.ctl + kCtlState) == kStateTimedOut;
     for (int e = tid; e < R * p.k; e += kLoopThreads) {
       const int m = e / p.k, st = e - m * p.k;
       int64_t id = -1;
-      if (dead == 0u && prev0_ok(p, m)) {  // tok_s holds this call's tokens (each in [0, V))
+      if (prev0_ok(p, m)) {  // tok_s holds this call's tokens (each in [0, V))
         const int tok = tok_s[st * R + m];
         id = p.d2t ? p.d2t[tok] : static_cast<int64_t>(tok);
       }
       p.ids[e] = bad ? -2 : id;
     }
-    if (tid == 0) {
+    if (tid == 0 && !bad) {
       __hip_atomic_store(p.ctl + kCtlUsed + cur, static_cast<uint32_t>(p.k * R * G), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctl + kCtlSeq, seq + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (state == kStateRepaired)
+        __hip_atomic_store(p.ctl + kCtlState, kStateOk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  // A call that finds the workspace marked: every workgroup clears its
+  // share of both slot buffers; workgroup 0 writes -2 ids and records the
+  // repair (or, for a late workgroup's launch, drops the record).
+  auto repair_workspace = [&]() {
+    constexpr size_t kAll = 2 * kSlotsPerBuffer;
+    for (size_t e = static_cast<size_t>(blockIdx.x) * kLoopThreads + tid; e < kAll;
+         e += static_cast<size_t>(G) * kLoopThreads)
+      __hip_atomic_store(p.slots + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x != 0) return;
+    for (int e = tid; e < R * p.k; e += kLoopThreads) p.ids[e] = -2;
+    if (tid == 0) {
+      if (state == kStateRepaired) {
+        __hip_atomic_store(p.ctl + kCtlRepairedBy, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        __hip_atomic_store(p.ctl + kCtlUsed + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctl + kCtlUsed + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctl + kCtlRepairedBy, p.nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctl + kCtlState, kStateRepaired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   };
 
@@ -388,8 +435,8 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     }
   };
 
-  if (dead != 0u) {  // an earlier call gave up: report it and touch no slot
-    if (blockIdx.x == 0) finish();
+  if (repair) {  // an earlier call gave up: repair the workspace, sample nothing
+    repair_workspace();
     if (blockIdx.x != 0 || G == 1) probe_rows();
     return;
   }
@@ -667,8 +714,12 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
           }
           break;
         }
-        if (++spins > kSpinLimit) {
-          if (lane == 0) __hip_atomic_store(p.ctl + kCtlWatchdog, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (++spins > p.spin_limit) {
+          // Mark the workspace; the fence makes the mark visible before any
+          // later key of this workgroup, so workgroup 0, which sees those
+          // keys, sees the mark when it writes the ids.
+          if (lane == 0) __hip_atomic_store(p.ctl + kCtlState, kStateTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 #pragma unroll
           for (int u = 0; u < kMaxPoll; ++u) {
             const int j = lane + u * kWave;
@@ -682,7 +733,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       kk = umax64(kk, __shfl_xor(kk, 16));
       kk = umax64(kk, __shfl_xor(kk, 32));
       int tok = static_cast<int>(key_index(kk));
-      if (tok < 0 || tok >= V) tok = 0;  // only if the watchdog fired
+      if (tok < 0 || tok >= V) tok = 0;  // only if a poll gave up
       if (lane == 0) tok_s[step * R + m] = tok;
       if (!last && h == 0) gather_fetch(tok, gv, gs);
       if (!last && h > 0) {
@@ -823,6 +874,10 @@ hipError_t launch_markov_any(MarkovParams prm, bool q8, const ProbeArgs* probe, 
   }
   prm.G = pl.G;
   prm.tiles = tiles;
+  uint32_t nonce = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
+  if (nonce == 0u) nonce = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
+  prm.nonce = nonce;
+  prm.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   prm.lds_tiles = pl.lds_tiles;
   prm.bstride = pl.bstride;
   prm.base_in_lds = pl.base_in_lds;
@@ -851,6 +906,10 @@ MarkovParams common_params(const float* base, int R, int B, int V, int r, const 
 }
 
 }  // namespace
+
+uint32_t markov_set_spin_limit(uint32_t polls) {
+  return g_spin_limit.exchange(polls == 0u ? kDefaultSpinLimit : polls, std::memory_order_relaxed);
+}
 
 size_t markov_workspace_bytes(int num_reqs, int k, int V) {
   if (num_reqs < 1 || num_reqs > kMaxReqs || k < 1 || k > kMaxSteps || V < 1) return 0;

@@ -39,6 +39,7 @@ SIGNATURES = {
     "dspark_draft_block": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _f, _i,
                                 _p, _sz, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
+    "dspark_markov_set_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
     "dspark_markov_sample_probe": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
@@ -351,6 +352,12 @@ def markov_workspace(num_reqs: int, k: int, V: int, device) -> torch.Tensor:
     if n == 0:
         raise ValueError("sizes out of range for the Markov loop")
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def markov_set_spin_limit(polls: int) -> int:
+    """Bound of the Markov loop's grid-wide waits, in polls (0: the default);
+    returns the previous setting (dspark_markov_set_spin_limit)."""
+    return int(lib().dspark_markov_set_spin_limit(int(polls)))
 
 
 def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor, k: int,

@@ -42,9 +42,11 @@
  *    BEFORE any HIP call is made and nothing is enqueued. A failed launch
  *    returns DSPARK_ERR_HIP. Faults during execution surface at the caller's
  *    next synchronization, as usual in HIP.
- *  - The library keeps no host-side state and every call is reentrant. The
- *    Markov workspace carries device-side state from one call to the next,
- *    so calls that share a workspace must not run concurrently.
+ *  - The library keeps no host-side state besides a launch counter and the
+ *    Markov loop's poll bound (dspark_markov_set_spin_limit), and every call
+ *    is reentrant. The Markov workspace carries device-side state from one
+ *    call to the next, so calls that share a workspace must not run
+ *    concurrently (see dspark_markov_sample).
  *  - Results are deterministic: no floating-point atomics are used, and the
  *    summation order of every output is fixed by the shapes alone.
  */
@@ -172,17 +174,29 @@ size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V);
  *   ids_out   int64 [num_reqs, k], overwritten
  *   workspace >= dspark_markov_workspace_bytes(num_reqs, k, V) bytes,
  *             8-byte aligned, owned by the caller. It must be ZERO-FILLED
- *             ONCE before its first use; every call leaves it ready for the
- *             next one (the loop keeps its own state there: key slots of the
- *             grid-wide exchange and a call counter), so no clearing launch
- *             precedes a call. Calls that share a workspace must be ordered
- *             (one stream, or event dependencies).
- * The loop's workgroups exchange one key per step and must all be resident
- * at once; the call checks that the grid fits the device
- * (DSPARK_ERR_HIP otherwise). Should a grid-wide wait still time out (other
- * work holding the compute units for a long time), every id of that call is
- * -2, and so is every id of later calls on the same workspace until it is
- * zero-filled again.
+ *             ONCE before its first use.
+ * The workspace contract. Unlike plain scratch memory, this workspace
+ * carries device-side state from one call to the next: the key slots of
+ * the grid-wide exchange (two buffers; each call leaves the one it used for
+ * the next call to clear), a call counter and a state word. That is what
+ * lets a call start without a clearing launch in front of it. Hence:
+ *   - zero-fill it once after allocation, and never write it yourself
+ *     afterwards (a workspace zero-filled again at any point between calls
+ *     is also valid);
+ *   - calls that share a workspace must be ordered (one stream, or event
+ *     dependencies); calls that overlap in time need workspaces of their
+ *     own. One workspace serves calls of every shape and both weight
+ *     formats;
+ *   - the loop's workgroups exchange one key per step and must all be
+ *     resident at once. The call checks that the grid fits an otherwise idle
+ *     device (DSPARK_ERR_HIP otherwise); kernels of other streams may delay
+ *     some workgroups, which the bounded waits absorb;
+ *   - should a grid-wide wait still give up (other work holding compute
+ *     units for longer than the bound, ~0.3 s of polling by default; see
+ *     dspark_markov_set_spin_limit), every id of that call is -2. The next
+ *     call on the workspace repairs it: it samples nothing, clears the key
+ *     slots, and its ids are -2 as well. The call after that (and every
+ *     later one) samples normally. No caller action is needed.
  * Sizes: 1 <= num_reqs <= 16, 1 <= k <= min(B, 32), V >= 1, 8 <= r <= 1024 with
  * r % 8 == 0. A request whose prev0 lies outside [0, V) gets -1 in every
  * entry of its ids row (a device-side check; nothing out of range is read).
@@ -192,6 +206,18 @@ dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V
                                    const int64_t* d2t, const int64_t* prev0, int k,
                                    int64_t* ids_out, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * dspark_markov_set_spin_limit -- the bound of the Markov loop's grid-wide
+ * waits, in polls (each a few hundred nanoseconds); 0 restores the default
+ * (2^18 polls, ~0.3 s). Returns the previous setting. It applies to every
+ * Markov launch enqueued afterwards by this process (a launch recorded into
+ * a HIP graph keeps the value it was recorded with). It exists so that the
+ * give-up path and the repair that follows it (see dspark_markov_sample)
+ * can be exercised from the host: a bound of a few polls makes the waits of
+ * an ordinary call give up. Every kernel still exits normally.
+ */
+uint32_t dspark_markov_set_spin_limit(uint32_t polls);
 
 /*
  * dspark_conf_probe -- the proposer's confidence probe.
@@ -267,7 +293,8 @@ dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B,
  *   ids_out   int64 [num_reqs, k]          overwritten
  *   logit_out fp32  [num_reqs * B]         overwritten (required when probe_w is given)
  *   pass_out  int32 [num_reqs * B] or NULL
- *   workspace as for dspark_markov_sample (zero-filled once before first use)
+ *   workspace as for dspark_markov_sample (zero-filled once before first use;
+ *             the same contract)
  * Sizes and errors: those of the three calls above; every check is made
  * before anything is enqueued.
  */

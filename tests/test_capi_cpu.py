@@ -115,6 +115,15 @@ def test_markov_errors(L):
     assert call(wsb=ws - 1) == ERR_WORKSPACE
 
 
+def test_markov_spin_limit_setting(L):
+    """The poll bound is host state only: setting it makes no HIP call."""
+    f = L.dspark_markov_set_spin_limit
+    first = f(5)
+    assert first == 1 << 18          # the default
+    assert f(0) == 5                 # 0 restores the default
+    assert f(0) == 1 << 18
+
+
 def test_markov_workspace_bytes(L):
     f = L.dspark_markov_workspace_bytes
     assert f(0, 7, 100) == 0 and f(17, 7, 100) == 0 and f(1, 0, 100) == 0 and f(1, 7, 0) == 0

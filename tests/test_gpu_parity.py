@@ -240,26 +240,142 @@ def test_markov_workspace_reused_across_shapes(dev):
         check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
 
 
-def test_markov_sticky_watchdog_flag(dev):
-    """A workspace whose watchdog word is set (as a timed-out grid-wide wait
-    leaves it; set here from the host) makes every id -2 without touching a
-    key slot, call after call, until the workspace is zero-filled again."""
+def _markov_case(dev, R, B, k, V, r, seed):
+    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, seed)
+    return (base, w1, w2, prev0), (_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k)
+
+
+@pytest.mark.parametrize("mark", [1, 7])
+def test_markov_marked_workspace_repairs_itself(dev, mark):
+    """A workspace marked as a grid-wide wait that gave up leaves it (the
+    state word set from the host: 1, or any value but 0 and 2) is repaired by
+    the next call, whose ids are -2; the call after that samples normally,
+    with no zero-fill by the caller."""
     R, B, k, V, r = 2, 5, 5, 3000, 64
-    say(f"[markov watchdog flag] R={R} V={V} r={r}")
-    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, 91)
-    args = (_up(base, dev), _bf(w1, dev), _bf(w2, dev), _up(prev0, dev), k)
+    say(f"[markov repair] mark={mark} R={R} V={V} r={r}")
+    host, args = _markov_case(dev, R, B, k, V, r, 91)
     ws = _ops().markov_workspace(R, k, V, dev)
     good = _ops().markov_sample(*args, workspace=ws).clone()
-    ws[0] = 1  # low byte of the watchdog word
-    for _ in range(2):
-        ids = _ops().markov_sample(*args, workspace=ws)
-        torch.cuda.synchronize()
-        assert torch.all(ids == -2)
-    ws.zero_()
+    ws[0] = mark  # low byte of the state word
     ids = _ops().markov_sample(*args, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(ids, good)
-    check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
+    assert torch.all(ids == -2)
+    for _ in range(3):
+        ids = _ops().markov_sample(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, good)
+    assert int(ws[:4].view(torch.int32)[0]) == 0, "the state word is back to normal"
+    check_markov(ids.cpu().numpy(), host[0], host[1], host[2], host[3], k)
+
+
+def test_markov_repair_inside_a_replayed_graph(dev):
+    """The repair under graph replay: the replay that finds the mark repairs
+    (-2); the next replay of the same recorded launch recognises the repair
+    as its own and only drops the record (-2); every later replay samples."""
+    R, B, k, V, r = 1, 7, 7, 20011, 256
+    say(f"[markov repair in graph] R={R} V={V} r={r}")
+    _, args = _markov_case(dev, R, B, k, V, r, 92)
+    ops = _ops()
+    ws = ops.markov_workspace(R, k, V, dev)
+    out = torch.empty(R, k, dtype=torch.int64, device=dev)
+    good = ops.markov_sample(*args, workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ops.markov_sample(*args, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.markov_sample(*args, workspace=ws, out=out)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, good)
+    ws[0] = 1
+    want = ["repair", "own record", "sample", "sample"]
+    for rep, what in enumerate(want):
+        out.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        if what == "sample":
+            assert torch.equal(out, good), f"replay {rep}"
+        else:
+            assert torch.all(out == -2), f"replay {rep} ({what})"
+        _ = ops.markov_sample(*args)  # eager work (own workspace) between replays
+        torch.cuda.synchronize()
+
+
+def test_markov_forced_give_up_then_recovers(dev):
+    """A poll bound of one poll (set from the host) makes the grid-wide waits
+    of an ordinary call give up: that call's ids are -2 and every kernel
+    exits normally. With the default bound restored, the next call repairs
+    the workspace (-2) and the one after it samples correctly."""
+    R, B, k, V, r = 1, 7, 7, 151936, 256
+    say(f"[markov forced give-up] R={R} V={V} r={r}")
+    host, args = _markov_case(dev, R, B, k, V, r, 93)
+    ops = _ops()
+    ws = ops.markov_workspace(R, k, V, dev)
+    good = ops.markov_sample(*args, workspace=ws).clone()
+    gave_up = False
+    for attempt in range(3):
+        prev = ops.markov_set_spin_limit(1)
+        try:
+            ids = ops.markov_sample(*args, workspace=ws)
+        finally:
+            ops.markov_set_spin_limit(0)
+        torch.cuda.synchronize()
+        if torch.all(ids == -2):
+            gave_up = True
+            ids = ops.markov_sample(*args, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.all(ids == -2), "the call after a give-up repairs"
+        else:
+            assert torch.equal(ids, good), f"attempt {attempt}: neither -2 nor correct"
+        ids = ops.markov_sample(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, good)
+        if gave_up:
+            break
+    assert prev == 1 << 18
+    assert gave_up, "a one-poll bound never gave up (the path was not exercised)"
+    check_markov(ids.cpu().numpy(), host[0], host[1], host[2], host[3], k)
+
+
+def test_markov_beside_a_long_gemv_on_another_stream(dev):
+    """The loop launched while lm_head GEMVs queued on another stream of the
+    same process hold compute units: its workgroups may start late, which
+    the bounded waits absorb. The ids are correct, or (if a wait gave up)
+    -2 followed by the documented repair."""
+    R, B, k, V, r = 1, 7, 7, 151936, 256
+    say(f"[markov beside gemv] R={R} V={V} r={r}")
+    host, args = _markov_case(dev, R, B, k, V, r, 94)
+    ops = _ops()
+    ws = ops.markov_workspace(R, k, V, dev)
+    good = ops.markov_sample(*args, workspace=ws).clone()
+    W = (torch.randn(151936, 4096, device=dev) * 0.02).to(torch.bfloat16)
+    H = torch.randn(7, 4096, device=dev)
+    y = torch.empty(7, 151936, device=dev)
+    torch.cuda.synchronize()
+    s2 = torch.cuda.Stream()
+    outcomes = []
+    for trial in range(3):
+        with torch.cuda.stream(s2):
+            for _ in range(6):
+                ops.lm_head(W, H, out=y)
+        ids = ops.markov_sample(*args, workspace=ws)  # current stream, beside them
+        torch.cuda.synchronize()
+        if torch.all(ids == -2):
+            outcomes.append("gave up")
+            again = ops.markov_sample(*args, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.all(again == -2)
+        else:
+            outcomes.append("ok")
+            assert torch.equal(ids, good), f"trial {trial}"
+        ids = ops.markov_sample(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, good)
+    say(f"[markov beside gemv] outcomes {outcomes}")
+    check_markov(ids.cpu().numpy(), host[0], host[1], host[2], host[3], k)
 
 
 def test_markov_d2t_and_sentinel(dev):
@@ -471,11 +587,12 @@ def test_markov_sample_probe(dev, R, B, k, V, r, M, D):
         check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
 
 
-def test_draft_round_without_probe_and_watchdog(dev):
-    """Without probe_w the round writes no probe output; with the watchdog
-    word set the ids are -2 and the probe is still computed."""
+def test_draft_round_without_probe_and_repair(dev):
+    """Without probe_w the round writes no probe output; on a workspace
+    marked by a wait that gave up, the round's ids are -2 (it repairs the
+    workspace), its probe is still computed, and the next round is normal."""
     inp, t = _round_tensors("tiny", dev)
-    say("[draft_round no probe / watchdog] tiny")
+    say("[draft_round no probe / repair] tiny")
     R, B, V, k = inp["num_reqs"], inp["B"], inp["V"], inp["k"]
     ws = _ops().markov_workspace(R, k, V, dev)
     lg = torch.full((R * B,), 7.0, device=dev)
@@ -483,14 +600,13 @@ def test_draft_round_without_probe_and_watchdog(dev):
     torch.cuda.synchronize()
     assert out["logit"] is None and torch.all(lg == 7.0)
     good = out["ids"].clone()
-    ws[0] = 1  # the watchdog word, as a timed-out wait leaves it
+    ws[0] = 1  # the state word, as a wait that gave up leaves it
     out = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, probe_w=t["pw"], workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(out["ids"] == -2)
     ref_lg, ref_ps = _ops().conf_probe(t["H"], t["pw"])
     torch.cuda.synchronize()
     assert torch.equal(out["logit"], ref_lg) and torch.equal(out["passed"], ref_ps)
-    ws.zero_()
     out = _ops().draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out["ids"], good)
