@@ -158,6 +158,19 @@ dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V
                                         nullptr, static_cast<hipStream_t>(stream)));
 }
 
+dspark_status dspark_markov_sample_noalloc(const float* base, int num_reqs, int B, int V, const uint16_t* w1,
+                                           const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
+                                           int k, int64_t* ids_out, void* stream) {
+  const size_t have = dspark::markov_scratch_bytes();
+  // (a non-null stand-in: the static workspace is looked up below, after every check)
+  dspark_status st = markov_checks(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, ids_out, have);
+  if (st != DSPARK_OK) return st;
+  void* ws = nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dspark::markov_scratch(&ws, s) != hipSuccess) return DSPARK_ERR_HIP;
+  return from_hip(dspark::launch_markov(base, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, ws, nullptr, s));
+}
+
 dspark_status dspark_conf_probe(const float* x, int M, int D, const uint16_t* w, float bias, float threshold,
                                 float* logit_out, int32_t* pass_out, void* stream) {
   const dspark_status st = probe_checks(x, M, D, w, logit_out, pass_out);

@@ -225,6 +225,10 @@ size_t markov_workspace_bytes(int num_reqs, int k, int V);
 // Polls before a grid-wide wait of the loop gives up (0: the default);
 // returns the previous setting. Applies to launches enqueued afterwards.
 uint32_t markov_set_spin_limit(uint32_t polls);
+// The per-device static workspace of the allocation-free loop entry point:
+// its size, and its device address (set up on the first call per device).
+size_t markov_scratch_bytes();
+hipError_t markov_scratch(void** out, hipStream_t stream);
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
                          int k, int64_t* ids, void* workspace, const ProbeArgs* probe,

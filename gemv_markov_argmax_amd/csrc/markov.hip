@@ -64,6 +64,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace dspark {
@@ -914,6 +915,56 @@ uint32_t markov_set_spin_limit(uint32_t polls) {
 size_t markov_workspace_bytes(int num_reqs, int k, int V) {
   if (num_reqs < 1 || num_reqs > kMaxReqs || k < 1 || k > kMaxSteps || V < 1) return 0;
   return kCtlBytes + 2 * kSlotsPerBuffer * sizeof(uint64_t);  // one layout for every size
+}
+
+// ---------------------------------------------------------------------------
+// The loop without a caller workspace, for callers that cannot allocate
+// (code under graph capture, tight serving loops): its workspace is a
+// file-scope device array, one copy per GPU, kept until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// host code uses only the address hipGetSymbolAddress returns for it.
+namespace {
+
+constexpr size_t kScratchBytes = kCtlBytes + 2 * kSlotsPerBuffer * sizeof(uint64_t);  // 2 MiB + 256 B
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* p, size_t n16) {
+  for (size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; e < n16; e += static_cast<size_t>(gridDim.x) * 256)
+    p[e] = u32x4{0u, 0u, 0u, 0u};
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+size_t markov_scratch_bytes() { return kScratchBytes; }
+
+// Address of this device's copy of `scratch`, set up on the first call per
+// device (with that device current): its address from
+// hipGetSymbolAddress, then one zero fill, a kernel on `stream` ordered
+// before the caller's first loop launch (a kernel rather than a memset, so
+// that a first call made under graph capture stays valid).
+hipError_t markov_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    static_assert(kScratchBytes % 16 == 0, "the fill kernel writes 16-byte words");
+    zero_fill_kernel<<<dim3(64), dim3(256), 0, stream>>>(static_cast<u32x4*>(ptr), kScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,

@@ -40,6 +40,7 @@ SIGNATURES = {
                                 _p, _sz, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_set_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
+    "dspark_markov_sample_noalloc": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
     "dspark_markov_sample_probe": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
@@ -358,6 +359,37 @@ def markov_set_spin_limit(polls: int) -> int:
     """Bound of the Markov loop's grid-wide waits, in polls (0: the default);
     returns the previous setting (dspark_markov_set_spin_limit)."""
     return int(lib().dspark_markov_set_spin_limit(int(polls)))
+
+
+def markov_sample_noalloc(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor, k: int,
+                          d2t: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """markov_sample with the library's static per-device workspace
+    (dspark_markov_sample_noalloc). ``out`` int64 [R, k] must be given by a
+    caller that may not allocate; it is allocated here otherwise."""
+    _dev(base, torch.float32, "base", 3)
+    _dev(w1, torch.bfloat16, "w1", 2)
+    _dev(w2, torch.bfloat16, "w2", 2)
+    _dev(prev0, torch.int64, "prev0", 1)
+    R, B, V = base.shape
+    r = w1.shape[1]
+    if tuple(w1.shape) != (V, r) or tuple(w2.shape) != (V, r):
+        raise ValueError("w1 and w2 must both be [V, r]")
+    if prev0.shape[0] != R:
+        raise ValueError("prev0 must have num_reqs entries")
+    d2t_ptr = None
+    if d2t is not None:
+        _dev(d2t, torch.int64, "d2t", 1)
+        if d2t.shape[0] != V:
+            raise ValueError("d2t must have V entries")
+        d2t_ptr = d2t.data_ptr()
+    if out is None:
+        out = torch.empty((R, k), dtype=torch.int64, device=base.device)
+    if tuple(out.shape) != (R, k):
+        raise ValueError("out must be [num_reqs, k]")
+    out_ptr = _out_ptr(out, torch.int64, "out", 2)
+    _check(lib().dspark_markov_sample_noalloc(base.data_ptr(), R, B, V, w1.data_ptr(), w2.data_ptr(), r, d2t_ptr,
+                                              prev0.data_ptr(), k, out_ptr, _stream(base)))
+    return out
 
 
 def markov_sample(base: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prev0: torch.Tensor, k: int,

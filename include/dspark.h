@@ -208,6 +208,33 @@ dspark_status dspark_markov_sample(const float* base, int num_reqs, int B, int V
                                    void* stream);
 
 /*
+ * dspark_markov_sample_noalloc -- dspark_markov_sample without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * The loop's workspace is instead a static device array inside the library
+ * (2 MiB + 256 bytes, the size dspark_markov_workspace_bytes returns for
+ * every valid shape), one copy per GPU, set up on the first call on each
+ * device (its address looked up once, then zero-filled by a small kernel on
+ * `stream`) and held until the process ends. The call allocates nothing:
+ * no hipMalloc, no hipFree, no allocating library routine.
+ *
+ * Arguments, sizes, results and errors are those of dspark_markov_sample
+ * (the same kernel, bit-identical ids), minus workspace and
+ * workspace_bytes; sizes beyond the array (num_reqs > 16 or k > 32) return
+ * DSPARK_ERR_SHAPE before anything is enqueued, and a failed set-up returns
+ * DSPARK_ERR_HIP. Every call on a GPU shares that GPU's array, which keeps
+ * the last call's state, as a caller workspace does (see the workspace
+ * contract above): calls on one GPU must be ordered (one stream, or event
+ * dependencies); calls that overlap in time on one GPU race and give
+ * undefined ids.
+ */
+dspark_status dspark_markov_sample_noalloc(const float* base, int num_reqs, int B, int V,
+                                           const uint16_t* w1, const uint16_t* w2, int r,
+                                           const int64_t* d2t, const int64_t* prev0, int k,
+                                           int64_t* ids_out, void* stream);
+
+/*
  * dspark_markov_set_spin_limit -- the bound of the Markov loop's grid-wide
  * waits, in polls (each a few hundred nanoseconds); 0 restores the default
  * (2^18 polls, ~0.3 s). Returns the previous setting. It applies to every

@@ -124,6 +124,27 @@ def test_markov_spin_limit_setting(L):
     assert f(0) == 1 << 18
 
 
+def test_markov_noalloc_errors(L):
+    """The allocation-free loop rejects what dspark_markov_sample rejects,
+    before its static workspace is set up or anything is launched."""
+    f = L.dspark_markov_sample_noalloc
+    good = dict(base=A, R=1, B=7, V=151936, w1=A, w2=A2, r=256, d2t=None, prev0=A, k=7, ids=A2)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["base"], a["R"], a["B"], a["V"], a["w1"], a["w2"], a["r"], a["d2t"], a["prev0"], a["k"],
+                 a["ids"], None)
+    assert call(base=None) == ERR_NULL
+    assert call(w2=None) == ERR_NULL
+    assert call(ids=None) == ERR_NULL
+    assert call(R=17) == ERR_SHAPE         # beyond the static workspace
+    assert call(B=40, k=33) == ERR_SHAPE   # beyond the static workspace
+    assert call(k=8) == ERR_SHAPE
+    assert call(r=12) == ERR_SHAPE
+    assert call(w1=MIS) == ERR_ALIGN
+    assert call(ids=A2 + 4) == ERR_ALIGN
+
+
 def test_markov_workspace_bytes(L):
     f = L.dspark_markov_workspace_bytes
     assert f(0, 7, 100) == 0 and f(17, 7, 100) == 0 and f(1, 0, 100) == 0 and f(1, 7, 0) == 0
