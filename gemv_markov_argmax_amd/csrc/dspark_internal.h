@@ -242,6 +242,11 @@ hipError_t launch_markov_q8(const float* base, int R, int B, int V, const int8_t
 hipError_t launch_probe(const float* x, int M, int D, const uint16_t* w, float bias,
                         float threshold, float* logit, int32_t* pass, hipStream_t stream);
 
+// Streaming read of [buf, buf + bytes) by `groups` workgroups of `threads`
+// (256, 512 or 1024), one word per workgroup into sink (a measurement aid).
+hipError_t launch_stream_read(const void* buf, size_t bytes, int groups, int threads, uint32_t* sink,
+                              hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -40,6 +40,7 @@ SIGNATURES = {
                                 _p, _sz, _p]),
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_set_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
+    "dspark_stream_read": (_i, [_p, _sz, _i, _i, _p, _p]),
     "dspark_markov_sample_noalloc": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -353,6 +354,20 @@ def markov_workspace(num_reqs: int, k: int, V: int, device) -> torch.Tensor:
     if n == 0:
         raise ValueError("sizes out of range for the Markov loop")
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def stream_read(buf: torch.Tensor, groups: int, threads: int, sink: torch.Tensor | None = None,
+                nbytes: int | None = None) -> torch.Tensor:
+    """Streaming read of a device tensor's bytes (dspark_stream_read, a
+    measurement aid); returns the per-workgroup sink words."""
+    if not buf.is_cuda:
+        raise ValueError("buf must be a device tensor")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if sink is None:
+        sink = torch.empty(groups, dtype=torch.int32, device=buf.device)
+    _check(lib().dspark_stream_read(buf.data_ptr() if n else None, n, groups, threads, sink.data_ptr(),
+                                    _stream(buf)))
+    return sink
 
 
 def markov_set_spin_limit(polls: int) -> int:

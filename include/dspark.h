@@ -491,6 +491,23 @@ dspark_status dspark_draft_block(const uint16_t* w_qkv, const uint16_t* w_o, con
                                  const int32_t* ctx_len, float eps, int block_causal, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * dspark_stream_read -- a measurement aid, not a step of the method: a
+ * plain streaming read of `bytes` bytes at `buf` by `groups` workgroups of
+ * `threads` threads, workgroup b reading the b-th contiguous share with
+ * 16-byte non-temporal loads and writing one word (a fold of what it read)
+ * to sink[b]. It measures the device's HBM read ceiling at a given launch
+ * shape, beside the round's kernels, in the same run; the pages judge the
+ * round's GEMVs against a bandwidth bound ([W7] "W7 LANDED"; [SI441]
+ * "Observation"). With bytes == 0 it is an empty launch (the launch-latency
+ * floor).
+ *   buf   device memory, 16-byte aligned (may be NULL when bytes == 0)
+ *   sink  uint32 [groups], device memory, overwritten
+ * Sizes: bytes % 16 == 0, 1 <= groups <= 65536, threads 256, 512 or 1024.
+ */
+dspark_status dspark_stream_read(const void* buf, size_t bytes, int groups, int threads, uint32_t* sink,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

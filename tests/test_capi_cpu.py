@@ -145,6 +145,18 @@ def test_markov_noalloc_errors(L):
     assert call(ids=A2 + 4) == ERR_ALIGN
 
 
+def test_stream_read_errors(L):
+    f = L.dspark_stream_read
+    assert f(None, 4096, 8, 256, A, None) == ERR_NULL
+    assert f(A, 4096, 8, 256, None, None) == ERR_NULL
+    assert f(A, 4096, 0, 256, A2, None) == ERR_SHAPE
+    assert f(A, 4096, 65537, 256, A2, None) == ERR_SHAPE
+    assert f(A, 4096, 8, 128, A2, None) == ERR_SHAPE
+    assert f(A, 4100, 8, 256, A2, None) == ERR_SHAPE   # bytes % 16 != 0
+    assert f(MIS, 4096, 8, 256, A2, None) == ERR_ALIGN
+    assert f(A, 4096, 8, 256, A2 + 2, None) == ERR_ALIGN
+
+
 def test_markov_workspace_bytes(L):
     f = L.dspark_markov_workspace_bytes
     assert f(0, 7, 100) == 0 and f(17, 7, 100) == 0 and f(1, 0, 100) == 0 and f(1, 7, 0) == 0
