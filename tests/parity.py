@@ -23,6 +23,18 @@ LOGIT_ATOL = 1e-3
 LOGIT_RTOL = 1e-3
 PROBE_RTOL = 1e-4
 
+# Every near-tie met by any test of the session (id checks and probe gates),
+# with the test that met it; conftest.py prints them in the terminal summary
+# and, when DSPARK_NEAR_TIES_JSON names a file, writes them there.
+NEAR_TIES: list = []
+
+
+def _record(kind, recs):
+    import os
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    for r in recs:
+        NEAR_TIES.append(dict(kind=kind, test=test, **(r if isinstance(r, dict) else {"row": r})))
+
 
 def say(*a):
     print(*a, flush=True)
@@ -50,6 +62,7 @@ def probe_close(gpu_logit, gpu_pass, ref_logit, ref_pass, threshold):
     err = np.abs(gl - rl)
     assert np.all(err <= win), f"probe logit off: max err {err.max():.3e}"
     near = np.abs(rl - threshold) < win
+    _record("probe gate", [dict(row=int(m), logit=float(rl[m]), threshold=float(threshold)) for m in np.flatnonzero(near)])
     if gpu_pass is not None:
         gp = np.asarray(gpu_pass).astype(bool)
         mism = (gp != np.asarray(ref_pass)) & ~near
@@ -94,6 +107,7 @@ def check_markov(gpu_ids, base, w1, w2, prev0, k, d2t=None, report=None):
             prev = g_tok  # equal to the oracle's token unless a near-tie was taken the other way
     if report is not None:
         report.extend(near)
+    _record("drafted id", near)
     if near:
         say(f"  near-ties (margin < {oracle.NEAR_TIE}): {len(near)}")
         for rec in near[:20]:
