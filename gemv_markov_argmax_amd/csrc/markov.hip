@@ -80,11 +80,23 @@ constexpr int kMaxGroups = 256;          // grid cap: one workgroup per CU
 constexpr int kLoopWavesMax = 8;
 constexpr size_t kCtlBytes = 256;        // control words, then two slot buffers
 constexpr size_t kSlotsPerBuffer = static_cast<size_t>(kMaxSteps) * kMaxReqs * kMaxGroups;
+// Copies of every key slot: each workgroup publishes its key into all of
+// them and polls the one of its own index modulo the copies, so the 256
+// polling waves spread over that many separate memory regions instead of
+// all reading the same few lines. A copy takes kCopyStride slots of a
+// buffer; calls whose k * R * G slots do not fit use fewer copies.
+// Measured on MI355X: 40.1 -> 39.0 us per call at the Qwen3-8B head, 119 ->
+// 115 us at the 27B lane (polling two reads in flight, or re-reading only
+// the empty slots, or longer sleeps between polls, did not help).
+constexpr int kMaxRep = 8;
+constexpr size_t kCopyStride = kSlotsPerBuffer / kMaxRep;
+
 // Control words (uint32) at the start of the workspace.
 constexpr int kCtlState = 0;       // kStateOk, kStateTimedOut (a poll gave up) or kStateRepaired
 constexpr int kCtlSeq = 1;         // call sequence number; its parity selects the active slot buffer
 constexpr int kCtlRepairedBy = 2;  // launch number of the call that repaired the workspace
-constexpr int kCtlUsed = 4;        // [4 + b]: slots the last call that used buffer b wrote
+constexpr int kCtlUsed = 4;        // [4 + b]: slots per copy the last call that used buffer b wrote
+constexpr int kCtlReps = 6;        // [6 + b]: copies that call wrote
 constexpr uint32_t kStateOk = 0;
 constexpr uint32_t kStateTimedOut = 1;  // any value but kStateOk and kStateRepaired is treated so
 constexpr uint32_t kStateRepaired = 2;
@@ -103,6 +115,7 @@ struct MarkovParams {
   uint32_t* ctl;         // control words (kCtl*)
   uint64_t* slots;       // [2][kSlotsPerBuffer]; active buffer: [k][R][G] per-workgroup best keys
   int R, B, V, r, k, G, tiles;
+  int nrep;              // copies of the key slots this call writes (1..kMaxRep)
   int lds_tiles;         // markov_w2 tiles held in LDS per workgroup
   int bstride;           // floats per request in the LDS base slice (>= 16 * tiles per workgroup)
   int base_in_lds;       // 0: base values are read straight from memory (slice too large)
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   // LDS tiles: eight loads per thread in flight at a time, then their LDS
   // writes (one load and write after the other would serialize the latency).
   {
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const int nl = (nheld - nreg) * KB * kWave;
     for (int e0 = 0; e0 < nl; e0 += kBatch * kLoopThreads) {
       BF v[kBatch];
@@ -281,16 +294,20 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   const int cur = static_cast<int>(seq & 1u);
   uint64_t* part = p.slots + cur * kSlotsPerBuffer;
   const uint32_t used_other = load_coherent(p.ctl + kCtlUsed + (cur ^ 1));
+  const uint32_t reps_other = load_coherent(p.ctl + kCtlReps + (cur ^ 1));
   // Clears what the previous call left in the other buffer (which the next
   // call uses), shared by the workgroups that finish early: all but 0, or 0
   // alone. These stores stay out of the step loop: a store in flight would
   // make a wave drain its outstanding loads before it may use any of them.
   auto clear_other = [&]() {
     uint64_t* other = p.slots + (cur ^ 1) * kSlotsPerBuffer;
-    const uint32_t used = min(used_other, static_cast<uint32_t>(kSlotsPerBuffer));
+    const uint32_t reps = min(max(reps_other, 1u), static_cast<uint32_t>(kMaxRep));
+    const uint32_t used = min(used_other, static_cast<uint32_t>(reps > 1 ? kCopyStride : kSlotsPerBuffer));
     const uint32_t nwg = G > 1 ? G - 1 : 1, wg = G > 1 ? blockIdx.x - 1 : 0;
-    for (uint32_t e = wg * kLoopThreads + tid; e < used; e += nwg * kLoopThreads)
-      __hip_atomic_store(other + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (uint32_t e = wg * kLoopThreads + tid; e < used * reps; e += nwg * kLoopThreads) {
+      const uint32_t c = e / used, o = e - c * used;
+      __hip_atomic_store(other + c * kCopyStride + o, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   };
   // Workgroup 0 after the last step (every other workgroup has published
   // every step, so none reads a slot any more): the ids of all steps, the
@@ -310,6 +327,8 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     }
     if (tid == 0 && !bad) {
       __hip_atomic_store(p.ctl + kCtlUsed + cur, static_cast<uint32_t>(p.k * R * G), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctl + kCtlReps + cur, static_cast<uint32_t>(p.nrep), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctl + kCtlSeq, seq + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (state == kStateRepaired)
@@ -332,6 +351,8 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       } else {
         __hip_atomic_store(p.ctl + kCtlUsed + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.ctl + kCtlUsed + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctl + kCtlReps + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctl + kCtlReps + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.ctl + kCtlRepairedBy, p.nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.ctl + kCtlState, kStateRepaired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -667,12 +688,13 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       for (int v = 0; v < 4; ++v) keys_s[w * kMaxReqs + 4 * g + v] = best[v];
     __syncthreads();  // keys complete; every wave is done with this step's A block and base slice
 
-    // ---- publish this workgroup's key of every request
-    if (tid < R) {
-      uint64_t kk = keys_s[tid];
-      for (int ww = 1; ww < NW; ++ww) kk = umax64(kk, keys_s[ww * kMaxReqs + tid]);
-      __hip_atomic_store(part + (static_cast<size_t>(step) * R + tid) * G + blockIdx.x, kk, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    // ---- publish this workgroup's key of every request, into every copy
+    if (tid < R * p.nrep) {
+      const int m = tid % R, c = tid / R;
+      uint64_t kk = keys_s[m];
+      for (int ww = 1; ww < NW; ++ww) kk = umax64(kk, keys_s[ww * kMaxReqs + m]);
+      __hip_atomic_store(part + c * kCopyStride + (static_cast<size_t>(step) * R + m) * G + blockIdx.x, kk,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (last && blockIdx.x != 0) {  // only workgroup 0 needs the final step's winner
       clear_other();
@@ -694,11 +716,11 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     for (int h = 0; h < kMaxReqs / NW; ++h) {
       const int m = w + h * NW;
       if (m >= R) break;
-      const uint64_t* src = part + (static_cast<size_t>(step) * R + m) * G;
+      const uint64_t* src = part + (blockIdx.x % p.nrep) * kCopyStride + (static_cast<size_t>(step) * R + m) * G;
       uint64_t kk = 0;
       uint32_t spins = 0;
+      uint64_t slot[kMaxPoll];
       for (;;) {
-        uint64_t slot[kMaxPoll];
         bool have = true;
 #pragma unroll
         for (int u = 0; u < kMaxPoll; ++u) {
@@ -707,28 +729,22 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
         }
 #pragma unroll
         for (int u = 0; u < kMaxPoll; ++u) have = have && slot[u] != 0ull;
-        if (__all(have)) {
-#pragma unroll
-          for (int u = 0; u < kMaxPoll; ++u) {
-            const int j = ll + u * kWave;
-            if (j < G) kk = umax64(kk, slot[u]);
-          }
-          break;
-        }
+        if (__all(have)) break;
         if (++spins > p.spin_limit) {
           // Mark the workspace; the fence makes the mark visible before any
           // later key of this workgroup, so workgroup 0, which sees those
           // keys, sees the mark when it writes the ids.
-          if (lane == 0) __hip_atomic_store(p.ctl + kCtlState, kStateTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0)
+            __hip_atomic_store(p.ctl + kCtlState, kStateTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-#pragma unroll
-          for (int u = 0; u < kMaxPoll; ++u) {
-            const int j = lane + u * kWave;
-            if (j < G) kk = umax64(kk, slot[u]);
-          }
           break;
         }
         __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int u = 0; u < kMaxPoll; ++u) {
+        const int j = lane + u * kWave;
+        if (j < G) kk = umax64(kk, slot[u]);
       }
       kk = row_max64(kk);
       kk = umax64(kk, __shfl_xor(kk, 16));
@@ -765,6 +781,9 @@ constexpr size_t kBaseLdsMax = 64 * 1024;  // larger base slices are read straig
 // markov_w2 tiles held in registers per wave (the largest counts that leave
 // no register spills; one wave per SIMD is built for bf16 at r = 256 only).
 // A Q8_0 tile takes half the registers of a bf16 one, plus its scales.
+// (One wave per SIMD holds 11 tiles only with the base read straight from
+// memory in the scoring, which made the 27B-lane loop 115 -> 167 us; with the
+// base slice in LDS the eleventh tile spills.)
 constexpr int reg_tiles(int NW, int KB, bool Q8, bool BL = true) {
   if (Q8) return NW != 8 ? 0 : KB <= 2 ? 6 : KB == 4 ? 5 : KB == 8 ? (BL ? 3 : 1) : KB == 16 ? 1 : 0;
   return NW == 4 ? (KB == 8 ? 10 : 0) : KB <= 4 ? 4 : KB == 8 ? 3 : (KB == 16 ? 1 : 0);
@@ -875,6 +894,10 @@ hipError_t launch_markov_any(MarkovParams prm, bool q8, const ProbeArgs* probe, 
   }
   prm.G = pl.G;
   prm.tiles = tiles;
+  {
+    const size_t per_copy = static_cast<size_t>(k) * R * pl.G;
+    prm.nrep = static_cast<int>(std::max<size_t>(1, std::min<size_t>(kMaxRep, kCopyStride / per_copy)));
+  }
   uint32_t nonce = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
   if (nonce == 0u) nonce = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
   prm.nonce = nonce;
