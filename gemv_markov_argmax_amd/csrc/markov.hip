@@ -566,6 +566,20 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       }
     };
 
+    // The first tile of this wave beyond on-chip capacity, if any (one wave
+    // per SIMD only): its fragments are loaded before the on-chip tiles are
+    // computed, so their memory round trip overlaps that work (a single
+    // request: with four rows per lane the registers spill). (frag_of
+    // clamps the row, so a wave without such a tile loads a valid row it
+    // never uses.)
+    constexpr bool kStreamPre = NW == 4 && !Q8 && NV == 1;
+    const int js0 = nheld + (((nreg + w - nheld) % NW) + NW) % NW;
+    BF spre[kStreamPre ? KB : 1];
+    if constexpr (kStreamPre) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) spre[kb] = frag_of(js0, kb, li, lg);
+    }
+
     // The scores of every tile of this workgroup.
     {
     // Register tiles and the wave's first LT LDS tiles, all accumulation
@@ -662,7 +676,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       score(j, true, acc);
     }
     // Tiles beyond on-chip capacity are read from memory at every step.
-    for (int j = nheld + (((nreg + w - nheld) % NW) + NW) % NW; j < nt; j += NW) {
+    for (int j = js0; j < nt; j += NW) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       uint32_t sc1[Q8 ? kSH : 1];
       if constexpr (Q8) scales_of(j, li, sc1);
@@ -670,7 +684,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       for (int kb = 0; kb < KB; ++kb) {
         float s1[4];
         a_scales(kb, s1);
-        mac(acc, a_frag[4 * kb], frag_of(j, kb, li, lg), sc1, kb, s1);
+        mac(acc, a_frag[4 * kb], kStreamPre && j == js0 ? spre[kStreamPre ? kb : 0] : frag_of(j, kb, li, lg), sc1, kb, s1);
       }
       score(j, true, acc);
     }
