@@ -232,8 +232,12 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
     }
   };
   // Tiles [c0, c1), two per iteration; the back edge carries b0 older than b1.
+  // An odd last tile is computed alone (a chunk has an even number of tiles
+  // except the last one, after which nothing reads b0 or b1 before the next
+  // prologue).
   auto run_tiles = [&]() {
-    for (int rr = c0; rr < c1; rr += 2) {
+    int rr = c0;
+    for (; rr + 2 <= c1; rr += 2) {
       compute_publish(b0, s0, 0);
       load(b0, s0, rr + 2);
       __syncthreads();
@@ -241,7 +245,12 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
       compute_publish(b1, s1, 1);
       load(b1, s1, rr + 3);
       __syncthreads();
-      if (rr + 1 < c1) reduce(1, rr + 1);
+      reduce(1, rr + 1);
+    }
+    if (rr < c1) {
+      compute_publish(b0, s0, 0);
+      __syncthreads();
+      reduce(0, rr);
     }
   };
   auto write_out = [&]() {
