@@ -491,12 +491,13 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
       *yl = ph == 0 ? y : *yl + y;
     }
   };
-  // Tiles [c0, c1), two per iteration with a single exit: the back edge
-  // always carries b0 older than b1, so the head waits for b0 alone. Chunks
-  // are even sized but the last; its odd tail runs the second half on the
-  // zeros of tile c1 and keeps nothing.
+  // Tiles [c0, c1), two per iteration: the back edge always carries b0
+  // older than b1, so the head waits for b0 alone. Chunks are even sized but
+  // the last; its odd last tile is computed alone (after it nothing reads b0
+  // or b1 before the next prologue).
   auto run_tiles = [&]() {
-    for (int rr = c0; rr < c1; rr += 2) {
+    int rr = c0;
+    for (; rr + 2 <= c1; rr += 2) {
       compute_publish(b0, 0);
       load(b0, rr + 2);
       __syncthreads();
@@ -504,7 +505,12 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
       compute_publish(b1, 1);
       load(b1, rr + 3);
       __syncthreads();
-      if (rr + 1 < c1) reduce(1, rr + 1);
+      reduce(1, rr + 1);
+    }
+    if (rr < c1) {
+      compute_publish(b0, 0);
+      __syncthreads();
+      reduce(0, rr);
     }
   };
   // The chunk's outputs, row by row: columns [r0 + 16*c0, min(r1, r0 + 16*c1)).
