@@ -46,6 +46,7 @@ struct Q8Params {
 
 constexpr int kQNW = 16;  // waves per workgroup
 constexpr size_t kQLds = 160 * 1024;
+constexpr int kQShortTiles = 16;  // workgroups with at most this many tiles take gemv_q8_short_kernel
 
 __device__ __forceinline__ int2 q8_rows(const Q8Params& p) {
   const int b = blockIdx.x;
@@ -286,6 +287,220 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
   }
 }
 
+// Short variant: at most kQShortTiles tiles per workgroup (the projections
+// of a draft layer, where a workgroup often has a single tile). The
+// streaming kernel above issues a tile's activations and weights and then
+// waits for both before any MFMA: with one tile per workgroup that is one
+// long memory round trip. Here K is covered in phases of 16 * KBW blocks,
+// and the activations and weights of phase P + 1 are in flight while phase
+// P is converted, multiplied and reduced (as in the bf16 short kernel).
+// Per phase, each wave stages its 16 x 32*KBW-byte segment of the tile (and
+// the segment's block scales) in a private LDS area; its activations are
+// split into bf16 hi/lo in registers while the weights are on their way.
+// MANY: several tiles per workgroup, one tile of weights in flight per wave,
+// the next issued as soon as the current one is in LDS. The per-block
+// arithmetic and the wave-order sum are those of the streaming kernel.
+template <bool PACK, int KBW, bool MANY>
+__global__ __launch_bounds__(kQNW * kWave) void gemv_q8_short_kernel(Q8Params p) {
+  static_assert(KBW == 2 || KBW == 4 || KBW == 8, "16-row tiles need 2, 4 or 8 blocks per wave");
+  constexpr int NW = kQNW;
+  constexpr int SEG = 32 * KBW;     // quant bytes of a row segment
+  constexpr int RS = SEG + 16;      // padded LDS row stride
+  constexpr int LPR = SEG / 16;     // lanes per row in a load instruction
+  constexpr int RPI = kWave / LPR;  // rows per load instruction
+  constexpr int NLD = 16 / RPI;     // load instructions per tile
+  constexpr int SPL = (KBW + 3) / 4;  // scale loads per lane and tile
+  constexpr int F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16, XH = PACK ? 1 : 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* tr = smem;                                                           // [NW][16][RS] quants
+  uint16_t* sc = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(NW) * 16 * RS);  // [NW][16][KBW] scales
+  float* red = reinterpret_cast<float*>(sc + NW * 16 * KBW);                         // [2][NW][ROWS][16]
+  float* ysum = red + 2 * NW * ROWS * 16;                                            // [tiles][ROWS][16]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int K = p.K, M = p.M;
+  const int KB = K / 32;
+  const int phases = (KB + NW * KBW - 1) / (NW * KBW);
+
+  const int2 rows = q8_rows(p);
+  const int r0 = rows.x, r1 = rows.y;
+  const int rounds = (r1 - r0 + 15) / 16;
+  const int lrow = lane / LPR, lchunk = lane % LPR;
+  unsigned char* wr_base = tr + (w * 16 + lrow) * RS + 16 * lchunk;  // + RPI*q*RS
+  const unsigned char* rd_base = tr + (w * 16 + i) * RS + 8 * g;     // + 32*kb
+  uint16_t* wsc = sc + w * 16 * KBW;
+
+  const uint32_t rowb = static_cast<uint32_t>(K);       // quant bytes per row
+  const uint32_t drow = static_cast<uint32_t>(KB) * 2;  // scale bytes per row
+  const BufRes qres = buf_res(p.Wq + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
+  const BufRes dres = buf_res(p.Wd + static_cast<size_t>(r0) * KB, static_cast<uint32_t>(r1 - r0) * drow);
+  const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+
+  // Phase ph, tile t: lane offsets of the quants (16 bytes of row lrow) and
+  // of the scales (row i, blocks g + 4j of the segment). A lane past K or
+  // past the segment, or a phase past the last, reads zeros.
+  auto q_off = [&](int ph, int t) -> uint32_t {
+    const int kseg = SEG * (ph * NW + w);
+    return (ph < phases) & (kseg + 16 * lchunk < K)
+               ? static_cast<uint32_t>(16 * t + lrow) * rowb + static_cast<uint32_t>(kseg + 16 * lchunk)
+               : kBufOutOfRange;
+  };
+  auto d_off = [&](int ph, int t, int j) -> uint32_t {
+    const int blk = KBW * (ph * NW + w) + g + 4 * j;
+    return (ph < phases) & (g + 4 * j < KBW) & (blk < KB)
+               ? static_cast<uint32_t>(16 * t + i) * drow + static_cast<uint32_t>(blk) * 2
+               : kBufOutOfRange;
+  };
+  auto load = [&](u32x4 (&b)[NLD], uint32_t (&s)[SPL], int ph, int t) {
+    const uint32_t off = q_off(ph, t);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q)
+      b[q] = buf_load16_nt(qres, off + static_cast<uint32_t>(q * RPI) * rowb);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j)
+      s[j] = __builtin_amdgcn_raw_buffer_load_b16(dres, static_cast<int>(d_off(ph, t, j)), 0, 0);
+  };
+  auto stage = [&](const u32x4 (&b)[NLD], const uint32_t (&s)[SPL]) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j)
+      if (g + 4 * j < KBW) wsc[i * KBW + g + 4 * j] = static_cast<uint16_t>(s[j]);
+  };
+  // Activations of phase ph, block kb: k = kseg + 32*kb + 8*g + (0..7) of
+  // row m (packed rows: each lane of a hi/lo pair loads one half).
+  const int m = PACK ? (i & 7) : i;
+  const bool mrow = m < M;
+  const uint32_t xrow = static_cast<uint32_t>(m) * K * 4;
+  auto load_x = [&](float4 (&xr)[KBW][XH], int ph) {
+    const int kseg = SEG * (ph * NW + w);
+    const bool live = (ph < phases) & mrow;
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const int k = kseg + 32 * kb + 8 * g;
+      const uint32_t off = live & (k < K) ? xrow + static_cast<uint32_t>(k) * 4 : kBufOutOfRange;
+      if (PACK) {
+        xr[kb][0] = buf_load_f32x4(xres, off + 16 * (i >> 3));
+      } else {
+        xr[kb][0] = buf_load_f32x4(xres, off);
+        xr[kb][XH - 1] = buf_load_f32x4(xres, off + 16);
+      }
+    }
+  };
+  auto split = [&](const float4 (&xr)[KBW][XH], u32x4 (&afr)[KBW][F]) {
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      float4 x0 = xr[kb][0], x1 = xr[kb][XH - 1];
+      if (PACK) pair_halves(xr[kb][0], i, x0, x1);
+      const uint2 sa = split_bf16x2(x0.x, x0.y), sb = split_bf16x2(x0.z, x0.w);
+      const uint2 sc2 = split_bf16x2(x1.x, x1.y), sd = split_bf16x2(x1.z, x1.w);
+      const u32x4 h = {sa.x, sb.x, sc2.x, sd.x}, l = {sa.y, sb.y, sc2.y, sd.y};
+      if (PACK) {
+        afr[kb][0] = (i >> 3) ? l : h;
+      } else {
+        afr[kb][0] = h;
+        afr[kb][F - 1] = l;
+      }
+    }
+  };
+  // The staged segment: per block, the exact bf16 conversion of 8 quants,
+  // a fresh MFMA (hi, then lo), scaled by row i's block scale and added.
+  auto mma_publish = [&](const u32x4 (&afr)[KBW][F], int buf) {
+    float scale[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) scale[kb] = half_bits_to_float(wsc[i * KBW + kb]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const u32x4 bv = q8x8_to_bf16(*reinterpret_cast<const uint2*>(rd_base + 32 * kb));
+      f32x4 acc = mfma_16x16x32(afr[kb][0], bv, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (!PACK) acc = mfma_16x16x32(afr[kb][F - 1], bv, acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot[v] = __builtin_fmaf(acc[v], scale[kb], tot[v]);
+    }
+    float* dst = red + (buf * NW + w) * ROWS * 16;
+    if (PACK) {
+      // lanes 0..31 hold rows 0..7 (hi), lanes 32..63 rows 8..15 (lo) of the same columns
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float lo = __shfl_down(tot[v], 32);
+        if (g < 2) dst[(4 * g + v) * 16 + i] = tot[v] + lo;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[(4 * g + v) * 16 + i] = tot[v];
+    }
+  };
+  // Wave-order sum of tile t into the LDS outputs (phases add, in order).
+  auto reduce = [&](int buf, int t, int ph) {
+    if (tid < ROWS * 16) {
+      float y = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) y += red[(buf * NW + ww) * ROWS * 16 + tid];
+      float* ys = ysum + t * ROWS * 16 + tid;
+      *ys = ph == 0 ? y : *ys + y;
+    }
+  };
+
+  float4 xr[KBW][XH];
+  u32x4 b[NLD], afr[KBW][F];
+  uint32_t s[SPL];
+  if (!MANY) {
+    // One tile: phase ph + 1's activations go out before phase ph's MFMAs,
+    // its weights right after them (when their registers are free); the
+    // last phase is peeled so that nothing is loaded past it.
+    auto phase = [&](int ph, auto more) {
+      __builtin_amdgcn_sched_barrier(0);
+      split(xr, afr);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(b, s);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(more)::value) load_x(xr, ph + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_publish(afr, ph & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(more)::value) load(b, s, ph + 1, 0);
+      __syncthreads();
+      reduce(ph & 1, 0, ph);
+    };
+    load_x(xr, 0);
+    load(b, s, 0, 0);
+    int ph = 0;
+    for (; ph + 1 < phases; ++ph) phase(ph, std::true_type{});
+    phase(ph, std::false_type{});
+  } else {
+    load_x(xr, 0);
+    load(b, s, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    split(xr, afr);
+    int j = 0;  // items so far: parity of the reduction buffer
+    for (int ph = 0; ph < phases; ++ph) {
+      for (int t = 0; t < rounds; ++t, ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        stage(b, s);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool last_t = t + 1 == rounds;
+        const bool more = !last_t || ph + 1 < phases;
+        if (last_t && more) load_x(xr, ph + 1);
+        if (more) load(b, s, last_t ? ph + 1 : ph, last_t ? 0 : t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_publish(afr, j & 1);
+        __syncthreads();
+        reduce(j & 1, t, ph);
+        if (last_t && more) split(xr, afr);
+      }
+    }
+  }
+  __syncthreads();
+  // Outputs, once: tile t covers columns r0 + 16t + (0..15).
+  for (int e = tid; e < rounds * M * 16; e += NW * kWave) {
+    const int t = e / (M * 16), rem = e - t * M * 16, mm = rem >> 4, col = rem & 15;
+    const int n = r0 + 16 * t + col;
+    if (n < r1) p.Y[static_cast<size_t>(mm) * p.ldy + n] = ysum[(t * ROWS + mm) * 16 + col];
+  }
+}
+
 template <bool PACK, int KBW>
 hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
   const void* one = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, false, KBW>);
@@ -299,6 +514,22 @@ hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipS
   Q8Params a = prm;
   void* args[] = {&a};
   return hipLaunchKernel(multi ? many : one, dim3(grid), dim3(kQNW * kWave), args, lds, st);
+}
+
+template <bool PACK, int KBW>
+hipError_t launch_q8_short(const Q8Params& prm, int grid, size_t lds, bool many, hipStream_t st) {
+  const void* one = reinterpret_cast<const void*>(&gemv_q8_short_kernel<PACK, KBW, false>);
+  const void* several = reinterpret_cast<const void*>(&gemv_q8_short_kernel<PACK, KBW, true>);
+  static const hipError_t attr = [&] {
+    const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kQLds));
+    return e != hipSuccess ? e
+                           : hipFuncSetAttribute(several, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kQLds));
+  }();
+  if (attr != hipSuccess) return attr;
+  Q8Params a = prm;
+  void* args[] = {&a};
+  return hipLaunchKernel(many ? several : one, dim3(grid), dim3(kQNW * kWave), args, lds, st);
 }
 
 }  // namespace
@@ -324,15 +555,6 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
     const int mm = std::min(16, M - m0);
     const bool pack = mm <= 8;
     const int rowsl = pack ? 8 : 16;
-    // 8 blocks (256 quant bytes of a row) per wave and phase keep twice the
-    // bytes in flight of 4; rows of 9..16 activations take 4 (registers).
-    const int kbw = pack ? 8 : 4;
-    const bool multi = (KB + kQNW * kbw - 1) / (kQNW * kbw) > 1;
-    const size_t fixed = static_cast<size_t>(kQNW) * 16 * (32 * kbw + 16) + static_cast<size_t>(kQNW) * 16 * kbw * 2 +
-                         static_cast<size_t>(2) * kQNW * rowsl * 16 * 4;
-    const size_t per_tile = static_cast<size_t>(mm) * 16 * 4;
-    int chunk = static_cast<int>((kQLds - fixed) / per_tile) & ~1;
-    chunk = std::max(2, std::min(chunk, (rounds + 1) & ~1));
     Q8Params prm{};
     prm.Wq = Wq;
     prm.Wd = Wd;
@@ -342,9 +564,32 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
     prm.K = K;
     prm.M = mm;
     prm.ldy = N;
-    prm.chunk = chunk;
     prm.pq = (N / 2) / grid;
     prm.prem = (N / 2) % grid;
+    if (rounds <= kQShortTiles) {
+      // Few tiles per workgroup. 4 blocks (128 quant bytes of a row) per
+      // wave and phase, one tile or several: measured on MI355X at the
+      // projections of a draft layer (M = 7 and 15), 2 blocks was as fast or
+      // slower, 8 no faster where it does not spill.
+      constexpr int kbw = 4;
+      const size_t lds = static_cast<size_t>(kQNW) * 16 * (32 * kbw + 16) + static_cast<size_t>(kQNW) * 16 * kbw * 2 +
+                         static_cast<size_t>(2) * kQNW * rowsl * 16 * 4 + static_cast<size_t>(rounds) * rowsl * 16 * 4;
+      const bool many = rounds > 1;
+      const hipError_t e = pack ? launch_q8_short<true, kbw>(prm, grid, lds, many, stream)
+                                : launch_q8_short<false, kbw>(prm, grid, lds, many, stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    // 8 blocks (256 quant bytes of a row) per wave and phase keep twice the
+    // bytes in flight of 4; rows of 9..16 activations take 4 (registers).
+    const int kbw = pack ? 8 : 4;
+    const bool multi = (KB + kQNW * kbw - 1) / (kQNW * kbw) > 1;
+    const size_t fixed = static_cast<size_t>(kQNW) * 16 * (32 * kbw + 16) + static_cast<size_t>(kQNW) * 16 * kbw * 2 +
+                         static_cast<size_t>(2) * kQNW * rowsl * 16 * 4;
+    const size_t per_tile = static_cast<size_t>(mm) * 16 * 4;
+    int chunk = static_cast<int>((kQLds - fixed) / per_tile) & ~1;
+    chunk = std::max(2, std::min(chunk, (rounds + 1) & ~1));
+    prm.chunk = chunk;
     const size_t lds = fixed + chunk * per_tile;
     const hipError_t e = pack ? launch_q8<true, 8>(prm, grid, lds, multi, stream)
                               : launch_q8<false, 4>(prm, grid, lds, multi, stream);

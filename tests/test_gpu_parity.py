@@ -115,9 +115,13 @@ def test_lm_head_full_size_sampled(dev):
 GEMV_Q8_CASES = [
     # (M, N, K): one block, K not a multiple of the 128-entry wave segment,
     # several phases with a partial last one, ragged N, both row packings,
-    # more than 16 rows (several launches)
+    # more than 16 rows (several launches). Up to 16 tiles per workgroup
+    # (N up to ~65k rows on 256 CUs) take the short kernel, one tile or
+    # several; longer workgroups the streaming kernel, with one K phase or
+    # several (last three cases).
     (1, 1, 32), (7, 4096, 4096), (7, 4099, 96), (15, 1000, 160), (16, 2049, 4128), (3, 300, 7424),
-    (8, 33, 64), (9, 777, 2080), (20, 515, 256), (4, 65, 5120), (7, 16, 12288),
+    (8, 33, 64), (9, 777, 2080), (20, 515, 256), (4, 65, 5120), (7, 16, 12288), (15, 4096, 4128),
+    (7, 70001, 160), (15, 66003, 2080), (5, 90017, 4160),
 ]
 
 
