@@ -283,6 +283,20 @@ dspark_status dspark_proj_smallm_add(const uint16_t* W, int N, int K, const floa
   return from_hip(dspark::launch_gemv(W, N, K, X, M, Y, static_cast<hipStream_t>(stream), residual));
 }
 
+int dspark_proj_smallm_norm_fits(int N, int K, int M) {
+  return N >= 2 && K >= 8 && (K % 8) == 0 && M >= 1 && dspark::gemv_norm_fits(N, K, M) ? 1 : 0;
+}
+
+dspark_status dspark_proj_smallm_norm(const uint16_t* W, int N, int K, const float* X, int M, const uint16_t* gamma,
+                                      float eps, float* Y, void* stream) {
+  dspark_status st = gemv_checks(W, N, K, X, M, Y);
+  if (st == DSPARK_OK && !gamma) st = DSPARK_ERR_NULL;
+  if (st == DSPARK_OK && (!(eps >= 0.f) || !dspark_proj_smallm_norm_fits(N, K, M))) st = DSPARK_ERR_SHAPE;
+  if (st == DSPARK_OK && !aligned(gamma, 16)) st = DSPARK_ERR_ALIGN;
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv_norm(W, N, K, X, M, gamma, eps, Y, static_cast<hipStream_t>(stream)));
+}
+
 size_t dspark_attention_workspace_bytes(int num_reqs, int B, int H, int Dh, int Lmax) {
   if (!dspark::attention_shape_fits(num_reqs, B, H, Dh, Lmax)) return 0;
   return dspark::attention_workspace_bytes(num_reqs, B, H, Dh, Lmax);
@@ -365,14 +379,29 @@ dspark_status dspark_draft_block(const uint16_t* w_qkv, const uint16_t* w_o, con
   float* act = reinterpret_cast<float*>(base + l.act);
   float* aws = reinterpret_cast<float*>(base + l.attn_ws);
   const int M = num_reqs * B, HD = H * Dh;
-  hipError_t e = dspark::launch_rmsnorm(h_in, M, d, ln1, eps, x, st);
-  if (e == hipSuccess) e = dspark::launch_gemv(w_qkv, 3 * HD, d, x, M, qkv, st);
+  // Each norm runs inside the projection it feeds where that projection's
+  // shape allows (dspark_proj_smallm_norm), else as its own launch.
+  const bool fuse1 = dspark_proj_smallm_norm_fits(3 * HD, d, M) && aligned(ln1, 16);
+  const bool fuse2 = dspark_proj_smallm_norm_fits(2 * F, d, M) && aligned(ln2, 16);
+  hipError_t e = hipSuccess;
+  if (fuse1) {
+    e = dspark::launch_gemv_norm(w_qkv, 3 * HD, d, h_in, M, ln1, eps, qkv, st);
+  } else {
+    e = dspark::launch_rmsnorm(h_in, M, d, ln1, eps, x, st);
+    if (e == hipSuccess) e = dspark::launch_gemv(w_qkv, 3 * HD, d, x, M, qkv, st);
+  }
   if (e == hipSuccess)
     e = dspark::launch_attention(qkv, qkv + HD, qkv + 2 * HD, 3 * HD, num_reqs, B, H, Dh, k_ctx, v_ctx, Lmax, ctx_len,
                                  block_causal ? 1 : 0, attn, aws, st);
   if (e == hipSuccess) e = dspark::launch_gemv(w_o, d, HD, attn, M, h2, st, h_in);
-  if (e == hipSuccess) e = dspark::launch_rmsnorm(h2, M, d, ln2, eps, x, st);
-  if (e == hipSuccess) e = dspark::launch_gemv_gated(w_gate_up, F, d, x, M, act, gu, st);
+  if (e == hipSuccess) {
+    if (fuse2) {
+      e = dspark::launch_gemv_gated_norm(w_gate_up, F, d, h2, M, ln2, eps, act, st);
+    } else {
+      e = dspark::launch_rmsnorm(h2, M, d, ln2, eps, x, st);
+      if (e == hipSuccess) e = dspark::launch_gemv_gated(w_gate_up, F, d, x, M, act, gu, st);
+    }
+  }
   if (e == hipSuccess) e = dspark::launch_gemv(w_down, d, F, act, M, h_out, st, h2);
   return from_hip(e);
 }

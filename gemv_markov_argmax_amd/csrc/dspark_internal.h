@@ -55,6 +55,10 @@ __device__ __forceinline__ float4 buf_load_f32x4(BufRes r, uint32_t off) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
 }
 
+__device__ __forceinline__ uint2 buf_load_b64(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
+}
+
 __device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
 }
@@ -194,6 +198,14 @@ hipError_t launch_rmsnorm(const float* x, int M, int D, const uint16_t* gamma, f
 hipError_t launch_gemv_gated(const uint16_t* W, int F, int K, const float* X, int M, float* act, float* gu,
                              hipStream_t stream);
 hipError_t launch_silu_gate(const float* gu, int M, int F, float* a, hipStream_t st);
+// The GEMVs above with the RMSNorm of X fused into them (see
+// dspark_proj_smallm_norm): Y = rmsnorm(X; gamma, eps) W^T, and the gated
+// form. Only for shapes the short GEMV kernel takes (gemv_norm_fits).
+bool gemv_norm_fits(int N, int K, int M);
+hipError_t launch_gemv_norm(const uint16_t* W, int N, int K, const float* X, int M, const uint16_t* gamma, float eps,
+                            float* Y, hipStream_t stream);
+hipError_t launch_gemv_gated_norm(const uint16_t* W, int F, int K, const float* X, int M, const uint16_t* gamma,
+                                  float eps, float* act, hipStream_t stream);
 bool attention_shape_fits(int R, int B, int H, int Dh, int Lmax);
 size_t attention_workspace_bytes(int R, int B, int H, int Dh, int Lmax);
 hipError_t launch_attention(const float* q, const float* kb, const float* vb, int ld, int R, int B, int H, int Dh,

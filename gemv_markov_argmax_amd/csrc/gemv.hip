@@ -45,6 +45,8 @@ struct GemvParams {
   int chunk;     // gemv_tstream_kernel: tiles whose outputs are staged in LDS at once (even)
   int pq, prem;  // row pairs per workgroup: N/2 = pq * gridDim.x + prem (the first prem get one more)
   const float* res;  // null, or [M, N] (row stride ldy) added to the outputs; may be Y itself
+  const uint16_t* gamma;  // gemv_short_kernel with NORM: the RMSNorm weights bf16 [K]
+  float eps;              // and its epsilon
 };
 
 // The output value of (m, n), plus the residual when there is one (read and
@@ -102,7 +104,14 @@ inline int wg_rows_max(int N, int grid) {
 // halves of activation j land in the same workgroup (rows come in pairs), and
 // the epilogue writes act[m, j] = silu(g) * u, silu(g) = g / (1 + exp(-g)),
 // into Y [M, F]; each row's own value is computed exactly as without GATED.
-template <bool PACK, int KBW, bool MANY, bool GATED = false>
+// NORM (the RMSNorm of X fused in front): the A operand is x * gamma[k],
+// rounded to fp32 and split as above, and each output is scaled at the end
+// by 1 / sqrt(mean_k x[m, k]^2 + eps), the RMSNorm factor of its row m. Each
+// lane sums the squares of the activations it loads itself (every one once,
+// over the phases, in a fixed order); lanes of the same row are then added
+// by a fixed butterfly and the waves in wave order. A row's factor depends on
+// that row alone.
+template <bool PACK, int KBW, bool MANY, bool GATED = false, bool NORM = false>
 __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   constexpr int NW = 16, F = PACK ? 1 : 2, ROWS = PACK ? 8 : 16;
   constexpr int SEG = 64 * KBW;                 // bytes of a row segment
@@ -126,6 +135,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   const int2 rows = wg_rows(p);
   const int r0 = rows.x, r1 = rows.y;
   const int rounds = (r1 - r0 + 15) / 16;
+  float* nrm = ysum + rounds * ROWS * 16;  // NORM: [NW][16] per-wave sums of squares
   const int lrow = lane / LPR, lchunk = lane % LPR;
   unsigned char* wtr = tr + w * 16 * RS;
   unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
@@ -139,6 +149,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   const BufRes wres = GATED ? buf_res(p.W, static_cast<uint32_t>(N) * rowb)
                             : buf_res(p.W + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
   const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+  const BufRes gres = buf_res(NORM ? static_cast<const void*>(p.gamma) : static_cast<const void*>(p.W),
+                              NORM ? static_cast<uint32_t>(K) * 2 : 0u);
   const uint32_t row_off = GATED ? static_cast<uint32_t>((lrow & 1) * (N >> 1) + (r0 >> 1) + (lrow >> 1)) * rowb
                                  : static_cast<uint32_t>(lrow) * rowb;
   const uint32_t tile_step = (GATED ? 8u : 16u) * rowb;  // 16 rows further
@@ -197,7 +209,10 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
   const uint32_t xrow = static_cast<uint32_t>(m) * K * 4;
   // (the conditions combine with & rather than &&: no short-circuit, so the
   // compiler selects offsets instead of branching around the address math)
-  auto load_x = [&](float4 (&xr)[KBW][XH], int ph) {
+  // NORM: gamma of the same entries (8 bytes for a packed lane's half, 16
+  // otherwise), per column, so not masked by the row.
+  constexpr int GN = NORM ? KBW : 1;
+  auto load_x = [&](float4 (&xr)[KBW][XH], u32x4 (&gr)[GN], int ph) {
     const int kseg = 32 * KBW * (ph * NW + w);
     const bool live = (ph < phases) & mrow;
 #pragma unroll
@@ -210,6 +225,15 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
         xr[kb][0] = buf_load_f32x4(xres, off);
         xr[kb][XH - 1] = buf_load_f32x4(xres, off + 16);
       }
+      if constexpr (NORM) {
+        const uint32_t goff = (ph < phases) & (k < K) ? static_cast<uint32_t>(k) * 2 : kBufOutOfRange;
+        if (PACK) {
+          const uint2 v = buf_load_b64(gres, goff + 8 * (i >> 3));
+          gr[kb] = u32x4{v.x, v.y, 0u, 0u};
+        } else {
+          gr[kb] = __builtin_bit_cast(u32x4, buf_load_f32x4(gres, goff));
+        }
+      }
     }
   };
   // Offset of this lane's first weight load in phase ph (tile 0). A lane
@@ -220,11 +244,29 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     return (ph < phases) & (kseg + 8 * lchunk < K) ? row_off + static_cast<uint32_t>(kseg + 8 * lchunk) * 2
                                                    : kBufOutOfRange;
   };
-  auto split = [&](const float4 (&xr)[KBW][XH], u32x4 (&afr)[KBW][F]) {
+  auto gmul = [](float4 x, uint32_t lo, uint32_t hi) {  // x * four bf16 (entry order)
+    return float4{x.x * __uint_as_float(lo << 16), x.y * __uint_as_float(lo & 0xffff0000u),
+                  x.z * __uint_as_float(hi << 16), x.w * __uint_as_float(hi & 0xffff0000u)};
+  };
+  auto sq4 = [](float4 x, float s) {
+    s = __builtin_fmaf(x.x, x.x, s);
+    s = __builtin_fmaf(x.y, x.y, s);
+    s = __builtin_fmaf(x.z, x.z, s);
+    return __builtin_fmaf(x.w, x.w, s);
+  };
+  float ss = 0.f;  // NORM: this lane's sum of squares
+  auto split = [&](const float4 (&xr)[KBW][XH], const u32x4 (&gr)[GN], u32x4 (&afr)[KBW][F]) {
 #pragma unroll
     for (int kb = 0; kb < KBW; ++kb) {
-      float4 x0 = xr[kb][0], x1 = xr[kb][XH - 1];
-      if (PACK) pair_halves(xr[kb][0], i, x0, x1);
+      float4 a0 = xr[kb][0], a1 = xr[kb][XH - 1];
+      if constexpr (NORM) {
+        ss = sq4(a0, ss);
+        if (!PACK) ss = sq4(a1, ss);
+        a0 = gmul(a0, gr[kb].x, gr[kb].y);
+        if (!PACK) a1 = gmul(a1, gr[kb].z, gr[kb].w);
+      }
+      float4 x0 = a0, x1 = a1;
+      if (PACK) pair_halves(a0, i, x0, x1);
       const uint2 s0 = split_bf16x2(x0.x, x0.y), s1 = split_bf16x2(x0.z, x0.w);
       const uint2 s2 = split_bf16x2(x1.x, x1.y), s3 = split_bf16x2(x1.z, x1.w);
       const u32x4 h = {s0.x, s1.x, s2.x, s3.x}, l = {s0.y, s1.y, s2.y, s3.y};
@@ -243,18 +285,18 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     // after them, when their registers are free), so they overlap its
     // reduction and the next split.
     float4 xr[KBW][XH];
-    u32x4 b[NLD], afr[KBW][F];
+    u32x4 b[NLD], afr[KBW][F], gr[GN];
     // (the scheduling barriers keep each step's registers apart: the
     // activations become A fragments, the weights go to LDS, and only then
     // do the next phase's loads reuse those registers; the last phase is
     // peeled so that no load is issued for a phase that does not exist)
     auto phase = [&](int ph, auto more) {
       __builtin_amdgcn_sched_barrier(0);
-      split(xr, afr);
+      split(xr, gr, afr);
       __builtin_amdgcn_sched_barrier(0);
       stage(b);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(more)::value) load_x(xr, ph + 1);
+      if constexpr (decltype(more)::value) load_x(xr, gr, ph + 1);
       __builtin_amdgcn_sched_barrier(0);
       mma_publish(afr, ph & 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -262,7 +304,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
       __syncthreads();
       reduce(ph & 1, 0, ph);
     };
-    load_x(xr, 0);
+    load_x(xr, gr, 0);
     load(b, w_off(0));
     int ph = 0;
     for (; ph + 1 < phases; ++ph) phase(ph, std::true_type{});
@@ -274,11 +316,11 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     // split once per phase. 16 waves x one tile keep enough bytes in flight
     // per CU to cover the memory latency.
     float4 xr[KBW][XH];
-    u32x4 b[NLD], afr[KBW][F];
-    load_x(xr, 0);
+    u32x4 b[NLD], afr[KBW][F], gr[GN];
+    load_x(xr, gr, 0);
     load(b, w_off(0));
     __builtin_amdgcn_sched_barrier(0);
-    split(xr, afr);
+    split(xr, gr, afr);
     int j = 0;  // items so far: parity of the reduction buffer
     for (int ph = 0; ph < phases; ++ph) {
       const uint32_t off = w_off(ph);
@@ -288,24 +330,49 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
         __builtin_amdgcn_sched_barrier(0);
         const bool last_t = t + 1 == rounds;
         const bool more = !last_t || ph + 1 < phases;
-        if (last_t && more) load_x(xr, ph + 1);
+        if (last_t && more) load_x(xr, gr, ph + 1);
         if (more) load(b, last_t ? w_off(ph + 1) : off + static_cast<uint32_t>(t + 1) * tile_step);
         __builtin_amdgcn_sched_barrier(0);
         mma_publish(afr, j & 1);
         __syncthreads();
         reduce(j & 1, t, ph);
-        if (last_t && more) split(xr, afr);
+        if (last_t && more) split(xr, gr, afr);
       }
     }
   }
+  if constexpr (NORM) {
+    // Row sums of squares: the lanes of row m are (m or m + 8 when packed, g = 0..3).
+    float t = ss;
+    if (PACK) t += __shfl_xor(t, 8);
+    t += __shfl_xor(t, 16);
+    t += __shfl_xor(t, 32);
+    if (lane < (PACK ? 8 : 16)) nrm[w * 16 + lane] = t;
+  }
   __syncthreads();
+  // The RMSNorm factor of row mm (1 without NORM).
+  auto rfac = [&](int mm) -> float {
+    if constexpr (!NORM) {
+      (void)mm;
+      return 1.0f;
+    } else {
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) tot += nrm[ww * 16 + mm];
+      return 1.0f / sqrtf(tot / static_cast<float>(K) + p.eps);
+    }
+  };
   if constexpr (GATED) {
     // Activations, once: row pair (n, n + 1) of tile t is (gate, up) of j = n / 2.
     for (int e = tid; e < rounds * M * 8; e += NW * kWave) {
       const int t = e / (M * 8), rem = e - t * M * 8, mm = rem >> 3, pc = rem & 7;
       const int n = r0 + 16 * t + 2 * pc;
       if (n < r1) {
-        const float g = ysum[(t * ROWS + mm) * 16 + 2 * pc], u = ysum[(t * ROWS + mm) * 16 + 2 * pc + 1];
+        float g = ysum[(t * ROWS + mm) * 16 + 2 * pc], u = ysum[(t * ROWS + mm) * 16 + 2 * pc + 1];
+        if constexpr (NORM) {
+          const float rf = rfac(mm);
+          g *= rf;
+          u *= rf;
+        }
         p.Y[static_cast<size_t>(mm) * p.ldy + (n >> 1)] = g / (1.0f + expf(-g)) * u;
       }
     }
@@ -316,7 +383,9 @@ __global__ __launch_bounds__(16 * kWave) void gemv_short_kernel(GemvParams p) {
     const int t = e / (M * 16), rem = e - t * M * 16, mm = rem >> 4, col = rem & 15;
     const int n = r0 + 16 * t + col;
     const size_t idx = static_cast<size_t>(mm) * p.ldy + n;
-    if (n < r1) p.Y[idx] = with_res(p, idx, ysum[(t * ROWS + mm) * 16 + col]);
+    float y = ysum[(t * ROWS + mm) * 16 + col];
+    if constexpr (NORM) y *= rfac(mm);
+    if (n < r1) p.Y[idx] = with_res(p, idx, y);
   }
 }
 
@@ -763,7 +832,9 @@ constexpr int kShortTiles = 16;  // workgroups with at most this many tiles take
 // M <= 16: K slices of 32*KBW per wave, phases for longer K. Workgroups with
 // at most kShortTiles tiles take the short kernel, longer ones the streaming
 // kernel with its LDS output chunks.
-Plan make_plan(int M, int N, int K, int cus) {
+// norm: the NORM variant, whose gamma values take registers: with hi and lo
+// A blocks (M > 8) at most 2 k-blocks per wave (4 spill).
+Plan make_plan(int M, int N, int K, int cus, bool norm = false) {
   Plan pl{};
   pl.pack = M <= 8;
   const int tiles = (N + 15) / 16;
@@ -775,7 +846,7 @@ Plan make_plan(int M, int N, int K, int cus) {
   // Measured on MI355X (M = 7 and 15, K = 4096 and 12288): one tile per
   // workgroup runs fastest with 2 k-blocks per wave and phase, several tiles
   // with 4, and the short kernel beats the streaming one up to 16 tiles.
-  const int kbw_max = pl.shortk ? (pl.many ? 4 : 2) : 4;
+  const int kbw_max = pl.shortk ? (pl.many && !(norm && !pl.pack) ? 4 : 2) : 4;
   int kbw = 1;
   while (kbw < kbw_max && 16 * kbw < KB) kbw *= 2;
   pl.tkbw = kbw;
@@ -783,7 +854,8 @@ Plan make_plan(int M, int N, int K, int cus) {
   const size_t fixed = static_cast<size_t>(16) * 16 * (64 * kbw + 16) + static_cast<size_t>(2) * 16 * rows * 16 * 4;
   if (pl.shortk) {
     pl.chunk = 0;
-    pl.lds = fixed + static_cast<size_t>(rounds) * rows * 16 * 4;  // + the LDS outputs of its tiles
+    pl.lds = fixed + static_cast<size_t>(rounds) * rows * 16 * 4  // + the LDS outputs of its tiles
+             + static_cast<size_t>(16) * 16 * 4;                     // + the NORM variant's row sums
     return pl;
   }
   const size_t per_tile = static_cast<size_t>(M) * 16 * 4;
@@ -811,10 +883,10 @@ hipError_t launch_tstream(const GemvParams& prm, const Plan& pl, hipStream_t st)
   return hipLaunchKernel(phased ? multi : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
 }
 
-template <bool PACK, int KBW, bool GATED = false>
+template <bool PACK, int KBW, bool GATED = false, bool NORM = false>
 hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  const void* one = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, false, GATED>);
-  const void* many = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true, GATED>);
+  const void* one = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, false, GATED, NORM>);
+  const void* many = reinterpret_cast<const void*>(&gemv_short_kernel<PACK, KBW, true, GATED, NORM>);
   static const hipError_t attr = [&] {
     const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
     return e != hipSuccess ? e
@@ -827,36 +899,29 @@ hipError_t launch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   return hipLaunchKernel(pl.many ? many : one, dim3(pl.grid), dim3(16 * kWave), args, pl.lds, st);
 }
 
-hipError_t dispatch_gated(const GemvParams& prm, const Plan& pl, hipStream_t st) {
+template <bool GATED, bool NORM>
+hipError_t dispatch_short(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   if (pl.pack) {
     switch (pl.tkbw) {
-      case 1: return launch_short<true, 1, true>(prm, pl, st);
-      case 2: return launch_short<true, 2, true>(prm, pl, st);
-      default: return launch_short<true, 4, true>(prm, pl, st);
+      case 1: return launch_short<true, 1, GATED, NORM>(prm, pl, st);
+      case 2: return launch_short<true, 2, GATED, NORM>(prm, pl, st);
+      default: return launch_short<true, 4, GATED, NORM>(prm, pl, st);
     }
   }
   switch (pl.tkbw) {
-    case 1: return launch_short<false, 1, true>(prm, pl, st);
-    case 2: return launch_short<false, 2, true>(prm, pl, st);
-    default: return launch_short<false, 4, true>(prm, pl, st);
+    case 1: return launch_short<false, 1, GATED, NORM>(prm, pl, st);
+    case 2: return launch_short<false, 2, GATED, NORM>(prm, pl, st);
+    default:
+      if constexpr (NORM) {
+        return hipErrorInvalidValue;  // the plan caps NORM at 2 here
+      } else {
+        return launch_short<false, 4, GATED, NORM>(prm, pl, st);
+      }
   }
 }
 
 hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
-  if (pl.tkbw > 0 && pl.shortk) {
-    if (pl.pack) {
-      switch (pl.tkbw) {
-        case 1: return launch_short<true, 1>(prm, pl, st);
-        case 2: return launch_short<true, 2>(prm, pl, st);
-        default: return launch_short<true, 4>(prm, pl, st);
-      }
-    }
-    switch (pl.tkbw) {
-      case 1: return launch_short<false, 1>(prm, pl, st);
-      case 2: return launch_short<false, 2>(prm, pl, st);
-      default: return launch_short<false, 4>(prm, pl, st);
-    }
-  }
+  if (pl.tkbw > 0 && pl.shortk) return dispatch_short<false, false>(prm, pl, st);
   if (pl.tkbw > 0) {
     if (pl.pack) {
       switch (pl.tkbw) {
@@ -951,13 +1016,60 @@ hipError_t launch_gemv_gated(const uint16_t* W, int F, int K, const float* X, in
       prm.ldy = F;
       prm.pq = (N / 2) / pl.grid;
       prm.prem = (N / 2) % pl.grid;
-      return dispatch_gated(prm, pl, stream);
+      return dispatch_short<true, false>(prm, pl, stream);
     }
   }
   // Other shapes: the projection into gu [M, 2F], then the gate.
   hipError_t e = launch_gemv(W, N, K, X, M, gu, stream);
   if (e != hipSuccess) return e;
   return launch_silu_gate(gu, M, F, act, stream);
+}
+
+bool gemv_norm_fits(int N, int K, int M) {
+  if (N < 2 || M < 1 || M > 16 || K < 8 || static_cast<long long>(N) * K * 2 >= (1LL << 31)) return false;
+  const int cus = device_cu_count();
+  if (cus <= 0) return false;
+  const Plan pl = make_plan(M, N, K, cus, true);
+  return pl.shortk && pl.tkbw > 0;
+}
+
+hipError_t launch_gemv_norm(const uint16_t* W, int N, int K, const float* X, int M, const uint16_t* gamma, float eps,
+                            float* Y, hipStream_t stream) {
+  if (!gemv_norm_fits(N, K, M)) return hipErrorInvalidValue;
+  const Plan pl = make_plan(M, N, K, device_cu_count(), true);
+  GemvParams prm{};
+  prm.W = W;
+  prm.X = X;
+  prm.Y = Y;
+  prm.N = N;
+  prm.K = K;
+  prm.M = M;
+  prm.ldy = N;
+  prm.pq = (N / 2) / pl.grid;
+  prm.prem = (N / 2) % pl.grid;
+  prm.gamma = gamma;
+  prm.eps = eps;
+  return dispatch_short<false, true>(prm, pl, stream);
+}
+
+hipError_t launch_gemv_gated_norm(const uint16_t* W, int F, int K, const float* X, int M, const uint16_t* gamma,
+                                  float eps, float* act, hipStream_t stream) {
+  const int N = 2 * F;
+  if (F < 1 || !gemv_norm_fits(N, K, M)) return hipErrorInvalidValue;
+  const Plan pl = make_plan(M, N, K, device_cu_count(), true);
+  GemvParams prm{};
+  prm.W = W;
+  prm.X = X;
+  prm.Y = act;
+  prm.N = N;
+  prm.K = K;
+  prm.M = M;
+  prm.ldy = F;
+  prm.pq = (N / 2) / pl.grid;
+  prm.prem = (N / 2) % pl.grid;
+  prm.gamma = gamma;
+  prm.eps = eps;
+  return dispatch_short<true, true>(prm, pl, stream);
 }
 
 }  // namespace dspark

@@ -33,6 +33,8 @@ SIGNATURES = {
     "dspark_rmsnorm": (_i, [_p, _i, _i, _p, _f, _p, _p]),
     "dspark_silu_gate": (_i, [_p, _i, _i, _p, _p]),
     "dspark_proj_smallm_add": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
+    "dspark_proj_smallm_norm_fits": (_i, [_i, _i, _i]),
+    "dspark_proj_smallm_norm": (_i, [_p, _i, _i, _p, _i, _p, _f, _p, _p]),
     "dspark_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_attention_ragged": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _i, _p, _p, _sz, _p]),
     "dspark_draft_block_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -199,6 +201,30 @@ def proj_smallm_add(W: torch.Tensor, X: torch.Tensor, residual: torch.Tensor, ou
     return out
 
 
+def proj_smallm_norm_fits(N: int, K: int, M: int) -> bool:
+    """Whether dspark_proj_smallm_norm takes this shape (dspark_proj_smallm_norm_fits)."""
+    return bool(lib().dspark_proj_smallm_norm_fits(N, K, M))
+
+
+def proj_smallm_norm(W: torch.Tensor, X: torch.Tensor, gamma: torch.Tensor, eps: float,
+                     out: torch.Tensor | None = None):
+    """Y = rmsnorm(X; gamma, eps) @ W.T with the norm fused into the projection
+    (dspark_proj_smallm_norm); gamma bf16 [K]."""
+    _dev(W, torch.bfloat16, "W", 2)
+    _dev(X, torch.float32, "X", 2)
+    _dev(gamma, torch.bfloat16, "gamma", 1)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K or gamma.shape[0] != K:
+        raise ValueError("W [N, K], X [M, K] and gamma [K] required")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _dev(out, torch.float32, "out", 2)
+    _check(lib().dspark_proj_smallm_norm(W.data_ptr(), N, K, X.data_ptr(), M, gamma.data_ptr(), float(eps),
+                                         out.data_ptr(), _stream(W)))
+    return out
+
+
 def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out: torch.Tensor | None = None):
     """x / sqrt(mean(x^2) + eps) * gamma per row (dspark_rmsnorm); gamma bf16 [D]."""
     _dev(x, torch.float32, "x", 2)
@@ -267,9 +293,10 @@ def draft_block_workspace_bytes(R: int, B: int, H: int, Dh: int, d: int, F: int,
 def draft_block_forward(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor,
                         v_ctx: torch.Tensor, ctx_len: torch.Tensor, eps: float, block_causal: bool = False,
                         scratch: dict | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """One draft block (layer) in one C-ABI call (dspark_draft_block): rmsnorm,
-    the fused qkv projection, attention, o with the residual, rmsnorm, the
-    fused gate/up projection, the SiLU gate, and down with the residual. w
+    """One draft block (layer) in one C-ABI call (dspark_draft_block): the
+    fused qkv projection with the rmsnorm in front of it, attention, o with
+    the residual, the fused gate/up projection with its rmsnorm, the SiLU
+    gate, and down with the residual. w
     holds bf16 tensors qkv [3 H Dh, d], o [d, H Dh], gate_up [2F, d],
     down [d, F], ln1, ln2 [d]. ``scratch`` (a dict) keeps the workspace
     between calls; ``out`` may be h itself."""
@@ -321,17 +348,23 @@ def draft_forward(x_in: torch.Tensor, fc: torch.Tensor, layers: list, k_ctx: lis
 def draft_block_forward_calls(h: torch.Tensor, w: dict, R: int, B: int, H: int, Dh: int, k_ctx: torch.Tensor,
                               v_ctx: torch.Tensor, ctx_len: torch.Tensor, eps: float, block_causal: bool = False,
                               out: torch.Tensor | None = None) -> torch.Tensor:
-    """The same block as eight separate C-ABI calls (rmsnorm, proj_smallm,
-    attention_ragged, proj_smallm_add, rmsnorm, proj_smallm, silu_gate,
-    proj_smallm_add); dspark_draft_block must match it bit for bit."""
+    """The same block as separate C-ABI calls: proj_smallm_norm (or rmsnorm
+    then proj_smallm where its shape or the norm weights' alignment rule it
+    out), attention_ragged, proj_smallm_add, proj_smallm_norm (or rmsnorm
+    then proj_smallm), silu_gate, proj_smallm_add; dspark_draft_block must
+    match it bit for bit."""
     M, d = h.shape
     F = w["down"].shape[1]
-    x = rmsnorm(h, w["ln1"], eps)
-    qkv = proj_smallm(w["qkv"], x)
+
+    def normed_proj(W, x, gamma):
+        if proj_smallm_norm_fits(W.shape[0], W.shape[1], x.shape[0]) and gamma.data_ptr() % 16 == 0:
+            return proj_smallm_norm(W, x, gamma, eps)
+        return proj_smallm(W, rmsnorm(x, gamma, eps))
+
+    qkv = normed_proj(w["qkv"], h, w["ln1"])
     attn = attention_ragged(qkv, R, B, H, Dh, k_ctx, v_ctx, ctx_len, block_causal)
     h2 = proj_smallm_add(w["o"], attn, h)
-    x2 = rmsnorm(h2, w["ln2"], eps)
-    gu = proj_smallm(w["gate_up"], x2)
+    gu = normed_proj(w["gate_up"], h2, w["ln2"])
     act = silu_gate(gu)
     return proj_smallm_add(w["down"], act, h2, out=out if out is not None else torch.empty_like(h))
 

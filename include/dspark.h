@@ -416,6 +416,30 @@ dspark_status dspark_proj_smallm_add(const uint16_t* W, int N, int K, const floa
                                      const float* residual, float* Y, void* stream);
 
 /*
+ * dspark_proj_smallm_norm: Y = rmsnorm(X; gamma, eps) W^T, the RMSNorm of
+ * dspark_rmsnorm fused into the projection it feeds (the qkv and gate/up
+ * projections of a draft block, [SI441] "Observation"), so the normed
+ * activations never go through memory and the norm costs no launch of its
+ * own. Computed as (X * gamma) W^T, each output then scaled by its row's
+ * factor 1 / sqrt(mean_k X[m, k]^2 + eps); the same products as the two
+ * calls up to fp32 rounding (not bit for bit).
+ *
+ *   W      bf16 [N, K]   16-byte aligned
+ *   X      fp32 [M, K]   16-byte aligned (the un-normed activations)
+ *   gamma  bf16 [K]      16-byte aligned
+ *   Y      fp32 [M, N]   4-byte aligned, overwritten
+ * Sizes: those of dspark_proj_smallm, and only where its short kernel
+ * applies: M <= 16, N >= 2, N * K * 2 < 2^31 and at most 16 tiles of 16 rows
+ * per compute unit (N up to about 256 x the device's compute units).
+ * dspark_proj_smallm_norm_fits(N, K, M) says whether a shape qualifies (1)
+ * or not (0, and the call returns DSPARK_ERR_SHAPE); eps >= 0.
+ * Errors: DSPARK_ERR_NULL, _SHAPE, _ALIGN, before anything is launched.
+ */
+int dspark_proj_smallm_norm_fits(int N, int K, int M);
+dspark_status dspark_proj_smallm_norm(const uint16_t* W, int N, int K, const float* X, int M,
+                                      const uint16_t* gamma, float eps, float* Y, void* stream);
+
+/*
  * dspark_attention_ragged -- attention of the B draft positions of each of
  * R requests, H heads of Dh dimensions.
  *
@@ -451,18 +475,19 @@ dspark_status dspark_attention_ragged(const float* q, const float* k, const floa
 /*
  * dspark_draft_block -- one whole draft block (layer) at small M, as the
  * composition of the entry points above on one stream:
- *   x    = rmsnorm(h_in, ln1)                       (dspark_rmsnorm)
- *   qkv  = x W_qkv^T                                (dspark_proj_smallm)
+ *   qkv  = rmsnorm(h_in, ln1) W_qkv^T               (dspark_proj_smallm_norm)
  *   a    = attention(qkv, context)                  (dspark_attention_ragged)
  *   h2   = h_in + a W_o^T                           (dspark_proj_smallm_add)
- *   x    = rmsnorm(h2, ln2)
- *   gu   = x W_gate_up^T
+ *   gu   = rmsnorm(h2, ln2) W_gate_up^T             (dspark_proj_smallm_norm)
  *   act  = silu(gu[:, :F]) * gu[:, F:]              (dspark_silu_gate)
- *   h_out = h2 + act W_down^T
+ *   h_out = h2 + act W_down^T                       (dspark_proj_smallm_add)
+ * where a projection's shape is outside dspark_proj_smallm_norm's (or its
+ * norm weights are not 16-byte aligned), its norm is dspark_rmsnorm followed
+ * by dspark_proj_smallm instead.
  * [SI441] "Observation" lists the block's projections (q/k/v/o, gate/up/down)
  * and its attention over a short context; the norms, the gated MLP and the
  * residuals are the plainest reading of a Qwen3-derived drafter. Results are
- * bit-identical to making the eight calls one by one (where the shape allows,
+ * bit-identical to making those calls one by one (where the shape allows,
  * the gate runs in the gate/up projection's epilogue instead of a launch of
  * its own, computing the same values).
  *

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
               "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
               "dspark_markov_sample_q8", "dspark_draft_round_q8", "dspark_rmsnorm", "dspark_silu_gate",
-              "dspark_proj_smallm_add", "dspark_attention_ragged",
+              "dspark_proj_smallm_add", "dspark_proj_smallm_norm", "dspark_proj_smallm_norm_fits",
+              "dspark_attention_ragged",
               "dspark_markov_workspace_bytes",
               "dspark_status_string"]:
         assert n in names
@@ -283,6 +284,17 @@ def test_block_errors(L):
     assert L.dspark_proj_smallm_add(A, 16, 64, A, 7, None, A2, None) == ERR_NULL
     assert L.dspark_proj_smallm_add(A, 16, 12, A, 7, A, A2, None) == ERR_SHAPE
     assert L.dspark_proj_smallm_add(A, 16, 64, A, 7, A + 2, A2, None) == ERR_ALIGN
+    # the fused norm: arguments checked like dspark_proj_smallm's, then gamma
+    # and eps; without a device no shape qualifies for the fused kernel
+    g = L.dspark_proj_smallm_norm
+    assert L.dspark_proj_smallm_norm_fits(4096, 4096, 7) == 0
+    assert L.dspark_proj_smallm_norm_fits(4096, 4096, 17) == 0
+    assert g(None, 16, 64, A, 7, A2, 1e-6, A2, None) == ERR_NULL
+    assert g(A, 16, 64, A, 7, None, 1e-6, A2, None) == ERR_NULL
+    assert g(A, 16, 12, A, 7, A2, 1e-6, A2, None) == ERR_SHAPE       # K % 8 != 0
+    assert g(A, 16, 64, A, 7, A2, -1.0, A2, None) == ERR_SHAPE
+    assert g(A, 16, 64, A, 17, A2, 1e-6, A2, None) == ERR_SHAPE      # more than 16 rows
+    assert g(A, 16, 64, MIS, 7, A2, 1e-6, A2, None) == ERR_ALIGN
     f = L.dspark_attention_ragged
     need = L.dspark_attention_workspace_bytes(1, 7, 32, 128, 512)
     assert need == 32 * 9 * 7 * 130 * 4                       # 9 chunks of 64 keys, m, l and o per chunk

@@ -876,6 +876,50 @@ def test_proj_smallm_add(dev, M, N, K):
     logits_close(y.cpu().numpy(), oracle.gemv(W, X) + res.astype(np.float64), f"proj add M={M} N={N} K={K}")
 
 
+NORM_CASES = [
+    # (M, N, K): packed rows with one tile per workgroup and several phases,
+    # several tiles; hi/lo rows with a partial last phase, several tiles;
+    # ragged N with one short phase; the smallest shape; 8 packed rows
+    (7, 4096, 4096), (7, 12288, 4096), (15, 4096, 4128), (16, 24576, 4096), (3, 1000, 264), (1, 2, 8),
+    (8, 777, 2080),
+]
+
+
+@pytest.mark.parametrize("M,N,K", NORM_CASES)
+def test_proj_smallm_norm_matches_oracle(dev, M, N, K):
+    """rmsnorm fused into the projection: Y = rmsnorm(X; gamma, eps) W^T
+    against the oracle's rmsnorm followed by its gemv."""
+    seed = 7350 + M + N + K
+    say(f"[proj norm] M={M} N={N} K={K} seed={seed}")
+    W, X = synth.gemv_inputs(M, N, K, seed)
+    X = X * np.float32(3.0) + np.float32(0.5)  # rows with a mean: the norm must not centre them
+    gamma = synth.bf16_bits_rne(1.0 + synth.normal_f32(seed, synth.S_BASE, (K,), 0.2))
+    eps = 1e-6
+    assert _ops().proj_smallm_norm_fits(N, K, M)
+    y = _ops().proj_smallm_norm(_bf(W, dev), _up(X, dev), _bf(gamma, dev), eps)
+    torch.cuda.synchronize()
+    logits_close(y.cpu().numpy(), oracle.gemv(W, oracle.rmsnorm(X, gamma, eps)), f"proj norm M={M} N={N} K={K}")
+
+
+def test_proj_smallm_norm_row_properties(dev):
+    """A row's output depends on that row alone (same bits for M = 7 and for
+    the row by itself), and at eps = 0 scaling X by 8 changes no bit (every
+    step of the factor is exact under a power-of-two scale)."""
+    M, N, K = 7, 12288, 4096
+    say(f"[proj norm rows] M={M} N={N} K={K}")
+    W, X = synth.gemv_inputs(M, N, K, 7399)
+    gamma = _bf(synth.bf16_bits_rne(1.0 + synth.normal_f32(7399, synth.S_BASE, (K,), 0.2)), dev)
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    ops = _ops()
+    y = ops.proj_smallm_norm(Wd, Xd, gamma, 0.0)
+    y3 = ops.proj_smallm_norm(Wd, Xd[3:4].contiguous(), gamma, 0.0)
+    y8 = ops.proj_smallm_norm(Wd, Xd * 8.0, gamma, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y[3:4], y3), "row 3 depends on the other rows"
+    assert torch.equal(y, y8), "scaling X by 8 changed the result"
+    assert not ops.proj_smallm_norm_fits(N, K, 17)
+
+
 ATTN_CASES = [
     # (R, B, H, Dh, Lmax, ctx_len, causal)
     (1, 7, 32, 128, 512, [512], False), (1, 7, 32, 128, 512, [300], True), (2, 3, 4, 64, 128, [0, 100], False),
