@@ -473,11 +473,11 @@ def main():
     bias, thr = float(inp["probe_bias"]), float(inp["probe_threshold"])
     torch.cuda.synchronize()
 
-    def lm():
+    def lm():  # the round's own lm_head: rows handed out by the workspace's counter word
         if q8:
             ops.lm_head_q8(*W, H, out=logits)
         else:
-            ops.lm_head(W, H, out=logits)
+            ops.lm_head_sched(W, H, ws, out=logits, counter_offset=ops.markov_lm_counter_offset())
 
     probe = dict(x=H, w=pw, bias=bias, threshold=thr, logit_out=plog, pass_out=ppass)
 
@@ -500,7 +500,8 @@ def main():
     # with the probe on its idle waves, in order on one stream, the results
     # landing in host memory. In the rounds that carry HIP events around the
     # lm_head, the same two launches are issued by their own entry points
-    # (dspark_lm_head, dspark_markov_sample_probe), so that the events can
+    # (dspark_lm_head_sched on the workspace's counter word, or
+    # dspark_lm_head_q8; dspark_markov_sample_probe), so that the events can
     # sit between them.
     main_stream = torch.cuda.current_stream()
 
@@ -664,7 +665,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "num_reqs": R, "B": B, "k": k, "d": d, "V": V, "r": r,
                    "weights": "q8_0" if q8 else "bf16"},
-        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head_q8)" if q8 else "lm_head GEMV (dspark_lm_head)",
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head_q8)" if q8 else "lm_head GEMV (dspark_lm_head_sched)",
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
                      "traffic": tr_lm, "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3,
                      "frac_of_stream_ceiling": lm_gbs / ceil["lm_head_shape"]["gbs"]},

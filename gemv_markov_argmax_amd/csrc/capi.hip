@@ -87,6 +87,15 @@ dspark_status dspark_proj_smallm_q8(const int8_t* Wq, const uint16_t* Wd, int N,
   return from_hip(dspark::launch_gemv_q8(Wq, Wd, N, K, X, M, Y, static_cast<hipStream_t>(stream)));
 }
 
+dspark_status dspark_lm_head_sched(const uint16_t* W_lm, int V, int d, const float* H, int rows, float* logits,
+                                  uint32_t* counter, void* stream) {
+  const dspark_status st = gemv_checks(W_lm, V, d, H, rows, logits);
+  if (st != DSPARK_OK) return st;
+  if (!counter) return DSPARK_ERR_NULL;
+  if (!aligned(counter, 4)) return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_gemv_sched(W_lm, V, d, H, rows, logits, counter, static_cast<hipStream_t>(stream)));
+}
+
 dspark_status dspark_lm_head_q8(const int8_t* Wq, const uint16_t* Wd, int V, int d, const float* H, int rows,
                                 float* logits, void* stream) {
   const dspark_status st = gemv_q8_checks(Wq, Wd, V, d, H, rows, logits);
@@ -216,7 +225,7 @@ dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float
   if (st == DSPARK_OK && probe_w) st = probe_checks(H, rows, d, probe_w, logit_out, pass_out);
   if (st != DSPARK_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = dspark::launch_gemv(W_lm, V, d, H, rows, base_out, s);
+  const hipError_t e = dspark::launch_gemv_sched(W_lm, V, d, H, rows, base_out, dspark::markov_lm_counter(workspace), s);
   if (e != hipSuccess) return DSPARK_ERR_HIP;
   const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
   return from_hip(dspark::launch_markov(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,

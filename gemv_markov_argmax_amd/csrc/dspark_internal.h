@@ -220,6 +220,15 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
 // Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
                        hipStream_t stream, const float* res = nullptr);
+// The same product with the weight rows handed out to workgroups by a
+// counter (see dspark_lm_head_sched) where the shape allows (M <= 8,
+// K <= 4096), else launch_gemv. The counter reads 0 before and after.
+bool gemv_sched_fits(int N, int K, int M);
+hipError_t launch_gemv_sched(const uint16_t* W, int N, int K, const float* X, int M, float* Y, uint32_t* counter,
+                             hipStream_t stream);
+// The word of the Markov workspace that dspark_draft_round gives its
+// lm_head as counter (a control word the loop itself never touches).
+uint32_t* markov_lm_counter(void* workspace);
 
 // The confidence probe's arguments (see dspark_conf_probe).
 struct ProbeArgs {

@@ -621,6 +621,234 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
   }
 }
 
+// Dynamically scheduled streaming variant, M <= 8 and K <= 4096 (the
+// lm_head of a single request's draft round).
+//
+// With every workgroup owning an equal contiguous share, the launch ends
+// when the slowest XCD does. Measured on MI355X with a plain streaming read
+// of the Qwen3-8B lm_head's 1.25 GB: the workgroups of the odd XCDs finish
+// 20-35 us after those of the even ones (shares assigned cyclically instead
+// of contiguously change nothing), 203 us in all; handing out 256 KB pieces
+// from a counter instead brings every XCD to within ~7 us of the others and
+// the read to 177 us.
+//
+// So the weight rows are cut into units of two tiles (32 rows, 256 KB at
+// K = 4096). Each workgroup first runs a contiguous run of units of its own
+// (90% of an equal share, fixed on the host), then takes units from a
+// counter in caller memory until they run out: the workgroups of the faster
+// XCDs take more of them. Handing out every unit was slower per CU (the
+// contiguous runs stream faster) and handing out none leaves the XCDs
+// unbalanced; the mix beats both. A unit is processed like two tiles of the streaming
+// kernel, phase by phase; with U = 2 each (unit, phase) is one pair of tiles
+// (b0, b1), and each tile of the next pair (the next phase, or the next
+// unit's first) is loaded as soon as its buffer is free, two tiles ahead as
+// in the streaming kernel, so the stream does not stop at phase or unit
+// boundaries. The A fragments of every phase
+// stay in registers (X is read once). The next units' indices are known
+// two units ahead: thread 0 issues the atomic for the unit after next when a
+// unit starts and publishes its result in LDS when the unit ends, so no wave
+// waits for it. Outputs stay in LDS (phases add there) and are written after
+// the loop, with the unit list, or when that LDS fills (64 units, far more
+// than a workgroup takes at the sizes in use).
+//
+// The counter must read 0 when a launch starts, and the launch leaves it 0
+// (the workgroup whose take is the last of the launch stores 0; see the
+// loop). Launches that share a counter must be ordered (one stream).
+constexpr int kSchedU = 2;     // tiles per unit
+constexpr int kSchedCap = 64;  // units whose outputs a workgroup holds in LDS
+
+template <int NPH>
+__global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, uint32_t* __restrict__ counter) {
+  constexpr int NW = 16, KBW = 4, ROWS = 8, U = kSchedU;
+  constexpr int SEG = 64 * KBW;     // bytes of a row segment
+  constexpr int RS = SEG + 16;      // padded LDS row stride
+  constexpr int LPR = SEG / 16;     // lanes per row in a load instruction
+  constexpr int RPI = kWave / LPR;  // rows per load instruction
+  constexpr int NLD = 16 / RPI;     // load instructions per tile
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* tr = smem;                                                            // [NW][16][RS]
+  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(NW) * 16 * RS);    // [2][NW][ROWS][16]
+  float* ylds = red + 2 * NW * ROWS * 16;                                              // [cap][U][ROWS][16]
+  uint32_t* ulist = reinterpret_cast<uint32_t*>(ylds + kSchedCap * U * ROWS * 16);    // [cap] unit of each slot
+  uint32_t* sgrab = ulist + kSchedCap;                                                 // [2] published takes
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
+  const int N = p.N, K = p.K, M = p.M;
+  const uint32_t nunits = static_cast<uint32_t>(((N + 15) / 16 + U - 1) / U);
+  const uint32_t last_take = nunits + gridDim.x - 1;
+  const int lrow = lane / LPR, lchunk = lane % LPR;
+  unsigned char* wtr = tr + w * 16 * RS;
+  unsigned char* wr_base = wtr + lrow * RS + 16 * lchunk;  // + RPI*q*RS
+  const unsigned char* rd_base = wtr + i * RS + 16 * g;   // + 64*kb
+  const uint32_t rowb = static_cast<uint32_t>(K) * 2;
+  const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
+
+  // A fragments of every phase (packed rows: hi in rows 0..7, lo in 8..15).
+  u32x4 afr[NPH][KBW];
+  {
+    const int m = i & 7;
+    float4 xr[NPH][KBW];
+#pragma unroll
+    for (int q = 0; q < NPH; ++q)
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        const int k = 32 * KBW * (q * NW + w) + 32 * kb + 8 * g;
+        const uint32_t off = (m < M) & (k < K) ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
+        xr[q][kb] = buf_load_f32x4(xres, off + 16 * (i >> 3));
+      }
+#pragma unroll
+    for (int q = 0; q < NPH; ++q)
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        float4 x0, x1;
+        pair_halves(xr[q][kb], i, x0, x1);
+        const uint2 s0 = split_bf16x2(x0.x, x0.y), s1 = split_bf16x2(x0.z, x0.w);
+        const uint2 s2 = split_bf16x2(x1.x, x1.y), s3 = split_bf16x2(x1.z, x1.w);
+        afr[q][kb] = (i >> 3) ? u32x4{s0.y, s1.y, s2.y, s3.y} : u32x4{s0.x, s1.x, s2.x, s3.x};
+      }
+  }
+
+  // Tile t of unit u in phase q (unit u covers rows 32u .. 32u + 31; rows
+  // past N, lanes past K and units past the last read zeros).
+  const uint16_t* const Wmat = p.W;
+  auto load_tile = [&](u32x4 (&b)[NLD], uint32_t u, int q, int t) {
+    u = __builtin_amdgcn_readfirstlane(u);
+    const bool live = u < nunits;
+    const int row0 = live ? static_cast<int>(u) * U * 16 + 16 * t : 0;
+    const int nrows = live ? max(0, min(16, N - row0)) : 0;
+    // (the descriptor from scalar values only, or every load becomes a
+    // loop over the lanes' distinct descriptors; readfirstlane returns an
+    // int, so each half goes back through uint32_t before it is widened, or
+    // a low half >= 2^31 would sign-extend into the high half)
+    const uint64_t addr = reinterpret_cast<uint64_t>(Wmat + static_cast<size_t>(row0) * K);
+    const uint32_t alo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr)));
+    const uint32_t ahi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32)));
+    const uint32_t bytes = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(nrows) * rowb));
+    const BufRes res =
+        buf_res(reinterpret_cast<const void*>((static_cast<uint64_t>(ahi) << 32) | static_cast<uint64_t>(alo)), bytes);
+    const int kseg = 32 * KBW * (q * NW + w);
+    const uint32_t off = kseg + 8 * lchunk < K
+                             ? static_cast<uint32_t>(lrow) * rowb + static_cast<uint32_t>(kseg + 8 * lchunk) * 2
+                             : kBufOutOfRange;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) b[j] = buf_load16_nt(res, off + static_cast<uint32_t>(j * RPI) * rowb);
+  };
+  auto compute_publish = [&](const u32x4 (&b)[NLD], const u32x4 (&a)[KBW], int buf) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) *reinterpret_cast<u32x4*>(wr_base + RPI * j * RS) = b[j];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) acc = mfma_16x16x32(a[kb], *reinterpret_cast<const u32x4*>(rd_base + 64 * kb), acc);
+    float* dst = red + (buf * NW + w) * ROWS * 16;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float lo = __shfl_down(acc[v], 32);
+      if (g < 2) dst[(4 * g + v) * 16 + i] = acc[v] + lo;
+    }
+  };
+  // Wave-order sum of tile t of the unit in slot s into its LDS outputs.
+  auto reduce = [&](int buf, int s, int t, int q) {
+    if (tid < M * 16) {
+      float y = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) y += red[((buf * NW + ww) * ROWS + (tid >> 4)) * 16 + (tid & 15)];
+      float* yl = ylds + ((s * U + t) * ROWS + (tid >> 4)) * 16 + (tid & 15);
+      *yl = q == 0 ? y : *yl + y;
+    }
+  };
+  // The outputs of slots [0, ns), row by row.
+  auto write_out = [&](int ns) {
+    __syncthreads();
+    for (int e = tid; e < ns * M * U * 16; e += NW * kWave) {
+      const int s = e / (M * U * 16), rem = e - s * (M * U * 16), m = rem / (U * 16), j = rem - m * (U * 16);
+      const int n = static_cast<int>(ulist[s]) * U * 16 + j;
+      if (n < N) {
+        const size_t idx = static_cast<size_t>(m) * p.ldy + n;
+        p.Y[idx] = with_res(p, idx, ylds[((s * U + (j >> 4)) * ROWS + m) * 16 + (j & 15)]);
+      }
+    }
+    __syncthreads();
+  };
+
+  // This workgroup's units: first S2 static ones (no take needed, so the
+  // stream starts at once), then D0 + v for each take v. With S = p.chunk
+  // >= 2 the static ones are the contiguous run b*S .. b*S + S - 1 (S*G <= T,
+  // set on the host), else b and b + G; D0 = S2 * G. One take is in flight
+  // from the start of position S2 - 2 on: issued when a unit starts and
+  // read when it ends, so the unit after next is known before the next
+  // unit's loads go out. Every workgroup takes until it gets a unit past the
+  // last, so the G final takes return max(0, T - D0) .. + G - 1 and the one
+  // that returns the largest is the last take of the launch: it stores 0.
+  // Takes are atomicInc (an add of 1 below 2^32 - 1): an atomicAdd would be
+  // turned into a wave-wide reduction whose result is waited for at once,
+  // and the wait would drain the tiles in flight.
+  constexpr uint32_t kNoWrap = 0xffffffffu;
+  const uint32_t G = gridDim.x, b = blockIdx.x;
+  const uint32_t S = p.chunk >= 2 ? static_cast<uint32_t>(p.chunk) : 0u;
+  const uint32_t S2 = S >= 2 ? S : 2u;
+  const uint32_t D0 = S2 * G;
+  auto static_unit = [&](uint32_t k) { return S >= 2 ? b * S + k : b + k * G; };  // k < S2
+  const uint32_t first_final = nunits > D0 ? nunits - D0 : 0u;
+  const uint32_t final_take = first_final + G - 1;
+  uint32_t ucur = static_unit(0), unext = static_unit(1);
+  if (ucur >= nunits) {  // uniform (only where T < G): no unit here; this workgroup's one take is final
+    if (tid == 0) {
+      const uint32_t v = atomicInc(counter, kNoWrap);
+      if (v == final_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  // Two tiles in flight, as in the streaming kernel: the back edge always
+  // carries b0 older than b1, so the head waits for b0 alone.
+  u32x4 b0[NLD], b1[NLD];
+  load_tile(b0, ucur, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(b1, ucur, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  int ns = 0;
+  uint32_t pending = 0;
+  for (uint32_t pos = 0;; ++pos) {
+    // The unit after next comes from a take from position S2 - 2 on (there
+    // always, later while the sequence goes on).
+    const bool take = pos + 2 == S2 || (pos + 2 > S2 && unext < nunits);
+    if (tid == 0 && take) pending = atomicInc(counter, kNoWrap);
+    if (tid == 0) ulist[ns] = ucur;
+#pragma unroll
+    for (int q = 0; q < NPH; ++q) {
+      const bool lastq = q + 1 == NPH;
+      const uint32_t nu = lastq ? unext : ucur;  // the next pair: next phase, or the next unit's first
+      const int nq = lastq ? 0 : q + 1;
+      compute_publish(b0, afr[q], 0);
+      load_tile(b0, nu, nq, 0);
+      __syncthreads();
+      reduce(0, ns, 0, q);
+      compute_publish(b1, afr[q], 1);
+      load_tile(b1, nu, nq, 1);
+      if (lastq && tid == 0 && take) {
+        if (pending == final_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sgrab[0] = pending;
+      }
+      __syncthreads();
+      reduce(1, ns, 1, q);
+    }
+    ++ns;
+    // (sgrab is rewritten only after the next unit's first barrier, which
+    // every wave passes after this read)
+    const uint32_t after = take ? D0 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(sgrab[0]))
+                                : (pos + 2 < S2 ? static_unit(pos + 2) : nunits);
+    ucur = unext;
+    unext = after;
+    if (ucur >= nunits) break;  // uniform
+    if (ns == kSchedCap) {
+      write_out(ns);
+      ns = 0;
+    }
+  }
+  write_out(ns);
+}
+
 // Medium-M variant, 16 < M <= 80 (the batched lm_head of several requests):
 // a small GEMM. With the hi/lo split the A side has 2M rows, too many to
 // keep per wave, so the workgroup streams K in chunks through LDS: a chunk
@@ -1070,6 +1298,53 @@ hipError_t launch_gemv_gated_norm(const uint16_t* W, int F, int K, const float* 
   prm.gamma = gamma;
   prm.eps = eps;
   return dispatch_short<true, true>(prm, pl, stream);
+}
+
+bool gemv_sched_fits(int N, int K, int M) {
+  const int KB = (K + 31) / 32;
+  return N >= 1 && M >= 1 && M <= 8 && K >= 8 && KB <= 2 * 16 * 4;
+}
+
+size_t gemv_sched_lds_bytes() {
+  return static_cast<size_t>(16) * 16 * (64 * 4 + 16) + static_cast<size_t>(2) * 16 * 8 * 16 * 4 +
+         static_cast<size_t>(kSchedCap) * kSchedU * 8 * 16 * 4 + static_cast<size_t>(kSchedCap) * 4 + 2 * 4;
+}
+
+template <int NPH>
+hipError_t launch_sched(const GemvParams& prm, uint32_t* counter, int grid, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_sched_kernel<NPH>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (attr != hipSuccess) return attr;
+  GemvParams a = prm;
+  uint32_t* c = counter;
+  void* args[] = {&a, &c};
+  return hipLaunchKernel(fn, dim3(grid), dim3(16 * kWave), args, gemv_sched_lds_bytes(), st);
+}
+
+hipError_t launch_gemv_sched(const uint16_t* W, int N, int K, const float* X, int M, float* Y, uint32_t* counter,
+                             hipStream_t stream) {
+  if (!gemv_sched_fits(N, K, M) || !counter) return launch_gemv(W, N, K, X, M, Y, stream);
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorNoDevice;
+  GemvParams prm{};
+  prm.W = W;
+  prm.X = X;
+  prm.Y = Y;
+  prm.N = N;
+  prm.K = K;
+  prm.M = M;
+  prm.ldy = N;
+  const int KB = (K + 31) / 32;
+  // Static contiguous units per workgroup: 90% of an equal share (the rest
+  // is handed out). Measured on MI355X at [7 x 4096] x [151936 x 4096]:
+  // 0% (b and b + G, then all from the counter) 188.5 us, 50% 180 us, 80%
+  // 179 us, 90% 178.5 us, 100% (only the remainder handed out) 185 us, equal
+  // shares 187 us; at K = 2048: 102, 96, 92.5, 91.4, 93 and 93.6 us.
+  const int nunits = ((N + 15) / 16 + kSchedU - 1) / kSchedU;
+  const int S = 90 * (nunits / cus) / 100;
+  prm.chunk = S >= 2 ? S : 0;
+  return KB <= 16 * 4 ? launch_sched<1>(prm, counter, cus, stream) : launch_sched<2>(prm, counter, cus, stream);
 }
 
 }  // namespace dspark

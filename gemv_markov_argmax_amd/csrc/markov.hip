@@ -97,6 +97,7 @@ constexpr int kCtlSeq = 1;         // call sequence number; its parity selects t
 constexpr int kCtlRepairedBy = 2;  // launch number of the call that repaired the workspace
 constexpr int kCtlUsed = 4;        // [4 + b]: slots per copy the last call that used buffer b wrote
 constexpr int kCtlReps = 6;        // [6 + b]: copies that call wrote
+constexpr int kCtlLmCounter = 16;  // not used by the loop: the round's lm_head takes its units from here
 constexpr uint32_t kStateOk = 0;
 constexpr uint32_t kStateTimedOut = 1;  // any value but kStateOk and kStateRepaired is treated so
 constexpr uint32_t kStateRepaired = 2;
@@ -948,6 +949,8 @@ MarkovParams common_params(const float* base, int R, int B, int V, int r, const 
 uint32_t markov_set_spin_limit(uint32_t polls) {
   return g_spin_limit.exchange(polls == 0u ? kDefaultSpinLimit : polls, std::memory_order_relaxed);
 }
+
+uint32_t* markov_lm_counter(void* workspace) { return static_cast<uint32_t*>(workspace) + kCtlLmCounter; }
 
 size_t markov_workspace_bytes(int num_reqs, int k, int V) {
   if (num_reqs < 1 || num_reqs > kMaxReqs || k < 1 || k > kMaxSteps || V < 1) return 0;

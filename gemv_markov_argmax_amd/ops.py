@@ -24,6 +24,7 @@ SIGNATURES = {
     "dspark_status_string": (ctypes.c_char_p, [_i]),
     "dspark_proj_smallm": (_i, [_p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head": (_i, [_p, _i, _i, _p, _i, _p, _p]),
+    "dspark_lm_head_sched": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "dspark_proj_smallm_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_markov_sample_q8": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
@@ -144,6 +145,43 @@ def _gemv(entry, W, X, out):
         raise ValueError("out must be [M, N]")
     _check(entry(W.data_ptr(), N, K, X.data_ptr(), M, out.data_ptr(), _stream(W)))
     return out
+
+
+def lm_head_counter(device) -> torch.Tensor:
+    """A zeroed counter for lm_head_sched (one 32-bit word of device memory)."""
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def lm_head_sched(W_lm: torch.Tensor, H: torch.Tensor, counter: torch.Tensor, out: torch.Tensor | None = None,
+                  counter_offset: int = 0) -> torch.Tensor:
+    """Base logits with the weight rows handed out by a counter
+    (dspark_lm_head_sched). ``counter``: device memory whose word at byte
+    ``counter_offset`` reads 0 (lm_head_counter(), or a Markov workspace at
+    offset markov_lm_counter_offset()); every call leaves it 0."""
+    _dev(W_lm, torch.bfloat16, "W_lm", 2)
+    _dev(H, torch.float32, "H", 2)
+    if not counter.is_cuda:
+        raise ValueError("counter must be a GPU tensor")
+    if counter_offset < 0 or counter_offset + 4 > counter.numel() * counter.element_size():
+        raise ValueError("counter word out of range")
+    V, d = W_lm.shape
+    rows = H.shape[0]
+    if H.shape[1] != d:
+        raise ValueError(f"H has {H.shape[1]} columns, W_lm has {d}")
+    if out is None:
+        out = torch.empty((rows, V), dtype=torch.float32, device=W_lm.device)
+    _dev(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (rows, V):
+        raise ValueError("out must be [rows, V]")
+    _check(lib().dspark_lm_head_sched(W_lm.data_ptr(), V, d, H.data_ptr(), rows, out.data_ptr(),
+                                      counter.data_ptr() + counter_offset, _stream(W_lm)))
+    return out
+
+
+def markov_lm_counter_offset() -> int:
+    """Byte offset of the word of a Markov workspace that dspark_draft_round
+    gives its lm_head as counter."""
+    return 64
 
 
 def proj_smallm(W: torch.Tensor, X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

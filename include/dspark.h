@@ -114,6 +114,29 @@ dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H,
                              float* logits, void* stream);
 
 /*
+ * dspark_lm_head_sched -- dspark_lm_head with the weight rows handed out to
+ * the workgroups by a counter instead of in equal shares, so that compute
+ * units that stream faster take more of them (on MI355X the XCDs stream at
+ * different rates: with equal shares the launch waits for the slowest).
+ * Same product, arguments, sizes, errors and accuracy as dspark_lm_head;
+ * the summation order of every logit is the same as with equal shares of
+ * the same launch shape (it depends on the shape only), so results do not
+ * depend on which workgroup computed which rows.
+ *
+ *   counter  device memory, one uint32, 4-byte aligned, caller-owned. It
+ *            must read 0 before the first call (zero-fill it once); every
+ *            call leaves it 0 again. Calls that share a counter must be
+ *            ordered on one stream.
+ * Applies where rows <= 8 and d <= 4096; other shapes run dspark_lm_head's
+ * kernels and leave the counter alone. dspark_draft_round runs its lm_head
+ * this way, with a word of its workspace as the counter.
+ * Errors: those of dspark_lm_head; DSPARK_ERR_NULL for a null counter,
+ * DSPARK_ERR_ALIGN for a misaligned one.
+ */
+dspark_status dspark_lm_head_sched(const uint16_t* W_lm, int V, int d, const float* H, int rows,
+                                   float* logits, uint32_t* counter, void* stream);
+
+/*
  * dspark_proj_smallm_q8, dspark_lm_head_q8 -- the same products over Q8_0
  * weights.
  *

@@ -29,7 +29,7 @@ def declared():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_markov_sample", "dspark_conf_probe",
+    for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_lm_head_sched", "dspark_markov_sample", "dspark_conf_probe",
               "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
               "dspark_markov_sample_q8", "dspark_draft_round_q8", "dspark_rmsnorm", "dspark_silu_gate",
               "dspark_proj_smallm_add", "dspark_proj_smallm_norm", "dspark_proj_smallm_norm_fits",
@@ -54,6 +54,15 @@ def test_status_strings(L):
 A = 0x10000      # 16-byte-aligned fake device addresses: never dereferenced,
 A2 = 0x20000     # every call below fails validation before any HIP call
 MIS = 0x10002
+
+
+def test_lm_head_sched_errors(L):
+    f = L.dspark_lm_head_sched
+    assert f(None, 16, 64, A, 7, A2, A, None) == ERR_NULL
+    assert f(A, 16, 64, A, 7, A2, None, None) == ERR_NULL      # no counter
+    assert f(A, 16, 12, A, 7, A2, A, None) == ERR_SHAPE        # d % 8 != 0
+    assert f(A, 16, 64, A, 7, A2, A + 2, None) == ERR_ALIGN    # misaligned counter
+    assert f(A, 16, 64, MIS, 7, A2, A, None) == ERR_ALIGN
 
 
 def test_gemv_errors(L):

@@ -93,6 +93,60 @@ def test_draft_layer_fused_projections(dev):
         assert col == y.shape[1]
 
 
+SCHED_CASES = [
+    # (rows, V, d): one K phase, two (the second partial), a ragged last unit,
+    # fewer units than workgroups, one row, many units; units of 32 rows:
+    # between one and two per workgroup of 256, and just over two per
+    # workgroup (the first ones taken from the counter)
+    (7, 33, 256), (8, 4099, 4096), (3, 1000, 2056), (7, 64, 4096), (1, 1, 8), (5, 70001, 1024),
+    (7, 12800, 512), (7, 19200, 256),
+]
+
+
+@pytest.mark.parametrize("rows,V,d", SCHED_CASES)
+def test_lm_head_sched_matches_oracle(dev, rows, V, d):
+    """Rows handed out by a counter: every row computed once, the counter
+    left at 0 by every call, reruns bit-identical."""
+    seed = 7700 + rows + V + d
+    say(f"[lm_head sched] rows={rows} V={V} d={d} seed={seed}")
+    W, X = synth.gemv_inputs(rows, V, d, seed)
+    ops = _ops()
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    cnt = ops.lm_head_counter(dev)
+    y = ops.lm_head_sched(Wd, Xd, cnt)
+    y2 = ops.lm_head_sched(Wd, Xd, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0, "the counter was not left at 0"
+    assert torch.equal(y, y2), "rerun differs"
+    logits_close(y.cpu().numpy(), oracle.gemv(W, X), f"lm_head sched rows={rows} V={V} d={d}")
+
+
+def test_lm_head_sched_full_size(dev):
+    """At the Qwen3-8B head's shape the scheduled lm_head gives the bits of
+    dspark_lm_head (the same summation order for every logit), whichever
+    workgroup computed a row; shapes it does not take (9 rows) run
+    dspark_lm_head's kernels and leave the counter alone."""
+    cfg = synth.CONFIGS["qwen3_8b_head"]
+    V, d, rows = cfg["V"], cfg["d"], cfg["B"]
+    seed = synth.config_seed("qwen3_8b_head")
+    say(f"[lm_head sched full] V={V} d={d} rows={rows}")
+    ops = _ops()
+    W = _bf(synth.normal_bf16(seed, synth.S_W_LM, (V, d)), dev)
+    H = _up(synth.normal_f32(seed, synth.S_H, (9, d)), dev)
+    cnt = ops.lm_head_counter(dev)
+    ref = ops.lm_head(W, H[:rows].contiguous())
+    for rep in range(3):
+        y = ops.lm_head_sched(W, H[:rows].contiguous(), cnt)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"call {rep} differs from dspark_lm_head"
+        assert int(cnt.item()) == 0
+    cnt.fill_(5)
+    y9 = ops.lm_head_sched(W, H, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 5, "a shape outside the scheduled kernel touched the counter"
+    assert torch.equal(y9, ops.lm_head(W, H))
+
+
 def test_lm_head_full_size_sampled(dev):
     """Qwen3-8B-shaped head at full size in the benchmark's launch
     configuration; oracle on sampled vocabulary rows incl. the ragged tail."""
@@ -495,9 +549,11 @@ def _round_tensors(name, dev):
 
 
 def _run_round(inp, t, logits=None, ids=None, ws=None, lg=None, ps=None):
+    """The round as separate calls, with the lm_head scheduled like the
+    round's own (dspark_lm_head_sched) on a counter of its own."""
     ops = _ops()
     R, B, V = inp["num_reqs"], inp["B"], inp["V"]
-    logits = ops.lm_head(t["W"], t["H"], out=logits)
+    logits = ops.lm_head_sched(t["W"], t["H"], ops.lm_head_counter(t["H"].device), out=logits)
     ids = ops.markov_sample(logits.view(R, B, V), t["w1"], t["w2"], t["prev0"], inp["k"], out=ids, workspace=ws)
     lg, ps = ops.conf_probe(t["H"], t["pw"], float(inp["probe_bias"]), float(inp["probe_threshold"]),
                             logit_out=lg, pass_out=ps)
