@@ -617,16 +617,26 @@ def main():
 
     # The streaming-read ceiling of this device in this run: 4 GiB read at
     # the lm_head's launch shape (one workgroup of 1024 threads per CU, a
-    # contiguous share each) and at a finer shape (8192 workgroups of 256).
+    # contiguous share each), at a finer shape (8192 workgroups of 256), and
+    # with the scheduled lm_head's schedule (a contiguous run per workgroup,
+    # the rest handed out by a counter).
     big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     big.fill_(1)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    cnt = ops.lm_head_counter(dev)
     ceil = {}
-    for label, g, t in (("lm_head_shape", cus, 1024), ("fine_grid", 8192, 256)):
-        ms = per_call_ms(lambda: ops.stream_read(big, g, t, sink=sink), n=10)
+    for label, g, t, fn in (("lm_head_shape", cus, 1024, lambda: ops.stream_read(big, cus, 1024, sink=sink)),
+                            ("fine_grid", 8192, 256, lambda: ops.stream_read(big, 8192, 256, sink=sink)),
+                            ("lm_head_schedule", cus, 1024,
+                             lambda: ops.stream_read_sched(big, cus, 1024, cnt, sink=sink))):
+        ms = per_call_ms(fn, n=10)
         ceil[label] = dict(groups=g, threads=t, us=ms * 1e3, gbs=big.numel() / (ms * 1e-3) / 1e9)
     del big
     torch.cuda.synchronize()
+    # the ceiling of the lm_head's own schedule: scheduled rows where the
+    # round's lm_head takes them (bf16, rows <= 8, d <= 4096)
+    sched_lm = (not q8) and rows <= 8 and inp["d"] <= 4096
+    ceil_ref = "lm_head_schedule" if sched_lm else "lm_head_shape"
 
     rounds_per_s = args.steps / elapsed
     round_us = 1e6 * elapsed / args.steps
@@ -668,7 +678,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head_q8)" if q8 else "lm_head GEMV (dspark_lm_head_sched)",
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
                      "traffic": tr_lm, "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3,
-                     "frac_of_stream_ceiling": lm_gbs / ceil["lm_head_shape"]["gbs"]},
+                     "frac_of_stream_ceiling": lm_gbs / ceil[ceil_ref]["gbs"], "stream_ceiling_ref": ceil_ref},
         # Whole round. HBM bytes are the counters' (markov_w2 is read from
         # memory once per call and served on chip for every step); the
         # algorithmic figure counts markov_w2 once per step, as the method

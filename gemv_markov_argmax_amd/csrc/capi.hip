@@ -109,6 +109,17 @@ size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V) {
 
 uint32_t dspark_markov_set_spin_limit(uint32_t polls) { return dspark::markov_set_spin_limit(polls); }
 
+dspark_status dspark_stream_read_sched(const void* buf, size_t bytes, int groups, int threads, uint32_t* counter,
+                                       uint32_t* sink, void* stream) {
+  if ((bytes > 0 && !buf) || !sink || !counter) return DSPARK_ERR_NULL;
+  if (groups < 1 || groups > 65536 || (threads != 256 && threads != 512 && threads != 1024) || (bytes % 16) != 0 ||
+      bytes / (16u * 16384u) >= (1u << 30))
+    return DSPARK_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4) || !aligned(counter, 4)) return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_stream_read_sched(buf, bytes, groups, threads, counter, sink,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 dspark_status dspark_stream_read(const void* buf, size_t bytes, int groups, int threads, uint32_t* sink,
                                  void* stream) {
   if ((bytes > 0 && !buf) || !sink) return DSPARK_ERR_NULL;

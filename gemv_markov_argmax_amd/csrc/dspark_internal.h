@@ -267,6 +267,8 @@ hipError_t launch_probe(const float* x, int M, int D, const uint16_t* w, float b
 // (256, 512 or 1024), one word per workgroup into sink (a measurement aid).
 hipError_t launch_stream_read(const void* buf, size_t bytes, int groups, int threads, uint32_t* sink,
                               hipStream_t stream);
+hipError_t launch_stream_read_sched(const void* buf, size_t bytes, int groups, int threads, uint32_t* counter,
+                                    uint32_t* sink, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -44,6 +44,7 @@ SIGNATURES = {
     "dspark_markov_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_markov_set_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
     "dspark_stream_read": (_i, [_p, _sz, _i, _i, _p, _p]),
+    "dspark_stream_read_sched": (_i, [_p, _sz, _i, _i, _p, _p, _p]),
     "dspark_markov_sample_noalloc": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p]),
     "dspark_markov_sample": (_i, [_p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "dspark_conf_probe": (_i, [_p, _i, _i, _p, _f, _f, _p, _p, _p]),
@@ -438,6 +439,20 @@ def stream_read(buf: torch.Tensor, groups: int, threads: int, sink: torch.Tensor
         sink = torch.empty(groups, dtype=torch.int32, device=buf.device)
     _check(lib().dspark_stream_read(buf.data_ptr() if n else None, n, groups, threads, sink.data_ptr(),
                                     _stream(buf)))
+    return sink
+
+
+def stream_read_sched(buf: torch.Tensor, groups: int, threads: int, counter: torch.Tensor,
+                      sink: torch.Tensor | None = None, nbytes: int | None = None) -> torch.Tensor:
+    """The same read with the scheduled lm_head's schedule
+    (dspark_stream_read_sched); ``counter`` as for lm_head_sched."""
+    if not buf.is_cuda or not counter.is_cuda:
+        raise ValueError("buf and counter must be device tensors")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if sink is None:
+        sink = torch.empty(groups, dtype=torch.int32, device=buf.device)
+    _check(lib().dspark_stream_read_sched(buf.data_ptr() if n else None, n, groups, threads, counter.data_ptr(),
+                                          sink.data_ptr(), _stream(buf)))
     return sink
 
 

@@ -556,6 +556,19 @@ dspark_status dspark_draft_block(const uint16_t* w_qkv, const uint16_t* w_o, con
 dspark_status dspark_stream_read(const void* buf, size_t bytes, int groups, int threads, uint32_t* sink,
                                  void* stream);
 
+/*
+ * dspark_stream_read_sched -- the same read with dspark_lm_head_sched's
+ * schedule: 256 KB units, a contiguous run of 90% of an equal share per
+ * workgroup, the rest taken from `counter` (one uint32 of device memory,
+ * 4-byte aligned, reading 0 before the call and left 0 by it; calls that
+ * share it must be ordered). It measures the ceiling that lm_head streams
+ * against. sink[b] is workgroup b's fold of what it read; the fold over all
+ * workgroups equals dspark_stream_read's. Sizes: as dspark_stream_read, and
+ * bytes < 2^30 units of 256 KB. Errors: DSPARK_ERR_NULL, _SHAPE, _ALIGN.
+ */
+dspark_status dspark_stream_read_sched(const void* buf, size_t bytes, int groups, int threads, uint32_t* counter,
+                                       uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -167,6 +167,16 @@ def test_stream_read_errors(L):
     assert f(A, 4096, 8, 256, A2 + 2, None) == ERR_ALIGN
 
 
+def test_stream_read_sched_errors(L):
+    f = L.dspark_stream_read_sched
+    assert f(None, 4096, 8, 256, A, A2, None) == ERR_NULL
+    assert f(A, 4096, 8, 256, None, A2, None) == ERR_NULL     # no counter
+    assert f(A, 4096, 8, 256, A, None, None) == ERR_NULL
+    assert f(A, 4096, 8, 128, A, A2, None) == ERR_SHAPE
+    assert f(A, 4100, 8, 256, A, A2, None) == ERR_SHAPE
+    assert f(A, 4096, 8, 256, A + 2, A2, None) == ERR_ALIGN
+
+
 def test_markov_workspace_bytes(L):
     f = L.dspark_markov_workspace_bytes
     assert f(0, 7, 100) == 0 and f(17, 7, 100) == 0 and f(1, 0, 100) == 0 and f(1, 7, 0) == 0

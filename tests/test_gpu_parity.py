@@ -147,6 +147,28 @@ def test_lm_head_sched_full_size(dev):
     assert torch.equal(y9, ops.lm_head(W, H))
 
 
+@pytest.mark.parametrize("nbytes,groups,threads", [(1 << 30, 256, 1024), (40 * 256 * 1024 + 4096, 8, 256), (0, 4, 512),
+                                                    (3 * 256 * 1024, 16, 1024)])
+def test_stream_read_sched_reads_every_byte_once(dev, nbytes, groups, threads):
+    """The scheduled read (static runs, then units from the counter) folds
+    to the same word as the plain read, so every 16-byte piece was read once
+    by one workgroup; the counter is left at 0 (also with fewer units than
+    workgroups, or none)."""
+    say(f"[stream read sched] bytes={nbytes} groups={groups} threads={threads}")
+    ops = _ops()
+    g = torch.Generator(device="cpu").manual_seed(nbytes % 1000 + groups)
+    buf = torch.randint(0, 2 ** 31 - 1, (max(nbytes // 4, 1),), dtype=torch.int32, generator=g).to(dev)
+    cnt = ops.lm_head_counter(dev)
+    a = ops.stream_read(buf, groups, threads, nbytes=nbytes)
+    for _ in range(2):
+        b = ops.stream_read_sched(buf, groups, threads, cnt, nbytes=nbytes)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == 0
+        fa = int(np.bitwise_xor.reduce(a.cpu().numpy().astype(np.uint32)))
+        fb = int(np.bitwise_xor.reduce(b.cpu().numpy().astype(np.uint32)))
+        assert fa == fb, "the scheduled read did not read every piece once"
+
+
 def test_lm_head_full_size_sampled(dev):
     """Qwen3-8B-shaped head at full size in the benchmark's launch
     configuration; oracle on sampled vocabulary rows incl. the ragged tail."""
