@@ -180,6 +180,39 @@ __device__ __forceinline__ uint64_t row_max64(uint64_t v) {
   return v;
 }
 
+// The unit schedule of the scheduled GEMV (gemv_sched_kernel). Workgroup
+// b's units: first S2 static ones, with
+// S = chunk >= 2 the contiguous run b*S .. b*S + S - 1 (S*G <= T, set on the
+// host), else b and b + G; then D0 + v for each take v of the counter, D0 =
+// S2 * G. A take is issued at the start of position S2 - 2 (always) and of
+// every later position while the sequence goes on (take_at), and read at the
+// end of that position, so the unit after next is known before the next
+// unit's loads go out. Every workgroup takes until it gets a unit past the
+// last, so the G final takes return max(0, T - D0) .. + G - 1; the one that
+// returns the largest is the last take of the launch and stores 0, leaving
+// the counter as the launch found it. Takes are atomicInc (an add of 1 below
+// 2^32 - 1): an atomicAdd would be turned into a wave-wide reduction whose
+// result is waited for at once, which drains the loads in flight.
+struct UnitSched {
+  uint32_t G, b, S, S2, D0, T, final_take;
+  __device__ UnitSched(uint32_t nunits, int chunk)
+      : G(gridDim.x), b(blockIdx.x), S(chunk >= 2 ? static_cast<uint32_t>(chunk) : 0u), S2(S >= 2 ? S : 2u),
+        D0(S2 * gridDim.x), T(nunits), final_take((nunits > S2 * gridDim.x ? nunits - S2 * gridDim.x : 0u) + gridDim.x - 1) {}
+  __device__ uint32_t static_unit(uint32_t k) const { return S >= 2 ? b * S + k : b + k * G; }  // k < S2
+  __device__ bool take_at(uint32_t pos, uint32_t unext) const { return pos + 2 == S2 || (pos + 2 > S2 && unext < T); }
+  __device__ uint32_t take(uint32_t* counter) const {
+    const uint32_t v = atomicInc(counter, 0xffffffffu);
+    return v;
+  }
+  // After a take's value is known: the last take of the launch resets the counter.
+  __device__ void settle(uint32_t* counter, uint32_t v) const {
+    if (v == final_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+// Static units per workgroup of the scheduled GEMV: 90% of an equal share.
+inline int sched_static_units(int nunits, int groups) { return 90 * (nunits / groups) / 100; }
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------

@@ -652,8 +652,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_tstream_kernel(GemvParams p) 
 // than a workgroup takes at the sizes in use).
 //
 // The counter must read 0 when a launch starts, and the launch leaves it 0
-// (the workgroup whose take is the last of the launch stores 0; see the
-// loop). Launches that share a counter must be ordered (one stream).
+// (the workgroup whose take is the last of the launch stores 0; see
+// UnitSched). Launches that share a counter must be ordered (one stream).
 constexpr int kSchedU = 2;     // tiles per unit
 constexpr int kSchedCap = 64;  // units whose outputs a workgroup holds in LDS
 
@@ -771,32 +771,11 @@ __global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, ui
     __syncthreads();
   };
 
-  // This workgroup's units: first S2 static ones (no take needed, so the
-  // stream starts at once), then D0 + v for each take v. With S = p.chunk
-  // >= 2 the static ones are the contiguous run b*S .. b*S + S - 1 (S*G <= T,
-  // set on the host), else b and b + G; D0 = S2 * G. One take is in flight
-  // from the start of position S2 - 2 on: issued when a unit starts and
-  // read when it ends, so the unit after next is known before the next
-  // unit's loads go out. Every workgroup takes until it gets a unit past the
-  // last, so the G final takes return max(0, T - D0) .. + G - 1 and the one
-  // that returns the largest is the last take of the launch: it stores 0.
-  // Takes are atomicInc (an add of 1 below 2^32 - 1): an atomicAdd would be
-  // turned into a wave-wide reduction whose result is waited for at once,
-  // and the wait would drain the tiles in flight.
-  constexpr uint32_t kNoWrap = 0xffffffffu;
-  const uint32_t G = gridDim.x, b = blockIdx.x;
-  const uint32_t S = p.chunk >= 2 ? static_cast<uint32_t>(p.chunk) : 0u;
-  const uint32_t S2 = S >= 2 ? S : 2u;
-  const uint32_t D0 = S2 * G;
-  auto static_unit = [&](uint32_t k) { return S >= 2 ? b * S + k : b + k * G; };  // k < S2
-  const uint32_t first_final = nunits > D0 ? nunits - D0 : 0u;
-  const uint32_t final_take = first_final + G - 1;
-  uint32_t ucur = static_unit(0), unext = static_unit(1);
+  // This workgroup's units: a static run, then takes (UnitSched).
+  const UnitSched us(nunits, p.chunk);
+  uint32_t ucur = us.static_unit(0), unext = us.static_unit(1);
   if (ucur >= nunits) {  // uniform (only where T < G): no unit here; this workgroup's one take is final
-    if (tid == 0) {
-      const uint32_t v = atomicInc(counter, kNoWrap);
-      if (v == final_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) us.settle(counter, us.take(counter));
     return;
   }
 
@@ -810,10 +789,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, ui
   int ns = 0;
   uint32_t pending = 0;
   for (uint32_t pos = 0;; ++pos) {
-    // The unit after next comes from a take from position S2 - 2 on (there
-    // always, later while the sequence goes on).
-    const bool take = pos + 2 == S2 || (pos + 2 > S2 && unext < nunits);
-    if (tid == 0 && take) pending = atomicInc(counter, kNoWrap);
+    const bool take = us.take_at(pos, unext);  // the unit after next comes from a take
+    if (tid == 0 && take) pending = us.take(counter);
     if (tid == 0) ulist[ns] = ucur;
 #pragma unroll
     for (int q = 0; q < NPH; ++q) {
@@ -827,7 +804,7 @@ __global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, ui
       compute_publish(b1, afr[q], 1);
       load_tile(b1, nu, nq, 1);
       if (lastq && tid == 0 && take) {
-        if (pending == final_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        us.settle(counter, pending);
         sgrab[0] = pending;
       }
       __syncthreads();
@@ -836,8 +813,8 @@ __global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, ui
     ++ns;
     // (sgrab is rewritten only after the next unit's first barrier, which
     // every wave passes after this read)
-    const uint32_t after = take ? D0 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(sgrab[0]))
-                                : (pos + 2 < S2 ? static_unit(pos + 2) : nunits);
+    const uint32_t after = take ? us.D0 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(sgrab[0]))
+                                : (pos + 2 < us.S2 ? us.static_unit(pos + 2) : nunits);
     ucur = unext;
     unext = after;
     if (ucur >= nunits) break;  // uniform
@@ -1341,8 +1318,7 @@ hipError_t launch_gemv_sched(const uint16_t* W, int N, int K, const float* X, in
   // 0% (b and b + G, then all from the counter) 188.5 us, 50% 180 us, 80%
   // 179 us, 90% 178.5 us, 100% (only the remainder handed out) 185 us, equal
   // shares 187 us; at K = 2048: 102, 96, 92.5, 91.4, 93 and 93.6 us.
-  const int nunits = ((N + 15) / 16 + kSchedU - 1) / kSchedU;
-  const int S = 90 * (nunits / cus) / 100;
+  const int S = sched_static_units(((N + 15) / 16 + kSchedU - 1) / kSchedU, cus);
   prm.chunk = S >= 2 ? S : 0;
   return KB <= 16 * 4 ? launch_sched<1>(prm, counter, cus, stream) : launch_sched<2>(prm, counter, cus, stream);
 }
