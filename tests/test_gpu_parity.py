@@ -100,6 +100,9 @@ SCHED_CASES = [
     # workgroup (the first ones taken from the counter)
     (7, 33, 256), (8, 4099, 4096), (3, 1000, 2056), (7, 64, 4096), (1, 1, 8), (5, 70001, 1024),
     (7, 12800, 512), (7, 19200, 256),
+    # 65 static units per workgroup: its LDS holds 64 units' outputs, so it
+    # writes them out mid-way and goes on
+    (2, 600001, 8),
 ]
 
 
