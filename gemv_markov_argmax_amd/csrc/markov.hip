@@ -56,6 +56,11 @@
 //    clears and leaves. Every call after that samples normally, and the
 //    first one that completes removes the repair record. No caller action
 //    is needed.
+//  * The round's lm_head (dspark_draft_round) takes its rows from a counter
+//    word of this workspace and leaves it 0. A nonzero word at the start of
+//    the loop means that lm_head started on a dirty counter (a workspace that
+//    was never zero-filled) and left base rows out: that call's ids are -2,
+//    workgroup 0 stores 0, and the next round is whole again.
 //  * Nothing but the exchange sits on the per-step path of workgroup 0: the
 //    drafted tokens stay in LDS and the ids (d2t applied) are written once,
 //    after the last step.
@@ -203,6 +208,10 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   const uint32_t seq = load_coherent(p.ctl + kCtlSeq);
   const uint32_t state = load_coherent(p.ctl + kCtlState);
   const uint32_t repaired_by = load_coherent(p.ctl + kCtlRepairedBy);
+  // The round's lm_head counter (dspark_draft_round): a clean lm_head leaves
+  // it 0, so a nonzero word means that lm_head ran on a counter that was not
+  // (the workspace was never zero-filled) and some base rows are missing.
+  const uint32_t lm_counter = load_coherent(p.ctl + kCtlLmCounter);
   // kStateRepaired under this launch's number: a late workgroup of the
   // repairing launch, or a replay of that captured launch.
   const bool repair = !(state == kStateOk || (state == kStateRepaired && repaired_by != p.nonce));
@@ -316,7 +325,10 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   // up, every id is -2 and the state stays as it is (the next call repairs).
   auto finish = [&]() {
     if (G == 1) clear_other();
-    const bool bad = load_coherent(p.ctl + kCtlState) == kStateTimedOut;
+    const bool timed_out = load_coherent(p.ctl + kCtlState) == kStateTimedOut;
+    const bool bad = timed_out || lm_counter != 0u;
+    if (tid == 0 && lm_counter != 0u)  // this call's ids are -2; the next round starts clean
+      __hip_atomic_store(p.ctl + kCtlLmCounter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int e = tid; e < R * p.k; e += kLoopThreads) {
       const int m = e / p.k, st = e - m * p.k;
       int64_t id = -1;
@@ -326,7 +338,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
       }
       p.ids[e] = bad ? -2 : id;
     }
-    if (tid == 0 && !bad) {
+    if (tid == 0 && !timed_out) {
       __hip_atomic_store(p.ctl + kCtlUsed + cur, static_cast<uint32_t>(p.k * R * G), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctl + kCtlReps + cur, static_cast<uint32_t>(p.nrep), __ATOMIC_RELAXED,
@@ -347,6 +359,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     if (blockIdx.x != 0) return;
     for (int e = tid; e < R * p.k; e += kLoopThreads) p.ids[e] = -2;
     if (tid == 0) {
+      __hip_atomic_store(p.ctl + kCtlLmCounter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (state == kStateRepaired) {
         __hip_atomic_store(p.ctl + kCtlRepairedBy, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {

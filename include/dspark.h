@@ -326,12 +326,17 @@ dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B,
  * logit goes back.
  *
  * Equivalent to, in this order on `stream`,
- *   dspark_lm_head(W_lm, V, d, H, num_reqs * B, base_out)
+ *   dspark_lm_head_sched(W_lm, V, d, H, num_reqs * B, base_out, <counter>)
  *   dspark_markov_sample(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, ...)
  *   dspark_conf_probe(H, num_reqs * B, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out)
- * and bit-identical to those three calls. The probe runs inside the Markov
- * loop's launch (as in dspark_markov_sample_probe), so the round is two
- * kernels instead of three.
+ * and bit-identical to those three calls, <counter> being the uint32 at
+ * byte 64 of the workspace (a control word the loop does not otherwise
+ * use). The probe runs inside the Markov loop's launch (as in
+ * dspark_markov_sample_probe), so the round is two kernels instead of three.
+ * A zero-filled workspace keeps that word 0 across rounds. If it is not 0
+ * when the loop starts (a workspace that was never zero-filled), the
+ * lm_head may have left base rows out: that round's ids are all -2 and the
+ * word is set back to 0, so the next round is whole again.
  *
  *   W_lm      bf16  [V, d]                 16-byte aligned
  *   H         fp32  [num_reqs * B, d]      16-byte aligned (hidden states, also the probe's x)

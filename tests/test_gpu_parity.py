@@ -600,6 +600,28 @@ def test_round_chained(dev, name):
     probe_close(lg.cpu().numpy(), ps.cpu().numpy(), ref["logit"], ref["passed"], float(inp["probe_threshold"]))
 
 
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head"])
+def test_draft_round_dirty_lm_counter(dev, name):
+    """A workspace whose lm_head counter word is not 0 (never zero-filled):
+    that round's ids are all -2 and the word goes back to 0; the next round
+    gives the ids of a clean workspace."""
+    inp, t = _round_tensors(name, dev)
+    say(f"[draft_round dirty counter {name}] seed={inp['seed']}")
+    ops = _ops()
+    R, B, k, V = inp["num_reqs"], inp["B"], inp["k"], inp["V"]
+    clean = ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k)["ids"].clone()
+    ws = ops.markov_workspace(R, k, V, dev)
+    word = ops.markov_lm_counter_offset() // 4
+    ws.view(torch.int32)[word] = 12345
+    out = ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert (out["ids"] == -2).all(), "a round on a dirty lm_head counter was not reported"
+    assert int(ws.view(torch.int32)[word].item()) == 0, "the counter word was not set back to 0"
+    again = ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again["ids"], clean)
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head", "reduced_vocab_batched", "lane27b"])
 def test_draft_round_fused(dev, name):
     """dspark_draft_round (the probe inside the Markov launch) gives the same
