@@ -634,8 +634,9 @@ def main():
     del big
     torch.cuda.synchronize()
     # the ceiling of the lm_head's own schedule: scheduled rows where the
-    # round's lm_head takes them (bf16, rows <= 8, d <= 4096)
-    sched_lm = (not q8) and rows <= 8 and inp["d"] <= 4096
+    # round's lm_head takes them (bf16, rows <= 8, d <= 4096, more than 16
+    # tiles of 16 rows per CU)
+    sched_lm = (not q8) and rows <= 8 and inp["d"] <= 4096 and inp["V"] > 16 * 16 * cus
     ceil_ref = "lm_head_schedule" if sched_lm else "lm_head_shape"
 
     rounds_per_s = args.steps / elapsed

@@ -1277,9 +1277,15 @@ hipError_t launch_gemv_gated_norm(const uint16_t* W, int F, int K, const float* 
   return dispatch_short<true, true>(prm, pl, stream);
 }
 
+// Long streams only (more than kShortTiles tiles per workgroup, where the
+// plan would take the streaming kernel): on a few tiles per CU the short
+// kernel is faster (the tiny round's [4 x 256] x [4096 x 256] lm_head: 7.2
+// against 10.9 us) and there is no tail to balance.
 bool gemv_sched_fits(int N, int K, int M) {
   const int KB = (K + 31) / 32;
-  return N >= 1 && M >= 1 && M <= 8 && K >= 8 && KB <= 2 * 16 * 4;
+  if (N < 1 || M < 1 || M > 8 || K < 8 || KB > 2 * 16 * 4) return false;
+  const int cus = device_cu_count();
+  return cus > 0 && !make_plan(M, N, K, cus).shortk;
 }
 
 size_t gemv_sched_lds_bytes() {

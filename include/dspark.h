@@ -127,9 +127,11 @@ dspark_status dspark_lm_head(const uint16_t* W_lm, int V, int d, const float* H,
  *            must read 0 before the first call (zero-fill it once); every
  *            call leaves it 0 again. Calls that share a counter must be
  *            ordered on one stream.
- * Applies where rows <= 8 and d <= 4096; other shapes run dspark_lm_head's
- * kernels and leave the counter alone. dspark_draft_round runs its lm_head
- * this way, with a word of its workspace as the counter.
+ * Applies where rows <= 8, d <= 4096 and the vocabulary is long enough to
+ * give every compute unit more than 16 tiles of 16 rows (V > 256 x the
+ * device's compute units); other shapes run dspark_lm_head's kernels and
+ * leave the counter alone. dspark_draft_round runs its lm_head this way,
+ * with a word of its workspace as the counter.
  * Errors: those of dspark_lm_head; DSPARK_ERR_NULL for a null counter,
  * DSPARK_ERR_ALIGN for a misaligned one.
  */

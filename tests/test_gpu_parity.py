@@ -94,12 +94,12 @@ def test_draft_layer_fused_projections(dev):
 
 
 SCHED_CASES = [
-    # (rows, V, d): one K phase, two (the second partial), a ragged last unit,
-    # fewer units than workgroups, one row, many units; units of 32 rows:
-    # between one and two per workgroup of 256, and just over two per
-    # workgroup (the first ones taken from the counter)
-    (7, 33, 256), (8, 4099, 4096), (3, 1000, 2056), (7, 64, 4096), (1, 1, 8), (5, 70001, 1024),
-    (7, 12800, 512), (7, 19200, 256),
+    # (rows, V, d): the scheduled kernel takes vocabularies of more than 16
+    # tiles of 16 rows per CU (V > 65536 on 256 CUs): a ragged last unit of
+    # 32 rows, two K phases (the second full, then partial), a single row
+    # with one partial k-block; smaller vocabularies run dspark_lm_head's
+    # kernels and leave the counter alone
+    (5, 70001, 1024), (8, 66003, 4096), (3, 70000, 2056), (1, 65601, 8), (7, 33, 256), (7, 19200, 256),
     # 65 static units per workgroup: its LDS holds 64 units' outputs, so it
     # writes them out mid-way and goes on
     (2, 600001, 8),
