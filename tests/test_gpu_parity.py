@@ -61,6 +61,40 @@ def test_gemv_matches_oracle(dev, entry, M, N, K):
     logits_close(y.cpu().numpy(), oracle.gemv(W, X), f"{entry} M={M} N={N} K={K}")
 
 
+MWIDE_CASES = [
+    # (M, N, K) with 16 < M <= 80, one launch: every count of A blocks (a hi
+    # and a lo block per 16 rows, one shared block for an odd last group of
+    # at most 8), ragged N (past a multiple of 128 and of 16), K tails
+    # (K % 128 != 0, one k-group of 8), K of several pipeline rounds
+    (17, 300, 136), (24, 1000 + 5, 776), (25, 129, 8), (32, 515, 1032), (40, 2000 + 3, 264),
+    (41, 128, 5120), (48, 700, 520), (49, 1000, 1544), (56, 257, 776), (64, 1001, 264),
+    (65, 3000, 1032), (72, 4000 + 3, 5120), (73, 515, 776), (80, 1027, 2056),
+]
+
+
+@pytest.mark.parametrize("M,N,K", MWIDE_CASES)
+def test_gemv_medium_m_matches_oracle(dev, M, N, K):
+    """The batched lm_head's small-GEMM path: every output within the
+    tolerance of the oracle, reruns bit-identical, and a residual added to
+    the outputs in place."""
+    seed = 7300 + M * 31 + N + K
+    say(f"[gemv medium M] M={M} N={N} K={K} seed={seed}")
+    W, X = synth.gemv_inputs(M, N, K, seed)
+    ops = _ops()
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    y = ops.lm_head(Wd, Xd)
+    y2 = ops.lm_head(Wd, Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "rerun differs"
+    ref = oracle.gemv(W, X)
+    logits_close(y.cpu().numpy(), ref, f"lm_head M={M} N={N} K={K}")
+    r = torch.randn(M, N, device=dev, generator=torch.Generator(device=dev).manual_seed(seed))
+    r0 = r.clone()
+    ops.proj_smallm_add(Wd, Xd, r, out=r)
+    torch.cuda.synchronize()
+    assert torch.equal(r, r0 + y), "residual not added to the same outputs"
+
+
 @pytest.mark.parametrize("name", ["draft_layer"])
 def test_draft_layer_projections(dev, name):
     inp = synth.layer_inputs()
