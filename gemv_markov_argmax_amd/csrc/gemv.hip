@@ -882,11 +882,12 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   const int brow = tid >> 4, bpc = tid & 15;
   u32x4 bq[3][kMrBQ];   // weights of chunk j: set j%3
   float4 aq[2][kMrAQ];  // X of chunk j: set j%2 (from L2, so one chunk less ahead)
-  // Workgroup b walks the K chunks starting at chunk b % nchunks, so the
-  // workgroups of an XCD read X from different lines of its L2 at any one
+  // Workgroup b walks the K chunks starting at chunk (b / 8) % nchunks:
+  // workgroups go to the 8 XCDs in turn, so those of one XCD start at
+  // different chunks and read X from different lines of its L2 at any one
   // time. (Step c of the walk is chunk rot(c); past the last step, out of
   // range.)
-  const int r0 = static_cast<int>(blockIdx.x % static_cast<unsigned>(nchunks));
+  const int r0 = static_cast<int>((blockIdx.x >> 3) % static_cast<unsigned>(nchunks));
   auto rot = [&](int c) { return c >= nchunks ? nchunks : (c + r0 >= nchunks ? c + r0 - nchunks : c + r0); };
   auto issue_b = [&](int set, int cs) {
     const int c = rot(cs);
