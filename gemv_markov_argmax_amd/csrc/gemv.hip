@@ -17,17 +17,22 @@
 //    fp32. The expected logit error is ~1e-5. For M <= 8 the hi and lo rows
 //    share one 16-row A block (rows 0..7 hi, 8..15 lo): one MFMA per 1 KB of
 //    weights.
-//  * Three kernels, chosen by shape:
+//  * Four kernels, chosen by shape and entry point:
 //      - gemv_short_kernel: M <= 16, at most 16 tiles of 16 rows per workgroup
 //        (the projections of a draft layer): the shortest dependency chain.
+//        Variants fuse the RMSNorm of X and the gated activation.
 //      - gemv_tstream_kernel: M <= 16, many tiles per workgroup (the
 //        lm_heads): K split over 16 waves, two tiles of loads in flight,
 //        outputs summed in LDS and written once per chunk of tiles.
+//      - gemv_sched_kernel: the streaming kernel's work for M <= 8 and
+//        K <= 4096 with rows handed out by a counter after a static run per
+//        workgroup, which balances the XCDs (dspark_lm_head_sched).
 //      - gemv_mrows_kernel: 16 < M <= 80 per launch (batched requests): a
 //        small GEMM streaming K chunks of weights and A through LDS.
-//  * Summation order depends on the shape only (never on timing), so reruns
-//    are bit-identical; for M <= 16 an output row does not depend on the
-//    other rows, and equal weight rows give equal outputs.
+//  * Summation order depends on the shape only (never on timing or on which
+//    workgroup took a row), so reruns are bit-identical; for M <= 16 an
+//    output row does not depend on the other rows, and equal weight rows
+//    give equal outputs.
 #include "dspark_internal.h"
 
 #include <algorithm>
