@@ -1,18 +1,19 @@
-"""A seeded sweep of GEMV shapes against the fp64 oracle on an MI355X.
+"""A seeded sweep of shapes against the fp64 oracle on an MI355X.
 
 The parity tests of test_gpu_parity.py pick their shapes by hand, one per
 case the kernels distinguish. This sweep draws further shapes from a fixed
 seed across every entry point's size range, so the boundaries between the
-kernels (tiles per workgroup, K phases, packed or split A blocks, the
-scheduled lm_head's reach, launches of more than 16 or 80 rows) are crossed
-at places nobody chose. The draw is the same on every run.
+kernel variants (tiles per workgroup, K phases, packed or split A blocks,
+the scheduled lm_head's reach, launches of more than 16 or 80 rows, the
+Markov loop's grid, register and LDS tiles, request counts) are crossed at
+places nobody chose. The draw is the same on every run.
 """
 import numpy as np
 import pytest
 
 import oracle
 from gemv_markov_argmax_amd import synth
-from parity import logits_close, say
+from parity import check_markov, logits_close, probe_close, say
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +122,75 @@ def test_sweep_norm(dev, M, N, K):
     y = ops.proj_smallm_norm(ops.bf16_from_bits(W, dev), _up(X, dev), ops.bf16_from_bits(gamma, dev), 1e-6)
     torch.cuda.synchronize()
     logits_close(y.cpu().numpy(), oracle.gemv(W, oracle.rmsnorm(X, gamma, 1e-6)), f"proj norm M={M} N={N} K={K}")
+
+
+def _draw_markov(seed, n):
+    """n shapes (R, B, k, V, r, tie_frac): up to 16 requests and 16 steps,
+    V log-uniform up to 60000, r a multiple of 8 up to 512; every other one
+    (where V leaves room for two entries per row) with exactly tied maxima in
+    5% of its base rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for j in range(n):
+        R = int(rng.integers(1, 17))
+        B = int(rng.integers(1, 17))
+        k = int(rng.integers(1, B + 1))
+        V = int(np.exp(rng.uniform(0.0, np.log(60000))))
+        r = 8 * int(rng.integers(1, 65))
+        out.append((R, B, k, V, r, 0.05 if j % 2 and V >= 4 * R * B else 0.0))
+    return out
+
+
+MARKOV_SHAPES = _draw_markov(20255, 14)
+
+
+@pytest.mark.parametrize("R,B,k,V,r,tie", MARKOV_SHAPES)
+def test_sweep_markov(dev, R, B, k, V, r, tie):
+    seed = 8500 + R * 7 + V + r
+    say(f"[sweep markov] R={R} B={B} k={k} V={V} r={r} tie={tie} seed={seed}")
+    base, w1, w2, prev0, _ = synth.markov_inputs(R, B, V, r, seed, tie_frac=tie)
+    ops = _ops()
+    ids = ops.markov_sample(_up(base, dev), ops.bf16_from_bits(w1, dev), ops.bf16_from_bits(w2, dev),
+                            _up(prev0, dev), k)
+    torch.cuda.synchronize()
+    check_markov(ids.cpu().numpy(), base, w1, w2, prev0, k)
+
+
+def _draw_rounds(seed, n):
+    """n whole-round shapes (R, B, k, V, d, r): R * B <= 72 rows (one or
+    more lm_head kernels), V log-uniform from 16 to 40000, d a multiple of 8
+    up to 1024, r a multiple of 8 up to 256."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        R = int(rng.integers(1, 9))
+        B = int(rng.integers(1, 10))
+        k = int(rng.integers(1, B + 1))
+        V = int(np.exp(rng.uniform(np.log(16), np.log(40000))))
+        d = 8 * int(rng.integers(1, 129))
+        r = 8 * int(rng.integers(1, 33))
+        out.append((R, B, k, V, d, r))
+    return out
+
+
+ROUND_SHAPES = _draw_rounds(20256, 8)
+
+
+@pytest.mark.parametrize("R,B,k,V,d,r", ROUND_SHAPES)
+def test_sweep_draft_round(dev, R, B, k, V, d, r):
+    """dspark_draft_round end to end: logits, drafted ids and probe."""
+    seed = 8600 + R * 7 + V + d + r
+    say(f"[sweep round] R={R} B={B} k={k} V={V} d={d} r={r} seed={seed}")
+    W, H = synth.gemv_inputs(R * B, V, d, seed)
+    _, w1, w2, prev0, _ = synth.markov_inputs(R, 1, V, r, seed)
+    _, pw = synth.probe_inputs(1, d, seed)
+    thr = 0.01
+    ops = _ops()
+    out = ops.draft_round(ops.bf16_from_bits(W, dev), _up(H, dev), ops.bf16_from_bits(w1, dev),
+                          ops.bf16_from_bits(w2, dev), _up(prev0, dev), B, k, probe_w=ops.bf16_from_bits(pw, dev),
+                          probe_bias=-0.02, probe_threshold=thr)
+    torch.cuda.synchronize()
+    ref = oracle.draft_round(W, H, w1, w2, prev0, R, B, k, pw, -0.02, thr)
+    logits_close(out["base"].view(R * B, -1).cpu().numpy(), ref["base"], "sweep round logits")
+    check_markov(out["ids"].cpu().numpy(), ref["base32"], w1, w2, prev0, k)
+    probe_close(out["logit"].cpu().numpy(), out["passed"].cpu().numpy(), ref["logit"], ref["passed"], thr)
