@@ -17,6 +17,10 @@
 //  * Each wave loads its 16 x 256-byte (128-byte) segment of a tile in whole
 //    128-byte lines (non-temporal raw buffer loads; zeros past the range),
 //    together with the tile's scales, and stages both in a private LDS area.
+//    The scales come two per 32-bit load where rows allow (K / 32 even):
+//    a wave's scales of a tile are 16 rows apart, so each load instruction
+//    touches 16 lines for a few bytes of each, and halving the instructions
+//    took the Qwen3-8B-shaped Q8_0 lm_head from ~114 to ~109 us.
 //  * B fragments: 8 quants per lane, converted exactly to bf16 (a signed
 //    byte has at most 8 significant bits: one sign-extending convert per
 //    value and a byte permute per pair). A fragments: X split exactly into
@@ -75,7 +79,7 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 // KBW: 32-entry blocks per wave and phase (4 or 8: 128 or 256 quant bytes
 // of each row per wave). MULTI: more than one K phase (the chunk loop runs
 // every phase per chunk).
-template <bool PACK, bool MULTI, int KBW>
+template <bool PACK, bool MULTI, int KBW, bool PAIRED>
 __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
   constexpr int NW = kQNW;
   constexpr int SEG = 32 * KBW;     // quant bytes of a row segment
@@ -116,7 +120,12 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
 
   u32x4 afr[KBW][F];
   u32x4 b0[NLD], b1[NLD];
-  uint32_t s0[SPL], s1[SPL];  // scale halves of this lane: row i, blocks g + 4j of the segment
+  // Scales of this lane: with an even number of blocks per row, one word of
+  // two (row i, blocks 2g and 2g + 1 of the segment, lanes 2g < KBW), so a
+  // wave's scales of a tile take one load instruction instead of KBW / 4;
+  // else halves (row i, blocks g + 4j).
+  constexpr bool paired = PAIRED;  // the host launches it for K / 32 even only
+  uint32_t s0[SPL], s1[SPL];
   int ph = 0, c0 = 0, c1 = 0, lim = 0;
   uint32_t lane_off = 0, sc_off[SPL];
 
@@ -129,8 +138,10 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
                                       : kBufOutOfRange;
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
-      const int blk = kseg / 32 + g + 4 * j;
-      sc_off[j] = blk < KB ? static_cast<uint32_t>(i) * drow + static_cast<uint32_t>(blk) * 2 : kBufOutOfRange;
+      const int blk = paired ? kseg / 32 + 2 * g : kseg / 32 + g + 4 * j;
+      sc_off[j] = blk < KB && (!paired || 2 * g < KBW)
+                      ? static_cast<uint32_t>(i) * drow + static_cast<uint32_t>(blk) * 2
+                      : kBufOutOfRange;
     }
   };
   // A fragments of phase ph: block kb covers k = kseg + 32*kb + 8*g + (0..7).
@@ -175,10 +186,15 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
     const uint32_t off = live ? lane_off + static_cast<uint32_t>(rr) * 16 * rowb : kBufOutOfRange;
 #pragma unroll
     for (int q = 0; q < NLD; ++q) b[q] = buf_load16_nt(qres, off + static_cast<uint32_t>(q * RPI) * rowb);
+    if (paired) {
+      s[0] = __builtin_amdgcn_raw_buffer_load_b32(
+          dres, static_cast<int>(live ? sc_off[0] + static_cast<uint32_t>(rr) * 16 * drow : kBufOutOfRange), 0, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < SPL; ++j)
-      s[j] = __builtin_amdgcn_raw_buffer_load_b16(
-          dres, static_cast<int>(live ? sc_off[j] + static_cast<uint32_t>(rr) * 16 * drow : kBufOutOfRange), 0, 0);
+      for (int j = 0; j < SPL; ++j)
+        s[j] = __builtin_amdgcn_raw_buffer_load_b16(
+            dres, static_cast<int>(live ? sc_off[j] + static_cast<uint32_t>(rr) * 16 * drow : kBufOutOfRange), 0, 0);
+    }
   };
   auto prologue = [&](bool with_a) {
     load(b0, s0, c0);
@@ -190,8 +206,12 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
   auto compute_publish = [&](u32x4 (&b)[NLD], const uint32_t (&s)[SPL], int buf) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wr_base + RPI * q * RS) = b[q];
+    if (paired) {
+      if (2 * g < KBW) *reinterpret_cast<uint32_t*>(wsc + i * KBW + 2 * g) = s[0];
+    } else {
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) wsc[i * KBW + g + 4 * j] = static_cast<uint16_t>(s[j]);
+      for (int j = 0; j < SPL; ++j) wsc[i * KBW + g + 4 * j] = static_cast<uint16_t>(s[j]);
+    }
     float scale[KBW];  // the KBW scales of row i
 #pragma unroll
     for (int j = 0; j < KBW / 4; ++j) {
@@ -501,10 +521,10 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_short_kernel(Q8Params p)
   }
 }
 
-template <bool PACK, int KBW>
-hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
-  const void* one = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, false, KBW>);
-  const void* many = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, true, KBW>);
+template <bool PACK, int KBW, bool PAIRED>
+hipError_t launch_q8_as(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
+  const void* one = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, false, KBW, PAIRED>);
+  const void* many = reinterpret_cast<const void*>(&gemv_q8_kernel<PACK, true, KBW, PAIRED>);
   static const hipError_t attr = [&] {
     const hipError_t e = hipFuncSetAttribute(one, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kQLds));
     return e != hipSuccess ? e
@@ -514,6 +534,13 @@ hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipS
   Q8Params a = prm;
   void* args[] = {&a};
   return hipLaunchKernel(multi ? many : one, dim3(grid), dim3(kQNW * kWave), args, lds, st);
+}
+
+// Scale words of two blocks need 4-byte aligned scale rows: K / 32 even.
+template <bool PACK, int KBW>
+hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
+  return (prm.K / 32) % 2 == 0 ? launch_q8_as<PACK, KBW, true>(prm, grid, lds, multi, st)
+                               : launch_q8_as<PACK, KBW, false>(prm, grid, lds, multi, st);
 }
 
 template <bool PACK, int KBW>
