@@ -418,7 +418,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and no multi-GPU "
-              "path is built (see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+              "path is built. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
