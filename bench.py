@@ -345,7 +345,7 @@ def bench_block(args, dev, layers: int, with_head: bool):
         head = dict(W=ops.bf16_from_bits(hinp["W_lm"], dev), w1=ops.bf16_from_bits(hinp["w1"], dev),
                     w2=ops.bf16_from_bits(hinp["w2"], dev), prev0=torch.from_numpy(hinp["prev0"]).to(dev),
                     pw=ops.bf16_from_bits(hinp["probe_w"], dev), base=torch.empty(R, B, V, device=dev),
-                    ws=ops.markov_workspace(R, k, V, dev), k=k)
+                    ws=ops.draft_round_workspace(R, B, k, V, d, dev), k=k)
         out_host = torch.empty(R * k * 8 + M * 8, dtype=torch.uint8, pin_memory=True)
         ids = out_host[: R * k * 8].view(torch.int64).view(R, k)
         plog = out_host[R * k * 8: R * k * 8 + M * 4].view(torch.float32)
@@ -462,7 +462,11 @@ def main():
     prev0 = torch.from_numpy(inp["prev0"]).to(dev)
     pw = ops.bf16_from_bits(inp["probe_w"], dev)
     logits = torch.empty(rows, V, device=dev)
-    ws = ops.markov_workspace(R, k, V, dev)
+    # The round's workspace: the Markov loop's, then (more than 16 rows, bf16)
+    # the split lm_head's, which starts at the next 256-byte boundary.
+    ws = ops.markov_workspace(R, k, V, dev) if q8 else ops.draft_round_workspace(R, B, k, V, d, dev)
+    split_at = (ops.markov_workspace_bytes(R, k, V) + 255) // 256 * 256
+    split = not q8 and ops.lm_head_split_workspace_bytes(V, d, rows) > 0
     # The round's results (drafted ids, probe logits and gates) are stored by
     # the kernels straight into pinned host memory mapped for the device: no
     # copy follows the round.
@@ -473,9 +477,11 @@ def main():
     bias, thr = float(inp["probe_bias"]), float(inp["probe_threshold"])
     torch.cuda.synchronize()
 
-    def lm():  # the round's own lm_head: rows handed out by the workspace's counter word
+    def lm():  # the round's own lm_head: rows handed out by the workspace's counter word, or K split
         if q8:
             ops.lm_head_q8(*W, H, out=logits)
+        elif split:
+            ops.lm_head_split(W, H, ws[split_at:], out=logits)
         else:
             ops.lm_head_sched(W, H, ws, out=logits, counter_offset=ops.markov_lm_counter_offset())
 
@@ -500,7 +506,8 @@ def main():
     # with the probe on its idle waves, in order on one stream, the results
     # landing in host memory. In the rounds that carry HIP events around the
     # lm_head, the same two launches are issued by their own entry points
-    # (dspark_lm_head_sched on the workspace's counter word, or
+    # (dspark_lm_head_sched on the workspace's counter word,
+    # dspark_lm_head_split on the workspace's split part, or
     # dspark_lm_head_q8; dspark_markov_sample_probe), so that the events can
     # sit between them.
     main_stream = torch.cuda.current_stream()
@@ -638,6 +645,9 @@ def main():
     # tiles of 16 rows per CU)
     sched_lm = (not q8) and rows <= 8 and inp["d"] <= 4096 and inp["V"] > 16 * 16 * cus
     ceil_ref = "lm_head_schedule" if sched_lm else "lm_head_shape"
+    lm_label = ("lm_head GEMV (dspark_lm_head_q8)" if q8 else "lm_head GEMV (dspark_lm_head_split)" if split
+                else "lm_head GEMV (dspark_lm_head_sched)" if sched_lm
+                else "lm_head GEMV (dspark_lm_head_sched, running dspark_lm_head's kernel at this shape)")
 
     rounds_per_s = args.steps / elapsed
     round_us = 1e6 * elapsed / args.steps
@@ -676,7 +686,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "num_reqs": R, "B": B, "k": k, "d": d, "V": V, "r": r,
                    "weights": "q8_0" if q8 else "bf16"},
-        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (dspark_lm_head_q8)" if q8 else "lm_head GEMV (dspark_lm_head_sched)",
+        "roofline": {"bound": "hbm", "kernel": lm_label,
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
                      "traffic": tr_lm, "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3,
                      "frac_of_stream_ceiling": lm_gbs / ceil[ceil_ref]["gbs"], "stream_ceiling_ref": ceil_ref},

@@ -33,6 +33,10 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Where the round's split lm_head workspace starts: past the Markov loop's,
+// on a 256-byte boundary.
+size_t round_split_offset(size_t markov_bytes) { return (markov_bytes + 255) / 256 * 256; }
+
 dspark_status gemv_checks(const uint16_t* W, int N, int K, const float* X, int M, const float* Y) {
   if (!W || !X || !Y) return DSPARK_ERR_NULL;
   if (N < 1 || K < 8 || (K % 8) != 0 || M < 1 || !dspark::gemv_shape_fits(N, K, M)) return DSPARK_ERR_SHAPE;
@@ -94,6 +98,23 @@ dspark_status dspark_lm_head_sched(const uint16_t* W_lm, int V, int d, const flo
   if (!counter) return DSPARK_ERR_NULL;
   if (!aligned(counter, 4)) return DSPARK_ERR_ALIGN;
   return from_hip(dspark::launch_gemv_sched(W_lm, V, d, H, rows, logits, counter, static_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_lm_head_split_workspace_bytes(int V, int d, int rows) {
+  if (V < 1 || d < 1 || rows < 1) return 0;
+  return dspark::gemv_split_workspace_bytes(V, d, rows);
+}
+
+dspark_status dspark_lm_head_split(const uint16_t* W_lm, int V, int d, const float* H, int rows, float* logits,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  const dspark_status st = gemv_checks(W_lm, V, d, H, rows, logits);
+  if (st != DSPARK_OK) return st;
+  const size_t need = dspark::gemv_split_workspace_bytes(V, d, rows);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need == 0) return from_hip(dspark::launch_gemv(W_lm, V, d, H, rows, logits, s));
+  if (!workspace || workspace_bytes < need) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSPARK_ERR_ALIGN;
+  return from_hip(dspark::launch_gemv_split(W_lm, V, d, H, rows, logits, workspace, s));
 }
 
 dspark_status dspark_lm_head_q8(const int8_t* Wq, const uint16_t* Wd, int V, int d, const float* H, int rows,
@@ -223,6 +244,13 @@ dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B,
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t dspark_draft_round_workspace_bytes(int num_reqs, int B, int k, int V, int d) {
+  if (num_reqs < 1 || num_reqs > 16 || B < 1 || B > (1 << 20) || d < 1) return 0;
+  const size_t mk = dspark::markov_workspace_bytes(num_reqs, k, V);
+  if (mk == 0) return 0;
+  return round_split_offset(mk) + dspark::gemv_split_workspace_bytes(V, d, num_reqs * B);
+}
+
 dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float* H, int num_reqs, int B,
                                  const uint16_t* w1, const uint16_t* w2, int r, const int64_t* d2t,
                                  const int64_t* prev0, int k, const uint16_t* probe_w, float probe_bias,
@@ -235,8 +263,14 @@ dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float
     st = markov_checks(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace, workspace_bytes);
   if (st == DSPARK_OK && probe_w) st = probe_checks(H, rows, d, probe_w, logit_out, pass_out);
   if (st != DSPARK_OK) return st;
+  const size_t split = dspark::gemv_split_workspace_bytes(V, d, rows);
+  const size_t split_at = round_split_offset(dspark::markov_workspace_bytes(num_reqs, k, V));
+  if (split > 0 && workspace_bytes < split_at + split) return DSPARK_ERR_WORKSPACE;
+  if (split > 0 && !aligned(workspace, 256)) return DSPARK_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = dspark::launch_gemv_sched(W_lm, V, d, H, rows, base_out, dspark::markov_lm_counter(workspace), s);
+  const hipError_t e =
+      split > 0 ? dspark::launch_gemv_split(W_lm, V, d, H, rows, base_out, static_cast<unsigned char*>(workspace) + split_at, s)
+                : dspark::launch_gemv_sched(W_lm, V, d, H, rows, base_out, dspark::markov_lm_counter(workspace), s);
   if (e != hipSuccess) return DSPARK_ERR_HIP;
   const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
   return from_hip(dspark::launch_markov(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,

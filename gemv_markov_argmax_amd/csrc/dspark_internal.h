@@ -51,6 +51,17 @@ __device__ __forceinline__ u32x4 buf_load16_nt(BufRes r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2));
 }
 
+// 16 bytes with agent scope (cache policy sc1): the load and store that
+// relaxed agent-scope atomics compile to on gfx950. A store completes (and
+// leaves the wave's vmcnt) once workgroups on any XCD can load its value
+// this way.
+__device__ __forceinline__ u32x4 buf_load16_coherent(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 16));
+}
+__device__ __forceinline__ void buf_store16_coherent(BufRes r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 16);
+}
+
 __device__ __forceinline__ float4 buf_load_f32x4(BufRes r, uint32_t off) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
 }
@@ -253,6 +264,16 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
 // Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,
                        hipStream_t stream, const float* res = nullptr);
+// The same product for 16 < M with K split in two halves computed by
+// different workgroups (half the activations per compute unit), their
+// partials added in a caller workspace of gemv_split_workspace_bytes(N, K,
+// M) bytes (256-byte aligned, zero-filled once; every launch leaves its
+// ticket words 0). Shapes outside gemv_split_fits, or a null workspace, run
+// launch_gemv.
+bool gemv_split_fits(int N, int K, int M);
+size_t gemv_split_workspace_bytes(int N, int K, int M);
+hipError_t launch_gemv_split(const uint16_t* W, int N, int K, const float* X, int M, float* Y, void* workspace,
+                             hipStream_t stream, const float* res = nullptr);
 // The same product with the weight rows handed out to workgroups by a
 // counter (see dspark_lm_head_sched) where the shape allows (M <= 8,
 // K <= 4096), else launch_gemv. The counter reads 0 before and after.

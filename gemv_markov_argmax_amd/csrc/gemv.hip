@@ -28,9 +28,13 @@
 //        K <= 4096 with rows handed out by a counter after a static run per
 //        workgroup, which balances the XCDs (dspark_lm_head_sched).
 //      - gemv_mrows_kernel: 16 < M <= 80 per launch (batched requests): a
-//        small GEMM streaming K chunks of weights and A through LDS.
+//        small GEMM streaming K chunks of weights and A through LDS; with a
+//        caller workspace (dspark_lm_head_split), K is split in two halves
+//        taken by different workgroups, whose partials the second to finish
+//        adds.
 //  * Summation order depends on the shape only (never on timing or on which
-//    workgroup took a row), so reruns are bit-identical; for M <= 16 an
+//    workgroup took a row; the split sums exactly two partials, whose order
+//    does not matter), so reruns are bit-identical; for M <= 16 an
 //    output row does not depend on the other rows, and equal weight rows
 //    give equal outputs.
 #include "dspark_internal.h"
@@ -52,6 +56,12 @@ struct GemvParams {
   const float* res;  // null, or [M, N] (row stride ldy) added to the outputs; may be Y itself
   const uint16_t* gamma;  // gemv_short_kernel with NORM: the RMSNorm weights bf16 [K]
   float eps;              // and its epsilon
+  // gemv_mrows_kernel with SPLIT: a ticket word per row block (0 between
+  // launches), the two halves' partial outputs, and the padded number of
+  // row blocks (a multiple of 8).
+  uint32_t* tick;
+  float* part;
+  int nrb;
 };
 
 // The output value of (m, n), plus the residual when there is one (read and
@@ -834,114 +844,138 @@ __global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, ui
 // Medium-M variant, 16 < M <= 80 (the batched lm_head of several requests):
 // a small GEMM. With the hi/lo split the A side has 2M rows, too many to
 // keep per wave, so the workgroup streams K in chunks through LDS: a chunk
-// holds 128 weight rows and all 2M A rows (hi parts in rows 0..M-1, lo parts
-// in rows M..2M-1), each 4 k-blocks long. Eight waves split the
-// 8 x ceil(M/8) output tiles of the workgroup 4 x 2 (32 weight rows by half
-// the A blocks), so each B fragment read from LDS feeds up to 5 MFMAs and
-// each A fragment 2, which keeps LDS traffic under its bandwidth at the HBM
-// rate and the registers of a wave under 256.
+// holds the workgroup's 64*NT weight rows and all 2M A rows (hi parts in
+// rows 0..M-1, lo parts in rows M..2M-1), each KC k-blocks long. Eight waves
+// split the 4*NT x ceil(M/8) output tiles of the workgroup 4 x 2 (16*NT
+// weight rows by half the A blocks), so each B fragment read from LDS feeds
+// up to 5 MFMAs and each A fragment NT, which keeps LDS traffic under its
+// bandwidth and the registers of a wave under 256.
 // Loads run two chunks ahead in registers (weights first, then X, in the
 // order they are consumed), and there is no global store before the end, so
 // the compiler never drains the prefetch. The output tile is assembled in
 // LDS and y = hi + lo is written row by row.
-constexpr int kMrRows = 128;                    // weight rows per workgroup
-constexpr int kMrKC = 4;                        // k-blocks per K chunk
-constexpr int kMrStride = kMrKC * 64 + 16;      // bytes per LDS row of a chunk (padded)
+// Two tiles are used: 128 rows x all of K in chunks of 4 k-blocks (NT = 2,
+// KC = 4), and, with K split in halves (SPLIT), 256 rows x half of K in
+// chunks of 2 (NT = 4, KC = 2). For a compute unit's share of the weights
+// the split reads half the activation bytes and does 2/3 of the LDS
+// traffic per weight byte (larger wave tiles); measured on MI355X at
+// [72 x 5120] x [32000 x 5120]: 81 against 94 us.
 constexpr int kMrMaxM = 80;                     // activation rows per launch
 constexpr int kMrWaves = 8;
 constexpr int kMrThreads = kMrWaves * kWave;
-constexpr int kMrBQ = kMrRows * 16 / kMrThreads;                 // weight loads per thread per chunk
-constexpr int kMrAQ = (kMrMaxM * 32 + kMrThreads - 1) / kMrThreads;  // X float4 loads per thread per chunk
+// Tile of a workgroup with NT weight tiles per wave (4 wave groups of 16*NT
+// rows) and K chunks of KC k-blocks.
+template <int NT, int KC>
+struct MrShape {
+  static constexpr int rows = 64 * NT;                              // weight rows per workgroup
+  static constexpr int stride = KC * 64 + 16;                       // bytes per LDS row of a chunk (padded)
+  static constexpr int tpr = KC * 4;                                // threads per weight row of a chunk
+  static constexpr int rpq = kMrThreads / tpr;                      // weight rows per load instruction
+  static constexpr int bq = rows / rpq;                             // weight loads per thread per chunk
+  static constexpr int aq = (kMrMaxM * KC * 8 + kMrThreads - 1) / kMrThreads;  // X float4 loads per thread
+};
 
-template <int MB2>
+template <int MB2, int NT, int KC, bool SPLIT>
 __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
+  using S = MrShape<NT, KC>;
+  // Row block and K half of this workgroup. With SPLIT, workgroup b takes
+  // half h = (b / 8) % 2 of row block 8 * (b / 16) + b % 8, so the two
+  // halves of a block are 8 apart (the same XCD when workgroups go to the
+  // XCDs in turn); blocks past the last leave at once.
+  const int rb = SPLIT ? static_cast<int>(((blockIdx.x >> 4) << 3) | (blockIdx.x & 7)) : static_cast<int>(blockIdx.x);
+  const int h = SPLIT ? static_cast<int>((blockIdx.x >> 3) & 1) : 0;
+  if (SPLIT && rb * S::rows >= p.N) return;  // uniform: before any barrier
   // 2*MB2 A blocks of 16 rows (rows past 2M are zero), MB2 per wave group,
   // then one scratch row that takes the writes of lanes past M. The two
   // chunk buffers are separate arrays, so the compiler can see that staging
   // one never touches what the MFMAs read from the other.
   constexpr int arows = 32 * MB2;
-  constexpr int bufbytes = (kMrRows + arows + 1) * kMrStride;
+  constexpr int bufbytes = (S::rows + arows + 1) * S::stride;
   __shared__ __align__(16) unsigned char lds0[bufbytes];
   __shared__ __align__(16) unsigned char lds1[bufbytes];
   const int M = p.M, N = p.N, K = p.K;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
   const int ng = w & 3, mg = w >> 2;  // 32-row weight group, A block group
   const int mb0 = mg * MB2;
-  const int n0 = blockIdx.x * kMrRows;
-  const int nrows = min(kMrRows, N - n0);
-  const int nchunks = (K + 32 * kMrKC - 1) / (32 * kMrKC);
+  const int n0 = rb * S::rows;
+  const int nrows = min(S::rows, N - n0);
+  const int nchunks_all = (K + 32 * KC - 1) / (32 * KC);
+  // SPLIT: half 0 takes the first ceil(chunks / 2) K chunks, half 1 the rest.
+  const int cbase = SPLIT && h ? (nchunks_all + 1) / 2 : 0;
+  const int nchunks = SPLIT ? (h ? nchunks_all - cbase : (nchunks_all + 1) / 2) : nchunks_all;
   const uint32_t rowb = static_cast<uint32_t>(K) * 2;
   const BufRes wres = buf_res(p.W + static_cast<size_t>(n0) * K, static_cast<uint32_t>(nrows) * rowb);
   const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
 
   // Rows of the last A block past 2M stay zero in both buffers.
-  for (int e = tid; e < (arows - 2 * M) * kMrStride / 16; e += kMrThreads) {
-    const int off = (kMrRows + 2 * M) * kMrStride + 16 * e;
+  for (int e = tid; e < (arows - 2 * M) * S::stride / 16; e += kMrThreads) {
+    const int off = (S::rows + 2 * M) * S::stride + 16 * e;
     *reinterpret_cast<u32x4*>(lds0 + off) = u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(lds1 + off) = u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Chunk c: weight piece q of thread t is row 32q + t/16, bytes 16*(t%16) of
-  // the chunk; X float4 q is f = t + 512q: row f/32, floats 4*(f%32).
+  // Chunk c: weight piece q of thread t is row rpq*q + t/tpr, bytes
+  // 16*(t%tpr) of the chunk; X float4 q is f = t + 512q: row f/(8 KC),
+  // floats 4*(f%(8 KC)).
   // Anything past N, K, M or the last chunk reads zeros.
-  const int brow = tid >> 4, bpc = tid & 15;
-  u32x4 bq[3][kMrBQ];   // weights of chunk j: set j%3
-  float4 aq[2][kMrAQ];  // X of chunk j: set j%2 (from L2, so one chunk less ahead)
-  // Workgroup b walks the K chunks starting at chunk (b / 8) % nchunks:
-  // workgroups go to the 8 XCDs in turn, so those of one XCD start at
-  // different chunks and read X from different lines of its L2 at any one
-  // time. (Step c of the walk is chunk rot(c); past the last step, out of
+  const int brow = tid / S::tpr, bpc = tid % S::tpr;
+  u32x4 bq[3][S::bq];   // weights of chunk j: set j%3
+  float4 aq[2][S::aq];  // X of chunk j: set j%2 (from L2, so one chunk less ahead)
+  // Workgroup b walks its K chunks starting at chunk (b / 8) % nchunks
+  // (b / 16 with SPLIT): workgroups go to the 8 XCDs in turn, so those of
+  // one XCD start at different chunks and read X from different lines of its
+  // L2 at any one time. (Step c of the walk is chunk rot(c); past the last step, out of
   // range.)
-  const int r0 = static_cast<int>((blockIdx.x >> 3) % static_cast<unsigned>(nchunks));
+  const int r0 = nchunks > 0 ? static_cast<int>((blockIdx.x >> (SPLIT ? 4 : 3)) % static_cast<unsigned>(nchunks)) : 0;
   auto rot = [&](int c) { return c >= nchunks ? nchunks : (c + r0 >= nchunks ? c + r0 - nchunks : c + r0); };
   auto issue_b = [&](int set, int cs) {
     const int c = rot(cs);
-    const int kb = 32 * kMrKC * c + 8 * bpc;
+    const int kb = 32 * KC * (cbase + c) + 8 * bpc;
 #pragma unroll
-    for (int q = 0; q < kMrBQ; ++q) {
+    for (int q = 0; q < S::bq; ++q) {
       const uint32_t off = c < nchunks && kb < K
-                               ? static_cast<uint32_t>(32 * q + brow) * rowb + static_cast<uint32_t>(kb) * 2
+                               ? static_cast<uint32_t>(S::rpq * q + brow) * rowb + static_cast<uint32_t>(kb) * 2
                                : kBufOutOfRange;
       bq[set][q] = buf_load16_nt(wres, off);
     }
   };
   auto issue_a = [&](int set, int cs) {
     const int c = rot(cs);
-    const int kc = 32 * kMrKC * c;
+    const int kc = 32 * KC * (cbase + c);
 #pragma unroll
-    for (int q = 0; q < kMrAQ; ++q) {
-      const int f = tid + kMrThreads * q, m = f >> 5, k = kc + 4 * (f & 31);
+    for (int q = 0; q < S::aq; ++q) {
+      const int f = tid + kMrThreads * q, m = f / (8 * KC), k = kc + 4 * (f % (8 * KC));
       const uint32_t off =
           c < nchunks && m < M && k < K ? static_cast<uint32_t>(m * K + k) * 4 : kBufOutOfRange;
       aq[set][q] = buf_load_f32x4(xres, off);
     }
   };
-  // Part `part` (of kMrKC) of moving register set -> LDS buffer b; X is
+  // Part `part` (of KC) of moving register set -> LDS buffer b; X is
   // split into its bf16 hi and lo rows.
   auto stage_part = [&](int bset, int aset, int b, int part) {
     unsigned char* Bs = b ? lds1 : lds0;
-    unsigned char* As = Bs + kMrRows * kMrStride;
+    unsigned char* As = Bs + S::rows * S::stride;
 #pragma unroll
-    for (int q = 0; q < kMrBQ; ++q)
-      if (q % kMrKC == part) *reinterpret_cast<u32x4*>(Bs + (32 * q + brow) * kMrStride + 16 * bpc) = bq[bset][q];
+    for (int q = 0; q < S::bq; ++q)
+      if (q % KC == part) *reinterpret_cast<u32x4*>(Bs + (S::rpq * q + brow) * S::stride + 16 * bpc) = bq[bset][q];
 #pragma unroll
-    for (int q = 0; q < kMrAQ; ++q) {
-      if (q % kMrKC != part) continue;
-      const int f = tid + kMrThreads * q, m = f >> 5, col = f & 31;
+    for (int q = 0; q < S::aq; ++q) {
+      if (q % KC != part) continue;
+      const int f = tid + kMrThreads * q, m = f / (8 * KC), col = f % (8 * KC);
       const float4 x = aq[aset][q];
       const uint2 s0 = split_bf16x2(x.x, x.y), s1 = split_bf16x2(x.z, x.w);
       const int rh = m < M ? m : arows, rl = m < M ? M + m : arows;  // no branch: scratch row
-      *reinterpret_cast<uint2*>(As + rh * kMrStride + 8 * col) = uint2{s0.x, s1.x};
-      *reinterpret_cast<uint2*>(As + rl * kMrStride + 8 * col) = uint2{s0.y, s1.y};
+      *reinterpret_cast<uint2*>(As + rh * S::stride + 8 * col) = uint2{s0.x, s1.x};
+      *reinterpret_cast<uint2*>(As + rl * S::stride + 8 * col) = uint2{s0.y, s1.y};
     }
   };
   auto stage = [&](int bset, int aset, int b) {
 #pragma unroll
-    for (int part = 0; part < kMrKC; ++part) stage_part(bset, aset, b, part);
+    for (int part = 0; part < KC; ++part) stage_part(bset, aset, b, part);
   };
-  f32x4 acc[2][MB2];
+  f32x4 acc[NT][MB2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int mb = 0; mb < MB2; ++mb) acc[nt][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Computes the chunk in buffer b; part kb of staging register sets
@@ -949,19 +983,19 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   // conversions and LDS writes sit between the MFMAs in program order.
   auto compute_stage = [&](int b, int bset, int aset) {
     const unsigned char* base = b ? lds1 : lds0;
-    const unsigned char* Bs = base + (32 * ng + i) * kMrStride + 16 * g;
-    const unsigned char* As = base + (kMrRows + 16 * mb0 + i) * kMrStride + 16 * g;
+    const unsigned char* Bs = base + (16 * NT * ng + i) * S::stride + 16 * g;
+    const unsigned char* As = base + (S::rows + 16 * mb0 + i) * S::stride + 16 * g;
 #pragma unroll
-    for (int kb = 0; kb < kMrKC; ++kb) {
-      u32x4 bf[2], af[MB2];
+    for (int kb = 0; kb < KC; ++kb) {
+      u32x4 bf[NT], af[MB2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) bf[nt] = *reinterpret_cast<const u32x4*>(Bs + 16 * nt * kMrStride + 64 * kb);
+      for (int nt = 0; nt < NT; ++nt) bf[nt] = *reinterpret_cast<const u32x4*>(Bs + 16 * nt * S::stride + 64 * kb);
 #pragma unroll
-      for (int mb = 0; mb < MB2; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(As + 16 * mb * kMrStride + 64 * kb);
+      for (int mb = 0; mb < MB2; ++mb) af[mb] = *reinterpret_cast<const u32x4*>(As + 16 * mb * S::stride + 64 * kb);
 #pragma unroll
       for (int mb = 0; mb < MB2; ++mb)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][mb] = mfma_16x16x32(af[mb], bf[nt], acc[nt][mb]);
+        for (int nt = 0; nt < NT; ++nt) acc[nt][mb] = mfma_16x16x32(af[mb], bf[nt], acc[nt][mb]);
       stage_part(bset, aset, 1 - b, kb);
     }
   };
@@ -1012,26 +1046,87 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   if (rest > 4) { DSPARK_MR_STEP(4) }
 #undef DSPARK_MR_STEP
 
-  // Output tile [2M x 128] through LDS in two halves of 64 columns (one
-  // half fits in a chunk buffer), then y[m] = hi row m + lo row M+m.
+  // Output tile [2M x rows] through LDS in pieces of 64 columns (one piece
+  // fits in a chunk buffer), then y[m] = hi row m + lo row M+m. Tile nt of
+  // wave group ng covers workgroup rows 16*(NT*ng + nt) .. + 15.
+  // SPLIT: y is this half's partial. Each half stores it (agent-scope
+  // stores, which other XCDs see once they complete), waits until they have
+  // completed, and then takes a ticket from its row block's word; the half
+  // that draws 1 finishes second, so the other's partial is complete: it
+  // reads both partials back (agent-scope loads, all in flight at once),
+  // writes Y = P0 + P1 and puts the word back to 0. A sum of two terms does
+  // not depend on their order, and Y does not depend on which half finished
+  // first.
   float* L = reinterpret_cast<float*>(lds0);  // [arows][64]
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if ((ng >> 1) == half)
+  for (int piece = 0; piece < NT; ++piece) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = 16 * (NT * ng + nt);
+      if ((r >> 6) == piece)
 #pragma unroll
         for (int mb = 0; mb < MB2; ++mb)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            L[(16 * (mb0 + mb) + 4 * g + v) * 64 + 32 * (ng & 1) + 16 * nt + i] = acc[nt][mb][v];
-    __syncthreads();
-    for (int e = tid; e < M * 64; e += kMrThreads) {
-      const int m = e >> 6, col = 64 * half + (e & 63);
-      const size_t idx = static_cast<size_t>(m) * p.ldy + n0 + col;
-      if (col < nrows) p.Y[idx] = with_res(p, idx, L[m * 64 + (e & 63)] + L[(M + m) * 64 + (e & 63)]);
+          for (int v = 0; v < 4; ++v) L[(16 * (mb0 + mb) + 4 * g + v) * 64 + (r & 63) + i] = acc[nt][mb][v];
     }
     __syncthreads();
+    if constexpr (SPLIT) {
+      const BufRes pres = buf_res(p.part + (static_cast<size_t>(h * p.nrb + rb) * M) * S::rows,
+                                  static_cast<uint32_t>(M) * S::rows * 4);
+      for (int f = tid; f < M * 16; f += kMrThreads) {
+        const int m = f >> 4, c = 4 * (f & 15);
+        const float4 hi = *reinterpret_cast<const float4*>(L + m * 64 + c);
+        const float4 lo = *reinterpret_cast<const float4*>(L + (M + m) * 64 + c);
+        buf_store16_coherent(pres, static_cast<uint32_t>(m * S::rows + 64 * piece + c) * 4,
+                             __builtin_bit_cast(u32x4, float4{hi.x + lo.x, hi.y + lo.y, hi.z + lo.z, hi.w + lo.w}));
+      }
+      if (piece + 1 == NT) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every store of the partial has completed
+      }
+    } else {
+      for (int e = tid; e < M * 64; e += kMrThreads) {
+        const int m = e >> 6, col = 64 * piece + (e & 63);
+        const size_t idx = static_cast<size_t>(m) * p.ldy + n0 + col;
+        if (col < nrows) p.Y[idx] = with_res(p, idx, L[m * 64 + (e & 63)] + L[(M + m) * 64 + (e & 63)]);
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (SPLIT) {
+    __shared__ uint32_t ticket;
+    if (tid == 0) ticket = __hip_atomic_fetch_add(p.tick + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket == 0) return;  // uniform: the other half finishes the block
+    if (tid == 0) __hip_atomic_store(p.tick + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t pbytes = static_cast<uint32_t>(M) * S::rows * 4;
+    const BufRes r0 = buf_res(p.part + (static_cast<size_t>(rb) * M) * S::rows, pbytes);
+    const BufRes r1 = buf_res(p.part + (static_cast<size_t>(p.nrb + rb) * M) * S::rows, pbytes);
+    // Float4 q = tid + 512 j of each partial, in rounds of kQ per thread
+    // (past the partial: zeros, never used).
+    constexpr int kQ = (kMrMaxM * S::rows / 4 + 2 * kMrThreads - 1) / (2 * kMrThreads);
+    const int nq = M * (S::rows / 4);
+    for (int j0 = 0; j0 * kMrThreads < nq; j0 += kQ) {
+      u32x4 a[kQ], b[kQ];
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        a[j] = buf_load16_coherent(r0, static_cast<uint32_t>(tid + kMrThreads * (j0 + j)) * 16);
+        b[j] = buf_load16_coherent(r1, static_cast<uint32_t>(tid + kMrThreads * (j0 + j)) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        const int q = tid + kMrThreads * (j0 + j);
+        if (q >= nq) break;
+        const int m = q / (S::rows / 4), c = 4 * (q % (S::rows / 4));
+        const float4 x = __builtin_bit_cast(float4, a[j]), z = __builtin_bit_cast(float4, b[j]);
+        const float y[4] = {x.x + z.x, x.y + z.y, x.z + z.z, x.w + z.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const size_t idx = static_cast<size_t>(m) * p.ldy + n0 + c + v;
+          if (c + v < nrows) p.Y[idx] = with_res(p, idx, y[v]);
+        }
+      }
+    }
   }
 }
 
@@ -1158,15 +1253,69 @@ hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-template <int MB2>
+template <int MB2, int NT = 2, int KC = 4, bool SPLIT = false>
 hipError_t launch_mrows(const GemvParams& prm, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_mrows_kernel<MB2>);  // static LDS only
+  const void* fn = reinterpret_cast<const void*>(&gemv_mrows_kernel<MB2, NT, KC, SPLIT>);  // static LDS only
   GemvParams a = prm;
   void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3((prm.N + kMrRows - 1) / kMrRows), dim3(kMrThreads), args, 0, st);
+  const int grid = SPLIT ? 2 * prm.nrb : (prm.N + MrShape<NT, KC>::rows - 1) / MrShape<NT, KC>::rows;
+  return hipLaunchKernel(fn, dim3(grid), dim3(kMrThreads), args, 0, st);
+}
+
+// Split-K launches (16 < M): ticket words, then the two halves' partials,
+// each [nrb][kMrMaxM][256] fp32.
+constexpr int kSplitRows = MrShape<4, 2>::rows;
+int split_row_blocks(int N) { return ((N + kSplitRows - 1) / kSplitRows + 7) / 8 * 8; }
+size_t split_tick_bytes(int N) { return (static_cast<size_t>(split_row_blocks(N)) * 4 + 255) / 256 * 256; }
+
+template <int MB2>
+hipError_t launch_mrows_split(const GemvParams& prm, hipStream_t st) {
+  return launch_mrows<MB2, 4, 2, true>(prm, st);
 }
 
 }  // namespace
+
+size_t gemv_split_workspace_bytes(int N, int K, int M) {
+  if (!gemv_split_fits(N, K, M)) return 0;
+  return split_tick_bytes(N) + static_cast<size_t>(2) * split_row_blocks(N) * kMrMaxM * kSplitRows * 4;
+}
+
+bool gemv_split_fits(int N, int K, int M) {
+  // A workgroup's weight range (256 rows of K) must stay below 2^31 bytes.
+  return N >= 1 && M > 16 && K >= 1 && K <= (1 << 21);
+}
+
+hipError_t launch_gemv_split(const uint16_t* W, int N, int K, const float* X, int M, float* Y, void* workspace,
+                             hipStream_t stream, const float* res) {
+  if (!gemv_split_fits(N, K, M) || !workspace) return launch_gemv(W, N, K, X, M, Y, stream, res);
+  GemvParams prm{};
+  prm.W = W;
+  prm.N = N;
+  prm.K = K;
+  prm.ldy = N;
+  prm.nrb = split_row_blocks(N);
+  prm.tick = static_cast<uint32_t*>(workspace);
+  prm.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + split_tick_bytes(N));
+  // Balanced parts of at most kMrMaxM rows, one after the other on the
+  // stream: each leaves the ticket words at 0 for the next.
+  const int parts = (M + kMrMaxM - 1) / kMrMaxM;
+  for (int part = 0; part < parts; ++part) {
+    const int m0 = M * part / parts, mc = M * (part + 1) / parts - m0;
+    prm.X = X + static_cast<size_t>(m0) * K;
+    prm.Y = Y + static_cast<size_t>(m0) * N;
+    prm.res = res ? res + static_cast<size_t>(m0) * N : nullptr;
+    prm.M = mc;
+    hipError_t e;
+    switch (((mc + 7) / 8 + 1) / 2) {
+      case 2: e = launch_mrows_split<2>(prm, stream); break;
+      case 3: e = launch_mrows_split<3>(prm, stream); break;
+      case 4: e = launch_mrows_split<4>(prm, stream); break;
+      default: e = launch_mrows_split<5>(prm, stream); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 bool gemv_shape_fits(int N, int K, int M) {
   if (K > (1 << 22)) return false;  // X of a launch part: <= 80 rows * K * 4 bytes; W: 128 rows * 2K

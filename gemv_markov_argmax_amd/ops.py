@@ -25,6 +25,9 @@ SIGNATURES = {
     "dspark_proj_smallm": (_i, [_p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head": (_i, [_p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head_sched": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
+    "dspark_lm_head_split_workspace_bytes": (_sz, [_i, _i, _i]),
+    "dspark_lm_head_split": (_i, [_p, _i, _i, _p, _i, _p, _p, _sz, _p]),
+    "dspark_draft_round_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_proj_smallm_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_markov_sample_q8": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
@@ -176,6 +179,43 @@ def lm_head_sched(W_lm: torch.Tensor, H: torch.Tensor, counter: torch.Tensor, ou
         raise ValueError("out must be [rows, V]")
     _check(lib().dspark_lm_head_sched(W_lm.data_ptr(), V, d, H.data_ptr(), rows, out.data_ptr(),
                                       counter.data_ptr() + counter_offset, _stream(W_lm)))
+    return out
+
+
+def lm_head_split_workspace_bytes(V: int, d: int, rows: int) -> int:
+    return int(lib().dspark_lm_head_split_workspace_bytes(V, d, rows))
+
+
+def lm_head_split_workspace(V: int, d: int, rows: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace for dspark_lm_head_split (None where the split
+    does not apply); reusable by calls of the same or smaller sizes."""
+    n = lm_head_split_workspace_bytes(V, d, rows)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def lm_head_split(W_lm: torch.Tensor, H: torch.Tensor, workspace: torch.Tensor | None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Base logits [rows, V] = H @ W_lm^T with d split in two halves taken by
+    different workgroups (dspark_lm_head_split). ``workspace``: uint8 device
+    memory of lm_head_split_workspace_bytes(V, d, rows), zero-filled once
+    (None where that is 0)."""
+    _dev(W_lm, torch.bfloat16, "W_lm", 2)
+    _dev(H, torch.float32, "H", 2)
+    V, d = W_lm.shape
+    rows = H.shape[0]
+    if H.shape[1] != d:
+        raise ValueError(f"H has {H.shape[1]} columns, W_lm has {d}")
+    if out is None:
+        out = torch.empty((rows, V), dtype=torch.float32, device=W_lm.device)
+    _dev(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (rows, V):
+        raise ValueError("out must be [rows, V]")
+    wp, wn = None, 0
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace", 1)
+        wp, wn = workspace.data_ptr(), workspace.numel()
+    _check(lib().dspark_lm_head_split(W_lm.data_ptr(), V, d, H.data_ptr(), rows, out.data_ptr(), wp, wn,
+                                      _stream(W_lm)))
     return out
 
 
@@ -428,6 +468,19 @@ def markov_workspace(num_reqs: int, k: int, V: int, device) -> torch.Tensor:
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
+def draft_round_workspace_bytes(num_reqs: int, B: int, k: int, V: int, d: int) -> int:
+    return int(lib().dspark_draft_round_workspace_bytes(num_reqs, B, k, V, d))
+
+
+def draft_round_workspace(num_reqs: int, B: int, k: int, V: int, d: int, device) -> torch.Tensor:
+    """A zero-filled workspace for dspark_draft_round: the Markov loop's, then
+    (num_reqs * B > 16) the split lm_head's."""
+    n = draft_round_workspace_bytes(num_reqs, B, k, V, d)
+    if n == 0:
+        raise ValueError("sizes out of range for the draft round")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
 def stream_read(buf: torch.Tensor, groups: int, threads: int, sink: torch.Tensor | None = None,
                 nbytes: int | None = None) -> torch.Tensor:
     """Streaming read of a device tensor's bytes (dspark_stream_read, a
@@ -624,7 +677,7 @@ def draft_round(W_lm: torch.Tensor, H: torch.Tensor, w1: torch.Tensor, w2: torch
     else:
         logit_out = pass_out = None
     if workspace is None:
-        workspace = markov_workspace(R, k, V, dev)
+        workspace = draft_round_workspace(R, B, k, V, d, dev)
     _dev(workspace, torch.uint8, "workspace", 1)
     _check(lib().dspark_draft_round(W_lm.data_ptr(), V, d, H.data_ptr(), R, B, w1.data_ptr(), w2.data_ptr(), r,
                                     d2t_ptr, prev0.data_ptr(), k, pw_ptr, float(probe_bias), float(probe_threshold),

@@ -139,6 +139,43 @@ dspark_status dspark_lm_head_sched(const uint16_t* W_lm, int V, int d, const flo
                                    float* logits, uint32_t* counter, void* stream);
 
 /*
+ * dspark_lm_head_split -- dspark_lm_head for batched drafted rows
+ * (rows > 16: several requests per round), with the hidden dimension split
+ * into two halves that different workgroups multiply.
+ *
+ * [W7] "Measured": the reduced-vocabulary lane drafts 9 rows for each of
+ * several requests, so its lm_head multiplies dozens of hidden rows by the
+ * vocabulary; [SI441] "Hypothesis": such small-M products are bound by
+ * reading the weights once. With all of its rows' activations beside each
+ * weight tile, a compute unit reads about as many activation bytes as
+ * weight bytes; splitting d in two halves the activation bytes per unit.
+ *
+ * Same product, arguments, sizes, errors and accuracy as dspark_lm_head.
+ * Each logit is the sum of two fp32 partials, one per part of d (the first
+ * ceil(ceil(d / 64) / 2) blocks of 64 entries, and the rest), each partial
+ * summed in an order fixed by the shape; a sum of two terms does not depend
+ * on which partial came first, so the result does not depend on timing.
+ * (The logits differ from dspark_lm_head's by rounding only.)
+ *
+ *   workspace device memory of at least
+ *             dspark_lm_head_split_workspace_bytes(V, d, rows) bytes,
+ *             256-byte aligned, caller-owned: a ticket word per block of
+ *             256 vocabulary rows, then the two halves' partial logits.
+ *             ZERO-FILL IT ONCE before its first use; every call leaves
+ *             the ticket words 0 again, so calls need no clearing between
+ *             them. Calls that share a workspace must be ordered on one
+ *             stream.
+ * dspark_lm_head_split_workspace_bytes returns 0 where the split does not
+ * apply (rows <= 16, or d > 2^21); the call then runs dspark_lm_head's
+ * kernels and does not touch the workspace (which may be NULL).
+ * Errors: those of dspark_lm_head; DSPARK_ERR_WORKSPACE for a missing or
+ * smaller workspace, DSPARK_ERR_ALIGN for a misaligned one.
+ */
+size_t dspark_lm_head_split_workspace_bytes(int V, int d, int rows);
+dspark_status dspark_lm_head_split(const uint16_t* W_lm, int V, int d, const float* H, int rows,
+                                   float* logits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dspark_proj_smallm_q8, dspark_lm_head_q8 -- the same products over Q8_0
  * weights.
  *
@@ -329,11 +366,13 @@ dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B,
  *
  * Equivalent to, in this order on `stream`,
  *   dspark_lm_head_sched(W_lm, V, d, H, num_reqs * B, base_out, <counter>)
+ *     (dspark_lm_head_split(..., <split workspace>) when num_reqs * B > 16)
  *   dspark_markov_sample(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, ...)
  *   dspark_conf_probe(H, num_reqs * B, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out)
  * and bit-identical to those three calls, <counter> being the uint32 at
  * byte 64 of the workspace (a control word the loop does not otherwise
- * use). The probe runs inside the Markov loop's launch (as in
+ * use) and <split workspace> the bytes of the workspace past the first
+ * dspark_markov_workspace_bytes(num_reqs, k, V). The probe runs inside the Markov loop's launch (as in
  * dspark_markov_sample_probe), so the round is two kernels instead of three.
  * A zero-filled workspace keeps that word 0 across rounds. If it is not 0
  * when the loop starts (a workspace that was never zero-filled), the
@@ -350,11 +389,15 @@ dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B,
  *   ids_out   int64 [num_reqs, k]          overwritten
  *   logit_out fp32  [num_reqs * B]         overwritten (required when probe_w is given)
  *   pass_out  int32 [num_reqs * B] or NULL
- *   workspace as for dspark_markov_sample (zero-filled once before first use;
- *             the same contract)
+ *   workspace at least dspark_draft_round_workspace_bytes(num_reqs, B, k, V, d)
+ *             bytes, 256-byte aligned: the Markov loop's workspace, then
+ *             (num_reqs * B > 16) the split lm_head's. Zero-filled once
+ *             before first use; the contracts of dspark_markov_sample and
+ *             dspark_lm_head_split.
  * Sizes and errors: those of the three calls above; every check is made
  * before anything is enqueued.
  */
+size_t dspark_draft_round_workspace_bytes(int num_reqs, int B, int k, int V, int d);
 dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float* H, int num_reqs,
                                  int B, const uint16_t* w1, const uint16_t* w2, int r,
                                  const int64_t* d2t, const int64_t* prev0, int k,

@@ -29,7 +29,9 @@ def declared():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_lm_head_sched", "dspark_markov_sample", "dspark_conf_probe",
+    for n in ["dspark_proj_smallm", "dspark_lm_head", "dspark_lm_head_sched", "dspark_lm_head_split",
+              "dspark_lm_head_split_workspace_bytes", "dspark_draft_round_workspace_bytes",
+              "dspark_markov_sample", "dspark_conf_probe",
               "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
               "dspark_markov_sample_q8", "dspark_draft_round_q8", "dspark_rmsnorm", "dspark_silu_gate",
               "dspark_proj_smallm_add", "dspark_proj_smallm_norm", "dspark_proj_smallm_norm_fits",
@@ -63,6 +65,42 @@ def test_lm_head_sched_errors(L):
     assert f(A, 16, 12, A, 7, A2, A, None) == ERR_SHAPE        # d % 8 != 0
     assert f(A, 16, 64, A, 7, A2, A + 2, None) == ERR_ALIGN    # misaligned counter
     assert f(A, 16, 64, MIS, 7, A2, A, None) == ERR_ALIGN
+
+
+def test_lm_head_split_workspace_bytes(L):
+    f = L.dspark_lm_head_split_workspace_bytes
+    assert f(0, 64, 72) == 0 and f(100, 0, 72) == 0 and f(100, 64, 0) == 0
+    assert f(32000, 5120, 16) == 0                      # 16 rows or fewer: no split
+    assert f(32000, (1 << 21) + 8, 72) == 0             # a 256-row K half past the 32-bit buffer range
+    n = f(32000, 5120, 72)
+    # ticket words for 128 blocks of 256 rows (125 padded to a multiple of 8),
+    # then two partials of 80 rows x 256 columns per block
+    assert n == 512 + 2 * 128 * 80 * 256 * 4
+    assert f(32000, 5120, 17) == f(32000, 5120, 80) == f(32000, 5120, 500) == n  # parts of <= 80 rows reuse it
+    assert f(1, 8, 17) == 256 + 2 * 8 * 80 * 256 * 4
+
+
+def test_lm_head_split_errors(L):
+    f = L.dspark_lm_head_split
+    n = L.dspark_lm_head_split_workspace_bytes(3000, 64, 72)
+    assert f(None, 3000, 64, A, 72, A2, A, n, None) == ERR_NULL
+    assert f(A, 3000, 64, None, 72, A2, A, n, None) == ERR_NULL
+    assert f(A, 3000, 12, A, 72, A2, A, n, None) == ERR_SHAPE      # d % 8 != 0
+    assert f(A, 3000, 64, A, 0, A2, A, n, None) == ERR_SHAPE
+    assert f(A, 3000, 64, MIS, 72, A2, A, n, None) == ERR_ALIGN
+    assert f(A, 3000, 64, A, 72, A2, None, n, None) == ERR_WORKSPACE
+    assert f(A, 3000, 64, A, 72, A2, A, n - 1, None) == ERR_WORKSPACE
+    assert f(A, 3000, 64, A, 72, A2, A + 16, n, None) == ERR_ALIGN  # the workspace is 256-byte aligned
+
+
+def test_draft_round_workspace_bytes(L):
+    f = L.dspark_draft_round_workspace_bytes
+    mk = L.dspark_markov_workspace_bytes(8, 9, 32000)
+    assert f(1, 7, 7, 151936, 4096) == L.dspark_markov_workspace_bytes(1, 7, 151936)  # 7 rows: no split
+    at = (mk + 255) // 256 * 256
+    assert f(8, 9, 9, 32000, 5120) == at + L.dspark_lm_head_split_workspace_bytes(32000, 5120, 72)
+    assert f(0, 9, 9, 32000, 5120) == 0 and f(8, 0, 9, 32000, 5120) == 0 and f(8, 9, 33, 32000, 5120) == 0
+    assert f(8, 9, 9, 32000, 0) == 0
 
 
 def test_gemv_errors(L):
@@ -291,6 +329,13 @@ def test_draft_round_errors(L):
     assert call(ps=A + 2) == ERR_ALIGN
     assert call(ws=None) == ERR_WORKSPACE
     assert call(wsb=ws - 1) == ERR_WORKSPACE
+    # 8 requests x 9 rows: the round's lm_head splits K, so the workspace
+    # holds the loop's and the split's
+    big = L.dspark_draft_round_workspace_bytes(8, 9, 9, 32000, 5120)
+    batched = dict(V=32000, d=5120, R=8, B=9, k=9, wsb=big)
+    assert call(**dict(batched, wsb=L.dspark_markov_workspace_bytes(8, 9, 32000))) == ERR_WORKSPACE
+    assert call(**dict(batched, wsb=big - 1)) == ERR_WORKSPACE
+    assert call(**dict(batched, ws=A + 64)) == ERR_ALIGN
 
 
 def test_block_errors(L):

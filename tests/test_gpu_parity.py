@@ -95,6 +95,79 @@ def test_gemv_medium_m_matches_oracle(dev, M, N, K):
     assert torch.equal(r, r0 + y), "residual not added to the same outputs"
 
 
+SPLIT_CASES = [
+    # (M, N, K) with M > 16: every count of A blocks, ragged N (past a
+    # multiple of 256, one row, fewer rows than a block), K of one 64-wide
+    # chunk (the second half empty), an odd number of chunks, K tails
+    # (K % 64 != 0), several launches of at most 80 rows
+    (17, 300, 136), (24, 1000 + 5, 776), (25, 129, 8), (32, 515, 1032), (41, 257, 5120),
+    (49, 1000, 1544), (56, 1, 64), (64, 1001, 264), (65, 3000, 1032), (72, 4000 + 3, 5120),
+    (73, 515, 200), (80, 1027, 2056), (81, 700, 1000), (160, 513, 320),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_CASES)
+def test_lm_head_split_matches_oracle(dev, M, N, K):
+    """dspark_lm_head_split (K in two halves, the second finisher adds):
+    every output within the tolerance of the oracle; reruns bit-identical;
+    every ticket word 0 after each call; a workspace sized for a larger
+    shape serves a smaller one; and the outputs equal dspark_lm_head's up to
+    rounding."""
+    seed = 7500 + M * 31 + N + K
+    say(f"[lm_head split] M={M} N={N} K={K} seed={seed}")
+    W, X = synth.gemv_inputs(M, N, K, seed)
+    ops = _ops()
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    n = ops.lm_head_split_workspace_bytes(N, K, M)
+    assert n > 0
+    ws = torch.zeros(ops.lm_head_split_workspace_bytes(N + 1000, K, M) + 4096, dtype=torch.uint8, device=dev)
+    y = ops.lm_head_split(Wd, Xd, ws)
+    torch.cuda.synchronize()
+    ticks = (((N + 255) // 256 + 7) // 8) * 8
+    assert int(ws[: 4 * ticks].count_nonzero().item()) == 0, "a ticket word was left set"
+    y2 = ops.lm_head_split(Wd, Xd, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "rerun differs"
+    ref = oracle.gemv(W, X)
+    logits_close(y.cpu().numpy(), ref, f"lm_head_split M={M} N={N} K={K}")
+    one = ops.lm_head(Wd, Xd)
+    torch.cuda.synchronize()
+    assert torch.allclose(y, one, rtol=1e-5, atol=1e-5)
+
+
+def test_lm_head_split_full_size_and_graph(dev):
+    """The batched lane's lm_head [72 x 5120] x [32000 x 5120] through the
+    split, sampled rows against the oracle; the same call recorded in a HIP
+    graph and replayed (eager work between replays) gives the same bits."""
+    M, N, K, seed = 72, 32000, 5120, 7641
+    say(f"[lm_head split full] M={M} N={N} K={K} seed={seed}")
+    W, X = synth.gemv_inputs(M, N, K, seed)
+    ops = _ops()
+    Wd, Xd = _bf(W, dev), _up(X, dev)
+    ws = ops.lm_head_split_workspace(N, K, M, dev)
+    out = torch.empty(M, N, device=dev)
+    ops.lm_head_split(Wd, Xd, ws, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    rows = np.random.default_rng(seed).choice(N, 512, replace=False)
+    logits_close(eager.cpu().numpy()[:, rows], oracle.gemv(W[rows], X), "lm_head_split full sampled")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ops.lm_head_split(Wd, Xd, ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.lm_head_split(Wd, Xd, ws, out=out)
+    for rep in range(3):
+        out.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        _ = ops.lm_head(Wd, Xd[:20])  # eager work between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name", ["draft_layer"])
 def test_draft_layer_projections(dev, name):
     inp = synth.layer_inputs()
@@ -608,11 +681,17 @@ def _round_tensors(name, dev):
 
 
 def _run_round(inp, t, logits=None, ids=None, ws=None, lg=None, ps=None):
-    """The round as separate calls, with the lm_head scheduled like the
-    round's own (dspark_lm_head_sched) on a counter of its own."""
+    """The round as separate calls, with the lm_head run like the round's
+    own: scheduled (dspark_lm_head_sched) on a counter of its own, or, for
+    more than 16 rows, split (dspark_lm_head_split) in a workspace of its
+    own."""
     ops = _ops()
     R, B, V = inp["num_reqs"], inp["B"], inp["V"]
-    logits = ops.lm_head_sched(t["W"], t["H"], ops.lm_head_counter(t["H"].device), out=logits)
+    if R * B > 16:
+        split_ws = ops.lm_head_split_workspace(V, t["W"].shape[1], R * B, t["H"].device)
+        logits = ops.lm_head_split(t["W"], t["H"], split_ws, out=logits)
+    else:
+        logits = ops.lm_head_sched(t["W"], t["H"], ops.lm_head_counter(t["H"].device), out=logits)
     ids = ops.markov_sample(logits.view(R, B, V), t["w1"], t["w2"], t["prev0"], inp["k"], out=ids, workspace=ws)
     lg, ps = ops.conf_probe(t["H"], t["pw"], float(inp["probe_bias"]), float(inp["probe_threshold"]),
                             logit_out=lg, pass_out=ps)
@@ -788,7 +867,7 @@ def test_draft_round_graph_replay(dev):
     ops = _ops()
     bufs = dict(base_out=torch.empty(R, B, V, device=dev), ids_out=torch.empty(R, k, dtype=torch.int64, device=dev),
                 logit_out=torch.empty(R * B, device=dev), pass_out=torch.empty(R * B, dtype=torch.int32, device=dev),
-                workspace=ops.markov_workspace(R, k, V, dev))
+                workspace=ops.draft_round_workspace(R, B, k, V, t["W"].shape[1], dev))
 
     def run():
         return ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, probe_w=t["pw"], **bufs)
@@ -1247,7 +1326,7 @@ def test_draft_forward_graph_replay(dev):
     ids = torch.empty(R, B, dtype=torch.int64, device=dev)
     lg = torch.empty(R * B, device=dev)
     ps = torch.empty(R * B, dtype=torch.int32, device=dev)
-    mws = ops.markov_workspace(R, B, V, dev)
+    mws = ops.draft_round_workspace(R, B, B, V, H * Dh, dev)
 
     def run():
         ops.draft_forward(x_in, fc, layers, kcs, vcs, R, B, H, Dh, ln, norm, float(inp["eps"]), scratch=scratch,
