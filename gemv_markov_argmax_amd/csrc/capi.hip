@@ -269,12 +269,14 @@ dspark_status dspark_draft_round(const uint16_t* W_lm, int V, int d, const float
   if (split > 0 && !aligned(workspace, 256)) return DSPARK_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      split > 0 ? dspark::launch_gemv_split(W_lm, V, d, H, rows, base_out, static_cast<unsigned char*>(workspace) + split_at, s)
+      split > 0 ? dspark::launch_gemv_split(W_lm, V, d, H, rows, base_out, static_cast<unsigned char*>(workspace) + split_at,
+                                            s, nullptr, dspark::markov_lm_counter(workspace))
                 : dspark::launch_gemv_sched(W_lm, V, d, H, rows, base_out, dspark::markov_lm_counter(workspace), s);
   if (e != hipSuccess) return DSPARK_ERR_HIP;
   const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
+  uint32_t* ticks = split > 0 ? reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + split_at) : nullptr;
   return from_hip(dspark::launch_markov(base_out, num_reqs, B, V, w1, w2, r, d2t, prev0, k, ids_out, workspace,
-                                        probe_w ? &pa : nullptr, s));
+                                        probe_w ? &pa : nullptr, s, ticks, split > 0 ? dspark::gemv_split_tick_words(V) : 0));
 }
 
 dspark_status dspark_markov_sample_q8(const float* base, int num_reqs, int B, int V, const int8_t* w1q,

@@ -269,11 +269,13 @@ hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, f
 // partials added in a caller workspace of gemv_split_workspace_bytes(N, K,
 // M) bytes (256-byte aligned, zero-filled once; every launch leaves its
 // ticket words 0). Shapes outside gemv_split_fits, or a null workspace, run
-// launch_gemv.
+// launch_gemv. `dirty`, when given, is set to 1 if a ticket word was found
+// not 0 (the outputs of that launch may then be wrong).
 bool gemv_split_fits(int N, int K, int M);
 size_t gemv_split_workspace_bytes(int N, int K, int M);
+int gemv_split_tick_words(int N);  // ticket words at the start of that workspace
 hipError_t launch_gemv_split(const uint16_t* W, int N, int K, const float* X, int M, float* Y, void* workspace,
-                             hipStream_t stream, const float* res = nullptr);
+                             hipStream_t stream, const float* res = nullptr, uint32_t* dirty = nullptr);
 // The same product with the weight rows handed out to workgroups by a
 // counter (see dspark_lm_head_sched) where the shape allows (M <= 8,
 // K <= 4096), else launch_gemv. The counter reads 0 before and after.
@@ -304,10 +306,12 @@ uint32_t markov_set_spin_limit(uint32_t polls);
 // its size, and its device address (set up on the first call per device).
 size_t markov_scratch_bytes();
 hipError_t markov_scratch(void** out, hipStream_t stream);
+// lm_ticks (the round): n_lm_ticks ticket words of the round's split lm_head
+// that every call sets to 0.
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
                          int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
-                         hipStream_t stream);
+                         hipStream_t stream, uint32_t* lm_ticks = nullptr, int n_lm_ticks = 0);
 
 // The same loop over Q8_0 markov weights (r % 32 == 0); see dspark_markov_sample_q8.
 hipError_t launch_markov_q8(const float* base, int R, int B, int V, const int8_t* w1q, const uint16_t* w1d,

@@ -62,6 +62,7 @@ struct GemvParams {
   uint32_t* tick;
   float* part;
   int nrb;
+  uint32_t* dirty;  // or null: set to 1 by a workgroup that draws a ticket past 1 (a word not left 0)
 };
 
 // The output value of (m, n), plus the residual when there is one (read and
@@ -1095,7 +1096,13 @@ __global__ __launch_bounds__(kMrThreads) void gemv_mrows_kernel(GemvParams p) {
   }
   if constexpr (SPLIT) {
     __shared__ uint32_t ticket;
-    if (tid == 0) ticket = __hip_atomic_fetch_add(p.tick + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      ticket = __hip_atomic_fetch_add(p.tick + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // A ticket past 1 means the word was not 0 before this launch (a
+      // workspace never zero-filled): the outputs of this block may be
+      // wrong, and the caller's flag word says so.
+      if (ticket > 1u && p.dirty) __hip_atomic_store(p.dirty, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     if (ticket == 0) return;  // uniform: the other half finishes the block
     if (tid == 0) __hip_atomic_store(p.tick + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1275,6 +1282,8 @@ hipError_t launch_mrows_split(const GemvParams& prm, hipStream_t st) {
 
 }  // namespace
 
+int gemv_split_tick_words(int N) { return split_row_blocks(N); }
+
 size_t gemv_split_workspace_bytes(int N, int K, int M) {
   if (!gemv_split_fits(N, K, M)) return 0;
   return split_tick_bytes(N) + static_cast<size_t>(2) * split_row_blocks(N) * kMrMaxM * kSplitRows * 4;
@@ -1286,7 +1295,7 @@ bool gemv_split_fits(int N, int K, int M) {
 }
 
 hipError_t launch_gemv_split(const uint16_t* W, int N, int K, const float* X, int M, float* Y, void* workspace,
-                             hipStream_t stream, const float* res) {
+                             hipStream_t stream, const float* res, uint32_t* dirty) {
   if (!gemv_split_fits(N, K, M) || !workspace) return launch_gemv(W, N, K, X, M, Y, stream, res);
   GemvParams prm{};
   prm.W = W;
@@ -1296,6 +1305,7 @@ hipError_t launch_gemv_split(const uint16_t* W, int N, int K, const float* X, in
   prm.nrb = split_row_blocks(N);
   prm.tick = static_cast<uint32_t*>(workspace);
   prm.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + split_tick_bytes(N));
+  prm.dirty = dirty;
   // Balanced parts of at most kMrMaxM rows, one after the other on the
   // stream: each leaves the ticket words at 0 for the next.
   const int parts = (M + kMrMaxM - 1) / kMrMaxM;

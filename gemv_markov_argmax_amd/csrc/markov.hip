@@ -128,6 +128,8 @@ struct MarkovParams {
   int probe_on;          // nonzero: also compute the confidence probe described by `probe`
   uint32_t nonce;        // launch number (never 0): tells a late workgroup of a repairing launch
   uint32_t spin_limit;   // polls before a grid-wide wait gives up
+  uint32_t* lm_ticks;    // the round's split lm_head ticket words, set to 0 by every call (or null)
+  int n_lm_ticks;
   ProbeArgs probe;
   // Q8_0 weights (the Q8 kernels): quants [V, r] and binary16 block scales [V, r / 32]
   const int8_t* w1q;
@@ -212,6 +214,13 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
   // it 0, so a nonzero word means that lm_head ran on a counter that was not
   // (the workspace was never zero-filled) and some base rows are missing.
   const uint32_t lm_counter = load_coherent(p.ctl + kCtlLmCounter);
+  // The round's split lm_head (more than 16 rows) has finished, and the next
+  // one starts after this launch: its ticket words are set to 0 here, so a
+  // word that was not (a workspace never zero-filled) spoils one round at
+  // most. A clean lm_head has already left them 0.
+  if (tid == 0)
+    for (int e = static_cast<int>(blockIdx.x); e < p.n_lm_ticks; e += G)
+      __hip_atomic_store(p.lm_ticks + e, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // kStateRepaired under this launch's number: a late workgroup of the
   // repairing launch, or a replay of that captured launch.
   const bool repair = !(state == kStateOk || (state == kStateRepaired && repaired_by != p.nonce));
@@ -1023,10 +1032,12 @@ hipError_t markov_scratch(void** out, hipStream_t stream) {
 hipError_t launch_markov(const float* base, int R, int B, int V, const uint16_t* w1,
                          const uint16_t* w2, int r, const int64_t* d2t, const int64_t* prev0,
                          int k, int64_t* ids, void* workspace, const ProbeArgs* probe,
-                         hipStream_t stream) {
+                         hipStream_t stream, uint32_t* lm_ticks, int n_lm_ticks) {
   MarkovParams prm = common_params(base, R, B, V, r, d2t, prev0, k, ids, workspace);
   prm.w1 = w1;
   prm.w2 = w2;
+  prm.lm_ticks = lm_ticks;
+  prm.n_lm_ticks = lm_ticks ? n_lm_ticks : 0;
   return launch_markov_any(prm, false, probe, stream);
 }
 

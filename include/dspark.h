@@ -377,7 +377,11 @@ dspark_status dspark_markov_sample_probe(const float* base, int num_reqs, int B,
  * A zero-filled workspace keeps that word 0 across rounds. If it is not 0
  * when the loop starts (a workspace that was never zero-filled), the
  * lm_head may have left base rows out: that round's ids are all -2 and the
- * word is set back to 0, so the next round is whole again.
+ * word is set back to 0, so the next round is whole again. The split
+ * lm_head (more than 16 rows) sets that word when it draws a ticket that
+ * shows its own ticket words were not 0, with the same outcome; and the
+ * loop sets those ticket words to 0 in every round, so a workspace that
+ * was never zero-filled spoils its first round at most.
  *
  *   W_lm      bf16  [V, d]                 16-byte aligned
  *   H         fp32  [num_reqs * B, d]      16-byte aligned (hidden states, also the probe's x)

@@ -735,6 +735,33 @@ def test_draft_round_dirty_lm_counter(dev, name):
     assert torch.equal(again["ids"], clean)
 
 
+def test_draft_round_dirty_split_tickets(dev):
+    """The batched round's split lm_head on ticket words that are not 0 (a
+    workspace never zero-filled): a word past 1 makes that round's ids -2;
+    the loop leaves every ticket word 0, and the next round equals a round
+    on a clean workspace, bit for bit."""
+    inp, t = _round_tensors("reduced_vocab_batched", dev)
+    ops = _ops()
+    R, B, k, V = inp["num_reqs"], inp["B"], inp["k"], inp["V"]
+    d = t["W"].shape[1]
+    say(f"[draft_round dirty split tickets] seed={inp['seed']}")
+    clean = ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k)
+    clean = {n: x.clone() for n, x in clean.items() if x is not None}
+    ws = ops.draft_round_workspace(R, B, k, V, d, dev)
+    at = (ops.markov_workspace_bytes(R, k, V) + 255) // 256 * 64  # int32 index of the first ticket word
+    n = ((V + 255) // 256 + 7) // 8 * 8
+    for val in (12345, 1):
+        ws.view(torch.int32)[at: at + n] = val
+        out = ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws)
+        torch.cuda.synchronize()
+        if val > 1:
+            assert (out["ids"] == -2).all(), "a round on dirty ticket words was not reported"
+        assert int(ws.view(torch.int32)[at: at + n].count_nonzero().item()) == 0, "ticket words left set"
+        again = ops.draft_round(t["W"], t["H"], t["w1"], t["w2"], t["prev0"], B, k, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again["ids"], clean["ids"]) and torch.equal(again["base"], clean["base"])
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen3_8b_head", "reduced_vocab_batched", "lane27b"])
 def test_draft_round_fused(dev, name):
     """dspark_draft_round (the probe inside the Markov launch) gives the same
