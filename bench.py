@@ -602,6 +602,10 @@ def main():
 
     sink = torch.empty(8192, dtype=torch.int32, device=dev)
     mk_ms, mka_ms = per_call_ms(mk), per_call_ms(mk_alone)
+    # The round's lm_head back to back, and (when the round splits K) the
+    # one-pass kernel of dspark_lm_head on the same tensors beside it.
+    lm_b2b_ms = per_call_ms(lm)
+    one_pass_ms = per_call_ms(lambda: ops.lm_head(W, H, out=logits)) if split else None
     pr_ms = per_call_graph_ms(pr)
     empty_ms = per_call_graph_ms(lambda: ops.stream_read(sink, 1, 256, sink=sink, nbytes=0))
 
@@ -689,7 +693,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": lm_label,
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
                      "traffic": tr_lm, "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3,
-                     "frac_of_stream_ceiling": lm_gbs / ceil[ceil_ref]["gbs"], "stream_ceiling_ref": ceil_ref},
+                     "frac_of_stream_ceiling": lm_gbs / ceil[ceil_ref]["gbs"], "stream_ceiling_ref": ceil_ref,
+                     "back_to_back_us": lm_b2b_ms * 1e3,
+                     "one_pass_back_to_back_us": one_pass_ms * 1e3 if one_pass_ms is not None else None},
         # Whole round. HBM bytes are the counters' (markov_w2 is read from
         # memory once per call and served on chip for every step); the
         # algorithmic figure counts markov_w2 once per step, as the method

@@ -855,12 +855,19 @@ __global__ __launch_bounds__(16 * kWave) void gemv_sched_kernel(GemvParams p, ui
 // order they are consumed), and there is no global store before the end, so
 // the compiler never drains the prefetch. The output tile is assembled in
 // LDS and y = hi + lo is written row by row.
-// Two tiles are used: 128 rows x all of K in chunks of 4 k-blocks (NT = 2,
-// KC = 4), and, with K split in halves (SPLIT), 256 rows x half of K in
-// chunks of 2 (NT = 4, KC = 2). For a compute unit's share of the weights
-// the split reads half the activation bytes and does 2/3 of the LDS
-// traffic per weight byte (larger wave tiles); measured on MI355X at
-// [72 x 5120] x [32000 x 5120]: 81 against 94 us.
+// Two tiles are used: 128 rows x all of K (NT = 2), and, with K split in
+// halves (SPLIT), 256 rows x half of K (NT = 4), both in chunks of 2
+// k-blocks (KC = 2). For a compute unit's share of the weights the split
+// reads half the activation bytes and does 2/3 of the LDS traffic per
+// weight byte (larger wave tiles).
+// LDS rows are padded by 32 bytes: on gfx950 a ds_read_b128 whose 16 lanes
+// of a fragment column read 16 rows is conflict-free when the row stride
+// is 32 mod 64 bytes (measured with the LDS bank-conflict counter: 4
+// cycles per read at strides 160, 224, 288, 352; 8 cycles at 144, 272 and
+// every other multiple of 16 tried). A 16-byte pad doubled the fragment
+// reads' LDS time. With the 32-byte pad a K chunk of 4 k-blocks no longer
+// fits twice in LDS beside the A rows, hence KC = 2. Measured on MI355X at
+// [72 x 5120] x [32000 x 5120]: one pass 87.5 -> 79 us, split 82 -> 77 us.
 constexpr int kMrMaxM = 80;                     // activation rows per launch
 constexpr int kMrWaves = 8;
 constexpr int kMrThreads = kMrWaves * kWave;
@@ -869,7 +876,7 @@ constexpr int kMrThreads = kMrWaves * kWave;
 template <int NT, int KC>
 struct MrShape {
   static constexpr int rows = 64 * NT;                              // weight rows per workgroup
-  static constexpr int stride = KC * 64 + 16;                       // bytes per LDS row of a chunk (padded)
+  static constexpr int stride = KC * 64 + 32;                       // bytes per LDS row of a chunk (padded)
   static constexpr int tpr = KC * 4;                                // threads per weight row of a chunk
   static constexpr int rpq = kMrThreads / tpr;                      // weight rows per load instruction
   static constexpr int bq = rows / rpq;                             // weight loads per thread per chunk
@@ -1260,7 +1267,7 @@ hipError_t dispatch(const GemvParams& prm, const Plan& pl, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-template <int MB2, int NT = 2, int KC = 4, bool SPLIT = false>
+template <int MB2, int NT = 2, int KC = 2, bool SPLIT = false>
 hipError_t launch_mrows(const GemvParams& prm, hipStream_t st) {
   const void* fn = reinterpret_cast<const void*>(&gemv_mrows_kernel<MB2, NT, KC, SPLIT>);  // static LDS only
   GemvParams a = prm;
