@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "draft rounds/s + achieved HBM GB/s (% of peak), V=151936 r=256 B=7"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 
 
 def log(*a):
@@ -695,7 +696,16 @@ def main():
                      "traffic": tr_lm, "algorithmic_bytes_per_launch": lm_b, "avg_launch_us": lm_avg * 1e3,
                      "frac_of_stream_ceiling": lm_gbs / ceil[ceil_ref]["gbs"], "stream_ceiling_ref": ceil_ref,
                      "back_to_back_us": lm_b2b_ms * 1e3,
-                     "one_pass_back_to_back_us": one_pass_ms * 1e3 if one_pass_ms is not None else None},
+                     "one_pass_back_to_back_us": one_pass_ms * 1e3 if one_pass_ms is not None else None,
+                     # The same launch against the matrix cores: the bf16 MFMA
+                     # work of the exact hi/lo split of the activations (2M
+                     # bf16 rows of A), 2 * 2M * V * d flops, against the dense
+                     # bf16 peak. Not the binding limit of any lm_head here.
+                     "mfma": None if q8 else {
+                         "flops_per_launch": 2 * 2 * rows * inp["V"] * inp["d"],
+                         "tflops": 2 * 2 * rows * inp["V"] * inp["d"] / (lm_avg * 1e-3) / 1e12,
+                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                         "frac": 2 * 2 * rows * inp["V"] * inp["d"] / (lm_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
         # Whole round. HBM bytes are the counters' (markov_w2 is read from
         # memory once per call and served on chip for every step); the
         # algorithmic figure counts markov_w2 once per step, as the method

@@ -616,11 +616,12 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
 #pragma unroll
     for (int u0 = 0; u0 < (RT > 0 ? RT : 1); u0 += RG) {
       constexpr int L1 = LT;
+      constexpr int L1A = LT > 0 ? LT : 1;  // (array sizes)
       const bool first = u0 == 0;
-      f32x4 accr[RG], accl[L1];
-      int jl[L1];
-      const BF* srcl[L1];
-      uint32_t lsc[L1][Q8 ? kSH : 1];  // Q8_0: block scales of those LDS tiles (row li)
+      f32x4 accr[RG], accl[L1A];
+      int jl[L1A];
+      const BF* srcl[L1A];
+      uint32_t lsc[L1A][Q8 ? kSH : 1];  // Q8_0: block scales of those LDS tiles (row li)
 #pragma unroll
       for (int t = 0; t < L1; ++t) {
         jl[t] = nreg + w + NW * t;
@@ -641,12 +642,12 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
         const BF a = a_frag[4 * kb];
         float s1[4];
         a_scales(kb, s1);
-        BF bl[L1];
+        BF bl[L1A];
         if (first)
 #pragma unroll
           for (int t = 0; t < L1; ++t) bl[t] = srcl[t][kb * kWave];
         if constexpr (Q8) {
-          i32x4 dr[RG], dl[L1];
+          i32x4 dr[RG], dl[L1A];
 #pragma unroll
           for (int u = 0; u < RG; ++u)
             if (RT > 0 && u0 + u < RT) dr[u] = mma8(a, wreg[u0 + u < RT ? u0 + u : 0][kb]);
@@ -850,10 +851,9 @@ LoopPlan make_loop_plan(int R, int V, int r, int k, int G, int NW, bool q8) {
   return pl;
 }
 
-template <int NW, int KB, bool BL, bool Q8, int NV = 4>
-hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
+template <int NW, int KB, bool BL, bool Q8, int NV, int LT>
+hipError_t launch_loop_lt(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
   constexpr int RT = reg_tiles(NW, KB, Q8, BL);
-  constexpr int LT = KB >= 16 ? 1 : 2;
   constexpr int kLoopThreads = NW * kWave;
   const void* fn = reinterpret_cast<const void*>(&markov_loop_kernel<NW, KB, RT, LT, BL, Q8, NV>);
   static const hipError_t attr =
@@ -869,6 +869,16 @@ hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream
   if (per_cu < 1 || pl.G > per_cu * cus) return hipErrorCooperativeLaunchTooLarge;
   void* args[] = {&prm};
   return hipLaunchKernel(fn, dim3(pl.G), dim3(kLoopThreads), args, pl.lds, st);
+}
+
+// LT: LDS tiles of a wave that ride in the register tiles' MFMA chains. When
+// every tile of a workgroup is in registers (small vocabularies, the batched
+// lane) there are none, and LT = 0 drops the two chains that would otherwise
+// run on a stand-in tile at every step.
+template <int NW, int KB, bool BL, bool Q8, int NV = 4>
+hipError_t launch_loop(MarkovParams& prm, const LoopPlan& pl, int cus, hipStream_t st) {
+  if (pl.lds_tiles == 0) return launch_loop_lt<NW, KB, BL, Q8, NV, 0>(prm, pl, cus, st);
+  return launch_loop_lt<NW, KB, BL, Q8, NV, (KB >= 16 ? 1 : 2)>(prm, pl, cus, st);
 }
 
 template <bool Q8>
@@ -933,7 +943,9 @@ hipError_t launch_markov_any(MarkovParams prm, bool q8, const ProbeArgs* probe, 
   prm.tiles = tiles;
   {
     const size_t per_copy = static_cast<size_t>(k) * R * pl.G;
-    prm.nrep = static_cast<int>(std::max<size_t>(1, std::min<size_t>(kMaxRep, kCopyStride / per_copy)));
+    // Copy c takes slots [c * kCopyStride, c * kCopyStride + per_copy): all
+    // kMaxRep copies fit when one call's slots fit in one stride.
+    prm.nrep = per_copy <= kCopyStride ? kMaxRep : 1;
   }
   uint32_t nonce = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
   if (nonce == 0u) nonce = g_launches.fetch_add(1, std::memory_order_relaxed) + 1u;
