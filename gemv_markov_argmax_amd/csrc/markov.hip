@@ -682,22 +682,40 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
 #pragma unroll
         for (int t = 0; t < L1; ++t) score(jl[t], jl[t] < nheld, accl[t]);
     }
-    // Further LDS tiles of this wave, if any.
-    for (int j = nreg + w + NW * LT; j < nheld; j += NW) {
-      const BF* src = w2l + static_cast<size_t>(j - nreg) * KB * kWave + ll;
-      uint32_t sc1[Q8 ? kSH : 1];
-      if constexpr (Q8)
+    // Further LDS tiles of this wave, if any, FG at a time: their MFMA chains
+    // interleaved per k-block (a group's missing tiles compute on LDS tile 0
+    // and are not scored). One chain at a time leaves each MFMA waiting on
+    // the one before it. Pairs with eight waves (the Q8_0 27B-lane loop:
+    // 117 -> 114 us); with four waves and ten register tiles a pair spills
+    // (the bf16 27B-lane loop: 112 -> 126 us), so those go one at a time.
+    constexpr int FG = NW == 4 ? 1 : 2;
+    for (int j0 = nreg + w + NW * LT; j0 < nheld; j0 += NW * FG) {
+      const BF* srcf[FG];
+      uint32_t scf[FG][Q8 ? kSH : 1];
+      f32x4 accf[FG];
 #pragma unroll
-        for (int h = 0; h < kSH; ++h)
-          sc1[h] = reinterpret_cast<const uint32_t*>(w2ls + (static_cast<size_t>(j - nreg) * 16 + li) * kSR)[h];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < FG; ++f) {
+        const int j = j0 + NW * f;
+        const int lt = j < nheld ? j - nreg : 0;
+        srcf[f] = w2l + static_cast<size_t>(lt) * KB * kWave + ll;
+        accf[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (Q8)
+#pragma unroll
+          for (int h = 0; h < kSH; ++h)
+            scf[f][h] = reinterpret_cast<const uint32_t*>(w2ls + (static_cast<size_t>(lt) * 16 + li) * kSR)[h];
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float s1[4];
         a_scales(kb, s1);
-        mac(acc, a_frag[4 * kb], src[kb * kWave], sc1, kb, s1);
+        BF bf[FG];
+#pragma unroll
+        for (int f = 0; f < FG; ++f) bf[f] = srcf[f][kb * kWave];
+#pragma unroll
+        for (int f = 0; f < FG; ++f) mac(accf[f], a_frag[4 * kb], bf[f], scf[f], kb, s1);
       }
-      score(j, true, acc);
+#pragma unroll
+      for (int f = 0; f < FG; ++f) score(j0 + NW * f, j0 + NW * f < nheld, accf[f]);
     }
     // Tiles beyond on-chip capacity are read from memory at every step.
     for (int j = js0; j < nt; j += NW) {
