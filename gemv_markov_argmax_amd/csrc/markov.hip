@@ -610,21 +610,24 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     // others' latency and the LDS reads of a k-block go out together. An
     // absent tile computes on zeros (or on LDS tile 0) and is not scored.
     // With many register tiles (one wave per SIMD) they go in two passes,
-    // which halves the accumulators held at once; the LDS tiles ride along
-    // with the first pass.
+    // which halves the accumulators held at once; LT LDS tiles ride along
+    // with each pass (other tiles in each), so that four waves keep LDS
+    // tiles in interleaved chains too.
     constexpr int RG = RT > 6 ? (RT + 1) / 2 : (RT > 0 ? RT : 1);  // register tiles per pass
+    constexpr int NPASS = RT > 0 ? (RT + RG - 1) / RG : 1;
 #pragma unroll
     for (int u0 = 0; u0 < (RT > 0 ? RT : 1); u0 += RG) {
       constexpr int L1 = LT;
       constexpr int L1A = LT > 0 ? LT : 1;  // (array sizes)
-      const bool first = u0 == 0;
+      const int pass = u0 / RG;
+      const bool first = true;  // (every pass carries its LDS tiles)
       f32x4 accr[RG], accl[L1A];
       int jl[L1A];
       const BF* srcl[L1A];
       uint32_t lsc[L1A][Q8 ? kSH : 1];  // Q8_0: block scales of those LDS tiles (row li)
 #pragma unroll
       for (int t = 0; t < L1; ++t) {
-        jl[t] = nreg + w + NW * t;
+        jl[t] = nreg + w + NW * (LT * pass + t);
         const int lt = jl[t] < nheld ? jl[t] - nreg : 0;
         srcl[t] = w2l + static_cast<size_t>(lt) * KB * kWave + ll;
         accl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(NW * kWave) void markov_loop_kernel(MarkovParams p)
     // 117 -> 114 us); with four waves and ten register tiles a pair spills
     // (the bf16 27B-lane loop: 112 -> 126 us), so those go one at a time.
     constexpr int FG = NW == 4 ? 1 : 2;
-    for (int j0 = nreg + w + NW * LT; j0 < nheld; j0 += NW * FG) {
+    for (int j0 = nreg + w + NW * LT * NPASS; j0 < nheld; j0 += NW * FG) {
       const BF* srcf[FG];
       uint32_t scf[FG][Q8 ? kSH : 1];
       f32x4 accf[FG];
