@@ -621,10 +621,12 @@ def main():
             ops.markov_sample(logits.view(R, B, V), w1, w2, prev0, 1, out=ids1, workspace=ws)
     mk1_ms = per_call_ms(mk_one)
     step_us = (mka_ms - mk1_ms) * 1e3 / (k - 1) if k > 1 else None
-    # Cold: a 512 MiB streaming read before each call evicts markov_w2 from
-    # the caches (the read is outside the events).
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    mk_cold_ms = per_call_ms(mk_alone, n=20, before=lambda: ops.stream_read(flush, 8192, 256, sink=sink))
+    # Cold: a 1 GiB read with plain loads before each call evicts markov_w2
+    # from L2 and from the Infinity Cache (outside the events). A
+    # non-temporal read, like the lm_head's weight stream, would leave it in
+    # the Infinity Cache; a pass that writes would add its write-backs.
+    flush = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    mk_cold_ms = per_call_ms(mk_alone, n=20, before=lambda: flush.sum())
     del flush
 
     # The streaming-read ceiling of this device in this run: 4 GiB read at
