@@ -453,6 +453,9 @@ def main():
     q8 = inp.get("weights") == "q8_0"
     if q8:  # Q8_0 lm_head and markov weights: (quants, scales) pairs
         W = ops.q8_from_numpy(inp["Wq_lm"], inp["Wd_lm"], dev)
+        # the lm_head's scale rows padded to whole 128-byte lines, a layout
+        # made once when the weights are packed (same values, same products)
+        W = (W[0], ops.q8_pad_scales(W[1]))
         w1 = ops.q8_from_numpy(inp["w1q"], inp["w1d"], dev)
         w2 = ops.q8_from_numpy(inp["w2q"], inp["w2d"], dev)
     else:

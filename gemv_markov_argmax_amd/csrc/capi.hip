@@ -54,6 +54,12 @@ dspark_status gemv_q8_checks(const int8_t* Wq, const uint16_t* Wd, int N, int K,
 
 dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
+// A Q8_0 scale row stride: at least the K / 32 scales of a row, at most one
+// 128-byte line (64 scales) of padding beyond them.
+dspark_status q8_ldd_check(int ldd, int K) {
+  return ldd >= K / 32 && ldd <= K / 32 + 64 ? DSPARK_OK : DSPARK_ERR_SHAPE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,6 +128,14 @@ dspark_status dspark_lm_head_q8(const int8_t* Wq, const uint16_t* Wd, int V, int
   const dspark_status st = gemv_q8_checks(Wq, Wd, V, d, H, rows, logits);
   if (st != DSPARK_OK) return st;
   return from_hip(dspark::launch_gemv_q8(Wq, Wd, V, d, H, rows, logits, static_cast<hipStream_t>(stream)));
+}
+
+dspark_status dspark_lm_head_q8_ld(const int8_t* Wq, const uint16_t* Wd, int ldd, int V, int d, const float* H,
+                                   int rows, float* logits, void* stream) {
+  dspark_status st = gemv_q8_checks(Wq, Wd, V, d, H, rows, logits);
+  if (st == DSPARK_OK) st = q8_ldd_check(ldd, d);
+  if (st != DSPARK_OK) return st;
+  return from_hip(dspark::launch_gemv_q8(Wq, Wd, V, d, H, rows, logits, static_cast<hipStream_t>(stream), ldd));
 }
 
 size_t dspark_markov_workspace_bytes(int num_reqs, int k, int V) {
@@ -300,16 +314,28 @@ dspark_status dspark_draft_round_q8(const int8_t* Wq_lm, const uint16_t* Wd_lm, 
                                     const uint16_t* probe_w, float probe_bias, float probe_threshold, float* base_out,
                                     int64_t* ids_out, float* logit_out, int32_t* pass_out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+  return dspark_draft_round_q8_ld(Wq_lm, Wd_lm, d / 32, V, d, H, num_reqs, B, w1q, w1d, w2q, w2d, r, d2t, prev0, k,
+                                  probe_w, probe_bias, probe_threshold, base_out, ids_out, logit_out, pass_out,
+                                  workspace, workspace_bytes, stream);
+}
+
+dspark_status dspark_draft_round_q8_ld(const int8_t* Wq_lm, const uint16_t* Wd_lm, int ldd_lm, int V, int d,
+                                       const float* H, int num_reqs, int B, const int8_t* w1q, const uint16_t* w1d,
+                                       const int8_t* w2q, const uint16_t* w2d, int r, const int64_t* d2t,
+                                       const int64_t* prev0, int k, const uint16_t* probe_w, float probe_bias,
+                                       float probe_threshold, float* base_out, int64_t* ids_out, float* logit_out,
+                                       int32_t* pass_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_reqs < 1 || num_reqs > 16 || B < 1 || B > (1 << 20)) return DSPARK_ERR_SHAPE;
   const int rows = num_reqs * B;
   dspark_status st = gemv_q8_checks(Wq_lm, Wd_lm, V, d, H, rows, base_out);
+  if (st == DSPARK_OK) st = q8_ldd_check(ldd_lm, d);
   if (st == DSPARK_OK)
     st = markov_q8_checks(base_out, num_reqs, B, V, w1q, w1d, w2q, w2d, r, d2t, prev0, k, ids_out, workspace,
                           workspace_bytes);
   if (st == DSPARK_OK && probe_w) st = probe_checks(H, rows, d, probe_w, logit_out, pass_out);
   if (st != DSPARK_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dspark::launch_gemv_q8(Wq_lm, Wd_lm, V, d, H, rows, base_out, s) != hipSuccess) return DSPARK_ERR_HIP;
+  if (dspark::launch_gemv_q8(Wq_lm, Wd_lm, V, d, H, rows, base_out, s, ldd_lm) != hipSuccess) return DSPARK_ERR_HIP;
   const dspark::ProbeArgs pa{H, rows, d, probe_w, probe_bias, probe_threshold, logit_out, pass_out};
   return from_hip(dspark::launch_markov_q8(base_out, num_reqs, B, V, w1q, w1d, w2q, w2d, r, d2t, prev0, k, ids_out,
                                            workspace, probe_w ? &pa : nullptr, s));

@@ -258,8 +258,9 @@ hipError_t launch_attention(const float* q, const float* kb, const float* vb, in
 
 // Small-M GEMV over Q8_0 weights; see dspark_proj_smallm_q8.
 bool gemv_q8_shape_fits(int N, int K, int M);
+// ldd: binary16 scales per row of Wd (0: K / 32, the dense layout).
 hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M, float* Y,
-                          hipStream_t stream);
+                          hipStream_t stream, int ldd = 0);
 
 // Y[m, n] = sum_t X[m, t] W[n, t] for all M rows (any M >= 1).
 hipError_t launch_gemv(const uint16_t* W, int N, int K, const float* X, int M, float* Y,

@@ -44,6 +44,7 @@ struct Q8Params {
   float* Y;
   int N, K, M;  // M rows in this launch (<= 16)
   int ldy;
+  int ldd;      // binary16 scales per row of Wd (>= K / 32; more when rows are padded)
   int chunk;    // tiles whose outputs are staged in LDS at once (even)
   int pq, prem; // row pairs per workgroup: N/2 = pq * gridDim.x + prem
 };
@@ -113,9 +114,9 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
   uint16_t* wsc = sc + w * 16 * KBW;
 
   const uint32_t rowb = static_cast<uint32_t>(K);       // quant bytes per row
-  const uint32_t drow = static_cast<uint32_t>(KB) * 2;  // scale bytes per row
+  const uint32_t drow = static_cast<uint32_t>(p.ldd) * 2;  // scale bytes per row (with any padding)
   const BufRes qres = buf_res(p.Wq + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
-  const BufRes dres = buf_res(p.Wd + static_cast<size_t>(r0) * KB, static_cast<uint32_t>(r1 - r0) * drow);
+  const BufRes dres = buf_res(p.Wd + static_cast<size_t>(r0) * p.ldd, static_cast<uint32_t>(r1 - r0) * drow);
   const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
 
   u32x4 afr[KBW][F];
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_kernel(Q8Params p) {
   // two (row i, blocks 2g and 2g + 1 of the segment, lanes 2g < KBW), so a
   // wave's scales of a tile take one load instruction instead of KBW / 4;
   // else halves (row i, blocks g + 4j).
-  constexpr bool paired = PAIRED;  // the host launches it for K / 32 even only
+  constexpr bool paired = PAIRED;  // the host launches it for K / 32 and the row stride even only
   uint32_t s0[SPL], s1[SPL];
   int ph = 0, c0 = 0, c1 = 0, lim = 0;
   uint32_t lane_off = 0, sc_off[SPL];
@@ -352,9 +353,9 @@ __global__ __launch_bounds__(kQNW * kWave) void gemv_q8_short_kernel(Q8Params p)
   uint16_t* wsc = sc + w * 16 * KBW;
 
   const uint32_t rowb = static_cast<uint32_t>(K);       // quant bytes per row
-  const uint32_t drow = static_cast<uint32_t>(KB) * 2;  // scale bytes per row
+  const uint32_t drow = static_cast<uint32_t>(p.ldd) * 2;  // scale bytes per row (with any padding)
   const BufRes qres = buf_res(p.Wq + static_cast<size_t>(r0) * K, static_cast<uint32_t>(r1 - r0) * rowb);
-  const BufRes dres = buf_res(p.Wd + static_cast<size_t>(r0) * KB, static_cast<uint32_t>(r1 - r0) * drow);
+  const BufRes dres = buf_res(p.Wd + static_cast<size_t>(r0) * p.ldd, static_cast<uint32_t>(r1 - r0) * drow);
   const BufRes xres = buf_res(p.X, static_cast<uint32_t>(M) * K * 4);
 
   // Phase ph, tile t: lane offsets of the quants (16 bytes of row lrow) and
@@ -536,11 +537,12 @@ hipError_t launch_q8_as(const Q8Params& prm, int grid, size_t lds, bool multi, h
   return hipLaunchKernel(multi ? many : one, dim3(grid), dim3(kQNW * kWave), args, lds, st);
 }
 
-// Scale words of two blocks need 4-byte aligned scale rows: K / 32 even.
+// Scale words of two blocks need 4-byte aligned scale rows: K / 32 and the
+// row stride even.
 template <bool PACK, int KBW>
 hipError_t launch_q8(const Q8Params& prm, int grid, size_t lds, bool multi, hipStream_t st) {
-  return (prm.K / 32) % 2 == 0 ? launch_q8_as<PACK, KBW, true>(prm, grid, lds, multi, st)
-                               : launch_q8_as<PACK, KBW, false>(prm, grid, lds, multi, st);
+  return (prm.K / 32) % 2 == 0 && prm.ldd % 2 == 0 ? launch_q8_as<PACK, KBW, true>(prm, grid, lds, multi, st)
+                                                   : launch_q8_as<PACK, KBW, false>(prm, grid, lds, multi, st);
 }
 
 template <bool PACK, int KBW>
@@ -570,7 +572,7 @@ bool gemv_q8_shape_fits(int N, int K, int M) {
 }
 
 hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, const float* X, int M, float* Y,
-                          hipStream_t stream) {
+                          hipStream_t stream, int ldd) {
   const int cus = device_cu_count();
   if (cus <= 0) return hipErrorNoDevice;
   const int tiles = (N + 15) / 16;
@@ -591,6 +593,7 @@ hipError_t launch_gemv_q8(const int8_t* Wq, const uint16_t* Wd, int N, int K, co
     prm.K = K;
     prm.M = mm;
     prm.ldy = N;
+    prm.ldd = ldd > 0 ? ldd : KB;
     prm.pq = (N / 2) / grid;
     prm.prem = (N / 2) % grid;
     if (rounds <= kQShortTiles) {

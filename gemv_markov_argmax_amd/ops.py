@@ -30,10 +30,13 @@ SIGNATURES = {
     "dspark_draft_round_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_proj_smallm_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
     "dspark_lm_head_q8": (_i, [_p, _p, _i, _i, _p, _i, _p, _p]),
+    "dspark_lm_head_q8_ld": (_i, [_p, _p, _i, _i, _i, _p, _i, _p, _p]),
     "dspark_markov_sample_q8": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _p, _sz,
                                      _p, _i, _i, _p, _f, _f, _p, _p, _p]),
     "dspark_draft_round_q8": (_i, [_p, _p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _f, _f,
                                    _p, _p, _p, _p, _p, _sz, _p]),
+    "dspark_draft_round_q8_ld": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _i, _p, _p, _i, _p, _f, _f,
+                                      _p, _p, _p, _p, _p, _sz, _p]),
     "dspark_rmsnorm": (_i, [_p, _i, _i, _p, _f, _p, _p]),
     "dspark_silu_gate": (_i, [_p, _i, _i, _p, _p]),
     "dspark_proj_smallm_add": (_i, [_p, _i, _i, _p, _i, _p, _p, _p]),
@@ -259,8 +262,41 @@ def proj_smallm_q8(Wq: torch.Tensor, Wd: torch.Tensor, X: torch.Tensor, out: tor
 
 
 def lm_head_q8(Wq: torch.Tensor, Wd: torch.Tensor, H: torch.Tensor, out: torch.Tensor | None = None):
-    """Base logits from a Q8_0 lm_head (dspark_lm_head_q8)."""
-    return _gemv_q8(lib().dspark_lm_head_q8, Wq, Wd, H, out)
+    """Base logits from a Q8_0 lm_head (dspark_lm_head_q8). Wd may have
+    padded rows, [V, ldd] with d / 32 <= ldd <= d / 32 + 64 (as q8_pad_scales
+    makes them); the call is then dspark_lm_head_q8_ld."""
+    V, d = Wq.shape
+    if Wd.dim() != 2 or Wd.shape[0] != V or Wd.shape[1] == d // 32:
+        return _gemv_q8(lib().dspark_lm_head_q8, Wq, Wd, H, out)
+    ldd = Wd.shape[1]
+    _dev(Wq, torch.int8, "Wq", 2)
+    _dev(Wd, torch.float16, "Wd", 2)
+    _dev(H, torch.float32, "H", 2)
+    M = H.shape[0]
+    if H.shape[1] != d or d % 32 != 0:
+        raise ValueError("Wq [V, d] (d % 32 == 0) and H [rows, d] required")
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=H.device)
+    _dev(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (M, V):
+        raise ValueError("out must be [rows, V]")
+    _check(lib().dspark_lm_head_q8_ld(Wq.data_ptr(), Wd.data_ptr(), ldd, V, d, H.data_ptr(), M, out.data_ptr(),
+                                      _stream(Wq)))
+    return out
+
+
+def q8_pad_scales(Wd: torch.Tensor, line: int = 64) -> torch.Tensor:
+    """Q8_0 scale rows padded with zeros to a multiple of ``line`` values (64
+    binary16 values: whole 128-byte lines), for dspark_lm_head_q8_ld and
+    dspark_draft_round_q8_ld. A layout made once when the weights are packed;
+    the products are the same, bit for bit."""
+    N, kb = Wd.shape
+    ldd = (kb + line - 1) // line * line
+    if ldd == kb:
+        return Wd
+    out = torch.zeros((N, ldd), dtype=Wd.dtype, device=Wd.device)
+    out[:, :kb] = Wd
+    return out
 
 
 def proj_smallm_add(W: torch.Tensor, X: torch.Tensor, residual: torch.Tensor, out: torch.Tensor | None = None):
@@ -755,8 +791,9 @@ def draft_round_q8(Wq: torch.Tensor, Wd: torch.Tensor, H: torch.Tensor, w1q: tor
     V, d = Wq.shape
     R = prev0.shape[0]
     r = w1q.shape[1]
-    if tuple(Wd.shape) != (V, d // 32) or tuple(H.shape) != (R * B, d):
-        raise ValueError("Wq [V, d], Wd [V, d / 32] and H [num_reqs * B, d] required")
+    if Wd.shape[0] != V or not (d // 32 <= Wd.shape[1] <= d // 32 + 64) or tuple(H.shape) != (R * B, d):
+        raise ValueError("Wq [V, d], Wd [V, ldd] (d / 32 <= ldd <= d / 32 + 64) and H [num_reqs * B, d] required")
+    ldd = Wd.shape[1]
     _q8_pair(w1q, w1d, V, r, "w1")
     _q8_pair(w2q, w2d, V, r, "w2")
     dev = H.device
@@ -787,10 +824,18 @@ def draft_round_q8(Wq: torch.Tensor, Wd: torch.Tensor, H: torch.Tensor, w1q: tor
     if workspace is None:
         workspace = markov_workspace(R, k, V, dev)
     _dev(workspace, torch.uint8, "workspace", 1)
-    _check(lib().dspark_draft_round_q8(Wq.data_ptr(), Wd.data_ptr(), V, d, H.data_ptr(), R, B, w1q.data_ptr(),
-                                       w1d.data_ptr(), w2q.data_ptr(), w2d.data_ptr(), r, d2t_ptr, prev0.data_ptr(),
-                                       k, pw_ptr, float(probe_bias), float(probe_threshold), base_out.data_ptr(),
-                                       ids_ptr, lo_ptr, pa_ptr, workspace.data_ptr(), workspace.numel(), _stream(H)))
+    if ldd == d // 32:
+        _check(lib().dspark_draft_round_q8(Wq.data_ptr(), Wd.data_ptr(), V, d, H.data_ptr(), R, B, w1q.data_ptr(),
+                                           w1d.data_ptr(), w2q.data_ptr(), w2d.data_ptr(), r, d2t_ptr,
+                                           prev0.data_ptr(), k, pw_ptr, float(probe_bias), float(probe_threshold),
+                                           base_out.data_ptr(), ids_ptr, lo_ptr, pa_ptr, workspace.data_ptr(),
+                                           workspace.numel(), _stream(H)))
+    else:
+        _check(lib().dspark_draft_round_q8_ld(Wq.data_ptr(), Wd.data_ptr(), ldd, V, d, H.data_ptr(), R, B,
+                                              w1q.data_ptr(), w1d.data_ptr(), w2q.data_ptr(), w2d.data_ptr(), r,
+                                              d2t_ptr, prev0.data_ptr(), k, pw_ptr, float(probe_bias),
+                                              float(probe_threshold), base_out.data_ptr(), ids_ptr, lo_ptr, pa_ptr,
+                                              workspace.data_ptr(), workspace.numel(), _stream(H)))
     return dict(base=base_out, ids=ids_out, logit=logit_out, passed=pass_out)
 
 

@@ -206,6 +206,23 @@ dspark_status dspark_lm_head_q8(const int8_t* Wq, const uint16_t* Wd, int V, int
                                 float* logits, void* stream);
 
 /*
+ * dspark_lm_head_q8_ld -- dspark_lm_head_q8 with scale rows ldd binary16
+ * values apart (Wd [V, ldd]; the first d / 32 of each row are the scales,
+ * the rest padding that is never read as a scale).
+ *
+ * A layout choice of the caller, made once when the weights are packed:
+ * the computation is that of dspark_lm_head_q8 on the same values, bit for
+ * bit. With rows padded to whole 128-byte lines (ldd a multiple of 64), no
+ * line holds the scales of two rows, so none is fetched once per K phase of
+ * each row that shares it (at d = 5120 a dense row's 320 bytes of scales
+ * start mid-line on every other row).
+ * Sizes: those of dspark_lm_head_q8, and d / 32 <= ldd <= d / 32 + 64
+ * (DSPARK_ERR_SHAPE otherwise).
+ */
+dspark_status dspark_lm_head_q8_ld(const int8_t* Wq, const uint16_t* Wd, int ldd, int V, int d, const float* H,
+                                   int rows, float* logits, void* stream);
+
+/*
  * Bytes of device workspace dspark_markov_sample needs for these sizes
  * (0 when a size is out of range). The layout is the same for every valid
  * size (about 2 MiB), so one workspace serves calls of any shape.
@@ -451,6 +468,15 @@ dspark_status dspark_draft_round_q8(const int8_t* Wq_lm, const uint16_t* Wd_lm, 
                                     float probe_threshold, float* base_out, int64_t* ids_out,
                                     float* logit_out, int32_t* pass_out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+/* The same with the lm_head's scale rows ldd_lm apart (as dspark_lm_head_q8_ld). */
+dspark_status dspark_draft_round_q8_ld(const int8_t* Wq_lm, const uint16_t* Wd_lm, int ldd_lm, int V, int d,
+                                       const float* H, int num_reqs, int B, const int8_t* w1q,
+                                       const uint16_t* w1d, const int8_t* w2q, const uint16_t* w2d, int r,
+                                       const int64_t* d2t, const int64_t* prev0, int k,
+                                       const uint16_t* probe_w, float probe_bias, float probe_threshold,
+                                       float* base_out, int64_t* ids_out, float* logit_out,
+                                       int32_t* pass_out, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /*
  * The rest of the draft block forward at small M.

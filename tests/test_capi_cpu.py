@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
               "dspark_lm_head_split_workspace_bytes", "dspark_draft_round_workspace_bytes",
               "dspark_markov_sample", "dspark_conf_probe",
               "dspark_markov_sample_probe", "dspark_draft_round", "dspark_proj_smallm_q8", "dspark_lm_head_q8",
-              "dspark_markov_sample_q8", "dspark_draft_round_q8", "dspark_rmsnorm", "dspark_silu_gate",
+              "dspark_markov_sample_q8", "dspark_draft_round_q8", "dspark_lm_head_q8_ld",
+              "dspark_draft_round_q8_ld", "dspark_rmsnorm", "dspark_silu_gate",
               "dspark_proj_smallm_add", "dspark_proj_smallm_norm", "dspark_proj_smallm_norm_fits",
               "dspark_attention_ragged",
               "dspark_markov_workspace_bytes",
@@ -132,6 +133,16 @@ def test_gemv_q8_errors(L):
         assert fn(A + 8, A, 16, 64, A, 7, A2, None) == ERR_ALIGN  # quants need 16 bytes
         assert fn(A, A + 1, 16, 64, A, 7, A2, None) == ERR_ALIGN  # scales need 2
         assert fn(A, A, 16, 64, MIS, 7, A2, None) == ERR_ALIGN
+
+
+def test_lm_head_q8_ld_errors(L):
+    f = L.dspark_lm_head_q8_ld
+    assert f(None, A, 2, 16, 64, A, 7, A2, None) == ERR_NULL
+    assert f(A, A, 2, 16, 80, A, 7, A2, None) == ERR_SHAPE       # K % 32 != 0
+    assert f(A, A, 1, 16, 64, A, 7, A2, None) == ERR_SHAPE       # fewer scales per row than K / 32
+    assert f(A, A, 67, 16, 64, A, 7, A2, None) == ERR_SHAPE      # more than one line of padding
+    assert f(A, A + 1, 64, 16, 64, A, 7, A2, None) == ERR_ALIGN
+    assert f(A, A, 64, 16, 64, MIS, 7, A2, None) == ERR_ALIGN
 
 
 def test_markov_errors(L):
@@ -297,6 +308,25 @@ def test_draft_round_q8_errors(L):
     assert call(d=4100) == ERR_SHAPE      # d % 32 != 0
     assert call(r=1024) == ERR_SHAPE
     assert call(R=0) == ERR_SHAPE
+    assert call(Wd=A + 1) == ERR_ALIGN
+    assert call(ws=None) == ERR_WORKSPACE
+
+
+def test_draft_round_q8_ld_errors(L):
+    f = L.dspark_draft_round_q8_ld
+    ws = L.dspark_markov_workspace_bytes(1, 7, 151936)
+    good = dict(Wq=A, Wd=A2, ldd=192, V=151936, d=5120, H=A2, R=1, B=7, w1q=A, w1d=A2, w2q=A2, w2d=A, r=256,
+                d2t=None, prev0=A, k=7, pw=A, base=A2, ids=A, lo=A2, ps=None, ws=A, wsb=ws)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["Wq"], a["Wd"], a["ldd"], a["V"], a["d"], a["H"], a["R"], a["B"], a["w1q"], a["w1d"], a["w2q"],
+                 a["w2d"], a["r"], a["d2t"], a["prev0"], a["k"], a["pw"], 0.0, 0.0, a["base"], a["ids"], a["lo"],
+                 a["ps"], a["ws"], a["wsb"], None)
+    assert call(Wq=None) == ERR_NULL
+    assert call(ldd=159) == ERR_SHAPE     # d / 32 = 160 scales per row at least
+    assert call(ldd=225) == ERR_SHAPE     # at most 64 of padding
+    assert call(d=4100) == ERR_SHAPE
     assert call(Wd=A + 1) == ERR_ALIGN
     assert call(ws=None) == ERR_WORKSPACE
 

@@ -1021,6 +1021,61 @@ def _round_q8_tensors(inp, dev):
                 pw=_bf(inp["probe_w"], dev))
 
 
+Q8_LDD_CASES = [
+    # (M, N, K, ldd): the 27B-lane shape with three and two K phases, rows
+    # padded to 128-byte lines and an odd stride (single-scale loads); a
+    # dense-aligned K; an odd block count; the short kernel.
+    (15, 70001, 5120, 192), (7, 66003, 5120, 161), (7, 9000, 4096, 192), (9, 5003, 160, 64), (3, 300, 7424, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K,ldd", Q8_LDD_CASES)
+def test_lm_head_q8_padded_scales_equal_dense(dev, M, N, K, ldd):
+    """Scale rows ldd apart, the padding filled with NaN: the logits of the
+    dense layout bit for bit (no padding is read as a scale)."""
+    seed = 7150 + M + N + K + ldd
+    say(f"[lm_head q8 ldd] M={M} N={N} K={K} ldd={ldd} seed={seed}")
+    Wq, Wd, X = synth.gemv_q8_inputs(M, N, K, seed)
+    q, d = _ops().q8_from_numpy(Wq, Wd, dev)
+    dp = torch.full((N, ldd), float("nan"), dtype=torch.float16, device=dev)
+    dp[:, :K // 32] = d
+    Xd = _up(X, dev)
+    y0 = _ops().lm_head_q8(q, d, Xd)
+    y1 = _ops().lm_head_q8(q, dp, Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1), "padded scale rows changed the logits"
+    if K % 32 == 0 and (K // 32) % 64 != 0:
+        y2 = _ops().lm_head_q8(q, _ops().q8_pad_scales(d), Xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y2)
+
+
+def test_draft_round_q8_padded_scales_equal_dense(dev):
+    """dspark_draft_round_q8_ld with the lm_head's scale rows padded to whole
+    lines: base logits, ids and probe equal to the dense round's bit for bit,
+    and the ids right against the oracle."""
+    R, B, k, V, d, r = 2, 4, 3, 3000, 5120, 64
+    seed = 8310
+    say(f"[draft_round q8 ldd] R={R} B={B} k={k} V={V} d={d} r={r}")
+    Wq, Wd, H = synth.gemv_q8_inputs(R * B, V, d, seed)
+    _, w1q, w1d, w2q, w2d, prev0 = synth.markov_q8_inputs(R, 1, V, r, seed)
+    _, pw = synth.probe_inputs(1, d, seed)
+    inp = dict(Wq_lm=Wq, Wd_lm=Wd, H=H, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d, prev0=prev0, probe_w=pw)
+    t = _round_q8_tensors(inp, dev)
+    q, dd = t["Wq"]
+    dp = _ops().q8_pad_scales(dd)
+    assert dp.shape[1] == 192
+    a = _ops().draft_round_q8(q, dd, t["H"], *t["w1"], *t["w2"], t["prev0"], B, k, probe_w=t["pw"])
+    b = _ops().draft_round_q8(q, dp, t["H"], *t["w1"], *t["w2"], t["prev0"], B, k, probe_w=t["pw"])
+    torch.cuda.synchronize()
+    for key in ("base", "ids", "logit", "passed"):
+        assert torch.equal(a[key], b[key]), key
+    ref = oracle.draft_round_q8(Wq, Wd, H, w1q, w1d, w2q, w2d, prev0, R, B, k, pw, 0.0, 0.0)
+    logits_close(b["base"].view(R * B, V).cpu().numpy(), ref["base"], "draft_round_q8_ld logits")
+    check_markov(b["ids"].cpu().numpy(), ref["base32"], oracle.q8_0_to_f64(w1q, w1d),
+                 oracle.q8_0_to_f64(w2q, w2d), prev0, k)
+
+
 def test_draft_round_q8_small(dev):
     """A small Q8_0 round against the oracle and against the separate calls."""
     R, B, k, V, d, r = 2, 4, 3, 3000, 256, 64
