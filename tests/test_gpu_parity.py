@@ -103,6 +103,8 @@ SPLIT_CASES = [
     (17, 300, 136), (24, 1000 + 5, 776), (25, 129, 8), (32, 515, 1032), (41, 257, 5120),
     (49, 1000, 1544), (56, 1, 64), (64, 1001, 264), (65, 3000, 1032), (72, 4000 + 3, 5120),
     (73, 515, 200), (80, 1027, 2056), (81, 700, 1000), (160, 513, 320),
+    # the batched lane's d with 84 and 90 rows (two launch parts each)
+    (84, 9003, 5120), (90, 2003, 4096),
 ]
 
 
