@@ -790,7 +790,9 @@ def test_draft_round_fused(dev, name):
 
 # (R, B, k, V, d, r): one workgroup (V <= 256: the probe runs after workgroup
 # 0's last step), and more probe rows than the waves that compute them.
-SMALL_ROUNDS = [(2, 3, 3, 200, 64, 16), (16, 2, 2, 600, 136, 64), (3, 5, 4, 1000, 8, 8)]
+SMALL_ROUNDS = [(2, 3, 3, 200, 64, 16), (16, 2, 2, 600, 136, 64), (3, 5, 4, 1000, 8, 8),
+                # 84 and 90 drafted rows: the split lm_head in two launch parts inside the round
+                (12, 7, 7, 3000, 512, 64), (10, 9, 9, 2000, 256, 32)]
 
 
 @pytest.mark.parametrize("R,B,k,V,d,r", SMALL_ROUNDS)
