@@ -1030,6 +1030,8 @@ Q8_LDD_CASES = [
     # padded to 128-byte lines and an odd stride (single-scale loads); a
     # dense-aligned K; an odd block count; the short kernel.
     (15, 70001, 5120, 192), (7, 66003, 5120, 161), (7, 9000, 4096, 192), (9, 5003, 160, 64), (3, 300, 7424, 256),
+    # more than 16 rows: two launches over the same padded scales
+    (20, 5003, 5120, 192),
 ]
 
 
